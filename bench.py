@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Throughput of the Int4-Block64 linear layer on one MI355X.
+
+One step = the two launches the headline metric names, on synthetic seeded
+inputs resident in HBM: the decode GEMV (M=1, K=4096, N=11008) and the
+prefill GEMM (M=512, K=4096, N=4096), both through qgemm_run on torch's
+current stream. GFLOPS follow the MNN GemmSpeed page's convention
+2*M*K*N / t (section "Measurement flow").
+
+The weights, activations and outputs rotate over enough copies that the
+working set of the timed region exceeds twice the 256 MB Infinity Cache, so
+every launch streams its weights from HBM as a real multi-layer model would.
+
+Printed: one JSON line (the metric of the run) with a `roofline` object for
+the dominant kernel (the prefill GEMM on the fp16 matrix cores), a
+`decode_roofline` object for the GEMV against HBM bandwidth, and a
+`cpu_baseline` object (the CPU oracle timed on a bounded row sample of the
+same workload, whose outputs are also compared with the GPU's).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GFLOPS + % roofline: int4b64 GEMM at M=1 (HBM GB/s) and M=512 (MFMA util)"
+DECODE, PREFILL = "int4b64_decode", "int4b64_prefill"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
+MALL_BYTES = 256 << 20
+
+
+def algorithmic_bytes(M: int, K: int, N: int) -> int:
+    """Bytes the Int4-Block64 product must move: A fp16, codes (K/2 per
+    channel), fp32 [offset, scale] pairs (8 per 64-block per channel), C fp32."""
+    return M * K * 2 + N * K // 2 + N * (K // 64) * 8 + M * N * 4
+
+
+def flops(M: int, K: int, N: int) -> int:
+    return 2 * M * K * N
+
+
+class Workload:
+    """Packed weights, activations and outputs of one named shape, R copies."""
+
+    def __init__(self, name: str, copies: int):
+        import torch
+        from weight_quantized_gemm_amd import qgemm as Q
+        from weight_quantized_gemm_amd import synth
+        inp = synth.make_inputs(name)
+        self.name = name
+        self.M, self.K, self.N = inp["M"], inp["K"], inp["N"]
+        self.A_host = inp["A"]
+        self.W_host = inp["W"]
+        q, p = Q.qgemm_quantize_weights(inp["W"], "int4b64")
+        self.q_host, self.pairs_host = q, p
+        wp, sp = Q.qgemm_pack_weights(self.K, self.N, "int4b64", q, p)
+        A0 = torch.from_numpy(inp["A"]).cuda()
+        B0 = torch.from_numpy(wp).cuda()
+        S0 = torch.from_numpy(sp).cuda()
+        self.A = [A0] + [A0.clone() for _ in range(copies - 1)]
+        self.B = [B0] + [B0.clone() for _ in range(copies - 1)]
+        self.S = [S0] + [S0.clone() for _ in range(copies - 1)]
+        self.C = [torch.empty((self.M, self.N), dtype=torch.float32, device="cuda")
+                  for _ in range(copies)]
+        self.Q = Q
+
+    def bytes_per_copy(self) -> int:
+        return (self.A[0].nbytes + self.B[0].nbytes + self.S[0].nbytes + self.C[0].nbytes)
+
+    def run(self, i: int) -> None:
+        c = i % len(self.A)
+        self.Q.qgemm_run(self.M, self.K, self.N, self.Q.QGEMM_INT4_B64, self.A[c], self.B[c],
+                         self.S[c], self.C[c])
+
+
+def traffic_record(kernel_src: str, kernel: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec:
+        return None
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
+    if rec.get("source_sha") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(dec: Workload, pre: Workload, budget_s: float):
+    """The CPU oracle, as it stands, on a bounded sample of the step: the full
+    decode GEMV and a row sample of the prefill, scaled to one step."""
+    from oracle import oracle as O
+    threads = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
+    lib = O.load()
+    q, p = O.quantize(dec.W_host, "int4b64")
+    t0 = time.perf_counter()
+    c_dec = O.gemm_blockq(dec.A_host, q, p, "int4b64", lib)
+    t_dec = time.perf_counter() - t0
+    qp, pp = O.quantize(pre.W_host, "int4b64")
+    probe = 2
+    t0 = time.perf_counter()
+    O.gemm_blockq(pre.A_host[:probe], qp, pp, "int4b64", lib)
+    t_probe = (time.perf_counter() - t0) / probe
+    rows = int(max(probe, min(pre.M, (budget_s - t_dec) / max(t_probe, 1e-9))))
+    sel = np.linspace(0, pre.M - 1, rows).astype(int)
+    t0 = time.perf_counter()
+    c_pre = O.gemm_blockq(pre.A_host[sel], qp, pp, "int4b64", lib)
+    t_pre = time.perf_counter() - t0
+    step_s = t_dec + t_pre * pre.M / rows
+    step_flops = flops(dec.M, dec.K, dec.N) + flops(pre.M, pre.K, pre.N)
+    # the GPU's outputs on the same sample
+    g_dec = dec.C[0].cpu().numpy().astype(np.float64)
+    g_pre = pre.C[0].cpu().numpy().astype(np.float64)[sel]
+    err = max(float(np.abs(g_dec - c_dec).max()), float(np.abs(g_pre - c_pre).max()))
+    return {
+        "value": step_flops / step_s / 1e9,
+        "unit": "GFLOPS",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"full decode GEMV (1x4096x11008) + {rows} of 512 prefill rows "
+                   f"(x4096x4096), fp64 naive loops, scaled to one step; "
+                   f"{t_dec + t_pre:.1f} s of CPU time"),
+        "seconds_per_step": step_s,
+        "gpu_max_abs_err_on_sample": err,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=0, help="rotation copies (0: auto)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of CPU oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {args.gpus}); "
+              "multi-GPU sharding is described in the design notes but not built.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    torch.cuda.set_device(0)
+
+    # one decode + one prefill copy is ~50 MB; rotate past 2x the MALL
+    per_step_bytes = (algorithmic_bytes(1, 4096, 11008) + algorithmic_bytes(512, 4096, 4096))
+    copies = args.copies or max(2, -(-2 * MALL_BYTES // per_step_bytes) + 1)
+    dec = Workload(DECODE, copies)
+    pre = Workload(PREFILL, copies)
+
+    for i in range(args.warmup):
+        pre.run(i)
+        dec.run(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        ev[i][0].record()
+        pre.run(i)
+        ev[i][1].record()
+        dec.run(i)
+        ev[i][2].record()
+    stop.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ms_step = start.elapsed_time(stop) / K
+    pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+
+    step_flops = flops(dec.M, dec.K, dec.N) + flops(pre.M, pre.K, pre.N)
+    value = step_flops / (ms_step * 1e-3) / 1e9
+    pre_tflops = flops(pre.M, pre.K, pre.N) / (pre_ms * 1e-3) / 1e12
+    dec_gbs = algorithmic_bytes(dec.M, dec.K, dec.N) / (dec_ms * 1e-3) / 1e9
+    src = os.path.join(ROOT, "weight_quantized_gemm_amd", "csrc")
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "GFLOPS",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": ("int4b64 linear layer: decode GEMV M=1 K=4096 N=11008 + "
+                         "prefill GEMM M=512 K=4096 N=4096 (fp16 A, Int4-Block64 B, fp32 C)"),
+            "rotation_copies": copies,
+            "rotated_bytes": copies * (dec.bytes_per_copy() + pre.bytes_per_copy()),
+            "wall_ms_per_step": wall_ms / K,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "gemm_f16dq_kernel<INT4_B64> (prefill M=512 K=4096 N=4096)",
+            "achieved": pre_tflops,
+            "peak": FP16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": pre_tflops / FP16_PEAK_TFLOPS,
+            "traffic": traffic_record(os.path.join(src, "gemm_f16dq.hip"), "gemm_f16dq_int4b64"),
+            "avg_launch_ms": pre_ms,
+        },
+        "decode_roofline": {
+            "bound": "hbm",
+            "kernel": "gemv_int4b64_kernel (decode M=1 K=4096 N=11008)",
+            "achieved": dec_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": dec_gbs / HBM_PEAK_GBS,
+            "traffic": traffic_record(os.path.join(src, "gemv.hip"), "gemv_int4b64"),
+            "avg_launch_ms": dec_ms,
+            "gflops": flops(dec.M, dec.K, dec.N) / (dec_ms * 1e-3) / 1e9,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(dec, pre, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,225 @@
+/*
+ * qgemm.h -- C ABI of libqgemm, the weight-quantized GEMM for AMD MI355X
+ * (gfx950 / CDNA4).
+ *
+ * The one operation (MNN GemmSpeed benchmark page, section "Why Conv1x1 is
+ * used to measure GEMM"): an LLM linear layer C = A[M,K] x B[K,N], where the
+ * weight B is held in one of the page's formats:
+ *
+ *   QGEMM_F32       float weights (page mode 0, "float-gemm"); fp32 A, B, C.
+ *   QGEMM_INT4_B64  Int4-Block64 (mode 1, "int4b64-gemm"): 4-bit codes, one
+ *                   [offset, scale] pair per 64 K-elements per output
+ *                   channel, w = offset + scale * q.
+ *   QGEMM_INT8_B0   Int8-Block0 (mode 2, "int8b0-gemm"): 8-bit codes, one
+ *                   pair per output channel (blockSize = K).
+ *   QGEMM_W4A8      Int4-Block0 W4A8 (mode 3, section "Test cases and
+ *                   registration"): 4-bit per-channel codes unpacked to
+ *                   int8; each row of A is quantised on the fly to int8; the
+ *                   product is s8 x s8 -> s32, exact, then rescaled to fp32.
+ *
+ * Format ids equal the page's mode numbers. For every quantised format A is
+ * fp16 and C is fp32.
+ *
+ * Canonical (user-facing) weight layouts, on the host:
+ *   - F32:      B float [K][N] row-major (the page's weight shape {ic, oc}).
+ *   - INT8_B0:  q uint8 [N][K]; pairs float [N][1][2] = {offset, scale}.
+ *   - INT4_B64: q uint8 [N][K/2], byte j of a row = q[2j] | q[2j+1] << 4
+ *               (two codes per byte along K, low nibble first);
+ *               pairs float [N][K/64][2] = {offset, scale} (the page: oc x
+ *               blockNum groups of [offset, scale]).
+ *   - W4A8:     q as INT4_B64 with one block over all of K; pairs float
+ *               [N][1][2].
+ * Codes are unsigned: q in [0, 2^bits - 1].
+ *
+ * Packed (device) layouts are opaque and owned by this library: they are
+ * produced by qgemm_pack_weights on the host, copied to device memory by the
+ * caller, and consumed by qgemm_run. They are padded (channels to a multiple
+ * of 4 or 32, K to the kernels' step) with zero codes and zero pairs.
+ *
+ * Conventions shared by every function:
+ *   - Return a qgemm_status; nothing aborts, throws, prints or exits.
+ *   - Every argument is checked before anything is enqueued on the GPU; a
+ *     rejected call has no effect.
+ *   - Shapes are ints; M, N >= 0, K >= 0. M == 0 or N == 0 is a valid empty
+ *     product: OK, nothing is read or written, pointers are not inspected.
+ *   - Device pointers must be 16-byte aligned (torch allocations are).
+ *   - The caller owns every buffer. qgemm_run keeps no pointer after it
+ *     returns, but the GPU reads and writes the buffers asynchronously until
+ *     the stream reaches that point: keep them alive until then.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default
+ *     stream. Faults during execution surface at the caller's next
+ *     synchronisation with the stream (ordinary HIP semantics).
+ *   - Functions are thread-safe: the only global state is the dispatch
+ *     threshold (an atomic) and the per-process HIP module state.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QGEMM_ABI_VERSION 1
+
+typedef enum qgemm_format {
+    QGEMM_F32 = 0,
+    QGEMM_INT4_B64 = 1,
+    QGEMM_INT8_B0 = 2,
+    QGEMM_W4A8 = 3
+} qgemm_format;
+
+typedef enum qgemm_status {
+    QGEMM_OK = 0,
+    QGEMM_ERR_NULL = 1,     /* a required pointer is NULL                     */
+    QGEMM_ERR_SHAPE = 2,    /* a shape is negative, too large, or violates the
+                               format's block rule (INT4_B64: K % 64 == 0;
+                               INT4/W4A8: K even; quantised formats: K > 0)   */
+    QGEMM_ERR_FORMAT = 3,   /* unknown format, or an operation the format does
+                               not have (e.g. quantising to F32)              */
+    QGEMM_ERR_ALIGN = 4,    /* a device pointer is not 16-byte aligned        */
+    QGEMM_ERR_NOMEM = 5,    /* the library could not allocate its scratch     */
+    QGEMM_ERR_DEVICE = 6,   /* no usable HIP device                           */
+    QGEMM_ERR_LAUNCH = 7,   /* the HIP runtime rejected a kernel launch       */
+    QGEMM_ERR_SIZE = 8,     /* a caller buffer is smaller than required       */
+    QGEMM_ERR_VALUE = 9     /* non-finite input to the quantiser              */
+} qgemm_status;
+
+/* Human-readable name of a status; never NULL. */
+const char *qgemm_status_string(int status);
+
+/* QGEMM_ABI_VERSION of the built library. */
+int qgemm_abi_version(void);
+
+/*
+ * Sizes of the canonical buffers of a format: q_bytes for the codes (or the
+ * fp32 B for F32) and pair_floats for the [offset, scale] pairs (0 for F32).
+ * Errors: ERR_NULL, ERR_FORMAT, ERR_SHAPE.
+ */
+qgemm_status qgemm_canonical_size(int K, int N, qgemm_format f,
+                                  size_t *q_bytes, size_t *pair_floats);
+
+/*
+ * Host-side quantiser (the offline export step the page attributes to
+ * mnnconvert; MNN GemmSpeed page, section "Why Conv1x1 is used to measure
+ * GEMM": asymmetric quantisation with [offset, scale] pairs).
+ * W: host float [N][K] (one row per output channel). For each (channel,
+ * block): offset = minimum, scale = (maximum - minimum) / (2^bits - 1)
+ * computed in double and stored as float, q = rint((w - offset) / scale) in
+ * double from the stored pair, clamped to [0, 2^bits - 1]; a constant block
+ * gets scale 0 and q 0. Writes the canonical q (q_bytes) and pairs
+ * (pair_floats floats), both host memory owned by the caller.
+ * Errors: ERR_NULL, ERR_FORMAT (F32 or unknown), ERR_SHAPE, ERR_SIZE,
+ * ERR_VALUE (a NaN or infinite weight; nothing useful is written then).
+ */
+qgemm_status qgemm_quantize_weights(int K, int N, qgemm_format f,
+                                    const float *W, void *q, size_t q_bytes,
+                                    float *pairs, size_t pair_floats);
+
+/*
+ * Sizes in bytes of the packed weight buffer (w_bytes) and the packed pair
+ * buffer (s_bytes, 0 for F32) of a K x N weight.
+ * Errors: ERR_NULL, ERR_FORMAT, ERR_SHAPE.
+ */
+qgemm_status qgemm_packed_size(int K, int N, qgemm_format f,
+                               size_t *w_bytes, size_t *s_bytes);
+
+/*
+ * Host-side packer: canonical layout -> the library's device layout. Pure
+ * byte/nibble permutation plus zero padding; no value changes (the
+ * LLM-on-PowerVR page, section 2, re-lays weights out offline into the
+ * order its kernel fetches them in; this packer does the same for gfx950).
+ * w_canonical / pairs_canonical: host, read-only, canonical layouts above
+ * (pairs_canonical ignored and may be NULL for F32). w_packed / s_packed:
+ * host, caller-allocated, at least qgemm_packed_size() bytes; the caller
+ * then copies them to device memory.
+ * Errors: ERR_NULL, ERR_FORMAT, ERR_SHAPE, ERR_SIZE.
+ */
+qgemm_status qgemm_pack_weights(int K, int N, qgemm_format f,
+                                const void *w_canonical,
+                                const float *pairs_canonical,
+                                void *w_packed, size_t w_bytes,
+                                void *s_packed, size_t s_bytes);
+
+/*
+ * Inverse of qgemm_pack_weights (host): recovers the canonical buffers from
+ * packed ones. Lets a caller check or re-export packed weights.
+ * Errors: ERR_NULL, ERR_FORMAT, ERR_SHAPE, ERR_SIZE.
+ */
+qgemm_status qgemm_unpack_weights(int K, int N, qgemm_format f,
+                                  const void *w_packed, size_t w_bytes,
+                                  const void *s_packed, size_t s_bytes,
+                                  void *w_canonical, float *pairs_canonical);
+
+/*
+ * Device scratch qgemm_run_ws needs: 0 except W4A8, which stores the
+ * quantised activations (int8 [M][K rounded up to 64]), the row scales
+ * (float [M]) and the row sums of the quantised activations (int32 [M]).
+ * Errors: ERR_NULL, ERR_FORMAT, ERR_SHAPE.
+ */
+qgemm_status qgemm_workspace_size(int M, int K, int N, qgemm_format f,
+                                  size_t *bytes);
+
+/*
+ * C = A x B on the GPU, enqueued on `stream`; returns without waiting.
+ *   A       device, [M][K] row-major: float for F32, fp16 otherwise.
+ *   Bq      device, packed weights from qgemm_pack_weights (for F32 the
+ *           packed B is the float [K][N] matrix itself).
+ *   scales  device, packed pairs; must be NULL for F32.
+ *   C       device, float [M][N] row-major, fully overwritten (no alpha or
+ *           beta; K == 0 for F32 writes zeros).
+ * Dispatch: INT4_B64 / INT8_B0 with M at most the GEMV threshold (default 8,
+ * see qgemm_set_gemv_max_m) take the streaming GEMV (the page: M = 8 is the
+ * narrow, near-decode case, bounded by GEMV bandwidth); larger M take the
+ * LDS-staged fp16 MFMA kernel. W4A8 runs the activation quantiser then the
+ * int8 MFMA kernel; its scratch is allocated stream-ordered on `stream`
+ * (hipMallocAsync / hipFreeAsync). F32 runs the fp32 tiled kernel.
+ * The buffers' sizes are not visible to the library: the caller guarantees
+ * A holds M*K, C M*N elements and Bq / scales qgemm_packed_size() bytes.
+ * Errors: ERR_NULL, ERR_FORMAT, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE,
+ * ERR_NOMEM, ERR_LAUNCH.
+ */
+qgemm_status qgemm_run(int M, int K, int N, qgemm_format f, const void *A,
+                       const void *Bq, const void *scales, float *C,
+                       void *stream);
+
+/*
+ * As qgemm_run, with caller-provided device scratch `workspace` of
+ * ws_bytes >= qgemm_workspace_size() bytes (may be NULL when that size is
+ * 0). The library allocates nothing. Calls that share a workspace must be
+ * ordered (same stream, or synchronised).
+ * Errors: as qgemm_run, plus ERR_SIZE for a short workspace.
+ */
+qgemm_status qgemm_run_ws(int M, int K, int N, qgemm_format f, const void *A,
+                          const void *Bq, const void *scales, float *C,
+                          void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * W4A8 with its intermediate results exposed, for bit-exact checks of the
+ * integer path: the quantised activations qa (int8 [M][K]), the row scales
+ * sa (float [M]), the row sums S of qa (int32 [M]) and the exact integer
+ * product D (int32 [M][N], D[m][n] = sum_k qa[m][k] * q[n][k]); C as
+ * qgemm_run. All device buffers, caller-owned; workspace as qgemm_run_ws.
+ * Errors: as qgemm_run_ws.
+ */
+qgemm_status qgemm_w4a8_debug(int M, int K, int N, const void *A,
+                              const void *Bq, const void *scales, float *C,
+                              int8_t *qa, float *sa, int32_t *S, int32_t *D,
+                              void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Sets the largest M that INT4_B64 / INT8_B0 send to the GEMV kernel
+ * (0..8; default 8, or the QGEMM_GEMV_MAX_M environment variable read at
+ * first use) and returns the previous value; a value outside 0..8 is
+ * ignored and only the current value returned. Affects only which kernel
+ * runs, never the result beyond rounding.
+ */
+int qgemm_set_gemv_max_m(int max_m);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

@@ -1,0 +1,182 @@
+"""C-ABI checks that need no GPU: exports, argument validation (every
+rejection happens before anything touches the GPU), the host quantiser
+against the oracle's quantiser (bit-exact), and packer round trips."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from weight_quantized_gemm_amd import qgemm as Q
+from weight_quantized_gemm_amd import synth
+
+FMTS = ["int4b64", "int8b0", "w4a8"]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return Q.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    import os
+    import re
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "qgemm.h")).read()
+    declared = set(re.findall(r"^\s*(?:const char \*|int |qgemm_status )(qgemm_\w+)\(", hdr, re.M))
+    assert declared == set(Q.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert Q.qgemm_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code, name in Q.STATUS.items():
+        assert Q.qgemm_status_string(code).startswith(name)
+    assert Q.qgemm_status_string(12345) == "QGEMM_ERR_UNKNOWN"
+
+
+def _run(lib, M, K, N, f, A=256, B=256, S=256, C=256, stream=None):
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.qgemm_run(M, K, N, f, v(A), v(B), v(S), v(C), stream)
+
+
+def test_run_validation_before_device(lib):
+    OK, NULL, SHAPE, FMT, ALIGN, DEV = 0, 1, 2, 3, 4, 6
+    # unknown format
+    assert _run(lib, 1, 64, 4, 7) == FMT
+    # shapes
+    assert _run(lib, -1, 64, 4, 1) == SHAPE
+    assert _run(lib, 1, 63, 4, 1) == SHAPE          # Int4-Block64 needs K % 64 == 0
+    assert _run(lib, 1, 0, 4, 1) == SHAPE
+    assert _run(lib, 1, 0, 4, 2) == SHAPE
+    assert _run(lib, 1, 65, 4, 3) == SHAPE          # W4A8 needs even K
+    assert _run(lib, 1, 2 * 1127500, 4, 3) == SHAPE  # int32 D could overflow
+    # empty products are valid and touch nothing
+    assert _run(lib, 0, 64, 4, 1, None, None, None, None) == OK
+    assert _run(lib, 5, 64, 0, 1, None, None, None, None) == OK
+    # null pointers
+    assert _run(lib, 1, 64, 4, 1, C=None) == NULL
+    assert _run(lib, 1, 64, 4, 1, A=None) == NULL
+    assert _run(lib, 1, 64, 4, 1, S=None) == NULL
+    assert _run(lib, 1, 64, 4, 0, S=256) == FMT      # F32 takes no scales
+    # alignment
+    assert _run(lib, 1, 64, 4, 1, A=258) == ALIGN
+    assert _run(lib, 1, 64, 4, 1, C=260) == ALIGN
+    # a valid request on a host without a gfx950 GPU
+    import torch
+    if not torch.cuda.is_available():
+        assert _run(lib, 1, 64, 4, 1) == DEV
+        assert _run(lib, 3, 0, 4, 0, S=None) == DEV   # F32 with K = 0 is valid
+
+
+def test_run_ws_validation(lib):
+    v = ctypes.c_void_p
+    ws = Q.qgemm_workspace_size(8, 128, 16, "w4a8")
+    assert ws > 0 and Q.qgemm_workspace_size(8, 128, 16, "int4b64") == 0
+    st = lib.qgemm_run_ws(8, 128, 16, 3, v(256), v(256), v(256), v(256), None, 0, None)
+    assert st == 1                                   # W4A8 needs a workspace
+    st = lib.qgemm_run_ws(8, 128, 16, 3, v(256), v(256), v(256), v(256), v(512), ws - 1, None)
+    assert st == 8                                   # too small
+    st = lib.qgemm_run_ws(8, 128, 16, 3, v(256), v(256), v(256), v(256), v(520), ws, None)
+    assert st == 4                                   # misaligned
+
+
+def test_sizes():
+    assert Q.qgemm_packed_size(4096, 11008, "int4b64") == (22544384, 5636096)
+    assert Q.qgemm_packed_size(4096, 4096, "int8b0") == (16777216, 32768)
+    assert Q.qgemm_packed_size(3072, 8192, "w4a8") == (12582912, 65536)
+    assert Q.qgemm_packed_size(256, 256, "f32") == (262144, 0)
+    # ragged shapes pad channels and K, then round to 256 bytes
+    w, s = Q.qgemm_packed_size(137, 70, "int8b0")
+    assert w == 72 * 192 and s == 768
+    assert Q.qgemm_canonical_size(4096, 11008, "int4b64") == (11008 * 2048, 11008 * 64 * 2)
+    with pytest.raises(Q.QGemmError):
+        Q.qgemm_packed_size(100, 8, "int4b64")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", [(1, 64), (5, 128), (70, 192), (33, 1024)])
+def test_quantizer_matches_oracle_bit_exact(fmt, shape):
+    N, K = shape
+    rng = np.random.default_rng(N * 1000 + K)
+    W = synth.normal_weights(rng, N, K)
+    W[0, :16] = 0.25                                  # partly constant block
+    if N > 2:
+        W[2, :] = -0.125                              # a fully constant channel
+    q_lib, p_lib = Q.qgemm_quantize_weights(W, fmt)
+    q_orc, p_orc = O.quantize(W, fmt)
+    assert np.array_equal(q_lib, q_orc)
+    assert np.array_equal(p_lib.view(np.uint32), p_orc.view(np.uint32))
+
+
+def test_quantizer_rejects_nonfinite():
+    W = np.zeros((4, 64), np.float32)
+    W[1, 3] = np.nan
+    with pytest.raises(Q.QGemmError) as e:
+        Q.qgemm_quantize_weights(W, "int4b64")
+    assert e.value.status == 9
+    with pytest.raises(Q.QGemmError):
+        Q.qgemm_quantize_weights(np.zeros((4, 64), np.float32), "f32")
+
+
+@pytest.mark.parametrize("fmt", FMTS + ["f32"])
+@pytest.mark.parametrize("shape", [(1, 64), (3, 128), (70, 192), (37, 4160)])
+def test_pack_unpack_round_trip(fmt, shape):
+    N, K = shape
+    rng = np.random.default_rng(K + N)
+    if fmt == "f32":
+        wc = rng.standard_normal((K, N)).astype(np.float32)
+        pc = None
+    else:
+        qb, pf = Q.qgemm_canonical_size(K, N, fmt)
+        wc = rng.integers(0, 256, size=qb).astype(np.uint8)
+        pc = rng.standard_normal(pf).astype(np.float32)
+    wp, sp = Q.qgemm_pack_weights(K, N, fmt, wc, pc)
+    q2, p2 = Q.qgemm_unpack_weights(K, N, fmt, wp, sp)
+    assert np.array_equal(q2, wc.reshape(-1).view(np.uint8))
+    if pc is not None:
+        assert np.array_equal(p2, pc)
+    # padding is zero: the packed buffer holds exactly the canonical content
+    if fmt == "int8b0":
+        assert int(np.count_nonzero(wp)) == int(np.count_nonzero(wc))
+    elif fmt != "f32":
+        nz = lambda b: int(np.count_nonzero(b & 15) + np.count_nonzero(b >> 4))
+        assert nz(wp) == nz(wc)
+
+
+def test_int4_packed_layout_golden():
+    """Chunk (g, j, b) of the Int4-Block64 layout holds bytes [32b + 16(j&1), +16)
+    of channel 4g + j/2; pair record (g, h, b) holds channels 4g+2h, 4g+2h+1."""
+    N, K = 8, 128
+    nblk = K // 64
+    wc = np.arange(N * K // 2, dtype=np.int64).astype(np.uint8).reshape(N, K // 2)
+    pc = np.arange(N * nblk * 2, dtype=np.float32).reshape(N, nblk, 2)
+    wp, sp = Q.qgemm_pack_weights(K, N, "int4b64", wc, pc)
+    chunks = wp.reshape(-1, 16)
+    recs = sp.view(np.float32).reshape(-1, 4)
+    for n in range(N):
+        g, c = divmod(n, 4)
+        for b in range(nblk):
+            for half in range(2):
+                j = 2 * c + half
+                assert np.array_equal(chunks[(g * 8 + j) * nblk + b],
+                                      wc[n, 32 * b + 16 * half: 32 * b + 16 * half + 16])
+            rec = recs[(g * 2 + c // 2) * nblk + b]
+            assert list(rec[(c % 2) * 2:(c % 2) * 2 + 2]) == list(pc[n, b])
+
+
+def test_w4a8_packed_word_order_golden():
+    """Each word of a W4A8 record holds code k0+i in the low and k0+4+i in the
+    high nibble of byte i, so nibble masks give codes in natural k order."""
+    K, N = 64, 1
+    codes = np.arange(64) % 16
+    wc = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)[None, :]
+    pc = np.zeros((1, 1, 2), np.float32)
+    wp, _ = Q.qgemm_pack_weights(K, N, "w4a8", wc, pc)
+    rec = wp[:32]
+    lo = rec & 15
+    hi = rec >> 4
+    for w in range(8):
+        for i in range(4):
+            assert lo[4 * w + i] == codes[8 * w + i]
+            assert hi[4 * w + i] == codes[8 * w + 4 + i]

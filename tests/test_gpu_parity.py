@@ -1,0 +1,309 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Inputs come from the seeded generator; the library's own host quantiser
+produces the HIP side's canonical weights and the oracle's quantiser the
+oracle side's (the two are bit-identical, checked on the CPU). Tolerances:
+max-abs 1e-2 and relative-Frobenius 2e-3 for the fp16/fp32-accumulated
+paths; bit-exact for the W4A8 integer intermediates (qa, sa, S, D).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import compare, dev, require_gpu, run
+from oracle import oracle as O
+from weight_quantized_gemm_amd import qgemm as Q
+from weight_quantized_gemm_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+    prev = Q.qgemm_set_gemv_max_m(8)
+    yield
+    Q.qgemm_set_gemv_max_m(prev)
+
+
+def _case(fmt, M, K, N, seed):
+    rng = np.random.default_rng(seed)
+    if fmt == "f32":
+        A = synth.activations(rng, M, K, fp16=False)
+        return A, synth.float_pattern_weights(K, N), None
+    A = synth.activations(rng, M, K, fp16=True)
+    W = synth.normal_weights(rng, N, K)
+    return A, W, None
+
+
+def _quantized_pair(fmt, W):
+    q_lib, p_lib = Q.qgemm_quantize_weights(W, fmt)
+    q_orc, p_orc = O.quantize(W, fmt)
+    assert np.array_equal(q_lib, q_orc) and np.array_equal(p_lib, p_orc)
+    return q_lib, p_lib, q_orc, p_orc
+
+
+def _parity(fmt, M, K, N, seed, rows=None, stream=None, ws=False):
+    """Runs one shape on the GPU and checks it (optionally on sampled rows)."""
+    A, W, _ = _case(fmt, M, K, N, seed)
+    if fmt == "f32":
+        C = run(fmt, M, K, N, A, W, None, stream=stream)
+        sel = slice(None) if rows is None else rows
+        ref = O.gemm_f32(A[sel], W)
+        return compare(C[sel], ref, f"f32 {M}x{K}x{N}")
+    q, p, qo, po = _quantized_pair(fmt, W)
+    C = run(fmt, M, K, N, A, q, p, stream=stream, ws=ws)
+    sel = slice(None) if rows is None else rows
+    ref = O.reference(fmt, A[sel], q=qo, pairs=po)
+    return compare(C[sel], ref, f"{fmt} {M}x{K}x{N}")
+
+
+# ---------------------------------------------------------------------------
+# The named workloads, in the launch configuration the bench uses.
+# ---------------------------------------------------------------------------
+SAMPLE_ROWS = {512: [0, 1, 31, 32, 63, 64, 127, 128, 200, 255, 256, 383, 384, 450, 510, 511],
+               1024: [0, 1, 63, 64, 127, 128, 255, 256, 511, 512, 700, 767, 768, 900, 1022, 1023]}
+
+
+@pytest.mark.parametrize("name", list(synth.CONFIGS))
+def test_named_workload(name):
+    fmt, M, K, N, seed = synth.CONFIGS[name]
+    inp = synth.make_inputs(name)
+    A = inp["A"]
+    if fmt == "f32":
+        C = run(fmt, M, K, N, A, inp["B"], None)
+        compare(C, O.gemm_f32(A, inp["B"]), name)
+        return
+    q, p, qo, po = _quantized_pair(fmt, inp["W"])
+    rows = SAMPLE_ROWS.get(M)
+    if fmt == "w4a8":
+        nbytes = Q.qgemm_workspace_size(M, K, N, fmt)
+        wp, sp = Q.qgemm_pack_weights(K, N, fmt, q, p)
+        Ad, Bd, Sd = dev(A), dev(wp), dev(sp)
+        C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        qa = torch.empty((M, K), dtype=torch.int8, device="cuda")
+        sa = torch.empty(M, dtype=torch.float32, device="cuda")
+        S = torch.empty(M, dtype=torch.int32, device="cuda")
+        D = torch.empty((M, N), dtype=torch.int32, device="cuda")
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        Q.qgemm_w4a8_debug(M, K, N, Ad, Bd, Sd, C, qa, sa, S, D, ws, nbytes)
+        torch.cuda.synchronize()
+        qa_o, sa_o, S_o = O.w4a8_actquant(A)
+        # activation quantisation of every row, bit-exact
+        assert np.array_equal(qa.cpu().numpy(), qa_o)
+        assert np.array_equal(sa.cpu().numpy().view(np.uint32), sa_o.view(np.uint32))
+        assert np.array_equal(S.cpu().numpy(), S_o)
+        # the exact integer product and C on sampled rows
+        D_o = O.w4a8_dot(qa_o[rows], qo)
+        assert np.array_equal(D.cpu().numpy()[rows].astype(np.int64), D_o)
+        ref = O.w4a8_rescale(D_o, sa_o[rows], S_o[rows], po)
+        compare(C.cpu().numpy()[rows], ref, name)
+        # the plain entry point (library-allocated scratch) gives the same C
+        C2 = run(fmt, M, K, N, A, q, p)
+        assert np.array_equal(C2, C.cpu().numpy())
+        return
+    C = run(fmt, M, K, N, A, q, p)
+    assert np.all(np.isfinite(C))
+    if rows is None:
+        compare(C, O.reference(fmt, A, q=qo, pairs=po), name)
+    else:
+        compare(C[rows], O.reference(fmt, A[rows], q=qo, pairs=po), name)
+
+
+# ---------------------------------------------------------------------------
+# Ragged shapes, both dispatch paths, tails over several tiles.
+# ---------------------------------------------------------------------------
+SMALL_M = [1, 2, 3, 4, 5, 7, 8, 9, 63, 64, 65, 129]
+
+
+@pytest.mark.parametrize("M", SMALL_M)
+def test_int4b64_shapes(M):
+    for K, N in [(64, 1), (64, 5), (192, 70), (256, 130), (4160, 67)]:
+        _parity("int4b64", M, K, N, seed=M * 7 + K + N)
+
+
+@pytest.mark.parametrize("M", SMALL_M)
+def test_int8b0_shapes(M):
+    for K, N in [(1, 3), (7, 4), (12, 9), (64, 64), (100, 70), (1000, 33), (4100, 6)]:
+        _parity("int8b0", M, K, N, seed=M * 11 + K + N)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 31, 32, 33, 127, 128, 129, 300])
+def test_w4a8_shapes(M):
+    for K, N in [(2, 1), (8, 33), (62, 5), (64, 64), (66, 130), (200, 31), (1030, 257)]:
+        _parity("w4a8", M, K, N, seed=M * 13 + K + N)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 1, 1), (3, 137, 70), (16, 256, 256), (65, 17, 129),
+                                   (130, 300, 67), (64, 64, 64)])
+def test_f32_shapes(M, K, N):
+    _parity("f32", M, K, N, seed=M + K + N)
+
+
+def test_f32_k_zero_writes_zeros():
+    C = run("f32", 3, 0, 5, np.zeros((3, 0), np.float32), np.zeros((0, 5), np.float32), None)
+    assert np.array_equal(C, np.zeros((3, 5), np.float32))
+
+
+@pytest.mark.parametrize("fmt", ["int4b64", "int8b0"])
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_gemv_and_tiled_paths_agree_with_oracle(fmt, M):
+    """M <= 8 runs the GEMV by default; forcing the threshold to 0 sends the
+    same call to the MFMA kernel. Both must meet the oracle's tolerance."""
+    K, N = 1024, 300
+    A, W, _ = _case(fmt, M, K, N, seed=99 + M)
+    q, p, qo, po = _quantized_pair(fmt, W)
+    ref = O.reference(fmt, A, q=qo, pairs=po)
+    C_gemv = run(fmt, M, K, N, A, q, p)
+    prev = Q.qgemm_set_gemv_max_m(0)
+    try:
+        C_mfma = run(fmt, M, K, N, A, q, p)
+    finally:
+        Q.qgemm_set_gemv_max_m(prev)
+    compare(C_gemv, ref, "gemv")
+    compare(C_mfma, ref, "mfma")
+
+
+# ---------------------------------------------------------------------------
+# Closed forms through the real kernels.
+# ---------------------------------------------------------------------------
+def _identity(fmt, K):
+    eye = np.eye(K, dtype=np.uint8)
+    return eye if fmt == "int8b0" else (eye[:, 0::2] | (eye[:, 1::2] << 4)).astype(np.uint8)
+
+
+@pytest.mark.parametrize("fmt", ["int4b64", "int8b0"])
+def test_identity_weights(fmt):
+    """offset 0, scale 1, q = delta_kn: C = A. The MFMA path sums one nonzero
+    product per output, so it is exact; the GEMV path removes a bias from an
+    fp32 sum, so it is held to the tolerance."""
+    K = 128
+    rng = np.random.default_rng(5)
+    A = rng.standard_normal((70, K)).astype(np.float16)
+    q = _identity(fmt, K)
+    nblk = K // 64 if fmt == "int4b64" else 1
+    p = np.zeros((K, nblk, 2), np.float32)
+    p[:, :, 1] = 1.0
+    C = run(fmt, 70, K, K, A, q, p)
+    assert np.array_equal(C, A.astype(np.float32))
+    C1 = run(fmt, 1, K, K, A[:1], q, p)
+    compare(C1, A[:1].astype(np.float64), "gemv identity")
+
+
+@pytest.mark.parametrize("fmt", ["int4b64", "int8b0"])
+@pytest.mark.parametrize("M", [1, 100])
+def test_constant_blocks(fmt, M):
+    """scale = 0: C[m][n] = sum_b offset[n][b] * sum_{k in b} A[m][k]."""
+    K, N = 256, 40
+    rng = np.random.default_rng(6)
+    A = rng.integers(-4, 5, size=(M, K)).astype(np.float16)
+    nblk = K // 64 if fmt == "int4b64" else 1
+    p = np.zeros((N, nblk, 2), np.float32)
+    p[:, :, 0] = 2.0 ** rng.integers(-3, 3, size=(N, nblk))
+    qb, _ = Q.qgemm_canonical_size(K, N, fmt)
+    q = rng.integers(0, 256, size=qb).astype(np.uint8)
+    C = run(fmt, M, K, N, A, q, p)
+    want = A.astype(np.float64).reshape(M, nblk, K // nblk).sum(2) @ p[:, :, 0].T.astype(np.float64)
+    compare(C, want, "constant blocks")
+
+
+def test_w4a8_golden_rows_and_identity():
+    """The hand-worked activation rows (ties, zero row, subnormals, the
+    near-tie that separates division from reciprocal-multiply) through the
+    GPU's quantiser, with identity weights so that D = qa."""
+    g = json.load(open(os.path.join(GOLDEN, "w4a8_actquant_rows.json")))
+    A = np.array([r["a"] for r in g["rows"]], dtype=np.float16)
+    M, K = A.shape
+    N = K
+    q = _identity("int4b64", K)
+    p = np.zeros((N, 1, 2), np.float32)
+    p[:, 0, 1] = 1.0
+    wp, sp = Q.qgemm_pack_weights(K, N, "w4a8", q, p)
+    nbytes = Q.qgemm_workspace_size(M, K, N, "w4a8")
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    qa = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    sa = torch.empty(M, dtype=torch.float32, device="cuda")
+    S = torch.empty(M, dtype=torch.int32, device="cuda")
+    D = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    Q.qgemm_w4a8_debug(M, K, N, dev(A), dev(wp), dev(sp), C, qa, sa, S, D, ws, nbytes)
+    torch.cuda.synchronize()
+    for i, r in enumerate(g["rows"]):
+        assert qa[i].cpu().tolist() == r["qa"], i
+        assert int(sa[i].cpu().numpy().view(np.uint32)) == int(r["sa_bits"], 16), i
+        assert int(S[i]) == r["S"], i
+    assert np.array_equal(D.cpu().numpy(), qa.cpu().numpy().astype(np.int32))
+    assert np.array_equal(C.cpu().numpy(), sa.cpu().numpy()[:, None] * qa.cpu().numpy())
+
+
+def test_w4a8_debug_bit_exact_mid_size():
+    M, K, N = 200, 3072, 300
+    A, W, _ = _case("w4a8", M, K, N, seed=77)
+    A[3] = 0                                   # a zero row
+    q, p, qo, po = _quantized_pair("w4a8", W)
+    wp, sp = Q.qgemm_pack_weights(K, N, "w4a8", q, p)
+    nbytes = Q.qgemm_workspace_size(M, K, N, "w4a8")
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    qa = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    sa = torch.empty(M, dtype=torch.float32, device="cuda")
+    S = torch.empty(M, dtype=torch.int32, device="cuda")
+    D = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    Q.qgemm_w4a8_debug(M, K, N, dev(A), dev(wp), dev(sp), C, qa, sa, S, D, ws, nbytes)
+    torch.cuda.synchronize()
+    Cr, qa_o, sa_o, S_o, D_o = O.w4a8_gemm(A, qo, po)
+    assert np.array_equal(qa.cpu().numpy(), qa_o)
+    assert np.array_equal(sa.cpu().numpy(), sa_o)
+    assert np.array_equal(S.cpu().numpy(), S_o)
+    assert np.array_equal(D.cpu().numpy().astype(np.int64), D_o)
+    compare(C.cpu().numpy(), Cr, "w4a8 mid")
+    assert np.all(C.cpu().numpy()[3] == 0)
+
+
+# ---------------------------------------------------------------------------
+# Runtime behaviour.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("fmt", ["int4b64", "int8b0", "w4a8", "f32"])
+def test_deterministic_and_stream(fmt):
+    """Repeated runs are bit-identical (no atomics), also on a side stream
+    and through the workspace entry point."""
+    M, K, N = (130, 512, 200)
+    A, W, _ = _case(fmt, M, K, N, seed=3)
+    if fmt == "f32":
+        wc, p = W, None
+    else:
+        wc, p = Q.qgemm_quantize_weights(W, fmt)
+    C1 = run(fmt, M, K, N, A, wc, p)
+    C2 = run(fmt, M, K, N, A, wc, p)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        C3 = run(fmt, M, K, N, A, wc, p, stream=s)
+    C4 = run(fmt, M, K, N, A, wc, p, ws=True)
+    assert np.array_equal(C1, C2) and np.array_equal(C1, C3) and np.array_equal(C1, C4)
+
+
+def test_empty_product_touches_nothing():
+    C = torch.full((4, 3), 7.0, device="cuda")
+    Q.qgemm_run(0, 64, 3, "int4b64", None, None, None, C)
+    Q.qgemm_run(4, 64, 0, "int4b64", None, None, None, C)
+    torch.cuda.synchronize()
+    assert torch.all(C == 7.0)
+
+
+def test_errors_leave_output_untouched():
+    C = torch.full((2, 8), 7.0, device="cuda")
+    A = torch.zeros((2, 64), dtype=torch.float16, device="cuda")
+    B = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    with pytest.raises(Q.QGemmError) as e:
+        Q.qgemm_run(2, 64, 8, "int4b64", A, B, None, C)     # missing scales
+    assert e.value.status == 1
+    with pytest.raises(Q.QGemmError) as e:
+        Q.qgemm_run(2, 60, 8, "int4b64", A, B, B, C)        # K % 64 != 0
+    assert e.value.status == 2
+    torch.cuda.synchronize()
+    assert torch.all(C == 7.0)

@@ -1,0 +1,205 @@
+// api.hip -- qgemm_run / qgemm_run_ws / qgemm_w4a8_debug: argument checks,
+// kernel choice and launches on the caller's stream.
+//
+// Kernel choice follows the MNN GemmSpeed benchmark page, section "Default
+// test sizes and the meaning of M": M = 8 is the narrow, near-decode GEMM
+// (bounded by the GEMV bandwidth floor, section "Sample data"), M = 512 a
+// dense prefill GEMM. Small M therefore streams the weights once through a
+// GEMV kernel; larger M goes to the MFMA tile kernels.
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+
+#include "qgemm_internal.h"
+
+namespace qg {
+
+static std::atomic<int> g_gemv_max_m{-1};
+
+static int gemv_max_m() {
+    int v = g_gemv_max_m.load(std::memory_order_relaxed);
+    if (v >= 0) return v;
+    int init = kGemvMaxM;
+    if (const char *e = std::getenv("QGEMM_GEMV_MAX_M")) {
+        char *end = nullptr;
+        long x = std::strtol(e, &end, 10);
+        if (end != e && x >= 0 && x <= kGemvMaxM) init = (int)x;
+    }
+    int expected = -1;
+    g_gemv_max_m.compare_exchange_strong(expected, init);
+    return g_gemv_max_m.load(std::memory_order_relaxed);
+}
+
+// 0 unknown, 1 usable gfx950, 2 not usable; indexed by HIP device ordinal.
+static std::atomic<int> g_dev_state[64];
+
+static qgemm_status check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return QGEMM_ERR_DEVICE;
+    }
+    if (dev >= 64) return QGEMM_ERR_DEVICE;
+    int st = g_dev_state[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        st = 2;
+        if (hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+            std::strncmp(prop.gcnArchName, "gfx950", 6) == 0)
+            st = 1;
+        (void)hipGetLastError();
+        g_dev_state[dev].store(st, std::memory_order_release);
+    }
+    return st == 1 ? QGEMM_OK : QGEMM_ERR_DEVICE;
+}
+
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks shared by every run entry point; *empty is set for M == 0 or N == 0.
+static qgemm_status check_run(int M, int K, int N, qgemm_format f, const void *A,
+                              const void *Bq, const void *scales, const float *C,
+                              Geometry *g, bool *empty) {
+    qgemm_status st = geometry(K, N, f, g);
+    if (st != QGEMM_OK) return st;
+    if (M < 0 || M > (1 << 24)) return QGEMM_ERR_SHAPE;
+    *empty = (M == 0 || N == 0);
+    if (*empty) return QGEMM_OK;
+    if (!C) return QGEMM_ERR_NULL;
+    if (K > 0 && (!A || !Bq)) return QGEMM_ERR_NULL;
+    if (f == QGEMM_F32) {
+        if (scales) return QGEMM_ERR_FORMAT;
+    } else if (!scales) {
+        return QGEMM_ERR_NULL;
+    }
+    if (!aligned16(C) || (A && !aligned16(A)) || (Bq && !aligned16(Bq)) ||
+        (scales && !aligned16(scales)))
+        return QGEMM_ERR_ALIGN;
+    return QGEMM_OK;
+}
+
+static qgemm_status launched(hipError_t e) {
+    return e == hipSuccess ? QGEMM_OK : QGEMM_ERR_LAUNCH;
+}
+
+static qgemm_status run_w4a8(int M, int K, int N, const Geometry &g, const void *A,
+                             const void *Bq, const void *scales, float *C, void *ws,
+                             hipStream_t s, int32_t *D_debug) {
+    W4A8Workspace w = w4a8_workspace(M, g.Kp);
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    int8_t *qa = reinterpret_cast<int8_t *>(base + w.qa_off);
+    float *sa = reinterpret_cast<float *>(base + w.sa_off);
+    int32_t *S = reinterpret_cast<int32_t *>(base + w.S_off);
+    hipError_t e = launch_w4a8_actquant(M, K, g.Kp, A, qa, sa, S, s);
+    if (e != hipSuccess) return QGEMM_ERR_LAUNCH;
+    return launched(launch_w4a8_gemm(M, K, N, qa, sa, S, Bq, scales, C, D_debug, s));
+}
+
+static qgemm_status dispatch(int M, int K, int N, qgemm_format f, const Geometry &g,
+                             const void *A, const void *Bq, const void *scales, float *C,
+                             void *ws, hipStream_t s) {
+    (void)hipGetLastError();   // start from a clean per-thread error state
+    const bool gemv = M <= gemv_max_m() && K <= kGemvMaxK;
+    switch (f) {
+    case QGEMM_F32:
+        return launched(launch_gemm_f32(M, K, N, static_cast<const float *>(A),
+                                        static_cast<const float *>(Bq), C, s));
+    case QGEMM_INT4_B64:
+        return launched(gemv ? launch_gemv_int4b64(M, K, N, A, Bq, scales, C, s)
+                             : launch_gemm_int4b64(M, K, N, A, Bq, scales, C, s));
+    case QGEMM_INT8_B0:
+        return launched(gemv ? launch_gemv_int8b0(M, K, N, A, Bq, scales, C, s)
+                             : launch_gemm_int8b0(M, K, N, A, Bq, scales, C, s));
+    case QGEMM_W4A8:
+        return run_w4a8(M, K, N, g, A, Bq, scales, C, ws, s, nullptr);
+    }
+    return QGEMM_ERR_FORMAT;
+}
+
+}  // namespace qg
+
+using namespace qg;
+
+extern "C" {
+
+int qgemm_set_gemv_max_m(int max_m) {
+    int prev = gemv_max_m();
+    if (max_m >= 0 && max_m <= kGemvMaxM) g_gemv_max_m.store(max_m);
+    return prev;
+}
+
+qgemm_status qgemm_run_ws(int M, int K, int N, qgemm_format f, const void *A,
+                          const void *Bq, const void *scales, float *C, void *workspace,
+                          size_t ws_bytes, void *stream) {
+    Geometry g;
+    bool empty = false;
+    qgemm_status st = check_run(M, K, N, f, A, Bq, scales, C, &g, &empty);
+    if (st != QGEMM_OK || empty) return st;
+    if (f == QGEMM_W4A8) {
+        if (!workspace) return QGEMM_ERR_NULL;
+        if (!aligned16(workspace)) return QGEMM_ERR_ALIGN;
+        if (ws_bytes < w4a8_workspace(M, g.Kp).bytes) return QGEMM_ERR_SIZE;
+    }
+    st = check_device();
+    if (st != QGEMM_OK) return st;
+    return dispatch(M, K, N, f, g, A, Bq, scales, C, workspace,
+                    static_cast<hipStream_t>(stream));
+}
+
+qgemm_status qgemm_run(int M, int K, int N, qgemm_format f, const void *A, const void *Bq,
+                       const void *scales, float *C, void *stream) {
+    Geometry g;
+    bool empty = false;
+    qgemm_status st = check_run(M, K, N, f, A, Bq, scales, C, &g, &empty);
+    if (st != QGEMM_OK || empty) return st;
+    st = check_device();
+    if (st != QGEMM_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (f != QGEMM_W4A8)
+        return dispatch(M, K, N, f, g, A, Bq, scales, C, nullptr, s);
+    // W4A8 scratch, allocated and released in stream order.
+    const size_t bytes = w4a8_workspace(M, g.Kp).bytes;
+    void *ws = nullptr;
+    if (hipMallocAsync(&ws, bytes, s) != hipSuccess || !ws) {
+        (void)hipGetLastError();
+        return QGEMM_ERR_NOMEM;
+    }
+    st = dispatch(M, K, N, f, g, A, Bq, scales, C, ws, s);
+    if (hipFreeAsync(ws, s) != hipSuccess) {
+        (void)hipGetLastError();
+        if (st == QGEMM_OK) st = QGEMM_ERR_LAUNCH;
+    }
+    return st;
+}
+
+qgemm_status qgemm_w4a8_debug(int M, int K, int N, const void *A, const void *Bq,
+                              const void *scales, float *C, int8_t *qa, float *sa,
+                              int32_t *S, int32_t *D, void *workspace, size_t ws_bytes,
+                              void *stream) {
+    Geometry g;
+    bool empty = false;
+    qgemm_status st = check_run(M, K, N, QGEMM_W4A8, A, Bq, scales, C, &g, &empty);
+    if (st != QGEMM_OK || empty) return st;
+    if (!qa || !sa || !S || !D || !workspace) return QGEMM_ERR_NULL;
+    if (!aligned16(workspace) || !aligned16(D)) return QGEMM_ERR_ALIGN;
+    W4A8Workspace w = w4a8_workspace(M, g.Kp);
+    if (ws_bytes < w.bytes) return QGEMM_ERR_SIZE;
+    st = check_device();
+    if (st != QGEMM_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    st = run_w4a8(M, K, N, g, A, Bq, scales, C, workspace, s, D);
+    if (st != QGEMM_OK) return st;
+    const uint8_t *base = static_cast<const uint8_t *>(workspace);
+    if (hipMemcpy2DAsync(qa, (size_t)K, base + w.qa_off, (size_t)g.Kp, (size_t)K, (size_t)M,
+                         hipMemcpyDeviceToDevice, s) != hipSuccess ||
+        hipMemcpyAsync(sa, base + w.sa_off, (size_t)M * sizeof(float),
+                       hipMemcpyDeviceToDevice, s) != hipSuccess ||
+        hipMemcpyAsync(S, base + w.S_off, (size_t)M * sizeof(int32_t),
+                       hipMemcpyDeviceToDevice, s) != hipSuccess) {
+        (void)hipGetLastError();
+        return QGEMM_ERR_LAUNCH;
+    }
+    return QGEMM_OK;
+}
+
+}  // extern "C"

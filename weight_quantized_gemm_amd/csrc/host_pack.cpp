@@ -1,0 +1,345 @@
+// host_pack.cpp -- host side of libqgemm that never touches the GPU:
+// geometry of the formats, the quantiser, the packer and its inverse.
+//
+// Formats follow the MNN GemmSpeed benchmark page, section "Why Conv1x1 is
+// used to measure GEMM" (Int8-Block0: 8-bit codes, blockSize = K; Int4-Block64:
+// 4-bit codes, blockSize 64, K % 64 == 0 or the shape is skipped; pairs laid
+// out as oc x blockNum groups of [offset, scale]) and section "Test cases and
+// registration" (W4A8: per-channel 4-bit weights).
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "qgemm_internal.h"
+
+namespace qg {
+
+static bool valid_format(int f) {
+    return f == QGEMM_F32 || f == QGEMM_INT4_B64 || f == QGEMM_INT8_B0 || f == QGEMM_W4A8;
+}
+
+// Shapes are capped so that every element count and byte offset the kernels
+// form stays far inside 64-bit and every per-dimension index inside int32.
+constexpr int kMaxDim = 1 << 24;
+// W4A8 keeps D = sum_k qa * q in int32: |D| <= K * 127 * 15 must stay < 2^31.
+constexpr long long kW4A8MaxK = ((1LL << 31) - 1) / (127 * 15);
+
+qgemm_status geometry(int K, int N, qgemm_format f, Geometry *g) {
+    if (!valid_format(f)) return QGEMM_ERR_FORMAT;
+    if (K < 0 || N < 0 || K > kMaxDim || N > kMaxDim) return QGEMM_ERR_SHAPE;
+    Geometry r;
+    r.K = K;
+    r.N = N;
+    switch (f) {
+    case QGEMM_F32:
+        r.Kp = K; r.Np = N; r.nblk = 0;
+        r.w_bytes = round_up((size_t)K * N * sizeof(float), kPackAlign);
+        r.s_bytes = 0;
+        break;
+    case QGEMM_INT4_B64:
+        if (K == 0 || K % 64 != 0) return QGEMM_ERR_SHAPE;
+        r.Kp = K; r.Np = (int)round_up(N, 4); r.nblk = K / 64;
+        r.w_bytes = round_up((size_t)(r.Np / 4) * r.nblk * 128, kPackAlign);
+        r.s_bytes = round_up((size_t)(r.Np / 4) * r.nblk * 32, kPackAlign);
+        break;
+    case QGEMM_INT8_B0:
+        if (K == 0) return QGEMM_ERR_SHAPE;
+        r.Kp = (int)round_up(K, 64); r.Np = (int)round_up(N, 4); r.nblk = 1;
+        r.w_bytes = round_up((size_t)r.Np * r.Kp, kPackAlign);
+        r.s_bytes = round_up((size_t)r.Np * 2 * sizeof(float), kPackAlign);
+        break;
+    case QGEMM_W4A8:
+        if (K == 0 || K % 2 != 0 || K > kW4A8MaxK) return QGEMM_ERR_SHAPE;
+        r.Kp = (int)round_up(K, 64); r.Np = (int)round_up(N, 32); r.nblk = 1;
+        r.w_bytes = round_up((size_t)r.Np * (r.Kp / 2), kPackAlign);
+        r.s_bytes = round_up((size_t)r.Np * 2 * sizeof(float), kPackAlign);
+        break;
+    }
+    *g = r;
+    return QGEMM_OK;
+}
+
+W4A8Workspace w4a8_workspace(int M, int Kp) {
+    W4A8Workspace w;
+    w.qa_off = 0;
+    w.sa_off = round_up((size_t)M * Kp, kPackAlign);
+    w.S_off = w.sa_off + round_up((size_t)M * sizeof(float), kPackAlign);
+    w.bytes = w.S_off + round_up((size_t)M * sizeof(int32_t), kPackAlign);
+    return w;
+}
+
+static size_t canonical_q_bytes(const Geometry &g, qgemm_format f) {
+    switch (f) {
+    case QGEMM_F32: return (size_t)g.K * g.N * sizeof(float);
+    case QGEMM_INT8_B0: return (size_t)g.N * g.K;
+    default: return (size_t)g.N * (g.K / 2);
+    }
+}
+
+static size_t canonical_pair_floats(const Geometry &g, qgemm_format f) {
+    return f == QGEMM_F32 ? 0 : (size_t)g.N * g.nblk * 2;
+}
+
+// Canonical code of channel n at k (INT4 / W4A8: low nibble first).
+static inline uint8_t nib(const uint8_t *row, int k) {
+    uint8_t b = row[k >> 1];
+    return (k & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 15);
+}
+
+}  // namespace qg
+
+using namespace qg;
+
+extern "C" {
+
+const char *qgemm_status_string(int s) {
+    switch (s) {
+    case QGEMM_OK: return "QGEMM_OK";
+    case QGEMM_ERR_NULL: return "QGEMM_ERR_NULL: a required pointer is NULL";
+    case QGEMM_ERR_SHAPE: return "QGEMM_ERR_SHAPE: invalid shape for this format";
+    case QGEMM_ERR_FORMAT: return "QGEMM_ERR_FORMAT: unknown or unsupported format";
+    case QGEMM_ERR_ALIGN: return "QGEMM_ERR_ALIGN: device pointer not 16-byte aligned";
+    case QGEMM_ERR_NOMEM: return "QGEMM_ERR_NOMEM: scratch allocation failed";
+    case QGEMM_ERR_DEVICE: return "QGEMM_ERR_DEVICE: no usable gfx950 HIP device";
+    case QGEMM_ERR_LAUNCH: return "QGEMM_ERR_LAUNCH: kernel launch failed";
+    case QGEMM_ERR_SIZE: return "QGEMM_ERR_SIZE: buffer smaller than required";
+    case QGEMM_ERR_VALUE: return "QGEMM_ERR_VALUE: non-finite weight";
+    default: return "QGEMM_ERR_UNKNOWN";
+    }
+}
+
+int qgemm_abi_version(void) { return QGEMM_ABI_VERSION; }
+
+qgemm_status qgemm_canonical_size(int K, int N, qgemm_format f, size_t *q_bytes,
+                                  size_t *pair_floats) {
+    Geometry g;
+    qgemm_status st = geometry(K, N, f, &g);
+    if (st != QGEMM_OK) return st;
+    if (!q_bytes || !pair_floats) return QGEMM_ERR_NULL;
+    *q_bytes = canonical_q_bytes(g, f);
+    *pair_floats = canonical_pair_floats(g, f);
+    return QGEMM_OK;
+}
+
+qgemm_status qgemm_packed_size(int K, int N, qgemm_format f, size_t *w_bytes,
+                               size_t *s_bytes) {
+    Geometry g;
+    qgemm_status st = geometry(K, N, f, &g);
+    if (st != QGEMM_OK) return st;
+    if (!w_bytes || !s_bytes) return QGEMM_ERR_NULL;
+    *w_bytes = g.w_bytes;
+    *s_bytes = g.s_bytes;
+    return QGEMM_OK;
+}
+
+qgemm_status qgemm_workspace_size(int M, int K, int N, qgemm_format f, size_t *bytes) {
+    Geometry g;
+    qgemm_status st = geometry(K, N, f, &g);
+    if (st != QGEMM_OK) return st;
+    if (M < 0 || M > (1 << 24)) return QGEMM_ERR_SHAPE;
+    if (!bytes) return QGEMM_ERR_NULL;
+    *bytes = (f == QGEMM_W4A8 && M > 0) ? w4a8_workspace(M, g.Kp).bytes : 0;
+    return QGEMM_OK;
+}
+
+qgemm_status qgemm_quantize_weights(int K, int N, qgemm_format f, const float *W,
+                                    void *q_out, size_t q_bytes, float *pairs,
+                                    size_t pair_floats) {
+    if (f == QGEMM_F32) return QGEMM_ERR_FORMAT;
+    Geometry g;
+    qgemm_status st = geometry(K, N, f, &g);
+    if (st != QGEMM_OK) return st;
+    if (N == 0) return QGEMM_OK;
+    if (!W || !q_out || !pairs) return QGEMM_ERR_NULL;
+    if (q_bytes < canonical_q_bytes(g, f) || pair_floats < canonical_pair_floats(g, f))
+        return QGEMM_ERR_SIZE;
+    const size_t total = (size_t)N * K;
+    for (size_t i = 0; i < total; ++i)
+        if (!std::isfinite(W[i])) return QGEMM_ERR_VALUE;
+
+    const int bits = (f == QGEMM_INT8_B0) ? 8 : 4;
+    const int block = (f == QGEMM_INT4_B64) ? 64 : K;
+    const int nblk = K / block;
+    const int qmax = (1 << bits) - 1;
+    uint8_t *q = static_cast<uint8_t *>(q_out);
+    if (bits == 4) std::memset(q, 0, (size_t)N * (K / 2));
+
+    for (int n = 0; n < N; ++n) {
+        const float *wrow = W + (size_t)n * K;
+        for (int b = 0; b < nblk; ++b) {
+            const float *wb = wrow + (size_t)b * block;
+            double lo = wb[0], hi = wb[0];
+            for (int i = 1; i < block; ++i) {
+                double v = wb[i];
+                lo = v < lo ? v : lo;
+                hi = v > hi ? v : hi;
+            }
+            const float offset = (float)lo;
+            const float scale = (float)((hi - lo) / (double)qmax);
+            pairs[((size_t)n * nblk + b) * 2 + 0] = offset;
+            pairs[((size_t)n * nblk + b) * 2 + 1] = scale;
+            const double off_d = offset, scale_d = scale;
+            for (int i = 0; i < block; ++i) {
+                int code = 0;
+                if (scale != 0.0f) {
+                    double r = std::nearbyint(((double)wb[i] - off_d) / scale_d);
+                    r = r < 0.0 ? 0.0 : (r > qmax ? (double)qmax : r);
+                    code = (int)r;
+                }
+                const int k = b * block + i;
+                if (bits == 8)
+                    q[(size_t)n * K + k] = (uint8_t)code;
+                else
+                    q[(size_t)n * (K / 2) + (k >> 1)] |= (uint8_t)(code << ((k & 1) * 4));
+            }
+        }
+    }
+    return QGEMM_OK;
+}
+
+qgemm_status qgemm_pack_weights(int K, int N, qgemm_format f, const void *w_canonical,
+                                const float *pairs_canonical, void *w_packed,
+                                size_t w_bytes, void *s_packed, size_t s_bytes) {
+    Geometry g;
+    qgemm_status st = geometry(K, N, f, &g);
+    if (st != QGEMM_OK) return st;
+    if (!w_packed || (g.s_bytes && !s_packed)) return QGEMM_ERR_NULL;
+    if (w_bytes < g.w_bytes || s_bytes < g.s_bytes) return QGEMM_ERR_SIZE;
+    if ((size_t)N * K > 0 && !w_canonical) return QGEMM_ERR_NULL;
+    if (f != QGEMM_F32 && N > 0 && !pairs_canonical) return QGEMM_ERR_NULL;
+
+    uint8_t *wp = static_cast<uint8_t *>(w_packed);
+    uint8_t *sp = static_cast<uint8_t *>(s_packed);
+    float *spf = reinterpret_cast<float *>(s_packed);
+    std::memset(wp, 0, g.w_bytes);
+    if (g.s_bytes) std::memset(sp, 0, g.s_bytes);
+    const uint8_t *wc = static_cast<const uint8_t *>(w_canonical);
+
+    switch (f) {
+    case QGEMM_F32:
+        if ((size_t)K * N) std::memcpy(wp, wc, (size_t)K * N * sizeof(float));
+        break;
+    case QGEMM_INT4_B64: {
+        const int nblk = g.nblk;
+        const size_t row = (size_t)K / 2;
+        for (int n = 0; n < N; ++n) {
+            const int grp = n >> 2, c = n & 3;
+            for (int b = 0; b < nblk; ++b) {
+                for (int half = 0; half < 2; ++half) {
+                    const int j = 2 * c + half;
+                    uint8_t *dst = wp + (((size_t)grp * 8 + j) * nblk + b) * 16;
+                    std::memcpy(dst, wc + (size_t)n * row + (size_t)b * 32 + half * 16, 16);
+                }
+                float *rec = spf + (((size_t)grp * 2 + (c >> 1)) * nblk + b) * 4 + (c & 1) * 2;
+                rec[0] = pairs_canonical[((size_t)n * nblk + b) * 2 + 0];
+                rec[1] = pairs_canonical[((size_t)n * nblk + b) * 2 + 1];
+            }
+        }
+        break;
+    }
+    case QGEMM_INT8_B0:
+        for (int n = 0; n < N; ++n) {
+            std::memcpy(wp + (size_t)n * g.Kp, wc + (size_t)n * K, (size_t)K);
+            spf[(size_t)n * 2 + 0] = pairs_canonical[(size_t)n * 2 + 0];
+            spf[(size_t)n * 2 + 1] = pairs_canonical[(size_t)n * 2 + 1];
+        }
+        break;
+    case QGEMM_W4A8: {
+        const int nkc = g.Kp / 64;
+        const size_t row = (size_t)K / 2;
+        for (int n = 0; n < N; ++n) {
+            const uint8_t *src = wc + (size_t)n * row;
+            const int grp = n >> 5, c = n & 31;
+            for (int kc = 0; kc < nkc; ++kc) {
+                uint8_t *rec = wp + (((size_t)grp * nkc + kc) * 32 + c) * 32;
+                for (int w = 0; w < 8; ++w) {
+                    const int k0 = kc * 64 + w * 8;
+                    for (int i = 0; i < 4; ++i) {
+                        const uint8_t lo = (k0 + i < K) ? nib(src, k0 + i) : 0;
+                        const uint8_t hi = (k0 + 4 + i < K) ? nib(src, k0 + 4 + i) : 0;
+                        rec[w * 4 + i] = (uint8_t)(lo | (hi << 4));
+                    }
+                }
+            }
+            spf[(size_t)n * 2 + 0] = pairs_canonical[(size_t)n * 2 + 0];
+            spf[(size_t)n * 2 + 1] = pairs_canonical[(size_t)n * 2 + 1];
+        }
+        break;
+    }
+    }
+    return QGEMM_OK;
+}
+
+qgemm_status qgemm_unpack_weights(int K, int N, qgemm_format f, const void *w_packed,
+                                  size_t w_bytes, const void *s_packed, size_t s_bytes,
+                                  void *w_canonical, float *pairs_canonical) {
+    Geometry g;
+    qgemm_status st = geometry(K, N, f, &g);
+    if (st != QGEMM_OK) return st;
+    if (!w_packed || (g.s_bytes && !s_packed)) return QGEMM_ERR_NULL;
+    if (w_bytes < g.w_bytes || s_bytes < g.s_bytes) return QGEMM_ERR_SIZE;
+    if ((size_t)N * K > 0 && !w_canonical) return QGEMM_ERR_NULL;
+    if (f != QGEMM_F32 && N > 0 && !pairs_canonical) return QGEMM_ERR_NULL;
+
+    const uint8_t *wp = static_cast<const uint8_t *>(w_packed);
+    const float *spf = reinterpret_cast<const float *>(s_packed);
+    uint8_t *wc = static_cast<uint8_t *>(w_canonical);
+
+    switch (f) {
+    case QGEMM_F32:
+        if ((size_t)K * N) std::memcpy(wc, wp, (size_t)K * N * sizeof(float));
+        break;
+    case QGEMM_INT4_B64: {
+        const int nblk = g.nblk;
+        const size_t row = (size_t)K / 2;
+        for (int n = 0; n < N; ++n) {
+            const int grp = n >> 2, c = n & 3;
+            for (int b = 0; b < nblk; ++b) {
+                for (int half = 0; half < 2; ++half) {
+                    const int j = 2 * c + half;
+                    std::memcpy(wc + (size_t)n * row + (size_t)b * 32 + half * 16,
+                                wp + (((size_t)grp * 8 + j) * nblk + b) * 16, 16);
+                }
+                const float *rec = spf + (((size_t)grp * 2 + (c >> 1)) * nblk + b) * 4 + (c & 1) * 2;
+                pairs_canonical[((size_t)n * nblk + b) * 2 + 0] = rec[0];
+                pairs_canonical[((size_t)n * nblk + b) * 2 + 1] = rec[1];
+            }
+        }
+        break;
+    }
+    case QGEMM_INT8_B0:
+        for (int n = 0; n < N; ++n) {
+            std::memcpy(wc + (size_t)n * K, wp + (size_t)n * g.Kp, (size_t)K);
+            pairs_canonical[(size_t)n * 2 + 0] = spf[(size_t)n * 2 + 0];
+            pairs_canonical[(size_t)n * 2 + 1] = spf[(size_t)n * 2 + 1];
+        }
+        break;
+    case QGEMM_W4A8: {
+        const int nkc = g.Kp / 64;
+        const size_t row = (size_t)K / 2;
+        for (int n = 0; n < N; ++n) {
+            uint8_t *dst = wc + (size_t)n * row;
+            std::memset(dst, 0, row);
+            const int grp = n >> 5, c = n & 31;
+            for (int kc = 0; kc < nkc; ++kc) {
+                const uint8_t *rec = wp + (((size_t)grp * nkc + kc) * 32 + c) * 32;
+                for (int w = 0; w < 8; ++w) {
+                    const int k0 = kc * 64 + w * 8;
+                    for (int i = 0; i < 4; ++i) {
+                        const uint8_t byte = rec[w * 4 + i];
+                        const int ka = k0 + i, kb = k0 + 4 + i;
+                        if (ka < K) dst[ka >> 1] |= (uint8_t)((byte & 15) << ((ka & 1) * 4));
+                        if (kb < K) dst[kb >> 1] |= (uint8_t)((byte >> 4) << ((kb & 1) * 4));
+                    }
+                }
+            }
+            pairs_canonical[(size_t)n * 2 + 0] = spf[(size_t)n * 2 + 0];
+            pairs_canonical[(size_t)n * 2 + 1] = spf[(size_t)n * 2 + 1];
+        }
+        break;
+    }
+    }
+    return QGEMM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// qgemm_internal.h -- layouts and kernel launchers shared by the library's
+// own translation units (never installed, never used by the oracle).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/qgemm.h"
+
+namespace qg {
+
+inline size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
+inline int div_up(int x, int m) { return (x + m - 1) / m; }
+
+// Every packed buffer is padded to a multiple of this many bytes.
+constexpr size_t kPackAlign = 256;
+
+// ---------------------------------------------------------------------------
+// Packed layouts (host packer <-> kernels).
+//
+// INT4_B64, nblk = K / 64, G = ceil(N / 4) channel groups of 4:
+//   weights: 16-byte chunks, chunk (g, j, b) at ((g * 8 + j) * nblk + b) * 16
+//            holding canonical bytes [32 b + 16 (j & 1), +16) of channel
+//            4 g + (j >> 1). A wave that gives lane b block b reads every
+//            chunk j of a group as 64 consecutive 16-byte pieces.
+//   pairs:   16-byte records, record (g, h, b) at ((g * 2 + h) * nblk + b) * 16
+//            = {offset, scale} of channel 4g + 2h, then of channel 4g + 2h + 1,
+//            for block b.
+// INT8_B0, Kp = roundup(K, 64), Np = roundup(N, 4):
+//   weights: [Np][Kp] bytes (canonical rows, zero padded);
+//   pairs:   [Np][2] floats.
+// W4A8, Kp = roundup(K, 64), Np = roundup(N, 32):
+//   weights: 32-byte records, record (g, kc, c) at ((g * (Kp/64) + kc) * 32 + c) * 32
+//            for channel 32 g + c and k in [64 kc, 64 kc + 64); word w of the
+//            record (k0 = 64 kc + 8 w) has byte i = q[k0 + i] | q[k0 + 4 + i] << 4,
+//            so masking a word with 0x0F0F0F0F / shifting by 4 yields codes of
+//            k0..k0+3 / k0+4..k0+7 in natural order as int8.
+//   pairs:   [Np][2] floats.
+// F32: weights = B float [K][N] unchanged; no pairs.
+// ---------------------------------------------------------------------------
+struct Geometry {
+    int K = 0, N = 0;
+    int Kp = 0;        // K padded to the kernels' step (64) where relevant
+    int Np = 0;        // N padded to the channel group
+    int nblk = 0;      // pairs per channel
+    size_t w_bytes = 0, s_bytes = 0;
+};
+
+qgemm_status geometry(int K, int N, qgemm_format f, Geometry *g);
+
+constexpr int kGemvMaxM = 8;          // largest M the GEMV kernels take
+constexpr int kGemvMaxK = 16384;      // A rows staged in LDS: MR * K * 2 bytes
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (defined in the .hip files). They assume validated
+// arguments and return hipGetLastError() of their launches.
+// ---------------------------------------------------------------------------
+hipError_t launch_gemv_int4b64(int M, int K, int N, const void *A, const void *Wp,
+                               const void *Sp, float *C, hipStream_t s);
+hipError_t launch_gemv_int8b0(int M, int K, int N, const void *A, const void *Wp,
+                              const void *Sp, float *C, hipStream_t s);
+hipError_t launch_gemm_int4b64(int M, int K, int N, const void *A, const void *Wp,
+                               const void *Sp, float *C, hipStream_t s);
+hipError_t launch_gemm_int8b0(int M, int K, int N, const void *A, const void *Wp,
+                              const void *Sp, float *C, hipStream_t s);
+hipError_t launch_gemm_f32(int M, int K, int N, const float *A, const float *B,
+                           float *C, hipStream_t s);
+// W4A8: qa [M][Kp] int8, sa [M] float, S [M] int32 live in `ws`.
+hipError_t launch_w4a8_actquant(int M, int K, int Kp, const void *A, int8_t *qa,
+                                float *sa, int32_t *S, hipStream_t s);
+hipError_t launch_w4a8_gemm(int M, int K, int N, const int8_t *qa, const float *sa,
+                            const int32_t *S, const void *Wp, const void *Sp,
+                            float *C, int32_t *D_debug, hipStream_t s);
+
+struct W4A8Workspace {
+    size_t qa_off, sa_off, S_off, bytes;
+};
+W4A8Workspace w4a8_workspace(int M, int Kp);
+
+}  // namespace qg

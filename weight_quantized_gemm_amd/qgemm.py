@@ -1,0 +1,239 @@
+"""Thin Python binding of libqgemm's C ABI (include/qgemm.h).
+
+Same names as the C entry points; this module only marshals arguments
+(numpy arrays for the host-side quantiser and packer, torch tensors for
+device buffers, torch's current HIP stream). Every step of the GEMM runs in
+the library's HIP kernels. There is no fallback: if libqgemm.so is missing or
+a call fails, an exception is raised.
+
+torch is imported before the library is loaded so that the process uses one
+HIP runtime (torch's), which the library then binds to by its soname.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+import torch  # noqa: F401  (must be loaded before libqgemm.so; see module doc)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgemm.so")
+
+# Format ids (the MNN GemmSpeed page's mode numbers) and names.
+QGEMM_F32, QGEMM_INT4_B64, QGEMM_INT8_B0, QGEMM_W4A8 = 0, 1, 2, 3
+FORMATS = {"f32": QGEMM_F32, "int4b64": QGEMM_INT4_B64, "int8b0": QGEMM_INT8_B0,
+           "w4a8": QGEMM_W4A8}
+
+STATUS = {0: "QGEMM_OK", 1: "QGEMM_ERR_NULL", 2: "QGEMM_ERR_SHAPE", 3: "QGEMM_ERR_FORMAT",
+          4: "QGEMM_ERR_ALIGN", 5: "QGEMM_ERR_NOMEM", 6: "QGEMM_ERR_DEVICE",
+          7: "QGEMM_ERR_LAUNCH", 8: "QGEMM_ERR_SIZE", 9: "QGEMM_ERR_VALUE"}
+
+# Every symbol include/qgemm.h declares.
+EXPORTS = ["qgemm_status_string", "qgemm_abi_version", "qgemm_canonical_size",
+           "qgemm_quantize_weights", "qgemm_packed_size", "qgemm_pack_weights",
+           "qgemm_unpack_weights", "qgemm_workspace_size", "qgemm_run", "qgemm_run_ws",
+           "qgemm_w4a8_debug", "qgemm_set_gemv_max_m"]
+
+
+class QGemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads libqgemm.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m weight_quantized_gemm_amd.build_lib` "
+            "(there is no fallback path)")
+    lib = ctypes.CDLL(path)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    ZP = ctypes.POINTER(ctypes.c_size_t)
+    sig = {
+        "qgemm_status_string": ([I], ctypes.c_char_p),
+        "qgemm_abi_version": ([], I),
+        "qgemm_canonical_size": ([I, I, I, ZP, ZP], I),
+        "qgemm_quantize_weights": ([I, I, I, P, P, Z, P, Z], I),
+        "qgemm_packed_size": ([I, I, I, ZP, ZP], I),
+        "qgemm_pack_weights": ([I, I, I, P, P, P, Z, P, Z], I),
+        "qgemm_unpack_weights": ([I, I, I, P, Z, P, Z, P, P], I),
+        "qgemm_workspace_size": ([I, I, I, I, ZP], I),
+        "qgemm_run": ([I, I, I, I, P, P, P, P, P], I),
+        "qgemm_run_ws": ([I, I, I, I, P, P, P, P, P, Z, P], I),
+        "qgemm_w4a8_debug": ([I, I, I, P, P, P, P, P, P, P, P, P, Z, P], I),
+        "qgemm_set_gemv_max_m": ([I], I),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _fmt(f) -> int:
+    return FORMATS[f] if isinstance(f, str) else int(f)
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        raise QGemmError(st, where)
+
+
+def _np_ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dev_ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
+    assert t.is_cuda and t.is_contiguous(), "device buffers must be contiguous GPU tensors"
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+# ---------------------------------------------------------------------------
+def qgemm_status_string(status: int) -> str:
+    return load().qgemm_status_string(status).decode()
+
+
+def qgemm_abi_version() -> int:
+    return load().qgemm_abi_version()
+
+
+def qgemm_canonical_size(K: int, N: int, fmt) -> tuple[int, int]:
+    q, p = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().qgemm_canonical_size(K, N, _fmt(fmt), ctypes.byref(q), ctypes.byref(p)),
+           "qgemm_canonical_size")
+    return q.value, p.value
+
+
+def qgemm_packed_size(K: int, N: int, fmt) -> tuple[int, int]:
+    w, s = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().qgemm_packed_size(K, N, _fmt(fmt), ctypes.byref(w), ctypes.byref(s)),
+           "qgemm_packed_size")
+    return w.value, s.value
+
+
+def qgemm_workspace_size(M: int, K: int, N: int, fmt) -> int:
+    b = ctypes.c_size_t()
+    _check(load().qgemm_workspace_size(M, K, N, _fmt(fmt), ctypes.byref(b)),
+           "qgemm_workspace_size")
+    return b.value
+
+
+def qgemm_quantize_weights(W: np.ndarray, fmt):
+    """Float W [N][K] -> (canonical codes uint8, pairs float32 [N][nblk][2])."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    qb, pf = qgemm_canonical_size(K, N, fmt)
+    q = np.empty(qb, dtype=np.uint8)
+    pairs = np.empty(pf, dtype=np.float32)
+    _check(load().qgemm_quantize_weights(K, N, _fmt(fmt), _np_ptr(W), _np_ptr(q), qb,
+                                         _np_ptr(pairs), pf), "qgemm_quantize_weights")
+    f = _fmt(fmt)
+    qshape = (N, K) if f == QGEMM_INT8_B0 else (N, K // 2)
+    nblk = K // 64 if f == QGEMM_INT4_B64 else 1
+    return q.reshape(qshape), pairs.reshape(N, nblk, 2)
+
+
+def qgemm_pack_weights(K: int, N: int, fmt, w_canonical: np.ndarray,
+                       pairs_canonical: np.ndarray | None):
+    """Canonical host arrays -> (packed weights uint8, packed pairs uint8), host."""
+    wb, sb = qgemm_packed_size(K, N, fmt)
+    wp = np.empty(wb, dtype=np.uint8)
+    sp = np.empty(max(sb, 1), dtype=np.uint8)
+    wc = np.ascontiguousarray(w_canonical)
+    pc = None if pairs_canonical is None else np.ascontiguousarray(pairs_canonical, dtype=np.float32)
+    _check(load().qgemm_pack_weights(K, N, _fmt(fmt), _np_ptr(wc), _np_ptr(pc), _np_ptr(wp), wb,
+                                     _np_ptr(sp), sb), "qgemm_pack_weights")
+    return wp, sp[:sb]
+
+
+def qgemm_unpack_weights(K: int, N: int, fmt, w_packed: np.ndarray, s_packed: np.ndarray):
+    f = _fmt(fmt)
+    qb, pf = qgemm_canonical_size(K, N, f)
+    q = np.empty(max(qb, 1), dtype=np.uint8)
+    pairs = np.empty(max(pf, 1), dtype=np.float32)
+    sp = s_packed if s_packed.size else np.zeros(1, np.uint8)
+    _check(load().qgemm_unpack_weights(K, N, f, _np_ptr(w_packed), w_packed.nbytes, _np_ptr(sp),
+                                       s_packed.nbytes, _np_ptr(q), _np_ptr(pairs)),
+           "qgemm_unpack_weights")
+    return q[:qb], pairs[:pf]
+
+
+def qgemm_run(M: int, K: int, N: int, fmt, A, Bq, scales, C, stream=None) -> None:
+    """C = A x B on the GPU (torch tensors or raw device addresses)."""
+    _check(load().qgemm_run(M, K, N, _fmt(fmt), _dev_ptr(A), _dev_ptr(Bq), _dev_ptr(scales),
+                            _dev_ptr(C), _stream(stream)), "qgemm_run")
+
+
+def qgemm_run_ws(M: int, K: int, N: int, fmt, A, Bq, scales, C, workspace, ws_bytes: int,
+                 stream=None) -> None:
+    _check(load().qgemm_run_ws(M, K, N, _fmt(fmt), _dev_ptr(A), _dev_ptr(Bq), _dev_ptr(scales),
+                               _dev_ptr(C), _dev_ptr(workspace), ws_bytes, _stream(stream)),
+           "qgemm_run_ws")
+
+
+def qgemm_w4a8_debug(M: int, K: int, N: int, A, Bq, scales, C, qa, sa, S, D, workspace,
+                     ws_bytes: int, stream=None) -> None:
+    _check(load().qgemm_w4a8_debug(M, K, N, _dev_ptr(A), _dev_ptr(Bq), _dev_ptr(scales),
+                                   _dev_ptr(C), _dev_ptr(qa), _dev_ptr(sa), _dev_ptr(S),
+                                   _dev_ptr(D), _dev_ptr(workspace), ws_bytes, _stream(stream)),
+           "qgemm_w4a8_debug")
+
+
+def qgemm_set_gemv_max_m(max_m: int) -> int:
+    return load().qgemm_set_gemv_max_m(max_m)
+
+
+# ---------------------------------------------------------------------------
+# Convenience: a packed weight resident on the GPU.
+# ---------------------------------------------------------------------------
+class PackedWeight:
+    """Quantise (or take) a weight, pack it and upload it to the GPU."""
+
+    def __init__(self, fmt, K: int, N: int, w_canonical: np.ndarray,
+                 pairs_canonical: np.ndarray | None, device="cuda"):
+        self.fmt = _fmt(fmt)
+        self.K, self.N = K, N
+        wp, sp = qgemm_pack_weights(K, N, self.fmt, w_canonical, pairs_canonical)
+        self.Bq = torch.from_numpy(wp).to(device)
+        self.scales = torch.from_numpy(sp).to(device) if sp.size else None
+
+    @classmethod
+    def from_float(cls, fmt, W: np.ndarray, device="cuda"):
+        """W [N][K] float -> quantised by the library's host quantiser."""
+        f = _fmt(fmt)
+        N, K = W.shape
+        if f == QGEMM_F32:
+            return cls(f, K, N, np.ascontiguousarray(W.T, dtype=np.float32), None, device)
+        q, pairs = qgemm_quantize_weights(W, f)
+        return cls(f, K, N, q, pairs, device)
+
+    def __call__(self, A: torch.Tensor, C: torch.Tensor | None = None, stream=None):
+        M = A.shape[0]
+        if C is None:
+            C = torch.empty((M, self.N), dtype=torch.float32, device=A.device)
+        qgemm_run(M, self.K, self.N, self.fmt, A, self.Bq, self.scales, C, stream)
+        return C
