@@ -83,6 +83,7 @@ def test_run_ws_validation(lib):
 
 def test_sizes():
     assert Q.qgemm_packed_size(4096, 11008, "int4b64") == (22544384, 5636096)
+    assert Q.qgemm_packed_size(4096, 100, "int4b64") == (4 * 64 * 1024, 4 * 64 * 256)
     assert Q.qgemm_packed_size(4096, 4096, "int8b0") == (16777216, 32768)
     assert Q.qgemm_packed_size(3072, 8192, "w4a8") == (12582912, 65536)
     assert Q.qgemm_packed_size(256, 256, "f32") == (262144, 0)
@@ -145,24 +146,26 @@ def test_pack_unpack_round_trip(fmt, shape):
 
 
 def test_int4_packed_layout_golden():
-    """Chunk (g, j, b) of the Int4-Block64 layout holds bytes [32b + 16(j&1), +16)
-    of channel 4g + j/2; pair record (g, h, b) holds channels 4g+2h, 4g+2h+1."""
-    N, K = 8, 128
+    """Record (t, b) of the Int4-Block64 layout is 1 KiB: piece 32 h + c holds
+    canonical bytes [32 b + 16 h, +16) of channel 32 t + c; pair record (t, b)
+    holds the 32 channels' {offset, scale} of block b."""
+    N, K = 40, 128
     nblk = K // 64
     wc = np.arange(N * K // 2, dtype=np.int64).astype(np.uint8).reshape(N, K // 2)
     pc = np.arange(N * nblk * 2, dtype=np.float32).reshape(N, nblk, 2)
     wp, sp = Q.qgemm_pack_weights(K, N, "int4b64", wc, pc)
-    chunks = wp.reshape(-1, 16)
-    recs = sp.view(np.float32).reshape(-1, 4)
+    assert wp.size == 2 * nblk * 1024 and sp.size == 2 * nblk * 256
+    pieces = wp.reshape(-1, 64, 16)
+    recs = sp.view(np.float32).reshape(-1, 32, 2)
     for n in range(N):
-        g, c = divmod(n, 4)
+        t, c = divmod(n, 32)
         for b in range(nblk):
             for half in range(2):
-                j = 2 * c + half
-                assert np.array_equal(chunks[(g * 8 + j) * nblk + b],
+                assert np.array_equal(pieces[t * nblk + b, 32 * half + c],
                                       wc[n, 32 * b + 16 * half: 32 * b + 16 * half + 16])
-            rec = recs[(g * 2 + c // 2) * nblk + b]
-            assert list(rec[(c % 2) * 2:(c % 2) * 2 + 2]) == list(pc[n, b])
+            assert list(recs[t * nblk + b, c]) == list(pc[n, b])
+    # channels 40..63 of the second tile are zero padding
+    assert not np.any(pieces[nblk:, :, :][:, [c for c in range(64) if (c % 32) >= 8]])
 
 
 def test_w4a8_packed_word_order_golden():

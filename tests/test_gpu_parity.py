@@ -307,3 +307,40 @@ def test_errors_leave_output_untouched():
     assert e.value.status == 2
     torch.cuda.synchronize()
     assert torch.all(C == 7.0)
+
+
+def test_graph_capture_replays_match_eager():
+    """The kernels record into a HIP graph (through torch's capture) and
+    every replay, with unrelated eager work in between, reproduces the eager
+    result bit for bit. W4A8 goes through qgemm_run_ws (qgemm_run allocates
+    its scratch and is not meant for capture)."""
+    calls = []
+    for fmt, M, K, N in [("int4b64", 1, 4096, 1000), ("int4b64", 200, 1024, 300),
+                         ("int8b0", 3, 1000, 130), ("w4a8", 100, 640, 256)]:
+        A, W, _ = _case(fmt, M, K, N, seed=M + N)
+        q, p = Q.qgemm_quantize_weights(W, fmt)
+        wp, sp = Q.qgemm_pack_weights(K, N, fmt, q, p)
+        nbytes = Q.qgemm_workspace_size(M, K, N, fmt)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+        calls.append((fmt, M, K, N, dev(A), dev(wp), dev(sp),
+                      torch.empty((M, N), dtype=torch.float32, device="cuda"), ws, nbytes))
+
+    def issue():
+        for fmt, M, K, N, A, B, S, C, ws, nb in calls:
+            Q.qgemm_run_ws(M, K, N, fmt, A, B, S, C, ws, nb)
+
+    issue()
+    torch.cuda.synchronize()
+    eager = [c[7].clone() for c in calls]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        issue()
+    for rep in range(4):
+        for c in calls:
+            c[7].fill_(float("nan"))
+        x = torch.randn(1 << 20, device="cuda")
+        _ = (x * 2).sum().item()
+        g.replay()
+        torch.cuda.synchronize()
+        for c, e in zip(calls, eager):
+            assert torch.equal(c[7], e), (rep, c[0], c[1])

@@ -38,9 +38,9 @@ qgemm_status geometry(int K, int N, qgemm_format f, Geometry *g) {
         break;
     case QGEMM_INT4_B64:
         if (K == 0 || K % 64 != 0) return QGEMM_ERR_SHAPE;
-        r.Kp = K; r.Np = (int)round_up(N, 4); r.nblk = K / 64;
-        r.w_bytes = round_up((size_t)(r.Np / 4) * r.nblk * 128, kPackAlign);
-        r.s_bytes = round_up((size_t)(r.Np / 4) * r.nblk * 32, kPackAlign);
+        r.Kp = K; r.Np = (int)round_up(N, 32); r.nblk = K / 64;
+        r.w_bytes = round_up((size_t)(r.Np / 32) * r.nblk * 1024, kPackAlign);
+        r.s_bytes = round_up((size_t)(r.Np / 32) * r.nblk * 256, kPackAlign);
         break;
     case QGEMM_INT8_B0:
         if (K == 0) return QGEMM_ERR_SHAPE;
@@ -223,16 +223,14 @@ qgemm_status qgemm_pack_weights(int K, int N, qgemm_format f, const void *w_cano
         const int nblk = g.nblk;
         const size_t row = (size_t)K / 2;
         for (int n = 0; n < N; ++n) {
-            const int grp = n >> 2, c = n & 3;
+            const int t = n >> 5, c = n & 31;
             for (int b = 0; b < nblk; ++b) {
-                for (int half = 0; half < 2; ++half) {
-                    const int j = 2 * c + half;
-                    uint8_t *dst = wp + (((size_t)grp * 8 + j) * nblk + b) * 16;
-                    std::memcpy(dst, wc + (size_t)n * row + (size_t)b * 32 + half * 16, 16);
-                }
-                float *rec = spf + (((size_t)grp * 2 + (c >> 1)) * nblk + b) * 4 + (c & 1) * 2;
-                rec[0] = pairs_canonical[((size_t)n * nblk + b) * 2 + 0];
-                rec[1] = pairs_canonical[((size_t)n * nblk + b) * 2 + 1];
+                const size_t rec = (size_t)t * nblk + b;
+                for (int half = 0; half < 2; ++half)
+                    std::memcpy(wp + rec * 1024 + (size_t)(32 * half + c) * 16,
+                                wc + (size_t)n * row + (size_t)b * 32 + half * 16, 16);
+                spf[rec * 64 + c * 2 + 0] = pairs_canonical[((size_t)n * nblk + b) * 2 + 0];
+                spf[rec * 64 + c * 2 + 1] = pairs_canonical[((size_t)n * nblk + b) * 2 + 1];
             }
         }
         break;
@@ -293,16 +291,14 @@ qgemm_status qgemm_unpack_weights(int K, int N, qgemm_format f, const void *w_pa
         const int nblk = g.nblk;
         const size_t row = (size_t)K / 2;
         for (int n = 0; n < N; ++n) {
-            const int grp = n >> 2, c = n & 3;
+            const int t = n >> 5, c = n & 31;
             for (int b = 0; b < nblk; ++b) {
-                for (int half = 0; half < 2; ++half) {
-                    const int j = 2 * c + half;
+                const size_t rec = (size_t)t * nblk + b;
+                for (int half = 0; half < 2; ++half)
                     std::memcpy(wc + (size_t)n * row + (size_t)b * 32 + half * 16,
-                                wp + (((size_t)grp * 8 + j) * nblk + b) * 16, 16);
-                }
-                const float *rec = spf + (((size_t)grp * 2 + (c >> 1)) * nblk + b) * 4 + (c & 1) * 2;
-                pairs_canonical[((size_t)n * nblk + b) * 2 + 0] = rec[0];
-                pairs_canonical[((size_t)n * nblk + b) * 2 + 1] = rec[1];
+                                wp + rec * 1024 + (size_t)(32 * half + c) * 16, 16);
+                pairs_canonical[((size_t)n * nblk + b) * 2 + 0] = spf[rec * 64 + c * 2 + 0];
+                pairs_canonical[((size_t)n * nblk + b) * 2 + 1] = spf[rec * 64 + c * 2 + 1];
             }
         }
         break;

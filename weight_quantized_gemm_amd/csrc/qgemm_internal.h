@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/qgemm.h"
+#include "qgemm.h"
 
 namespace qg {
 
@@ -19,14 +19,16 @@ constexpr size_t kPackAlign = 256;
 // ---------------------------------------------------------------------------
 // Packed layouts (host packer <-> kernels).
 //
-// INT4_B64, nblk = K / 64, G = ceil(N / 4) channel groups of 4:
-//   weights: 16-byte chunks, chunk (g, j, b) at ((g * 8 + j) * nblk + b) * 16
-//            holding canonical bytes [32 b + 16 (j & 1), +16) of channel
-//            4 g + (j >> 1). A wave that gives lane b block b reads every
-//            chunk j of a group as 64 consecutive 16-byte pieces.
-//   pairs:   16-byte records, record (g, h, b) at ((g * 2 + h) * nblk + b) * 16
-//            = {offset, scale} of channel 4g + 2h, then of channel 4g + 2h + 1,
-//            for block b.
+// INT4_B64, nblk = K / 64, Np = roundup(N, 32), tiles t of 32 channels:
+//   weights: 1 KiB records, record (t, b) at (t * nblk + b) * 1024; its
+//            16-byte piece h * 32 + c holds canonical bytes [32 b + 16 h, +16)
+//            (the codes of k = 64 b + 32 h .. 64 b + 32 h + 31) of channel
+//            32 t + c. Piece order is the lane order of a 32 x 32 MFMA operand
+//            (lane = 32 h + c), so one K-block of a 32-channel tile is a single
+//            contiguous 1 KiB load; four consecutive channels of one half are
+//            a contiguous 64-byte run.
+//   pairs:   256-byte records, record (t, b) at (t * nblk + b) * 256 holding
+//            {offset, scale} of channels 32 t .. 32 t + 31 for block b.
 // INT8_B0, Kp = roundup(K, 64), Np = roundup(N, 4):
 //   weights: [Np][Kp] bytes (canonical rows, zero padded);
 //   pairs:   [Np][2] floats.
