@@ -38,10 +38,21 @@ FP16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
 MALL_BYTES = 256 << 20
 
 
-def algorithmic_bytes(M: int, K: int, N: int) -> int:
-    """Bytes the Int4-Block64 product must move: A fp16, codes (K/2 per
-    channel), fp32 [offset, scale] pairs (8 per 64-block per channel), C fp32."""
-    return M * K * 2 + N * K // 2 + N * (K // 64) * 8 + M * N * 4
+def algorithmic_bytes(M: int, K: int, N: int, fmt: str = "int4b64") -> int:
+    """Bytes the product must move at least once: A, the stored weight codes,
+    the fp32 [offset, scale] pairs and C (fp32). Int4 formats hold K/2 bytes of
+    codes per channel, Int8-Block0 K bytes, fp32 B 4*K*N bytes; Int4-Block64
+    has K/64 pairs per channel, the per-channel formats one."""
+    a_bytes = M * K * (4 if fmt == "f32" else 2)
+    if fmt == "f32":
+        w_bytes, p_bytes = 4 * K * N, 0
+    elif fmt == "int8b0":
+        w_bytes, p_bytes = K * N, 8 * N
+    elif fmt == "int4b64":
+        w_bytes, p_bytes = N * K // 2, N * (K // 64) * 8
+    else:  # w4a8
+        w_bytes, p_bytes = N * K // 2, 8 * N
+    return a_bytes + w_bytes + p_bytes + M * N * 4
 
 
 def flops(M: int, K: int, N: int) -> int:
@@ -57,29 +68,41 @@ class Workload:
         from weight_quantized_gemm_amd import synth
         inp = synth.make_inputs(name)
         self.name = name
+        self.fmt = inp["format"]
         self.M, self.K, self.N = inp["M"], inp["K"], inp["N"]
         self.A_host = inp["A"]
-        self.W_host = inp["W"]
-        q, p = Q.qgemm_quantize_weights(inp["W"], "int4b64")
-        self.q_host, self.pairs_host = q, p
-        wp, sp = Q.qgemm_pack_weights(self.K, self.N, "int4b64", q, p)
+        if self.fmt == "f32":
+            self.W_host = inp["B"]
+            wp, sp = inp["B"], None
+        else:
+            self.W_host = inp["W"]
+            q, p = Q.qgemm_quantize_weights(inp["W"], self.fmt)
+            self.q_host, self.pairs_host = q, p
+            wp, sp = Q.qgemm_pack_weights(self.K, self.N, self.fmt, q, p)
         A0 = torch.from_numpy(inp["A"]).cuda()
         B0 = torch.from_numpy(wp).cuda()
-        S0 = torch.from_numpy(sp).cuda()
         self.A = [A0] + [A0.clone() for _ in range(copies - 1)]
         self.B = [B0] + [B0.clone() for _ in range(copies - 1)]
-        self.S = [S0] + [S0.clone() for _ in range(copies - 1)]
+        if sp is None:
+            self.S = [None] * copies
+        else:
+            S0 = torch.from_numpy(sp).cuda()
+            self.S = [S0] + [S0.clone() for _ in range(copies - 1)]
         self.C = [torch.empty((self.M, self.N), dtype=torch.float32, device="cuda")
                   for _ in range(copies)]
+        # caller-owned scratch (W4A8 activation codes), so the timed region allocates nothing
+        self.ws_bytes = Q.qgemm_workspace_size(self.M, self.K, self.N, self.fmt)
+        self.ws = (torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+                   if self.ws_bytes else None)
         self.Q = Q
 
     def bytes_per_copy(self) -> int:
-        return (self.A[0].nbytes + self.B[0].nbytes + self.S[0].nbytes + self.C[0].nbytes)
+        return sum(t.nbytes for t in (self.A[0], self.B[0], self.S[0], self.C[0]) if t is not None)
 
     def run(self, i: int) -> None:
         c = i % len(self.A)
-        self.Q.qgemm_run(self.M, self.K, self.N, self.Q.QGEMM_INT4_B64, self.A[c], self.B[c],
-                         self.S[c], self.C[c])
+        self.Q.qgemm_run_ws(self.M, self.K, self.N, self.fmt, self.A[c], self.B[c], self.S[c],
+                            self.C[c], self.ws, self.ws_bytes)
 
 
 def traffic_record(kernel_src: str, kernel: str):
@@ -137,6 +160,56 @@ def cpu_baseline(dec: Workload, pre: Workload, budget_s: float):
     }
 
 
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
+
+
+def single_workload(args, torch) -> int:
+    """Times one named workload alone (all launches of one qgemm_run call,
+    weights rotated past twice the Infinity Cache) and prints a diagnostic
+    JSON line with its roofline fraction."""
+    from weight_quantized_gemm_amd import synth
+    fmt, M, K, N, _ = synth.CONFIGS[args.workload]
+    per_copy = algorithmic_bytes(M, K, N, fmt)
+    copies = args.copies or min(256, max(2, -(-2 * MALL_BYTES // per_copy) + 1))
+    w = Workload(args.workload, copies)
+    for i in range(args.warmup):
+        w.run(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(copies):
+            w.run(i)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, -(-args.steps // copies))
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / (reps * copies)
+    fl = flops(M, K, N)
+    by = algorithmic_bytes(M, K, N, fmt)
+    if fmt == "w4a8":
+        bound, achieved, peak, unit = "mfma", fl / ms / 1e9, INT8_PEAK_TOPS, "TOP/s"
+    elif M == 1:
+        bound, achieved, peak, unit = "hbm", by / ms / 1e6, HBM_PEAK_GBS, "GB/s"
+    elif fmt == "f32":
+        bound, achieved, peak, unit = "launch", fl / ms / 1e9, 157.3, "TFLOP/s"
+    else:
+        bound, achieved, peak, unit = "mfma", fl / ms / 1e9, FP16_PEAK_TFLOPS, "TFLOP/s"
+    print(json.dumps({
+        "workload": args.workload, "format": fmt, "M": M, "K": K, "N": N,
+        "rotation_copies": copies, "launches": reps * copies, "ms_per_call": ms,
+        "gflops": fl / ms / 1e6, "algorithmic_bytes": by, "gb_s": by / ms / 1e6,
+        "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                     "frac": achieved / peak},
+    }), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +219,13 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of CPU oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="", metavar="NAME",
+                    help="diagnostic: time only this named workload (" +
+                         ", ".join(("f32", "int8b0_decode", "int4b64_decode", "int4b64_prefill",
+                                    "w4a8_prefill")) + ") and print its own JSON line")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run torch's plain device copy of MIB MiB (fp32) 10 times, "
+                         "the reference kernel for scaling the HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -156,6 +236,18 @@ def main() -> int:
 
     import torch
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration << 18          # fp32 elements in MIB MiB
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 4 * n, "launches": 10}), flush=True)
+        return 0
+
+    if args.workload:
+        return single_workload(args, torch)
 
     # one decode + one prefill copy is ~50 MB; rotate past 2x the MALL
     per_step_bytes = (algorithmic_bytes(1, 4096, 11008) + algorithmic_bytes(512, 4096, 4096))
@@ -170,40 +262,49 @@ def main() -> int:
 
     # One graph holds `copies` steps (prefill then decode, each on its own
     # rotation copy); replaying it keeps the GPU fed without per-launch host
-    # work. Two more graphs hold `copies` back-to-back launches of one kernel
-    # each and give that kernel's average launch duration.
-    def capture(fn):
+    # work. A second graph holds the remaining steps % copies steps, so the
+    # timed region runs exactly --steps steps. Two more graphs hold `copies`
+    # back-to-back launches of one kernel each and give that kernel's average
+    # launch duration.
+    def capture(fn, count):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for i in range(copies):
+            for i in range(count):
                 fn(i)
         return g
 
-    g_step = capture(lambda i: (pre.run(i), dec.run(i)))
-    g_pre = capture(pre.run)
-    g_dec = capture(dec.run)
-    for g in (g_step, g_pre, g_dec):
-        g.replay()
+    full, rem = divmod(args.steps, copies)
+    step = lambda i: (pre.run(i), dec.run(i))
+    g_step = capture(step, copies)
+    g_rem = capture(step, rem) if rem else None
+    g_pre = capture(pre.run, copies)
+    g_dec = capture(dec.run, copies)
+    for g in (g_step, g_rem, g_pre, g_dec):
+        if g is not None:
+            g.replay()
     torch.cuda.synchronize()
 
-    def timed(graph, launches_per_replay, replays):
+    def timed(graphs, launches):
+        """Replays `graphs` in order between two events on the current stream
+        (the stream the kernels are launched on); ms per launch, device and
+        wall clock."""
         start = torch.cuda.Event(enable_timing=True)
         stop = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         start.record()
-        for _ in range(replays):
-            graph.replay()
+        for g in graphs:
+            g.replay()
         stop.record()
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) * 1e3
-        return start.elapsed_time(stop) / (replays * launches_per_replay), wall / (replays * launches_per_replay)
+        return start.elapsed_time(stop) / launches, wall / launches
 
-    replays = max(1, -(-args.steps // copies))
-    K = replays * copies                      # steps actually timed
-    ms_step, wall_ms_step = timed(g_step, copies, replays)
-    pre_ms, _ = timed(g_pre, copies, replays)
-    dec_ms, _ = timed(g_dec, copies, replays)
+    K = args.steps
+    ms_step, wall_ms_step = timed([g_step] * full + ([g_rem] if g_rem else []), K)
+    kr = max(1, -(-K // copies))              # kernel-only graphs: about K launches each
+    pre_ms, _ = timed([g_pre] * kr, kr * copies)
+    dec_ms, _ = timed([g_dec] * kr, kr * copies)
 
     step_flops = flops(dec.M, dec.K, dec.N) + flops(pre.M, pre.K, pre.N)
     value = step_flops / (ms_step * 1e-3) / 1e9

@@ -127,6 +127,21 @@ def test_int4b64_shapes(M):
         _parity("int4b64", M, K, N, seed=M * 7 + K + N)
 
 
+@pytest.mark.parametrize("K", [64, 128, 192, 256, 320, 384, 448, 512, 576, 640, 1024])
+def test_int4b64_tiled_short_k(K):
+    """The tiled kernel splits the K-blocks over four waves and pads each
+    wave's count to its register ring; every per-wave count from 0 to 4
+    blocks (plus a ragged remainder) must match the oracle and be
+    bit-identical across calls."""
+    M, N = 65, 130
+    A, W, _ = _case("int4b64", M, K, N, seed=K)
+    q, p, qo, po = _quantized_pair("int4b64", W)
+    C1 = run("int4b64", M, K, N, A, q, p)
+    C2 = run("int4b64", M, K, N, A, q, p)
+    compare(C1, O.reference("int4b64", A, q=qo, pairs=po), f"int4b64 tiled K={K}")
+    assert np.array_equal(C1, C2)
+
+
 @pytest.mark.parametrize("M", SMALL_M)
 def test_int8b0_shapes(M):
     for K, N in [(1, 3), (7, 4), (12, 9), (64, 64), (100, 70), (1000, 33), (4100, 6)]:

@@ -45,27 +45,43 @@ constexpr int CF = BN / 32;            // 32-column accumulator tiles per wave
 constexpr int AS_STRIDE = BK + 8;      // halves per LDS row of the A tile (144 bytes)
 constexpr int RED_STRIDE = BN + 4;     // floats per LDS row of the reduction
 constexpr int RING = 4;                // B register ring (3 blocks ahead)
-constexpr size_t AS_BYTES = (size_t)BM * AS_STRIDE * 2;          // per wave
+constexpr size_t AS_BYTES = (size_t)BM * AS_STRIDE * 2;          // one A tile
 constexpr size_t RED_BYTES = (size_t)4 * BM * RED_STRIDE * 4;    // all waves
-constexpr size_t LDS_BYTES = RED_BYTES > 4 * AS_BYTES ? RED_BYTES : 4 * AS_BYTES;
+constexpr size_t LDS_BYTES = RED_BYTES > 8 * AS_BYTES ? RED_BYTES : 8 * AS_BYTES;
+
+// Per (channel tile, block) dequantisation constants. Even codes decode as
+// x = 1024 + q and odd codes as x = 1024 + 16 q (the nibble is left in
+// place), so w = offset + scale * q is x * s_lo + b_lo or x * s_hi + b_hi.
+struct DqParams {
+    float s_lo, b_lo, s_hi, b_hi;
+};
+
+__device__ __forceinline__ DqParams dq_params(f2_t pair) {
+    const float off = pair.x, sc = pair.y;
+    return {sc, fmaf(-1024.0f, sc, off), sc * 0.0625f, fmaf(-64.0f, sc, off)};
+}
 }
 
 // 8 Int4 codes (one word, k ascending, low nibble first) -> 8 fp16 weights
-// w = offset + scale * q in k order. bias = offset - 1024 * scale.
-__device__ __forceinline__ h8_t dequant8(unsigned word, float scale, float bias) {
-    const h2_t x0 = as_h2((word & 0x000F000Fu) | 0x64006400u);          // 1024 + q0, q4
-    const h2_t x1 = as_h2(((word >> 4) & 0x000F000Fu) | 0x64006400u);   // q1, q5
-    const h2_t x2 = as_h2(((word >> 8) & 0x000F000Fu) | 0x64006400u);   // q2, q6
-    const h2_t x3 = as_h2(((word >> 12) & 0x000F000Fu) | 0x64006400u);  // q3, q7
+// in k order, each one fp32 fused multiply-add rounded once to fp16. m_lo,
+// m_hi and magic are the constants 0x000F000F, 0x00F000F0 and 0x64006400 held
+// in registers, so each pair of codes costs one v_and_or_b32.
+__device__ __forceinline__ h8_t dequant8(unsigned word, const DqParams &p, unsigned m_lo,
+                                         unsigned m_hi, unsigned magic) {
+    const unsigned w8 = word >> 8;
+    const h2_t x0 = as_h2((word & m_lo) | magic);   // codes 0, 4 -> 1024 + q
+    const h2_t x1 = as_h2((word & m_hi) | magic);   // codes 1, 5 -> 1024 + 16 q
+    const h2_t x2 = as_h2((w8 & m_lo) | magic);     // codes 2, 6
+    const h2_t x3 = as_h2((w8 & m_hi) | magic);     // codes 3, 7
     h8_t o;
-    o[0] = (_Float16)fmaf((float)x0.x, scale, bias);
-    o[1] = (_Float16)fmaf((float)x1.x, scale, bias);
-    o[2] = (_Float16)fmaf((float)x2.x, scale, bias);
-    o[3] = (_Float16)fmaf((float)x3.x, scale, bias);
-    o[4] = (_Float16)fmaf((float)x0.y, scale, bias);
-    o[5] = (_Float16)fmaf((float)x1.y, scale, bias);
-    o[6] = (_Float16)fmaf((float)x2.y, scale, bias);
-    o[7] = (_Float16)fmaf((float)x3.y, scale, bias);
+    o[0] = (_Float16)fmaf((float)x0.x, p.s_lo, p.b_lo);
+    o[1] = (_Float16)fmaf((float)x1.x, p.s_hi, p.b_hi);
+    o[2] = (_Float16)fmaf((float)x2.x, p.s_lo, p.b_lo);
+    o[3] = (_Float16)fmaf((float)x3.x, p.s_hi, p.b_hi);
+    o[4] = (_Float16)fmaf((float)x0.y, p.s_lo, p.b_lo);
+    o[5] = (_Float16)fmaf((float)x1.y, p.s_hi, p.b_hi);
+    o[6] = (_Float16)fmaf((float)x2.y, p.s_lo, p.b_lo);
+    o[7] = (_Float16)fmaf((float)x3.y, p.s_hi, p.b_hi);
     return o;
 }
 
@@ -99,16 +115,20 @@ __global__ __launch_bounds__(256) void gemm_int4b64_kernel(
     const int nb = kb1 - kb0;
     const int ntiles_b = (N + 31) / 32;                              // packed 32-channel tiles
 
-    _Float16 *As = reinterpret_cast<_Float16 *>(lds + wave * AS_BYTES);
+    // two A tiles per wave: block i is read from tile i % 2 while block i + 1
+    // is written into the other
+    _Float16 *As0 = reinterpret_cast<_Float16 *>(lds + (2 * wave) * AS_BYTES);
+    _Float16 *As1 = reinterpret_cast<_Float16 *>(lds + (2 * wave + 1) * AS_BYTES);
 
-    // A loader role: 8 rows x 128 bytes per instruction, lane -> (row, 16 B piece).
+    // A loader role: 8 rows x 128 bytes per instruction, lane -> (row, 16 B
+    // piece); byte offsets from the tile's first row (rows past M are
+    // clamped: loaded, never stored).
     const int arow = lane >> 3, apc = lane & 7;
-    const _Float16 *a_src[8];
+    const char *A_tile = reinterpret_cast<const char *>(A + (size_t)m0 * K);
+    unsigned a_off[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int gm = min(m0 + 8 * i + arow, M - 1);   // rows past M: loaded, never stored
-        a_src[i] = A + (size_t)gm * K + 8 * apc;
-    }
+    for (int i = 0; i < 8; ++i)
+        a_off[i] = (unsigned)(min(8 * i + arow, M - 1 - m0) * K + 8 * apc) * 2u;
     // B: tile index of each accumulator column tile (tiles past N: loaded, never stored)
     size_t b_rec0[CF];
 #pragma unroll
@@ -116,7 +136,18 @@ __global__ __launch_bounds__(256) void gemm_int4b64_kernel(
 
     auto load_a = [&](u4_t (&dst)[8], int kt) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dst[i] = *reinterpret_cast<const u4_t *>(a_src[i] + kt * BK);
+        for (int i = 0; i < 8; ++i)
+            dst[i] = *reinterpret_cast<const u4_t *>(A_tile + a_off[i] + (unsigned)kt * (BK * 2));
+    };
+    auto store_a = [&](_Float16 *As, const u4_t (&src)[8]) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            *reinterpret_cast<u4_t *>(As + (8 * j + arow) * AS_STRIDE + 8 * apc) = src[j];
+    };
+    auto read_a = [&](const _Float16 *As, int s, h8_t (&af)[RF]) {
+#pragma unroll
+        for (int rf = 0; rf < RF; ++rf)
+            af[rf] = *reinterpret_cast<const h8_t *>(As + (32 * rf + r) * AS_STRIDE + 32 * h + 8 * s);
     };
     auto load_b = [&](u4_t (&codes)[CF], f2_t (&pairs)[CF], int kt) {
 #pragma unroll
@@ -127,6 +158,11 @@ __global__ __launch_bounds__(256) void gemm_int4b64_kernel(
         }
     };
 
+    // decode constants, opaque to the optimiser so they stay in registers
+    unsigned m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, magic = 0x64006400u;
+    asm volatile("" : "+s"(m_lo), "+s"(m_hi));
+    asm volatile("" : "+v"(magic));
+
     f16_t acc[RF][CF];
 #pragma unroll
     for (int i = 0; i < RF; ++i)
@@ -135,44 +171,92 @@ __global__ __launch_bounds__(256) void gemm_int4b64_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    u4_t an[8];
-    u4_t bc[RING][CF];
-    f2_t bp[RING][CF];
-    if (nb > 0) load_a(an, kb0);
-#pragma unroll
-    for (int d = 0; d < RING - 1; ++d)
-        if (d < nb) load_b(bc[d], bp[d], kb0 + d);
+    if (nb > 0) {
+        u4_t an[8];
+        u4_t bc[RING][CF];
+        f2_t bp[RING][CF];
+        DqParams prm[CF];
+        h8_t acur[RF], anxt[RF], bcur[CF], bnxt[CF];
 
-    for (int base = 0; base < nb; base += RING) {
+        // prologue: A of the first block in LDS, A of the second in flight,
+        // B of the first RING - 1 blocks in flight, step (0, 0) operands
+        // ready. Ring slots past the last block hold that block again, so
+        // every slot always decodes to finite weights.
+        load_a(an, kb0);
 #pragma unroll
-        for (int u = 0; u < RING; ++u) {
-            const int i = base + u;
-            if (i < nb) {
-                // stage this block's A rows (loaded one block earlier)
+        for (int d = 0; d < RING - 1; ++d) load_b(bc[d], bp[d], kb0 + min(d, nb - 1));
+        // the last slot is otherwise first filled inside the loop, and only
+        // when that block exists
+        if (nb < RING) load_b(bc[RING - 1], bp[RING - 1], kb1 - 1);
+        store_a(As0, an);
+        if (nb > 1) {
+            load_a(an, kb0 + 1);
+        } else {
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    *reinterpret_cast<u4_t *>(As + (8 * j + arow) * AS_STRIDE + 8 * apc) = an[j];
-                if (i + 1 < nb) load_a(an, kb0 + i + 1);
-                if (i + RING - 1 < nb) load_b(bc[(u + RING - 1) % RING], bp[(u + RING - 1) % RING], kb0 + i + RING - 1);
-                float sc[CF], bias[CF];
+            for (int j = 0; j < 8; ++j) an[j] = u4_t{0, 0, 0, 0};
+        }
 #pragma unroll
-                for (int cf = 0; cf < CF; ++cf) {
-                    sc[cf] = bp[u][cf].y;
-                    bias[cf] = fmaf(-1024.0f, sc[cf], bp[u][cf].x);
+        for (int cf = 0; cf < CF; ++cf) prm[cf] = dq_params(bp[0][cf]);
+        read_a(As0, 0, acur);
+#pragma unroll
+        for (int cf = 0; cf < CF; ++cf) bcur[cf] = dequant8(bc[0][cf][0], prm[cf], m_lo, m_hi, magic);
+
+        // The block count is padded to a multiple of RING so the unrolled
+        // loop has a single exit; a padded block has an all-zero A tile and
+        // adds exactly zero to every accumulator.
+        const int nb_pad = (nb + RING - 1) / RING * RING;
+        for (int base = 0; base < nb_pad; base += RING) {
+#pragma unroll
+            for (int u = 0; u < RING; ++u) {
+                const int i = base + u;
+                _Float16 *As_cur = (u & 1) ? As1 : As0;
+                _Float16 *As_nxt = (u & 1) ? As0 : As1;
+                // block i + 1's A into the other tile (its global loads were
+                // issued a block ago), then the loads for blocks i + 2 (A)
+                // and i + RING - 1 (B, into the slot block i - 1 has freed)
+                store_a(As_nxt, an);
+                if (i + 2 < nb) {
+                    load_a(an, kb0 + i + 2);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) an[j] = u4_t{0, 0, 0, 0};
                 }
+                if (i + RING - 1 < nb)
+                    load_b(bc[(u + RING - 1) % RING], bp[(u + RING - 1) % RING], kb0 + i + RING - 1);
+                // four MFMA steps; while the matrix cores work on step s the
+                // operands of the next step (this block's s + 1, or the next
+                // block's step 0) are read and dequantised
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    h8_t af[RF], bf[CF];
+                    if (s < 3) {
+                        read_a(As_cur, s + 1, anxt);
 #pragma unroll
-                    for (int rf = 0; rf < RF; ++rf)
-                        af[rf] = *reinterpret_cast<const h8_t *>(As + (32 * rf + r) * AS_STRIDE + 32 * h + 8 * s);
+                        for (int cf = 0; cf < CF; ++cf)
+                            bnxt[cf] = dequant8(bc[u][cf][s + 1], prm[cf], m_lo, m_hi, magic);
+                    } else {
+                        const int un = (u + 1) % RING;
+                        read_a(As_nxt, 0, anxt);
 #pragma unroll
-                    for (int cf = 0; cf < CF; ++cf) bf[cf] = dequant8(bc[u][cf][s], sc[cf], bias[cf]);
+                        for (int cf = 0; cf < CF; ++cf) {
+                            prm[cf] = dq_params(bp[un][cf]);
+                            bnxt[cf] = dequant8(bc[un][cf][0], prm[cf], m_lo, m_hi, magic);
+                        }
+                    }
 #pragma unroll
                     for (int rf = 0; rf < RF; ++rf)
 #pragma unroll
                         for (int cf = 0; cf < CF; ++cf)
-                            acc[rf][cf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[rf], bf[cf], acc[rf][cf], 0, 0, 0);
+                            acc[rf][cf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(acur[rf], bcur[cf], acc[rf][cf], 0, 0, 0);
+                    // one MFMA, then up to seven VALU instructions, eight times
+#pragma unroll
+                    for (int j = 0; j < RF * CF; ++j) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+                    }
+#pragma unroll
+                    for (int rf = 0; rf < RF; ++rf) acur[rf] = anxt[rf];
+#pragma unroll
+                    for (int cf = 0; cf < CF; ++cf) bcur[cf] = bnxt[cf];
                 }
             }
         }

@@ -102,7 +102,8 @@ def _dev_ptr(t):
         return None
     if isinstance(t, int):
         return ctypes.c_void_p(t)
-    assert t.is_cuda and t.is_contiguous(), "device buffers must be contiguous GPU tensors"
+    if not (t.is_cuda and t.is_contiguous()):
+        raise ValueError("device buffers must be contiguous GPU tensors")
     return ctypes.c_void_p(t.data_ptr())
 
 
