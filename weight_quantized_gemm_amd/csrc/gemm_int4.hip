@@ -12,20 +12,27 @@
 //
 // Decomposition, chosen from what limits this shape on CDNA4 (a 512 x 4096
 // output gives each of 256 CUs only 8192 outputs, so operand traffic from L2
-// bounds the kernel before the matrix cores do):
-//  - a 256-thread workgroup owns a 64 x 128 tile of C (a taller-than-wide
+// and the per-weight dequantisation work bound the kernel before the matrix
+// cores do):
+//  - a 512-thread workgroup owns a 64 x 128 tile of C (a taller-than-wide
 //    tile would read A from L2 twice as often);
-//  - its four waves split K into contiguous quarters and each accumulates
-//    the whole 64 x 128 tile with v_mfma_f32_32x32x16_f16 (2 x 4 accumulator
-//    tiles), so every A and B element is fetched and dequantised once per
-//    workgroup;
-//  - A rows are fetched with fully coalesced loads (8 rows x 128 bytes per
-//    instruction) into a wave-private LDS tile and read back in the operand
-//    layout; a wave only reads what it wrote, so no barrier is needed;
+//  - wave (h, q) owns the 64 x 64 half h of the tile for the contiguous K
+//    quarter q and accumulates it with v_mfma_f32_32x32x16_f16 (2 x 2
+//    accumulator tiles), so every B element is fetched and dequantised once
+//    per workgroup; two waves per SIMD let one wave's dequantisation issue
+//    while the other's matrix instructions run;
+//  - the two waves of a quarter share its A tiles in LDS: each fetches 32 of
+//    the 64 rows with fully coalesced loads (8 rows x 128 bytes per
+//    instruction) four blocks ahead through a register ring; four LDS tiles
+//    per quarter and one barrier per block keep writers behind readers;
 //  - a K-block of a 32-channel B tile is one contiguous 1 KiB record already
 //    in operand lane order (see the packed layout), fetched three blocks
-//    ahead through a register ring;
-//  - the four partial tiles meet in LDS and are summed in a fixed order.
+//    ahead through a register ring and dequantised in registers (one fp32
+//    multiply-add per weight, no LDS round trip);
+//  - the operands of MFMA step s + 1 are read and dequantised while the
+//    matrix cores run step s;
+//  - the eight partial tiles meet in LDS and the four K quarters are summed
+//    in a fixed order.
 // Lane (r, h) = (lane % 32, lane / 32) holds K-elements 32 h + 8 s .. +7 of
 // every 64-wide block in MFMA step s, for its A row and B column alike (the K
 // order inside an MFMA only has to agree between A and B).
@@ -40,14 +47,17 @@ namespace qg {
 
 namespace {
 constexpr int BM = 64, BN = 128, BK = 64;
+constexpr int NWAVE = 8;               // (N half, K quarter) per wave
+constexpr int WN = BN / 2;             // columns per wave
 constexpr int RF = BM / 32;            // 32-row accumulator tiles per wave
-constexpr int CF = BN / 32;            // 32-column accumulator tiles per wave
-constexpr int AS_STRIDE = BK + 8;      // halves per LDS row of the A tile (144 bytes)
-constexpr int RED_STRIDE = BN + 4;     // floats per LDS row of the reduction
-constexpr int RING = 4;                // B register ring (3 blocks ahead)
-constexpr size_t AS_BYTES = (size_t)BM * AS_STRIDE * 2;          // one A tile
-constexpr size_t RED_BYTES = (size_t)4 * BM * RED_STRIDE * 4;    // all waves
-constexpr size_t LDS_BYTES = RED_BYTES > 8 * AS_BYTES ? RED_BYTES : 8 * AS_BYTES;
+constexpr int CF = WN / 32;            // 32-column accumulator tiles per wave
+constexpr int AS_STRIDE = BK + 8;      // halves per LDS row of an A tile (144 bytes)
+constexpr int RING = 4;                // B register ring (3 blocks ahead) = A tiles per quarter
+constexpr int RED_STRIDE = WN + 4;     // floats per LDS row of the reduction
+constexpr size_t AS_BYTES = (size_t)BM * AS_STRIDE * 2;                 // one A tile
+constexpr size_t A_LDS = (size_t)4 * RING * AS_BYTES;                   // all quarters
+constexpr size_t RED_BYTES = (size_t)NWAVE * BM * RED_STRIDE * 4;       // all waves
+constexpr size_t LDS_BYTES = RED_BYTES > A_LDS ? RED_BYTES : A_LDS;
 
 // Per (channel tile, block) dequantisation constants. Even codes decode as
 // x = 1024 + q and odd codes as x = 1024 + 16 q (the nibble is left in
@@ -85,7 +95,7 @@ __device__ __forceinline__ h8_t dequant8(unsigned word, const DqParams &p, unsig
     return o;
 }
 
-__global__ __launch_bounds__(256) void gemm_int4b64_kernel(
+__global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     int M, int K, int N, int tiles_m, int tiles_n, int xcd_bands,
     const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ Sp, float *__restrict__ C) {
@@ -109,40 +119,50 @@ __global__ __launch_bounds__(256) void gemm_int4b64_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = uniform(tid >> 6);
+    const int nh = wave & 1, kq = wave >> 1;      // N half, K quarter
     const int r = lane & 31, h = lane >> 5;
-    const int nblk = K / BK;
-    const int kb0 = wave * nblk / 4, kb1 = (wave + 1) * nblk / 4;   // contiguous quarter
-    const int nb = kb1 - kb0;
-    const int ntiles_b = (N + 31) / 32;                              // packed 32-channel tiles
+    const int nblk = K / BK;                       // >= 1
+    const int kb0 = kq * nblk / 4, kb1 = (kq + 1) * nblk / 4;   // contiguous quarter
+    const int nb = kb1 - kb0;                      // kb0 is a valid block even when nb == 0
+    const int last = max(kb1 - 1, kb0);
+    // every wave runs the same number of (padded) blocks: the largest
+    // quarter rounded up to the ring, so all waves meet every barrier
+    const int nsteps = ((nblk + 3) / 4 + RING - 1) / RING * RING;
+    const int ntiles_b = (N + 31) / 32;            // packed 32-channel tiles
 
-    // two A tiles per wave: block i is read from tile i % 2 while block i + 1
-    // is written into the other
-    _Float16 *As0 = reinterpret_cast<_Float16 *>(lds + (2 * wave) * AS_BYTES);
-    _Float16 *As1 = reinterpret_cast<_Float16 *>(lds + (2 * wave + 1) * AS_BYTES);
+    auto a_tile = [&](int slot) {
+        return reinterpret_cast<_Float16 *>(lds + (size_t)(kq * RING + slot) * AS_BYTES);
+    };
 
-    // A loader role: 8 rows x 128 bytes per instruction, lane -> (row, 16 B
-    // piece); byte offsets from the tile's first row (rows past M are
-    // clamped: loaded, never stored).
+    // A loader role: the two waves of a quarter each fetch 32 of the 64 rows,
+    // 8 rows x 128 bytes per instruction, lane -> (row, 16 B piece); byte
+    // offsets from the tile's first row (rows past M are clamped: loaded,
+    // never stored).
     const int arow = lane >> 3, apc = lane & 7;
     const char *A_tile = reinterpret_cast<const char *>(A + (size_t)m0 * K);
-    unsigned a_off[8];
+    unsigned a_off[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        a_off[i] = (unsigned)(min(8 * i + arow, M - 1 - m0) * K + 8 * apc) * 2u;
-    // B: tile index of each accumulator column tile (tiles past N: loaded, never stored)
+    for (int i = 0; i < 4; ++i)
+        a_off[i] = (unsigned)(min(32 * nh + 8 * i + arow, M - 1 - m0) * K + 8 * apc) * 2u;
+    // B: packed tile of each accumulator column tile (tiles past N: loaded, never stored)
     size_t b_rec0[CF];
 #pragma unroll
-    for (int cf = 0; cf < CF; ++cf) b_rec0[cf] = (size_t)min(n0 / 32 + cf, ntiles_b - 1) * nblk;
+    for (int cf = 0; cf < CF; ++cf)
+        b_rec0[cf] = (size_t)min(n0 / 32 + CF * nh + cf, ntiles_b - 1) * nblk;
 
-    auto load_a = [&](u4_t (&dst)[8], int kt) {
+    auto load_a = [&](u4_t (&dst)[4], int kt) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 4; ++i)
             dst[i] = *reinterpret_cast<const u4_t *>(A_tile + a_off[i] + (unsigned)kt * (BK * 2));
     };
-    auto store_a = [&](_Float16 *As, const u4_t (&src)[8]) {
+    auto zero_a = [&](u4_t (&dst)[4]) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            *reinterpret_cast<u4_t *>(As + (8 * j + arow) * AS_STRIDE + 8 * apc) = src[j];
+        for (int i = 0; i < 4; ++i) dst[i] = u4_t{0, 0, 0, 0};
+    };
+    auto store_a = [&](_Float16 *As, const u4_t (&src)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<u4_t *>(As + (32 * nh + 8 * i + arow) * AS_STRIDE + 8 * apc) = src[i];
     };
     auto read_a = [&](const _Float16 *As, int s, h8_t (&af)[RF]) {
 #pragma unroll
@@ -171,98 +191,86 @@ __global__ __launch_bounds__(256) void gemm_int4b64_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    if (nb > 0) {
-        u4_t an[8];
-        u4_t bc[RING][CF];
-        f2_t bp[RING][CF];
-        DqParams prm[CF];
-        h8_t acur[RF], anxt[RF], bcur[CF], bnxt[CF];
+    u4_t an[RING][4];          // A register ring: stage j holds a block = j mod RING
+    u4_t bc[RING][CF];
+    f2_t bp[RING][CF];
+    DqParams prm[CF];
+    h8_t acur[RF], anxt[RF], bcur[CF], bnxt[CF];
 
-        // prologue: A of the first block in LDS, A of the second in flight,
-        // B of the first RING - 1 blocks in flight, step (0, 0) operands
-        // ready. Ring slots past the last block hold that block again, so
-        // every slot always decodes to finite weights.
-        load_a(an, kb0);
+    // prologue: block 0's A in tile 0 and blocks 1 .. RING in flight in the
+    // A ring, B of blocks 0 .. RING - 1 in flight (slots past the quarter's
+    // last block hold that block again, so every slot decodes to finite
+    // weights), step (0, 0) operands ready. Blocks past the quarter's end
+    // stage zero A tiles.
+    if (nb > 0) load_a(an[0], kb0); else zero_a(an[0]);
 #pragma unroll
-        for (int d = 0; d < RING - 1; ++d) load_b(bc[d], bp[d], kb0 + min(d, nb - 1));
-        // the last slot is otherwise first filled inside the loop, and only
-        // when that block exists
-        if (nb < RING) load_b(bc[RING - 1], bp[RING - 1], kb1 - 1);
-        store_a(As0, an);
-        if (nb > 1) {
-            load_a(an, kb0 + 1);
-        } else {
+    for (int d = 0; d < RING; ++d) load_b(bc[d], bp[d], min(kb0 + d, last));
+    store_a(a_tile(0), an[0]);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) an[j] = u4_t{0, 0, 0, 0};
-        }
+    for (int d = 1; d <= RING; ++d) {
+        if (d < nb) load_a(an[d % RING], kb0 + d); else zero_a(an[d % RING]);
+    }
+    __syncthreads();
 #pragma unroll
-        for (int cf = 0; cf < CF; ++cf) prm[cf] = dq_params(bp[0][cf]);
-        read_a(As0, 0, acur);
+    for (int cf = 0; cf < CF; ++cf) prm[cf] = dq_params(bp[0][cf]);
+    read_a(a_tile(0), 0, acur);
 #pragma unroll
-        for (int cf = 0; cf < CF; ++cf) bcur[cf] = dequant8(bc[0][cf][0], prm[cf], m_lo, m_hi, magic);
+    for (int cf = 0; cf < CF; ++cf) bcur[cf] = dequant8(bc[0][cf][0], prm[cf], m_lo, m_hi, magic);
 
-        // The block count is padded to a multiple of RING so the unrolled
-        // loop has a single exit; a padded block has an all-zero A tile and
-        // adds exactly zero to every accumulator.
-        const int nb_pad = (nb + RING - 1) / RING * RING;
-        for (int base = 0; base < nb_pad; base += RING) {
+    // Block i uses A tile i % RING and B slot i % RING. A padded block
+    // (i >= nb) has an all-zero A tile and adds exactly zero.
+    for (int base = 0; base < nsteps; base += RING) {
 #pragma unroll
-            for (int u = 0; u < RING; ++u) {
-                const int i = base + u;
-                _Float16 *As_cur = (u & 1) ? As1 : As0;
-                _Float16 *As_nxt = (u & 1) ? As0 : As1;
-                // block i + 1's A into the other tile (its global loads were
-                // issued a block ago), then the loads for blocks i + 2 (A)
-                // and i + RING - 1 (B, into the slot block i - 1 has freed)
-                store_a(As_nxt, an);
-                if (i + 2 < nb) {
-                    load_a(an, kb0 + i + 2);
+        for (int u = 0; u < RING; ++u) {
+            const int i = base + u;
+            // block i + 1's A (loaded RING - 1 blocks ago) into its tile,
+            // which was last read in block i - 3, before the previous
+            // barrier; its ring stage then takes block i + 1 + RING
+            store_a(a_tile((u + 1) % RING), an[(u + 1) % RING]);
+            if (i + 1 + RING < nb) load_a(an[(u + 1) % RING], kb0 + i + 1 + RING);
+            else zero_a(an[(u + 1) % RING]);
+            __syncthreads();
+            // four MFMA steps; while the matrix cores work on step s the
+            // operands of the next step (this block's s + 1, or the next
+            // block's step 0) are read and dequantised
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                if (s < 3) {
+                    read_a(a_tile(u), s + 1, anxt);
+#pragma unroll
+                    for (int cf = 0; cf < CF; ++cf)
+                        bnxt[cf] = dequant8(bc[u][cf][s + 1], prm[cf], m_lo, m_hi, magic);
                 } else {
+                    const int un = (u + 1) % RING;
+                    read_a(a_tile(un), 0, anxt);
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) an[j] = u4_t{0, 0, 0, 0};
-                }
-                if (i + RING - 1 < nb)
-                    load_b(bc[(u + RING - 1) % RING], bp[(u + RING - 1) % RING], kb0 + i + RING - 1);
-                // four MFMA steps; while the matrix cores work on step s the
-                // operands of the next step (this block's s + 1, or the next
-                // block's step 0) are read and dequantised
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    if (s < 3) {
-                        read_a(As_cur, s + 1, anxt);
-#pragma unroll
-                        for (int cf = 0; cf < CF; ++cf)
-                            bnxt[cf] = dequant8(bc[u][cf][s + 1], prm[cf], m_lo, m_hi, magic);
-                    } else {
-                        const int un = (u + 1) % RING;
-                        read_a(As_nxt, 0, anxt);
-#pragma unroll
-                        for (int cf = 0; cf < CF; ++cf) {
-                            prm[cf] = dq_params(bp[un][cf]);
-                            bnxt[cf] = dequant8(bc[un][cf][0], prm[cf], m_lo, m_hi, magic);
-                        }
+                    for (int cf = 0; cf < CF; ++cf) {
+                        prm[cf] = dq_params(bp[un][cf]);
+                        bnxt[cf] = dequant8(bc[un][cf][0], prm[cf], m_lo, m_hi, magic);
                     }
-#pragma unroll
-                    for (int rf = 0; rf < RF; ++rf)
-#pragma unroll
-                        for (int cf = 0; cf < CF; ++cf)
-                            acc[rf][cf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(acur[rf], bcur[cf], acc[rf][cf], 0, 0, 0);
-                    // one MFMA, then up to seven VALU instructions, eight times
-#pragma unroll
-                    for (int j = 0; j < RF * CF; ++j) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
-                    }
-#pragma unroll
-                    for (int rf = 0; rf < RF; ++rf) acur[rf] = anxt[rf];
-#pragma unroll
-                    for (int cf = 0; cf < CF; ++cf) bcur[cf] = bnxt[cf];
                 }
+#pragma unroll
+                for (int rf = 0; rf < RF; ++rf)
+#pragma unroll
+                    for (int cf = 0; cf < CF; ++cf)
+                        acc[rf][cf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(acur[rf], bcur[cf], acc[rf][cf], 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < RF * CF; ++j) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+                }
+#pragma unroll
+                for (int rf = 0; rf < RF; ++rf) acur[rf] = anxt[rf];
+#pragma unroll
+                for (int cf = 0; cf < CF; ++cf) bcur[cf] = bnxt[cf];
             }
+            // slot u is free now (its last use was the dequantisation in
+            // step 2): refill it with block i + RING
+            if (i + RING < nb) load_b(bc[u], bp[u], kb0 + i + RING);
         }
     }
 
-    // ---- the four partial tiles to LDS (reusing the A tiles' space) ----
+    // ---- the eight partial tiles to LDS (reusing the A tiles' space) ----
     __syncthreads();
     float *red = reinterpret_cast<float *>(lds) + (size_t)wave * BM * RED_STRIDE;
 #pragma unroll
@@ -274,22 +282,24 @@ __global__ __launch_bounds__(256) void gemm_int4b64_kernel(
                 red[(32 * rf + 8 * (e >> 2) + 4 * h + (e & 3)) * RED_STRIDE + 32 * cf + r] = acc[rf][cf][e];
     __syncthreads();
 
-    // ---- sum in a fixed order and store: thread -> row tid / 4, 32 columns ----
-    const int row = tid >> 2;
-    const int c0 = (tid & 3) * 32;
+    // ---- sum the four K quarters in a fixed order and store:
+    //      thread -> row tid / 8, 16 columns ----
+    const int row = tid >> 3;
+    const int c0 = (tid & 7) * 16;                 // column in the 128-wide tile
     const int gm = m0 + row;
     if (gm >= M) return;
+    const int half = c0 / WN, ch = c0 % WN;
     const float *red0 = reinterpret_cast<const float *>(lds);
     float *dst = C + (size_t)gm * N + n0 + c0;
-    const bool vec_store = (N & 3) == 0 && n0 + c0 + 32 <= N;
+    const bool vec_store = (N & 3) == 0 && n0 + c0 + 16 <= N;
 #pragma unroll
-    for (int j = 0; j < 32; j += 4) {
-        const size_t o = (size_t)row * RED_STRIDE + c0 + j;
+    for (int j = 0; j < 16; j += 4) {
+        const size_t o = (size_t)row * RED_STRIDE + ch + j;
         const size_t W = (size_t)BM * RED_STRIDE;
-        const f4_t sum = *reinterpret_cast<const f4_t *>(red0 + o) +
-                         *reinterpret_cast<const f4_t *>(red0 + W + o) +
-                         *reinterpret_cast<const f4_t *>(red0 + 2 * W + o) +
-                         *reinterpret_cast<const f4_t *>(red0 + 3 * W + o);
+        f4_t sum = *reinterpret_cast<const f4_t *>(red0 + (size_t)half * W + o);
+#pragma unroll
+        for (int q = 1; q < 4; ++q)
+            sum += *reinterpret_cast<const f4_t *>(red0 + (size_t)(2 * q + half) * W + o);
         if (vec_store) {
             *reinterpret_cast<f4_t *>(dst + j) = sum;
         } else {
@@ -304,7 +314,7 @@ hipError_t launch_gemm_int4b64(int M, int K, int N, const void *A, const void *W
                                const void *Sp, float *C, hipStream_t s) {
     const int tiles_m = div_up(M, BM), tiles_n = div_up(N, BN);
     const int xcd_bands = (tiles_n % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL(gemm_int4b64_kernel, dim3(tiles_m * tiles_n), dim3(256), 0, s, M, K, N,
+    hipLaunchKernelGGL(gemm_int4b64_kernel, dim3(tiles_m * tiles_n), dim3(64 * NWAVE), 0, s, M, K, N,
                        tiles_m, tiles_n, xcd_bands, static_cast<const _Float16 *>(A),
                        static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), C);
     return hipGetLastError();
