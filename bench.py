@@ -344,7 +344,7 @@ def main() -> int:
         },
         "decode_roofline": {
             "bound": "hbm",
-            "kernel": "gemv_int4b64_quarter_kernel (decode M=1 K=4096 N=11008)",
+            "kernel": "gemv_int4b64_tile_kernel (decode M=1 K=4096 N=11008)",
             "achieved": dec_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -155,9 +155,10 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
         for (int i = 0; i < 4; ++i)
             dst[i] = *reinterpret_cast<const u4_t *>(A_tile + a_off[i] + (unsigned)kt * (BK * 2));
     };
-    auto zero_a = [&](u4_t (&dst)[4]) {
+    auto store_zero = [&](_Float16 *As) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = u4_t{0, 0, 0, 0};
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<u4_t *>(As + (32 * nh + 8 * i + arow) * AS_STRIDE + 8 * apc) = u4_t{0, 0, 0, 0};
     };
     auto store_a = [&](_Float16 *As, const u4_t (&src)[4]) {
 #pragma unroll
@@ -197,19 +198,22 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     DqParams prm[CF];
     h8_t acur[RF], anxt[RF], bcur[CF], bnxt[CF];
 
+    // Every global load below is unconditional, from a block index clamped
+    // into the quarter (kb0 is valid even for an empty quarter): with no
+    // skipped loads the compiler's in-order count of outstanding loads stays
+    // exact, so a wait only ever covers the data it needs. What a clamped
+    // load brings is never used: a block past the quarter's end gets an
+    // all-zero A tile instead, and adds exactly zero.
+    //
     // prologue: block 0's A in tile 0 and blocks 1 .. RING in flight in the
-    // A ring, B of blocks 0 .. RING - 1 in flight (slots past the quarter's
-    // last block hold that block again, so every slot decodes to finite
-    // weights), step (0, 0) operands ready. Blocks past the quarter's end
-    // stage zero A tiles.
-    if (nb > 0) load_a(an[0], kb0); else zero_a(an[0]);
+    // A ring, B of blocks 0 .. RING - 1 in flight, step (0, 0) operands ready
+    load_a(an[0], kb0);
 #pragma unroll
     for (int d = 0; d < RING; ++d) load_b(bc[d], bp[d], min(kb0 + d, last));
     store_a(a_tile(0), an[0]);
+    if (nb == 0) store_zero(a_tile(0));     // an empty quarter: zero tile (ordered after the store)
 #pragma unroll
-    for (int d = 1; d <= RING; ++d) {
-        if (d < nb) load_a(an[d % RING], kb0 + d); else zero_a(an[d % RING]);
-    }
+    for (int d = 1; d <= RING; ++d) load_a(an[d % RING], min(kb0 + d, last));
     __syncthreads();
 #pragma unroll
     for (int cf = 0; cf < CF; ++cf) prm[cf] = dq_params(bp[0][cf]);
@@ -223,12 +227,12 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
 #pragma unroll
         for (int u = 0; u < RING; ++u) {
             const int i = base + u;
-            // block i + 1's A (loaded RING - 1 blocks ago) into its tile,
-            // which was last read in block i - 3, before the previous
-            // barrier; its ring stage then takes block i + 1 + RING
-            store_a(a_tile((u + 1) % RING), an[(u + 1) % RING]);
-            if (i + 1 + RING < nb) load_a(an[(u + 1) % RING], kb0 + i + 1 + RING);
-            else zero_a(an[(u + 1) % RING]);
+            // block i + 1's A (loaded RING blocks ago) into its tile, which
+            // was last read in block i - 3, before the previous barrier; its
+            // ring stage then takes block i + 1 + RING
+            if (i + 1 < nb) store_a(a_tile((u + 1) % RING), an[(u + 1) % RING]);
+            else store_zero(a_tile((u + 1) % RING));
+            load_a(an[(u + 1) % RING], min(kb0 + i + 1 + RING, last));
             __syncthreads();
             // four MFMA steps; while the matrix cores work on step s the
             // operands of the next step (this block's s + 1, or the next
@@ -266,7 +270,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
             }
             // slot u is free now (its last use was the dequantisation in
             // step 2): refill it with block i + RING
-            if (i + RING < nb) load_b(bc[u], bp[u], kb0 + i + RING);
+            load_b(bc[u], bp[u], min(kb0 + i + RING, last));
         }
     }
 

@@ -320,80 +320,69 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_int4b64_kernel(
     }
 }
 
-// The decode kernel for K <= 4096. One 1024-thread workgroup per CU owns a
-// contiguous run of at most V6_GROUPS channel groups (balanced to within one
-// group). The run is cut into units (group, K-quarter) of two 1 KiB loads
-// each; the 16 waves take units round-robin, so a CU keeps many small,
-// independent load streams in flight (a 28 MB stream needs about 16 waves per
-// CU to approach HBM bandwidth). Each unit's partial sums (per channel and
-// row) go to LDS and the four quarters of a group are added in a fixed order.
-constexpr int V6_WAVES = 16;
-constexpr int V6_GROUPS = 12;                       // groups per workgroup, at most
-constexpr int V6_UNITS = (4 * V6_GROUPS + V6_WAVES - 1) / V6_WAVES;   // per wave
+// The decode kernel for K <= 4096. One 1024-thread workgroup per 32-channel
+// tile: every weight load is one whole 1 KiB record of the tile (64 lanes x
+// 16 contiguous bytes, all lanes active) and every pair load one whole
+// 256-byte pair record, the widest contiguous accesses the packed layout
+// offers. The tile's K-blocks are dealt to the 16 waves round-robin and all
+// of a wave's loads are issued before the activations are staged. For one
+// row two workgroups fit on a CU, so the tiles (about 1.3 per CU for a 7B
+// FFN shape) are all resident at once without a cross-workgroup reduction.
+// Lane (c, h) = (lane % 32, lane / 32) accumulates channel c, K-half h of its
+// blocks; the halves meet with one v_permlane32_swap and the 16 waves'
+// partial sums are added in LDS in a fixed order.
+constexpr int TILE_WAVES = 16;
+constexpr int TILE_RPW = 64 / TILE_WAVES;      // blocks per wave (K <= 4096)
 
 template <int MR>
-__global__ __launch_bounds__(64 * V6_WAVES) void gemv_int4b64_quarter_kernel(
+__global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
     int M, int K, int N, const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ Sp, float *__restrict__ C) {
     extern __shared__ __align__(16) unsigned char lds[];
-    const int nblk = K >> 6;                 // <= 64
+    const int nblk = K >> 6;                 // 1 .. 64
     const int nhb = nblk * 2;
     u4_t *ap = reinterpret_cast<u4_t *>(lds);                                   // [MR][K/8]
     f2_t *hs = reinterpret_cast<f2_t *>(lds + (size_t)MR * K * 2);              // [MR][nhb]
     float *part = reinterpret_cast<float *>(lds + (size_t)MR * K * 2 + (size_t)MR * nhb * 8);
-    // part: [V6_GROUPS][4 quarters][MR][4 channels]
+    // part: [TILE_WAVES][MR][32]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = uniform(tid >> 6);
+    const int t = blockIdx.x;                // 32-channel tile
     const int m0 = blockIdx.y * MR;
-    const int G = (N + 3) >> 2;
-    const long long nwg = gridDim.x;
-    const int gs = (int)((long long)blockIdx.x * G / nwg);
-    const int ge = (int)((long long)(blockIdx.x + 1) * G / nwg);
-    const int nunits = 4 * (ge - gs);
-    const int qblk = (nblk + 3) >> 2;        // blocks per quarter (<= 16)
-
-    const int cc = lane & 3, hh = (lane >> 2) & 1, bb = lane >> 3;
-    const unsigned magic = 0x64646464u;
+    const int c = lane & 31, h = lane >> 5;
 
     // 1. activations for this workgroup (one (row, block, half) per thread)
     u4_t araw[4];
-    const int it = tid;
-    const int ar = it / nhb, ahb = it - ar * nhb;
-    const bool alive = it < MR * nhb && m0 + ar < M;
+    const int ar = tid / nhb, ahb = tid - ar * nhb;
+    const bool alive = tid < MR * nhb && m0 + ar < M;
     {
         const u4_t *src = reinterpret_cast<const u4_t *>(
             A + (size_t)(alive ? m0 + ar : 0) * K + (alive ? ahb : 0) * 32);
 #pragma unroll
         for (int w = 0; w < 4; ++w) araw[w] = alive ? src[w] : u4_t{0u, 0u, 0u, 0u};
     }
-    // 2. every weight and pair load of this wave's units (non-temporal)
-    u4_t wq[V6_UNITS][2];
-    f2_t pr[V6_UNITS][2];
+    // 2. every pair and record load of this wave (non-temporal). Loads are
+    //    unconditional, block index clamped: with no skipped loads the
+    //    compiler's in-order count of outstanding loads stays exact, so each
+    //    block waits only for its own data. Clamped blocks are never used.
+    f2_t pr[TILE_RPW];
+    u4_t wq[TILE_RPW];
 #pragma unroll
-    for (int ui = 0; ui < V6_UNITS; ++ui) {
-        const int u = wave + V6_WAVES * ui;
-        const int g = gs + (u >> 2), qk = u & 3;
-        const int t = g >> 3, q = g & 7;
+    for (int i = 0; i < TILE_RPW; ++i) {
+        const int b = min(wave + TILE_WAVES * i, nblk - 1);
+        pr[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const f2_t *>(Sp + ((size_t)t * nblk + b) * 64 + c * 2));
+    }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int bl = 8 * i + bb;                   // block within the quarter
-            const int b = qk * qblk + bl;
-            if (u < nunits && bl < qblk && b < nblk) {
-                const size_t rec = (size_t)t * nblk + b;
-                wq[ui][i] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u4_t *>(Wp + rec * 1024 + (size_t)(32 * hh + 4 * q + cc) * 16));
-                pr[ui][i] = __builtin_nontemporal_load(
-                    reinterpret_cast<const f2_t *>(Sp + rec * 64 + (4 * q + cc) * 2));
-            } else {
-                wq[ui][i] = u4_t{0u, 0u, 0u, 0u};
-                pr[ui][i] = f2_t{0.f, 0.f};
-            }
-        }
+    for (int i = 0; i < TILE_RPW; ++i) {
+        const int b = min(wave + TILE_WAVES * i, nblk - 1);
+        wq[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const u4_t *>(Wp + ((size_t)t * nblk + b) * 1024) + lane);
     }
     // 3. activations to LDS in decode pair order, with even / odd sums
-    if (it < MR * nhb) {
+    if (tid < MR * nhb) {
         float se = 0.f, so = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -410,61 +399,53 @@ __global__ __launch_bounds__(64 * V6_WAVES) void gemv_int4b64_quarter_kernel(
     }
     __syncthreads();
 
-    // 4. decode, accumulate, reduce each unit over its lanes, park in LDS
+    // 4. decode and accumulate this wave's blocks
+    const unsigned magic = 0x64646464u;
+    float acc[MR];
 #pragma unroll
-    for (int ui = 0; ui < V6_UNITS; ++ui) {
-        const int u = wave + V6_WAVES * ui;
-        if (u >= nunits) break;                          // wave-uniform
-        const int qk = u & 3;
-        float acc[MR];
+    for (int r = 0; r < MR; ++r) acc[r] = 0.f;
 #pragma unroll
-        for (int r = 0; r < MR; ++r) acc[r] = 0.f;
+    for (int i = 0; i < TILE_RPW; ++i) {
+        const int b = wave + TILE_WAVES * i;
+        if (b >= nblk) break;                            // wave-uniform
+        const int hbg = 2 * b + h;
+        const float off = pr[i].x, sc = pr[i].y;
+        const float ce = fmaf(-1024.0f, sc, off);
+        const float co = fmaf(-64.0f, sc, off);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int bl = 8 * i + bb;
-            const int b = qk * qblk + bl;
-            if (bl >= qblk || b >= nblk) continue;
-            const int hbg = 2 * b + hh;
+        for (int r = 0; r < MR; ++r) {
+            float Te = 0.f, To = 0.f;
 #pragma unroll
-            for (int r = 0; r < MR; ++r) {
-                float Te = 0.f, To = 0.f;
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const u4_t av = ap[(size_t)r * (K >> 3) + hbg * 4 + d];
-                    const unsigned word = wq[ui][i][d];
-                    const unsigned y0 = __builtin_amdgcn_perm(magic, word, 0x04020400u);
-                    const unsigned y1 = __builtin_amdgcn_perm(magic, word, 0x04030401u);
-                    Te = dot2(as_h2(y0 & 0xFF0FFF0Fu), as_h2(av.x), Te);
-                    Te = dot2(as_h2(y1 & 0xFF0FFF0Fu), as_h2(av.y), Te);
-                    To = dot2(as_h2(y0 & 0xFFF0FFF0u), as_h2(av.z), To);
-                    To = dot2(as_h2(y1 & 0xFFF0FFF0u), as_h2(av.w), To);
-                }
-                const f2_t sv = hs[(size_t)r * nhb + hbg];
-                const float off = pr[ui][i].x, sc = pr[ui][i].y;
-                const float ce = fmaf(-1024.0f, sc, off);
-                const float co = fmaf(-64.0f, sc, off);
-                acc[r] += fmaf(ce, sv.x, fmaf(co, sv.y, fmaf(sc, Te, sc * 0.0625f * To)));
+            for (int d = 0; d < 4; ++d) {
+                const u4_t av = ap[(size_t)r * (K >> 3) + hbg * 4 + d];
+                const unsigned word = wq[i][d];
+                const unsigned y0 = __builtin_amdgcn_perm(magic, word, 0x04020400u);
+                const unsigned y1 = __builtin_amdgcn_perm(magic, word, 0x04030401u);
+                Te = dot2(as_h2(y0 & 0xFF0FFF0Fu), as_h2(av.x), Te);
+                Te = dot2(as_h2(y1 & 0xFF0FFF0Fu), as_h2(av.y), Te);
+                To = dot2(as_h2(y0 & 0xFFF0FFF0u), as_h2(av.z), To);
+                To = dot2(as_h2(y1 & 0xFFF0FFF0u), as_h2(av.w), To);
             }
+            const f2_t sv = hs[(size_t)r * nhb + hbg];
+            acc[r] += fmaf(ce, sv.x, fmaf(co, sv.y, fmaf(sc, Te, sc * 0.0625f * To)));
         }
-        constexpr int NV = MR;   // 1, 2 or 4
-        int idx;
-        const float total = group_transpose_sum<NV>(acc, lane, idx);
-        constexpr int USED = Log2<NV>::value;
-        const int rest_mask = ((1 << (3 - USED)) - 1) << 3;
-        if ((lane & 4) && (lane & rest_mask) == 0)
-            part[(((u >> 2) * 4 + qk) * MR + idx) * 4 + cc] = total;
+    }
+    // 5. halves meet (lanes c and c + 32), then per-wave channel sums to LDS
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+        float x = acc[r], y = acc[r];
+        swap32(x, y);
+        if (h == 0) part[(wave * MR + r) * 32 + c] = x + y;
     }
     __syncthreads();
 
-    // 5. add the four quarters in a fixed order and store
-    const int ng = ge - gs;
-    if (tid < ng * MR * 4) {
-        const int gl = tid / (MR * 4), rem = tid - gl * (MR * 4);
-        const int r = rem >> 2, c = rem & 3;
-        const int n = 4 * (gs + gl) + c, m = m0 + r;
-        const float *pp = part + (size_t)gl * 4 * MR * 4;
-        const float total = pp[(0 * MR + r) * 4 + c] + pp[(1 * MR + r) * 4 + c] +
-                            pp[(2 * MR + r) * 4 + c] + pp[(3 * MR + r) * 4 + c];
+    // 6. add the eight waves' partial sums in a fixed order and store
+    if (tid < MR * 32) {
+        const int r = tid >> 5, cc = tid & 31;
+        const int n = 32 * t + cc, m = m0 + r;
+        float total = 0.f;
+#pragma unroll
+        for (int w = 0; w < TILE_WAVES; ++w) total += part[(w * MR + r) * 32 + cc];
         if (n < N && m < M) C[(size_t)m * N + n] = total;
     }
 }
@@ -612,15 +593,13 @@ static hipError_t gemv_int4(int M, int K, int N, const void *A, const void *Wp, 
 }
 
 template <int MR>
-static hipError_t gemv_int4_quarter(int M, int K, int N, const void *A, const void *Wp,
-                                    const void *Sp, float *C, hipStream_t s) {
-    const int G = (N + 3) / 4;
-    const int nwg = std::max(cu_count(), div_up(G, V6_GROUPS));
+static hipError_t gemv_int4_tile(int M, int K, int N, const void *A, const void *Wp,
+                                 const void *Sp, float *C, hipStream_t s) {
     const size_t lds = (size_t)MR * K * 2 + (size_t)MR * (K / 32) * sizeof(f2_t) +
-                       (size_t)V6_GROUPS * 4 * MR * 4 * sizeof(float);
-    dim3 grid(nwg, div_up(M, MR));
-    hipLaunchKernelGGL((gemv_int4b64_quarter_kernel<MR>), grid, dim3(64 * V6_WAVES), lds, s, M,
-                       K, N, static_cast<const _Float16 *>(A), static_cast<const uint8_t *>(Wp),
+                       (size_t)TILE_WAVES * MR * 32 * sizeof(float);
+    dim3 grid(div_up(N, 32), div_up(M, MR));
+    hipLaunchKernelGGL((gemv_int4b64_tile_kernel<MR>), grid, dim3(64 * TILE_WAVES), lds, s, M, K,
+                       N, static_cast<const _Float16 *>(A), static_cast<const uint8_t *>(Wp),
                        static_cast<const float *>(Sp), C);
     return hipGetLastError();
 }
@@ -629,9 +608,9 @@ hipError_t launch_gemv_int4b64(int M, int K, int N, const void *A, const void *W
                                const void *Sp, float *C, hipStream_t s) {
     if (K <= 4096) {
         switch (M >= 4 ? 4 : (M >= 2 ? 2 : 1)) {
-        case 4: return gemv_int4_quarter<4>(M, K, N, A, Wp, Sp, C, s);
-        case 2: return gemv_int4_quarter<2>(M, K, N, A, Wp, Sp, C, s);
-        default: return gemv_int4_quarter<1>(M, K, N, A, Wp, Sp, C, s);
+        case 4: return gemv_int4_tile<4>(M, K, N, A, Wp, Sp, C, s);
+        case 2: return gemv_int4_tile<2>(M, K, N, A, Wp, Sp, C, s);
+        default: return gemv_int4_tile<1>(M, K, N, A, Wp, Sp, C, s);
         }
     }
     switch (M >= 4 ? 4 : (M >= 2 ? 2 : 1)) {
