@@ -169,17 +169,29 @@ def test_int4_packed_layout_golden():
 
 
 def test_w4a8_packed_word_order_golden():
-    """Each word of a W4A8 record holds code k0+i in the low and k0+4+i in the
-    high nibble of byte i, so nibble masks give codes in natural k order."""
-    K, N = 64, 1
-    codes = np.arange(64) % 16
-    wc = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)[None, :]
-    pc = np.zeros((1, 1, 2), np.float32)
+    """A W4A8 record holds 32 channels x 64 codes; piece 32 h + c of channel c
+    carries, for s = 0, 1, the codes of k = 32 s + 16 h + [0, 16) in bytes
+    [8 s, 8 s + 8), and byte i of word w (k0 = 32 s + 16 h + 8 w) holds code
+    k0 + i in the low and k0 + 4 + i in the high nibble, so nibble masks give
+    codes in natural k order."""
+    K, N = 64, 40
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 16, size=(N, K))
+    wc = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    pc = np.zeros((N, 1, 2), np.float32)
     wp, _ = Q.qgemm_pack_weights(K, N, "w4a8", wc, pc)
-    rec = wp[:32]
-    lo = rec & 15
-    hi = rec >> 4
-    for w in range(8):
-        for i in range(4):
-            assert lo[4 * w + i] == codes[8 * w + i]
-            assert hi[4 * w + i] == codes[8 * w + 4 + i]
+    assert wp.nbytes >= 2 * 1024
+    for n in range(N):
+        g, c = divmod(n, 32)
+        rec = wp[g * 1024:(g + 1) * 1024]
+        for h in range(2):
+            piece = rec[(32 * h + c) * 16:(32 * h + c + 1) * 16]
+            for s in range(2):
+                for w in range(2):
+                    k0 = 32 * s + 16 * h + 8 * w
+                    for i in range(4):
+                        byte = int(piece[8 * s + 4 * w + i])
+                        assert byte & 15 == codes[n, k0 + i]
+                        assert byte >> 4 == codes[n, k0 + 4 + i]
+    # channels 40 .. 63 of the second record are padding
+    assert not np.any(wp[1024:2048].reshape(2, 32, 16)[:, 8:, :])

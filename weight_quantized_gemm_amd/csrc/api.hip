@@ -84,14 +84,14 @@ static qgemm_status launched(hipError_t e) {
 static qgemm_status run_w4a8(int M, int K, int N, const Geometry &g, const void *A,
                              const void *Bq, const void *scales, float *C, void *ws,
                              hipStream_t s, int32_t *D_debug) {
-    W4A8Workspace w = w4a8_workspace(M, g.Kp);
+    W4A8Workspace w = w4a8_workspace(M, K);
     uint8_t *base = static_cast<uint8_t *>(ws);
     int8_t *qa = reinterpret_cast<int8_t *>(base + w.qa_off);
     float *sa = reinterpret_cast<float *>(base + w.sa_off);
     int32_t *S = reinterpret_cast<int32_t *>(base + w.S_off);
-    hipError_t e = launch_w4a8_actquant(M, K, g.Kp, A, qa, sa, S, s);
+    hipError_t e = launch_w4a8_actquant(M, K, w.qa_stride, A, qa, sa, S, s);
     if (e != hipSuccess) return QGEMM_ERR_LAUNCH;
-    return launched(launch_w4a8_gemm(M, K, N, qa, sa, S, Bq, scales, C, D_debug, s));
+    return launched(launch_w4a8_gemm(M, K, N, w.qa_stride, qa, sa, S, Bq, scales, C, D_debug, s));
 }
 
 static qgemm_status dispatch(int M, int K, int N, qgemm_format f, const Geometry &g,
@@ -137,7 +137,7 @@ qgemm_status qgemm_run_ws(int M, int K, int N, qgemm_format f, const void *A,
     if (f == QGEMM_W4A8) {
         if (!workspace) return QGEMM_ERR_NULL;
         if (!aligned16(workspace)) return QGEMM_ERR_ALIGN;
-        if (ws_bytes < w4a8_workspace(M, g.Kp).bytes) return QGEMM_ERR_SIZE;
+        if (ws_bytes < w4a8_workspace(M, K).bytes) return QGEMM_ERR_SIZE;
     }
     st = check_device();
     if (st != QGEMM_OK) return st;
@@ -157,7 +157,7 @@ qgemm_status qgemm_run(int M, int K, int N, qgemm_format f, const void *A, const
     if (f != QGEMM_W4A8)
         return dispatch(M, K, N, f, g, A, Bq, scales, C, nullptr, s);
     // W4A8 scratch, allocated and released in stream order.
-    const size_t bytes = w4a8_workspace(M, g.Kp).bytes;
+    const size_t bytes = w4a8_workspace(M, K).bytes;
     void *ws = nullptr;
     if (hipMallocAsync(&ws, bytes, s) != hipSuccess || !ws) {
         (void)hipGetLastError();
@@ -181,7 +181,7 @@ qgemm_status qgemm_w4a8_debug(int M, int K, int N, const void *A, const void *Bq
     if (st != QGEMM_OK || empty) return st;
     if (!qa || !sa || !S || !D || !workspace) return QGEMM_ERR_NULL;
     if (!aligned16(workspace) || !aligned16(D)) return QGEMM_ERR_ALIGN;
-    W4A8Workspace w = w4a8_workspace(M, g.Kp);
+    W4A8Workspace w = w4a8_workspace(M, K);
     if (ws_bytes < w.bytes) return QGEMM_ERR_SIZE;
     st = check_device();
     if (st != QGEMM_OK) return st;
@@ -190,7 +190,7 @@ qgemm_status qgemm_w4a8_debug(int M, int K, int N, const void *A, const void *Bq
     st = run_w4a8(M, K, N, g, A, Bq, scales, C, workspace, s, D);
     if (st != QGEMM_OK) return st;
     const uint8_t *base = static_cast<const uint8_t *>(workspace);
-    if (hipMemcpy2DAsync(qa, (size_t)K, base + w.qa_off, (size_t)g.Kp, (size_t)K, (size_t)M,
+    if (hipMemcpy2DAsync(qa, (size_t)K, base + w.qa_off, (size_t)w.qa_stride, (size_t)K, (size_t)M,
                          hipMemcpyDeviceToDevice, s) != hipSuccess ||
         hipMemcpyAsync(sa, base + w.sa_off, (size_t)M * sizeof(float),
                        hipMemcpyDeviceToDevice, s) != hipSuccess ||

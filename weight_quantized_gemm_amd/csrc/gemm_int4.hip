@@ -155,15 +155,13 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
         for (int i = 0; i < 4; ++i)
             dst[i] = *reinterpret_cast<const u4_t *>(A_tile + a_off[i] + (unsigned)kt * (BK * 2));
     };
-    auto store_zero = [&](_Float16 *As) {
+    // every word ANDed with a uniform mask (all ones, or zero for a block
+    // past the quarter's end): no branch, so no merge point for the
+    // compiler's count of outstanding loads
+    auto store_a = [&](_Float16 *As, const u4_t (&src)[4], unsigned mask) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<u4_t *>(As + (32 * nh + 8 * i + arow) * AS_STRIDE + 8 * apc) = u4_t{0, 0, 0, 0};
-    };
-    auto store_a = [&](_Float16 *As, const u4_t (&src)[4]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<u4_t *>(As + (32 * nh + 8 * i + arow) * AS_STRIDE + 8 * apc) = src[i];
+            *reinterpret_cast<u4_t *>(As + (32 * nh + 8 * i + arow) * AS_STRIDE + 8 * apc) = src[i] & mask;
     };
     auto read_a = [&](const _Float16 *As, int s, h8_t (&af)[RF]) {
 #pragma unroll
@@ -210,8 +208,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     load_a(an[0], kb0);
 #pragma unroll
     for (int d = 0; d < RING; ++d) load_b(bc[d], bp[d], min(kb0 + d, last));
-    store_a(a_tile(0), an[0]);
-    if (nb == 0) store_zero(a_tile(0));     // an empty quarter: zero tile (ordered after the store)
+    store_a(a_tile(0), an[0], nb > 0 ? ~0u : 0u);
 #pragma unroll
     for (int d = 1; d <= RING; ++d) load_a(an[d % RING], min(kb0 + d, last));
     __syncthreads();
@@ -230,8 +227,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
             // block i + 1's A (loaded RING blocks ago) into its tile, which
             // was last read in block i - 3, before the previous barrier; its
             // ring stage then takes block i + 1 + RING
-            if (i + 1 < nb) store_a(a_tile((u + 1) % RING), an[(u + 1) % RING]);
-            else store_zero(a_tile((u + 1) % RING));
+            store_a(a_tile((u + 1) % RING), an[(u + 1) % RING], i + 1 < nb ? ~0u : 0u);
             load_a(an[(u + 1) % RING], min(kb0 + i + 1 + RING, last));
             __syncthreads();
             // four MFMA steps; while the matrix cores work on step s the

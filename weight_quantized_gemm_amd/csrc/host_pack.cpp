@@ -59,10 +59,11 @@ qgemm_status geometry(int K, int N, qgemm_format f, Geometry *g) {
     return QGEMM_OK;
 }
 
-W4A8Workspace w4a8_workspace(int M, int Kp) {
+W4A8Workspace w4a8_workspace(int M, int K) {
     W4A8Workspace w;
+    w.qa_stride = (int)round_up((size_t)K, 128);
     w.qa_off = 0;
-    w.sa_off = round_up((size_t)M * Kp, kPackAlign);
+    w.sa_off = round_up((size_t)M * w.qa_stride, kPackAlign);
     w.S_off = w.sa_off + round_up((size_t)M * sizeof(float), kPackAlign);
     w.bytes = w.S_off + round_up((size_t)M * sizeof(int32_t), kPackAlign);
     return w;
@@ -138,7 +139,7 @@ qgemm_status qgemm_workspace_size(int M, int K, int N, qgemm_format f, size_t *b
     if (st != QGEMM_OK) return st;
     if (M < 0 || M > (1 << 24)) return QGEMM_ERR_SHAPE;
     if (!bytes) return QGEMM_ERR_NULL;
-    *bytes = (f == QGEMM_W4A8 && M > 0) ? w4a8_workspace(M, g.Kp).bytes : 0;
+    *bytes = (f == QGEMM_W4A8 && M > 0) ? w4a8_workspace(M, K).bytes : 0;
     return QGEMM_OK;
 }
 
@@ -243,21 +244,27 @@ qgemm_status qgemm_pack_weights(int K, int N, qgemm_format f, const void *w_cano
         }
         break;
     case QGEMM_W4A8: {
+        // 1 KiB records (g, kc) of 32 channels x 64 codes; piece 32 h + c
+        // (16 bytes) holds channel 32 g + c's codes of k = 64 kc + 32 s +
+        // 16 h + [0, 16) for s = 0, 1 (8 bytes each); in word w (k0 = 64 kc +
+        // 32 s + 16 h + 8 w) byte i holds q[k0 + i] | q[k0 + 4 + i] << 4.
         const int nkc = g.Kp / 64;
         const size_t row = (size_t)K / 2;
         for (int n = 0; n < N; ++n) {
             const uint8_t *src = wc + (size_t)n * row;
             const int grp = n >> 5, c = n & 31;
             for (int kc = 0; kc < nkc; ++kc) {
-                uint8_t *rec = wp + (((size_t)grp * nkc + kc) * 32 + c) * 32;
-                for (int w = 0; w < 8; ++w) {
-                    const int k0 = kc * 64 + w * 8;
-                    for (int i = 0; i < 4; ++i) {
-                        const uint8_t lo = (k0 + i < K) ? nib(src, k0 + i) : 0;
-                        const uint8_t hi = (k0 + 4 + i < K) ? nib(src, k0 + 4 + i) : 0;
-                        rec[w * 4 + i] = (uint8_t)(lo | (hi << 4));
-                    }
-                }
+                uint8_t *rec = wp + ((size_t)grp * nkc + kc) * 1024;
+                for (int h = 0; h < 2; ++h)
+                    for (int sv = 0; sv < 2; ++sv)
+                        for (int w = 0; w < 2; ++w) {
+                            const int k0 = 64 * kc + 32 * sv + 16 * h + 8 * w;
+                            for (int i = 0; i < 4; ++i) {
+                                const uint8_t lo = (k0 + i < K) ? nib(src, k0 + i) : 0;
+                                const uint8_t hi = (k0 + 4 + i < K) ? nib(src, k0 + 4 + i) : 0;
+                                rec[(32 * h + c) * 16 + 8 * sv + 4 * w + i] = (uint8_t)(lo | (hi << 4));
+                            }
+                        }
             }
             spf[(size_t)n * 2 + 0] = pairs_canonical[(size_t)n * 2 + 0];
             spf[(size_t)n * 2 + 1] = pairs_canonical[(size_t)n * 2 + 1];
@@ -318,16 +325,18 @@ qgemm_status qgemm_unpack_weights(int K, int N, qgemm_format f, const void *w_pa
             std::memset(dst, 0, row);
             const int grp = n >> 5, c = n & 31;
             for (int kc = 0; kc < nkc; ++kc) {
-                const uint8_t *rec = wp + (((size_t)grp * nkc + kc) * 32 + c) * 32;
-                for (int w = 0; w < 8; ++w) {
-                    const int k0 = kc * 64 + w * 8;
-                    for (int i = 0; i < 4; ++i) {
-                        const uint8_t byte = rec[w * 4 + i];
-                        const int ka = k0 + i, kb = k0 + 4 + i;
-                        if (ka < K) dst[ka >> 1] |= (uint8_t)((byte & 15) << ((ka & 1) * 4));
-                        if (kb < K) dst[kb >> 1] |= (uint8_t)((byte >> 4) << ((kb & 1) * 4));
-                    }
-                }
+                const uint8_t *rec = wp + ((size_t)grp * nkc + kc) * 1024;
+                for (int h = 0; h < 2; ++h)
+                    for (int sv = 0; sv < 2; ++sv)
+                        for (int w = 0; w < 2; ++w) {
+                            const int k0 = 64 * kc + 32 * sv + 16 * h + 8 * w;
+                            for (int i = 0; i < 4; ++i) {
+                                const uint8_t byte = rec[(32 * h + c) * 16 + 8 * sv + 4 * w + i];
+                                const int ka = k0 + i, kb = k0 + 4 + i;
+                                if (ka < K) dst[ka >> 1] |= (uint8_t)((byte & 15) << ((ka & 1) * 4));
+                                if (kb < K) dst[kb >> 1] |= (uint8_t)((byte >> 4) << ((kb & 1) * 4));
+                            }
+                        }
             }
             pairs_canonical[(size_t)n * 2 + 0] = spf[(size_t)n * 2 + 0];
             pairs_canonical[(size_t)n * 2 + 1] = spf[(size_t)n * 2 + 1];

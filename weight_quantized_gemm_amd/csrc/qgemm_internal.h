@@ -32,12 +32,16 @@ constexpr size_t kPackAlign = 256;
 // INT8_B0, Kp = roundup(K, 64), Np = roundup(N, 4):
 //   weights: [Np][Kp] bytes (canonical rows, zero padded);
 //   pairs:   [Np][2] floats.
-// W4A8, Kp = roundup(K, 64), Np = roundup(N, 32):
-//   weights: 32-byte records, record (g, kc, c) at ((g * (Kp/64) + kc) * 32 + c) * 32
-//            for channel 32 g + c and k in [64 kc, 64 kc + 64); word w of the
-//            record (k0 = 64 kc + 8 w) has byte i = q[k0 + i] | q[k0 + 4 + i] << 4,
-//            so masking a word with 0x0F0F0F0F / shifting by 4 yields codes of
-//            k0..k0+3 / k0+4..k0+7 in natural order as int8.
+// W4A8, Kp = roundup(K, 64), nkc = Kp / 64, Np = roundup(N, 32):
+//   weights: 1 KiB records, record (g, kc) at (g * nkc + kc) * 1024 for the
+//            channels 32 g .. 32 g + 31 and k in [64 kc, 64 kc + 64); its
+//            16-byte piece 32 h + c belongs to channel 32 g + c and holds, for
+//            s = 0, 1, the codes of k = 64 kc + 32 s + 16 h + [0, 16) in bytes
+//            [8 s, 8 s + 8): byte i of word w (k0 = 64 kc + 32 s + 16 h + 8 w)
+//            is q[k0 + i] | q[k0 + 4 + i] << 4, so masking a word with
+//            0x0F0F0F0F / shifting it by 4 gives the codes of k0..k0+3 /
+//            k0+4..k0+7 in natural order as int8. Piece order is the lane order
+//            of a 32 x 32 x 32 int8 MFMA operand (lane = 32 h + c).
 //   pairs:   [Np][2] floats.
 // F32: weights = B float [K][N] unchanged; no pairs.
 // ---------------------------------------------------------------------------
@@ -68,16 +72,20 @@ hipError_t launch_gemm_int8b0(int M, int K, int N, const void *A, const void *Wp
                               const void *Sp, float *C, hipStream_t s);
 hipError_t launch_gemm_f32(int M, int K, int N, const float *A, const float *B,
                            float *C, hipStream_t s);
-// W4A8: qa [M][Kp] int8, sa [M] float, S [M] int32 live in `ws`.
-hipError_t launch_w4a8_actquant(int M, int K, int Kp, const void *A, int8_t *qa,
+// W4A8: qa [M][Kq] int8 (Kq = roundup(K, 128)), sa [M] float, S [M] int32
+// live in the workspace.
+hipError_t launch_w4a8_actquant(int M, int K, int Kq, const void *A, int8_t *qa,
                                 float *sa, int32_t *S, hipStream_t s);
-hipError_t launch_w4a8_gemm(int M, int K, int N, const int8_t *qa, const float *sa,
+hipError_t launch_w4a8_gemm(int M, int K, int N, int Kq, const int8_t *qa, const float *sa,
                             const int32_t *S, const void *Wp, const void *Sp,
                             float *C, int32_t *D_debug, hipStream_t s);
 
+// W4A8 scratch: qa [M][qa_stride] int8 (qa_stride = roundup(K, 128), zero
+// past K), sa [M] float, S [M] int32.
 struct W4A8Workspace {
+    int qa_stride;
     size_t qa_off, sa_off, S_off, bytes;
 };
-W4A8Workspace w4a8_workspace(int M, int Kp);
+W4A8Workspace w4a8_workspace(int M, int K);
 
 }  // namespace qg

@@ -19,9 +19,84 @@
 namespace qg {
 
 // ---------------------------------------------------------------------------
-// Activation quantisation: one 256-thread workgroup per row.
+// Activation quantisation: one 256-thread workgroup per row. The row of qa
+// has Kq = roundup(K, 128) bytes, zero past K, so the GEMM can stage 128-wide
+// K slices without bounds cases.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void w4a8_actquant_kernel(int M, int K, int Kp,
+__device__ __forceinline__ int8_t quant1(float a, float s) {
+    float r = rintf(a / s);                 // IEEE division, ties to even
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int8_t)(int)r;
+}
+
+__device__ __forceinline__ float block_max(float v, float *red4) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    if ((threadIdx.x & 63) == 0) red4[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(red4[0], red4[1]), fmaxf(red4[2], red4[3]));
+}
+
+__device__ __forceinline__ void block_sum_store(int v, int *red4, int32_t *dst) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    if ((threadIdx.x & 63) == 0) red4[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) *dst = red4[0] + red4[1] + red4[2] + red4[3];
+}
+
+// K % 8 == 0 and K <= 2048 * NCH: the row stays in registers between the
+// maximum and the quantisation (NCH 8-element chunks per thread).
+template <int NCH>
+__global__ __launch_bounds__(256) void w4a8_actquant_reg_kernel(int K, int Kq,
+                                                                const _Float16 *__restrict__ A,
+                                                                int8_t *__restrict__ qa,
+                                                                float *__restrict__ sa,
+                                                                int32_t *__restrict__ S) {
+    __shared__ float red_f[4];
+    __shared__ int red_i[4];
+    const int m = blockIdx.x;
+    const int tid = threadIdx.x;
+    const _Float16 *row = A + (size_t)m * K;
+    int8_t *qrow = qa + (size_t)m * Kq;
+
+    h8_t v[NCH];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int k = (tid + 256 * i) * 8;
+        if (k < K) {
+            v[i] = *reinterpret_cast<const h8_t *>(row + k);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[i][e]));
+        }
+    }
+    amax = block_max(amax, red_f);
+    const float s = amax / 127.0f;           // IEEE division, one rounding
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int k = (tid + 256 * i) * 8;
+        if (k >= Kq) continue;
+        unsigned lo = 0u, hi = 0u;
+        if (k < K && amax != 0.0f) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int qi = quant1((float)v[i][e], s);
+                sum += qi;
+                const unsigned byte = (unsigned)(qi & 0xff);
+                if (e < 4) lo |= byte << (8 * e);
+                else hi |= byte << (8 * (e - 4));
+            }
+        }
+        *reinterpret_cast<u2_t *>(qrow + k) = u2_t{lo, hi};
+    }
+    if (tid == 0) sa[m] = amax != 0.0f ? s : 0.0f;
+    block_sum_store(sum, red_i, S + m);
+}
+
+// Any even K: two passes over the row, element by element.
+__global__ __launch_bounds__(256) void w4a8_actquant_kernel(int K, int Kq,
                                                             const _Float16 *__restrict__ A,
                                                             int8_t *__restrict__ qa,
                                                             float *__restrict__ sa,
@@ -31,99 +106,148 @@ __global__ __launch_bounds__(256) void w4a8_actquant_kernel(int M, int K, int Kp
     const int m = blockIdx.x;
     const int tid = threadIdx.x;
     const _Float16 *row = A + (size_t)m * K;
-    int8_t *qrow = qa + (size_t)m * Kp;
-    const bool vec = (K & 7) == 0;
-
+    int8_t *qrow = qa + (size_t)m * Kq;
     float amax = 0.0f;
-    if (vec) {
-        for (int k = tid * 8; k < K; k += 2048) {
-            const h8_t v = *reinterpret_cast<const h8_t *>(row + k);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[e]));
-        }
-    } else {
-        for (int k = tid; k < K; k += 256) amax = fmaxf(amax, fabsf((float)row[k]));
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-    if ((tid & 63) == 0) red_f[tid >> 6] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
-
-    const float s = amax / 127.0f;   // IEEE division, one rounding
+    for (int k = tid; k < K; k += 256) amax = fmaxf(amax, fabsf((float)row[k]));
+    amax = block_max(amax, red_f);
+    const float s = amax / 127.0f;
     int sum = 0;
-    if (vec) {
-        for (int k = tid * 8; k < Kp; k += 2048) {
-            unsigned lo = 0u, hi = 0u;
-            if (k < K && amax != 0.0f) {
-                const h8_t v = *reinterpret_cast<const h8_t *>(row + k);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float r = rintf((float)v[e] / s);
-                    r = fminf(fmaxf(r, -127.0f), 127.0f);
-                    const int qi = (int)r;
-                    sum += qi;
-                    const unsigned byte = (unsigned)(qi & 0xff);
-                    if (e < 4) lo |= byte << (8 * e);
-                    else hi |= byte << (8 * (e - 4));
-                }
-            }
-            *reinterpret_cast<u2_t *>(qrow + k) = u2_t{lo, hi};
-        }
-    } else {
-        for (int k = tid; k < Kp; k += 256) {
-            int qi = 0;
-            if (k < K && amax != 0.0f) {
-                float r = rintf((float)row[k] / s);
-                r = fminf(fmaxf(r, -127.0f), 127.0f);
-                qi = (int)r;
-            }
-            sum += qi;
-            qrow[k] = (int8_t)qi;
-        }
+    for (int k = tid; k < Kq; k += 256) {
+        int qi = 0;
+        if (k < K && amax != 0.0f) qi = quant1((float)row[k], s);
+        sum += qi;
+        qrow[k] = (int8_t)qi;
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-    if ((tid & 63) == 0) red_i[tid >> 6] = sum;
-    __syncthreads();
-    if (tid == 0) {
-        sa[m] = amax != 0.0f ? s : 0.0f;
-        S[m] = red_i[0] + red_i[1] + red_i[2] + red_i[3];
-    }
+    if (tid == 0) sa[m] = amax != 0.0f ? s : 0.0f;
+    block_sum_store(sum, red_i, S + m);
 }
 
-hipError_t launch_w4a8_actquant(int M, int K, int Kp, const void *A, int8_t *qa, float *sa,
+hipError_t launch_w4a8_actquant(int M, int K, int Kq, const void *A, int8_t *qa, float *sa,
                                 int32_t *S, hipStream_t s) {
-    hipLaunchKernelGGL(w4a8_actquant_kernel, dim3(M), dim3(256), 0, s, M, K, Kp,
-                       static_cast<const _Float16 *>(A), qa, sa, S);
+    const _Float16 *a = static_cast<const _Float16 *>(A);
+    if ((K & 7) == 0 && K <= 2048)
+        hipLaunchKernelGGL(w4a8_actquant_reg_kernel<1>, dim3(M), dim3(256), 0, s, K, Kq, a, qa, sa, S);
+    else if ((K & 7) == 0 && K <= 4096)
+        hipLaunchKernelGGL(w4a8_actquant_reg_kernel<2>, dim3(M), dim3(256), 0, s, K, Kq, a, qa, sa, S);
+    else
+        hipLaunchKernelGGL(w4a8_actquant_kernel, dim3(M), dim3(256), 0, s, K, Kq, a, qa, sa, S);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// int8 GEMM: 128 x 128 tile per 256-thread workgroup, K step 64 bytes; four
-// waves split the tile 2 x 2, each 64 x 64 with v_mfma_i32_32x32x32_i8.
+// int8 GEMM. A 512-thread workgroup owns a 128 x 256 tile of C; wave
+// (wm, wn) owns the 64 x 64 block (rows 64 wm, columns 64 wn) and runs every
+// K step with v_mfma_i32_32x32x32_i8 (2 x 2 accumulator tiles).
+//  - qa is staged in LDS 128 K-columns (one 128-byte run per row) at a time,
+//    four stages deep, loaded three stages ahead through a register ring;
+//    one barrier per stage;
+//  - a K-block of a 32-channel weight record is one contiguous 1 KiB load
+//    already in operand lane order, loaded three stages ahead; the int4
+//    codes become int8 operands with one mask (and one shift) per word;
+//  - every global load is unconditional with clamped indices (rows past M,
+//    channels past N, stages past the end read valid data that is never
+//    stored or, for padded stages, meets an all-zero A tile), which keeps
+//    the compiler's in-order count of outstanding loads exact;
+//  - the epilogue applies C = sa * (scale * D + offset * S) with the row
+//    scales and sums staged in LDS.
+// Lane (r, h) = (lane % 32, lane / 32) holds K-elements 32 s + 16 h .. +15 of
+// each 64-wide block in step s for its A row and B column alike.
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int TM = 128, TN = 128, TK = 64;
-constexpr int ROW = TK + 16;   // bytes per LDS row; 80-byte rows spread the banks
+constexpr int WBM = 128, WBN = 256, WSK = 128;
+constexpr int WNW = 8;                    // waves: 2 (rows) x 4 (columns)
+constexpr int WAROW = WSK + 16;           // bytes per LDS row of an A stage (144)
+constexpr int WRING = 4;                  // stages: LDS A tiles = A and B register ring slots
+constexpr size_t WAS_BYTES = (size_t)WBM * WAROW;
+}
+
+__device__ __forceinline__ i4_t unpack_codes(unsigned w0, unsigned w1) {
+    const unsigned m = 0x0F0F0F0Fu;
+    return i4_t{(int)(w0 & m), (int)((w0 >> 4) & m), (int)(w1 & m), (int)((w1 >> 4) & m)};
 }
 
 template <bool DEBUG_D>
-__global__ __launch_bounds__(256) void w4a8_gemm_kernel(
-    int M, int N, int Kp, const int8_t *__restrict__ qa, const float *__restrict__ sa,
-    const int32_t *__restrict__ S, const uint8_t *__restrict__ Wp, const f2_t *__restrict__ Sp,
-    float *__restrict__ C, int32_t *__restrict__ D) {
-    __shared__ __align__(16) int8_t As[TM * ROW];
-    __shared__ __align__(16) int8_t Bs[TN * ROW];
+__global__ __launch_bounds__(64 * WNW) void w4a8_gemm_kernel(
+    int M, int N, int Kq, int nkc, int tiles_n, int xcd_bands, const int8_t *__restrict__ qa,
+    const float *__restrict__ sa, const int32_t *__restrict__ S, const uint8_t *__restrict__ Wp,
+    const f2_t *__restrict__ Sp, float *__restrict__ C, int32_t *__restrict__ D) {
+    __shared__ __align__(16) int8_t As[WRING * WAS_BYTES];
+    __shared__ float sa_s[WBM];
+    __shared__ int S_s[WBM];
+
+    // ---- tile of this workgroup (XCD x = L % 8 owns a band of column tiles) ----
+    const int L = blockIdx.x;
+    int tm, tn;
+    if (xcd_bands) {
+        const int bw = tiles_n / 8;
+        const int j = L / 8;
+        tn = (L % 8) * bw + j % bw;
+        tm = j / bw;
+    } else {
+        tm = L / tiles_n;
+        tn = L % tiles_n;
+    }
+    const int m0 = tm * WBM, n0 = tn * WBN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int m0 = blockIdx.y * TM;
-    const int n0 = blockIdx.x * TN;
-    const int nkc = Kp >> 6;
-    const int Np = (N + 31) & ~31;
+    const int wave = uniform(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int r = lane & 31, h = lane >> 5;
+    const int nst = Kq / WSK;                          // >= 1
+    const int nsteps = (nst + WRING - 1) / WRING * WRING;
+    const int ntiles_b = (N + 31) / 32;
+
+    if (tid < WBM) {
+        const int gm = min(m0 + tid, M - 1);
+        sa_s[tid] = sa[gm];
+        S_s[tid] = S[gm];
+    }
+
+    // A loader role: 2 x (8 lanes x 16 bytes per row), rows tid / 8 and 64 + tid / 8
+    size_t a_off[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int idx = tid + 512 * i;
+        a_off[i] = (size_t)min(m0 + (idx >> 3), M - 1) * Kq + (size_t)(idx & 7) * 16;
+    }
+    auto load_a = [&](u4_t (&dst)[2], int st) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            dst[i] = *reinterpret_cast<const u4_t *>(qa + a_off[i] + (size_t)st * WSK);
+    };
+    auto a_tile = [&](int slot) { return As + (size_t)slot * WAS_BYTES; };
+    auto store_a = [&](int8_t *T, const u4_t (&src)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int idx = tid + 512 * i;
+            *reinterpret_cast<u4_t *>(T + (idx >> 3) * WAROW + (idx & 7) * 16) = src[i];
+        }
+    };
+    // the same, with every word ANDed with a uniform mask (all ones, or zero
+    // for a stage past the end): no branch, so no merge point for the
+    // compiler's count of outstanding loads
+    auto store_a_masked = [&](int8_t *T, const u4_t (&src)[2], unsigned mask) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int idx = tid + 512 * i;
+            *reinterpret_cast<u4_t *>(T + (idx >> 3) * WAROW + (idx & 7) * 16) = src[i] & mask;
+        }
+    };
+    // B: records of the wave's two 32-channel tiles, two K-blocks per stage
+    size_t b_rec0[2];
+#pragma unroll
+    for (int cf = 0; cf < 2; ++cf)
+        b_rec0[cf] = (size_t)min((n0 + 64 * wn) / 32 + cf, ntiles_b - 1) * nkc;
+    auto load_b = [&](u4_t (&dst)[2][2], int st) {
+#pragma unroll
+        for (int cf = 0; cf < 2; ++cf)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const size_t rec = b_rec0[cf] + min(2 * st + kk, nkc - 1);
+                dst[cf][kk] = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(Wp + rec * 1024) + lane);
+            }
+    };
 
     i16_t acc[2][2];
 #pragma unroll
@@ -133,90 +257,92 @@ __global__ __launch_bounds__(256) void w4a8_gemm_kernel(
 #pragma unroll
             for (int j = 0; j < 16; ++j) acc[a][b][j] = 0;
 
-    // B loader role: channel tid / 2 of the tile, half tid % 2 of its 32-byte record.
-    const int bn = tid >> 1, bh = tid & 1;
-    const int gn = n0 + bn;
+    u4_t an[WRING][2];
+    u4_t bq[WRING][2][2];
 
-    for (int kc = 0; kc < nkc; ++kc) {
+    // prologue: stage 0 in LDS tile 0, stages 1 .. WRING of A and 0 .. WRING - 1
+    // of B in flight (clamped past the end: never used)
+    load_a(an[0], 0);
 #pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int idx = it * 256 + tid;
-            const int r = idx >> 2, c16 = (idx & 3) * 16;
-            const int gm = m0 + r;
-            u4_t v = {0u, 0u, 0u, 0u};
-            if (gm < M)
-                v = *reinterpret_cast<const u4_t *>(qa + (size_t)gm * Kp + (size_t)kc * 64 + c16);
-            *reinterpret_cast<u4_t *>(As + r * ROW + c16) = v;
+    for (int d = 0; d < WRING; ++d) load_b(bq[d], min(d, nst - 1));
+    store_a(a_tile(0), an[0]);
+#pragma unroll
+    for (int d = 1; d <= WRING; ++d) load_a(an[d % WRING], min(d, nst - 1));
+    // Let the prologue's loads land before the loop: the loop header merges
+    // this path with the back edge, and the compiler may have issued these
+    // loads in any order, so without this wait it would count the slot the
+    // loop reads first as the newest load and drain everything every stage.
+    __builtin_amdgcn_s_waitcnt(0);
+
+    for (int base = 0; base < nsteps; base += WRING) {
+#pragma unroll
+        for (int u = 0; u < WRING; ++u) {
+            const int i = base + u;
+            // stage i + 1's A into its tile (last read in stage i - 3, before
+            // the previous barrier), then its ring slot takes stage i + 1 + WRING
+            store_a_masked(a_tile((u + 1) % WRING), an[(u + 1) % WRING], i + 1 < nst ? ~0u : 0u);
+            load_a(an[(u + 1) % WRING], min(i + 1 + WRING, nst - 1));
+            __syncthreads();
+            const int8_t *T = a_tile(u);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    i4_t af[2], bf[2];
+#pragma unroll
+                    for (int rf = 0; rf < 2; ++rf)
+                        af[rf] = *reinterpret_cast<const i4_t *>(
+                            T + (64 * wm + 32 * rf + r) * WAROW + 64 * kk + 32 * s + 16 * h);
+#pragma unroll
+                    for (int cf = 0; cf < 2; ++cf)
+                        bf[cf] = unpack_codes(bq[u][cf][kk][2 * s], bq[u][cf][kk][2 * s + 1]);
+#pragma unroll
+                    for (int rf = 0; rf < 2; ++rf)
+#pragma unroll
+                        for (int cf = 0; cf < 2; ++cf)
+                            acc[rf][cf] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[rf], bf[cf], acc[rf][cf], 0, 0, 0);
+                }
+            // B slot u is free: refill it with stage i + WRING
+            load_b(bq[u], min(i + WRING, nst - 1));
         }
-        {
-            u4_t v = {0u, 0u, 0u, 0u};
-            if (gn < Np) {
-                const int g = gn >> 5, c = gn & 31;
-                v = *reinterpret_cast<const u4_t *>(
-                    Wp + (((size_t)g * nkc + kc) * 32 + c) * 32 + bh * 16);
-            }
-            // each word -> codes of k0..k0+3 and k0+4..k0+7 as int8 (natural order)
-            u4_t lo, hi;
-#pragma unroll
-            for (int wi = 0; wi < 4; ++wi) {
-                lo[wi] = v[wi] & 0x0F0F0F0Fu;
-                hi[wi] = (v[wi] >> 4) & 0x0F0F0F0Fu;
-            }
-            u4_t *dst = reinterpret_cast<u4_t *>(Bs + bn * ROW + bh * 32);
-            dst[0] = u4_t{lo[0], hi[0], lo[1], hi[1]};
-            dst[1] = u4_t{lo[2], hi[2], lo[3], hi[3]};
-        }
-        __syncthreads();
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int kk = s * 32 + (lane >> 5) * 16;
-            i4_t a[2], b[2];
-#pragma unroll
-            for (int f = 0; f < 2; ++f) {
-                a[f] = *reinterpret_cast<const i4_t *>(As + (wm * 64 + f * 32 + (lane & 31)) * ROW + kk);
-                b[f] = *reinterpret_cast<const i4_t *>(Bs + (wn * 64 + f * 32 + (lane & 31)) * ROW + kk);
-            }
-#pragma unroll
-            for (int fm = 0; fm < 2; ++fm)
-#pragma unroll
-                for (int fn = 0; fn < 2; ++fn)
-                    acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
-        }
-        __syncthreads();
     }
 
+    // ---- epilogue: C = sa * (scale * D + offset * S) ----
 #pragma unroll
-    for (int fn = 0; fn < 2; ++fn) {
-        const int col = n0 + wn * 64 + fn * 32 + (lane & 31);
+    for (int cf = 0; cf < 2; ++cf) {
+        const int col = n0 + 64 * wn + 32 * cf + r;
         if (col >= N) continue;
         const f2_t pr = Sp[col];
 #pragma unroll
-        for (int fm = 0; fm < 2; ++fm) {
+        for (int rf = 0; rf < 2; ++rf) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const int row = m0 + wm * 64 + fm * 32 + (j >> 2) * 8 + (lane >> 5) * 4 + (j & 3);
+                const int rl = 64 * wm + 32 * rf + 8 * (j >> 2) + 4 * h + (j & 3);
+                const int row = m0 + rl;
                 if (row >= M) continue;
-                const int d = acc[fm][fn][j];
+                const int d = acc[rf][cf][j];
                 if (DEBUG_D) D[(size_t)row * N + col] = d;
-                C[(size_t)row * N + col] = sa[row] * fmaf(pr.y, (float)d, pr.x * (float)S[row]);
+                C[(size_t)row * N + col] = sa_s[rl] * fmaf(pr.y, (float)d, pr.x * (float)S_s[rl]);
             }
         }
     }
 }
 
-hipError_t launch_w4a8_gemm(int M, int K, int N, const int8_t *qa, const float *sa,
+hipError_t launch_w4a8_gemm(int M, int K, int N, int Kq, const int8_t *qa, const float *sa,
                             const int32_t *S, const void *Wp, const void *Sp, float *C,
                             int32_t *D_debug, hipStream_t s) {
-    const int Kp = (int)round_up(K, 64);
-    dim3 grid(div_up(N, TN), div_up(M, TM));
+    const int nkc = (int)round_up(K, 64) / 64;
+    const int tiles_m = div_up(M, WBM), tiles_n = div_up(N, WBN);
+    const int xcd_bands = (tiles_n % 8 == 0) ? 1 : 0;
+    dim3 grid(tiles_m * tiles_n);
     if (D_debug)
-        hipLaunchKernelGGL(w4a8_gemm_kernel<true>, grid, dim3(256), 0, s, M, N, Kp, qa, sa, S,
-                           static_cast<const uint8_t *>(Wp), static_cast<const f2_t *>(Sp), C,
-                           D_debug);
+        hipLaunchKernelGGL(w4a8_gemm_kernel<true>, grid, dim3(64 * WNW), 0, s, M, N, Kq, nkc,
+                           tiles_n, xcd_bands, qa, sa, S, static_cast<const uint8_t *>(Wp),
+                           static_cast<const f2_t *>(Sp), C, D_debug);
     else
-        hipLaunchKernelGGL(w4a8_gemm_kernel<false>, grid, dim3(256), 0, s, M, N, Kp, qa, sa, S,
-                           static_cast<const uint8_t *>(Wp), static_cast<const f2_t *>(Sp), C,
-                           D_debug);
+        hipLaunchKernelGGL(w4a8_gemm_kernel<false>, grid, dim3(64 * WNW), 0, s, M, N, Kq, nkc,
+                           tiles_n, xcd_bands, qa, sa, S, static_cast<const uint8_t *>(Wp),
+                           static_cast<const f2_t *>(Sp), C, D_debug);
     return hipGetLastError();
 }
 
