@@ -135,9 +135,11 @@ hipError_t launch_w4a8_actquant(int M, int K, int Kq, const void *A, int8_t *qa,
 }
 
 // ---------------------------------------------------------------------------
-// int8 GEMM. A 512-thread workgroup owns a 128 x 256 tile of C; wave
-// (wm, wn) owns the 64 x 64 block (rows 64 wm, columns 64 wn) and runs every
-// K step with v_mfma_i32_32x32x32_i8 (2 x 2 accumulator tiles).
+// int8 GEMM. A 512-thread workgroup owns a 128 x 256 tile of C; wave w owns
+// the 128 x 32 column block 32 w and runs every K step with
+// v_mfma_i32_32x32x32_i8 (4 accumulator tiles). Each wave loads only its own
+// weight record, so no weight byte enters a CU twice; two waves per SIMD
+// overlap one wave's loads and LDS reads with the other's matrix work.
 //  - qa is staged in LDS 128 K-columns (one 128-byte run per row) at a time,
 //    four stages deep, loaded three stages ahead through a register ring;
 //    one barrier per stage;
@@ -155,7 +157,7 @@ hipError_t launch_w4a8_actquant(int M, int K, int Kq, const void *A, int8_t *qa,
 // ---------------------------------------------------------------------------
 namespace {
 constexpr int WBM = 128, WBN = 256, WSK = 128;
-constexpr int WNW = 8;                    // waves: 2 (rows) x 4 (columns)
+constexpr int WNW = 8;                    // waves, one per 32-column block
 constexpr int WAROW = WSK + 16;           // bytes per LDS row of an A stage (144)
 constexpr int WRING = 4;                  // stages: LDS A tiles = A and B register ring slots
 constexpr size_t WAS_BYTES = (size_t)WBM * WAROW;
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(64 * WNW) void w4a8_gemm_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = uniform(tid >> 6);
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wn = wave;
     const int r = lane & 31, h = lane >> 5;
     const int nst = Kq / WSK;                          // >= 1
     const int nsteps = (nst + WRING - 1) / WRING * WRING;
@@ -234,31 +236,24 @@ __global__ __launch_bounds__(64 * WNW) void w4a8_gemm_kernel(
             *reinterpret_cast<u4_t *>(T + (idx >> 3) * WAROW + (idx & 7) * 16) = src[i] & mask;
         }
     };
-    // B: records of the wave's two 32-channel tiles, two K-blocks per stage
-    size_t b_rec0[2];
+    // B: the record of the wave's 32-channel tile, two K-blocks per stage
+    const size_t b_rec0 = (size_t)min(n0 / 32 + wn, ntiles_b - 1) * nkc;
+    auto load_b = [&](u4_t (&dst)[2], int st) {
 #pragma unroll
-    for (int cf = 0; cf < 2; ++cf)
-        b_rec0[cf] = (size_t)min((n0 + 64 * wn) / 32 + cf, ntiles_b - 1) * nkc;
-    auto load_b = [&](u4_t (&dst)[2][2], int st) {
-#pragma unroll
-        for (int cf = 0; cf < 2; ++cf)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const size_t rec = b_rec0[cf] + min(2 * st + kk, nkc - 1);
-                dst[cf][kk] = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(Wp + rec * 1024) + lane);
-            }
+        for (int kk = 0; kk < 2; ++kk) {
+            const size_t rec = b_rec0 + min(2 * st + kk, nkc - 1);
+            dst[kk] = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(Wp + rec * 1024) + lane);
+        }
     };
 
-    i16_t acc[2][2];
+    i16_t acc[4];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) acc[a][b][j] = 0;
+        for (int j = 0; j < 16; ++j) acc[a][j] = 0;
 
     u4_t an[WRING][2];
-    u4_t bq[WRING][2][2];
+    u4_t bq[WRING][2];
 
     // prologue: stage 0 in LDS tile 0, stages 1 .. WRING of A and 0 .. WRING - 1
     // of B in flight (clamped past the end: never used)
@@ -288,19 +283,15 @@ __global__ __launch_bounds__(64 * WNW) void w4a8_gemm_kernel(
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    i4_t af[2], bf[2];
+                    i4_t af[4];
 #pragma unroll
-                    for (int rf = 0; rf < 2; ++rf)
+                    for (int rf = 0; rf < 4; ++rf)
                         af[rf] = *reinterpret_cast<const i4_t *>(
-                            T + (64 * wm + 32 * rf + r) * WAROW + 64 * kk + 32 * s + 16 * h);
+                            T + (32 * rf + r) * WAROW + 64 * kk + 32 * s + 16 * h);
+                    const i4_t bf = unpack_codes(bq[u][kk][2 * s], bq[u][kk][2 * s + 1]);
 #pragma unroll
-                    for (int cf = 0; cf < 2; ++cf)
-                        bf[cf] = unpack_codes(bq[u][cf][kk][2 * s], bq[u][cf][kk][2 * s + 1]);
-#pragma unroll
-                    for (int rf = 0; rf < 2; ++rf)
-#pragma unroll
-                        for (int cf = 0; cf < 2; ++cf)
-                            acc[rf][cf] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[rf], bf[cf], acc[rf][cf], 0, 0, 0);
+                    for (int rf = 0; rf < 4; ++rf)
+                        acc[rf] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[rf], bf, acc[rf], 0, 0, 0);
                 }
             // B slot u is free: refill it with stage i + WRING
             load_b(bq[u], min(i + WRING, nst - 1));
@@ -308,19 +299,18 @@ __global__ __launch_bounds__(64 * WNW) void w4a8_gemm_kernel(
     }
 
     // ---- epilogue: C = sa * (scale * D + offset * S) ----
-#pragma unroll
-    for (int cf = 0; cf < 2; ++cf) {
-        const int col = n0 + 64 * wn + 32 * cf + r;
-        if (col >= N) continue;
+    {
+        const int col = n0 + 32 * wn + r;
+        if (col >= N) return;
         const f2_t pr = Sp[col];
 #pragma unroll
-        for (int rf = 0; rf < 2; ++rf) {
+        for (int rf = 0; rf < 4; ++rf) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const int rl = 64 * wm + 32 * rf + 8 * (j >> 2) + 4 * h + (j & 3);
+                const int rl = 32 * rf + 8 * (j >> 2) + 4 * h + (j & 3);
                 const int row = m0 + rl;
                 if (row >= M) continue;
-                const int d = acc[rf][cf][j];
+                const int d = acc[rf][j];
                 if (DEBUG_D) D[(size_t)row * N + col] = d;
                 C[(size_t)row * N + col] = sa_s[rl] * fmaf(pr.y, (float)d, pr.x * (float)S_s[rl]);
             }
