@@ -453,102 +453,116 @@ __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
 // ---------------------------------------------------------------------------
 // Int8-Block0
 // ---------------------------------------------------------------------------
-template <int MR, int CPW>
-__global__ __launch_bounds__(256) void gemv_int8b0_kernel(
+// One 1024-thread workgroup per 16 channels, one wave per channel. A
+// channel's codes are one contiguous run of Kp bytes: lane l reads the
+// 16-byte slices l, l + 64, ... of it, so each load instruction is 1 KiB of
+// contiguous bytes, and every slice a wave needs is requested before the
+// activations are staged. Loads are unconditional with clamped indices
+// (slices past the row end reread the last slice and are skipped in the
+// arithmetic), which keeps the compiler's in-order count of outstanding
+// loads exact. Per channel, sum(a * w) = offset * sum(a) + scale * sum(a * q);
+// sum(a) is formed once per workgroup.
+constexpr int I8_WAVES = 16;
+
+template <int MR, int NCH>
+__global__ __launch_bounds__(64 * I8_WAVES) void gemv_int8b0_kernel(
     int M, int K, int N, int Kp, const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
     const f2_t *__restrict__ Sp, float *__restrict__ C) {
-    extern __shared__ __align__(16) _Float16 As[];   // [MR][Kp], zero beyond K
+    extern __shared__ __align__(16) unsigned char lds[];
+    _Float16 *As = reinterpret_cast<_Float16 *>(lds);                      // [MR][Kp], zero past K
+    float *ssum = reinterpret_cast<float *>(lds + (size_t)MR * Kp * 2);    // [MR][I8_WAVES]
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = uniform(tid >> 6);
     const int m0 = blockIdx.y * MR;
+    const int Np = (N + 3) & ~3;
+    const int n = blockIdx.x * I8_WAVES + wave;
+    const int nc = min(n, Np - 1);
+    const int nchunk = Kp >> 4;              // 16-byte slices per channel
+
+    // 1. this wave's code slices and pair
+    u4_t wq[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int ci = min(lane + 64 * i, nchunk - 1);
+        wq[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const u4_t *>(Wp + (size_t)nc * Kp + (size_t)ci * 16));
+    }
+    const f2_t pr = Sp[nc];
+
+    // 2. activations to LDS (zero past K), and their row sums
+    float part[MR];
+#pragma unroll
+    for (int r = 0; r < MR; ++r) part[r] = 0.f;
+    const h2_t one = {(_Float16)1.0f, (_Float16)1.0f};
     if ((K & 7) == 0) {
         const int pieces = Kp >> 3;
-        for (int p = tid; p < MR * pieces; p += 256) {
+        for (int p = tid; p < MR * pieces; p += 64 * I8_WAVES) {
             const int r = p / pieces, c = p - r * pieces;
             u4_t v = {0u, 0u, 0u, 0u};
             if (m0 + r < M && c * 8 < K)
                 v = *reinterpret_cast<const u4_t *>(A + (size_t)(m0 + r) * K + (size_t)c * 8);
             *reinterpret_cast<u4_t *>(As + (size_t)r * Kp + (size_t)c * 8) = v;
+            float sp = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sp = dot2(as_h2(v[i]), one, sp);
+#pragma unroll
+            for (int rr = 0; rr < MR; ++rr) part[rr] += (rr == r) ? sp : 0.f;
         }
     } else {
-        for (int e = tid; e < MR * Kp; e += 256) {
+        for (int e = tid; e < MR * Kp; e += 64 * I8_WAVES) {
             const int r = e / Kp, k = e - r * Kp;
-            As[e] = (m0 + r < M && k < K) ? A[(size_t)(m0 + r) * K + k] : (_Float16)0.0f;
+            const _Float16 v = (m0 + r < M && k < K) ? A[(size_t)(m0 + r) * K + k] : (_Float16)0.0f;
+            As[e] = v;
+#pragma unroll
+            for (int rr = 0; rr < MR; ++rr) part[rr] += (rr == r) ? (float)v : 0.f;
         }
+    }
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+        float v = part[r];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+        if (lane == 0) ssum[r * I8_WAVES + wave] = v;
     }
     __syncthreads();
 
-    const int lane = tid & 63;
-    const int Np = (N + 3) & ~3;
-    const int ch0 = uniform((int)(blockIdx.x * 4 + (tid >> 6)) * CPW);
-    if (ch0 >= N) return;
-    const int nchunk = Kp >> 4;   // 16-byte chunks per channel
-    const h2_t one = {(_Float16)1.0f, (_Float16)1.0f};
-
-    float T[CPW][MR];
-    float s0[MR];
+    // 3. sum(a * (1024 + q)) per row over this lane's slices
+    float T[MR];
+#pragma unroll
+    for (int r = 0; r < MR; ++r) T[r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int ci = lane + 64 * i;
+        if (ci >= nchunk) break;
+#pragma unroll
+        for (int wi = 0; wi < 4; ++wi) {
+            const unsigned word = wq[i][wi];
+            // bytes (q0, q1) and (q2, q3) under 0x64: halves 1024 + q
+            const h2_t x0 = as_h2(__builtin_amdgcn_perm(0x64646464u, word, 0x04010400u));
+            const h2_t x1 = as_h2(__builtin_amdgcn_perm(0x64646464u, word, 0x04030402u));
+#pragma unroll
+            for (int r = 0; r < MR; ++r) {
+                const u2_t av = *reinterpret_cast<const u2_t *>(As + (size_t)r * Kp + ci * 16 + wi * 4);
+                T[r] = dot2(x0, as_h2(av.x), T[r]);
+                T[r] = dot2(x1, as_h2(av.y), T[r]);
+            }
+        }
+    }
+    // 4. per row: reduce over the wave, then offset * sum(a) + scale * sum(a q)
+    //    with sum(a q) = T - 1024 sum(a)
+    const float c1 = fmaf(-1024.0f, pr.y, pr.x);
 #pragma unroll
     for (int r = 0; r < MR; ++r) {
-        s0[r] = 0.f;
+        float v = T[r];
 #pragma unroll
-        for (int cc = 0; cc < CPW; ++cc) T[cc][r] = 0.f;
-    }
-    for (int ci = lane; ci < nchunk; ci += 64) {
-        u4_t wq[CPW];
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+        if (lane == 0 && n < N && m0 + r < M) {
+            float sa = 0.f;
 #pragma unroll
-        for (int cc = 0; cc < CPW; ++cc)
-            wq[cc] = (ch0 + cc < Np)
-                         ? *reinterpret_cast<const u4_t *>(Wp + (size_t)(ch0 + cc) * Kp + (size_t)ci * 16)
-                         : u4_t{0u, 0u, 0u, 0u};
-        h2_t ap[MR][8];
-#pragma unroll
-        for (int r = 0; r < MR; ++r) {
-            const u4_t v0 = *reinterpret_cast<const u4_t *>(As + (size_t)r * Kp + ci * 16);
-            const u4_t v1 = *reinterpret_cast<const u4_t *>(As + (size_t)r * Kp + ci * 16 + 8);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ap[r][i] = as_h2(v0[i]);
-                ap[r][4 + i] = as_h2(v1[i]);
-                s0[r] = dot2(ap[r][i], one, s0[r]);
-                s0[r] = dot2(ap[r][4 + i], one, s0[r]);
-            }
+            for (int w = 0; w < I8_WAVES; ++w) sa += ssum[r * I8_WAVES + w];
+            C[(size_t)(m0 + r) * N + n] = fmaf(c1, sa, pr.y * v);
         }
-#pragma unroll
-        for (int cc = 0; cc < CPW; ++cc) {
-#pragma unroll
-            for (int wi = 0; wi < 4; ++wi) {
-                const unsigned word = wq[cc][wi];
-                // bytes (q0, q1) and (q2, q3) under 0x64: halves 1024 + q
-                const h2_t x0 = as_h2(__builtin_amdgcn_perm(0x64646464u, word, 0x04010400u));
-                const h2_t x1 = as_h2(__builtin_amdgcn_perm(0x64646464u, word, 0x04030402u));
-#pragma unroll
-                for (int r = 0; r < MR; ++r) {
-                    T[cc][r] = dot2(x0, ap[r][2 * wi], T[cc][r]);
-                    T[cc][r] = dot2(x1, ap[r][2 * wi + 1], T[cc][r]);
-                }
-            }
-        }
-    }
-
-    constexpr int NV = CPW * MR;
-    float acc[NV];
-#pragma unroll
-    for (int cc = 0; cc < CPW; ++cc) {
-        f2_t pr = {0.f, 0.f};
-        if (ch0 + cc < Np) pr = Sp[ch0 + cc];
-        // offset*s0 + scale*sum(a q), with T = 1024 s0 + sum(a q)
-        const float c1 = fmaf(-1024.0f, pr.y, pr.x);
-#pragma unroll
-        for (int r = 0; r < MR; ++r) acc[cc * MR + r] = fmaf(c1, s0[r], pr.y * T[cc][r]);
-    }
-    int idx;
-    const float total = wave_transpose_sum<NV>(acc, lane, idx);
-    constexpr int LOW = 6 - Log2<NV>::value;
-    if ((lane & ((1 << LOW) - 1)) == 0) {
-        const int r = idx % MR;
-        const int cc = idx / MR;
-        const int n = ch0 + cc;
-        const int m = m0 + r;
-        if (n < N && m < M) C[(size_t)m * N + n] = total;
     }
 }
 
@@ -556,10 +570,11 @@ __global__ __launch_bounds__(256) void gemv_int8b0_kernel(
 // Launchers
 // ---------------------------------------------------------------------------
 static int rows_per_pass(int M, int K, int kp_bytes_per_row) {
-    // Rows of A staged in LDS at once, bounded by 64 KiB of LDS.
+    // Rows of A staged in LDS at once: they and 1 KiB of reduction space fit
+    // in 64 KiB of LDS.
     (void)K;
     int mr = M >= 4 ? 4 : (M >= 2 ? 2 : 1);
-    while (mr > 1 && mr * kp_bytes_per_row > 65536) mr >>= 1;
+    while (mr > 1 && mr * kp_bytes_per_row > 65536 - 1024) mr >>= 1;
     return mr;
 }
 
@@ -620,26 +635,36 @@ hipError_t launch_gemv_int4b64(int M, int K, int N, const void *A, const void *W
     }
 }
 
-template <int MR>
+template <int MR, int NCH>
 static hipError_t gemv_int8_mr(int M, int K, int N, int Kp, const void *A, const void *Wp,
                                const void *Sp, float *C, hipStream_t s) {
-    constexpr int CPW = 4;
-    const int waves = div_up(N, CPW);
-    dim3 grid(div_up(waves, 4), div_up(M, MR));
-    const size_t lds = (size_t)MR * Kp * sizeof(_Float16);
-    hipLaunchKernelGGL((gemv_int8b0_kernel<MR, CPW>), grid, dim3(256), lds, s, M, K, N, Kp,
-                       static_cast<const _Float16 *>(A), static_cast<const uint8_t *>(Wp),
+    dim3 grid(div_up(N, I8_WAVES), div_up(M, MR));
+    const size_t lds = (size_t)MR * Kp * sizeof(_Float16) + (size_t)MR * I8_WAVES * sizeof(float);
+    hipLaunchKernelGGL((gemv_int8b0_kernel<MR, NCH>), grid, dim3(64 * I8_WAVES), lds, s, M, K, N,
+                       Kp, static_cast<const _Float16 *>(A), static_cast<const uint8_t *>(Wp),
                        static_cast<const f2_t *>(Sp), C);
     return hipGetLastError();
+}
+
+template <int MR>
+static hipError_t gemv_int8_k(int M, int K, int N, int Kp, const void *A, const void *Wp,
+                              const void *Sp, float *C, hipStream_t s) {
+    // slices per lane: Kp / 1024, rounded up to a power of two (K <= 16384)
+    const int nch = div_up(Kp, 1024);
+    if (nch <= 1) return gemv_int8_mr<MR, 1>(M, K, N, Kp, A, Wp, Sp, C, s);
+    if (nch <= 2) return gemv_int8_mr<MR, 2>(M, K, N, Kp, A, Wp, Sp, C, s);
+    if (nch <= 4) return gemv_int8_mr<MR, 4>(M, K, N, Kp, A, Wp, Sp, C, s);
+    if (nch <= 8) return gemv_int8_mr<MR, 8>(M, K, N, Kp, A, Wp, Sp, C, s);
+    return gemv_int8_mr<MR, 16>(M, K, N, Kp, A, Wp, Sp, C, s);
 }
 
 hipError_t launch_gemv_int8b0(int M, int K, int N, const void *A, const void *Wp,
                               const void *Sp, float *C, hipStream_t s) {
     const int Kp = (int)round_up(K, 64);
     switch (rows_per_pass(M, K, Kp * 2)) {
-    case 4: return gemv_int8_mr<4>(M, K, N, Kp, A, Wp, Sp, C, s);
-    case 2: return gemv_int8_mr<2>(M, K, N, Kp, A, Wp, Sp, C, s);
-    default: return gemv_int8_mr<1>(M, K, N, Kp, A, Wp, Sp, C, s);
+    case 4: return gemv_int8_k<4>(M, K, N, Kp, A, Wp, Sp, C, s);
+    case 2: return gemv_int8_k<2>(M, K, N, Kp, A, Wp, Sp, C, s);
+    default: return gemv_int8_k<1>(M, K, N, Kp, A, Wp, Sp, C, s);
     }
 }
 
