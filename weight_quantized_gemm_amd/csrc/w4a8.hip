@@ -23,10 +23,16 @@ namespace qg {
 // has Kq = roundup(K, 128) bytes, zero past K, so the GEMM can stage 128-wide
 // K slices without bounds cases.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int8_t quant1(float a, float s) {
-    float r = rintf(a / s);                 // IEEE division, ties to even
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int8_t)(int)r;
+// clamp(rint(a / s), -127, 127) with a / s the correctly rounded fp32
+// quotient, formed from rs = RN(1 / s) with one residual correction:
+// y = RN(a * rs), q = y + rs * (a - y * s) (two fused multiply-adds). For
+// every fp16 a with |a| <= amax and s = RN(amax / 127) this q is bit-identical
+// to the IEEE division (checked exhaustively on the CPU by the test suite).
+__device__ __forceinline__ int quant1(float a, float s, float rs) {
+    const float y = a * rs;
+    const float e = fmaf(-y, s, a);
+    const float q = fmaf(e, rs, y);
+    return (int)fminf(fmaxf(rintf(q), -127.0f), 127.0f);   // ties to even
 }
 
 __device__ __forceinline__ float block_max(float v, float *red4) {
@@ -73,6 +79,7 @@ __global__ __launch_bounds__(256) void w4a8_actquant_reg_kernel(int K, int Kq,
     }
     amax = block_max(amax, red_f);
     const float s = amax / 127.0f;           // IEEE division, one rounding
+    const float rs = 1.0f / s;               // IEEE division, one rounding
     int sum = 0;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
@@ -82,7 +89,7 @@ __global__ __launch_bounds__(256) void w4a8_actquant_reg_kernel(int K, int Kq,
         if (k < K && amax != 0.0f) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int qi = quant1((float)v[i][e], s);
+                const int qi = quant1((float)v[i][e], s, rs);
                 sum += qi;
                 const unsigned byte = (unsigned)(qi & 0xff);
                 if (e < 4) lo |= byte << (8 * e);
@@ -111,10 +118,11 @@ __global__ __launch_bounds__(256) void w4a8_actquant_kernel(int K, int Kq,
     for (int k = tid; k < K; k += 256) amax = fmaxf(amax, fabsf((float)row[k]));
     amax = block_max(amax, red_f);
     const float s = amax / 127.0f;
+    const float rs = 1.0f / s;
     int sum = 0;
     for (int k = tid; k < Kq; k += 256) {
         int qi = 0;
-        if (k < K && amax != 0.0f) qi = quant1((float)row[k], s);
+        if (k < K && amax != 0.0f) qi = quant1((float)row[k], s, rs);
         sum += qi;
         qrow[k] = (int8_t)qi;
     }
