@@ -210,6 +210,55 @@ def single_workload(args, torch) -> int:
     return 0
 
 
+def vendor_reference(args, torch) -> int:
+    """The vendor libraries on the same prefill shapes, same protocol (rotated
+    copies past twice the Infinity Cache, replayed graph, HIP events): dense
+    fp16 x fp16 -> fp16 (torch.matmul) and int8 x int8 -> int32
+    (torch._int_mm). Context for what the matrix cores reach on these shapes;
+    never part of the metric."""
+    cases = [("fp16 matmul, dense weights", torch.float16, 512, 4096, 4096),
+             ("fp16 matmul, dense weights", torch.float16, 1024, 3072, 8192),
+             ("int8 _int_mm", torch.int8, 1024, 3072, 8192)]
+    for name, dt, M, K, N in cases:
+        per = M * K * dt.itemsize + K * N * dt.itemsize + M * N * 4
+        copies = max(2, -(-2 * MALL_BYTES // per) + 1)
+        g = torch.Generator(device="cuda").manual_seed(7)
+        if dt == torch.int8:
+            A = [torch.randint(-127, 128, (M, K), dtype=dt, device="cuda", generator=g) for _ in range(copies)]
+            B = [torch.randint(0, 16, (N, K), dtype=dt, device="cuda", generator=g) for _ in range(copies)]
+            C = [torch.empty((M, N), dtype=torch.int32, device="cuda") for _ in range(copies)]
+            fn = lambda i: torch._int_mm(A[i], B[i].t(), out=C[i])
+        else:
+            A = [torch.randn((M, K), dtype=dt, device="cuda", generator=g) for _ in range(copies)]
+            B = [torch.randn((K, N), dtype=dt, device="cuda", generator=g) for _ in range(copies)]
+            C = [torch.empty((M, N), dtype=dt, device="cuda") for _ in range(copies)]
+            fn = lambda i: torch.matmul(A[i], B[i], out=C[i])
+        for i in range(copies):
+            fn(i)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(copies):
+                fn(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, -(-args.steps // copies))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / (reps * copies)
+        rate = flops(M, K, N) / ms / 1e9
+        peak = INT8_PEAK_TOPS if dt == torch.int8 else FP16_PEAK_TFLOPS
+        print(json.dumps({"vendor_reference": name, "M": M, "K": K, "N": N, "ms_per_call": ms,
+                          "rate": rate, "unit": "TOP/s" if dt == torch.int8 else "TFLOP/s",
+                          "frac_of_peak": rate / peak}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +272,10 @@ def main() -> int:
                     help="diagnostic: time only this named workload (" +
                          ", ".join(("f32", "int8b0_decode", "int4b64_decode", "int4b64_prefill",
                                     "w4a8_prefill")) + ") and print its own JSON line")
+    ap.add_argument("--vendor-reference", action="store_true",
+                    help="context only: time torch's own fp16 GEMM and int8 GEMM (the vendor "
+                         "libraries) on the prefill shapes with the same rotation and print one "
+                         "JSON line per shape")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch's plain device copy of MIB MiB (fp32) 10 times, "
                          "the reference kernel for scaling the HBM byte counters")
@@ -248,6 +301,8 @@ def main() -> int:
 
     if args.workload:
         return single_workload(args, torch)
+    if args.vendor_reference:
+        return vendor_reference(args, torch)
 
     # one decode + one prefill copy is ~50 MB; rotate past 2x the MALL
     per_step_bytes = (algorithmic_bytes(1, 4096, 11008) + algorithmic_bytes(512, 4096, 4096))
