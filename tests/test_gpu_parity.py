@@ -127,6 +127,17 @@ def test_int4b64_shapes(M):
         _parity("int4b64", M, K, N, seed=M * 7 + K + N)
 
 
+@pytest.mark.parametrize("M", [1, 3, 5, 8])
+def test_int4b64_gemv_long_k(M):
+    """The decode kernel walks K in passes of 64 blocks: K = 9728 (a K of the
+    page's shape grid) takes two full passes and a partial third."""
+    K, N = 9728, 70
+    A, W, _ = _case("int4b64", M, K, N, seed=9728 + M)
+    q, p, qo, po = _quantized_pair("int4b64", W)
+    C = run("int4b64", M, K, N, A, q, p)
+    compare(C, O.reference("int4b64", A, q=qo, pairs=po), f"int4b64 gemv M={M} K={K}")
+
+
 @pytest.mark.parametrize("K", [64, 128, 192, 256, 320, 384, 448, 512, 576, 640, 1024])
 def test_int4b64_tiled_short_k(K):
     """The tiled kernel splits the K-blocks over four waves and pads each
