@@ -210,6 +210,89 @@ def single_workload(args, torch) -> int:
     return 0
 
 
+class ShapeWorkload(Workload):
+    """A Workload built from an explicit shape (seeded like the named ones)."""
+
+    def __init__(self, fmt: str, M: int, K: int, N: int, copies: int, seed: int):
+        import torch
+        from weight_quantized_gemm_amd import qgemm as Q
+        from weight_quantized_gemm_amd import synth
+        rng = np.random.default_rng(seed)
+        self.name, self.fmt, self.M, self.K, self.N = f"{fmt} {M}x{K}x{N}", fmt, M, K, N
+        self.A_host = synth.activations(rng, M, K, fp16=(fmt != "f32"))
+        if fmt == "f32":
+            wp, sp = synth.float_pattern_weights(K, N), None
+        else:
+            q, p = Q.qgemm_quantize_weights(synth.normal_weights(rng, N, K), fmt)
+            wp, sp = Q.qgemm_pack_weights(K, N, fmt, q, p)
+        A0, B0 = torch.from_numpy(self.A_host).cuda(), torch.from_numpy(wp).cuda()
+        self.A = [A0] + [A0.clone() for _ in range(copies - 1)]
+        self.B = [B0] + [B0.clone() for _ in range(copies - 1)]
+        if sp is None:
+            self.S = [None] * copies
+        else:
+            S0 = torch.from_numpy(sp).cuda()
+            self.S = [S0] + [S0.clone() for _ in range(copies - 1)]
+        self.C = [torch.empty((M, N), dtype=torch.float32, device="cuda") for _ in range(copies)]
+        self.ws_bytes = Q.qgemm_workspace_size(M, K, N, fmt)
+        self.ws = (torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+                   if self.ws_bytes else None)
+        self.Q = Q
+
+
+def time_calls(torch, run, copies: int, steps: int) -> float:
+    """ms per call: `copies` calls captured in one graph, replayed about
+    `steps` times over, HIP events on the launching stream."""
+    for i in range(copies):
+        run(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(copies):
+            run(i)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, -(-steps // copies))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * copies)
+
+
+def page_grid(args, torch) -> int:
+    """The benchmark page's default (K, N) x M sizes, per format: one JSON line
+    per shape with the time per call, the rate and its fraction of the bound
+    that applies (HBM for the decode-shaped M <= 8 GEMV, the matrix cores
+    otherwise)."""
+    from weight_quantized_gemm_amd import synth
+    for fmt in args.page_grid.split(","):
+        for K, N in synth.PAGE_KN:
+            for M in synth.PAGE_M:
+                per = algorithmic_bytes(M, K, N, fmt)
+                copies = args.copies or min(64, max(2, -(-2 * MALL_BYTES // per) + 1))
+                w = ShapeWorkload(fmt, M, K, N, copies, seed=K + N + M)
+                ms = time_calls(torch, w.run, copies, args.steps)
+                fl, by = flops(M, K, N), algorithmic_bytes(M, K, N, fmt)
+                if fmt == "w4a8":
+                    peak, unit = INT8_PEAK_TOPS, "TOP/s"
+                elif fmt == "f32":
+                    peak, unit = 157.3, "TFLOP/s"
+                else:
+                    peak, unit = FP16_PEAK_TFLOPS, "TFLOP/s"
+                rate = fl / ms / 1e9
+                print(json.dumps({"page_grid": fmt, "M": M, "K": K, "N": N, "ms_per_call": ms,
+                                  "rate": rate, "unit": unit, "frac_of_mfma_peak": rate / peak,
+                                  "gb_s": by / ms / 1e6, "frac_of_hbm_peak": by / ms / 1e6 / HBM_PEAK_GBS}),
+                      flush=True)
+                del w
+                torch.cuda.empty_cache()
+    return 0
+
+
 def vendor_reference(args, torch) -> int:
     """The vendor libraries on the same prefill shapes, same protocol (rotated
     copies past twice the Infinity Cache, replayed graph, HIP events): dense
@@ -272,6 +355,9 @@ def main() -> int:
                     help="diagnostic: time only this named workload (" +
                          ", ".join(("f32", "int8b0_decode", "int4b64_decode", "int4b64_prefill",
                                     "w4a8_prefill")) + ") and print its own JSON line")
+    ap.add_argument("--page-grid", default="", metavar="FORMATS",
+                    help="diagnostic: time the benchmark page's default (K, N) x M grid for the "
+                         "comma-separated formats (f32,int8b0,int4b64,w4a8), one JSON line each")
     ap.add_argument("--vendor-reference", action="store_true",
                     help="context only: time torch's own fp16 GEMM and int8 GEMM (the vendor "
                          "libraries) on the prefill shapes with the same rotation and print one "
@@ -303,6 +389,8 @@ def main() -> int:
         return single_workload(args, torch)
     if args.vendor_reference:
         return vendor_reference(args, torch)
+    if args.page_grid:
+        return page_grid(args, torch)
 
     # one decode + one prefill copy is ~50 MB; rotate past 2x the MALL
     per_step_bytes = (algorithmic_bytes(1, 4096, 11008) + algorithmic_bytes(512, 4096, 4096))

@@ -154,9 +154,14 @@ qgemm_status qgemm_unpack_weights(int K, int N, qgemm_format f,
                                   void *w_canonical, float *pairs_canonical);
 
 /*
- * Device scratch qgemm_run_ws needs: 0 except W4A8, which stores the
- * quantised activations (int8 [M][K rounded up to 64]), the row scales
- * (float [M]) and the row sums of the quantised activations (int32 [M]).
+ * Device scratch qgemm_run_ws may need for this shape; a function of
+ * (M, K, N, f) alone. It holds, in order: for W4A8 the quantised
+ * activations (int8 [M][K rounded up to 128]), the row scales (float [M])
+ * and the row sums of the quantised activations (int32 [M]); then, when the
+ * shape leaves too few output tiles to fill the GPU and the GEMM therefore
+ * splits K into S slices, S partial products (float [S][M][N]) that a
+ * second kernel adds in the fixed order 0..S-1 (so results are
+ * deterministic). 0 for shapes that need neither.
  * Errors: ERR_NULL, ERR_FORMAT, ERR_SHAPE.
  */
 qgemm_status qgemm_workspace_size(int M, int K, int N, qgemm_format f,
@@ -174,8 +179,9 @@ qgemm_status qgemm_workspace_size(int M, int K, int N, qgemm_format f,
  * see qgemm_set_gemv_max_m) take the streaming GEMV (the page: M = 8 is the
  * narrow, near-decode case, bounded by GEMV bandwidth); larger M take the
  * LDS-staged fp16 MFMA kernel. W4A8 runs the activation quantiser then the
- * int8 MFMA kernel; its scratch is allocated stream-ordered on `stream`
- * (hipMallocAsync / hipFreeAsync). F32 runs the fp32 tiled kernel.
+ * int8 MFMA kernel. F32 runs the fp32 tiled kernel. Any scratch the shape
+ * needs (qgemm_workspace_size) is allocated stream-ordered on `stream`
+ * (hipMallocAsync / hipFreeAsync).
  * The buffers' sizes are not visible to the library: the caller guarantees
  * A holds M*K, C M*N elements and Bq / scales qgemm_packed_size() bytes.
  * Errors: ERR_NULL, ERR_FORMAT, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE,
@@ -186,10 +192,11 @@ qgemm_status qgemm_run(int M, int K, int N, qgemm_format f, const void *A,
                        void *stream);
 
 /*
- * As qgemm_run, with caller-provided device scratch `workspace` of
- * ws_bytes >= qgemm_workspace_size() bytes (may be NULL when that size is
- * 0). The library allocates nothing. Calls that share a workspace must be
- * ordered (same stream, or synchronised).
+ * As qgemm_run, with caller-provided device scratch `workspace` (16-byte
+ * aligned) of ws_bytes >= qgemm_workspace_size() bytes (may be NULL when
+ * that size is 0, or when the call takes the GEMV, which uses none). The
+ * library allocates nothing. Calls that share a workspace must be ordered
+ * (same stream, or synchronised).
  * Errors: as qgemm_run, plus ERR_SIZE for a short workspace.
  */
 qgemm_status qgemm_run_ws(int M, int K, int N, qgemm_format f, const void *A,

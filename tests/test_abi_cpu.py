@@ -81,6 +81,22 @@ def test_run_ws_validation(lib):
     assert st == 4                                   # misaligned
 
 
+def test_split_k_workspace_plan():
+    """Workspace is a function of the shape: Int4 GEMMs with few output tiles
+    (64 x 128 each) split K into at most 8 slices of >= 8 K-blocks of 64 and
+    need S partial [M][N] float tiles; shapes that fill the GPU need none."""
+    def sz(M, K, N):
+        return Q.qgemm_workspace_size(M, K, N, "int4b64")
+    assert sz(64, 4096, 512) == 8 * 64 * 512 * 4          # 4 tiles -> 8 slices
+    assert sz(64, 1920, 384) == 3 * 64 * 384 * 4          # 30 K-blocks -> 3 slices
+    assert sz(512, 4096, 4096) == 0                       # 256 tiles fill the GPU
+    assert sz(64, 448, 128) == 0                          # 7 K-blocks: too short to split
+    assert sz(1, 4096, 4096) == sz(1, 4096, 4096)         # pure function of the shape
+    assert Q.qgemm_workspace_size(64, 4096, 512, "int8b0") == 0
+    w = Q.qgemm_workspace_size(8, 128, 16, "w4a8")
+    assert w == Q.qgemm_workspace_size(8, 128, 16000, "w4a8")   # W4A8 scratch has no N part
+
+
 def test_sizes():
     assert Q.qgemm_packed_size(4096, 11008, "int4b64") == (22544384, 5636096)
     assert Q.qgemm_packed_size(4096, 100, "int4b64") == (4 * 64 * 1024, 4 * 64 * 256)

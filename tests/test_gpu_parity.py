@@ -127,6 +127,32 @@ def test_int4b64_shapes(M):
         _parity("int4b64", M, K, N, seed=M * 7 + K + N)
 
 
+@pytest.mark.parametrize("fmt", ["f32", "int8b0", "int4b64", "w4a8"])
+@pytest.mark.parametrize("K,N", synth.PAGE_KN)
+def test_page_shape_grid(fmt, K, N):
+    """Every (K, N) of the benchmark page's default sizes at its M values, every
+    format; rows sampled (first, tile edges, last) once M is past 32."""
+    for M in synth.PAGE_M:
+        rows = None if M <= 32 else sorted({0, 1, 63, 64, M // 2, M - 2, M - 1})
+        _parity(fmt, M, K, N, seed=K + N + M, rows=rows)
+
+
+@pytest.mark.parametrize("M,K,N", [(9, 4160, 67), (65, 4096, 256), (64, 1920, 384),
+                                   (33, 9728, 2560), (128, 2560, 1024)])
+def test_int4b64_split_k(M, K, N):
+    """Shapes with few output tiles split K over several workgroups
+    (partials in the workspace, added in a fixed order): parity, run vs
+    run_ws and repeat runs bit-identical."""
+    assert Q.qgemm_workspace_size(M, K, N, "int4b64") >= 2 * M * N * 4   # the split engages
+    A, W, _ = _case("int4b64", M, K, N, seed=M + K + N)
+    q, p, qo, po = _quantized_pair("int4b64", W)
+    C1 = run("int4b64", M, K, N, A, q, p)
+    compare(C1, O.reference("int4b64", A, q=qo, pairs=po), f"split {M}x{K}x{N}")
+    C2 = run("int4b64", M, K, N, A, q, p, ws=True)
+    C3 = run("int4b64", M, K, N, A, q, p)
+    assert np.array_equal(C1, C2) and np.array_equal(C1, C3)
+
+
 @pytest.mark.parametrize("M", [1, 3, 5, 8])
 def test_int4b64_gemv_long_k(M):
     """The decode kernel walks K in passes of 64 blocks: K = 9728 (a K of the
@@ -342,6 +368,7 @@ def test_graph_capture_replays_match_eager():
     its scratch and is not meant for capture)."""
     calls = []
     for fmt, M, K, N in [("int4b64", 1, 4096, 1000), ("int4b64", 200, 1024, 300),
+                         ("int4b64", 64, 4096, 512),
                          ("int8b0", 3, 1000, 130), ("w4a8", 100, 640, 256)]:
         A, W, _ = _case(fmt, M, K, N, seed=M + N)
         q, p = Q.qgemm_quantize_weights(W, fmt)

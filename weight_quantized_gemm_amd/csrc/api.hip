@@ -94,18 +94,34 @@ static qgemm_status run_w4a8(int M, int K, int N, const Geometry &g, const void 
     return launched(launch_w4a8_gemm(M, K, N, w.qa_stride, qa, sa, S, Bq, scales, C, D_debug, s));
 }
 
+// The GEMV kernels serve M <= the current GEMV limit (and K within the
+// register budget); everything else takes the tiled GEMM.
+static bool use_gemv(int M, int K) { return M <= gemv_max_m() && K <= kGemvMaxK; }
+
+// Scratch bytes one call actually touches: the W4A8 activation codes first,
+// then (when the GEMM is split along K) the partial tiles. The size reported to
+// callers (run_workspace().bytes) is a function of the shape alone and never
+// smaller than this.
+static size_t used_bytes(const RunWorkspace &r, bool gemv) {
+    return (gemv || r.nsplit <= 1) ? r.w4a8.bytes : r.bytes;
+}
+
 static qgemm_status dispatch(int M, int K, int N, qgemm_format f, const Geometry &g,
                              const void *A, const void *Bq, const void *scales, float *C,
                              void *ws, hipStream_t s) {
     (void)hipGetLastError();   // start from a clean per-thread error state
-    const bool gemv = M <= gemv_max_m() && K <= kGemvMaxK;
+    const bool gemv = use_gemv(M, K);
+    const RunWorkspace r = run_workspace(f, M, K, N);
+    const int nsplit = gemv ? 1 : r.nsplit;
+    float *part = nsplit > 1 ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + r.part_off)
+                             : nullptr;
     switch (f) {
     case QGEMM_F32:
         return launched(launch_gemm_f32(M, K, N, static_cast<const float *>(A),
                                         static_cast<const float *>(Bq), C, s));
     case QGEMM_INT4_B64:
         return launched(gemv ? launch_gemv_int4b64(M, K, N, A, Bq, scales, C, s)
-                             : launch_gemm_int4b64(M, K, N, A, Bq, scales, C, s));
+                             : launch_gemm_int4b64(M, K, N, A, Bq, scales, C, nsplit, part, s));
     case QGEMM_INT8_B0:
         return launched(gemv ? launch_gemv_int8b0(M, K, N, A, Bq, scales, C, s)
                              : launch_gemm_int8b0(M, K, N, A, Bq, scales, C, s));
@@ -134,10 +150,11 @@ qgemm_status qgemm_run_ws(int M, int K, int N, qgemm_format f, const void *A,
     bool empty = false;
     qgemm_status st = check_run(M, K, N, f, A, Bq, scales, C, &g, &empty);
     if (st != QGEMM_OK || empty) return st;
-    if (f == QGEMM_W4A8) {
+    const size_t need = used_bytes(run_workspace(f, M, K, N), use_gemv(M, K));
+    if (need > 0) {
         if (!workspace) return QGEMM_ERR_NULL;
         if (!aligned16(workspace)) return QGEMM_ERR_ALIGN;
-        if (ws_bytes < w4a8_workspace(M, K).bytes) return QGEMM_ERR_SIZE;
+        if (ws_bytes < need) return QGEMM_ERR_SIZE;
     }
     st = check_device();
     if (st != QGEMM_OK) return st;
@@ -154,10 +171,9 @@ qgemm_status qgemm_run(int M, int K, int N, qgemm_format f, const void *A, const
     st = check_device();
     if (st != QGEMM_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (f != QGEMM_W4A8)
-        return dispatch(M, K, N, f, g, A, Bq, scales, C, nullptr, s);
-    // W4A8 scratch, allocated and released in stream order.
-    const size_t bytes = w4a8_workspace(M, K).bytes;
+    const size_t bytes = used_bytes(run_workspace(f, M, K, N), use_gemv(M, K));
+    if (bytes == 0) return dispatch(M, K, N, f, g, A, Bq, scales, C, nullptr, s);
+    // Scratch (W4A8 codes, split-K partials), allocated and released in stream order.
     void *ws = nullptr;
     if (hipMallocAsync(&ws, bytes, s) != hipSuccess || !ws) {
         (void)hipGetLastError();

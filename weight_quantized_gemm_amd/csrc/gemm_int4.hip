@@ -122,12 +122,18 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     const int nh = wave & 1, kq = wave >> 1;      // N half, K quarter
     const int r = lane & 31, h = lane >> 5;
     const int nblk = K / BK;                       // >= 1
-    const int kb0 = kq * nblk / 4, kb1 = (kq + 1) * nblk / 4;   // contiguous quarter
+    // split-K: this workgroup's blocks are [KB0, KB1) (all of K when
+    // gridDim.y == 1) and its output is partial tile blockIdx.y
+    const int KB0 = (int)((long long)blockIdx.y * nblk / gridDim.y);
+    const int KB1 = (int)((long long)(blockIdx.y + 1) * nblk / gridDim.y);
+    const int nbs = KB1 - KB0;                     // >= 1: the plan keeps gridDim.y <= nblk
+    float *const out = C + (size_t)blockIdx.y * M * N;
+    const int kb0 = KB0 + kq * nbs / 4, kb1 = KB0 + (kq + 1) * nbs / 4;   // contiguous quarter
     const int nb = kb1 - kb0;                      // kb0 is a valid block even when nb == 0
     const int last = max(kb1 - 1, kb0);
     // every wave runs the same number of (padded) blocks: the largest
     // quarter rounded up to the ring, so all waves meet every barrier
-    const int nsteps = ((nblk + 3) / 4 + RING - 1) / RING * RING;
+    const int nsteps = ((nbs + 3) / 4 + RING - 1) / RING * RING;
     const int ntiles_b = (N + 31) / 32;            // packed 32-channel tiles
 
     auto a_tile = [&](int slot) {
@@ -290,7 +296,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     if (gm >= M) return;
     const int half = c0 / WN, ch = c0 % WN;
     const float *red0 = reinterpret_cast<const float *>(lds);
-    float *dst = C + (size_t)gm * N + n0 + c0;
+    float *dst = out + (size_t)gm * N + n0 + c0;
     const bool vec_store = (N & 3) == 0 && n0 + c0 + 16 <= N;
 #pragma unroll
     for (int j = 0; j < 16; j += 4) {
@@ -311,13 +317,17 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
 }
 
 hipError_t launch_gemm_int4b64(int M, int K, int N, const void *A, const void *Wp,
-                               const void *Sp, float *C, hipStream_t s) {
+                               const void *Sp, float *C, int nsplit, float *part,
+                               hipStream_t s) {
     const int tiles_m = div_up(M, BM), tiles_n = div_up(N, BN);
     const int xcd_bands = (tiles_n % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL(gemm_int4b64_kernel, dim3(tiles_m * tiles_n), dim3(64 * NWAVE), 0, s, M, K, N,
-                       tiles_m, tiles_n, xcd_bands, static_cast<const _Float16 *>(A),
-                       static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), C);
-    return hipGetLastError();
+    float *out = nsplit > 1 ? part : C;
+    hipLaunchKernelGGL(gemm_int4b64_kernel, dim3(tiles_m * tiles_n, nsplit), dim3(64 * NWAVE), 0, s,
+                       M, K, N, tiles_m, tiles_n, xcd_bands, static_cast<const _Float16 *>(A),
+                       static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), out);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || nsplit <= 1) return e;
+    return launch_splitk_reduce_f32(part, nsplit, M, N, C, s);
 }
 
 }  // namespace qg

@@ -69,6 +69,35 @@ W4A8Workspace w4a8_workspace(int M, int K) {
     return w;
 }
 
+int splitk_plan(qgemm_format f, int M, int K, int N) {
+    if (M <= 0 || N <= 0 || K <= 0) return 1;
+    long long tiles = 0;
+    int kunits = 0;                  // K granules a split must keep at least 2 of per wave
+    switch (f) {
+    case QGEMM_INT4_B64:
+        tiles = (long long)div_up(M, 64) * div_up(N, 128);
+        kunits = K / 64 / 8;         // four waves, two or more 64-blocks each
+        break;
+    default:
+        return 1;
+    }
+    if (tiles >= kSplitTargetCUs / 2) return 1;
+    long long sp = kSplitTargetCUs / tiles;
+    if (sp > kMaxSplit) sp = kMaxSplit;
+    if (sp > kunits) sp = kunits;
+    return sp < 2 ? 1 : (int)sp;
+}
+
+RunWorkspace run_workspace(qgemm_format f, int M, int K, int N) {
+    RunWorkspace r;
+    r.w4a8 = f == QGEMM_W4A8 ? w4a8_workspace(M, K) : W4A8Workspace{0, 0, 0, 0, 0};
+    r.nsplit = splitk_plan(f, M, K, N);
+    r.part_off = round_up(r.w4a8.bytes, kPackAlign);
+    r.part_bytes = r.nsplit > 1 ? round_up((size_t)r.nsplit * M * N * 4, kPackAlign) : 0;
+    r.bytes = r.part_off + r.part_bytes;
+    return r;
+}
+
 static size_t canonical_q_bytes(const Geometry &g, qgemm_format f) {
     switch (f) {
     case QGEMM_F32: return (size_t)g.K * g.N * sizeof(float);
@@ -139,7 +168,7 @@ qgemm_status qgemm_workspace_size(int M, int K, int N, qgemm_format f, size_t *b
     if (st != QGEMM_OK) return st;
     if (M < 0 || M > (1 << 24)) return QGEMM_ERR_SHAPE;
     if (!bytes) return QGEMM_ERR_NULL;
-    *bytes = (f == QGEMM_W4A8 && M > 0) ? w4a8_workspace(M, K).bytes : 0;
+    *bytes = (M > 0 && N > 0) ? run_workspace(f, M, K, N).bytes : 0;
     return QGEMM_OK;
 }
 

@@ -66,8 +66,13 @@ hipError_t launch_gemv_int4b64(int M, int K, int N, const void *A, const void *W
                                const void *Sp, float *C, hipStream_t s);
 hipError_t launch_gemv_int8b0(int M, int K, int N, const void *A, const void *Wp,
                               const void *Sp, float *C, hipStream_t s);
+// Tiled kernels with split-K: nsplit > 1 writes partial tiles to `part`
+// ([nsplit][M][N]) and adds them into C with a fixed-order reduce.
 hipError_t launch_gemm_int4b64(int M, int K, int N, const void *A, const void *Wp,
-                               const void *Sp, float *C, hipStream_t s);
+                               const void *Sp, float *C, int nsplit, float *part,
+                               hipStream_t s);
+hipError_t launch_splitk_reduce_f32(const float *part, int nsplit, int M, int N, float *C,
+                                    hipStream_t s);
 hipError_t launch_gemm_int8b0(int M, int K, int N, const void *A, const void *Wp,
                               const void *Sp, float *C, hipStream_t s);
 hipError_t launch_gemm_f32(int M, int K, int N, const float *A, const float *B,
@@ -87,5 +92,24 @@ struct W4A8Workspace {
     size_t qa_off, sa_off, S_off, bytes;
 };
 W4A8Workspace w4a8_workspace(int M, int K);
+
+// Split-K for the tiled (prefill) kernels. When a shape has too few output
+// tiles to occupy the chip, nsplit workgroups share each tile, each over a
+// contiguous range of K, and write partial tiles (fp32; int32 for W4A8) that a
+// reduce kernel adds in a fixed order, so results stay bit-reproducible. The
+// plan is a pure function of the shape (sized for a 256-CU part), so the
+// workspace size never depends on the device.
+constexpr int kSplitTargetCUs = 256;
+constexpr int kMaxSplit = 8;
+int splitk_plan(qgemm_format f, int M, int K, int N);      // 1 = no split
+
+// Full scratch layout of one call: the W4A8 part (if any) first, then the
+// split-K partials [nsplit][M][N] (4 bytes each) when nsplit > 1.
+struct RunWorkspace {
+    W4A8Workspace w4a8;       // bytes == 0 unless W4A8
+    int nsplit;
+    size_t part_off, part_bytes, bytes;
+};
+RunWorkspace run_workspace(qgemm_format f, int M, int K, int N);
 
 }  // namespace qg

@@ -70,3 +70,9 @@ def make_inputs(name: str):
         out["A"] = activations(rng, M, K, fp16=True)
         out["W"] = normal_weights(rng, N, K)
     return out
+
+
+# The benchmark page's default test sizes ("Default test sizes and the meaning
+# of M"): LLM linear layers (K, N) run at M in {8, 32, 128, 512}.
+PAGE_KN = [(2560, 4096), (2560, 1024), (4096, 2560), (2560, 9728), (9728, 2560)]
+PAGE_M = [8, 32, 128, 512]
