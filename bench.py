@@ -293,15 +293,30 @@ def page_grid(args, torch) -> int:
     return 0
 
 
+def launch_floor(torch, steps: int) -> None:
+    """Time per call of a trivial kernel (torch's fill of 1024 floats) under
+    the same replayed-graph protocol: the floor every per-call time here
+    includes."""
+    bufs = [torch.empty(1024, device="cuda") for _ in range(64)]
+    ms = time_calls(torch, lambda i: bufs[i].fill_(1.0), 64, steps)
+    print(json.dumps({"launch_floor": "fill 4 KiB", "ms_per_call": ms}), flush=True)
+
+
 def vendor_reference(args, torch) -> int:
     """The vendor libraries on the same prefill shapes, same protocol (rotated
     copies past twice the Infinity Cache, replayed graph, HIP events): dense
     fp16 x fp16 -> fp16 (torch.matmul) and int8 x int8 -> int32
     (torch._int_mm). Context for what the matrix cores reach on these shapes;
     never part of the metric."""
-    cases = [("fp16 matmul, dense weights", torch.float16, 512, 4096, 4096),
-             ("fp16 matmul, dense weights", torch.float16, 1024, 3072, 8192),
-             ("int8 _int_mm", torch.int8, 1024, 3072, 8192)]
+    from weight_quantized_gemm_amd import synth
+    if args.vendor_reference == "page-grid":
+        cases = [("fp16 matmul, dense weights", torch.float16, M, K, N)
+                 for K, N in synth.PAGE_KN for M in synth.PAGE_M]
+        launch_floor(torch, args.steps)
+    else:
+        cases = [("fp16 matmul, dense weights", torch.float16, 512, 4096, 4096),
+                 ("fp16 matmul, dense weights", torch.float16, 1024, 3072, 8192),
+                 ("int8 _int_mm", torch.int8, 1024, 3072, 8192)]
     for name, dt, M, K, N in cases:
         per = M * K * dt.itemsize + K * N * dt.itemsize + M * N * 4
         copies = max(2, -(-2 * MALL_BYTES // per) + 1)
@@ -358,10 +373,12 @@ def main() -> int:
     ap.add_argument("--page-grid", default="", metavar="FORMATS",
                     help="diagnostic: time the benchmark page's default (K, N) x M grid for the "
                          "comma-separated formats (f32,int8b0,int4b64,w4a8), one JSON line each")
-    ap.add_argument("--vendor-reference", action="store_true",
+    ap.add_argument("--vendor-reference", nargs="?", const="prefill", default="",
+                    choices=["prefill", "page-grid"],
                     help="context only: time torch's own fp16 GEMM and int8 GEMM (the vendor "
-                         "libraries) on the prefill shapes with the same rotation and print one "
-                         "JSON line per shape")
+                         "libraries) on the prefill shapes (or, with 'page-grid', fp16 on the "
+                         "benchmark page's grid plus a trivial-kernel floor) with the same "
+                         "rotation and print one JSON line per shape")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch's plain device copy of MIB MiB (fp32) 10 times, "
                          "the reference kernel for scaling the HBM byte counters")

@@ -46,7 +46,7 @@
 namespace qg {
 
 namespace {
-constexpr int BM = 64, BN = 128, BK = 64;
+constexpr int BM = kInt4TileM, BN = kInt4TileN, BK = 64;
 constexpr int NWAVE = 8;               // (N half, K quarter) per wave
 constexpr int WN = BN / 2;             // columns per wave
 constexpr int RF = BM / 32;            // 32-row accumulator tiles per wave

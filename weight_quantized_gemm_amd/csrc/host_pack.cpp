@@ -75,7 +75,7 @@ int splitk_plan(qgemm_format f, int M, int K, int N) {
     int kunits = 0;                  // K granules a split must keep at least 2 of per wave
     switch (f) {
     case QGEMM_INT4_B64:
-        tiles = (long long)div_up(M, 64) * div_up(N, 128);
+        tiles = (long long)div_up(M, kInt4TileM) * div_up(N, kInt4TileN);
         kunits = K / 64 / 8;         // four waves, two or more 64-blocks each
         break;
     default:

@@ -99,6 +99,9 @@ W4A8Workspace w4a8_workspace(int M, int K);
 // reduce kernel adds in a fixed order, so results stay bit-reproducible. The
 // plan is a pure function of the shape (sized for a 256-CU part), so the
 // workspace size never depends on the device.
+// Output tile of the Int4-Block64 prefill GEMM (rows x columns), shared by
+// the kernel and the split-K planner.
+constexpr int kInt4TileM = 64, kInt4TileN = 128;
 constexpr int kSplitTargetCUs = 256;
 constexpr int kMaxSplit = 8;
 int splitk_plan(qgemm_format f, int M, int K, int N);      // 1 = no split
