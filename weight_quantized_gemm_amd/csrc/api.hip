@@ -94,9 +94,12 @@ static qgemm_status run_w4a8(int M, int K, int N, const Geometry &g, const void 
     return launched(launch_w4a8_gemm(M, K, N, w.qa_stride, qa, sa, S, Bq, scales, C, D_debug, s));
 }
 
-// The GEMV kernels serve M <= the current GEMV limit (and K within the
-// register budget); everything else takes the tiled GEMM.
-static bool use_gemv(int M, int K) { return M <= gemv_max_m() && K <= kGemvMaxK; }
+// The Int4-Block64 and Int8-Block0 GEMV kernels serve M <= the current GEMV
+// limit (and K within the register budget); everything else takes a tiled
+// GEMM.
+static bool use_gemv(qgemm_format f, int M, int K) {
+    return (f == QGEMM_INT4_B64 || f == QGEMM_INT8_B0) && M <= gemv_max_m() && K <= kGemvMaxK;
+}
 
 // Scratch bytes one call actually touches: the W4A8 activation codes first,
 // then (when the GEMM is split along K) the partial tiles. The size reported to
@@ -110,7 +113,7 @@ static qgemm_status dispatch(int M, int K, int N, qgemm_format f, const Geometry
                              const void *A, const void *Bq, const void *scales, float *C,
                              void *ws, hipStream_t s) {
     (void)hipGetLastError();   // start from a clean per-thread error state
-    const bool gemv = use_gemv(M, K);
+    const bool gemv = use_gemv(f, M, K);
     const RunWorkspace r = run_workspace(f, M, K, N);
     const int nsplit = gemv ? 1 : r.nsplit;
     float *part = nsplit > 1 ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + r.part_off)
@@ -118,7 +121,7 @@ static qgemm_status dispatch(int M, int K, int N, qgemm_format f, const Geometry
     switch (f) {
     case QGEMM_F32:
         return launched(launch_gemm_f32(M, K, N, static_cast<const float *>(A),
-                                        static_cast<const float *>(Bq), C, s));
+                                        static_cast<const float *>(Bq), C, nsplit, part, s));
     case QGEMM_INT4_B64:
         return launched(gemv ? launch_gemv_int4b64(M, K, N, A, Bq, scales, C, s)
                              : launch_gemm_int4b64(M, K, N, A, Bq, scales, C, nsplit, part, s));
@@ -150,7 +153,7 @@ qgemm_status qgemm_run_ws(int M, int K, int N, qgemm_format f, const void *A,
     bool empty = false;
     qgemm_status st = check_run(M, K, N, f, A, Bq, scales, C, &g, &empty);
     if (st != QGEMM_OK || empty) return st;
-    const size_t need = used_bytes(run_workspace(f, M, K, N), use_gemv(M, K));
+    const size_t need = used_bytes(run_workspace(f, M, K, N), use_gemv(f, M, K));
     if (need > 0) {
         if (!workspace) return QGEMM_ERR_NULL;
         if (!aligned16(workspace)) return QGEMM_ERR_ALIGN;
@@ -171,7 +174,7 @@ qgemm_status qgemm_run(int M, int K, int N, qgemm_format f, const void *A, const
     st = check_device();
     if (st != QGEMM_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const size_t bytes = used_bytes(run_workspace(f, M, K, N), use_gemv(M, K));
+    const size_t bytes = used_bytes(run_workspace(f, M, K, N), use_gemv(f, M, K));
     if (bytes == 0) return dispatch(M, K, N, f, g, A, Bq, scales, C, nullptr, s);
     // Scratch (W4A8 codes, split-K partials), allocated and released in stream order.
     void *ws = nullptr;

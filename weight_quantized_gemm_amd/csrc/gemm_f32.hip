@@ -1,19 +1,27 @@
 // gemm_f32.hip -- the float-weight GEMM (MNN GemmSpeed benchmark page, mode 0
 // "float-gemm": C = A[M,K] x B[K,N] with B laid out {ic, oc} = {K, N}).
 //
-// The float workloads are tiny and bound by launch and memory latency, so
-// this is a plain LDS-tiled fp32 FMA kernel (16 x 64 or 64 x 64 tiles, K in
-// chunks of 64 loaded two chunks ahead) that handles any M, K, N: ragged tails are
-// masked and K == 0 writes zeros. Each output is one fp32 FMA chain over k
-// in increasing order.
+// An LDS-tiled fp32 FMA kernel (16 x 64 or 64 x 64 tiles, K in chunks of 64
+// loaded two chunks ahead) that handles any M, K, N. Every global load is
+// unconditional, from indices clamped into the arrays; values past K are
+// replaced by zero on both operands (so they add exactly zero) and rows or
+// columns past M or N are computed and never stored. With no skippable load
+// the two-chunk prefetch really stays in flight. Each output of a K-slice is
+// one fp32 FMA chain over k in increasing order.
+//
+// Split-K: shapes with few output tiles split the chunks into contiguous
+// slices over a third grid dimension; slice z writes partial tile z of a
+// [nsplit][M][N] scratch array, which a second kernel adds in slice order.
+// K == 0 writes zeros.
 #include "kernels_common.h"
 #include "qgemm_internal.h"
 
 namespace qg {
 
 namespace {
-constexpr int FT = 64;   // output tile width (columns)
-constexpr int FK = 64;   // K chunk staged in LDS
+constexpr int FT = kF32TileN;    // output tile width (columns)
+constexpr int FK = kF32ChunkK;   // K chunk staged in LDS
+static_assert(kF32TileMSmall == 16 && kF32TileM == 64, "tile rows are 16 TM with TM = 1 or 4");
 constexpr int FVB = FT * FK / 256;   // values of B each thread loads per chunk
 
 // One K chunk of the tile (16 TM rows x FT columns), held in registers
@@ -34,13 +42,15 @@ __device__ __forceinline__ void load_chunk(Chunk<TM> &c, int k0, int m0, int n0,
     for (int i = 0; i < Chunk<TM>::FVA; ++i) {
         const int idx = i * 256 + tid;
         const int gm = m0 + idx / FK, gk = k0 + idx % FK;
-        c.a[i] = (gm < M && gk < K) ? A[(size_t)gm * K + gk] : 0.f;
+        const float v = A[(size_t)min(gm, M - 1) * K + min(gk, K - 1)];
+        c.a[i] = gk < K ? v : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < FVB; ++i) {
         const int idx = i * 256 + tid;
         const int bk = k0 + idx / FT, bn = n0 + idx % FT;
-        c.b[i] = (bk < K && bn < N) ? B[(size_t)bk * N + bn] : 0.f;
+        const float v = B[(size_t)min(bk, K - 1) * N + min(bn, N - 1)];
+        c.b[i] = bk < K ? v : 0.f;
     }
 }
 }
@@ -68,16 +78,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(int M, int K, int N,
     // Chunks c and c + 1 are in flight while chunk c - 1 is multiplied: the
     // two-deep ring keeps the latency of a global load off the critical path
     // for all but the first chunk.
-    auto stage = [&](const Chunk<TM> &c) {
+    // values at k >= kend (past K or past this slice) are stored as zero
+    auto stage = [&](const Chunk<TM> &c, int k0, int kend) {
 #pragma unroll
         for (int i = 0; i < Chunk<TM>::FVA; ++i) {
             const int idx = i * 256 + tid;
-            As[idx % FK][idx / FK] = c.a[i];
+            As[idx % FK][idx / FK] = k0 + idx % FK < kend ? c.a[i] : 0.f;
         }
 #pragma unroll
         for (int i = 0; i < FVB; ++i) {
             const int idx = i * 256 + tid;
-            Bs[idx / FT][idx % FT] = c.b[i];
+            Bs[idx / FT][idx % FT] = k0 + idx / FT < kend ? c.b[i] : 0.f;
         }
     };
     auto multiply = [&]() {
@@ -95,23 +106,32 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(int M, int K, int N,
         }
     };
 
+    // this slice's chunks [c0, c1) (all of K without a split), padded to an
+    // even count: a padded chunk lies past K and adds exactly zero
     const int nch = (K + FK - 1) / FK;
+    const int c0 = (int)((long long)blockIdx.z * nch / gridDim.z);
+    const int c1 = (int)((long long)(blockIdx.z + 1) * nch / gridDim.z);
+    const int npad = (c1 - c0 + 1) & ~1;
     Chunk<TM> r0, r1;
-    if (nch > 0) load_chunk<TM>(r0, 0, m0, n0, M, K, N, A, B, tid);
-    if (nch > 1) load_chunk<TM>(r1, FK, m0, n0, M, K, N, A, B, tid);
-    for (int c = 0; c < nch; c += 2) {
-        stage(r0);
+    if (npad > 0) {            // K == 0 (or an empty slice) reads nothing
+        load_chunk<TM>(r0, c0 * FK, m0, n0, M, K, N, A, B, tid);
+        load_chunk<TM>(r1, (c0 + 1) * FK, m0, n0, M, K, N, A, B, tid);
+    }
+    for (int c = 0; c < npad; c += 2) {
+        // a chunk of this slice past c1 is masked like one past K
+        const int kend = min(K, c1 * FK);
+        stage(r0, (c0 + c) * FK, kend);
         __syncthreads();
-        if (c + 2 < nch) load_chunk<TM>(r0, (c + 2) * FK, m0, n0, M, K, N, A, B, tid);
+        load_chunk<TM>(r0, min(c0 + c + 2, nch) * FK, m0, n0, M, K, N, A, B, tid);
         multiply();
         __syncthreads();
-        if (c + 1 >= nch) break;
-        stage(r1);
+        stage(r1, (c0 + c + 1) * FK, kend);
         __syncthreads();
-        if (c + 3 < nch) load_chunk<TM>(r1, (c + 3) * FK, m0, n0, M, K, N, A, B, tid);
+        load_chunk<TM>(r1, min(c0 + c + 3, nch) * FK, m0, n0, M, K, N, A, B, tid);
         multiply();
         __syncthreads();
     }
+    float *const out = C + (size_t)blockIdx.z * M * N;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int gm = m0 + ty * TM + i;
@@ -119,21 +139,24 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(int M, int K, int N,
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int gn = n0 + tx * 4 + j;
-            if (gn < N) C[(size_t)gm * N + gn] = acc[i][j];
+            if (gn < N) out[(size_t)gm * N + gn] = acc[i][j];
         }
     }
 }
 
 hipError_t launch_gemm_f32(int M, int K, int N, const float *A, const float *B, float *C,
-                           hipStream_t s) {
-    if (M <= 16) {
-        hipLaunchKernelGGL(gemm_f32_kernel<1>, dim3(div_up(N, FT), div_up(M, 16)), dim3(256), 0,
-                           s, M, K, N, A, B, C);
+                           int nsplit, float *part, hipStream_t s) {
+    float *out = nsplit > 1 ? part : C;
+    if (M <= kF32TileMSmall) {
+        hipLaunchKernelGGL(gemm_f32_kernel<1>, dim3(div_up(N, FT), div_up(M, 16), nsplit),
+                           dim3(256), 0, s, M, K, N, A, B, out);
     } else {
-        hipLaunchKernelGGL(gemm_f32_kernel<4>, dim3(div_up(N, FT), div_up(M, 64)), dim3(256), 0,
-                           s, M, K, N, A, B, C);
+        hipLaunchKernelGGL(gemm_f32_kernel<4>, dim3(div_up(N, FT), div_up(M, 64), nsplit),
+                           dim3(256), 0, s, M, K, N, A, B, out);
     }
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || nsplit <= 1) return e;
+    return launch_splitk_reduce_f32(part, nsplit, M, N, C, s);
 }
 
 }  // namespace qg

@@ -72,11 +72,16 @@ W4A8Workspace w4a8_workspace(int M, int K) {
 int splitk_plan(qgemm_format f, int M, int K, int N) {
     if (M <= 0 || N <= 0 || K <= 0) return 1;
     long long tiles = 0;
-    int kunits = 0;                  // K granules a split must keep at least 2 of per wave
+    int kunits = 0;                  // K granules: the most slices a split may have
     switch (f) {
     case QGEMM_INT4_B64:
         tiles = (long long)div_up(M, kInt4TileM) * div_up(N, kInt4TileN);
         kunits = K / 64 / 8;         // four waves, two or more 64-blocks each
+        break;
+    case QGEMM_F32:
+        tiles = (long long)div_up(M, M <= kF32TileMSmall ? kF32TileMSmall : kF32TileM) *
+                div_up(N, kF32TileN);
+        kunits = div_up(K, kF32ChunkK);   // one or more chunks per slice
         break;
     default:
         return 1;

@@ -75,8 +75,8 @@ hipError_t launch_splitk_reduce_f32(const float *part, int nsplit, int M, int N,
                                     hipStream_t s);
 hipError_t launch_gemm_int8b0(int M, int K, int N, const void *A, const void *Wp,
                               const void *Sp, float *C, hipStream_t s);
-hipError_t launch_gemm_f32(int M, int K, int N, const float *A, const float *B,
-                           float *C, hipStream_t s);
+hipError_t launch_gemm_f32(int M, int K, int N, const float *A, const float *B, float *C,
+                           int nsplit, float *part, hipStream_t s);
 // W4A8: qa [M][Kq] int8 (Kq = roundup(K, 128)), sa [M] float, S [M] int32
 // live in the workspace.
 hipError_t launch_w4a8_actquant(int M, int K, int Kq, const void *A, int8_t *qa,
@@ -102,6 +102,9 @@ W4A8Workspace w4a8_workspace(int M, int K);
 // Output tile of the Int4-Block64 prefill GEMM (rows x columns), shared by
 // the kernel and the split-K planner.
 constexpr int kInt4TileM = 64, kInt4TileN = 128;
+// Output tiles of the fp32 GEMM: 16 x 64 for M <= 16, else 64 x 64; K in
+// chunks of 64.
+constexpr int kF32TileN = 64, kF32TileMSmall = 16, kF32TileM = 64, kF32ChunkK = 64;
 constexpr int kSplitTargetCUs = 256;
 constexpr int kMaxSplit = 8;
 int splitk_plan(qgemm_format f, int M, int K, int N);      // 1 = no split
