@@ -93,6 +93,12 @@ def test_split_k_workspace_plan():
     assert sz(64, 448, 128) == 0                          # 7 K-blocks: too short to split
     assert sz(1, 4096, 4096) == sz(1, 4096, 4096)         # pure function of the shape
     assert Q.qgemm_workspace_size(64, 4096, 512, "int8b0") == 0
+    # fp32: 16x64 / 64x64 tiles; below 256 tiles each workgroup has two
+    # K-groups, and a cross-workgroup split only when that is still short and
+    # every group of every slice keeps four or more 64-wide chunks
+    assert Q.qgemm_workspace_size(16, 256, 256, "f32") == 0          # 4 tiles x 2 groups, 2 chunks each
+    assert Q.qgemm_workspace_size(8, 2560, 1024, "f32") == 5 * 8 * 1024 * 4   # 40 chunks / (2 x 4)
+    assert Q.qgemm_workspace_size(512, 4096, 4096, "f32") == 0       # 512 tiles
     w = Q.qgemm_workspace_size(8, 128, 16, "w4a8")
     assert w == Q.qgemm_workspace_size(8, 128, 16000, "w4a8")   # W4A8 scratch has no N part
 

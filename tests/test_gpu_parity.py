@@ -153,12 +153,16 @@ def test_int4b64_split_k(M, K, N):
     assert np.array_equal(C1, C2) and np.array_equal(C1, C3)
 
 
-@pytest.mark.parametrize("M,K,N", [(16, 256, 256), (3, 137, 70), (8, 2560, 1024), (1, 9728, 64),
-                                   (40, 640, 100)])
-def test_f32_split_k(M, K, N):
-    """fp32 shapes with few output tiles split K over workgroups (chunks of
-    64, the last one ragged): parity, run vs run_ws and repeats bit-identical."""
-    assert Q.qgemm_workspace_size(M, K, N, "f32") >= 2 * M * N * 4   # the split engages
+@pytest.mark.parametrize("M,K,N,split", [(16, 256, 256, False), (3, 137, 70, False),
+                                         (8, 2560, 1024, True), (1, 9728, 64, True),
+                                         (40, 640, 100, False), (17, 4096, 4096, True),
+                                         (64, 8192, 256, True)])
+def test_f32_split_k(M, K, N, split):
+    """fp32 shapes with few output tiles spread K over two thread groups per
+    workgroup and, when that is still too few, over workgroups (chunks of 64,
+    the last one ragged): parity, run vs run_ws and repeats bit-identical."""
+    ws = Q.qgemm_workspace_size(M, K, N, "f32")
+    assert (ws >= 2 * M * N * 4) if split else ws == 0
     A, W, _ = _case("f32", M, K, N, seed=M + K + N)
     C1 = run("f32", M, K, N, A, W, None)
     compare(C1, O.gemm_f32(A, W), f"f32 split {M}x{K}x{N}")

@@ -6,13 +6,17 @@
 // unconditional, from indices clamped into the arrays; values past K are
 // replaced by zero on both operands (so they add exactly zero) and rows or
 // columns past M or N are computed and never stored. With no skippable load
-// the two-chunk prefetch really stays in flight. Each output of a K-slice is
-// one fp32 FMA chain over k in increasing order.
+// the two-chunk prefetch really stays in flight.
 //
-// Split-K: shapes with few output tiles split the chunks into contiguous
-// slices over a third grid dimension; slice z writes partial tile z of a
-// [nsplit][M][N] scratch array, which a second kernel adds in slice order.
-// K == 0 writes zeros.
+// Work along K is spread two ways when a shape has few output tiles:
+//  - inside a workgroup, KG groups of 256 threads each take a contiguous
+//    share of the tile's chunks with their own LDS tiles; their partial
+//    tiles are added in LDS in group order (no second launch);
+//  - across workgroups, a third grid dimension splits the chunks into
+//    contiguous slices; slice z writes partial tile z of a [nsplit][M][N]
+//    scratch array, which a second kernel adds in slice order.
+// Each output of a group's share is one fp32 FMA chain over k in increasing
+// order. K == 0 writes zeros.
 #include "kernels_common.h"
 #include "qgemm_internal.h"
 
@@ -55,18 +59,28 @@ __device__ __forceinline__ void load_chunk(Chunk<TM> &c, int k0, int m0, int n0,
 }
 }
 
-// Tile of 16 TM rows x 64 columns; thread (tx, ty) of the 16 x 16 grid owns
-// rows ty * TM .. + TM - 1 and columns tx * 4 .. + 3. TM = 1 keeps small-M
-// products spread over more CUs without idle rows.
+// Tile of 16 TM rows x 64 columns; in each 256-thread group, thread
+// (tx, ty) of the 16 x 16 grid owns rows ty * TM .. + TM - 1 and columns
+// tx * 4 .. + 3. TM = 1 keeps small-M products spread over more CUs without
+// idle rows.
 template <int TM>
-__global__ __launch_bounds__(256) void gemm_f32_kernel(int M, int K, int N,
-                                                       const float *__restrict__ A,
-                                                       const float *__restrict__ B,
-                                                       float *__restrict__ C) {
+struct F32Tiles {
+    float As[FK][16 * TM + 4];   // A chunk transposed: As[k][m]
+    float Bs[FK][FT + 4];
+};
+
+template <int TM, int KG>
+__global__ __launch_bounds__(256 * KG) void gemm_f32_kernel(int M, int K, int N,
+                                                            const float *__restrict__ A,
+                                                            const float *__restrict__ B,
+                                                            float *__restrict__ C) {
     constexpr int BM = 16 * TM;
-    __shared__ float As[FK][BM + 4];   // A chunk transposed: As[k][m]
-    __shared__ float Bs[FK][FT + 4];
-    const int tid = threadIdx.x;
+    constexpr size_t TILE_BYTES = KG * sizeof(F32Tiles<TM>);
+    constexpr size_t RED_BYTES = (KG > 1 ? KG : 0) * (size_t)BM * (FT + 4) * sizeof(float);
+    __shared__ __align__(16) unsigned char smem[TILE_BYTES > RED_BYTES ? TILE_BYTES : RED_BYTES];
+    const int gi = uniform(threadIdx.x >> 8);
+    const int tid = threadIdx.x & 255;
+    F32Tiles<TM> &T = reinterpret_cast<F32Tiles<TM> *>(smem)[gi];
     const int tx = tid & 15, ty = tid >> 4;
     const int m0 = blockIdx.y * BM, n0 = blockIdx.x * FT;
     float acc[TM][4];
@@ -75,20 +89,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(int M, int K, int N,
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
 
-    // Chunks c and c + 1 are in flight while chunk c - 1 is multiplied: the
-    // two-deep ring keeps the latency of a global load off the critical path
-    // for all but the first chunk.
-    // values at k >= kend (past K or past this slice) are stored as zero
+    // values at k >= kend (past K or past this group's share) are stored as zero
     auto stage = [&](const Chunk<TM> &c, int k0, int kend) {
 #pragma unroll
         for (int i = 0; i < Chunk<TM>::FVA; ++i) {
             const int idx = i * 256 + tid;
-            As[idx % FK][idx / FK] = k0 + idx % FK < kend ? c.a[i] : 0.f;
+            T.As[idx % FK][idx / FK] = k0 + idx % FK < kend ? c.a[i] : 0.f;
         }
 #pragma unroll
         for (int i = 0; i < FVB; ++i) {
             const int idx = i * 256 + tid;
-            Bs[idx / FT][idx % FT] = k0 + idx / FT < kend ? c.b[i] : 0.f;
+            T.Bs[idx / FT][idx % FT] = k0 + idx / FT < kend ? c.b[i] : 0.f;
         }
     };
     auto multiply = [&]() {
@@ -96,9 +107,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(int M, int K, int N,
         for (int kk = 0; kk < FK; ++kk) {
             float a[TM], b[4];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) a[i] = As[kk][ty * TM + i];
+            for (int i = 0; i < TM; ++i) a[i] = T.As[kk][ty * TM + i];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+            for (int j = 0; j < 4; ++j) b[j] = T.Bs[kk][tx * 4 + j];
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -106,30 +117,55 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(int M, int K, int N,
         }
     };
 
-    // this slice's chunks [c0, c1) (all of K without a split), padded to an
-    // even count: a padded chunk lies past K and adds exactly zero
+    // chunks of this slice [s0, s1) (all of K without a split), then this
+    // group's share [c0, c1); every group runs the same padded, even number
+    // of iterations (a chunk past its share is neither staged nor
+    // multiplied: a uniform branch that contains no load)
     const int nch = (K + FK - 1) / FK;
-    const int c0 = (int)((long long)blockIdx.z * nch / gridDim.z);
-    const int c1 = (int)((long long)(blockIdx.z + 1) * nch / gridDim.z);
-    const int npad = (c1 - c0 + 1) & ~1;
+    const int s0 = (int)((long long)blockIdx.z * nch / gridDim.z);
+    const int s1 = (int)((long long)(blockIdx.z + 1) * nch / gridDim.z);
+    const int c0 = s0 + gi * (s1 - s0) / KG, c1 = s0 + (gi + 1) * (s1 - s0) / KG;
+    const int npad = ((s1 - s0 + KG - 1) / KG + 1) & ~1;
+    const int kend = min(K, c1 * FK);
     Chunk<TM> r0, r1;
     if (npad > 0) {            // K == 0 (or an empty slice) reads nothing
         load_chunk<TM>(r0, c0 * FK, m0, n0, M, K, N, A, B, tid);
         load_chunk<TM>(r1, (c0 + 1) * FK, m0, n0, M, K, N, A, B, tid);
     }
     for (int c = 0; c < npad; c += 2) {
-        // a chunk of this slice past c1 is masked like one past K
-        const int kend = min(K, c1 * FK);
-        stage(r0, (c0 + c) * FK, kend);
+        const bool live0 = c0 + c < c1, live1 = c0 + c + 1 < c1;
+        if (live0) stage(r0, (c0 + c) * FK, kend);
         __syncthreads();
         load_chunk<TM>(r0, min(c0 + c + 2, nch) * FK, m0, n0, M, K, N, A, B, tid);
-        multiply();
+        if (live0) multiply();
         __syncthreads();
-        stage(r1, (c0 + c + 1) * FK, kend);
+        if (live1) stage(r1, (c0 + c + 1) * FK, kend);
         __syncthreads();
         load_chunk<TM>(r1, min(c0 + c + 3, nch) * FK, m0, n0, M, K, N, A, B, tid);
-        multiply();
+        if (live1) multiply();
         __syncthreads();
+    }
+
+    // the groups' partial tiles meet in LDS (reusing the tiles' space) and
+    // are added in group order
+    if (KG > 1) {
+        float *red = reinterpret_cast<float *>(smem);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                red[((size_t)gi * BM + ty * TM + i) * (FT + 4) + tx * 4 + j] = acc[i][j];
+        __syncthreads();
+        if (gi != 0) return;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float v = red[(size_t)(ty * TM + i) * (FT + 4) + tx * 4 + j];
+#pragma unroll
+                for (int g = 1; g < KG; ++g) v += red[((size_t)g * BM + ty * TM + i) * (FT + 4) + tx * 4 + j];
+                acc[i][j] = v;
+            }
     }
     float *const out = C + (size_t)blockIdx.z * M * N;
 #pragma unroll
@@ -147,12 +183,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(int M, int K, int N,
 hipError_t launch_gemm_f32(int M, int K, int N, const float *A, const float *B, float *C,
                            int nsplit, float *part, hipStream_t s) {
     float *out = nsplit > 1 ? part : C;
-    if (M <= kF32TileMSmall) {
-        hipLaunchKernelGGL(gemm_f32_kernel<1>, dim3(div_up(N, FT), div_up(M, 16), nsplit),
-                           dim3(256), 0, s, M, K, N, A, B, out);
+    const bool small = M <= kF32TileMSmall;
+    const dim3 grid(div_up(N, FT), div_up(M, small ? kF32TileMSmall : kF32TileM), nsplit);
+    if (f32_kgroups(M, N) > 1) {
+        if (small) hipLaunchKernelGGL((gemm_f32_kernel<1, kF32KGroups>), grid, dim3(256 * kF32KGroups), 0, s, M, K, N, A, B, out);
+        else hipLaunchKernelGGL((gemm_f32_kernel<4, kF32KGroups>), grid, dim3(256 * kF32KGroups), 0, s, M, K, N, A, B, out);
     } else {
-        hipLaunchKernelGGL(gemm_f32_kernel<4>, dim3(div_up(N, FT), div_up(M, 64), nsplit),
-                           dim3(256), 0, s, M, K, N, A, B, out);
+        if (small) hipLaunchKernelGGL((gemm_f32_kernel<1, 1>), grid, dim3(256), 0, s, M, K, N, A, B, out);
+        else hipLaunchKernelGGL((gemm_f32_kernel<4, 1>), grid, dim3(256), 0, s, M, K, N, A, B, out);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nsplit <= 1) return e;

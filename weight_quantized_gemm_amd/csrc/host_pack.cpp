@@ -69,6 +69,12 @@ W4A8Workspace w4a8_workspace(int M, int K) {
     return w;
 }
 
+int f32_kgroups(int M, int N) {
+    const long long tiles = (long long)div_up(M, M <= kF32TileMSmall ? kF32TileMSmall : kF32TileM) *
+                            div_up(N, kF32TileN);
+    return tiles < kSplitTargetCUs ? kF32KGroups : 1;
+}
+
 int splitk_plan(qgemm_format f, int M, int K, int N) {
     if (M <= 0 || N <= 0 || K <= 0) return 1;
     long long tiles = 0;
@@ -78,11 +84,16 @@ int splitk_plan(qgemm_format f, int M, int K, int N) {
         tiles = (long long)div_up(M, kInt4TileM) * div_up(N, kInt4TileN);
         kunits = K / 64 / 8;         // four waves, two or more 64-blocks each
         break;
-    case QGEMM_F32:
+    case QGEMM_F32: {
+        // the K-groups of a workgroup share its CU, so only the split spreads
+        // a tile over more CUs; a split costs a second launch, so each group
+        // of each slice keeps four or more chunks
+        const int kg = f32_kgroups(M, N);
         tiles = (long long)div_up(M, M <= kF32TileMSmall ? kF32TileMSmall : kF32TileM) *
                 div_up(N, kF32TileN);
-        kunits = div_up(K, kF32ChunkK);   // one or more chunks per slice
+        kunits = div_up(K, kF32ChunkK) / (kg * 4);
         break;
+    }
     default:
         return 1;
     }

@@ -105,6 +105,10 @@ constexpr int kInt4TileM = 64, kInt4TileN = 128;
 // Output tiles of the fp32 GEMM: 16 x 64 for M <= 16, else 64 x 64; K in
 // chunks of 64.
 constexpr int kF32TileN = 64, kF32TileMSmall = 16, kF32TileM = 64, kF32ChunkK = 64;
+// K-groups (256 threads each) inside an fp32 workgroup when the shape has
+// fewer output tiles than CUs; 1 otherwise.
+constexpr int kF32KGroups = 2;
+int f32_kgroups(int M, int N);
 constexpr int kSplitTargetCUs = 256;
 constexpr int kMaxSplit = 8;
 int splitk_plan(qgemm_format f, int M, int K, int N);      // 1 = no split
