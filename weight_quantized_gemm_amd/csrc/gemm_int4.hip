@@ -37,9 +37,11 @@
 // every 64-wide block in MFMA step s, for its A row and B column alike (the K
 // order inside an MFMA only has to agree between A and B).
 //
-// The 256 tiles of a 512 x 4096 output are dealt so that each XCD (the
-// hardware deals workgroups to XCDs round-robin) owns a band of four B
-// tiles across all row tiles: B is read from HBM once and A stays in L2.
+// Tiles are dealt to XCDs (the hardware deals workgroups to them
+// round-robin, and each has its own L2) as a grid of row bands x column
+// bands: each XCD fetches only its bands of A and B. For 512 x 4096 the
+// host picks 2 x 4 (A read by four XCDs, B by two), fewer bytes than one
+// column band per XCD across all rows.
 #include "kernels_common.h"
 #include "qgemm_internal.h"
 
@@ -96,7 +98,7 @@ __device__ __forceinline__ h8_t dequant8(unsigned word, const DqParams &p, unsig
 }
 
 __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
-    int M, int K, int N, int tiles_m, int tiles_n, int xcd_bands,
+    int M, int K, int N, int tiles_m, int tiles_n, int xcd_rows,
     const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ Sp, float *__restrict__ C) {
     __shared__ __align__(16) unsigned char lds[LDS_BYTES];
@@ -104,12 +106,14 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     // ---- tile of this workgroup ----
     const int L = blockIdx.x;
     int tm, tn;
-    if (xcd_bands) {
-        // XCD x = L % 8 owns B tiles [x * bw, (x + 1) * bw) for every row tile
-        const int bw = tiles_n / 8;
-        const int j = L / 8;
-        tn = (L % 8) * bw + j % bw;
-        tm = j / bw;
+    if (xcd_rows > 0) {
+        // the eight XCDs form an xcd_rows x (8 / xcd_rows) grid over the
+        // tiles; XCD x = L % 8 owns row band x / gc and column band x % gc
+        const int gc = 8 / xcd_rows;
+        const int rb = tiles_m / xcd_rows, cb = tiles_n / gc;
+        const int x = L % 8, j = L / 8;
+        tm = (x / gc) * rb + j / cb;
+        tn = (x % gc) * cb + j % cb;
     } else {
         tm = L / tiles_n;
         tn = L % tiles_n;
@@ -320,10 +324,21 @@ hipError_t launch_gemm_int4b64(int M, int K, int N, const void *A, const void *W
                                const void *Sp, float *C, int nsplit, float *part,
                                hipStream_t s) {
     const int tiles_m = div_up(M, BM), tiles_n = div_up(N, BN);
-    const int xcd_bands = (tiles_n % 8 == 0) ? 1 : 0;
+    // XCD grid: row bands x column bands = 8, each XCD's L2 then fetches
+    // A of its row band and B of its column band; pick the grid the tile
+    // counts divide that fetches the fewest bytes (0: plain order)
+    int xcd_rows = 0;
+    double best = 0;
+    const double a_bytes = (double)M * K * 2, b_bytes = (double)N * K * 0.625;
+    for (int gr = 1; gr <= 8; gr *= 2) {
+        const int gc = 8 / gr;
+        if (tiles_m % gr || tiles_n % gc) continue;
+        const double fetched = gc * a_bytes + gr * b_bytes;
+        if (xcd_rows == 0 || fetched < best) { xcd_rows = gr; best = fetched; }
+    }
     float *out = nsplit > 1 ? part : C;
     hipLaunchKernelGGL(gemm_int4b64_kernel, dim3(tiles_m * tiles_n, nsplit), dim3(64 * NWAVE), 0, s,
-                       M, K, N, tiles_m, tiles_n, xcd_bands, static_cast<const _Float16 *>(A),
+                       M, K, N, tiles_m, tiles_n, xcd_rows, static_cast<const _Float16 *>(A),
                        static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nsplit <= 1) return e;
