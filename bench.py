@@ -38,9 +38,10 @@ FP16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
 MALL_BYTES = 256 << 20
 
 
-def algorithmic_bytes(M: int, K: int, N: int, fmt: str = "int4b64") -> int:
+def algorithmic_bytes(M: int, K: int, N: int, fmt: str = "int4b64", epi: dict | None = None) -> int:
     """Bytes the product must move at least once: A, the stored weight codes,
-    the fp32 [offset, scale] pairs and C (fp32). Int4 formats hold K/2 bytes of
+    the fp32 [offset, scale] pairs and C (fp32, or fp16 with an fp16
+    epilogue, plus its bias and residual). Int4 formats hold K/2 bytes of
     codes per channel, Int8-Block0 K bytes, fp32 B 4*K*N bytes; Int4-Block64
     has K/64 pairs per channel, the per-channel formats one."""
     a_bytes = M * K * (4 if fmt == "f32" else 2)
@@ -52,7 +53,11 @@ def algorithmic_bytes(M: int, K: int, N: int, fmt: str = "int4b64") -> int:
         w_bytes, p_bytes = N * K // 2, N * (K // 64) * 8
     else:  # w4a8
         w_bytes, p_bytes = N * K // 2, 8 * N
-    return a_bytes + w_bytes + p_bytes + M * N * 4
+    c_elem = 2 if epi and epi["out"] == "f16" else 4
+    e_bytes = 0
+    if epi:
+        e_bytes = (4 * N if epi["bias"] else 0) + (M * N * c_elem if epi["residual"] else 0)
+    return a_bytes + w_bytes + p_bytes + M * N * c_elem + e_bytes
 
 
 def flops(M: int, K: int, N: int) -> int:
@@ -62,11 +67,12 @@ def flops(M: int, K: int, N: int) -> int:
 class Workload:
     """Packed weights, activations and outputs of one named shape, R copies."""
 
-    def __init__(self, name: str, copies: int):
+    def __init__(self, name: str, copies: int, epi: dict | None = None):
         import torch
         from weight_quantized_gemm_amd import qgemm as Q
         from weight_quantized_gemm_amd import synth
         inp = synth.make_inputs(name)
+        self.epi = epi
         self.name = name
         self.fmt = inp["format"]
         self.M, self.K, self.N = inp["M"], inp["K"], inp["N"]
@@ -88,8 +94,14 @@ class Workload:
         else:
             S0 = torch.from_numpy(sp).cuda()
             self.S = [S0] + [S0.clone() for _ in range(copies - 1)]
-        self.C = [torch.empty((self.M, self.N), dtype=torch.float32, device="cuda")
-                  for _ in range(copies)]
+        cdt = torch.float16 if epi and epi["out"] == "f16" else torch.float32
+        self.C = [torch.empty((self.M, self.N), dtype=cdt, device="cuda") for _ in range(copies)]
+        if epi:
+            g = torch.Generator(device="cuda").manual_seed(3)
+            self.bias = (torch.randn(self.N, device="cuda", generator=g)
+                         if epi["bias"] else None)
+            self.res = ([torch.randn((self.M, self.N), device="cuda", generator=g).to(cdt)
+                         for _ in range(copies)] if epi["residual"] else None)
         # caller-owned scratch (W4A8 activation codes), so the timed region allocates nothing
         self.ws_bytes = Q.qgemm_workspace_size(self.M, self.K, self.N, self.fmt)
         self.ws = (torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
@@ -101,6 +113,13 @@ class Workload:
 
     def run(self, i: int) -> None:
         c = i % len(self.A)
+        if self.epi:
+            self.Q.qgemm_run_ex(self.M, self.K, self.N, self.fmt, self.A[c], self.B[c], self.S[c],
+                                self.C[c], bias=self.bias,
+                                residual=self.res[c] if self.res else None,
+                                activation=self.epi["act"], out_type=self.epi["out"],
+                                workspace=self.ws, ws_bytes=self.ws_bytes)
+            return
         self.Q.qgemm_run_ws(self.M, self.K, self.N, self.fmt, self.A[c], self.B[c], self.S[c],
                             self.C[c], self.ws, self.ws_bytes)
 
@@ -163,15 +182,30 @@ def cpu_baseline(dec: Workload, pre: Workload, budget_s: float):
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
 
 
+def parse_epilogue(spec: str):
+    """'bias,residual,silu,f16' -> {'bias': True, 'residual': True, 'act': 'silu',
+    'out': 'f16'}; empty -> None (the plain call)."""
+    if not spec:
+        return None
+    parts = {p.strip() for p in spec.split(",") if p.strip()}
+    acts = parts & {"relu", "silu", "gelu"}
+    unknown = parts - {"bias", "residual", "f16", "f32"} - acts
+    if unknown or len(acts) > 1:
+        raise SystemExit(f"bad --epilogue {spec!r}")
+    return {"bias": "bias" in parts, "residual": "residual" in parts,
+            "act": next(iter(acts), "none"), "out": "f16" if "f16" in parts else "f32"}
+
+
 def single_workload(args, torch) -> int:
     """Times one named workload alone (all launches of one qgemm_run call,
     weights rotated past twice the Infinity Cache) and prints a diagnostic
     JSON line with its roofline fraction."""
     from weight_quantized_gemm_amd import synth
     fmt, M, K, N, _ = synth.CONFIGS[args.workload]
-    per_copy = algorithmic_bytes(M, K, N, fmt)
+    epi = parse_epilogue(args.epilogue)
+    per_copy = algorithmic_bytes(M, K, N, fmt, epi)
     copies = args.copies or min(256, max(2, -(-2 * MALL_BYTES // per_copy) + 1))
-    w = Workload(args.workload, copies)
+    w = Workload(args.workload, copies, epi)
     for i in range(args.warmup):
         w.run(i)
     torch.cuda.synchronize()
@@ -191,7 +225,7 @@ def single_workload(args, torch) -> int:
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / (reps * copies)
     fl = flops(M, K, N)
-    by = algorithmic_bytes(M, K, N, fmt)
+    by = algorithmic_bytes(M, K, N, fmt, epi)
     if fmt == "w4a8":
         bound, achieved, peak, unit = "mfma", fl / ms / 1e9, INT8_PEAK_TOPS, "TOP/s"
     elif M == 1:
@@ -202,7 +236,7 @@ def single_workload(args, torch) -> int:
         bound, achieved, peak, unit = "mfma", fl / ms / 1e9, FP16_PEAK_TFLOPS, "TFLOP/s"
     print(json.dumps({
         "workload": args.workload, "format": fmt, "M": M, "K": K, "N": N,
-        "rotation_copies": copies, "launches": reps * copies, "ms_per_call": ms,
+        "epilogue": args.epilogue or None, "rotation_copies": copies, "launches": reps * copies, "ms_per_call": ms,
         "gflops": fl / ms / 1e6, "algorithmic_bytes": by, "gb_s": by / ms / 1e6,
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak},
@@ -370,6 +404,9 @@ def main() -> int:
                     help="diagnostic: time only this named workload (" +
                          ", ".join(("f32", "int8b0_decode", "int4b64_decode", "int4b64_prefill",
                                     "w4a8_prefill")) + ") and print its own JSON line")
+    ap.add_argument("--epilogue", default="", metavar="SPEC",
+                    help="with --workload: time the call with a fused epilogue, a comma list of "
+                         "bias, residual, one of relu/silu/gelu, and f16 (fp16 C and residual)")
     ap.add_argument("--page-grid", default="", metavar="FORMATS",
                     help="diagnostic: time the benchmark page's default (K, N) x M grid for the "
                          "comma-separated formats (f32,int8b0,int4b64,w4a8), one JSON line each")

@@ -204,6 +204,60 @@ qgemm_status qgemm_run_ws(int M, int K, int N, qgemm_format f, const void *A,
                           void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * Fused epilogue (SimdPaddleOCR pull request, the GEMM change that keeps
+ * accumulators in fp32 until bias, residual and activation are applied):
+ *
+ *   C[m][n] = act(P[m][n] + bias[n] + residual[m][n])
+ *
+ * with P = A x B the fp32-accumulated product, every step in fp32 in the
+ * order written, and C stored once as fp32 or rounded once to fp16 (round
+ * to nearest even). Fields:
+ *   bias        device, float [N], or NULL (no bias).
+ *   residual    device, [M][N] row-major in C's type (float or fp16), or
+ *               NULL. It may be the same buffer as C (an in-place residual
+ *               update): each element is read before it is written, by the
+ *               same thread.
+ *   activation  QGEMM_ACT_NONE, _RELU (max(x, 0)), _SILU (x / (1 + e^-x)) or
+ *               _GELU (x * Phi(x), Phi the standard normal CDF, via erf).
+ *   out_type    QGEMM_OUT_F32: C is float [M][N]; QGEMM_OUT_F16: C is fp16
+ *               [M][N].
+ * bias and residual must be 16-byte aligned.
+ */
+typedef enum qgemm_activation {
+    QGEMM_ACT_NONE = 0,
+    QGEMM_ACT_RELU = 1,
+    QGEMM_ACT_SILU = 2,
+    QGEMM_ACT_GELU = 3
+} qgemm_activation;
+
+typedef enum qgemm_out_type {
+    QGEMM_OUT_F32 = 0,
+    QGEMM_OUT_F16 = 1
+} qgemm_out_type;
+
+typedef struct qgemm_epilogue {
+    const float *bias;
+    const void *residual;
+    int activation;
+    int out_type;
+} qgemm_epilogue;
+
+/*
+ * qgemm_run with a fused epilogue (`epi` may be NULL: none, fp32 C) and an
+ * optional caller workspace: with workspace == NULL and ws_bytes == 0 any
+ * scratch the shape needs is allocated stream-ordered as in qgemm_run;
+ * otherwise it is used as in qgemm_run_ws. C is float or fp16 per
+ * epi->out_type. Split-K shapes apply the epilogue once, after their slices
+ * are added.
+ * Errors: as qgemm_run_ws; ERR_FORMAT for an unknown activation or output
+ * type; ERR_ALIGN for misaligned bias or residual.
+ */
+qgemm_status qgemm_run_ex(int M, int K, int N, qgemm_format f, const void *A,
+                          const void *Bq, const void *scales, void *C,
+                          const qgemm_epilogue *epi, void *workspace,
+                          size_t ws_bytes, void *stream);
+
+/*
  * W4A8 with its intermediate results exposed, for bit-exact checks of the
  * integer path: the quantised activations qa (int8 [M][K]), the row scales
  * sa (float [M]), the row sums S of qa (int32 [M]) and the exact integer

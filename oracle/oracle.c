@@ -284,3 +284,62 @@ int orc_w4a8_dequant_product(int M, int K, int N, const int8_t *qa,
         }
     return ORC_OK;
 }
+
+/*
+ * The fused epilogue of the SimdPaddleOCR pull request (the GEMM keeps its
+ * accumulators wide until bias, residual and activation are applied), as
+ * the plain definition in double, in the order the pull request names them:
+ *   out[m][n] = act(P[m][n] + bias[n] + residual[m][n])
+ * act 0: identity; 1: ReLU, max(x, 0); 2: SiLU, x * sigma(x) with
+ * sigma(x) = 1 / (1 + e^-x); 3: GELU, x * Phi(x) with Phi the standard
+ * normal distribution function, Phi(x) = (1 + erf(x / sqrt(2))) / 2.
+ * bias (float [N]) may be NULL; the residual is float [M][N] (res_f32) or
+ * fp16 bits [M][N] (res_f16), or neither.
+ */
+static double act_apply(double x, int act)
+{
+    switch (act) {
+    case 1: return x > 0.0 ? x : 0.0;
+    case 2: return x / (1.0 + exp(-x));
+    case 3: return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));
+    default: return x;
+    }
+}
+
+int orc_epilogue(int M, int N, const double *P, const float *bias, const float *res_f32,
+                 const uint16_t *res_f16, int act, double *out)
+{
+    if (M < 0 || N < 0 || act < 0 || act > 3 || (res_f32 && res_f16))
+        return ORC_BAD;
+    for (int m = 0; m < M; ++m)
+        for (int n = 0; n < N; ++n) {
+            const size_t i = (size_t)m * N + n;
+            double v = P[i];
+            if (bias) v += (double)bias[n];
+            if (res_f32) v += (double)res_f32[i];
+            if (res_f16) v += orc_half_to_double(res_f16[i]);
+            out[i] = act_apply(v, act);
+        }
+    return ORC_OK;
+}
+
+/*
+ * The value of x rounded to IEEE binary16 (round to nearest, ties to even;
+ * magnitudes that round past the largest finite value 65504 become
+ * infinite; the subnormal step is 2^-24), returned as a double. Written
+ * from the format's definition: 11 significant bits down to 2^-14, a fixed
+ * quantum of 2^-24 below it.
+ */
+double orc_round_half(double x)
+{
+    if (isnan(x) || isinf(x) || x == 0.0)
+        return x;
+    const double ax = fabs(x);
+    int e;
+    frexp(ax, &e);                        /* ax = f * 2^e, f in [0.5, 1) */
+    const int exp2 = e - 1;               /* ax in [2^exp2, 2^(exp2+1)) */
+    const double quantum = exp2 < -14 ? ldexp(1.0, -24) : ldexp(1.0, exp2 - 10);
+    const double r = nearbyint(ax / quantum) * quantum;   /* exact scaling; ties to even */
+    const double y = r > 65504.0 ? INFINITY : r;
+    return x < 0 ? -y : y;
+}

@@ -65,9 +65,12 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.orc_w4a8_dot.argtypes = [I, I, I, P, P, P]
     lib.orc_w4a8_rescale.argtypes = [I, I, P, P, P, P, P]
     lib.orc_w4a8_dequant_product.argtypes = [I, I, I, P, P, P, P, P]
+    lib.orc_epilogue.argtypes = [I, I, P, P, P, P, I, P]
+    lib.orc_round_half.argtypes = [ctypes.c_double]
+    lib.orc_round_half.restype = ctypes.c_double
     for f in ("orc_quantize", "orc_gemm_f32", "orc_gemm_blockq",
               "orc_w4a8_actquant", "orc_w4a8_dot", "orc_w4a8_rescale",
-              "orc_w4a8_dequant_product"):
+              "orc_w4a8_dequant_product", "orc_epilogue"):
         getattr(lib, f).restype = I
     return lib
 
@@ -197,6 +200,40 @@ def w4a8_gemm(A, q, pairs, lib=None):
     D = w4a8_dot(qa, q, lib)
     C = w4a8_rescale(D, sa, S, pairs, lib)
     return C, qa, sa, S, D
+
+
+ACTIVATIONS = {"none": 0, "relu": 1, "silu": 2, "gelu": 3}
+
+
+def epilogue(P: np.ndarray, bias=None, residual=None, activation="none", out_f16=False,
+             lib=None) -> np.ndarray:
+    """act(P + bias + residual) in double (the SimdPaddleOCR pull request's
+    epilogue order), optionally rounded to fp16 (nearest even). residual is
+    float32 or float16 [M][N]; bias float32 [N]."""
+    lib = lib or load()
+    P = np.ascontiguousarray(P, dtype=np.float64)
+    M, N = P.shape
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    r32 = r16 = None
+    if residual is not None:
+        residual = np.ascontiguousarray(residual)
+        if residual.dtype == np.float16:
+            r16 = residual.view(np.uint16)
+        else:
+            r32 = np.ascontiguousarray(residual, dtype=np.float32)
+    act = ACTIVATIONS[activation] if isinstance(activation, str) else int(activation)
+    out = np.zeros((M, N), dtype=np.float64)
+    _check(lib.orc_epilogue(M, N, _p(P), _p(b) if b is not None else None,
+                            _p(r32) if r32 is not None else None,
+                            _p(r16) if r16 is not None else None, act, _p(out)), "epilogue")
+    if out_f16:
+        out = np.vectorize(lib.orc_round_half, otypes=[np.float64])(out) if out.size else out
+    return out
+
+
+def round_half(x: float, lib=None) -> float:
+    """x rounded to IEEE binary16 (nearest even), as a double."""
+    return (lib or load()).orc_round_half(float(x))
 
 
 def reference(fmt: str, A, B=None, q=None, pairs=None, lib=None) -> np.ndarray:

@@ -340,4 +340,67 @@ def pin_w4a8_error_bound(lib):
     assert np.all(np.abs(C - exact) <= bound * (1 + 1e-6) + 1e-12)
 
 
+# --------------------------------------------------------------------------
+# Fused epilogue and fp16 output rounding
+# --------------------------------------------------------------------------
+def pin_epilogue_sum_exact(lib):
+    """No activation: small integers (exact in every type) add exactly, with a
+    float32 and with an fp16 residual."""
+    rng = np.random.default_rng(11)
+    P = rng.integers(-50, 50, (3, 5)).astype(np.float64)
+    b = rng.integers(-9, 9, 5).astype(np.float32)
+    r = rng.integers(-20, 20, (3, 5)).astype(np.float32)
+    assert np.array_equal(O.epilogue(P, b, r, "none", lib=lib), P + b + r)
+    assert np.array_equal(O.epilogue(P, b, r.astype(np.float16), "none", lib=lib), P + b + r)
+    assert np.array_equal(O.epilogue(P, None, None, "none", lib=lib), P)
+
+
+def pin_epilogue_textbook_values(lib):
+    """SiLU(1) = logistic(1) = 0.7310585786300049; GELU(+-1) = +-Phi(+-1) with
+    the tabulated normal distribution value Phi(1) = 0.8413447460685429;
+    ReLU of (-2.5, -0, 0, 3.25)."""
+    x = np.array([[1.0, -1.0]])
+    _rel_close(O.epilogue(x, activation="silu", lib=lib), [[0.7310585786300049, -0.2689414213699951]], 1.0)
+    _rel_close(O.epilogue(x, activation="gelu", lib=lib), [[0.8413447460685429, -0.15865525393145705]], 1.0)
+    r = O.epilogue(np.array([[-2.5, -0.0, 0.0, 3.25]]), activation="relu", lib=lib)
+    assert np.array_equal(r, [[0.0, 0.0, 0.0, 3.25]])
+
+
+def pin_epilogue_odd_parts(lib):
+    """x sigma(x) - (-x) sigma(-x) = x and x Phi(x) - (-x) Phi(-x) = x, since
+    sigma(x) + sigma(-x) = Phi(x) + Phi(-x) = 1."""
+    x = np.linspace(-6, 6, 49)
+    X = np.stack([x, -x])
+    for act in ("silu", "gelu"):
+        y = O.epilogue(X, activation=act, lib=lib)
+        _rel_close(y[0] - y[1], x, np.maximum(np.abs(x), 1.0), tol=1e-14)
+
+
+def pin_epilogue_order(lib):
+    """Bias and residual are added before the activation: ReLU(-2 + 0.5 + 1)
+    = 0, SiLU(0 + 0 + 1) = logistic(1)."""
+    P = np.array([[-2.0, 0.0]])
+    b = np.array([0.5, 0.0], np.float32)
+    r = np.array([[1.0, 1.0]], np.float32)
+    assert O.epilogue(P, b, r, "relu", lib=lib)[0, 0] == 0.0
+    _rel_close(O.epilogue(P, b, r, "silu", lib=lib)[0, 1], 0.7310585786300049, 1.0)
+
+
+def pin_round_half_numpy(lib):
+    """Rounding to binary16 matches numpy's float64 -> float16 conversion
+    (round to nearest even, overflow to infinity) on random values, exact
+    ties, subnormals and the overflow boundary."""
+    rng = np.random.default_rng(12)
+    vals = list(rng.standard_normal(300) * np.exp2(rng.integers(-26, 17, 300)))
+    for e in (-24, -20, -14, -1, 0, 5, 15):            # exact ties at several exponents
+        ulp = 2.0 ** max(e - 10, -24)
+        base = 2.0 ** e
+        vals += [base + ulp / 2, base + 1.5 * ulp, -(base + 2.5 * ulp)]
+    vals += [65504.0, 65519.99, 65520.0, -65520.0, 2.0 ** -25, 3 * 2.0 ** -25, 1e-9, 7e4]
+    for v in vals:
+        got = O.round_half(v, lib=lib)
+        want = float(np.float64(v).astype(np.float16))
+        assert got == want or (np.isnan(got) and np.isnan(want)), (v, got, want)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

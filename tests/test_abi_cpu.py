@@ -103,6 +103,21 @@ def test_split_k_workspace_plan():
     assert w == Q.qgemm_workspace_size(8, 128, 16000, "w4a8")   # W4A8 scratch has no N part
 
 
+def test_run_ex_validation(lib):
+    """Epilogue checks happen before any device work: unknown activation or
+    output type -> ERR_FORMAT, misaligned bias or residual -> ERR_ALIGN, a
+    short caller workspace -> ERR_SIZE."""
+    v = ctypes.c_void_p
+    def ex(act=0, out=0, bias=None, res=None, ws=None, nb=0):
+        e = Q.Epilogue(bias, res, act, out)
+        return lib.qgemm_run_ex(64, 4096, 512, 1, v(256), v(256), v(256), v(256), ctypes.byref(e),
+                                ws, nb, None)
+    assert ex(act=4) == 3 and ex(act=-1) == 3 and ex(out=2) == 3
+    assert ex(bias=v(260)) == 4 and ex(res=v(264)) == 4
+    need = Q.qgemm_workspace_size(64, 4096, 512, "int4b64")
+    assert need > 0 and ex(ws=v(512), nb=need - 1) == 8
+
+
 def test_sizes():
     assert Q.qgemm_packed_size(4096, 11008, "int4b64") == (22544384, 5636096)
     assert Q.qgemm_packed_size(4096, 100, "int4b64") == (4 * 64 * 1024, 4 * 64 * 256)

@@ -1,0 +1,90 @@
+"""GPU parity of the fused epilogue C = act(A x B + bias + residual), C fp32 or
+fp16, through qgemm_run_ex, against the oracle's product followed by the
+oracle's epilogue (fp16 outputs rounded to nearest even by the oracle).
+
+Every kernel path is covered: both GEMVs, the tiled Int4 / Int8 / fp32 GEMMs,
+the split-K reduce (Int4 and fp32), fp32 K-groups, and W4A8. Tolerances are
+the library's (max-abs 1e-2, relative-Frobenius 2e-3); an fp16 output may
+differ from the oracle's by one fp16 step where the two round values on
+either side of a tie point, which stays inside max-abs for |C| < 16.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import compare, dev, require_gpu
+from oracle import oracle as O
+from weight_quantized_gemm_amd import qgemm as Q
+from weight_quantized_gemm_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+    prev = Q.qgemm_set_gemv_max_m(8)
+    yield
+    Q.qgemm_set_gemv_max_m(prev)
+
+
+SHAPES = [("f32", 16, 256, 256), ("f32", 8, 2560, 1024), ("f32", 130, 512, 200),
+          ("int4b64", 1, 4096, 300), ("int4b64", 96, 1024, 300), ("int4b64", 65, 4096, 256),
+          ("int8b0", 3, 1000, 130), ("int8b0", 130, 640, 200), ("w4a8", 100, 640, 256)]
+EPILOGUES = [("bias", "silu", "f32", False), ("residual", "gelu", "f16", False),
+             ("bias+residual", "relu", "f32", False), ("bias+residual", "gelu", "f16", True),
+             ("bias+residual", "none", "f32", True)]
+
+
+def _product(fmt, M, K, N, seed):
+    """Inputs, packed device weights and the oracle's fp64 product."""
+    rng = np.random.default_rng(seed)
+    if fmt == "f32":
+        A = synth.activations(rng, M, K, fp16=False)
+        B = synth.float_pattern_weights(K, N)
+        wp, sp = Q.qgemm_pack_weights(K, N, fmt, B, None)
+        return A, dev(wp), None, O.gemm_f32(A, B)
+    A = synth.activations(rng, M, K, fp16=True)
+    q, p = Q.qgemm_quantize_weights(synth.normal_weights(rng, N, K), fmt)
+    wp, sp = Q.qgemm_pack_weights(K, N, fmt, q, p)
+    return A, dev(wp), dev(sp), O.reference(fmt, A, q=q, pairs=p)
+
+
+@pytest.mark.parametrize("fmt,M,K,N", SHAPES)
+@pytest.mark.parametrize("parts,act,out,inplace", EPILOGUES)
+def test_epilogue(fmt, M, K, N, parts, act, out, inplace):
+    A, Bd, Sd, P = _product(fmt, M, K, N, seed=M * 3 + K + N)
+    rng = np.random.default_rng(M + N)
+    odt = np.float16 if out == "f16" else np.float32
+    tdt = torch.float16 if out == "f16" else torch.float32
+    bias = rng.standard_normal(N).astype(np.float32) if "bias" in parts else None
+    res = rng.standard_normal((M, N)).astype(odt) if "residual" in parts else None
+    want = O.epilogue(P, bias, res, act, out_f16=(out == "f16"))
+    C = torch.full((M, N), float("nan"), dtype=tdt, device="cuda")
+    if inplace:
+        C.copy_(torch.from_numpy(res))
+        res_d = C
+    else:
+        res_d = dev(res) if res is not None else None
+    Q.qgemm_run_ex(M, K, N, fmt, dev(A), Bd, Sd, C, bias=dev(bias) if bias is not None else None,
+                   residual=res_d, activation=act, out_type=out)
+    torch.cuda.synchronize()
+    compare(C.float().cpu().numpy(), want, f"{fmt} {M}x{K}x{N} {parts} {act} {out}")
+
+
+def test_plain_ex_equals_run():
+    """qgemm_run_ex with no epilogue (and with a caller workspace) gives
+    exactly what qgemm_run gives, on a split-K shape."""
+    M, K, N = 65, 4096, 256
+    A, Bd, Sd, _ = _product("int4b64", M, K, N, seed=7)
+    Ad = dev(A)
+    C1 = torch.empty((M, N), device="cuda")
+    C2 = torch.empty((M, N), device="cuda")
+    C3 = torch.empty((M, N), device="cuda")
+    Q.qgemm_run(M, K, N, "int4b64", Ad, Bd, Sd, C1)
+    Q.qgemm_run_ex(M, K, N, "int4b64", Ad, Bd, Sd, C2)
+    nb = Q.qgemm_workspace_size(M, K, N, "int4b64")
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    Q.qgemm_run_ex(M, K, N, "int4b64", Ad, Bd, Sd, C3, workspace=ws, ws_bytes=nb)
+    torch.cuda.synchronize()
+    assert torch.equal(C1, C2) and torch.equal(C1, C3)

@@ -22,6 +22,33 @@ SRC = os.path.join(ROOT, "oracle", "oracle.c")
 
 # (name, text in oracle.c, replacement)
 MUTANTS = [
+    ("epilogue_drops_bias",
+     "if (bias) v += (double)bias[n];",
+     "(void)bias;"),
+    ("epilogue_residual_sign",
+     "if (res_f32) v += (double)res_f32[i];",
+     "if (res_f32) v -= (double)res_f32[i];"),
+    ("epilogue_residual_after_activation",
+     "out[i] = act_apply(v, act);",
+     "out[i] = act_apply(v - (res_f32 ? (double)res_f32[i] : 0.0), act) + (res_f32 ? (double)res_f32[i] : 0.0);"),
+    ("silu_exponent_sign",
+     "case 2: return x / (1.0 + exp(-x));",
+     "case 2: return x / (1.0 + exp(x));"),
+    ("gelu_sqrt2_inverted",
+     "case 3: return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));",
+     "case 3: return 0.5 * x * (1.0 + erf(x * sqrt(2.0)));"),
+    ("relu_flipped",
+     "case 1: return x > 0.0 ? x : 0.0;",
+     "case 1: return x < 0.0 ? x : 0.0;"),
+    ("round_half_quantum",
+     "ldexp(1.0, exp2 - 10);",
+     "ldexp(1.0, exp2 - 11);"),
+    ("round_half_no_overflow",
+     "const double y = r > 65504.0 ? INFINITY : r;",
+     "const double y = r;"),
+    ("round_half_truncates",
+     "nearbyint(ax / quantum) * quantum;",
+     "floor(ax / quantum) * quantum;"),
     ("dequant_drops_offset",
      "return offset + scale * (double)code_at(q, K, bits, n, k);",
      "return scale * (double)code_at(q, K, bits, n, k);"),

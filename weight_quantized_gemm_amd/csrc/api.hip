@@ -1,5 +1,5 @@
-// api.hip -- qgemm_run / qgemm_run_ws / qgemm_w4a8_debug: argument checks,
-// kernel choice and launches on the caller's stream.
+// api.hip -- qgemm_run / qgemm_run_ws / qgemm_run_ex / qgemm_w4a8_debug:
+// argument checks, kernel choice and launches on the caller's stream.
 //
 // Kernel choice follows the MNN GemmSpeed benchmark page, section "Default
 // test sizes and the meaning of M": M = 8 is the narrow, near-decode GEMM
@@ -57,7 +57,7 @@ static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 // Checks shared by every run entry point; *empty is set for M == 0 or N == 0.
 static qgemm_status check_run(int M, int K, int N, qgemm_format f, const void *A,
-                              const void *Bq, const void *scales, const float *C,
+                              const void *Bq, const void *scales, const void *C,
                               Geometry *g, bool *empty) {
     qgemm_status st = geometry(K, N, f, g);
     if (st != QGEMM_OK) return st;
@@ -77,13 +77,29 @@ static qgemm_status check_run(int M, int K, int N, qgemm_format f, const void *A
     return QGEMM_OK;
 }
 
+// The caller's epilogue (NULL: none, fp32 C) as the kernels take it.
+static qgemm_status make_epilogue(const qgemm_epilogue *e, Epilogue *out) {
+    *out = Epilogue{nullptr, nullptr, QGEMM_ACT_NONE, 0, true};
+    if (!e) return QGEMM_OK;
+    if (e->activation < QGEMM_ACT_NONE || e->activation > QGEMM_ACT_GELU) return QGEMM_ERR_FORMAT;
+    if (e->out_type != QGEMM_OUT_F32 && e->out_type != QGEMM_OUT_F16) return QGEMM_ERR_FORMAT;
+    if ((e->bias && !aligned16(e->bias)) || (e->residual && !aligned16(e->residual)))
+        return QGEMM_ERR_ALIGN;
+    out->bias = e->bias;
+    out->residual = e->residual;
+    out->act = e->activation;
+    out->f16 = e->out_type == QGEMM_OUT_F16 ? 1 : 0;
+    out->plain = !e->bias && !e->residual && e->activation == QGEMM_ACT_NONE && !out->f16;
+    return QGEMM_OK;
+}
+
 static qgemm_status launched(hipError_t e) {
     return e == hipSuccess ? QGEMM_OK : QGEMM_ERR_LAUNCH;
 }
 
 static qgemm_status run_w4a8(int M, int K, int N, const Geometry &g, const void *A,
-                             const void *Bq, const void *scales, float *C, void *ws,
-                             hipStream_t s, int32_t *D_debug) {
+                             const void *Bq, const void *scales, void *C, const Epilogue &epi,
+                             void *ws, hipStream_t s, int32_t *D_debug) {
     W4A8Workspace w = w4a8_workspace(M, K);
     uint8_t *base = static_cast<uint8_t *>(ws);
     int8_t *qa = reinterpret_cast<int8_t *>(base + w.qa_off);
@@ -91,7 +107,7 @@ static qgemm_status run_w4a8(int M, int K, int N, const Geometry &g, const void 
     int32_t *S = reinterpret_cast<int32_t *>(base + w.S_off);
     hipError_t e = launch_w4a8_actquant(M, K, w.qa_stride, A, qa, sa, S, s);
     if (e != hipSuccess) return QGEMM_ERR_LAUNCH;
-    return launched(launch_w4a8_gemm(M, K, N, w.qa_stride, qa, sa, S, Bq, scales, C, D_debug, s));
+    return launched(launch_w4a8_gemm(M, K, N, w.qa_stride, qa, sa, S, Bq, scales, C, epi, D_debug, s));
 }
 
 // The Int4-Block64 and Int8-Block0 GEMV kernels serve M <= the current GEMV
@@ -110,8 +126,8 @@ static size_t used_bytes(const RunWorkspace &r, bool gemv) {
 }
 
 static qgemm_status dispatch(int M, int K, int N, qgemm_format f, const Geometry &g,
-                             const void *A, const void *Bq, const void *scales, float *C,
-                             void *ws, hipStream_t s) {
+                             const void *A, const void *Bq, const void *scales, void *C,
+                             const Epilogue &epi, void *ws, hipStream_t s) {
     (void)hipGetLastError();   // start from a clean per-thread error state
     const bool gemv = use_gemv(f, M, K);
     const RunWorkspace r = run_workspace(f, M, K, N);
@@ -121,15 +137,15 @@ static qgemm_status dispatch(int M, int K, int N, qgemm_format f, const Geometry
     switch (f) {
     case QGEMM_F32:
         return launched(launch_gemm_f32(M, K, N, static_cast<const float *>(A),
-                                        static_cast<const float *>(Bq), C, nsplit, part, s));
+                                        static_cast<const float *>(Bq), C, epi, nsplit, part, s));
     case QGEMM_INT4_B64:
-        return launched(gemv ? launch_gemv_int4b64(M, K, N, A, Bq, scales, C, s)
-                             : launch_gemm_int4b64(M, K, N, A, Bq, scales, C, nsplit, part, s));
+        return launched(gemv ? launch_gemv_int4b64(M, K, N, A, Bq, scales, C, epi, s)
+                             : launch_gemm_int4b64(M, K, N, A, Bq, scales, C, epi, nsplit, part, s));
     case QGEMM_INT8_B0:
-        return launched(gemv ? launch_gemv_int8b0(M, K, N, A, Bq, scales, C, s)
-                             : launch_gemm_int8b0(M, K, N, A, Bq, scales, C, s));
+        return launched(gemv ? launch_gemv_int8b0(M, K, N, A, Bq, scales, C, epi, s)
+                             : launch_gemm_int8b0(M, K, N, A, Bq, scales, C, epi, s));
     case QGEMM_W4A8:
-        return run_w4a8(M, K, N, g, A, Bq, scales, C, ws, s, nullptr);
+        return run_w4a8(M, K, N, g, A, Bq, scales, C, epi, ws, s, nullptr);
     }
     return QGEMM_ERR_FORMAT;
 }
@@ -146,48 +162,60 @@ int qgemm_set_gemv_max_m(int max_m) {
     return prev;
 }
 
-qgemm_status qgemm_run_ws(int M, int K, int N, qgemm_format f, const void *A,
-                          const void *Bq, const void *scales, float *C, void *workspace,
-                          size_t ws_bytes, void *stream) {
+qgemm_status qgemm_run_ex(int M, int K, int N, qgemm_format f, const void *A,
+                          const void *Bq, const void *scales, void *C,
+                          const qgemm_epilogue *epilogue, void *workspace, size_t ws_bytes,
+                          void *stream) {
     Geometry g;
     bool empty = false;
     qgemm_status st = check_run(M, K, N, f, A, Bq, scales, C, &g, &empty);
     if (st != QGEMM_OK || empty) return st;
+    Epilogue epi;
+    st = make_epilogue(epilogue, &epi);
+    if (st != QGEMM_OK) return st;
     const size_t need = used_bytes(run_workspace(f, M, K, N), use_gemv(f, M, K));
-    if (need > 0) {
+    const bool own = !workspace && ws_bytes == 0;   // scratch, if any, is ours to allocate
+    if (need > 0 && !own) {
         if (!workspace) return QGEMM_ERR_NULL;
         if (!aligned16(workspace)) return QGEMM_ERR_ALIGN;
         if (ws_bytes < need) return QGEMM_ERR_SIZE;
     }
     st = check_device();
     if (st != QGEMM_OK) return st;
-    return dispatch(M, K, N, f, g, A, Bq, scales, C, workspace,
-                    static_cast<hipStream_t>(stream));
-}
-
-qgemm_status qgemm_run(int M, int K, int N, qgemm_format f, const void *A, const void *Bq,
-                       const void *scales, float *C, void *stream) {
-    Geometry g;
-    bool empty = false;
-    qgemm_status st = check_run(M, K, N, f, A, Bq, scales, C, &g, &empty);
-    if (st != QGEMM_OK || empty) return st;
-    st = check_device();
-    if (st != QGEMM_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const size_t bytes = used_bytes(run_workspace(f, M, K, N), use_gemv(f, M, K));
-    if (bytes == 0) return dispatch(M, K, N, f, g, A, Bq, scales, C, nullptr, s);
+    if (need == 0 || !own) return dispatch(M, K, N, f, g, A, Bq, scales, C, epi, workspace, s);
     // Scratch (W4A8 codes, split-K partials), allocated and released in stream order.
     void *ws = nullptr;
-    if (hipMallocAsync(&ws, bytes, s) != hipSuccess || !ws) {
+    if (hipMallocAsync(&ws, need, s) != hipSuccess || !ws) {
         (void)hipGetLastError();
         return QGEMM_ERR_NOMEM;
     }
-    st = dispatch(M, K, N, f, g, A, Bq, scales, C, ws, s);
+    st = dispatch(M, K, N, f, g, A, Bq, scales, C, epi, ws, s);
     if (hipFreeAsync(ws, s) != hipSuccess) {
         (void)hipGetLastError();
         if (st == QGEMM_OK) st = QGEMM_ERR_LAUNCH;
     }
     return st;
+}
+
+qgemm_status qgemm_run_ws(int M, int K, int N, qgemm_format f, const void *A,
+                          const void *Bq, const void *scales, float *C, void *workspace,
+                          size_t ws_bytes, void *stream) {
+    // a caller workspace, never a library allocation (NULL with size 0 is
+    // only accepted when the shape needs none)
+    if (!workspace && ws_bytes == 0 && M > 0 && N > 0) {
+        Geometry g;
+        bool empty = false;
+        qgemm_status st = check_run(M, K, N, f, A, Bq, scales, C, &g, &empty);
+        if (st != QGEMM_OK) return st;
+        if (used_bytes(run_workspace(f, M, K, N), use_gemv(f, M, K)) > 0) return QGEMM_ERR_NULL;
+    }
+    return qgemm_run_ex(M, K, N, f, A, Bq, scales, C, nullptr, workspace, ws_bytes, stream);
+}
+
+qgemm_status qgemm_run(int M, int K, int N, qgemm_format f, const void *A, const void *Bq,
+                       const void *scales, float *C, void *stream) {
+    return qgemm_run_ex(M, K, N, f, A, Bq, scales, C, nullptr, nullptr, 0, stream);
 }
 
 qgemm_status qgemm_w4a8_debug(int M, int K, int N, const void *A, const void *Bq,
@@ -206,7 +234,8 @@ qgemm_status qgemm_w4a8_debug(int M, int K, int N, const void *A, const void *Bq
     if (st != QGEMM_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    st = run_w4a8(M, K, N, g, A, Bq, scales, C, workspace, s, D);
+    const Epilogue plain{nullptr, nullptr, QGEMM_ACT_NONE, 0, true};
+    st = run_w4a8(M, K, N, g, A, Bq, scales, C, plain, workspace, s, D);
     if (st != QGEMM_OK) return st;
     const uint8_t *base = static_cast<const uint8_t *>(workspace);
     if (hipMemcpy2DAsync(qa, (size_t)K, base + w.qa_off, (size_t)w.qa_stride, (size_t)K, (size_t)M,

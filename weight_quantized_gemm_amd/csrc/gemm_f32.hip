@@ -73,7 +73,8 @@ template <int TM, int KG>
 __global__ __launch_bounds__(256 * KG) void gemm_f32_kernel(int M, int K, int N,
                                                             const float *__restrict__ A,
                                                             const float *__restrict__ B,
-                                                            float *__restrict__ C) {
+                                                            void *__restrict__ C,
+                                                            Epilogue epi) {
     constexpr int BM = 16 * TM;
     constexpr size_t TILE_BYTES = KG * sizeof(F32Tiles<TM>);
     constexpr size_t RED_BYTES = (KG > 1 ? KG : 0) * (size_t)BM * (FT + 4) * sizeof(float);
@@ -167,34 +168,43 @@ __global__ __launch_bounds__(256 * KG) void gemm_f32_kernel(int M, int K, int N,
                 acc[i][j] = v;
             }
     }
-    float *const out = C + (size_t)blockIdx.z * M * N;
+    // partial tiles (split-K) and plain fp32 C take the raw store
+    const bool raw = gridDim.z > 1 || epi.plain;
+    float *const out = static_cast<float *>(C) + (size_t)blockIdx.z * M * N;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int gm = m0 + ty * TM + i;
         if (gm >= M) continue;
+        const int gn0 = n0 + tx * 4;
+        if (!raw && (N & 3) == 0 && gn0 + 4 <= N) {
+            epi_put4(epi, C, gm, gn0, N, f4_t{acc[i][0], acc[i][1], acc[i][2], acc[i][3]});
+            continue;
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int gn = n0 + tx * 4 + j;
-            if (gn < N) out[(size_t)gm * N + gn] = acc[i][j];
+            const int gn = gn0 + j;
+            if (gn >= N) continue;
+            if (raw) out[(size_t)gm * N + gn] = acc[i][j];
+            else epi_put(epi, C, gm, gn, N, acc[i][j]);
         }
     }
 }
 
-hipError_t launch_gemm_f32(int M, int K, int N, const float *A, const float *B, float *C,
-                           int nsplit, float *part, hipStream_t s) {
-    float *out = nsplit > 1 ? part : C;
+hipError_t launch_gemm_f32(int M, int K, int N, const float *A, const float *B, void *C,
+                           const Epilogue &epi, int nsplit, float *part, hipStream_t s) {
+    void *out = nsplit > 1 ? static_cast<void *>(part) : C;
     const bool small = M <= kF32TileMSmall;
     const dim3 grid(div_up(N, FT), div_up(M, small ? kF32TileMSmall : kF32TileM), nsplit);
     if (f32_kgroups(M, N) > 1) {
-        if (small) hipLaunchKernelGGL((gemm_f32_kernel<1, kF32KGroups>), grid, dim3(256 * kF32KGroups), 0, s, M, K, N, A, B, out);
-        else hipLaunchKernelGGL((gemm_f32_kernel<4, kF32KGroups>), grid, dim3(256 * kF32KGroups), 0, s, M, K, N, A, B, out);
+        if (small) hipLaunchKernelGGL((gemm_f32_kernel<1, kF32KGroups>), grid, dim3(256 * kF32KGroups), 0, s, M, K, N, A, B, out, epi);
+        else hipLaunchKernelGGL((gemm_f32_kernel<4, kF32KGroups>), grid, dim3(256 * kF32KGroups), 0, s, M, K, N, A, B, out, epi);
     } else {
-        if (small) hipLaunchKernelGGL((gemm_f32_kernel<1, 1>), grid, dim3(256), 0, s, M, K, N, A, B, out);
-        else hipLaunchKernelGGL((gemm_f32_kernel<4, 1>), grid, dim3(256), 0, s, M, K, N, A, B, out);
+        if (small) hipLaunchKernelGGL((gemm_f32_kernel<1, 1>), grid, dim3(256), 0, s, M, K, N, A, B, out, epi);
+        else hipLaunchKernelGGL((gemm_f32_kernel<4, 1>), grid, dim3(256), 0, s, M, K, N, A, B, out, epi);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nsplit <= 1) return e;
-    return launch_splitk_reduce_f32(part, nsplit, M, N, C, s);
+    return launch_splitk_reduce_f32(part, nsplit, M, N, C, epi, s);
 }
 
 }  // namespace qg

@@ -100,7 +100,7 @@ __device__ __forceinline__ h8_t dequant8(unsigned word, const DqParams &p, unsig
 __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     int M, int K, int N, int tiles_m, int tiles_n, int xcd_rows,
     const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
-    const float *__restrict__ Sp, float *__restrict__ C) {
+    const float *__restrict__ Sp, void *__restrict__ C, Epilogue epi) {
     __shared__ __align__(16) unsigned char lds[LDS_BYTES];
 
     // ---- tile of this workgroup ----
@@ -131,7 +131,10 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     const int KB0 = (int)((long long)blockIdx.y * nblk / gridDim.y);
     const int KB1 = (int)((long long)(blockIdx.y + 1) * nblk / gridDim.y);
     const int nbs = KB1 - KB0;                     // >= 1: the plan keeps gridDim.y <= nblk
-    float *const out = C + (size_t)blockIdx.y * M * N;
+    // partial tiles (split-K) and plain fp32 C take the raw store; otherwise
+    // every output goes through the epilogue
+    const bool raw = gridDim.y > 1 || epi.plain;
+    float *const out = static_cast<float *>(C) + (size_t)blockIdx.y * M * N;
     const int kb0 = KB0 + kq * nbs / 4, kb1 = KB0 + (kq + 1) * nbs / 4;   // contiguous quarter
     const int nb = kb1 - kb0;                      // kb0 is a valid block even when nb == 0
     const int last = max(kb1 - 1, kb0);
@@ -310,7 +313,13 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
 #pragma unroll
         for (int q = 1; q < 4; ++q)
             sum += *reinterpret_cast<const f4_t *>(red0 + (size_t)(2 * q + half) * W + o);
-        if (vec_store) {
+        if (!raw && vec_store) {
+            epi_put4(epi, C, gm, n0 + c0 + j, N, sum);
+        } else if (!raw) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (n0 + c0 + j + e < N) epi_put(epi, C, gm, n0 + c0 + j + e, N, sum[e]);
+        } else if (vec_store) {
             *reinterpret_cast<f4_t *>(dst + j) = sum;
         } else {
 #pragma unroll
@@ -321,8 +330,8 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
 }
 
 hipError_t launch_gemm_int4b64(int M, int K, int N, const void *A, const void *Wp,
-                               const void *Sp, float *C, int nsplit, float *part,
-                               hipStream_t s) {
+                               const void *Sp, void *C, const Epilogue &epi, int nsplit,
+                               float *part, hipStream_t s) {
     const int tiles_m = div_up(M, BM), tiles_n = div_up(N, BN);
     // XCD grid: row bands x column bands = 8, each XCD's L2 then fetches
     // A of its row band and B of its column band; pick the grid the tile
@@ -336,13 +345,13 @@ hipError_t launch_gemm_int4b64(int M, int K, int N, const void *A, const void *W
         const double fetched = gc * a_bytes + gr * b_bytes;
         if (xcd_rows == 0 || fetched < best) { xcd_rows = gr; best = fetched; }
     }
-    float *out = nsplit > 1 ? part : C;
+    void *out = nsplit > 1 ? static_cast<void *>(part) : C;
     hipLaunchKernelGGL(gemm_int4b64_kernel, dim3(tiles_m * tiles_n, nsplit), dim3(64 * NWAVE), 0, s,
                        M, K, N, tiles_m, tiles_n, xcd_rows, static_cast<const _Float16 *>(A),
-                       static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), out);
+                       static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), out, epi);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nsplit <= 1) return e;
-    return launch_splitk_reduce_f32(part, nsplit, M, N, C, s);
+    return launch_splitk_reduce_f32(part, nsplit, M, N, C, epi, s);
 }
 
 }  // namespace qg

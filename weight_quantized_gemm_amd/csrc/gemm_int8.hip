@@ -65,7 +65,8 @@ __device__ __forceinline__ h8_t codes_biased(u2_t codes) {
 template <int KMODE>
 __global__ __launch_bounds__(256) void gemm_int8b0_kernel(
     int M, int K, int N, int Kp, int tiles_n, int xcd_order, const _Float16 *__restrict__ A,
-    const uint8_t *__restrict__ Wp, const float *__restrict__ Sp, float *__restrict__ C) {
+    const uint8_t *__restrict__ Wp, const float *__restrict__ Sp, void *__restrict__ C,
+    Epilogue epi) {
     // element loads (any K) keep a shallower A ring to stay in registers
     constexpr int RA = KMODE == 2 ? 2 : RA_FAST;
     __shared__ __align__(16) float red[4][BM * RED_STRIDE];   // 4 x 34 KiB
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(256) void gemm_int8b0_kernel(
     const int gm = m0 + row;
     if (gm >= M) return;
     const float rsm = ((rsum[0][row] + rsum[1][row]) + rsum[2][row]) + rsum[3][row];
-    float *dst = C + (size_t)gm * N + n0 + c0;
+    float *dst = static_cast<float *>(C) + (size_t)gm * N + n0 + c0;
     const bool vec_store = (N & 3) == 0 && n0 + c0 + 32 <= N;
 #pragma unroll
     for (int j = 0; j < 32; j += 4) {
@@ -215,7 +216,13 @@ __global__ __launch_bounds__(256) void gemm_int8b0_kernel(
             const f2_t pr = *reinterpret_cast<const f2_t *>(Sp + (size_t)min(n0 + c0 + j + e, N - 1) * 2);
             out[e] = fmaf(pr.y, p[e], fmaf(-1024.0f, pr.y, pr.x) * rsm);
         }
-        if (vec_store) {
+        if (!epi.plain && vec_store) {
+            epi_put4(epi, C, gm, n0 + c0 + j, N, out);
+        } else if (!epi.plain) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (n0 + c0 + j + e < N) epi_put(epi, C, gm, n0 + c0 + j + e, N, out[e]);
+        } else if (vec_store) {
             *reinterpret_cast<f4_t *>(dst + j) = out;
         } else {
 #pragma unroll
@@ -226,7 +233,7 @@ __global__ __launch_bounds__(256) void gemm_int8b0_kernel(
 }
 
 hipError_t launch_gemm_int8b0(int M, int K, int N, const void *A, const void *Wp,
-                              const void *Sp, float *C, hipStream_t s) {
+                              const void *Sp, void *C, const Epilogue &epi, hipStream_t s) {
     const int Kp = (int)round_up(K, 64);
     const int tiles_n = div_up(N, BN);
     const int tiles = tiles_n * div_up(M, BM);
@@ -234,7 +241,7 @@ hipError_t launch_gemm_int8b0(int M, int K, int N, const void *A, const void *Wp
     auto launch = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, dim3(tiles), dim3(256), 0, s, M, K, N, Kp, tiles_n, xcd_order,
                            static_cast<const _Float16 *>(A), static_cast<const uint8_t *>(Wp),
-                           static_cast<const float *>(Sp), C);
+                           static_cast<const float *>(Sp), C, epi);
     };
     if (K % 64 == 0) launch(gemm_int8b0_kernel<0>);
     else if (K % 8 == 0) launch(gemm_int8b0_kernel<1>);

@@ -55,7 +55,7 @@ constexpr int TILE_RPW = TILE_PASS / TILE_WAVES;   // blocks per wave and pass
 template <int MR, bool ONE_PASS>
 __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
     int M, int K, int N, const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
-    const float *__restrict__ Sp, float *__restrict__ C) {
+    const float *__restrict__ Sp, void *__restrict__ C, Epilogue epi) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int nblk = K >> 6;
     const int pmax = min(nblk, TILE_PASS);
@@ -173,7 +173,10 @@ __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
         float total = 0.f;
 #pragma unroll
         for (int w = 0; w < TILE_WAVES; ++w) total += part[(w * MR + r) * 32 + cc];
-        if (n < N && m < M) C[(size_t)m * N + n] = total;
+        if (n < N && m < M) {
+            if (epi.plain) static_cast<float *>(C)[(size_t)m * N + n] = total;
+            else epi_put(epi, C, m, n, N, total);
+        }
     }
 }
 
@@ -194,7 +197,7 @@ constexpr int I8_WAVES = 16;
 template <int MR, int NCH>
 __global__ __launch_bounds__(64 * I8_WAVES) void gemv_int8b0_kernel(
     int M, int K, int N, int Kp, const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
-    const f2_t *__restrict__ Sp, float *__restrict__ C) {
+    const f2_t *__restrict__ Sp, void *__restrict__ C, Epilogue epi) {
     extern __shared__ __align__(16) unsigned char lds[];
     _Float16 *As = reinterpret_cast<_Float16 *>(lds);                      // [MR][Kp], zero past K
     float *ssum = reinterpret_cast<float *>(lds + (size_t)MR * Kp * 2);    // [MR][I8_WAVES]
@@ -288,7 +291,9 @@ __global__ __launch_bounds__(64 * I8_WAVES) void gemv_int8b0_kernel(
             float sa = 0.f;
 #pragma unroll
             for (int w = 0; w < I8_WAVES; ++w) sa += ssum[r * I8_WAVES + w];
-            C[(size_t)(m0 + r) * N + n] = fmaf(c1, sa, pr.y * v);
+            const float out = fmaf(c1, sa, pr.y * v);
+            if (epi.plain) static_cast<float *>(C)[(size_t)(m0 + r) * N + n] = out;
+            else epi_put(epi, C, m0 + r, n, N, out);
         }
     }
 }
@@ -307,7 +312,7 @@ static int rows_per_pass(int M, int K, int kp_bytes_per_row) {
 
 template <int MR>
 static hipError_t gemv_int4_tile(int M, int K, int N, const void *A, const void *Wp,
-                                 const void *Sp, float *C, hipStream_t s) {
+                                 const void *Sp, void *C, const Epilogue &epi, hipStream_t s) {
     const int pmax = std::min(K / 64, TILE_PASS);
     const size_t lds = (size_t)MR * pmax * 128 + (size_t)MR * pmax * 16 +
                        (size_t)TILE_WAVES * MR * 32 * sizeof(float);
@@ -315,53 +320,53 @@ static hipError_t gemv_int4_tile(int M, int K, int N, const void *A, const void 
     if (K <= 64 * TILE_PASS)
         hipLaunchKernelGGL((gemv_int4b64_tile_kernel<MR, true>), grid, dim3(64 * TILE_WAVES), lds, s,
                            M, K, N, static_cast<const _Float16 *>(A),
-                           static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), C);
+                           static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), C, epi);
     else
         hipLaunchKernelGGL((gemv_int4b64_tile_kernel<MR, false>), grid, dim3(64 * TILE_WAVES), lds, s,
                            M, K, N, static_cast<const _Float16 *>(A),
-                           static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), C);
+                           static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), C, epi);
     return hipGetLastError();
 }
 
 hipError_t launch_gemv_int4b64(int M, int K, int N, const void *A, const void *Wp,
-                               const void *Sp, float *C, hipStream_t s) {
+                               const void *Sp, void *C, const Epilogue &epi, hipStream_t s) {
     switch (M >= 4 ? 4 : (M >= 2 ? 2 : 1)) {
-    case 4: return gemv_int4_tile<4>(M, K, N, A, Wp, Sp, C, s);
-    case 2: return gemv_int4_tile<2>(M, K, N, A, Wp, Sp, C, s);
-    default: return gemv_int4_tile<1>(M, K, N, A, Wp, Sp, C, s);
+    case 4: return gemv_int4_tile<4>(M, K, N, A, Wp, Sp, C, epi, s);
+    case 2: return gemv_int4_tile<2>(M, K, N, A, Wp, Sp, C, epi, s);
+    default: return gemv_int4_tile<1>(M, K, N, A, Wp, Sp, C, epi, s);
     }
 }
 
 template <int MR, int NCH>
 static hipError_t gemv_int8_mr(int M, int K, int N, int Kp, const void *A, const void *Wp,
-                               const void *Sp, float *C, hipStream_t s) {
+                               const void *Sp, void *C, const Epilogue &epi, hipStream_t s) {
     dim3 grid(div_up(N, I8_WAVES), div_up(M, MR));
     const size_t lds = (size_t)MR * Kp * sizeof(_Float16) + (size_t)MR * I8_WAVES * sizeof(float);
     hipLaunchKernelGGL((gemv_int8b0_kernel<MR, NCH>), grid, dim3(64 * I8_WAVES), lds, s, M, K, N,
                        Kp, static_cast<const _Float16 *>(A), static_cast<const uint8_t *>(Wp),
-                       static_cast<const f2_t *>(Sp), C);
+                       static_cast<const f2_t *>(Sp), C, epi);
     return hipGetLastError();
 }
 
 template <int MR>
 static hipError_t gemv_int8_k(int M, int K, int N, int Kp, const void *A, const void *Wp,
-                              const void *Sp, float *C, hipStream_t s) {
+                              const void *Sp, void *C, const Epilogue &epi, hipStream_t s) {
     // slices per lane: Kp / 1024, rounded up to a power of two (K <= 16384)
     const int nch = div_up(Kp, 1024);
-    if (nch <= 1) return gemv_int8_mr<MR, 1>(M, K, N, Kp, A, Wp, Sp, C, s);
-    if (nch <= 2) return gemv_int8_mr<MR, 2>(M, K, N, Kp, A, Wp, Sp, C, s);
-    if (nch <= 4) return gemv_int8_mr<MR, 4>(M, K, N, Kp, A, Wp, Sp, C, s);
-    if (nch <= 8) return gemv_int8_mr<MR, 8>(M, K, N, Kp, A, Wp, Sp, C, s);
-    return gemv_int8_mr<MR, 16>(M, K, N, Kp, A, Wp, Sp, C, s);
+    if (nch <= 1) return gemv_int8_mr<MR, 1>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
+    if (nch <= 2) return gemv_int8_mr<MR, 2>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
+    if (nch <= 4) return gemv_int8_mr<MR, 4>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
+    if (nch <= 8) return gemv_int8_mr<MR, 8>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
+    return gemv_int8_mr<MR, 16>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
 }
 
 hipError_t launch_gemv_int8b0(int M, int K, int N, const void *A, const void *Wp,
-                              const void *Sp, float *C, hipStream_t s) {
+                              const void *Sp, void *C, const Epilogue &epi, hipStream_t s) {
     const int Kp = (int)round_up(K, 64);
     switch (rows_per_pass(M, K, Kp * 2)) {
-    case 4: return gemv_int8_k<4>(M, K, N, Kp, A, Wp, Sp, C, s);
-    case 2: return gemv_int8_k<2>(M, K, N, Kp, A, Wp, Sp, C, s);
-    default: return gemv_int8_k<1>(M, K, N, Kp, A, Wp, Sp, C, s);
+    case 4: return gemv_int8_k<4>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
+    case 2: return gemv_int8_k<2>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
+    default: return gemv_int8_k<1>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
     }
 }
 

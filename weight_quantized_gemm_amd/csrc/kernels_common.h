@@ -5,9 +5,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qgemm_internal.h"
+
 namespace qg {
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f2_t __attribute__((ext_vector_type(2)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
@@ -33,5 +36,65 @@ __device__ __forceinline__ float dot2(h2_t a, h2_t b, float c) {
 
 // Wave-uniform value as a scalar (lets the compiler use scalar loads).
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// ---------------------------------------------------------------------------
+// Fused epilogue (SimdPaddleOCR pull request: fp32 accumulators are never
+// narrowed before bias, residual and activation): for output (m, n) at
+// mn = m * N + n, v = act((p + bias[n]) + residual[mn]) in fp32, then stored
+// as fp32 or rounded once to fp16 (nearest even). The activations use the
+// device math library's expf / erff.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float epi_act(float v, int act) {
+    switch (act) {
+    case 1: return v > 0.f ? v : 0.f;                                     // ReLU
+    case 2: return v / (1.0f + expf(-v));                                 // SiLU
+    case 3: return 0.5f * v * (1.0f + erff(v * 0.7071067811865476f));     // GELU (erf)
+    default: return v;
+    }
+}
+
+__device__ __forceinline__ float epi_value(const Epilogue &e, float p, size_t mn, int n) {
+    float v = p;
+    if (e.bias) v += e.bias[n];
+    if (e.residual)
+        v += e.f16 ? (float)static_cast<const _Float16 *>(e.residual)[mn]
+                   : static_cast<const float *>(e.residual)[mn];
+    return epi_act(v, e.act);
+}
+
+__device__ __forceinline__ void epi_store(const Epilogue &e, void *C, size_t mn, float v) {
+    if (e.f16) static_cast<_Float16 *>(C)[mn] = (_Float16)v;
+    else static_cast<float *>(C)[mn] = v;
+}
+
+// One output through the epilogue.
+__device__ __forceinline__ void epi_put(const Epilogue &e, void *C, int m, int n, int N, float p) {
+    const size_t mn = (size_t)m * N + n;
+    epi_store(e, C, mn, epi_value(e, p, mn, n));
+}
+
+// Four consecutive outputs (m, n .. n + 3), the same arithmetic as epi_put
+// per element, with 16-byte (fp32) or 8-byte (fp16) accesses. Requires
+// n + 3 < N, n % 4 == 0 and N % 4 == 0 (so every access is aligned).
+__device__ __forceinline__ void epi_put4(const Epilogue &e, void *C, int m, int n, int N, f4_t p) {
+    const size_t mn = (size_t)m * N + n;
+    f4_t v = p;
+    if (e.bias) v += *reinterpret_cast<const f4_t *>(e.bias + n);
+    if (e.residual) {
+        if (e.f16) {
+            const h4_t r = *reinterpret_cast<const h4_t *>(static_cast<const _Float16 *>(e.residual) + mn);
+            v += f4_t{(float)r[0], (float)r[1], (float)r[2], (float)r[3]};
+        } else {
+            v += *reinterpret_cast<const f4_t *>(static_cast<const float *>(e.residual) + mn);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = epi_act(v[i], e.act);
+    if (e.f16)
+        *reinterpret_cast<h4_t *>(static_cast<_Float16 *>(C) + mn) =
+            h4_t{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    else
+        *reinterpret_cast<f4_t *>(static_cast<float *>(C) + mn) = v;
+}
 
 }  // namespace qg

@@ -59,31 +59,47 @@ constexpr int kGemvMaxM = 8;          // largest M the GEMV kernels take
 constexpr int kGemvMaxK = 16384;      // A rows staged in LDS: MR * K * 2 bytes
 
 // ---------------------------------------------------------------------------
+// Fused epilogue, as the kernels see it: C = act(P + bias + residual), fp32
+// throughout, stored as fp32 or fp16 (see qgemm_epilogue in qgemm.h).
+// `plain` (no bias, no residual, no activation, fp32 C) keeps each kernel's
+// plain store path.
+// ---------------------------------------------------------------------------
+struct Epilogue {
+    const float *bias;
+    const void *residual;
+    int act;
+    int f16;
+    bool plain;
+};
+
+// ---------------------------------------------------------------------------
 // Kernel launchers (defined in the .hip files). They assume validated
-// arguments and return hipGetLastError() of their launches.
+// arguments and return hipGetLastError() of their launches. C is float or
+// fp16 per the epilogue.
 // ---------------------------------------------------------------------------
 hipError_t launch_gemv_int4b64(int M, int K, int N, const void *A, const void *Wp,
-                               const void *Sp, float *C, hipStream_t s);
+                               const void *Sp, void *C, const Epilogue &epi, hipStream_t s);
 hipError_t launch_gemv_int8b0(int M, int K, int N, const void *A, const void *Wp,
-                              const void *Sp, float *C, hipStream_t s);
+                              const void *Sp, void *C, const Epilogue &epi, hipStream_t s);
 // Tiled kernels with split-K: nsplit > 1 writes partial tiles to `part`
-// ([nsplit][M][N]) and adds them into C with a fixed-order reduce.
+// ([nsplit][M][N] fp32) and adds them into C with a fixed-order reduce that
+// applies the epilogue.
 hipError_t launch_gemm_int4b64(int M, int K, int N, const void *A, const void *Wp,
-                               const void *Sp, float *C, int nsplit, float *part,
-                               hipStream_t s);
-hipError_t launch_splitk_reduce_f32(const float *part, int nsplit, int M, int N, float *C,
-                                    hipStream_t s);
+                               const void *Sp, void *C, const Epilogue &epi, int nsplit,
+                               float *part, hipStream_t s);
+hipError_t launch_splitk_reduce_f32(const float *part, int nsplit, int M, int N, void *C,
+                                    const Epilogue &epi, hipStream_t s);
 hipError_t launch_gemm_int8b0(int M, int K, int N, const void *A, const void *Wp,
-                              const void *Sp, float *C, hipStream_t s);
-hipError_t launch_gemm_f32(int M, int K, int N, const float *A, const float *B, float *C,
-                           int nsplit, float *part, hipStream_t s);
+                              const void *Sp, void *C, const Epilogue &epi, hipStream_t s);
+hipError_t launch_gemm_f32(int M, int K, int N, const float *A, const float *B, void *C,
+                           const Epilogue &epi, int nsplit, float *part, hipStream_t s);
 // W4A8: qa [M][Kq] int8 (Kq = roundup(K, 128)), sa [M] float, S [M] int32
 // live in the workspace.
 hipError_t launch_w4a8_actquant(int M, int K, int Kq, const void *A, int8_t *qa,
                                 float *sa, int32_t *S, hipStream_t s);
 hipError_t launch_w4a8_gemm(int M, int K, int N, int Kq, const int8_t *qa, const float *sa,
                             const int32_t *S, const void *Wp, const void *Sp,
-                            float *C, int32_t *D_debug, hipStream_t s);
+                            void *C, const Epilogue &epi, int32_t *D_debug, hipStream_t s);
 
 // W4A8 scratch: qa [M][qa_stride] int8 (qa_stride = roundup(K, 128), zero
 // past K), sa [M] float, S [M] int32.

@@ -180,7 +180,7 @@ template <bool DEBUG_D>
 __global__ __launch_bounds__(64 * WNW) void w4a8_gemm_kernel(
     int M, int N, int Kq, int nkc, int tiles_n, int xcd_bands, const int8_t *__restrict__ qa,
     const float *__restrict__ sa, const int32_t *__restrict__ S, const uint8_t *__restrict__ Wp,
-    const f2_t *__restrict__ Sp, float *__restrict__ C, int32_t *__restrict__ D) {
+    const f2_t *__restrict__ Sp, void *__restrict__ C, Epilogue epi, int32_t *__restrict__ D) {
     __shared__ __align__(16) int8_t As[WRING * WAS_BYTES];
     __shared__ float sa_s[WBM];
     __shared__ int S_s[WBM];
@@ -320,15 +320,17 @@ __global__ __launch_bounds__(64 * WNW) void w4a8_gemm_kernel(
                 if (row >= M) continue;
                 const int d = acc[rf][j];
                 if (DEBUG_D) D[(size_t)row * N + col] = d;
-                C[(size_t)row * N + col] = sa_s[rl] * fmaf(pr.y, (float)d, pr.x * (float)S_s[rl]);
+                const float out = sa_s[rl] * fmaf(pr.y, (float)d, pr.x * (float)S_s[rl]);
+                if (epi.plain) static_cast<float *>(C)[(size_t)row * N + col] = out;
+                else epi_put(epi, C, row, col, N, out);
             }
         }
     }
 }
 
 hipError_t launch_w4a8_gemm(int M, int K, int N, int Kq, const int8_t *qa, const float *sa,
-                            const int32_t *S, const void *Wp, const void *Sp, float *C,
-                            int32_t *D_debug, hipStream_t s) {
+                            const int32_t *S, const void *Wp, const void *Sp, void *C,
+                            const Epilogue &epi, int32_t *D_debug, hipStream_t s) {
     const int nkc = (int)round_up(K, 64) / 64;
     const int tiles_m = div_up(M, WBM), tiles_n = div_up(N, WBN);
     const int xcd_bands = (tiles_n % 8 == 0) ? 1 : 0;
@@ -336,11 +338,11 @@ hipError_t launch_w4a8_gemm(int M, int K, int N, int Kq, const int8_t *qa, const
     if (D_debug)
         hipLaunchKernelGGL(w4a8_gemm_kernel<true>, grid, dim3(64 * WNW), 0, s, M, N, Kq, nkc,
                            tiles_n, xcd_bands, qa, sa, S, static_cast<const uint8_t *>(Wp),
-                           static_cast<const f2_t *>(Sp), C, D_debug);
+                           static_cast<const f2_t *>(Sp), C, epi, D_debug);
     else
         hipLaunchKernelGGL(w4a8_gemm_kernel<false>, grid, dim3(64 * WNW), 0, s, M, N, Kq, nkc,
                            tiles_n, xcd_bands, qa, sa, S, static_cast<const uint8_t *>(Wp),
-                           static_cast<const f2_t *>(Sp), C, D_debug);
+                           static_cast<const f2_t *>(Sp), C, epi, D_debug);
     return hipGetLastError();
 }
 

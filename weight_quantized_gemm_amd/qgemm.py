@@ -34,7 +34,7 @@ STATUS = {0: "QGEMM_OK", 1: "QGEMM_ERR_NULL", 2: "QGEMM_ERR_SHAPE", 3: "QGEMM_ER
 EXPORTS = ["qgemm_status_string", "qgemm_abi_version", "qgemm_canonical_size",
            "qgemm_quantize_weights", "qgemm_packed_size", "qgemm_pack_weights",
            "qgemm_unpack_weights", "qgemm_workspace_size", "qgemm_run", "qgemm_run_ws",
-           "qgemm_w4a8_debug", "qgemm_set_gemv_max_m"]
+           "qgemm_run_ex", "qgemm_w4a8_debug", "qgemm_set_gemv_max_m"]
 
 
 class QGemmError(RuntimeError):
@@ -69,6 +69,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "qgemm_workspace_size": ([I, I, I, I, ZP], I),
         "qgemm_run": ([I, I, I, I, P, P, P, P, P], I),
         "qgemm_run_ws": ([I, I, I, I, P, P, P, P, P, Z, P], I),
+        "qgemm_run_ex": ([I, I, I, I, P, P, P, P, ctypes.POINTER(Epilogue), P, Z, P], I),
         "qgemm_w4a8_debug": ([I, I, I, P, P, P, P, P, P, P, P, P, Z, P], I),
         "qgemm_set_gemv_max_m": ([I], I),
     }
@@ -79,6 +80,16 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if path == LIB_PATH:
         _lib = lib
     return lib
+
+
+ACTIVATIONS = {"none": 0, "relu": 1, "silu": 2, "gelu": 3}
+OUT_TYPES = {"f32": 0, "f16": 1}
+
+
+class Epilogue(ctypes.Structure):
+    """Mirror of qgemm_epilogue: C = act(A x B + bias + residual), C fp32 or fp16."""
+    _fields_ = [("bias", ctypes.c_void_p), ("residual", ctypes.c_void_p),
+                ("activation", ctypes.c_int), ("out_type", ctypes.c_int)]
 
 
 def _fmt(f) -> int:
@@ -194,6 +205,20 @@ def qgemm_run_ws(M: int, K: int, N: int, fmt, A, Bq, scales, C, workspace, ws_by
     _check(load().qgemm_run_ws(M, K, N, _fmt(fmt), _dev_ptr(A), _dev_ptr(Bq), _dev_ptr(scales),
                                _dev_ptr(C), _dev_ptr(workspace), ws_bytes, _stream(stream)),
            "qgemm_run_ws")
+
+
+def qgemm_run_ex(M: int, K: int, N: int, fmt, A, Bq, scales, C, bias=None, residual=None,
+                 activation="none", out_type="f32", workspace=None, ws_bytes: int = 0,
+                 stream=None) -> None:
+    """C = act(A x B + bias + residual) on the GPU; C (and residual) fp32 or fp16
+    per out_type. With no workspace the library allocates any scratch the shape
+    needs in stream order."""
+    epi = Epilogue(_dev_ptr(bias), _dev_ptr(residual),
+                   ACTIVATIONS[activation] if isinstance(activation, str) else int(activation),
+                   OUT_TYPES[out_type] if isinstance(out_type, str) else int(out_type))
+    _check(load().qgemm_run_ex(M, K, N, _fmt(fmt), _dev_ptr(A), _dev_ptr(Bq), _dev_ptr(scales),
+                               _dev_ptr(C), ctypes.byref(epi), _dev_ptr(workspace), ws_bytes,
+                               _stream(stream)), "qgemm_run_ex")
 
 
 def qgemm_w4a8_debug(M: int, K: int, N: int, A, Bq, scales, C, qa, sa, S, D, workspace,
