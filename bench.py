@@ -42,11 +42,14 @@ def algorithmic_bytes(M: int, K: int, N: int, fmt: str = "int4b64", epi: dict | 
     """Bytes the product must move at least once: A, the stored weight codes,
     the fp32 [offset, scale] pairs and C (fp32, or fp16 with an fp16
     epilogue, plus its bias and residual). Int4 formats hold K/2 bytes of
-    codes per channel, Int8-Block0 K bytes, fp32 B 4*K*N bytes; Int4-Block64
+    codes per channel, Int8-Block0 K bytes, fp32 B 4*K*N bytes, fp16 B 2*K*N
+    bytes; Int4-Block64
     has K/64 pairs per channel, the per-channel formats one."""
     a_bytes = M * K * (4 if fmt == "f32" else 2)
     if fmt == "f32":
         w_bytes, p_bytes = 4 * K * N, 0
+    elif fmt == "f16":
+        w_bytes, p_bytes = 2 * K * N, 0
     elif fmt == "int8b0":
         w_bytes, p_bytes = K * N, 8 * N
     elif fmt == "int4b64":
@@ -253,9 +256,13 @@ class ShapeWorkload(Workload):
         from weight_quantized_gemm_amd import synth
         rng = np.random.default_rng(seed)
         self.name, self.fmt, self.M, self.K, self.N = f"{fmt} {M}x{K}x{N}", fmt, M, K, N
+        self.epi = None
         self.A_host = synth.activations(rng, M, K, fp16=(fmt != "f32"))
         if fmt == "f32":
             wp, sp = synth.float_pattern_weights(K, N), None
+        elif fmt == "f16":
+            wp, sp = Q.qgemm_pack_weights(K, N, fmt, synth.half_pattern_weights(K, N), None)
+            sp = None
         else:
             q, p = Q.qgemm_quantize_weights(synth.normal_weights(rng, N, K), fmt)
             wp, sp = Q.qgemm_pack_weights(K, N, fmt, q, p)

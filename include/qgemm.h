@@ -16,12 +16,16 @@
  *                   registration"): 4-bit per-channel codes unpacked to
  *                   int8; each row of A is quantised on the fly to int8; the
  *                   product is s8 x s8 -> s32, exact, then rescaled to fp32.
+ *   QGEMM_F16       fp16 weights: the float mode at FP16 precision, as the
+ *                   page ran it (section "Sample data"); fp16 A and B, fp32
+ *                   accumulation, fp32 C.
  *
- * Format ids equal the page's mode numbers. For every quantised format A is
- * fp16 and C is fp32.
+ * Format ids 0-3 equal the page's mode numbers. For every format but F32, A
+ * is fp16; C is fp32 (or fp16 through qgemm_run_ex).
  *
  * Canonical (user-facing) weight layouts, on the host:
  *   - F32:      B float [K][N] row-major (the page's weight shape {ic, oc}).
+ *   - F16:      B fp16 [K][N] row-major, as F32.
  *   - INT8_B0:  q uint8 [N][K]; pairs float [N][1][2] = {offset, scale}.
  *   - INT4_B64: q uint8 [N][K/2], byte j of a row = q[2j] | q[2j+1] << 4
  *               (two codes per byte along K, low nibble first);
@@ -68,7 +72,8 @@ typedef enum qgemm_format {
     QGEMM_F32 = 0,
     QGEMM_INT4_B64 = 1,
     QGEMM_INT8_B0 = 2,
-    QGEMM_W4A8 = 3
+    QGEMM_W4A8 = 3,
+    QGEMM_F16 = 4
 } qgemm_format;
 
 typedef enum qgemm_status {

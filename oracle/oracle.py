@@ -240,6 +240,11 @@ def reference(fmt: str, A, B=None, q=None, pairs=None, lib=None) -> np.ndarray:
     """C float64 of one format on canonical inputs."""
     if fmt == "f32":
         return gemm_f32(A, B, lib)
+    if fmt == "f16":
+        # fp16 weights (the float mode at FP16 precision): the same plain
+        # product of the fp16 values, each widened exactly
+        return gemm_f32(np.asarray(A, np.float16).astype(np.float32),
+                        np.asarray(B, np.float16).astype(np.float32), lib)
     if fmt in ("int4b64", "int8b0"):
         return gemm_blockq(A, q, pairs, fmt, lib)
     if fmt == "w4a8":

@@ -118,6 +118,25 @@ def test_run_ex_validation(lib):
     assert need > 0 and ex(ws=v(512), nb=need - 1) == 8
 
 
+def test_f16_layout_and_checks(lib):
+    """fp16 weights: channel rows [roundup(N,4)][roundup(K,64)] fp16, zero
+    padded; pack/unpack round trip; not quantisable; scales must be NULL."""
+    K, N = 137, 70
+    B = (np.arange(K * N, dtype=np.float64).reshape(K, N) / 997.0).astype(np.float16)
+    wb, sb = Q.qgemm_packed_size(K, N, "f16")
+    assert sb == 0 and wb == ((72 * 192 * 2 + 255) // 256) * 256
+    wp, sp = Q.qgemm_pack_weights(K, N, "f16", B, None)
+    rows = wp[: 72 * 192 * 2].view(np.float16).reshape(72, 192)
+    assert np.array_equal(rows[:N, :K], B.T) and not rows[N:].any() and not rows[:, K:].any()
+    q, _ = Q.qgemm_unpack_weights(K, N, "f16", wp, sp)
+    assert np.array_equal(q.view(np.float16).reshape(K, N), B)
+    with pytest.raises(Q.QGemmError) as e:
+        Q.qgemm_quantize_weights(np.zeros((N, K), np.float32), "f16")
+    assert e.value.status == 3
+    v = ctypes.c_void_p
+    assert lib.qgemm_run(2, K, N, 4, v(256), v(256), v(256), v(256), None) == 3   # scales given
+
+
 def test_sizes():
     assert Q.qgemm_packed_size(4096, 11008, "int4b64") == (22544384, 5636096)
     assert Q.qgemm_packed_size(4096, 100, "int4b64") == (4 * 64 * 1024, 4 * 64 * 256)

@@ -30,7 +30,8 @@ def _gpu():
 
 SHAPES = [("f32", 16, 256, 256), ("f32", 8, 2560, 1024), ("f32", 130, 512, 200),
           ("int4b64", 1, 4096, 300), ("int4b64", 96, 1024, 300), ("int4b64", 65, 4096, 256),
-          ("int8b0", 3, 1000, 130), ("int8b0", 130, 640, 200), ("w4a8", 100, 640, 256)]
+          ("int8b0", 3, 1000, 130), ("int8b0", 130, 640, 200), ("w4a8", 100, 640, 256),
+          ("f16", 3, 1000, 130), ("f16", 130, 640, 200)]
 EPILOGUES = [("bias", "silu", "f32", False), ("residual", "gelu", "f16", False),
              ("bias+residual", "relu", "f32", False), ("bias+residual", "gelu", "f16", True),
              ("bias+residual", "none", "f32", True)]
@@ -39,11 +40,11 @@ EPILOGUES = [("bias", "silu", "f32", False), ("residual", "gelu", "f16", False),
 def _product(fmt, M, K, N, seed):
     """Inputs, packed device weights and the oracle's fp64 product."""
     rng = np.random.default_rng(seed)
-    if fmt == "f32":
-        A = synth.activations(rng, M, K, fp16=False)
-        B = synth.float_pattern_weights(K, N)
+    if fmt in ("f32", "f16"):
+        A = synth.activations(rng, M, K, fp16=(fmt == "f16"))
+        B = synth.float_pattern_weights(K, N) if fmt == "f32" else synth.half_pattern_weights(K, N)
         wp, sp = Q.qgemm_pack_weights(K, N, fmt, B, None)
-        return A, dev(wp), None, O.gemm_f32(A, B)
+        return A, dev(wp), None, O.reference(fmt, A, B=B)
     A = synth.activations(rng, M, K, fp16=True)
     q, p = Q.qgemm_quantize_weights(synth.normal_weights(rng, N, K), fmt)
     wp, sp = Q.qgemm_pack_weights(K, N, fmt, q, p)

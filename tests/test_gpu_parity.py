@@ -36,6 +36,8 @@ def _case(fmt, M, K, N, seed):
     if fmt == "f32":
         A = synth.activations(rng, M, K, fp16=False)
         return A, synth.float_pattern_weights(K, N), None
+    if fmt == "f16":
+        return synth.activations(rng, M, K, fp16=True), synth.half_pattern_weights(K, N), None
     A = synth.activations(rng, M, K, fp16=True)
     W = synth.normal_weights(rng, N, K)
     return A, W, None
@@ -51,11 +53,11 @@ def _quantized_pair(fmt, W):
 def _parity(fmt, M, K, N, seed, rows=None, stream=None, ws=False):
     """Runs one shape on the GPU and checks it (optionally on sampled rows)."""
     A, W, _ = _case(fmt, M, K, N, seed)
-    if fmt == "f32":
+    if fmt in ("f32", "f16"):
         C = run(fmt, M, K, N, A, W, None, stream=stream)
         sel = slice(None) if rows is None else rows
-        ref = O.gemm_f32(A[sel], W)
-        return compare(C[sel], ref, f"f32 {M}x{K}x{N}")
+        ref = O.reference(fmt, A[sel], B=W)
+        return compare(C[sel], ref, f"{fmt} {M}x{K}x{N}")
     q, p, qo, po = _quantized_pair(fmt, W)
     C = run(fmt, M, K, N, A, q, p, stream=stream, ws=ws)
     sel = slice(None) if rows is None else rows
@@ -122,12 +124,20 @@ SMALL_M = [1, 2, 3, 4, 5, 7, 8, 9, 63, 64, 65, 129]
 
 
 @pytest.mark.parametrize("M", SMALL_M)
+def test_f16_shapes(M):
+    """fp16 weights: GEMV for M <= 8 up to K = 8192, the tiled GEMM otherwise
+    (so K = 9000 takes the GEMM at every M); ragged K and N."""
+    for K, N in [(64, 1), (137, 70), (256, 130), (4160, 67), (9000, 40)]:
+        _parity("f16", M, K, N, seed=M * 5 + K + N)
+
+
+@pytest.mark.parametrize("M", SMALL_M)
 def test_int4b64_shapes(M):
     for K, N in [(64, 1), (64, 5), (192, 70), (256, 130), (4160, 67)]:
         _parity("int4b64", M, K, N, seed=M * 7 + K + N)
 
 
-@pytest.mark.parametrize("fmt", ["f32", "int8b0", "int4b64", "w4a8"])
+@pytest.mark.parametrize("fmt", ["f32", "f16", "int8b0", "int4b64", "w4a8"])
 @pytest.mark.parametrize("K,N", synth.PAGE_KN)
 def test_page_shape_grid(fmt, K, N):
     """Every (K, N) of the benchmark page's default sizes at its M values, every
@@ -343,13 +353,13 @@ def test_w4a8_debug_bit_exact_mid_size():
 # ---------------------------------------------------------------------------
 # Runtime behaviour.
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("fmt", ["int4b64", "int8b0", "w4a8", "f32"])
+@pytest.mark.parametrize("fmt", ["int4b64", "int8b0", "w4a8", "f32", "f16"])
 def test_deterministic_and_stream(fmt):
     """Repeated runs are bit-identical (no atomics), also on a side stream
     and through the workspace entry point."""
     M, K, N = (130, 512, 200)
     A, W, _ = _case(fmt, M, K, N, seed=3)
-    if fmt == "f32":
+    if fmt in ("f32", "f16"):
         wc, p = W, None
     else:
         wc, p = Q.qgemm_quantize_weights(W, fmt)

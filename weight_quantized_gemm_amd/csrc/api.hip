@@ -66,7 +66,7 @@ static qgemm_status check_run(int M, int K, int N, qgemm_format f, const void *A
     if (*empty) return QGEMM_OK;
     if (!C) return QGEMM_ERR_NULL;
     if (K > 0 && (!A || !Bq)) return QGEMM_ERR_NULL;
-    if (f == QGEMM_F32) {
+    if (f == QGEMM_F32 || f == QGEMM_F16) {   // float weights: no pairs
         if (scales) return QGEMM_ERR_FORMAT;
     } else if (!scales) {
         return QGEMM_ERR_NULL;
@@ -110,11 +110,14 @@ static qgemm_status run_w4a8(int M, int K, int N, const Geometry &g, const void 
     return launched(launch_w4a8_gemm(M, K, N, w.qa_stride, qa, sa, S, Bq, scales, C, epi, D_debug, s));
 }
 
-// The Int4-Block64 and Int8-Block0 GEMV kernels serve M <= the current GEMV
-// limit (and K within the register budget); everything else takes a tiled
-// GEMM.
+// The Int4-Block64, Int8-Block0 and fp16-weight GEMV kernels serve M <= the
+// current GEMV limit (and K within their register budgets); everything else
+// takes a tiled GEMM.
 static bool use_gemv(qgemm_format f, int M, int K) {
-    return (f == QGEMM_INT4_B64 || f == QGEMM_INT8_B0) && M <= gemv_max_m() && K <= kGemvMaxK;
+    if (M > gemv_max_m()) return false;
+    if (f == QGEMM_INT4_B64 || f == QGEMM_INT8_B0) return K <= kGemvMaxK;
+    if (f == QGEMM_F16) return K <= kGemvF16MaxK;
+    return false;
 }
 
 // Scratch bytes one call actually touches: the W4A8 activation codes first,
@@ -146,6 +149,9 @@ static qgemm_status dispatch(int M, int K, int N, qgemm_format f, const Geometry
                              : launch_gemm_int8b0(M, K, N, A, Bq, scales, C, epi, s));
     case QGEMM_W4A8:
         return run_w4a8(M, K, N, g, A, Bq, scales, C, epi, ws, s, nullptr);
+    case QGEMM_F16:
+        return launched(gemv ? launch_gemv_f16(M, K, N, A, Bq, C, epi, s)
+                             : launch_gemm_f16(M, K, N, A, Bq, C, epi, s));
     }
     return QGEMM_ERR_FORMAT;
 }

@@ -1,5 +1,7 @@
-// gemm_int8.hip -- prefill GEMM (M above the GEMV threshold) with
-// Int8-Block0 weights on the fp16 matrix cores.
+// gemm_int8.hip -- prefill GEMM (M above the GEMV threshold) for weights
+// stored as channel rows [Np][Kp] on the fp16 matrix cores: Int8-Block0
+// codes, or fp16 weights (the float mode at FP16 precision, which the same
+// kernel multiplies as they are, with no pair and no regrouping).
 //
 // What is computed (MNN GemmSpeed benchmark page, section "Why Conv1x1 is
 // used to measure GEMM"): C = A x deq(B), deq(B)[k][n] = offset[n] +
@@ -30,6 +32,8 @@
 // re-load its last half-block and skip only the arithmetic, in a uniform
 // branch that contains no load. The four partial tiles and row sums are
 // added in LDS in a fixed order.
+#include <type_traits>
+
 #include "kernels_common.h"
 #include "qgemm_internal.h"
 
@@ -61,9 +65,10 @@ __device__ __forceinline__ h8_t codes_biased(u2_t codes) {
 }
 
 // KMODE 0: K % 64 == 0 (no masking); 1: K % 8 == 0 (16-byte pieces, masked
-// past K); 2: any K (element loads, masked past K).
-template <int KMODE>
-__global__ __launch_bounds__(256) void gemm_int8b0_kernel(
+// past K); 2: any K (element loads, masked past K). WF16: the rows hold fp16
+// weights (2 bytes each) instead of Int8-Block0 codes.
+template <int KMODE, bool WF16>
+__global__ __launch_bounds__(256) void gemm_rows_kernel(
     int M, int K, int N, int Kp, int tiles_n, int xcd_order, const _Float16 *__restrict__ A,
     const uint8_t *__restrict__ Wp, const float *__restrict__ Sp, void *__restrict__ C,
     Epilogue epi) {
@@ -94,9 +99,11 @@ __global__ __launch_bounds__(256) void gemm_int8b0_kernel(
     const _Float16 *a_row[RF];
 #pragma unroll
     for (int rf = 0; rf < RF; ++rf) a_row[rf] = A + (size_t)min(m0 + rf * 16 + r, M - 1) * K;
+    constexpr int WB = WF16 ? 2 : 1;          // bytes per weight
+    using BV = std::conditional_t<WF16, u4_t, u2_t>;   // one lane's 8 weights
     const uint8_t *b_row[CF];
 #pragma unroll
-    for (int cf = 0; cf < CF; ++cf) b_row[cf] = Wp + (size_t)min(n0 + cf * 16 + r, N - 1) * Kp;
+    for (int cf = 0; cf < CF; ++cf) b_row[cf] = Wp + (size_t)min(n0 + cf * 16 + r, N - 1) * Kp * WB;
 
     // lane (r, g) holds K-elements k0 + 8 g .. k0 + 8 g + 7 of each half-block
     auto k_of = [&](int it) { return (wave + 4 * (it >> 1)) * BK + 32 * (it & 1) + 8 * g; };
@@ -121,10 +128,10 @@ __global__ __launch_bounds__(256) void gemm_int8b0_kernel(
             }
         }
     };
-    auto load_b = [&](u2_t (&dst)[CF], int it) {
+    auto load_b = [&](BV (&dst)[CF], int it) {
         const int k = k_of(it);
 #pragma unroll
-        for (int cf = 0; cf < CF; ++cf) dst[cf] = *reinterpret_cast<const u2_t *>(b_row[cf] + k);
+        for (int cf = 0; cf < CF; ++cf) dst[cf] = *reinterpret_cast<const BV *>(b_row[cf] + (size_t)k * WB);
     };
 
     f4_t acc[RF][CF];
@@ -138,7 +145,7 @@ __global__ __launch_bounds__(256) void gemm_int8b0_kernel(
     const h2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
 
     u4_t ra[RA][RF];
-    u2_t rb[RB][CF];
+    BV rb[RB][CF];
     if (n_it > 0) {            // a wave with no K-block (K < 256) loads nothing
 #pragma unroll
         for (int d = 0; d < RA - 1; ++d) load_a(ra[d], min(d, it_last));
@@ -155,15 +162,20 @@ __global__ __launch_bounds__(256) void gemm_int8b0_kernel(
                 load_a(ra[(u + RA - 1) % RA], min(it + RA - 1, it_last));
                 h8_t bw[CF];
 #pragma unroll
-                for (int cf = 0; cf < CF; ++cf) bw[cf] = codes_biased(rb[u % RB][cf]);
+                for (int cf = 0; cf < CF; ++cf) {
+                    if constexpr (WF16) bw[cf] = __builtin_bit_cast(h8_t, rb[u % RB][cf]);
+                    else bw[cf] = codes_biased(rb[u % RB][cf]);
+                }
                 const u4_t (&av)[RF] = ra[u % RA];
                 if (it < n_it) {
 #pragma unroll
                     for (int rf = 0; rf < RF; ++rf) {
                         const h8_t a = __builtin_bit_cast(h8_t, av[rf]);
+                        if constexpr (!WF16) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            rs[rf] = dot2(h2_t{a[2 * e], a[2 * e + 1]}, ones, rs[rf]);
+                            for (int e = 0; e < 4; ++e)
+                                rs[rf] = dot2(h2_t{a[2 * e], a[2 * e + 1]}, ones, rs[rf]);
+                        }
 #pragma unroll
                         for (int cf = 0; cf < CF; ++cf)
                             acc[rf][cf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bw[cf], acc[rf][cf], 0, 0, 0);
@@ -213,8 +225,12 @@ __global__ __launch_bounds__(256) void gemm_int8b0_kernel(
         f4_t out;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const f2_t pr = *reinterpret_cast<const f2_t *>(Sp + (size_t)min(n0 + c0 + j + e, N - 1) * 2);
-            out[e] = fmaf(pr.y, p[e], fmaf(-1024.0f, pr.y, pr.x) * rsm);
+            if constexpr (WF16) {
+                out[e] = p[e];
+            } else {
+                const f2_t pr = *reinterpret_cast<const f2_t *>(Sp + (size_t)min(n0 + c0 + j + e, N - 1) * 2);
+                out[e] = fmaf(pr.y, p[e], fmaf(-1024.0f, pr.y, pr.x) * rsm);
+            }
         }
         if (!epi.plain && vec_store) {
             epi_put4(epi, C, gm, n0 + c0 + j, N, out);
@@ -232,8 +248,9 @@ __global__ __launch_bounds__(256) void gemm_int8b0_kernel(
     }
 }
 
-hipError_t launch_gemm_int8b0(int M, int K, int N, const void *A, const void *Wp,
-                              const void *Sp, void *C, const Epilogue &epi, hipStream_t s) {
+template <bool WF16>
+static hipError_t launch_rows(int M, int K, int N, const void *A, const void *Wp, const void *Sp,
+                              void *C, const Epilogue &epi, hipStream_t s) {
     const int Kp = (int)round_up(K, 64);
     const int tiles_n = div_up(N, BN);
     const int tiles = tiles_n * div_up(M, BM);
@@ -243,10 +260,20 @@ hipError_t launch_gemm_int8b0(int M, int K, int N, const void *A, const void *Wp
                            static_cast<const _Float16 *>(A), static_cast<const uint8_t *>(Wp),
                            static_cast<const float *>(Sp), C, epi);
     };
-    if (K % 64 == 0) launch(gemm_int8b0_kernel<0>);
-    else if (K % 8 == 0) launch(gemm_int8b0_kernel<1>);
-    else launch(gemm_int8b0_kernel<2>);
+    if (K % 64 == 0) launch(gemm_rows_kernel<0, WF16>);
+    else if (K % 8 == 0) launch(gemm_rows_kernel<1, WF16>);
+    else launch(gemm_rows_kernel<2, WF16>);
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_int8b0(int M, int K, int N, const void *A, const void *Wp,
+                              const void *Sp, void *C, const Epilogue &epi, hipStream_t s) {
+    return launch_rows<false>(M, K, N, A, Wp, Sp, C, epi, s);
+}
+
+hipError_t launch_gemm_f16(int M, int K, int N, const void *A, const void *Wp, void *C,
+                           const Epilogue &epi, hipStream_t s) {
+    return launch_rows<true>(M, K, N, A, Wp, nullptr, C, epi, s);
 }
 
 }  // namespace qg

@@ -299,6 +299,85 @@ __global__ __launch_bounds__(64 * I8_WAVES) void gemv_int8b0_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// fp16-weight GEMV (the float mode at FP16 precision): the Int8-Block0
+// structure with fp16 channel rows [Np][Kp]. One wave per channel reads its
+// row as 16-byte slices l, l + 64, ... (eight weights each; 1 KiB of
+// contiguous bytes per load instruction), all requested before the
+// activations are staged in LDS; each weight pair meets its activation pair
+// in one v_dot2 (products exact in fp32, fp32 sums).
+// ---------------------------------------------------------------------------
+template <int MR, int NCH>
+__global__ __launch_bounds__(64 * I8_WAVES) void gemv_f16_kernel(
+    int M, int K, int N, int Kp, const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
+    void *__restrict__ C, Epilogue epi) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    _Float16 *As = reinterpret_cast<_Float16 *>(lds);   // [MR][Kp], zero past K
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = uniform(tid >> 6);
+    const int m0 = blockIdx.y * MR;
+    const int Np = (N + 3) & ~3;
+    const int n = blockIdx.x * I8_WAVES + wave;
+    const int nc = min(n, Np - 1);
+    const int nslice = Kp >> 3;              // 16-byte slices per channel
+
+    // 1. this wave's weight slices (clamped: slices past the row end reread
+    //    the last slice and are skipped in the arithmetic)
+    u4_t wq[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int ci = min(lane + 64 * i, nslice - 1);
+        wq[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const u4_t *>(Wp + ((size_t)nc * Kp + (size_t)ci * 8) * 2));
+    }
+
+    // 2. activations to LDS, zero past K
+    if ((K & 7) == 0) {
+        const int pieces = Kp >> 3;
+        for (int p = tid; p < MR * pieces; p += 64 * I8_WAVES) {
+            const int r = p / pieces, c = p - r * pieces;
+            u4_t v = {0u, 0u, 0u, 0u};
+            if (m0 + r < M && c * 8 < K)
+                v = *reinterpret_cast<const u4_t *>(A + (size_t)(m0 + r) * K + (size_t)c * 8);
+            *reinterpret_cast<u4_t *>(As + (size_t)r * Kp + (size_t)c * 8) = v;
+        }
+    } else {
+        for (int e = tid; e < MR * Kp; e += 64 * I8_WAVES) {
+            const int r = e / Kp, k = e - r * Kp;
+            As[e] = (m0 + r < M && k < K) ? A[(size_t)(m0 + r) * K + k] : (_Float16)0.0f;
+        }
+    }
+    __syncthreads();
+
+    // 3. sum(a * w) per row over this lane's slices
+    float T[MR];
+#pragma unroll
+    for (int r = 0; r < MR; ++r) T[r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int ci = lane + 64 * i;
+        if (ci >= nslice) break;
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+            const u4_t av = *reinterpret_cast<const u4_t *>(As + (size_t)r * Kp + (size_t)ci * 8);
+#pragma unroll
+            for (int wi = 0; wi < 4; ++wi) T[r] = dot2(as_h2(wq[i][wi]), as_h2(av[wi]), T[r]);
+        }
+    }
+    // 4. per row: reduce over the wave and store
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+        float v = T[r];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+        if (lane == 0 && n < N && m0 + r < M) {
+            if (epi.plain) static_cast<float *>(C)[(size_t)(m0 + r) * N + n] = v;
+            else epi_put(epi, C, m0 + r, n, N, v);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 static int rows_per_pass(int M, int K, int kp_bytes_per_row) {
@@ -367,6 +446,38 @@ hipError_t launch_gemv_int8b0(int M, int K, int N, const void *A, const void *Wp
     case 4: return gemv_int8_k<4>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
     case 2: return gemv_int8_k<2>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
     default: return gemv_int8_k<1>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
+    }
+}
+
+template <int MR, int NCH>
+static hipError_t gemv_f16_mr(int M, int K, int N, int Kp, const void *A, const void *Wp, void *C,
+                              const Epilogue &epi, hipStream_t s) {
+    dim3 grid(div_up(N, I8_WAVES), div_up(M, MR));
+    const size_t lds = (size_t)MR * Kp * sizeof(_Float16);
+    hipLaunchKernelGGL((gemv_f16_kernel<MR, NCH>), grid, dim3(64 * I8_WAVES), lds, s, M, K, N, Kp,
+                       static_cast<const _Float16 *>(A), static_cast<const uint8_t *>(Wp), C, epi);
+    return hipGetLastError();
+}
+
+template <int MR>
+static hipError_t gemv_f16_k(int M, int K, int N, int Kp, const void *A, const void *Wp, void *C,
+                             const Epilogue &epi, hipStream_t s) {
+    // slices per lane: Kp / 512, rounded up to a power of two (K <= 8192)
+    const int nch = div_up(Kp, 512);
+    if (nch <= 1) return gemv_f16_mr<MR, 1>(M, K, N, Kp, A, Wp, C, epi, s);
+    if (nch <= 2) return gemv_f16_mr<MR, 2>(M, K, N, Kp, A, Wp, C, epi, s);
+    if (nch <= 4) return gemv_f16_mr<MR, 4>(M, K, N, Kp, A, Wp, C, epi, s);
+    if (nch <= 8) return gemv_f16_mr<MR, 8>(M, K, N, Kp, A, Wp, C, epi, s);
+    return gemv_f16_mr<MR, 16>(M, K, N, Kp, A, Wp, C, epi, s);
+}
+
+hipError_t launch_gemv_f16(int M, int K, int N, const void *A, const void *Wp, void *C,
+                           const Epilogue &epi, hipStream_t s) {
+    const int Kp = (int)round_up(K, 64);
+    switch (rows_per_pass(M, K, Kp * 2)) {
+    case 4: return gemv_f16_k<4>(M, K, N, Kp, A, Wp, C, epi, s);
+    case 2: return gemv_f16_k<2>(M, K, N, Kp, A, Wp, C, epi, s);
+    default: return gemv_f16_k<1>(M, K, N, Kp, A, Wp, C, epi, s);
     }
 }
 

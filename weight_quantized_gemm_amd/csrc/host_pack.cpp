@@ -15,7 +15,8 @@
 namespace qg {
 
 static bool valid_format(int f) {
-    return f == QGEMM_F32 || f == QGEMM_INT4_B64 || f == QGEMM_INT8_B0 || f == QGEMM_W4A8;
+    return f == QGEMM_F32 || f == QGEMM_INT4_B64 || f == QGEMM_INT8_B0 || f == QGEMM_W4A8 ||
+           f == QGEMM_F16;
 }
 
 // Shapes are capped so that every element count and byte offset the kernels
@@ -23,6 +24,9 @@ static bool valid_format(int f) {
 constexpr int kMaxDim = 1 << 24;
 // W4A8 keeps D = sum_k qa * q in int32: |D| <= K * 127 * 15 must stay < 2^31.
 constexpr long long kW4A8MaxK = ((1LL << 31) - 1) / (127 * 15);
+
+// The quantised formats carry [offset, scale] pairs; float weights do not.
+static bool has_pairs(qgemm_format f) { return f != QGEMM_F32 && f != QGEMM_F16; }
 
 qgemm_status geometry(int K, int N, qgemm_format f, Geometry *g) {
     if (!valid_format(f)) return QGEMM_ERR_FORMAT;
@@ -34,6 +38,13 @@ qgemm_status geometry(int K, int N, qgemm_format f, Geometry *g) {
     case QGEMM_F32:
         r.Kp = K; r.Np = N; r.nblk = 0;
         r.w_bytes = round_up((size_t)K * N * sizeof(float), kPackAlign);
+        r.s_bytes = 0;
+        break;
+    case QGEMM_F16:
+        // channel rows [Np][Kp] of fp16 weights, zero padded
+        if (K == 0) return QGEMM_ERR_SHAPE;
+        r.Kp = (int)round_up(K, 64); r.Np = (int)round_up(N, 4); r.nblk = 0;
+        r.w_bytes = round_up((size_t)r.Np * r.Kp * 2, kPackAlign);
         r.s_bytes = 0;
         break;
     case QGEMM_INT4_B64:
@@ -117,13 +128,14 @@ RunWorkspace run_workspace(qgemm_format f, int M, int K, int N) {
 static size_t canonical_q_bytes(const Geometry &g, qgemm_format f) {
     switch (f) {
     case QGEMM_F32: return (size_t)g.K * g.N * sizeof(float);
+    case QGEMM_F16: return (size_t)g.K * g.N * 2;
     case QGEMM_INT8_B0: return (size_t)g.N * g.K;
     default: return (size_t)g.N * (g.K / 2);
     }
 }
 
 static size_t canonical_pair_floats(const Geometry &g, qgemm_format f) {
-    return f == QGEMM_F32 ? 0 : (size_t)g.N * g.nblk * 2;
+    return has_pairs(f) ? (size_t)g.N * g.nblk * 2 : 0;
 }
 
 // Canonical code of channel n at k (INT4 / W4A8: low nibble first).
@@ -191,7 +203,7 @@ qgemm_status qgemm_workspace_size(int M, int K, int N, qgemm_format f, size_t *b
 qgemm_status qgemm_quantize_weights(int K, int N, qgemm_format f, const float *W,
                                     void *q_out, size_t q_bytes, float *pairs,
                                     size_t pair_floats) {
-    if (f == QGEMM_F32) return QGEMM_ERR_FORMAT;
+    if (!has_pairs(f)) return QGEMM_ERR_FORMAT;   // float weights are not quantised
     Geometry g;
     qgemm_status st = geometry(K, N, f, &g);
     if (st != QGEMM_OK) return st;
@@ -252,7 +264,7 @@ qgemm_status qgemm_pack_weights(int K, int N, qgemm_format f, const void *w_cano
     if (!w_packed || (g.s_bytes && !s_packed)) return QGEMM_ERR_NULL;
     if (w_bytes < g.w_bytes || s_bytes < g.s_bytes) return QGEMM_ERR_SIZE;
     if ((size_t)N * K > 0 && !w_canonical) return QGEMM_ERR_NULL;
-    if (f != QGEMM_F32 && N > 0 && !pairs_canonical) return QGEMM_ERR_NULL;
+    if (has_pairs(f) && N > 0 && !pairs_canonical) return QGEMM_ERR_NULL;
 
     uint8_t *wp = static_cast<uint8_t *>(w_packed);
     uint8_t *sp = static_cast<uint8_t *>(s_packed);
@@ -265,6 +277,14 @@ qgemm_status qgemm_pack_weights(int K, int N, qgemm_format f, const void *w_cano
     case QGEMM_F32:
         if ((size_t)K * N) std::memcpy(wp, wc, (size_t)K * N * sizeof(float));
         break;
+    case QGEMM_F16: {
+        // [K][N] -> channel rows [Np][Kp]
+        const uint16_t *src = reinterpret_cast<const uint16_t *>(wc);
+        uint16_t *dst = reinterpret_cast<uint16_t *>(wp);
+        for (int k = 0; k < K; ++k)
+            for (int n = 0; n < N; ++n) dst[(size_t)n * g.Kp + k] = src[(size_t)k * N + n];
+        break;
+    }
     case QGEMM_INT4_B64: {
         const int nblk = g.nblk;
         const size_t row = (size_t)K / 2;
@@ -329,7 +349,7 @@ qgemm_status qgemm_unpack_weights(int K, int N, qgemm_format f, const void *w_pa
     if (!w_packed || (g.s_bytes && !s_packed)) return QGEMM_ERR_NULL;
     if (w_bytes < g.w_bytes || s_bytes < g.s_bytes) return QGEMM_ERR_SIZE;
     if ((size_t)N * K > 0 && !w_canonical) return QGEMM_ERR_NULL;
-    if (f != QGEMM_F32 && N > 0 && !pairs_canonical) return QGEMM_ERR_NULL;
+    if (has_pairs(f) && N > 0 && !pairs_canonical) return QGEMM_ERR_NULL;
 
     const uint8_t *wp = static_cast<const uint8_t *>(w_packed);
     const float *spf = reinterpret_cast<const float *>(s_packed);
@@ -339,6 +359,13 @@ qgemm_status qgemm_unpack_weights(int K, int N, qgemm_format f, const void *w_pa
     case QGEMM_F32:
         if ((size_t)K * N) std::memcpy(wc, wp, (size_t)K * N * sizeof(float));
         break;
+    case QGEMM_F16: {
+        const uint16_t *src = reinterpret_cast<const uint16_t *>(wp);
+        uint16_t *dst = reinterpret_cast<uint16_t *>(wc);
+        for (int k = 0; k < K; ++k)
+            for (int n = 0; n < N; ++n) dst[(size_t)k * N + n] = src[(size_t)n * g.Kp + k];
+        break;
+    }
     case QGEMM_INT4_B64: {
         const int nblk = g.nblk;
         const size_t row = (size_t)K / 2;

@@ -56,6 +56,7 @@ struct Geometry {
 qgemm_status geometry(int K, int N, qgemm_format f, Geometry *g);
 
 constexpr int kGemvMaxM = 8;          // largest M the GEMV kernels take
+constexpr int kGemvF16MaxK = 8192;   // fp16-weight GEMV: 16 slices of 8 per lane
 constexpr int kGemvMaxK = 16384;      // A rows staged in LDS: MR * K * 2 bytes
 
 // ---------------------------------------------------------------------------
@@ -91,6 +92,11 @@ hipError_t launch_splitk_reduce_f32(const float *part, int nsplit, int M, int N,
                                     const Epilogue &epi, hipStream_t s);
 hipError_t launch_gemm_int8b0(int M, int K, int N, const void *A, const void *Wp,
                               const void *Sp, void *C, const Epilogue &epi, hipStream_t s);
+// fp16 weights as channel rows [Np][Kp] (Kp = roundup(K, 64)).
+hipError_t launch_gemv_f16(int M, int K, int N, const void *A, const void *Wp, void *C,
+                           const Epilogue &epi, hipStream_t s);
+hipError_t launch_gemm_f16(int M, int K, int N, const void *A, const void *Wp, void *C,
+                           const Epilogue &epi, hipStream_t s);
 hipError_t launch_gemm_f32(int M, int K, int N, const float *A, const float *B, void *C,
                            const Epilogue &epi, int nsplit, float *part, hipStream_t s);
 // W4A8: qa [M][Kq] int8 (Kq = roundup(K, 128)), sa [M] float, S [M] int32

@@ -58,6 +58,12 @@ def float_pattern_weights(K: int, N: int) -> np.ndarray:
     return (((i % 127) - 63).astype(np.float64) / 1000.0).astype(np.float32)
 
 
+def half_pattern_weights(K: int, N: int) -> np.ndarray:
+    """fp16 weights for the float mode at FP16 precision: the page's float
+    filler rounded to fp16, B float16 [K][N]."""
+    return float_pattern_weights(K, N).astype(np.float16)
+
+
 def make_inputs(name: str):
     """Inputs of a named workload: dict(format, M, K, N, seed, A, and W or B)."""
     fmt, M, K, N, seed = CONFIGS[name]
