@@ -19,6 +19,9 @@
  *   QGEMM_F16       fp16 weights: the float mode at FP16 precision, as the
  *                   page ran it (section "Sample data"); fp16 A and B, fp32
  *                   accumulation, fp32 C.
+ *   QGEMM_INT4_B0   Int4-Block0 without A8: W4A8's per-channel 4-bit weights
+ *                   with fp16 activations (no activation quantisation);
+ *                   K % 64 == 0.
  *
  * Format ids 0-3 equal the page's mode numbers. For every format but F32, A
  * is fp16; C is fp32 (or fp16 through qgemm_run_ex).
@@ -31,8 +34,8 @@
  *               (two codes per byte along K, low nibble first);
  *               pairs float [N][K/64][2] = {offset, scale} (the page: oc x
  *               blockNum groups of [offset, scale]).
- *   - W4A8:     q as INT4_B64 with one block over all of K; pairs float
- *               [N][1][2].
+ *   - W4A8, INT4_B0: q as INT4_B64 with one block over all of K; pairs
+ *               float [N][1][2].
  * Codes are unsigned: q in [0, 2^bits - 1].
  *
  * Packed (device) layouts are opaque and owned by this library: they are
@@ -73,7 +76,8 @@ typedef enum qgemm_format {
     QGEMM_INT4_B64 = 1,
     QGEMM_INT8_B0 = 2,
     QGEMM_W4A8 = 3,
-    QGEMM_F16 = 4
+    QGEMM_F16 = 4,
+    QGEMM_INT4_B0 = 5
 } qgemm_format;
 
 typedef enum qgemm_status {

@@ -86,7 +86,7 @@ def _check(rc: int, what: str):
 
 
 # Format table: name -> (bits, block) ; block None means "all of K".
-FORMATS = {"int4b64": (4, 64), "int8b0": (8, None), "w4a8": (4, None)}
+FORMATS = {"int4b64": (4, 64), "int8b0": (8, None), "w4a8": (4, None), "int4b0": (4, None)}
 
 
 def _bits_block(fmt: str, K: int):
@@ -245,7 +245,7 @@ def reference(fmt: str, A, B=None, q=None, pairs=None, lib=None) -> np.ndarray:
         # product of the fp16 values, each widened exactly
         return gemm_f32(np.asarray(A, np.float16).astype(np.float32),
                         np.asarray(B, np.float16).astype(np.float32), lib)
-    if fmt in ("int4b64", "int8b0"):
+    if fmt in ("int4b64", "int8b0", "int4b0"):
         return gemm_blockq(A, q, pairs, fmt, lib)
     if fmt == "w4a8":
         return w4a8_gemm(A, q, pairs, lib)[0]

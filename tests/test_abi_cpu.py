@@ -10,7 +10,7 @@ from oracle import oracle as O
 from weight_quantized_gemm_amd import qgemm as Q
 from weight_quantized_gemm_amd import synth
 
-FMTS = ["int4b64", "int8b0", "w4a8"]
+FMTS = ["int4b64", "int8b0", "w4a8", "int4b0"]
 
 
 @pytest.fixture(scope="module")
@@ -135,6 +135,19 @@ def test_f16_layout_and_checks(lib):
     assert e.value.status == 3
     v = ctypes.c_void_p
     assert lib.qgemm_run(2, K, N, 4, v(256), v(256), v(256), v(256), None) == 3   # scales given
+
+
+def test_int4b0_packs_as_block64_with_repeated_pairs():
+    """Int4-Block0 packs exactly like Int4-Block64 whose every 64-block holds
+    the channel's one pair."""
+    N, K = 40, 256
+    rng = np.random.default_rng(9)
+    q, p = Q.qgemm_quantize_weights(synth.normal_weights(rng, N, K), "int4b0")
+    assert p.shape == (N * 2,) or p.size == N * 2
+    wp0, sp0 = Q.qgemm_pack_weights(K, N, "int4b0", q, p)
+    p64 = np.repeat(p.reshape(N, 1, 2), K // 64, axis=1)
+    wp1, sp1 = Q.qgemm_pack_weights(K, N, "int4b64", q, p64)
+    assert np.array_equal(wp0, wp1) and np.array_equal(sp0, sp1)
 
 
 def test_sizes():

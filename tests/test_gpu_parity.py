@@ -131,6 +131,14 @@ def test_f16_shapes(M):
         _parity("f16", M, K, N, seed=M * 5 + K + N)
 
 
+@pytest.mark.parametrize("M", [1, 3, 8, 9, 64, 65, 129])
+def test_int4b0_shapes(M):
+    """Int4-Block0 with fp16 activations (per-channel pairs) through the
+    Int4 GEMV and GEMM, split-K shapes included."""
+    for K, N in [(64, 5), (256, 130), (4096, 256), (2560, 1024)]:
+        _parity("int4b0", M, K, N, seed=M * 13 + K + N)
+
+
 @pytest.mark.parametrize("M", SMALL_M)
 def test_int4b64_shapes(M):
     for K, N in [(64, 1), (64, 5), (192, 70), (256, 130), (4160, 67)]:

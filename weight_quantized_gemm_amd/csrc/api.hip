@@ -115,7 +115,7 @@ static qgemm_status run_w4a8(int M, int K, int N, const Geometry &g, const void 
 // takes a tiled GEMM.
 static bool use_gemv(qgemm_format f, int M, int K) {
     if (M > gemv_max_m()) return false;
-    if (f == QGEMM_INT4_B64 || f == QGEMM_INT8_B0) return K <= kGemvMaxK;
+    if (f == QGEMM_INT4_B64 || f == QGEMM_INT4_B0 || f == QGEMM_INT8_B0) return K <= kGemvMaxK;
     if (f == QGEMM_F16) return K <= kGemvF16MaxK;
     return false;
 }
@@ -142,6 +142,7 @@ static qgemm_status dispatch(int M, int K, int N, qgemm_format f, const Geometry
         return launched(launch_gemm_f32(M, K, N, static_cast<const float *>(A),
                                         static_cast<const float *>(Bq), C, epi, nsplit, part, s));
     case QGEMM_INT4_B64:
+    case QGEMM_INT4_B0:   // packed as Int4-Block64 (one pair repeated per block)
         return launched(gemv ? launch_gemv_int4b64(M, K, N, A, Bq, scales, C, epi, s)
                              : launch_gemm_int4b64(M, K, N, A, Bq, scales, C, epi, nsplit, part, s));
     case QGEMM_INT8_B0:

@@ -16,7 +16,7 @@ namespace qg {
 
 static bool valid_format(int f) {
     return f == QGEMM_F32 || f == QGEMM_INT4_B64 || f == QGEMM_INT8_B0 || f == QGEMM_W4A8 ||
-           f == QGEMM_F16;
+           f == QGEMM_F16 || f == QGEMM_INT4_B0;
 }
 
 // Shapes are capped so that every element count and byte offset the kernels
@@ -48,10 +48,13 @@ qgemm_status geometry(int K, int N, qgemm_format f, Geometry *g) {
         r.s_bytes = 0;
         break;
     case QGEMM_INT4_B64:
+    case QGEMM_INT4_B0:
+        // Int4-Block0 is packed as Int4-Block64 with the channel's one pair
+        // repeated in every 64-block: the same weights, the same kernels
         if (K == 0 || K % 64 != 0) return QGEMM_ERR_SHAPE;
-        r.Kp = K; r.Np = (int)round_up(N, 32); r.nblk = K / 64;
-        r.w_bytes = round_up((size_t)(r.Np / 32) * r.nblk * 1024, kPackAlign);
-        r.s_bytes = round_up((size_t)(r.Np / 32) * r.nblk * 256, kPackAlign);
+        r.Kp = K; r.Np = (int)round_up(N, 32); r.nblk = f == QGEMM_INT4_B0 ? 1 : K / 64;
+        r.w_bytes = round_up((size_t)(r.Np / 32) * (K / 64) * 1024, kPackAlign);
+        r.s_bytes = round_up((size_t)(r.Np / 32) * (K / 64) * 256, kPackAlign);
         break;
     case QGEMM_INT8_B0:
         if (K == 0) return QGEMM_ERR_SHAPE;
@@ -92,6 +95,7 @@ int splitk_plan(qgemm_format f, int M, int K, int N) {
     int kunits = 0;                  // K granules: the most slices a split may have
     switch (f) {
     case QGEMM_INT4_B64:
+    case QGEMM_INT4_B0:
         tiles = (long long)div_up(M, kInt4TileM) * div_up(N, kInt4TileN);
         kunits = K / 64 / 8;         // four waves, two or more 64-blocks each
         break;
@@ -285,18 +289,21 @@ qgemm_status qgemm_pack_weights(int K, int N, qgemm_format f, const void *w_cano
             for (int n = 0; n < N; ++n) dst[(size_t)n * g.Kp + k] = src[(size_t)k * N + n];
         break;
     }
-    case QGEMM_INT4_B64: {
-        const int nblk = g.nblk;
+    case QGEMM_INT4_B64:
+    case QGEMM_INT4_B0: {
+        const int nblk = K / 64;
         const size_t row = (size_t)K / 2;
         for (int n = 0; n < N; ++n) {
             const int t = n >> 5, c = n & 31;
             for (int b = 0; b < nblk; ++b) {
                 const size_t rec = (size_t)t * nblk + b;
+                // Block0: the channel's one pair for every 64-block
+                const size_t pi = f == QGEMM_INT4_B0 ? (size_t)n * 2 : ((size_t)n * nblk + b) * 2;
                 for (int half = 0; half < 2; ++half)
                     std::memcpy(wp + rec * 1024 + (size_t)(32 * half + c) * 16,
                                 wc + (size_t)n * row + (size_t)b * 32 + half * 16, 16);
-                spf[rec * 64 + c * 2 + 0] = pairs_canonical[((size_t)n * nblk + b) * 2 + 0];
-                spf[rec * 64 + c * 2 + 1] = pairs_canonical[((size_t)n * nblk + b) * 2 + 1];
+                spf[rec * 64 + c * 2 + 0] = pairs_canonical[pi + 0];
+                spf[rec * 64 + c * 2 + 1] = pairs_canonical[pi + 1];
             }
         }
         break;
@@ -366,18 +373,20 @@ qgemm_status qgemm_unpack_weights(int K, int N, qgemm_format f, const void *w_pa
             for (int n = 0; n < N; ++n) dst[(size_t)k * N + n] = src[(size_t)n * g.Kp + k];
         break;
     }
-    case QGEMM_INT4_B64: {
-        const int nblk = g.nblk;
+    case QGEMM_INT4_B64:
+    case QGEMM_INT4_B0: {
+        const int nblk = K / 64;
         const size_t row = (size_t)K / 2;
         for (int n = 0; n < N; ++n) {
             const int t = n >> 5, c = n & 31;
             for (int b = 0; b < nblk; ++b) {
                 const size_t rec = (size_t)t * nblk + b;
+                const size_t pi = f == QGEMM_INT4_B0 ? (size_t)n * 2 : ((size_t)n * nblk + b) * 2;
                 for (int half = 0; half < 2; ++half)
                     std::memcpy(wc + (size_t)n * row + (size_t)b * 32 + half * 16,
                                 wp + rec * 1024 + (size_t)(32 * half + c) * 16, 16);
-                pairs_canonical[((size_t)n * nblk + b) * 2 + 0] = spf[rec * 64 + c * 2 + 0];
-                pairs_canonical[((size_t)n * nblk + b) * 2 + 1] = spf[rec * 64 + c * 2 + 1];
+                pairs_canonical[pi + 0] = spf[rec * 64 + c * 2 + 0];   // Block0: every block holds it
+                pairs_canonical[pi + 1] = spf[rec * 64 + c * 2 + 1];
             }
         }
         break;

@@ -21,10 +21,11 @@ import torch  # noqa: F401  (must be loaded before libqgemm.so; see module doc)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqgemm.so")
 
-# Format ids (0-3: the MNN GemmSpeed page's mode numbers; 4: fp16 weights) and names.
-QGEMM_F32, QGEMM_INT4_B64, QGEMM_INT8_B0, QGEMM_W4A8, QGEMM_F16 = 0, 1, 2, 3, 4
+# Format ids (0-3: the MNN GemmSpeed page's mode numbers; 4: fp16 weights;
+# 5: Int4-Block0 with fp16 activations) and names.
+QGEMM_F32, QGEMM_INT4_B64, QGEMM_INT8_B0, QGEMM_W4A8, QGEMM_F16, QGEMM_INT4_B0 = 0, 1, 2, 3, 4, 5
 FORMATS = {"f32": QGEMM_F32, "int4b64": QGEMM_INT4_B64, "int8b0": QGEMM_INT8_B0,
-           "w4a8": QGEMM_W4A8, "f16": QGEMM_F16}
+           "w4a8": QGEMM_W4A8, "f16": QGEMM_F16, "int4b0": QGEMM_INT4_B0}
 
 STATUS = {0: "QGEMM_OK", 1: "QGEMM_ERR_NULL", 2: "QGEMM_ERR_SHAPE", 3: "QGEMM_ERR_FORMAT",
           4: "QGEMM_ERR_ALIGN", 5: "QGEMM_ERR_NOMEM", 6: "QGEMM_ERR_DEVICE",
