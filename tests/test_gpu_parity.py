@@ -334,6 +334,38 @@ def test_w4a8_golden_rows_and_identity():
     assert np.array_equal(C.cpu().numpy(), sa.cpu().numpy()[:, None] * qa.cpu().numpy())
 
 
+def _w4a8_debug_check(M, K, N, seed, zero_row=None):
+    A, W, _ = _case("w4a8", M, K, N, seed=seed)
+    if zero_row is not None:
+        A[zero_row] = 0
+    q, p, qo, po = _quantized_pair("w4a8", W)
+    wp, sp = Q.qgemm_pack_weights(K, N, "w4a8", q, p)
+    nbytes = Q.qgemm_workspace_size(M, K, N, "w4a8")
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    qa = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    sa = torch.empty(M, dtype=torch.float32, device="cuda")
+    S = torch.empty(M, dtype=torch.int32, device="cuda")
+    D = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    Q.qgemm_w4a8_debug(M, K, N, dev(A), dev(wp), dev(sp), C, qa, sa, S, D, ws, nbytes)
+    torch.cuda.synchronize()
+    Cr, qa_o, sa_o, S_o, D_o = O.w4a8_gemm(A, qo, po)
+    assert np.array_equal(qa.cpu().numpy(), qa_o)
+    assert np.array_equal(sa.cpu().numpy(), sa_o)
+    assert np.array_equal(S.cpu().numpy(), S_o)
+    assert np.array_equal(D.cpu().numpy().astype(np.int64), D_o)
+    compare(C.cpu().numpy(), Cr, f"w4a8 {M}x{K}x{N}")
+    if zero_row is not None:
+        assert np.all(C.cpu().numpy()[zero_row] == 0)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 3072, 8192), (3, 1000, 70), (5, 9000, 96), (8, 4096, 300)])
+def test_w4a8_gemv_debug_bit_exact(M, K, N):
+    """The decode-shaped W4A8 GEMV (M <= 8): qa, sa, S and the int32 products
+    D bit-exact, ragged K and N, K past 8192 (two passes of four rows)."""
+    _w4a8_debug_check(M, K, N, seed=M + K, zero_row=M - 1 if M > 1 else None)
+
+
 def test_w4a8_debug_bit_exact_mid_size():
     M, K, N = 200, 3072, 300
     A, W, _ = _case("w4a8", M, K, N, seed=77)

@@ -97,6 +97,17 @@ static qgemm_status launched(hipError_t e) {
     return e == hipSuccess ? QGEMM_OK : QGEMM_ERR_LAUNCH;
 }
 
+// The Int4 (Block64 and Block0), Int8-Block0, W4A8 and fp16-weight GEMV kernels serve M <= the
+// current GEMV limit (and K within their register budgets); everything else
+// takes a tiled GEMM.
+static bool use_gemv(qgemm_format f, int M, int K) {
+    if (M > gemv_max_m()) return false;
+    if (f == QGEMM_INT4_B64 || f == QGEMM_INT4_B0 || f == QGEMM_INT8_B0 || f == QGEMM_W4A8)
+        return K <= kGemvMaxK;
+    if (f == QGEMM_F16) return K <= kGemvF16MaxK;
+    return false;
+}
+
 static qgemm_status run_w4a8(int M, int K, int N, const Geometry &g, const void *A,
                              const void *Bq, const void *scales, void *C, const Epilogue &epi,
                              void *ws, hipStream_t s, int32_t *D_debug) {
@@ -107,18 +118,12 @@ static qgemm_status run_w4a8(int M, int K, int N, const Geometry &g, const void 
     int32_t *S = reinterpret_cast<int32_t *>(base + w.S_off);
     hipError_t e = launch_w4a8_actquant(M, K, w.qa_stride, A, qa, sa, S, s);
     if (e != hipSuccess) return QGEMM_ERR_LAUNCH;
+    if (use_gemv(QGEMM_W4A8, M, K))
+        return launched(launch_w4a8_gemv(M, K, N, w.qa_stride, qa, sa, S, Bq, scales, C, epi,
+                                         D_debug, s));
     return launched(launch_w4a8_gemm(M, K, N, w.qa_stride, qa, sa, S, Bq, scales, C, epi, D_debug, s));
 }
 
-// The Int4-Block64, Int8-Block0 and fp16-weight GEMV kernels serve M <= the
-// current GEMV limit (and K within their register budgets); everything else
-// takes a tiled GEMM.
-static bool use_gemv(qgemm_format f, int M, int K) {
-    if (M > gemv_max_m()) return false;
-    if (f == QGEMM_INT4_B64 || f == QGEMM_INT4_B0 || f == QGEMM_INT8_B0) return K <= kGemvMaxK;
-    if (f == QGEMM_F16) return K <= kGemvF16MaxK;
-    return false;
-}
 
 // Scratch bytes one call actually touches: the W4A8 activation codes first,
 // then (when the GEMM is split along K) the partial tiles. The size reported to

@@ -106,6 +106,10 @@ hipError_t launch_w4a8_actquant(int M, int K, int Kq, const void *A, int8_t *qa,
 hipError_t launch_w4a8_gemm(int M, int K, int N, int Kq, const int8_t *qa, const float *sa,
                             const int32_t *S, const void *Wp, const void *Sp,
                             void *C, const Epilogue &epi, int32_t *D_debug, hipStream_t s);
+// M <= 8 (the GEMV limit), K <= kGemvMaxK.
+hipError_t launch_w4a8_gemv(int M, int K, int N, int Kq, const int8_t *qa, const float *sa,
+                            const int32_t *S, const void *Wp, const void *Sp, void *C,
+                            const Epilogue &epi, int32_t *D_debug, hipStream_t s);
 
 // W4A8 scratch: qa [M][qa_stride] int8 (qa_stride = roundup(K, 128), zero
 // past K), sa [M] float, S [M] int32.

@@ -1,6 +1,7 @@
-// w4a8.hip -- the W4A8 prefill path: per-row dynamic int8 quantisation of the
-// fp16 activations, then an exact s8 x s8 -> s32 product on the int8 matrix
-// cores with an fp32 rescale epilogue.
+// w4a8.hip -- the W4A8 path: per-row dynamic int8 quantisation of the fp16
+// activations, then an exact s8 x s8 -> s32 product (on the int8 matrix
+// cores for prefill, with v_dot4 in a GEMV for decode-sized M) and an fp32
+// rescale epilogue.
 //
 // MNN GemmSpeed benchmark page, section "Test cases and registration", mode 3
 // (Int4-Block0 W4A8): per-channel 4-bit weights are unpacked to int8, the
@@ -326,6 +327,134 @@ __global__ __launch_bounds__(64 * WNW) void w4a8_gemm_kernel(
             }
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// W4A8 GEMV (M up to the GEMV limit, the decode shape): one 1024-thread
+// workgroup per 32-channel tile, reading the same 1 KiB records as the GEMM.
+// Wave w takes the tile's records kc = w, w + 16, ... (whole records, all
+// requested up front, clamped into the tile). Lane (c, h) = (lane % 32,
+// lane / 32) holds 32 codes of channel c per record (k = 64 kc + 32 s +
+// 16 h + [0, 16) for s = 0, 1), unpacks them to int8 with one mask and one
+// shift-mask per word, and meets the row's qa in v_dot4 (exact int32 sums).
+// The two halves h and then the 16 waves' partial sums are added in a fixed
+// order; the epilogue is C = sa (scale D + offset S) as in the GEMM.
+// ---------------------------------------------------------------------------
+constexpr int WG_WAVES = 16;
+
+template <int MR, int NREC, bool DEBUG_D>
+__global__ __launch_bounds__(64 * WG_WAVES) void w4a8_gemv_kernel(
+    int M, int N, int Kq, int nkc, const int8_t *__restrict__ qa, const float *__restrict__ sa,
+    const int32_t *__restrict__ S, const uint8_t *__restrict__ Wp, const f2_t *__restrict__ Sp,
+    void *__restrict__ C, Epilogue epi, int32_t *__restrict__ D) {
+    __shared__ int red[WG_WAVES][MR][32];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = uniform(tid >> 6);
+    const int c = lane & 31, h = lane >> 5;
+    const int t = blockIdx.x;
+    const int m0 = blockIdx.y * MR;
+
+    // 1. this wave's records (a record past the tile's end rereads the last)
+    u4_t rec[NREC];
+#pragma unroll
+    for (int i = 0; i < NREC; ++i) {
+        const int kc = min(wave + WG_WAVES * i, nkc - 1);
+        rec[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const u4_t *>(Wp + ((size_t)t * nkc + kc) * 1024) + lane);
+    }
+
+    // 2. exact int32 dot products; qa rows past M are clamped (never stored)
+    int acc[MR];
+#pragma unroll
+    for (int r = 0; r < MR; ++r) acc[r] = 0;
+    const int8_t *qrow[MR];
+#pragma unroll
+    for (int r = 0; r < MR; ++r) qrow[r] = qa + (size_t)min(m0 + r, M - 1) * Kq + 16 * h;
+#pragma unroll
+    for (int i = 0; i < NREC; ++i) {
+        const int kc = wave + WG_WAVES * i;
+        const i4_t b0 = unpack_codes(rec[i][0], rec[i][1]);   // k = 64 kc + 16 h + [0, 16)
+        const i4_t b1 = unpack_codes(rec[i][2], rec[i][3]);   // k = 64 kc + 32 + 16 h + [0, 16)
+        i4_t a0[MR], a1[MR];
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+            const int kk = 64 * min(kc, nkc - 1);
+            a0[r] = *reinterpret_cast<const i4_t *>(qrow[r] + kk);
+            a1[r] = *reinterpret_cast<const i4_t *>(qrow[r] + kk + 32);
+        }
+        if (kc < nkc) {        // uniform; no load inside
+#pragma unroll
+            for (int r = 0; r < MR; ++r) {
+                int v = acc[r];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v = __builtin_amdgcn_sdot4(a0[r][e], b0[e], v, false);
+                    v = __builtin_amdgcn_sdot4(a1[r][e], b1[e], v, false);
+                }
+                acc[r] = v;
+            }
+        }
+    }
+
+    // 3. halves, then waves, in a fixed order; then the epilogue
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+        const int v = acc[r] + __shfl_xor(acc[r], 32);
+        if (h == 0) red[wave][r][c] = v;
+    }
+    __syncthreads();
+    if (tid >= MR * 32) return;
+    const int r = tid >> 5, n = 32 * t + (tid & 31), m = m0 + r;
+    if (n >= N || m >= M) return;
+    int d = 0;
+#pragma unroll
+    for (int w = 0; w < WG_WAVES; ++w) d += red[w][r][tid & 31];
+    if (DEBUG_D) D[(size_t)m * N + n] = d;
+    const f2_t pr = Sp[n];
+    const float out = sa[m] * fmaf(pr.y, (float)d, pr.x * (float)S[m]);
+    if (epi.plain) static_cast<float *>(C)[(size_t)m * N + n] = out;
+    else epi_put(epi, C, m, n, N, out);
+}
+
+template <int MR, int NREC>
+static void w4a8_gemv_launch(dim3 grid, hipStream_t s, int M, int N, int Kq, int nkc,
+                             const int8_t *qa, const float *sa, const int32_t *S, const void *Wp,
+                             const void *Sp, void *C, const Epilogue &epi, int32_t *D) {
+    if (D)
+        hipLaunchKernelGGL((w4a8_gemv_kernel<MR, NREC, true>), grid, dim3(64 * WG_WAVES), 0, s, M,
+                           N, Kq, nkc, qa, sa, S, static_cast<const uint8_t *>(Wp),
+                           static_cast<const f2_t *>(Sp), C, epi, D);
+    else
+        hipLaunchKernelGGL((w4a8_gemv_kernel<MR, NREC, false>), grid, dim3(64 * WG_WAVES), 0, s, M,
+                           N, Kq, nkc, qa, sa, S, static_cast<const uint8_t *>(Wp),
+                           static_cast<const f2_t *>(Sp), C, epi, D);
+}
+
+template <int MR>
+static hipError_t w4a8_gemv_mr(int M, int K, int N, int Kq, const int8_t *qa, const float *sa,
+                               const int32_t *S, const void *Wp, const void *Sp, void *C,
+                               const Epilogue &epi, int32_t *D, hipStream_t s) {
+    const int nkc = (int)round_up(K, 64) / 64;
+    const dim3 grid(div_up(N, 32), div_up(M, MR));
+    const int nrec = div_up(nkc, WG_WAVES);   // K <= 16384: at most 16
+    if (nrec <= 1) w4a8_gemv_launch<MR, 1>(grid, s, M, N, Kq, nkc, qa, sa, S, Wp, Sp, C, epi, D);
+    else if (nrec <= 2) w4a8_gemv_launch<MR, 2>(grid, s, M, N, Kq, nkc, qa, sa, S, Wp, Sp, C, epi, D);
+    else if (nrec <= 4) w4a8_gemv_launch<MR, 4>(grid, s, M, N, Kq, nkc, qa, sa, S, Wp, Sp, C, epi, D);
+    else if (nrec <= 8 || MR == 8) w4a8_gemv_launch<MR, 8>(grid, s, M, N, Kq, nkc, qa, sa, S, Wp, Sp, C, epi, D);
+    else w4a8_gemv_launch<(MR < 8 ? MR : 4), 16>(grid, s, M, N, Kq, nkc, qa, sa, S, Wp, Sp, C, epi, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_w4a8_gemv(int M, int K, int N, int Kq, const int8_t *qa, const float *sa,
+                            const int32_t *S, const void *Wp, const void *Sp, void *C,
+                            const Epilogue &epi, int32_t *D_debug, hipStream_t s) {
+    if (M <= 1) return w4a8_gemv_mr<1>(M, K, N, Kq, qa, sa, S, Wp, Sp, C, epi, D_debug, s);
+    if (M <= 2) return w4a8_gemv_mr<2>(M, K, N, Kq, qa, sa, S, Wp, Sp, C, epi, D_debug, s);
+    // eight rows keep at most 8 records per lane in registers (K <= 8192);
+    // longer rows take two passes of four
+    if (M <= 4 || K > 8192) return w4a8_gemv_mr<4>(M, K, N, Kq, qa, sa, S, Wp, Sp, C, epi, D_debug, s);
+    return w4a8_gemv_mr<8>(M, K, N, Kq, qa, sa, S, Wp, Sp, C, epi, D_debug, s);
 }
 
 hipError_t launch_w4a8_gemm(int M, int K, int N, int Kq, const int8_t *qa, const float *sa,
