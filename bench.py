@@ -304,33 +304,39 @@ def time_calls(torch, run, copies: int, steps: int) -> float:
     return e0.elapsed_time(e1) / (reps * copies)
 
 
+def shape_rows(torch, shapes, steps, copies_arg, tag):
+    """One JSON line per (fmt, M, K, N): time per call, rate and the fraction of
+    the bound that applies (HBM for M <= 8, the matrix cores otherwise)."""
+    for fmt, M, K, N in shapes:
+        per = algorithmic_bytes(M, K, N, fmt)
+        copies = copies_arg or min(64, max(2, -(-2 * MALL_BYTES // per) + 1))
+        w = ShapeWorkload(fmt, M, K, N, copies, seed=K + N + M)
+        ms = time_calls(torch, w.run, copies, steps)
+        fl, by = flops(M, K, N), algorithmic_bytes(M, K, N, fmt)
+        if fmt == "w4a8":
+            peak, unit = INT8_PEAK_TOPS, "TOP/s"
+        elif fmt == "f32":
+            peak, unit = 157.3, "TFLOP/s"
+        else:
+            peak, unit = FP16_PEAK_TFLOPS, "TFLOP/s"
+        rate = fl / ms / 1e9
+        print(json.dumps({tag: fmt, "M": M, "K": K, "N": N, "ms_per_call": ms,
+                          "rate": rate, "unit": unit, "frac_of_mfma_peak": rate / peak,
+                          "gb_s": by / ms / 1e6, "frac_of_hbm_peak": by / ms / 1e6 / HBM_PEAK_GBS}),
+              flush=True)
+        del w
+        torch.cuda.empty_cache()
+
+
 def page_grid(args, torch) -> int:
     """The benchmark page's default (K, N) x M sizes, per format: one JSON line
     per shape with the time per call, the rate and its fraction of the bound
     that applies (HBM for the decode-shaped M <= 8 GEMV, the matrix cores
     otherwise)."""
     from weight_quantized_gemm_amd import synth
-    for fmt in args.page_grid.split(","):
-        for K, N in synth.PAGE_KN:
-            for M in synth.PAGE_M:
-                per = algorithmic_bytes(M, K, N, fmt)
-                copies = args.copies or min(64, max(2, -(-2 * MALL_BYTES // per) + 1))
-                w = ShapeWorkload(fmt, M, K, N, copies, seed=K + N + M)
-                ms = time_calls(torch, w.run, copies, args.steps)
-                fl, by = flops(M, K, N), algorithmic_bytes(M, K, N, fmt)
-                if fmt == "w4a8":
-                    peak, unit = INT8_PEAK_TOPS, "TOP/s"
-                elif fmt == "f32":
-                    peak, unit = 157.3, "TFLOP/s"
-                else:
-                    peak, unit = FP16_PEAK_TFLOPS, "TFLOP/s"
-                rate = fl / ms / 1e9
-                print(json.dumps({"page_grid": fmt, "M": M, "K": K, "N": N, "ms_per_call": ms,
-                                  "rate": rate, "unit": unit, "frac_of_mfma_peak": rate / peak,
-                                  "gb_s": by / ms / 1e6, "frac_of_hbm_peak": by / ms / 1e6 / HBM_PEAK_GBS}),
-                      flush=True)
-                del w
-                torch.cuda.empty_cache()
+    shapes = [(fmt, M, K, N) for fmt in args.page_grid.split(",")
+              for K, N in synth.PAGE_KN for M in synth.PAGE_M]
+    shape_rows(torch, shapes, args.steps, args.copies, "page_grid")
     return 0
 
 
@@ -417,6 +423,8 @@ def main() -> int:
     ap.add_argument("--page-grid", default="", metavar="FORMATS",
                     help="diagnostic: time the benchmark page's default (K, N) x M grid for the "
                          "comma-separated formats (f32,int8b0,int4b64,w4a8), one JSON line each")
+    ap.add_argument("--shape", action="append", default=[], metavar="FMT,M,K,N",
+                    help="diagnostic: time one shape of one format (repeatable), one JSON line each")
     ap.add_argument("--vendor-reference", nargs="?", const="prefill", default="",
                     choices=["prefill", "page-grid"],
                     help="context only: time torch's own fp16 GEMM and int8 GEMM (the vendor "
@@ -450,6 +458,13 @@ def main() -> int:
         return single_workload(args, torch)
     if args.vendor_reference:
         return vendor_reference(args, torch)
+    if args.shape:
+        shapes = []
+        for spec in args.shape:
+            f, m, k, n = spec.split(",")
+            shapes.append((f, int(m), int(k), int(n)))
+        shape_rows(torch, shapes, args.steps, args.copies, "shape")
+        return 0
     if args.page_grid:
         return page_grid(args, torch)
 
