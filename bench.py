@@ -44,7 +44,8 @@ def algorithmic_bytes(M: int, K: int, N: int, fmt: str = "int4b64", epi: dict | 
     epilogue, plus its bias and residual). Int4 formats hold K/2 bytes of
     codes per channel, Int8-Block0 K bytes, fp32 B 4*K*N bytes, fp16 B 2*K*N
     bytes; Int4-Block64
-    has K/64 pairs per channel, the per-channel formats one."""
+    has K/64 pairs per channel, the per-channel formats (Int8-Block0, W4A8,
+    Int4-Block0) one."""
     a_bytes = M * K * (4 if fmt == "f32" else 2)
     if fmt == "f32":
         w_bytes, p_bytes = 4 * K * N, 0
@@ -54,7 +55,7 @@ def algorithmic_bytes(M: int, K: int, N: int, fmt: str = "int4b64", epi: dict | 
         w_bytes, p_bytes = K * N, 8 * N
     elif fmt == "int4b64":
         w_bytes, p_bytes = N * K // 2, N * (K // 64) * 8
-    else:  # w4a8
+    else:  # w4a8, int4b0
         w_bytes, p_bytes = N * K // 2, 8 * N
     c_elem = 2 if epi and epi["out"] == "f16" else 4
     e_bytes = 0
