@@ -329,6 +329,34 @@ def shape_rows(torch, shapes, steps, copies_arg, tag):
         torch.cuda.empty_cache()
 
 
+def quantizer_rows(torch, specs, steps, copies_arg) -> None:
+    """The device quantise-and-pack (float W [N][K] in HBM -> packed codes and
+    pairs): one JSON line per (format, K, N) with the time per call and its
+    fraction of HBM bandwidth over the algorithmic bytes (the fp32 weights
+    read once, the packed buffers written once)."""
+    from weight_quantized_gemm_amd import qgemm as Q
+    from weight_quantized_gemm_amd import synth
+    for fmt, K, N in specs:
+        wb, sb = Q.qgemm_packed_size(K, N, fmt)
+        per = 4 * N * K + wb + sb
+        copies = copies_arg or min(16, max(2, -(-2 * MALL_BYTES // per) + 1))
+        W0 = torch.from_numpy(synth.normal_weights(np.random.default_rng(K + N), N, K)).cuda()
+        Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
+        Bs = [torch.empty(wb, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+        Ss = [torch.empty(sb, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+
+        def run(i, Ws=Ws, Bs=Bs, Ss=Ss, fmt=fmt):
+            c = i % len(Ws)
+            Q.qgemm_quantize_pack_device(Ws[c], fmt, Bs[c], Ss[c])
+
+        ms = time_calls(torch, run, copies, steps)
+        print(json.dumps({"quantize_pack": fmt, "K": K, "N": N, "ms_per_call": ms,
+                          "algorithmic_bytes": per, "gb_s": per / ms / 1e6,
+                          "frac_of_hbm_peak": per / ms / 1e6 / HBM_PEAK_GBS}), flush=True)
+        del Ws, Bs, Ss
+        torch.cuda.empty_cache()
+
+
 def page_grid(args, torch) -> int:
     """The benchmark page's default (K, N) x M sizes, per format: one JSON line
     per shape with the time per call, the rate and its fraction of the bound
@@ -426,6 +454,8 @@ def main() -> int:
                          "comma-separated formats (f32,int8b0,int4b64,w4a8), one JSON line each")
     ap.add_argument("--shape", action="append", default=[], metavar="FMT,M,K,N",
                     help="diagnostic: time one shape of one format (repeatable), one JSON line each")
+    ap.add_argument("--quantizer", action="append", default=[], metavar="FMT,K,N",
+                    help="diagnostic: time the device quantise-and-pack of one weight shape (repeatable)")
     ap.add_argument("--vendor-reference", nargs="?", const="prefill", default="",
                     choices=["prefill", "page-grid"],
                     help="context only: time torch's own fp16 GEMM and int8 GEMM (the vendor "
@@ -459,6 +489,13 @@ def main() -> int:
         return single_workload(args, torch)
     if args.vendor_reference:
         return vendor_reference(args, torch)
+    if args.quantizer:
+        specs = []
+        for spec in args.quantizer:
+            f, k, n = spec.split(",")
+            specs.append((f, int(k), int(n)))
+        quantizer_rows(torch, specs, args.steps, args.copies)
+        return 0
     if args.shape:
         shapes = []
         for spec in args.shape:

@@ -128,6 +128,36 @@ qgemm_status qgemm_quantize_weights(int K, int N, qgemm_format f,
                                     float *pairs, size_t pair_floats);
 
 /*
+ * Device-side quantiser: the same export step on the GPU (MNN GemmSpeed page,
+ * section "Why Conv1x1 is used to measure GEMM"), for weights that already
+ * live in device memory. Every step is the host quantiser's, in the same IEEE
+ * double operations, so codes and pairs equal qgemm_quantize_weights' bit for
+ * bit; of equal extremes (+0 and -0) the first in k order is kept, as a
+ * sequential scan keeps it.
+ *   W      device float [N][K], read-only.
+ *   q      device, canonical codes (qgemm_canonical_size's q_bytes).
+ *   pairs  device, canonical pairs [N][nblk][2] (pair_floats floats).
+ * Enqueued on `stream`; returns without waiting. The device cannot report a
+ * NaN or infinite weight before it runs, so instead of ERR_VALUE the block
+ * (the channel, for the per-channel formats) that holds one gets NaN offset
+ * and scale and zero codes.
+ * Errors: ERR_FORMAT (F32, F16, unknown), ERR_SHAPE, ERR_NULL, ERR_ALIGN (a
+ * pointer not 16-byte aligned), ERR_DEVICE, ERR_LAUNCH. N == 0 is a no-op.
+ */
+qgemm_status qgemm_quantize_weights_device(int K, int N, qgemm_format f, const float *W,
+                                           void *q, float *pairs, void *stream);
+
+/*
+ * Device-side quantise-and-pack: as qgemm_quantize_weights_device, but the
+ * codes and pairs go straight into the packed layouts qgemm_run reads (Bq
+ * and scales of qgemm_packed_size's w_bytes / s_bytes, every byte written,
+ * padding as zeros), byte-identical to qgemm_pack_weights of the canonical
+ * result. Same arguments, errors and non-finite handling.
+ */
+qgemm_status qgemm_quantize_pack_device(int K, int N, qgemm_format f, const float *W,
+                                        void *Bq, void *scales, void *stream);
+
+/*
  * Sizes in bytes of the packed weight buffer (w_bytes) and the packed pair
  * buffer (s_bytes, 0 for F32) of a K x N weight.
  * Errors: ERR_NULL, ERR_FORMAT, ERR_SHAPE.

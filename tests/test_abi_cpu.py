@@ -264,3 +264,28 @@ def test_w4a8_packed_word_order_golden():
                         assert byte >> 4 == codes[n, k0 + 4 + i]
     # channels 40 .. 63 of the second record are padding
     assert not np.any(wp[1024:2048].reshape(2, 32, 16)[:, 8:, :])
+
+
+def test_device_quantizer_validation_before_device(lib):
+    """Every rejection of the device quantisers happens before the GPU is touched."""
+    OK, NULL, SHAPE, FMT, ALIGN, DEV = 0, 1, 2, 3, 4, 6
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    for fn in (lib.qgemm_quantize_weights_device, lib.qgemm_quantize_pack_device):
+        q = lambda K, N, f, W=256, a=256, b=256: fn(K, N, f, v(W), v(a), v(b), None)
+        assert q(64, 4, 0) == FMT                     # float weights are not quantised
+        assert q(64, 4, 4) == FMT
+        assert q(64, 4, 9) == FMT
+        assert q(63, 4, 1) == SHAPE                   # Int4-Block64: K % 64 == 0
+        assert q(96, 4, 5) == SHAPE                   # Int4-Block0 packs as Block64
+        assert q(65, 4, 3) == SHAPE                   # W4A8: even K
+        assert q(0, 4, 2) == SHAPE
+        assert q(64, 0, 1, None, None, None) == OK    # nothing to do
+        assert q(64, 4, 1, W=None) == NULL
+        assert q(64, 4, 2, a=None) == NULL
+        assert q(64, 4, 3, b=None) == NULL
+        assert q(64, 4, 1, W=260) == ALIGN
+        assert q(64, 4, 2, a=264) == ALIGN
+        assert q(64, 4, 3, b=200) == ALIGN
+        import torch
+        if not torch.cuda.is_available():
+            assert q(64, 4, 1) == DEV

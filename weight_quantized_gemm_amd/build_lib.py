@@ -21,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "gemv.hip", "gemm_int4.hip", "gemm_int8.hip", "w4a8.hip", "gemm_f32.hip", "splitk.hip",
-           "host_pack.cpp"]
+           "quantize.hip", "host_pack.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           f"-I{os.path.join(ROOT, 'include')}"]

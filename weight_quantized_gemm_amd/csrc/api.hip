@@ -262,4 +262,39 @@ qgemm_status qgemm_w4a8_debug(int M, int K, int N, const void *A, const void *Bq
     return QGEMM_OK;
 }
 
+// Checks shared by the device quantisers; *empty is set for N == 0.
+static qgemm_status check_quantize(int K, int N, qgemm_format f, const float *W, const void *q,
+                                   const void *pairs, Geometry *g, bool *empty) {
+    if (f != QGEMM_INT4_B64 && f != QGEMM_INT8_B0 && f != QGEMM_W4A8 && f != QGEMM_INT4_B0)
+        return QGEMM_ERR_FORMAT;                   // float weights are not quantised
+    qgemm_status st = geometry(K, N, f, g);
+    if (st != QGEMM_OK) return st;
+    *empty = N == 0;
+    if (*empty) return QGEMM_OK;
+    if (!W || !q || !pairs) return QGEMM_ERR_NULL;
+    if (!aligned16(W) || !aligned16(q) || !aligned16(pairs)) return QGEMM_ERR_ALIGN;
+    return check_device();
+}
+
+qgemm_status qgemm_quantize_weights_device(int K, int N, qgemm_format f, const float *W,
+                                           void *q, float *pairs, void *stream) {
+    Geometry g;
+    bool empty = false;
+    qgemm_status st = check_quantize(K, N, f, W, q, pairs, &g, &empty);
+    if (st != QGEMM_OK || empty) return st;
+    (void)hipGetLastError();
+    return launched(launch_quantize(K, N, f, false, W, q, pairs, g, static_cast<hipStream_t>(stream)));
+}
+
+qgemm_status qgemm_quantize_pack_device(int K, int N, qgemm_format f, const float *W, void *Bq,
+                                        void *scales, void *stream) {
+    Geometry g;
+    bool empty = false;
+    qgemm_status st = check_quantize(K, N, f, W, Bq, scales, &g, &empty);
+    if (st != QGEMM_OK || empty) return st;
+    (void)hipGetLastError();
+    return launched(launch_quantize(K, N, f, true, W, Bq, static_cast<float *>(scales), g,
+                                    static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -111,6 +111,11 @@ hipError_t launch_w4a8_gemv(int M, int K, int N, int Kq, const int8_t *qa, const
                             const int32_t *S, const void *Wp, const void *Sp, void *C,
                             const Epilogue &epi, int32_t *D_debug, hipStream_t s);
 
+// Device quantiser (float W [N][K] -> codes and pairs): canonical layout, or
+// with `packed` the format's packed layout including its zero padding.
+hipError_t launch_quantize(int K, int N, qgemm_format f, bool packed, const float *W, void *q,
+                           float *pairs, const Geometry &g, hipStream_t s);
+
 // W4A8 scratch: qa [M][qa_stride] int8 (qa_stride = roundup(K, 128), zero
 // past K), sa [M] float, S [M] int32.
 struct W4A8Workspace {

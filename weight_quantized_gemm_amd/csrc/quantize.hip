@@ -1,0 +1,260 @@
+// quantize.hip -- the weight export step on the GPU: float weights [N][K] ->
+// 4- or 8-bit codes and [offset, scale] pairs, written either in the
+// canonical layout or straight into the packed layouts the GEMM kernels read.
+//
+// MNN GemmSpeed page, section "Why Conv1x1 is used to measure GEMM": the
+// weights are quantised offline (the converter's export), asymmetrically,
+// one [offset, scale] pair per (channel, block of K). Per block the offset is
+// the minimum, the scale (maximum - minimum) / (2^bits - 1) and a weight's
+// code rint((w - offset) / scale) clamped to [0, 2^bits - 1]. The kernel
+// takes every step in the same IEEE double operations as the host quantiser
+// (the pair from double, rounded to float; the quotient from the stored
+// float pair, in double, rounded half to even), so its codes and pairs equal
+// the host's bit for bit.
+//
+// One wave per channel. Lane l of a 64-element chunk holds k = 64 j + l; the
+// chunks are loaded eight at a time, every load unconditional from a clamped
+// index, and the codes leave as 32-bit words assembled across lanes.
+#include "kernels_common.h"
+
+#pragma clang fp contract(off)
+
+namespace qg {
+namespace {
+
+constexpr int kQWaves = 4;     // channels (waves) per workgroup
+constexpr int kQUnroll = 8;    // 64-element chunks loaded per batch
+
+struct QParams {
+    const float *W;
+    int K, N;
+    int rows;        // channels the grid covers: N (canonical) or the padded Np (packed)
+    int nkc;         // 64-element chunks per row: ceil(K / 64)
+    int kp;          // packed Int8-Block0 row length
+    uint8_t *q;      // codes
+    float *pairs;    // pairs
+    int tail_off, tail_len;   // floats of the packed pair buffer past the last pair (zeroed)
+};
+
+__device__ inline float wave_min(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fminf(v, __shfl_xor(v, m));
+    return v;
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+    return v;
+}
+
+__device__ inline uint32_t group_or(uint32_t x, int lanes) {
+    // OR over aligned groups of `lanes` (4 or 8) lanes
+    x |= __shfl_xor(x, 1);
+    x |= __shfl_xor(x, 2);
+    if (lanes == 8) x |= __shfl_xor(x, 4);
+    return x;
+}
+
+// The pair of one block from its reduced minimum and maximum.
+__device__ inline float2 block_pair(float lo, float hi, int qmax, bool bad, bool live) {
+    float2 p;
+    p.x = lo;
+    p.y = (float)(((double)hi - (double)lo) / (double)qmax);
+    if (bad) p.x = p.y = __builtin_nanf("");   // a non-finite weight poisons its block
+    if (!live) p.x = p.y = 0.0f;               // padding channels of a packed buffer
+    return p;
+}
+
+// Code of one weight from its block's stored float pair.
+__device__ inline int code_of(float w, float2 p, int qmax) {
+    if (p.y == 0.0f) return 0;
+    double r = rint(((double)w - (double)p.x) / (double)p.y);
+    r = r < 0.0 ? 0.0 : (r > (double)qmax ? (double)qmax : r);
+    return (int)r;
+}
+
+// Stores the codes of chunk kc (k = 64 kc + lane) of channel n. Every lane
+// calls it (the word assembly crosses lanes); codes past K arrive as 0.
+template <int OUT, int BITS>
+__device__ inline void store_codes(const QParams &p, int n, int kc, int lane, int code) {
+    const int k = kc * 64 + lane;
+    if (OUT == QGEMM_F32) {           // canonical layout (the format's own slot is unused here)
+        if (BITS == 8) {
+            if (k < p.K) p.q[(size_t)n * p.K + k] = (uint8_t)code;
+        } else if ((p.K & 7) == 0) {
+            // rows start on 4-byte boundaries: one word per 8 codes
+            const uint32_t x = group_or((uint32_t)code << (4 * (lane & 7)), 8);
+            if ((lane & 7) == 0 && k < p.K)
+                *reinterpret_cast<uint32_t *>(p.q + (size_t)n * (p.K / 2) + k / 2) = x;
+        } else {
+            uint32_t x = (uint32_t)code << (4 * (lane & 1));
+            x |= __shfl_xor(x, 1);
+            if ((lane & 1) == 0 && k < p.K) p.q[(size_t)n * (p.K / 2) + k / 2] = (uint8_t)x;
+        }
+    } else if (OUT == QGEMM_INT4_B64) {
+        // record (n / 32, kc); piece 32 h + (n % 32) holds canonical bytes
+        // [16 h, 16 h + 16) of the block, word w of it codes 32 h + 8 w + [0, 8)
+        const uint32_t x = group_or((uint32_t)code << (4 * (lane & 7)), 8);
+        const int G = lane >> 3, h = G >> 2, w = G & 3;
+        const size_t rec = (size_t)(n >> 5) * p.nkc + kc;
+        if ((lane & 7) == 0)
+            *reinterpret_cast<uint32_t *>(p.q + rec * 1024 + (size_t)(32 * h + (n & 31)) * 16 + 4 * w) = x;
+    } else if (OUT == QGEMM_INT8_B0) {
+        const uint32_t x = group_or((uint32_t)code << (8 * (lane & 3)), 4);
+        if ((lane & 3) == 0)
+            *reinterpret_cast<uint32_t *>(p.q + (size_t)n * p.kp + k) = x;
+    } else {                          // W4A8
+        // word of k0 = 64 kc + 32 s + 16 h + 8 w: byte i = q[k0 + i] | q[k0 + 4 + i] << 4
+        const uint32_t x = group_or((uint32_t)code << (8 * (lane & 3) + 4 * ((lane >> 2) & 1)), 8);
+        const int G = lane >> 3, s = G >> 2, h = (G >> 1) & 1, w = G & 1;
+        const size_t rec = (size_t)(n >> 5) * p.nkc + kc;
+        if ((lane & 7) == 0)
+            *reinterpret_cast<uint32_t *>(p.q + rec * 1024 + (size_t)(32 * h + (n & 31)) * 16 + 8 * s + 4 * w) = x;
+    }
+}
+
+// OUT: QGEMM_F32 stands for the canonical layout, else the packed layout of
+// that format (Int4-Block0 packs as QGEMM_INT4_B64 with REPEAT). B64: one
+// pair per 64-block, else one pair per channel.
+template <int OUT, int BITS, bool B64, bool REPEAT>
+__global__ __launch_bounds__(64 * kQWaves) void quantize_kernel(QParams p) {
+    const int lane = threadIdx.x & 63;
+    const int n = blockIdx.x * kQWaves + (threadIdx.x >> 6);
+    if (blockIdx.x == 0 && threadIdx.x < 64)
+        for (int i = lane; i < p.tail_len; i += 64) p.pairs[p.tail_off + i] = 0.0f;
+    if (n >= p.rows) return;                       // whole waves only
+    const bool live = n < p.N;
+    const float *row = p.W + (size_t)(live ? n : p.N - 1) * p.K;
+    constexpr int qmax = (1 << BITS) - 1;
+
+    if (B64) {
+        // K % 64 == 0: chunk kc is block kc
+        for (int j0 = 0; j0 < p.nkc; j0 += kQUnroll) {
+            float v[kQUnroll];
+#pragma unroll
+            for (int u = 0; u < kQUnroll; ++u) v[u] = row[min((j0 + u) * 64 + lane, p.K - 1)];
+#pragma unroll
+            for (int u = 0; u < kQUnroll; ++u) {
+                const int kc = j0 + u;
+                if (kc >= p.nkc) break;            // uniform
+                const bool bad = __ballot(!__builtin_isfinite(v[u])) != 0;
+                float lo = wave_min(v[u]), hi = wave_max(v[u]);
+                if (lo == 0.0f || hi == 0.0f) {
+                    // equal extremes differ only in the sign of zero: the first zero
+                    // in k order is the one a sequential scan keeps
+                    const unsigned long long z = __ballot(v[u] == 0.0f);
+                    const float z0 = __shfl(v[u], __builtin_ctzll(z));
+                    lo = lo == 0.0f ? z0 : lo;
+                    hi = hi == 0.0f ? z0 : hi;
+                }
+                const float2 pr = block_pair(lo, hi, qmax, bad, live);
+                const int code = (live && !bad) ? code_of(v[u], pr, qmax) : 0;
+                store_codes<OUT, BITS>(p, n, kc, lane, code);
+                if (lane == 0) {
+                    const size_t pi = OUT == QGEMM_F32 ? (size_t)n * p.nkc + kc
+                                                       : ((size_t)(n >> 5) * p.nkc + kc) * 32 + (n & 31);
+                    reinterpret_cast<float2 *>(p.pairs)[pi] = pr;
+                }
+            }
+        }
+        return;
+    }
+
+    // one pair per channel: the row's minimum and maximum, then its codes
+    float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+    bool bad_lane = false;
+    for (int j0 = 0; j0 < p.nkc; j0 += kQUnroll) {
+        float v[kQUnroll];
+#pragma unroll
+        for (int u = 0; u < kQUnroll; ++u) v[u] = row[min((j0 + u) * 64 + lane, p.K - 1)];
+#pragma unroll
+        for (int u = 0; u < kQUnroll; ++u) {
+            const bool valid = live && (j0 + u) * 64 + lane < p.K;
+            lo = valid ? fminf(lo, v[u]) : lo;
+            hi = valid ? fmaxf(hi, v[u]) : hi;
+            bad_lane |= valid && !__builtin_isfinite(v[u]);
+        }
+    }
+    const bool bad = __ballot(bad_lane) != 0;
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if ((lo == 0.0f || hi == 0.0f) && !bad) {
+        // an extreme of 0: the first zero in k order carries the sign a
+        // sequential scan keeps (rare, so found by a second scan)
+        for (int kc = 0; kc < p.nkc; ++kc) {
+            const int k = kc * 64 + lane;
+            const float v = row[min(k, p.K - 1)];
+            const unsigned long long z = __ballot(k < p.K && v == 0.0f);
+            if (z) {
+                const float z0 = __shfl(v, __builtin_ctzll(z));
+                lo = lo == 0.0f ? z0 : lo;
+                hi = hi == 0.0f ? z0 : hi;
+                break;
+            }
+        }
+    }
+    const float2 pr = block_pair(lo, hi, qmax, bad, live);
+    for (int j0 = 0; j0 < p.nkc; j0 += kQUnroll) {
+        float v[kQUnroll];
+#pragma unroll
+        for (int u = 0; u < kQUnroll; ++u) v[u] = row[min((j0 + u) * 64 + lane, p.K - 1)];
+#pragma unroll
+        for (int u = 0; u < kQUnroll; ++u) {
+            const int kc = j0 + u;
+            if (kc >= p.nkc) break;                // uniform
+            const bool valid = live && !bad && kc * 64 + lane < p.K;
+            store_codes<OUT, BITS>(p, n, kc, lane, valid ? code_of(v[u], pr, qmax) : 0);
+        }
+    }
+    float2 *pp = reinterpret_cast<float2 *>(p.pairs);
+    if (REPEAT) {
+        // packed Int4-Block0: the channel's pair in every 64-block record
+        for (int b = lane; b < p.nkc; b += 64) pp[((size_t)(n >> 5) * p.nkc + b) * 32 + (n & 31)] = pr;
+    } else if (lane == 0) {
+        pp[n] = pr;
+    }
+}
+
+template <int OUT, int BITS, bool B64, bool REPEAT>
+hipError_t launch(const QParams &p, hipStream_t s) {
+    const int grid = div_up(p.rows, kQWaves);
+    hipLaunchKernelGGL((quantize_kernel<OUT, BITS, B64, REPEAT>), dim3(grid), dim3(64 * kQWaves), 0,
+                       s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(int K, int N, qgemm_format f, bool packed, const float *W, void *q,
+                           float *pairs, const Geometry &g, hipStream_t s) {
+    QParams p{};
+    p.W = W;
+    p.K = K;
+    p.N = N;
+    p.rows = packed ? g.Np : N;
+    p.nkc = div_up(K, 64);
+    p.kp = g.Kp;
+    p.q = static_cast<uint8_t *>(q);
+    p.pairs = pairs;
+    if (packed && f == QGEMM_INT8_B0) {
+        // the packed pair buffer is padded to its alignment past the Np pairs
+        p.tail_off = g.Np * 2;
+        p.tail_len = (int)(g.s_bytes / sizeof(float)) - g.Np * 2;
+    }
+    if (!packed) {
+        switch (f) {
+        case QGEMM_INT4_B64: return launch<QGEMM_F32, 4, true, false>(p, s);
+        case QGEMM_INT8_B0:  return launch<QGEMM_F32, 8, false, false>(p, s);
+        default:             return launch<QGEMM_F32, 4, false, false>(p, s);   // W4A8, Int4-Block0
+        }
+    }
+    switch (f) {
+    case QGEMM_INT4_B64: return launch<QGEMM_INT4_B64, 4, true, false>(p, s);
+    case QGEMM_INT4_B0:  return launch<QGEMM_INT4_B64, 4, false, true>(p, s);
+    case QGEMM_INT8_B0:  return launch<QGEMM_INT8_B0, 8, false, false>(p, s);
+    default:             return launch<QGEMM_W4A8, 4, false, false>(p, s);
+    }
+}
+
+}  // namespace qg

@@ -35,7 +35,8 @@ STATUS = {0: "QGEMM_OK", 1: "QGEMM_ERR_NULL", 2: "QGEMM_ERR_SHAPE", 3: "QGEMM_ER
 EXPORTS = ["qgemm_status_string", "qgemm_abi_version", "qgemm_canonical_size",
            "qgemm_quantize_weights", "qgemm_packed_size", "qgemm_pack_weights",
            "qgemm_unpack_weights", "qgemm_workspace_size", "qgemm_run", "qgemm_run_ws",
-           "qgemm_run_ex", "qgemm_w4a8_debug", "qgemm_set_gemv_max_m"]
+           "qgemm_run_ex", "qgemm_w4a8_debug", "qgemm_set_gemv_max_m",
+           "qgemm_quantize_weights_device", "qgemm_quantize_pack_device"]
 
 
 class QGemmError(RuntimeError):
@@ -73,6 +74,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "qgemm_run_ex": ([I, I, I, I, P, P, P, P, ctypes.POINTER(Epilogue), P, Z, P], I),
         "qgemm_w4a8_debug": ([I, I, I, P, P, P, P, P, P, P, P, P, Z, P], I),
         "qgemm_set_gemv_max_m": ([I], I),
+        "qgemm_quantize_weights_device": ([I, I, I, P, P, P, P], I),
+        "qgemm_quantize_pack_device": ([I, I, I, P, P, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -228,6 +231,38 @@ def qgemm_w4a8_debug(M: int, K: int, N: int, A, Bq, scales, C, qa, sa, S, D, wor
                                    _dev_ptr(C), _dev_ptr(qa), _dev_ptr(sa), _dev_ptr(S),
                                    _dev_ptr(D), _dev_ptr(workspace), ws_bytes, _stream(stream)),
            "qgemm_w4a8_debug")
+
+
+def qgemm_quantize_weights_device(W, fmt, q=None, pairs=None, stream=None):
+    """Device float W [N][K] -> (canonical codes uint8, pairs float32 [N][nblk][2]),
+    both device tensors (allocated here unless given)."""
+    f = _fmt(fmt)
+    N, K = W.shape
+    qb, pf = qgemm_canonical_size(K, N, f)
+    if q is None:
+        q = torch.empty(max(qb, 1), dtype=torch.uint8, device=W.device)
+    if pairs is None:
+        pairs = torch.empty(max(pf, 1), dtype=torch.float32, device=W.device)
+    _check(load().qgemm_quantize_weights_device(K, N, f, _dev_ptr(W), _dev_ptr(q), _dev_ptr(pairs),
+                                                _stream(stream)), "qgemm_quantize_weights_device")
+    qshape = (N, K) if f == QGEMM_INT8_B0 else (N, K // 2)
+    nblk = K // 64 if f == QGEMM_INT4_B64 else 1
+    return q[:qb].view(qshape), pairs[:pf].view(N, nblk, 2)
+
+
+def qgemm_quantize_pack_device(W, fmt, Bq=None, scales=None, stream=None):
+    """Device float W [N][K] -> (packed weights uint8, packed pairs uint8), both
+    device tensors in the layout qgemm_run reads."""
+    f = _fmt(fmt)
+    N, K = W.shape
+    wb, sb = qgemm_packed_size(K, N, f)
+    if Bq is None:
+        Bq = torch.empty(wb, dtype=torch.uint8, device=W.device)
+    if scales is None:
+        scales = torch.empty(sb, dtype=torch.uint8, device=W.device)
+    _check(load().qgemm_quantize_pack_device(K, N, f, _dev_ptr(W), _dev_ptr(Bq), _dev_ptr(scales),
+                                             _stream(stream)), "qgemm_quantize_pack_device")
+    return Bq, scales
 
 
 def qgemm_set_gemv_max_m(max_m: int) -> int:
