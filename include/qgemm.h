@@ -22,6 +22,11 @@
  *   QGEMM_INT4_B0   Int4-Block0 without A8: W4A8's per-channel 4-bit weights
  *                   with fp16 activations (no activation quantisation);
  *                   K % 64 == 0.
+ *   QGEMM_INT4_BLOCK(b)  Int4 with one pair per b K-elements (the page's
+ *                   blockSize parameter, section "Why Conv1x1 is used to
+ *                   measure GEMM"), b a multiple of 64 that divides K;
+ *                   fp16 activations. QGEMM_INT4_BLOCK(64) behaves as
+ *                   QGEMM_INT4_B64 and QGEMM_INT4_BLOCK(K) as QGEMM_INT4_B0.
  *
  * Format ids 0-3 equal the page's mode numbers. For every format but F32, A
  * is fp16; C is fp32 (or fp16 through qgemm_run_ex).
@@ -36,6 +41,7 @@
  *               blockNum groups of [offset, scale]).
  *   - W4A8, INT4_B0: q as INT4_B64 with one block over all of K; pairs
  *               float [N][1][2].
+ *   - INT4_BLOCK(b): q as INT4_B64; pairs float [N][K/b][2].
  * Codes are unsigned: q in [0, 2^bits - 1].
  *
  * Packed (device) layouts are opaque and owned by this library: they are
@@ -77,8 +83,12 @@ typedef enum qgemm_format {
     QGEMM_INT8_B0 = 2,
     QGEMM_W4A8 = 3,
     QGEMM_F16 = 4,
-    QGEMM_INT4_B0 = 5
+    QGEMM_INT4_B0 = 5,
+    QGEMM_INT4_BLOCK_BASE = 0x10000   /* + b: see QGEMM_INT4_BLOCK */
 } qgemm_format;
+
+/* Format id of Int4 weights with one pair per b K-elements. */
+#define QGEMM_INT4_BLOCK(b) ((qgemm_format)(QGEMM_INT4_BLOCK_BASE + (b)))
 
 typedef enum qgemm_status {
     QGEMM_OK = 0,

@@ -164,9 +164,11 @@ def test_sizes():
         Q.qgemm_packed_size(100, 8, "int4b64")
 
 
-@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("fmt", FMTS + ["int4b128", "int4b192"])
 @pytest.mark.parametrize("shape", [(1, 64), (5, 128), (70, 192), (33, 1024)])
 def test_quantizer_matches_oracle_bit_exact(fmt, shape):
+    if fmt.startswith("int4b1") and shape[1] % int(fmt[5:]):
+        pytest.skip("the block does not divide K")
     N, K = shape
     rng = np.random.default_rng(N * 1000 + K)
     W = synth.normal_weights(rng, N, K)
@@ -189,10 +191,12 @@ def test_quantizer_rejects_nonfinite():
         Q.qgemm_quantize_weights(np.zeros((4, 64), np.float32), "f32")
 
 
-@pytest.mark.parametrize("fmt", FMTS + ["f32"])
+@pytest.mark.parametrize("fmt", FMTS + ["f32", "int4b128", "int4b320"])
 @pytest.mark.parametrize("shape", [(1, 64), (3, 128), (70, 192), (37, 4160)])
 def test_pack_unpack_round_trip(fmt, shape):
     N, K = shape
+    if fmt in ("int4b128", "int4b320") and K % int(fmt[5:]):
+        pytest.skip("the block does not divide K")
     rng = np.random.default_rng(K + N)
     if fmt == "f32":
         wc = rng.standard_normal((K, N)).astype(np.float32)
@@ -289,3 +293,39 @@ def test_device_quantizer_validation_before_device(lib):
         import torch
         if not torch.cuda.is_available():
             assert q(64, 4, 1) == DEV
+
+
+def test_int4_block_sizes_pack_as_block64_with_repeated_pairs():
+    """Int4 with block b (a multiple of 64) packs exactly as Int4-Block64 whose
+    64-blocks repeat the pair of the b-block holding them, so the Int4 kernels
+    read it unchanged; Block64 and Block-K ids behave as INT4_B64 and INT4_B0."""
+    N, K = 45, 768
+    rng = np.random.default_rng(12)
+    W = synth.normal_weights(rng, N, K)
+    for b in (128, 256, 384, 768):
+        q, p = Q.qgemm_quantize_weights(W, f"int4b{b}")
+        assert p.shape == (N, K // b, 2)
+        rep = np.repeat(p, b // 64, axis=1)            # one pair per 64-block
+        wp0, sp0 = Q.qgemm_pack_weights(K, N, "int4b64", q, rep)
+        wp, sp = Q.qgemm_pack_weights(K, N, f"int4b{b}", q, p)
+        assert np.array_equal(wp, wp0) and np.array_equal(sp, sp0)
+    q64, p64 = Q.qgemm_quantize_weights(W, Q.QGEMM_INT4_BLOCK(64))
+    qa, pa = Q.qgemm_quantize_weights(W, "int4b64")
+    assert np.array_equal(q64, qa) and np.array_equal(p64, pa)
+    qk, pk = Q.qgemm_quantize_weights(W, Q.QGEMM_INT4_BLOCK(K))
+    qb0, pb0 = Q.qgemm_quantize_weights(W, "int4b0")
+    assert np.array_equal(qk, qb0) and np.array_equal(pk, pb0)
+
+
+def test_int4_block_size_validation(lib):
+    SHAPE, FMT = 2, 3
+    size = lambda K, f: lib.qgemm_packed_size(K, 8, f, ctypes.byref(ctypes.c_size_t()),
+                                              ctypes.byref(ctypes.c_size_t()))
+    assert size(256, Q.QGEMM_INT4_BLOCK(128)) == 0
+    assert size(384, Q.QGEMM_INT4_BLOCK(256)) == SHAPE    # the block must divide K
+    assert size(256, Q.QGEMM_INT4_BLOCK(32)) == FMT       # blocks are multiples of 64
+    assert size(256, Q.QGEMM_INT4_BLOCK(96)) == FMT
+    assert size(256, Q.QGEMM_INT4_BLOCK(0)) == FMT
+    assert size(256, Q.QGEMM_INT4_BLOCK(-64)) == FMT
+    assert Q.qgemm_workspace_size(16, 4096, 256, "int4b128") == \
+        Q.qgemm_workspace_size(16, 4096, 256, "int4b64")  # same kernels, same split-K plan

@@ -132,6 +132,15 @@ def test_f16_shapes(M):
 
 
 @pytest.mark.parametrize("M", [1, 3, 8, 9, 64, 65, 129])
+def test_int4_other_block_sizes(M):
+    """Int4 with blocks of 128, 256 and 320 K-elements (the page's blockSize
+    parameter) through the Int4 GEMV and GEMM, split-K shapes included."""
+    for fmt, K, N in [("int4b128", 128, 5), ("int4b128", 4096, 256), ("int4b256", 2560, 1024),
+                      ("int4b320", 640, 130), ("int4b128", 9728, 96)]:
+        _parity(fmt, M, K, N, seed=M * 17 + K + N)
+
+
+@pytest.mark.parametrize("M", [1, 3, 8, 9, 64, 65, 129])
 def test_int4b0_shapes(M):
     """Int4-Block0 with fp16 activations (per-channel pairs) through the
     Int4 GEMV and GEMM, split-K shapes included."""

@@ -97,12 +97,13 @@ static qgemm_status launched(hipError_t e) {
     return e == hipSuccess ? QGEMM_OK : QGEMM_ERR_LAUNCH;
 }
 
-// The Int4 (Block64 and Block0), Int8-Block0, W4A8 and fp16-weight GEMV kernels serve M <= the
-// current GEMV limit (and K within their register budgets); everything else
-// takes a tiled GEMM.
+// The Int4 (every block size), Int8-Block0, W4A8 and fp16-weight GEMV kernels
+// serve M <= the current GEMV limit (and K within their register budgets);
+// everything else takes a tiled GEMM.
 static bool use_gemv(qgemm_format f, int M, int K) {
     if (M > gemv_max_m()) return false;
-    if (f == QGEMM_INT4_B64 || f == QGEMM_INT4_B0 || f == QGEMM_INT8_B0 || f == QGEMM_W4A8)
+    f = kernel_format(f);
+    if (f == QGEMM_INT4_B64 || f == QGEMM_INT8_B0 || f == QGEMM_W4A8)
         return K <= kGemvMaxK;
     if (f == QGEMM_F16) return K <= kGemvF16MaxK;
     return false;
@@ -142,12 +143,11 @@ static qgemm_status dispatch(int M, int K, int N, qgemm_format f, const Geometry
     const int nsplit = gemv ? 1 : r.nsplit;
     float *part = nsplit > 1 ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + r.part_off)
                              : nullptr;
-    switch (f) {
+    switch (kernel_format(f)) {
     case QGEMM_F32:
         return launched(launch_gemm_f32(M, K, N, static_cast<const float *>(A),
                                         static_cast<const float *>(Bq), C, epi, nsplit, part, s));
-    case QGEMM_INT4_B64:
-    case QGEMM_INT4_B0:   // packed as Int4-Block64 (one pair repeated per block)
+    case QGEMM_INT4_B64:   // every Int4 format without A8 packs as Int4-Block64
         return launched(gemv ? launch_gemv_int4b64(M, K, N, A, Bq, scales, C, epi, s)
                              : launch_gemm_int4b64(M, K, N, A, Bq, scales, C, epi, nsplit, part, s));
     case QGEMM_INT8_B0:
@@ -158,6 +158,8 @@ static qgemm_status dispatch(int M, int K, int N, qgemm_format f, const Geometry
     case QGEMM_F16:
         return launched(gemv ? launch_gemv_f16(M, K, N, A, Bq, C, epi, s)
                              : launch_gemm_f16(M, K, N, A, Bq, C, epi, s));
+    default:
+        break;
     }
     return QGEMM_ERR_FORMAT;
 }
@@ -265,8 +267,7 @@ qgemm_status qgemm_w4a8_debug(int M, int K, int N, const void *A, const void *Bq
 // Checks shared by the device quantisers; *empty is set for N == 0.
 static qgemm_status check_quantize(int K, int N, qgemm_format f, const float *W, const void *q,
                                    const void *pairs, Geometry *g, bool *empty) {
-    if (f != QGEMM_INT4_B64 && f != QGEMM_INT8_B0 && f != QGEMM_W4A8 && f != QGEMM_INT4_B0)
-        return QGEMM_ERR_FORMAT;                   // float weights are not quantised
+    if (f == QGEMM_F32 || f == QGEMM_F16) return QGEMM_ERR_FORMAT;   // float weights are not quantised
     qgemm_status st = geometry(K, N, f, g);
     if (st != QGEMM_OK) return st;
     *empty = N == 0;

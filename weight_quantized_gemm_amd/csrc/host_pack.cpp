@@ -16,7 +16,7 @@ namespace qg {
 
 static bool valid_format(int f) {
     return f == QGEMM_F32 || f == QGEMM_INT4_B64 || f == QGEMM_INT8_B0 || f == QGEMM_W4A8 ||
-           f == QGEMM_F16 || f == QGEMM_INT4_B0;
+           f == QGEMM_F16 || f == QGEMM_INT4_B0 || is_int4_blocked(f);
 }
 
 // Shapes are capped so that every element count and byte offset the kernels
@@ -34,6 +34,18 @@ qgemm_status geometry(int K, int N, qgemm_format f, Geometry *g) {
     Geometry r;
     r.K = K;
     r.N = N;
+    if (is_int4_blocked(f)) {
+        // Int4 with one pair per b K-elements, packed as Int4-Block64 with
+        // each pair repeated in the 64-blocks it covers
+        const int b = f - QGEMM_INT4_BLOCK_BASE;
+        if (b % 64 != 0) return QGEMM_ERR_FORMAT;
+        if (K == 0 || K % b != 0) return QGEMM_ERR_SHAPE;
+        r.Kp = K; r.Np = (int)round_up(N, 32); r.nblk = K / b; r.block = b;
+        r.w_bytes = round_up((size_t)(r.Np / 32) * (K / 64) * 1024, kPackAlign);
+        r.s_bytes = round_up((size_t)(r.Np / 32) * (K / 64) * 256, kPackAlign);
+        *g = r;
+        return QGEMM_OK;
+    }
     switch (f) {
     case QGEMM_F32:
         r.Kp = K; r.Np = N; r.nblk = 0;
@@ -53,18 +65,19 @@ qgemm_status geometry(int K, int N, qgemm_format f, Geometry *g) {
         // repeated in every 64-block: the same weights, the same kernels
         if (K == 0 || K % 64 != 0) return QGEMM_ERR_SHAPE;
         r.Kp = K; r.Np = (int)round_up(N, 32); r.nblk = f == QGEMM_INT4_B0 ? 1 : K / 64;
+        r.block = f == QGEMM_INT4_B0 ? K : 64;
         r.w_bytes = round_up((size_t)(r.Np / 32) * (K / 64) * 1024, kPackAlign);
         r.s_bytes = round_up((size_t)(r.Np / 32) * (K / 64) * 256, kPackAlign);
         break;
     case QGEMM_INT8_B0:
         if (K == 0) return QGEMM_ERR_SHAPE;
-        r.Kp = (int)round_up(K, 64); r.Np = (int)round_up(N, 4); r.nblk = 1;
+        r.Kp = (int)round_up(K, 64); r.Np = (int)round_up(N, 4); r.nblk = 1; r.block = K;
         r.w_bytes = round_up((size_t)r.Np * r.Kp, kPackAlign);
         r.s_bytes = round_up((size_t)r.Np * 2 * sizeof(float), kPackAlign);
         break;
     case QGEMM_W4A8:
         if (K == 0 || K % 2 != 0 || K > kW4A8MaxK) return QGEMM_ERR_SHAPE;
-        r.Kp = (int)round_up(K, 64); r.Np = (int)round_up(N, 32); r.nblk = 1;
+        r.Kp = (int)round_up(K, 64); r.Np = (int)round_up(N, 32); r.nblk = 1; r.block = K;
         r.w_bytes = round_up((size_t)r.Np * (r.Kp / 2), kPackAlign);
         r.s_bytes = round_up((size_t)r.Np * 2 * sizeof(float), kPackAlign);
         break;
@@ -91,6 +104,7 @@ int f32_kgroups(int M, int N) {
 
 int splitk_plan(qgemm_format f, int M, int K, int N) {
     if (M <= 0 || N <= 0 || K <= 0) return 1;
+    f = kernel_format(f);
     long long tiles = 0;
     int kunits = 0;                  // K granules: the most slices a split may have
     switch (f) {
@@ -220,7 +234,7 @@ qgemm_status qgemm_quantize_weights(int K, int N, qgemm_format f, const float *W
         if (!std::isfinite(W[i])) return QGEMM_ERR_VALUE;
 
     const int bits = (f == QGEMM_INT8_B0) ? 8 : 4;
-    const int block = (f == QGEMM_INT4_B64) ? 64 : K;
+    const int block = g.block;
     const int nblk = K / block;
     const int qmax = (1 << bits) - 1;
     uint8_t *q = static_cast<uint8_t *>(q_out);
@@ -277,7 +291,7 @@ qgemm_status qgemm_pack_weights(int K, int N, qgemm_format f, const void *w_cano
     if (g.s_bytes) std::memset(sp, 0, g.s_bytes);
     const uint8_t *wc = static_cast<const uint8_t *>(w_canonical);
 
-    switch (f) {
+    switch (kernel_format(f)) {
     case QGEMM_F32:
         if ((size_t)K * N) std::memcpy(wp, wc, (size_t)K * N * sizeof(float));
         break;
@@ -297,8 +311,9 @@ qgemm_status qgemm_pack_weights(int K, int N, qgemm_format f, const void *w_cano
             const int t = n >> 5, c = n & 31;
             for (int b = 0; b < nblk; ++b) {
                 const size_t rec = (size_t)t * nblk + b;
-                // Block0: the channel's one pair for every 64-block
-                const size_t pi = f == QGEMM_INT4_B0 ? (size_t)n * 2 : ((size_t)n * nblk + b) * 2;
+                // the pair of the block holding 64-block b (one per 64-block
+                // for Block64, the channel's one pair for Block0)
+                const size_t pi = ((size_t)n * g.nblk + (size_t)b * 64 / g.block) * 2;
                 for (int half = 0; half < 2; ++half)
                     std::memcpy(wp + rec * 1024 + (size_t)(32 * half + c) * 16,
                                 wc + (size_t)n * row + (size_t)b * 32 + half * 16, 16);
@@ -362,7 +377,7 @@ qgemm_status qgemm_unpack_weights(int K, int N, qgemm_format f, const void *w_pa
     const float *spf = reinterpret_cast<const float *>(s_packed);
     uint8_t *wc = static_cast<uint8_t *>(w_canonical);
 
-    switch (f) {
+    switch (kernel_format(f)) {
     case QGEMM_F32:
         if ((size_t)K * N) std::memcpy(wc, wp, (size_t)K * N * sizeof(float));
         break;
@@ -381,11 +396,11 @@ qgemm_status qgemm_unpack_weights(int K, int N, qgemm_format f, const void *w_pa
             const int t = n >> 5, c = n & 31;
             for (int b = 0; b < nblk; ++b) {
                 const size_t rec = (size_t)t * nblk + b;
-                const size_t pi = f == QGEMM_INT4_B0 ? (size_t)n * 2 : ((size_t)n * nblk + b) * 2;
+                const size_t pi = ((size_t)n * g.nblk + (size_t)b * 64 / g.block) * 2;
                 for (int half = 0; half < 2; ++half)
                     std::memcpy(wc + (size_t)n * row + (size_t)b * 32 + half * 16,
                                 wp + rec * 1024 + (size_t)(32 * half + c) * 16, 16);
-                pairs_canonical[pi + 0] = spf[rec * 64 + c * 2 + 0];   // Block0: every block holds it
+                pairs_canonical[pi + 0] = spf[rec * 64 + c * 2 + 0];   // every 64-block of a block holds it
                 pairs_canonical[pi + 1] = spf[rec * 64 + c * 2 + 1];
             }
         }

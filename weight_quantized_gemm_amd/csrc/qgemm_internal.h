@@ -19,7 +19,9 @@ constexpr size_t kPackAlign = 256;
 // ---------------------------------------------------------------------------
 // Packed layouts (host packer <-> kernels).
 //
-// INT4_B64, nblk = K / 64, Np = roundup(N, 32), tiles t of 32 channels:
+// INT4_B64 (and every Int4 format without A8: Int4-Block0 and the other
+// block sizes store each pair in every 64-block it covers), nblk = K / 64,
+// Np = roundup(N, 32), tiles t of 32 channels:
 //   weights: 1 KiB records, record (t, b) at (t * nblk + b) * 1024; its
 //            16-byte piece h * 32 + c holds canonical bytes [32 b + 16 h, +16)
 //            (the codes of k = 64 b + 32 h .. 64 b + 32 h + 31) of channel
@@ -50,10 +52,24 @@ struct Geometry {
     int Kp = 0;        // K padded to the kernels' step (64) where relevant
     int Np = 0;        // N padded to the channel group
     int nblk = 0;      // pairs per channel
+    int block = 0;     // K-elements per pair (0 for float weights)
     size_t w_bytes = 0, s_bytes = 0;
 };
 
 qgemm_status geometry(int K, int N, qgemm_format f, Geometry *g);
+
+// Int4 with a block size given in the format id (QGEMM_INT4_BLOCK(b)); the
+// id carries b, which geometry() checks against K.
+constexpr int kMaxBlock = 1 << 24;
+inline bool is_int4_blocked(int f) {
+    return f > QGEMM_INT4_BLOCK_BASE && f <= QGEMM_INT4_BLOCK_BASE + kMaxBlock;
+}
+// The format the kernels see: every Int4 weight format (Block64, Block0 and
+// the other block sizes) is packed as Int4-Block64, its pairs repeated in
+// each 64-block of their block.
+inline qgemm_format kernel_format(qgemm_format f) {
+    return (f == QGEMM_INT4_B0 || is_int4_blocked(f)) ? QGEMM_INT4_B64 : f;
+}
 
 constexpr int kGemvMaxM = 8;          // largest M the GEMV kernels take
 constexpr int kGemvF16MaxK = 8192;   // fp16-weight GEMV: 16 slices of 8 per lane

@@ -30,6 +30,7 @@ struct QParams {
     int K, N;
     int rows;        // channels the grid covers: N (canonical) or the padded Np (packed)
     int nkc;         // 64-element chunks per row: ceil(K / 64)
+    int block, nblk; // K-elements per pair and pairs per channel
     int kp;          // packed Int8-Block0 row length
     uint8_t *q;      // codes
     float *pairs;    // pairs
@@ -115,8 +116,9 @@ __device__ inline void store_codes(const QParams &p, int n, int kc, int lane, in
 }
 
 // OUT: QGEMM_F32 stands for the canonical layout, else the packed layout of
-// that format (Int4-Block0 packs as QGEMM_INT4_B64 with REPEAT). B64: one
-// pair per 64-block, else one pair per channel.
+// that format (the other Int4 block sizes pack as QGEMM_INT4_B64 with
+// REPEAT). B64: one pair per 64-block; else blocks of p.block elements (all
+// of K for the per-channel formats), each reduced before its codes.
 template <int OUT, int BITS, bool B64, bool REPEAT>
 __global__ __launch_bounds__(64 * kQWaves) void quantize_kernel(QParams p) {
     const int lane = threadIdx.x & 63;
@@ -161,58 +163,65 @@ __global__ __launch_bounds__(64 * kQWaves) void quantize_kernel(QParams p) {
         return;
     }
 
-    // one pair per channel: the row's minimum and maximum, then its codes
-    float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
-    bool bad_lane = false;
-    for (int j0 = 0; j0 < p.nkc; j0 += kQUnroll) {
-        float v[kQUnroll];
+    // blocks of several chunks: each block's minimum and maximum, then its codes
+    const int cpb = (p.block + 63) / 64;           // chunks per block
+    for (int blk = 0; blk < p.nblk; ++blk) {
+        const int c0 = blk * cpb, c1 = min(c0 + cpb, p.nkc);
+        const int kend = min((blk + 1) * p.block, p.K);
+        float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+        bool bad_lane = false;
+        for (int j0 = c0; j0 < c1; j0 += kQUnroll) {
+            float v[kQUnroll];
 #pragma unroll
-        for (int u = 0; u < kQUnroll; ++u) v[u] = row[min((j0 + u) * 64 + lane, p.K - 1)];
+            for (int u = 0; u < kQUnroll; ++u) v[u] = row[min((j0 + u) * 64 + lane, p.K - 1)];
 #pragma unroll
-        for (int u = 0; u < kQUnroll; ++u) {
-            const bool valid = live && (j0 + u) * 64 + lane < p.K;
-            lo = valid ? fminf(lo, v[u]) : lo;
-            hi = valid ? fmaxf(hi, v[u]) : hi;
-            bad_lane |= valid && !__builtin_isfinite(v[u]);
-        }
-    }
-    const bool bad = __ballot(bad_lane) != 0;
-    lo = wave_min(lo);
-    hi = wave_max(hi);
-    if ((lo == 0.0f || hi == 0.0f) && !bad) {
-        // an extreme of 0: the first zero in k order carries the sign a
-        // sequential scan keeps (rare, so found by a second scan)
-        for (int kc = 0; kc < p.nkc; ++kc) {
-            const int k = kc * 64 + lane;
-            const float v = row[min(k, p.K - 1)];
-            const unsigned long long z = __ballot(k < p.K && v == 0.0f);
-            if (z) {
-                const float z0 = __shfl(v, __builtin_ctzll(z));
-                lo = lo == 0.0f ? z0 : lo;
-                hi = hi == 0.0f ? z0 : hi;
-                break;
+            for (int u = 0; u < kQUnroll; ++u) {
+                const bool valid = live && (j0 + u) * 64 + lane < kend;
+                lo = valid ? fminf(lo, v[u]) : lo;
+                hi = valid ? fmaxf(hi, v[u]) : hi;
+                bad_lane |= valid && !__builtin_isfinite(v[u]);
             }
         }
-    }
-    const float2 pr = block_pair(lo, hi, qmax, bad, live);
-    for (int j0 = 0; j0 < p.nkc; j0 += kQUnroll) {
-        float v[kQUnroll];
-#pragma unroll
-        for (int u = 0; u < kQUnroll; ++u) v[u] = row[min((j0 + u) * 64 + lane, p.K - 1)];
-#pragma unroll
-        for (int u = 0; u < kQUnroll; ++u) {
-            const int kc = j0 + u;
-            if (kc >= p.nkc) break;                // uniform
-            const bool valid = live && !bad && kc * 64 + lane < p.K;
-            store_codes<OUT, BITS>(p, n, kc, lane, valid ? code_of(v[u], pr, qmax) : 0);
+        const bool bad = __ballot(bad_lane) != 0;
+        lo = wave_min(lo);
+        hi = wave_max(hi);
+        if ((lo == 0.0f || hi == 0.0f) && !bad) {
+            // an extreme of 0: the first zero in k order carries the sign a
+            // sequential scan keeps (rare, so found by a second scan)
+            for (int kc = c0; kc < c1; ++kc) {
+                const int k = kc * 64 + lane;
+                const float v = row[min(k, p.K - 1)];
+                const unsigned long long z = __ballot(k < kend && v == 0.0f);
+                if (z) {
+                    const float z0 = __shfl(v, __builtin_ctzll(z));
+                    lo = lo == 0.0f ? z0 : lo;
+                    hi = hi == 0.0f ? z0 : hi;
+                    break;
+                }
+            }
         }
-    }
-    float2 *pp = reinterpret_cast<float2 *>(p.pairs);
-    if (REPEAT) {
-        // packed Int4-Block0: the channel's pair in every 64-block record
-        for (int b = lane; b < p.nkc; b += 64) pp[((size_t)(n >> 5) * p.nkc + b) * 32 + (n & 31)] = pr;
-    } else if (lane == 0) {
-        pp[n] = pr;
+        const float2 pr = block_pair(lo, hi, qmax, bad, live);
+        for (int j0 = c0; j0 < c1; j0 += kQUnroll) {
+            float v[kQUnroll];
+#pragma unroll
+            for (int u = 0; u < kQUnroll; ++u) v[u] = row[min((j0 + u) * 64 + lane, p.K - 1)];
+#pragma unroll
+            for (int u = 0; u < kQUnroll; ++u) {
+                const int kc = j0 + u;
+                if (kc >= c1) break;                   // uniform
+                const bool valid = live && !bad && kc * 64 + lane < kend;
+                store_codes<OUT, BITS>(p, n, kc, lane, valid ? code_of(v[u], pr, qmax) : 0);
+            }
+        }
+        float2 *pp = reinterpret_cast<float2 *>(p.pairs);
+        if (OUT == QGEMM_F32) {
+            if (lane == 0) pp[(size_t)n * p.nblk + blk] = pr;
+        } else if (REPEAT) {
+            // packed as Int4-Block64: the pair in every 64-block record of the block
+            for (int b = c0 + lane; b < c1; b += 64) pp[((size_t)(n >> 5) * p.nkc + b) * 32 + (n & 31)] = pr;
+        } else if (lane == 0) {
+            pp[n] = pr;
+        }
     }
 }
 
@@ -234,6 +243,8 @@ hipError_t launch_quantize(int K, int N, qgemm_format f, bool packed, const floa
     p.N = N;
     p.rows = packed ? g.Np : N;
     p.nkc = div_up(K, 64);
+    p.block = g.block;
+    p.nblk = g.nblk;
     p.kp = g.Kp;
     p.q = static_cast<uint8_t *>(q);
     p.pairs = pairs;
@@ -242,19 +253,16 @@ hipError_t launch_quantize(int K, int N, qgemm_format f, bool packed, const floa
         p.tail_off = g.Np * 2;
         p.tail_len = (int)(g.s_bytes / sizeof(float)) - g.Np * 2;
     }
+    const bool b64 = g.block == 64;
     if (!packed) {
-        switch (f) {
-        case QGEMM_INT4_B64: return launch<QGEMM_F32, 4, true, false>(p, s);
-        case QGEMM_INT8_B0:  return launch<QGEMM_F32, 8, false, false>(p, s);
-        default:             return launch<QGEMM_F32, 4, false, false>(p, s);   // W4A8, Int4-Block0
-        }
+        if (f == QGEMM_INT8_B0) return launch<QGEMM_F32, 8, false, false>(p, s);
+        return b64 ? launch<QGEMM_F32, 4, true, false>(p, s)
+                   : launch<QGEMM_F32, 4, false, false>(p, s);   // W4A8 and the other Int4 blocks
     }
-    switch (f) {
-    case QGEMM_INT4_B64: return launch<QGEMM_INT4_B64, 4, true, false>(p, s);
-    case QGEMM_INT4_B0:  return launch<QGEMM_INT4_B64, 4, false, true>(p, s);
-    case QGEMM_INT8_B0:  return launch<QGEMM_INT8_B0, 8, false, false>(p, s);
-    default:             return launch<QGEMM_W4A8, 4, false, false>(p, s);
-    }
+    if (f == QGEMM_INT8_B0) return launch<QGEMM_INT8_B0, 8, false, false>(p, s);
+    if (f == QGEMM_W4A8) return launch<QGEMM_W4A8, 4, false, false>(p, s);
+    return b64 ? launch<QGEMM_INT4_B64, 4, true, false>(p, s)
+               : launch<QGEMM_INT4_B64, 4, false, true>(p, s);   // Int4-Block0, other blocks
 }
 
 }  // namespace qg

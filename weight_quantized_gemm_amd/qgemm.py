@@ -96,8 +96,34 @@ class Epilogue(ctypes.Structure):
                 ("activation", ctypes.c_int), ("out_type", ctypes.c_int)]
 
 
+QGEMM_INT4_BLOCK_BASE = 0x10000
+
+
+def QGEMM_INT4_BLOCK(b: int) -> int:
+    """Format id of Int4 weights with one pair per b K-elements."""
+    return QGEMM_INT4_BLOCK_BASE + b
+
+
 def _fmt(f) -> int:
-    return FORMATS[f] if isinstance(f, str) else int(f)
+    """Format id from a name ("int4b64", "int8b0", ..., "int4b<b>" for any other
+    Int4 block size b) or an id."""
+    if not isinstance(f, str):
+        return int(f)
+    if f in FORMATS:
+        return FORMATS[f]
+    if f.startswith("int4b") and f[5:].isdigit():
+        return QGEMM_INT4_BLOCK(int(f[5:]))
+    raise ValueError(f"unknown format {f}")
+
+
+def pairs_per_channel(fmt, K: int) -> int:
+    """Canonical pairs per channel of a quantised format."""
+    f = _fmt(fmt)
+    if f == QGEMM_INT4_B64:
+        return K // 64
+    if f > QGEMM_INT4_BLOCK_BASE:
+        return K // (f - QGEMM_INT4_BLOCK_BASE)
+    return 1
 
 
 def _check(st: int, where: str):
@@ -169,8 +195,7 @@ def qgemm_quantize_weights(W: np.ndarray, fmt):
                                          _np_ptr(pairs), pf), "qgemm_quantize_weights")
     f = _fmt(fmt)
     qshape = (N, K) if f == QGEMM_INT8_B0 else (N, K // 2)
-    nblk = K // 64 if f == QGEMM_INT4_B64 else 1
-    return q.reshape(qshape), pairs.reshape(N, nblk, 2)
+    return q.reshape(qshape), pairs.reshape(N, pairs_per_channel(f, K), 2)
 
 
 def qgemm_pack_weights(K: int, N: int, fmt, w_canonical: np.ndarray,
@@ -246,8 +271,7 @@ def qgemm_quantize_weights_device(W, fmt, q=None, pairs=None, stream=None):
     _check(load().qgemm_quantize_weights_device(K, N, f, _dev_ptr(W), _dev_ptr(q), _dev_ptr(pairs),
                                                 _stream(stream)), "qgemm_quantize_weights_device")
     qshape = (N, K) if f == QGEMM_INT8_B0 else (N, K // 2)
-    nblk = K // 64 if f == QGEMM_INT4_B64 else 1
-    return q[:qb].view(qshape), pairs[:pf].view(N, nblk, 2)
+    return q[:qb].view(qshape), pairs[:pf].view(N, pairs_per_channel(f, K), 2)
 
 
 def qgemm_quantize_pack_device(W, fmt, Bq=None, scales=None, stream=None):
