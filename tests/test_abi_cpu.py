@@ -92,7 +92,14 @@ def test_split_k_workspace_plan():
     assert sz(512, 4096, 4096) == 0                       # 256 tiles fill the GPU
     assert sz(64, 448, 128) == 0                          # 7 K-blocks: too short to split
     assert sz(1, 4096, 4096) == sz(1, 4096, 4096)         # pure function of the shape
-    assert Q.qgemm_workspace_size(64, 4096, 512, "int8b0") == 0
+    # channel-row GEMM (Int8-Block0, fp16 weights): 128 x 64 tiles, slices of
+    # >= 8 K-blocks; W4A8: 128 x 256 tiles, slices of >= 4 stages of 128
+    assert Q.qgemm_workspace_size(64, 4096, 512, "int8b0") == 8 * 64 * 512 * 4    # 8 tiles
+    assert Q.qgemm_workspace_size(32, 9728, 2560, "f16") == 6 * 32 * 2560 * 4     # 40 tiles
+    assert Q.qgemm_workspace_size(512, 2560, 4096, "f16") == 0                    # 256 tiles
+    assert Q.qgemm_workspace_size(64, 448, 512, "int8b0") == 0                   # 7 K-blocks
+    w4 = Q.qgemm_workspace_size(32, 9728, 2560, "w4a8")
+    assert w4 - Q.qgemm_workspace_size(32, 9728, 32, "w4a8") >= 8 * 32 * 2560 * 4 - 8 * 32 * 32 * 4
     # fp32: 16x64 / 64x64 tiles; below 256 tiles each workgroup has two
     # K-groups, and a cross-workgroup split only when that is still short and
     # every group of every slice keeps four or more 64-wide chunks

@@ -375,6 +375,25 @@ def test_w4a8_gemv_debug_bit_exact(M, K, N):
     _w4a8_debug_check(M, K, N, seed=M + K, zero_row=M - 1 if M > 1 else None)
 
 
+@pytest.mark.parametrize("M,K,N", [(9, 3072, 512), (40, 9728, 300), (130, 2560, 250)])
+def test_w4a8_split_k_debug_bit_exact(M, K, N):
+    """W4A8 GEMM shapes with few output tiles split K into slices whose int32
+    partial products are added exactly: D stays bit-exact and C matches."""
+    assert Q.qgemm_workspace_size(M, K, N, "w4a8") > Q.qgemm_workspace_size(M, K, 1, "w4a8")
+    _w4a8_debug_check(M, K, N, seed=M + K + N, zero_row=2)
+
+
+@pytest.mark.parametrize("fmt", ["int8b0", "f16"])
+@pytest.mark.parametrize("M", [9, 32, 129])
+def test_rows_gemm_split_k(fmt, M):
+    """Channel-row GEMM (Int8-Block0, fp16 weights) on shapes with few output
+    tiles: K split into slices, each carrying its share of the pair terms,
+    added by the fixed-order reduce; ragged K and N."""
+    for K, N in [(9728, 96), (4160, 200), (2500, 64)]:
+        assert Q.qgemm_workspace_size(M, K, N, fmt) > 0
+        _parity(fmt, M, K, N, seed=M + K + N)
+
+
 def test_w4a8_debug_bit_exact_mid_size():
     M, K, N = 200, 3072, 300
     A, W, _ = _case("w4a8", M, K, N, seed=77)

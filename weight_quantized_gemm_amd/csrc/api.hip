@@ -117,12 +117,15 @@ static qgemm_status run_w4a8(int M, int K, int N, const Geometry &g, const void 
     int8_t *qa = reinterpret_cast<int8_t *>(base + w.qa_off);
     float *sa = reinterpret_cast<float *>(base + w.sa_off);
     int32_t *S = reinterpret_cast<int32_t *>(base + w.S_off);
+    if (use_gemv(QGEMM_W4A8, M, K))     // quantises the activations itself
+        return launched(launch_w4a8_gemv(M, K, N, w.qa_stride, A, qa, sa, S, Bq, scales, C, epi,
+                                         D_debug, s));
     hipError_t e = launch_w4a8_actquant(M, K, w.qa_stride, A, qa, sa, S, s);
     if (e != hipSuccess) return QGEMM_ERR_LAUNCH;
-    if (use_gemv(QGEMM_W4A8, M, K))
-        return launched(launch_w4a8_gemv(M, K, N, w.qa_stride, qa, sa, S, Bq, scales, C, epi,
-                                         D_debug, s));
-    return launched(launch_w4a8_gemm(M, K, N, w.qa_stride, qa, sa, S, Bq, scales, C, epi, D_debug, s));
+    const RunWorkspace r = run_workspace(QGEMM_W4A8, M, K, N);
+    int32_t *part = r.nsplit > 1 ? reinterpret_cast<int32_t *>(base + r.part_off) : nullptr;
+    return launched(launch_w4a8_gemm(M, K, N, w.qa_stride, qa, sa, S, Bq, scales, C, epi, D_debug,
+                                     r.nsplit, part, s));
 }
 
 
@@ -152,12 +155,12 @@ static qgemm_status dispatch(int M, int K, int N, qgemm_format f, const Geometry
                              : launch_gemm_int4b64(M, K, N, A, Bq, scales, C, epi, nsplit, part, s));
     case QGEMM_INT8_B0:
         return launched(gemv ? launch_gemv_int8b0(M, K, N, A, Bq, scales, C, epi, s)
-                             : launch_gemm_int8b0(M, K, N, A, Bq, scales, C, epi, s));
+                             : launch_gemm_int8b0(M, K, N, A, Bq, scales, C, epi, nsplit, part, s));
     case QGEMM_W4A8:
         return run_w4a8(M, K, N, g, A, Bq, scales, C, epi, ws, s, nullptr);
     case QGEMM_F16:
         return launched(gemv ? launch_gemv_f16(M, K, N, A, Bq, C, epi, s)
-                             : launch_gemm_f16(M, K, N, A, Bq, C, epi, s));
+                             : launch_gemm_f16(M, K, N, A, Bq, C, epi, nsplit, part, s));
     default:
         break;
     }
@@ -243,7 +246,8 @@ qgemm_status qgemm_w4a8_debug(int M, int K, int N, const void *A, const void *Bq
     if (!qa || !sa || !S || !D || !workspace) return QGEMM_ERR_NULL;
     if (!aligned16(workspace) || !aligned16(D)) return QGEMM_ERR_ALIGN;
     W4A8Workspace w = w4a8_workspace(M, K);
-    if (ws_bytes < w.bytes) return QGEMM_ERR_SIZE;
+    if (ws_bytes < used_bytes(run_workspace(QGEMM_W4A8, M, K, N), use_gemv(QGEMM_W4A8, M, K)))
+        return QGEMM_ERR_SIZE;
     st = check_device();
     if (st != QGEMM_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);

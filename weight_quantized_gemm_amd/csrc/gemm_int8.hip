@@ -19,7 +19,11 @@
 // the same value up to rounding: this form rounds fewer times (the weight is
 // never narrowed to fp16).
 //
-// Decomposition: a 256-thread workgroup owns a 128 x 64 tile of C; its four
+// Decomposition: a 256-thread workgroup owns a 128 x 64 tile of C (over a
+// contiguous slice of the K-blocks when the shape has too few tiles to fill
+// the chip: split-K, slice blockIdx.y of gridDim.y, written as a partial tile
+// that already carries its slice's share of the regrouped pair terms, for
+// the fixed-order split-K reduce to add); its four
 // waves split K (wave w takes the 64-wide K-blocks w, w+4, ...) and each
 // accumulates the whole tile with v_mfma_f32_16x16x32_f16. Each K-block is
 // consumed as two halves of 32; lane (r, g) = (lane % 16, lane / 16) owns
@@ -40,7 +44,7 @@
 namespace qg {
 
 namespace {
-constexpr int BM = 128, BN = 64, BK = 64;
+constexpr int BM = kRowsTileM, BN = kRowsTileN, BK = 64;
 constexpr int RF = BM / 16;   // 16-row accumulator tiles per wave
 constexpr int CF = BN / 16;   // 16-column accumulator tiles per wave
 constexpr int RED_STRIDE = BN + 4;   // floats per LDS row of the reduction
@@ -89,7 +93,9 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
     const int lane = tid & 63;
     const int wave = uniform(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
-    const int nblk = Kp / BK;
+    // this workgroup's K-blocks [KB0, KB0 + nblk) (all of them unless split)
+    const int KB0 = (int)((long long)blockIdx.y * (Kp / BK) / gridDim.y);
+    const int nblk = (int)((long long)(blockIdx.y + 1) * (Kp / BK) / gridDim.y) - KB0;
     const int nb_w = nblk > wave ? (nblk - wave + 3) / 4 : 0;   // K-blocks of this wave
     const int n_it = 2 * nb_w;                                   // half-block iterations
     const int n_pad = (n_it + UNROLL - 1) / UNROLL * UNROLL;     // every wave: same unrolled body
@@ -106,7 +112,7 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
     for (int cf = 0; cf < CF; ++cf) b_row[cf] = Wp + (size_t)min(n0 + cf * 16 + r, N - 1) * Kp * WB;
 
     // lane (r, g) holds K-elements k0 + 8 g .. k0 + 8 g + 7 of each half-block
-    auto k_of = [&](int it) { return (wave + 4 * (it >> 1)) * BK + 32 * (it & 1) + 8 * g; };
+    auto k_of = [&](int it) { return (KB0 + wave + 4 * (it >> 1)) * BK + 32 * (it & 1) + 8 * g; };
     auto load_a = [&](u4_t (&dst)[RF], int it) {
         const int k = k_of(it);
 #pragma unroll
@@ -207,13 +213,15 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
     __syncthreads();
 
     // Sum the four partials (fixed order), apply the channel pairs and store:
-    // thread -> row tid/2, 32 consecutive columns.
+    // thread -> row tid/2, 32 consecutive columns. A split-K slice stores its
+    // raw partial tile (plain fp32) at slice blockIdx.y of C.
     const int row = tid >> 1;
     const int c0 = (tid & 1) * 32;
     const int gm = m0 + row;
     if (gm >= M) return;
+    const bool raw = gridDim.y > 1 || epi.plain;
     const float rsm = ((rsum[0][row] + rsum[1][row]) + rsum[2][row]) + rsum[3][row];
-    float *dst = static_cast<float *>(C) + (size_t)gm * N + n0 + c0;
+    float *dst = static_cast<float *>(C) + (size_t)blockIdx.y * M * N + (size_t)gm * N + n0 + c0;
     const bool vec_store = (N & 3) == 0 && n0 + c0 + 32 <= N;
 #pragma unroll
     for (int j = 0; j < 32; j += 4) {
@@ -232,9 +240,9 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
                 out[e] = fmaf(pr.y, p[e], fmaf(-1024.0f, pr.y, pr.x) * rsm);
             }
         }
-        if (!epi.plain && vec_store) {
+        if (!raw && vec_store) {
             epi_put4(epi, C, gm, n0 + c0 + j, N, out);
-        } else if (!epi.plain) {
+        } else if (!raw) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 if (n0 + c0 + j + e < N) epi_put(epi, C, gm, n0 + c0 + j + e, N, out[e]);
@@ -250,30 +258,36 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
 
 template <bool WF16>
 static hipError_t launch_rows(int M, int K, int N, const void *A, const void *Wp, const void *Sp,
-                              void *C, const Epilogue &epi, hipStream_t s) {
+                              void *C, const Epilogue &epi, int nsplit, float *part,
+                              hipStream_t s) {
     const int Kp = (int)round_up(K, 64);
     const int tiles_n = div_up(N, BN);
     const int tiles = tiles_n * div_up(M, BM);
     const int xcd_order = (tiles % 8) == 0 ? 1 : 0;
+    void *out = nsplit > 1 ? static_cast<void *>(part) : C;
     auto launch = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, dim3(tiles), dim3(256), 0, s, M, K, N, Kp, tiles_n, xcd_order,
-                           static_cast<const _Float16 *>(A), static_cast<const uint8_t *>(Wp),
-                           static_cast<const float *>(Sp), C, epi);
+        hipLaunchKernelGGL(kernel, dim3(tiles, nsplit), dim3(256), 0, s, M, K, N, Kp, tiles_n,
+                           xcd_order, static_cast<const _Float16 *>(A),
+                           static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), out,
+                           epi);
     };
     if (K % 64 == 0) launch(gemm_rows_kernel<0, WF16>);
     else if (K % 8 == 0) launch(gemm_rows_kernel<1, WF16>);
     else launch(gemm_rows_kernel<2, WF16>);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || nsplit <= 1) return e;
+    return launch_splitk_reduce_f32(part, nsplit, M, N, C, epi, s);
 }
 
 hipError_t launch_gemm_int8b0(int M, int K, int N, const void *A, const void *Wp,
-                              const void *Sp, void *C, const Epilogue &epi, hipStream_t s) {
-    return launch_rows<false>(M, K, N, A, Wp, Sp, C, epi, s);
+                              const void *Sp, void *C, const Epilogue &epi, int nsplit,
+                              float *part, hipStream_t s) {
+    return launch_rows<false>(M, K, N, A, Wp, Sp, C, epi, nsplit, part, s);
 }
 
 hipError_t launch_gemm_f16(int M, int K, int N, const void *A, const void *Wp, void *C,
-                           const Epilogue &epi, hipStream_t s) {
-    return launch_rows<true>(M, K, N, A, Wp, nullptr, C, epi, s);
+                           const Epilogue &epi, int nsplit, float *part, hipStream_t s) {
+    return launch_rows<true>(M, K, N, A, Wp, nullptr, C, epi, nsplit, part, s);
 }
 
 }  // namespace qg

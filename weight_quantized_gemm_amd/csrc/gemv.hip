@@ -381,11 +381,11 @@ __global__ __launch_bounds__(64 * I8_WAVES) void gemv_f16_kernel(
 // Launchers
 // ---------------------------------------------------------------------------
 static int rows_per_pass(int M, int K, int kp_bytes_per_row) {
-    // Rows of A staged in LDS at once: they and 1 KiB of reduction space fit
-    // in 64 KiB of LDS.
+    // Rows of A staged in LDS at once (up to all M <= 8, so that the weights
+    // stream once): they and the reduction space fit in kGemvLds bytes.
     (void)K;
-    int mr = M >= 4 ? 4 : (M >= 2 ? 2 : 1);
-    while (mr > 1 && mr * kp_bytes_per_row > 65536 - 1024) mr >>= 1;
+    int mr = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
+    while (mr > 1 && (size_t)mr * kp_bytes_per_row > kGemvLds - 2048) mr >>= 1;
     return mr;
 }
 
@@ -409,7 +409,9 @@ static hipError_t gemv_int4_tile(int M, int K, int N, const void *A, const void 
 
 hipError_t launch_gemv_int4b64(int M, int K, int N, const void *A, const void *Wp,
                                const void *Sp, void *C, const Epilogue &epi, hipStream_t s) {
-    switch (M >= 4 ? 4 : (M >= 2 ? 2 : 1)) {
+    // all rows in one pass (at most 88 KiB of LDS for eight), so the weights stream once
+    switch (M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8) {
+    case 8: return gemv_int4_tile<8>(M, K, N, A, Wp, Sp, C, epi, s);
     case 4: return gemv_int4_tile<4>(M, K, N, A, Wp, Sp, C, epi, s);
     case 2: return gemv_int4_tile<2>(M, K, N, A, Wp, Sp, C, epi, s);
     default: return gemv_int4_tile<1>(M, K, N, A, Wp, Sp, C, epi, s);
@@ -436,13 +438,17 @@ static hipError_t gemv_int8_k(int M, int K, int N, int Kp, const void *A, const 
     if (nch <= 2) return gemv_int8_mr<MR, 2>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
     if (nch <= 4) return gemv_int8_mr<MR, 4>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
     if (nch <= 8) return gemv_int8_mr<MR, 8>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
-    return gemv_int8_mr<MR, 16>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
+    if constexpr (MR < 8) return gemv_int8_mr<MR, 16>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
+    return hipErrorInvalidConfiguration;   // eight rows are only dispatched for Kp <= 8192
 }
 
 hipError_t launch_gemv_int8b0(int M, int K, int N, const void *A, const void *Wp,
                               const void *Sp, void *C, const Epilogue &epi, hipStream_t s) {
     const int Kp = (int)round_up(K, 64);
-    switch (rows_per_pass(M, K, Kp * 2)) {
+    int mr = rows_per_pass(M, K, Kp * 2);
+    if (mr == 8 && Kp > 8192) mr = 4;   // eight rows of 16 slices would spill registers
+    switch (mr) {
+    case 8: return gemv_int8_k<8>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
     case 4: return gemv_int8_k<4>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
     case 2: return gemv_int8_k<2>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
     default: return gemv_int8_k<1>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
@@ -475,6 +481,7 @@ hipError_t launch_gemv_f16(int M, int K, int N, const void *A, const void *Wp, v
                            const Epilogue &epi, hipStream_t s) {
     const int Kp = (int)round_up(K, 64);
     switch (rows_per_pass(M, K, Kp * 2)) {
+    case 8: return gemv_f16_k<8>(M, K, N, Kp, A, Wp, C, epi, s);
     case 4: return gemv_f16_k<4>(M, K, N, Kp, A, Wp, C, epi, s);
     case 2: return gemv_f16_k<2>(M, K, N, Kp, A, Wp, C, epi, s);
     default: return gemv_f16_k<1>(M, K, N, Kp, A, Wp, C, epi, s);

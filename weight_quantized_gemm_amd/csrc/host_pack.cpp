@@ -123,6 +123,17 @@ int splitk_plan(qgemm_format f, int M, int K, int N) {
         kunits = div_up(K, kF32ChunkK) / (kg * 4);
         break;
     }
+    case QGEMM_INT8_B0:
+    case QGEMM_F16:
+        // four waves, two or more 64-blocks each
+        tiles = (long long)div_up(M, kRowsTileM) * div_up(N, kRowsTileN);
+        kunits = (int)(round_up((size_t)K, 64) / 64) / 8;
+        break;
+    case QGEMM_W4A8:
+        // each slice keeps four or more K stages (one turn of the load ring)
+        tiles = (long long)div_up(M, kW4A8TileM) * div_up(N, kW4A8TileN);
+        kunits = (int)(round_up((size_t)K, kW4A8StageK) / kW4A8StageK) / 4;
+        break;
     default:
         return 1;
     }

@@ -74,6 +74,8 @@ inline qgemm_format kernel_format(qgemm_format f) {
 constexpr int kGemvMaxM = 8;          // largest M the GEMV kernels take
 constexpr int kGemvF16MaxK = 8192;   // fp16-weight GEMV: 16 slices of 8 per lane
 constexpr int kGemvMaxK = 16384;      // A rows staged in LDS: MR * K * 2 bytes
+// LDS a GEMV workgroup may use (gfx950 gives a workgroup up to 160 KiB).
+constexpr size_t kGemvLds = 150 * 1024;
 
 // ---------------------------------------------------------------------------
 // Fused epilogue, as the kernels see it: C = act(P + bias + residual), fp32
@@ -107,24 +109,29 @@ hipError_t launch_gemm_int4b64(int M, int K, int N, const void *A, const void *W
 hipError_t launch_splitk_reduce_f32(const float *part, int nsplit, int M, int N, void *C,
                                     const Epilogue &epi, hipStream_t s);
 hipError_t launch_gemm_int8b0(int M, int K, int N, const void *A, const void *Wp,
-                              const void *Sp, void *C, const Epilogue &epi, hipStream_t s);
+                              const void *Sp, void *C, const Epilogue &epi, int nsplit,
+                              float *part, hipStream_t s);
 // fp16 weights as channel rows [Np][Kp] (Kp = roundup(K, 64)).
 hipError_t launch_gemv_f16(int M, int K, int N, const void *A, const void *Wp, void *C,
                            const Epilogue &epi, hipStream_t s);
 hipError_t launch_gemm_f16(int M, int K, int N, const void *A, const void *Wp, void *C,
-                           const Epilogue &epi, hipStream_t s);
+                           const Epilogue &epi, int nsplit, float *part, hipStream_t s);
 hipError_t launch_gemm_f32(int M, int K, int N, const float *A, const float *B, void *C,
                            const Epilogue &epi, int nsplit, float *part, hipStream_t s);
 // W4A8: qa [M][Kq] int8 (Kq = roundup(K, 128)), sa [M] float, S [M] int32
 // live in the workspace.
 hipError_t launch_w4a8_actquant(int M, int K, int Kq, const void *A, int8_t *qa,
                                 float *sa, int32_t *S, hipStream_t s);
+// nsplit > 1: int32 partial tiles in `part` ([nsplit][M][N]), added exactly
+// by a reduce kernel that applies the rescale and epilogue.
 hipError_t launch_w4a8_gemm(int M, int K, int N, int Kq, const int8_t *qa, const float *sa,
                             const int32_t *S, const void *Wp, const void *Sp,
-                            void *C, const Epilogue &epi, int32_t *D_debug, hipStream_t s);
-// M <= 8 (the GEMV limit), K <= kGemvMaxK.
-hipError_t launch_w4a8_gemv(int M, int K, int N, int Kq, const int8_t *qa, const float *sa,
-                            const int32_t *S, const void *Wp, const void *Sp, void *C,
+                            void *C, const Epilogue &epi, int32_t *D_debug, int nsplit,
+                            int32_t *part, hipStream_t s);
+// M <= 8 (the GEMV limit), K <= kGemvMaxK: quantises A itself (one launch);
+// qa [M][Kq], sa and S are written only with D_debug.
+hipError_t launch_w4a8_gemv(int M, int K, int N, int Kq, const void *A, int8_t *qa, float *sa,
+                            int32_t *S, const void *Wp, const void *Sp, void *C,
                             const Epilogue &epi, int32_t *D_debug, hipStream_t s);
 
 // Device quantiser (float W [N][K] -> codes and pairs): canonical layout, or
@@ -149,6 +156,10 @@ W4A8Workspace w4a8_workspace(int M, int K);
 // Output tile of the Int4-Block64 prefill GEMM (rows x columns), shared by
 // the kernel and the split-K planner.
 constexpr int kInt4TileM = 64, kInt4TileN = 128;
+// Output tile of the channel-row (Int8-Block0, fp16-weight) prefill GEMM.
+constexpr int kRowsTileM = 128, kRowsTileN = 64;
+// Output tile of the W4A8 prefill GEMM and its K stage (qa bytes per row).
+constexpr int kW4A8TileM = 128, kW4A8TileN = 256, kW4A8StageK = 128;
 // Output tiles of the fp32 GEMM: 16 x 64 for M <= 16, else 64 x 64; K in
 // chunks of 64.
 constexpr int kF32TileN = 64, kF32TileMSmall = 16, kF32TileM = 64, kF32ChunkK = 64;

@@ -165,7 +165,7 @@ hipError_t launch_w4a8_actquant(int M, int K, int Kq, const void *A, int8_t *qa,
 // each 64-wide block in step s for its A row and B column alike.
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int WBM = 128, WBN = 256, WSK = 128;
+constexpr int WBM = kW4A8TileM, WBN = kW4A8TileN, WSK = kW4A8StageK;
 constexpr int WNW = 8;                    // waves, one per 32-column block
 constexpr int WAROW = WSK + 16;           // bytes per LDS row of an A stage (144)
 constexpr int WRING = 4;                  // stages: LDS A tiles = A and B register ring slots
@@ -205,7 +205,11 @@ __global__ __launch_bounds__(64 * WNW) void w4a8_gemm_kernel(
     const int wave = uniform(tid >> 6);
     const int wn = wave;
     const int r = lane & 31, h = lane >> 5;
-    const int nst = Kq / WSK;                          // >= 1
+    // split-K: slice blockIdx.y of gridDim.y takes stages [st0, st0 + nst) of
+    // the Kq / WSK (the plan keeps gridDim.y <= Kq / WSK, so nst >= 1)
+    const int nst_all = Kq / WSK;
+    const int st0 = (int)((long long)blockIdx.y * nst_all / gridDim.y);
+    const int nst = (int)((long long)(blockIdx.y + 1) * nst_all / gridDim.y) - st0;
     const int nsteps = (nst + WRING - 1) / WRING * WRING;
     const int ntiles_b = (N + 31) / 32;
 
@@ -225,7 +229,7 @@ __global__ __launch_bounds__(64 * WNW) void w4a8_gemm_kernel(
     auto load_a = [&](u4_t (&dst)[2], int st) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-            dst[i] = *reinterpret_cast<const u4_t *>(qa + a_off[i] + (size_t)st * WSK);
+            dst[i] = *reinterpret_cast<const u4_t *>(qa + a_off[i] + (size_t)(st0 + st) * WSK);
     };
     auto a_tile = [&](int slot) { return As + (size_t)slot * WAS_BYTES; };
     auto store_a = [&](int8_t *T, const u4_t (&src)[2]) {
@@ -250,7 +254,7 @@ __global__ __launch_bounds__(64 * WNW) void w4a8_gemm_kernel(
     auto load_b = [&](u4_t (&dst)[2], int st) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            const size_t rec = b_rec0 + min(2 * st + kk, nkc - 1);
+            const size_t rec = b_rec0 + min(2 * (st0 + st) + kk, nkc - 1);
             dst[kk] = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(Wp + rec * 1024) + lane);
         }
     };
@@ -307,10 +311,21 @@ __global__ __launch_bounds__(64 * WNW) void w4a8_gemm_kernel(
         }
     }
 
-    // ---- epilogue: C = sa * (scale * D + offset * S) ----
+    // ---- epilogue: C = sa * (scale * D + offset * S), or this slice's D ----
     {
         const int col = n0 + 32 * wn + r;
         if (col >= N) return;
+        if (gridDim.y > 1) {       // exact int32 partial tile; the reduce finishes
+            int32_t *dp = D + (size_t)blockIdx.y * M * N;
+#pragma unroll
+            for (int rf = 0; rf < 4; ++rf)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int row = m0 + 32 * rf + 8 * (j >> 2) + 4 * h + (j & 3);
+                    if (row < M) dp[(size_t)row * N + col] = acc[rf][j];
+                }
+            return;
+        }
         const f2_t pr = Sp[col];
 #pragma unroll
         for (int rf = 0; rf < 4; ++rf) {
@@ -331,31 +346,73 @@ __global__ __launch_bounds__(64 * WNW) void w4a8_gemm_kernel(
 
 // ---------------------------------------------------------------------------
 // W4A8 GEMV (M up to the GEMV limit, the decode shape): one 1024-thread
-// workgroup per 32-channel tile, reading the same 1 KiB records as the GEMM.
-// Wave w takes the tile's records kc = w, w + 16, ... (whole records, all
-// requested up front, clamped into the tile). Lane (c, h) = (lane % 32,
-// lane / 32) holds 32 codes of channel c per record (k = 64 kc + 32 s +
-// 16 h + [0, 16) for s = 0, 1), unpacks them to int8 with one mask and one
-// shift-mask per word, and meets the row's qa in v_dot4 (exact int32 sums).
-// The two halves h and then the 16 waves' partial sums are added in a fixed
-// order; the epilogue is C = sa (scale D + offset S) as in the GEMM.
+// workgroup per 32-channel tile and pass of MR rows, reading the same 1 KiB
+// records as the GEMM.
+//  1. Each thread requests its share of the MR activation rows, then its
+//     wave's weight records (kc = w, w + 16, ...; whole records, clamped into
+//     the tile). Loads complete in order, so waiting for the activations
+//     leaves the records in flight.
+//  2. FUSED (one or two rows): the fp16 rows are quantised into LDS (16 / MR
+//     waves per row) with the same arithmetic as the standalone quantiser
+//     (row maximum, sa = amax / 127, quant1), so the codes, sa and S equal its
+//     results bit for bit. Otherwise the standalone quantiser has run and its
+//     codes are copied into LDS (every workgroup requantising many rows would
+//     cost more than the separate launch).
+//  3. Lane (c, h) = (lane % 32, lane / 32) holds 32 codes of channel c per
+//     record (k = 64 kc + 32 s + 16 h + [0, 16) for s = 0, 1), unpacks them to
+//     int8 with one mask and one shift-mask per word, and meets the codes of
+//     each row (LDS broadcast reads) in v_dot4: exact int32 sums.
+//  4. The two halves h, then the 16 waves' partial sums, are added in a fixed
+//     order; the epilogue is C = sa (scale D + offset S) as in the GEMM.
+// FUSED: every workgroup quantises its rows itself (a few KiB, read from L2),
+// so the call is one launch and qa never leaves the chip; with the debug
+// outputs requested, the workgroups of tile 0 also store qa, sa and S.
 // ---------------------------------------------------------------------------
 constexpr int WG_WAVES = 16;
+// LDS for MR quantised rows of Kp bytes (the wave partial sums reuse it).
+constexpr size_t kW4A8GemvLds = kGemvLds;
 
-template <int MR, int NREC, bool DEBUG_D>
+template <int MR, int NREC, bool FUSED, bool DEBUG_D>
 __global__ __launch_bounds__(64 * WG_WAVES) void w4a8_gemv_kernel(
-    int M, int N, int Kq, int nkc, const int8_t *__restrict__ qa, const float *__restrict__ sa,
-    const int32_t *__restrict__ S, const uint8_t *__restrict__ Wp, const f2_t *__restrict__ Sp,
-    void *__restrict__ C, Epilogue epi, int32_t *__restrict__ D) {
-    __shared__ int red[WG_WAVES][MR][32];
+    int M, int K, int N, int Kq, int nkc, const _Float16 *__restrict__ A, int8_t *__restrict__ qa,
+    float *__restrict__ sa, int32_t *__restrict__ S, const uint8_t *__restrict__ Wp,
+    const f2_t *__restrict__ Sp, void *__restrict__ C, Epilogue epi, int32_t *__restrict__ D) {
+    constexpr int WPR = WG_WAVES / MR;                       // waves per activation row
+    constexpr int TPR = 64 * WPR;                            // threads per activation row
+    // per thread: fp16 pairs of its row (FUSED), or 16-byte pieces of the codes
+    constexpr int AP = FUSED ? (NREC * MR / 2 > 1 ? NREC * MR / 2 : 1)
+                             : (NREC * MR / 16 > 1 ? NREC * MR / 16 : 1);
+    extern __shared__ __align__(16) uint8_t lds[];           // qa [MR][Kp], then partial sums
+    __shared__ float amax_w[WG_WAVES];
+    __shared__ int sum_w[WG_WAVES];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = uniform(tid >> 6);
     const int c = lane & 31, h = lane >> 5;
     const int t = blockIdx.x;
     const int m0 = blockIdx.y * MR;
+    const int Kp = nkc * 64, npair = K >> 1;
 
-    // 1. this wave's records (a record past the tile's end rereads the last)
+    // 1. this thread's activations (rows past M repeat row M - 1, never
+    //    stored), then this wave's records
+    const int ar = wave / WPR, at = tid - ar * TPR;
+    unsigned ap[FUSED ? AP : 1];
+    u4_t qp[FUSED ? 1 : AP];
+    if (FUSED) {
+        const unsigned *arow = reinterpret_cast<const unsigned *>(A + (size_t)min(m0 + ar, M - 1) * K);
+#pragma unroll
+        for (int j = 0; j < AP; ++j) ap[j] = arow[min(at + TPR * j, npair - 1)];
+    } else {
+        // piece i of the MR code rows: row i / (Kp / 16), bytes 16 (i % (Kp / 16))
+        const int per_row = Kp / 16;
+#pragma unroll
+        for (int j = 0; j < AP; ++j) {
+            const int i = min(tid + 64 * WG_WAVES * j, MR * per_row - 1);
+            const int r = i / per_row;
+            qp[j] = *reinterpret_cast<const u4_t *>(qa + (size_t)min(m0 + r, M - 1) * Kq +
+                                                     16 * (i - r * per_row));
+        }
+    }
     u4_t rec[NREC];
 #pragma unroll
     for (int i = 0; i < NREC; ++i) {
@@ -364,44 +421,104 @@ __global__ __launch_bounds__(64 * WG_WAVES) void w4a8_gemv_kernel(
             reinterpret_cast<const u4_t *>(Wp + ((size_t)t * nkc + kc) * 1024) + lane);
     }
 
-    // 2. exact int32 dot products; qa rows past M are clamped (never stored)
+    // 2. the codes of the MR rows into LDS
+    if (!FUSED) {
+        const int per_row = Kp / 16;
+#pragma unroll
+        for (int j = 0; j < AP; ++j) {
+            const int i = tid + 64 * WG_WAVES * j;
+            if (i < MR * per_row) *reinterpret_cast<u4_t *>(lds + 16 * i) = qp[j];
+        }
+        __syncthreads();
+    } else {
+        // quantise: maximum, then codes (zero past K) and sums
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < AP; ++j) {
+            const _Float16 *hv = reinterpret_cast<const _Float16 *>(&ap[j]);
+            const float m2 = fmaxf(fabsf((float)hv[0]), fabsf((float)hv[1]));
+            amax = at + TPR * j < npair ? fmaxf(amax, m2) : amax;
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        if (lane == 0) amax_w[wave] = amax;
+        __syncthreads();
+        float rmax = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WPR; ++w) rmax = fmaxf(rmax, amax_w[ar * WPR + w]);
+        const float s = rmax / 127.0f;           // IEEE division, one rounding
+        const float rs = 1.0f / s;               // IEEE division, one rounding
+        int sum = 0;
+#pragma unroll
+        for (int j = 0; j < AP; ++j) {
+            const int i = at + TPR * j;
+            const _Float16 *hv = reinterpret_cast<const _Float16 *>(&ap[j]);
+            int q0 = 0, q1 = 0;
+            if (i < npair && rmax != 0.0f) {
+                q0 = quant1((float)hv[0], s, rs);
+                q1 = quant1((float)hv[1], s, rs);
+            }
+            sum += q0 + q1;
+            if (2 * i < Kp)
+                *reinterpret_cast<unsigned short *>(lds + ar * Kp + 2 * i) =
+                    (unsigned short)((q0 & 0xff) | ((q1 & 0xff) << 8));
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+        if (lane == 0) sum_w[wave] = sum;
+        __syncthreads();
+        if (DEBUG_D && t == 0) {
+            // the standalone quantiser's outputs: qa rows of Kq bytes, sa, S
+            for (int i = tid; i < MR * Kq; i += 64 * WG_WAVES) {
+                const int r = i / Kq, k = i - r * Kq;
+                if (m0 + r < M) qa[(size_t)(m0 + r) * Kq + k] = k < Kp ? (int8_t)lds[r * Kp + k] : 0;
+            }
+            if (tid < MR && m0 + tid < M) {
+                float mx = 0.0f;
+                int S_r = 0;
+                for (int w = 0; w < WPR; ++w) {
+                    mx = fmaxf(mx, amax_w[tid * WPR + w]);
+                    S_r += sum_w[tid * WPR + w];
+                }
+                sa[m0 + tid] = mx != 0.0f ? mx / 127.0f : 0.0f;
+                S[m0 + tid] = S_r;
+            }
+        }
+    }
+
+    // 3. exact int32 dot products against the codes in LDS
     int acc[MR];
 #pragma unroll
     for (int r = 0; r < MR; ++r) acc[r] = 0;
-    const int8_t *qrow[MR];
-#pragma unroll
-    for (int r = 0; r < MR; ++r) qrow[r] = qa + (size_t)min(m0 + r, M - 1) * Kq + 16 * h;
 #pragma unroll
     for (int i = 0; i < NREC; ++i) {
         const int kc = wave + WG_WAVES * i;
+        const int kk = 64 * min(kc, nkc - 1) + 16 * h;
         const i4_t b0 = unpack_codes(rec[i][0], rec[i][1]);   // k = 64 kc + 16 h + [0, 16)
         const i4_t b1 = unpack_codes(rec[i][2], rec[i][3]);   // k = 64 kc + 32 + 16 h + [0, 16)
-        i4_t a0[MR], a1[MR];
-#pragma unroll
-        for (int r = 0; r < MR; ++r) {
-            const int kk = 64 * min(kc, nkc - 1);
-            a0[r] = *reinterpret_cast<const i4_t *>(qrow[r] + kk);
-            a1[r] = *reinterpret_cast<const i4_t *>(qrow[r] + kk + 32);
-        }
-        if (kc < nkc) {        // uniform; no load inside
+        if (kc < nkc) {        // uniform; no global load inside
 #pragma unroll
             for (int r = 0; r < MR; ++r) {
+                const i4_t a0 = *reinterpret_cast<const i4_t *>(lds + r * Kp + kk);
+                const i4_t a1 = *reinterpret_cast<const i4_t *>(lds + r * Kp + kk + 32);
                 int v = acc[r];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    v = __builtin_amdgcn_sdot4(a0[r][e], b0[e], v, false);
-                    v = __builtin_amdgcn_sdot4(a1[r][e], b1[e], v, false);
+                    v = __builtin_amdgcn_sdot4(a0[e], b0[e], v, false);
+                    v = __builtin_amdgcn_sdot4(a1[e], b1[e], v, false);
                 }
                 acc[r] = v;
             }
         }
     }
 
-    // 3. halves, then waves, in a fixed order; then the epilogue
+    // 4. halves, then waves, in a fixed order; then the epilogue
+    __syncthreads();                                   // the codes are no longer read
+    int *red = reinterpret_cast<int *>(lds);           // [WG_WAVES][MR][32]
 #pragma unroll
     for (int r = 0; r < MR; ++r) {
         const int v = acc[r] + __shfl_xor(acc[r], 32);
-        if (h == 0) red[wave][r][c] = v;
+        if (h == 0) red[(wave * MR + r) * 32 + c] = v;
     }
     __syncthreads();
     if (tid >= MR * 32) return;
@@ -409,60 +526,131 @@ __global__ __launch_bounds__(64 * WG_WAVES) void w4a8_gemv_kernel(
     if (n >= N || m >= M) return;
     int d = 0;
 #pragma unroll
-    for (int w = 0; w < WG_WAVES; ++w) d += red[w][r][tid & 31];
+    for (int w = 0; w < WG_WAVES; ++w) d += red[(w * MR + r) * 32 + (tid & 31)];
+    float sa_r;
+    int S_r = 0;
+    if (FUSED) {
+        float mx = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WPR; ++w) {
+            mx = fmaxf(mx, amax_w[r * WPR + w]);
+            S_r += sum_w[r * WPR + w];
+        }
+        sa_r = mx != 0.0f ? mx / 127.0f : 0.0f;
+    } else {
+        sa_r = sa[m];
+        S_r = S[m];
+    }
     if (DEBUG_D) D[(size_t)m * N + n] = d;
     const f2_t pr = Sp[n];
-    const float out = sa[m] * fmaf(pr.y, (float)d, pr.x * (float)S[m]);
+    const float out = sa_r * fmaf(pr.y, (float)d, pr.x * (float)S_r);
     if (epi.plain) static_cast<float *>(C)[(size_t)m * N + n] = out;
     else epi_put(epi, C, m, n, N, out);
 }
 
+// Fusing the quantisation pays for one or two rows; more rows use the
+// standalone quantiser's codes.
 template <int MR, int NREC>
-static void w4a8_gemv_launch(dim3 grid, hipStream_t s, int M, int N, int Kq, int nkc,
-                             const int8_t *qa, const float *sa, const int32_t *S, const void *Wp,
-                             const void *Sp, void *C, const Epilogue &epi, int32_t *D) {
+constexpr bool w4a8_gemv_fused() { return MR == 1 || (MR == 2 && NREC <= 8); }
+
+template <int MR, int NREC>
+static void w4a8_gemv_launch(dim3 grid, size_t lds, hipStream_t s, int M, int K, int N, int Kq,
+                             int nkc, const void *A, int8_t *qa, float *sa, int32_t *S,
+                             const void *Wp, const void *Sp, void *C, const Epilogue &epi,
+                             int32_t *D) {
+    constexpr bool F = w4a8_gemv_fused<MR, NREC>();
+    const _Float16 *a = static_cast<const _Float16 *>(A);
+    const uint8_t *w = static_cast<const uint8_t *>(Wp);
+    const f2_t *p = static_cast<const f2_t *>(Sp);
     if (D)
-        hipLaunchKernelGGL((w4a8_gemv_kernel<MR, NREC, true>), grid, dim3(64 * WG_WAVES), 0, s, M,
-                           N, Kq, nkc, qa, sa, S, static_cast<const uint8_t *>(Wp),
-                           static_cast<const f2_t *>(Sp), C, epi, D);
+        hipLaunchKernelGGL((w4a8_gemv_kernel<MR, NREC, F, true>), grid, dim3(64 * WG_WAVES), lds, s,
+                           M, K, N, Kq, nkc, a, qa, sa, S, w, p, C, epi, D);
     else
-        hipLaunchKernelGGL((w4a8_gemv_kernel<MR, NREC, false>), grid, dim3(64 * WG_WAVES), 0, s, M,
-                           N, Kq, nkc, qa, sa, S, static_cast<const uint8_t *>(Wp),
-                           static_cast<const f2_t *>(Sp), C, epi, D);
+        hipLaunchKernelGGL((w4a8_gemv_kernel<MR, NREC, F, false>), grid, dim3(64 * WG_WAVES), lds, s,
+                           M, K, N, Kq, nkc, a, qa, sa, S, w, p, C, epi, D);
 }
 
 template <int MR>
-static hipError_t w4a8_gemv_mr(int M, int K, int N, int Kq, const int8_t *qa, const float *sa,
-                               const int32_t *S, const void *Wp, const void *Sp, void *C,
+static hipError_t w4a8_gemv_mr(int M, int K, int N, int Kq, const void *A, int8_t *qa, float *sa,
+                               int32_t *S, const void *Wp, const void *Sp, void *C,
                                const Epilogue &epi, int32_t *D, hipStream_t s) {
     const int nkc = (int)round_up(K, 64) / 64;
     const dim3 grid(div_up(N, 32), div_up(M, MR));
+    const size_t codes = (size_t)MR * nkc * 64, sums = (size_t)WG_WAVES * MR * 32 * sizeof(int);
+    const size_t lds = codes > sums ? codes : sums;
     const int nrec = div_up(nkc, WG_WAVES);   // K <= 16384: at most 16
-    if (nrec <= 1) w4a8_gemv_launch<MR, 1>(grid, s, M, N, Kq, nkc, qa, sa, S, Wp, Sp, C, epi, D);
-    else if (nrec <= 2) w4a8_gemv_launch<MR, 2>(grid, s, M, N, Kq, nkc, qa, sa, S, Wp, Sp, C, epi, D);
-    else if (nrec <= 4) w4a8_gemv_launch<MR, 4>(grid, s, M, N, Kq, nkc, qa, sa, S, Wp, Sp, C, epi, D);
-    else if (nrec <= 8 || MR == 8) w4a8_gemv_launch<MR, 8>(grid, s, M, N, Kq, nkc, qa, sa, S, Wp, Sp, C, epi, D);
-    else w4a8_gemv_launch<(MR < 8 ? MR : 4), 16>(grid, s, M, N, Kq, nkc, qa, sa, S, Wp, Sp, C, epi, D);
+    const bool fused = nrec <= 1   ? w4a8_gemv_fused<MR, 1>()
+                       : nrec <= 2 ? w4a8_gemv_fused<MR, 2>()
+                       : nrec <= 4 ? w4a8_gemv_fused<MR, 4>()
+                       : nrec <= 8 ? w4a8_gemv_fused<MR, 8>()
+                                   : w4a8_gemv_fused<MR, 16>();
+    if (!fused) {
+        const hipError_t e = launch_w4a8_actquant(M, K, Kq, A, qa, sa, S, s);
+        if (e != hipSuccess) return e;
+    }
+    if (nrec <= 1) w4a8_gemv_launch<MR, 1>(grid, lds, s, M, K, N, Kq, nkc, A, qa, sa, S, Wp, Sp, C, epi, D);
+    else if (nrec <= 2) w4a8_gemv_launch<MR, 2>(grid, lds, s, M, K, N, Kq, nkc, A, qa, sa, S, Wp, Sp, C, epi, D);
+    else if (nrec <= 4) w4a8_gemv_launch<MR, 4>(grid, lds, s, M, K, N, Kq, nkc, A, qa, sa, S, Wp, Sp, C, epi, D);
+    else if (nrec <= 8) w4a8_gemv_launch<MR, 8>(grid, lds, s, M, K, N, Kq, nkc, A, qa, sa, S, Wp, Sp, C, epi, D);
+    else w4a8_gemv_launch<MR, 16>(grid, lds, s, M, K, N, Kq, nkc, A, qa, sa, S, Wp, Sp, C, epi, D);
     return hipGetLastError();
 }
 
-hipError_t launch_w4a8_gemv(int M, int K, int N, int Kq, const int8_t *qa, const float *sa,
-                            const int32_t *S, const void *Wp, const void *Sp, void *C,
+hipError_t launch_w4a8_gemv(int M, int K, int N, int Kq, const void *A, int8_t *qa, float *sa,
+                            int32_t *S, const void *Wp, const void *Sp, void *C,
                             const Epilogue &epi, int32_t *D_debug, hipStream_t s) {
-    if (M <= 1) return w4a8_gemv_mr<1>(M, K, N, Kq, qa, sa, S, Wp, Sp, C, epi, D_debug, s);
-    if (M <= 2) return w4a8_gemv_mr<2>(M, K, N, Kq, qa, sa, S, Wp, Sp, C, epi, D_debug, s);
-    // eight rows keep at most 8 records per lane in registers (K <= 8192);
-    // longer rows take two passes of four
-    if (M <= 4 || K > 8192) return w4a8_gemv_mr<4>(M, K, N, Kq, qa, sa, S, Wp, Sp, C, epi, D_debug, s);
-    return w4a8_gemv_mr<8>(M, K, N, Kq, qa, sa, S, Wp, Sp, C, epi, D_debug, s);
+    // rows per pass: up to M (at most 8), as long as their codes fit the LDS
+    const size_t Kp = round_up(K, 64);
+    int mr = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
+    while (mr > 1 && (size_t)mr * Kp > (size_t)kW4A8GemvLds) mr >>= 1;
+    switch (mr) {
+    case 1: return w4a8_gemv_mr<1>(M, K, N, Kq, A, qa, sa, S, Wp, Sp, C, epi, D_debug, s);
+    case 2: return w4a8_gemv_mr<2>(M, K, N, Kq, A, qa, sa, S, Wp, Sp, C, epi, D_debug, s);
+    case 4: return w4a8_gemv_mr<4>(M, K, N, Kq, A, qa, sa, S, Wp, Sp, C, epi, D_debug, s);
+    default: return w4a8_gemv_mr<8>(M, K, N, Kq, A, qa, sa, S, Wp, Sp, C, epi, D_debug, s);
+    }
+}
+
+// Split-K reduction: D = sum of the int32 partial tiles (exact in any order),
+// then the same rescale and epilogue as the unsplit kernel, so the result is
+// bit-identical to it.
+__global__ __launch_bounds__(256) void w4a8_splitk_reduce_kernel(
+    const int32_t *__restrict__ part, int nsplit, int M, int N, const float *__restrict__ sa,
+    const int32_t *__restrict__ S, const f2_t *__restrict__ Sp, void *__restrict__ C, Epilogue epi,
+    int32_t *__restrict__ D) {
+    const size_t mn = (size_t)M * N;
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= mn) return;
+    int d = part[i];
+    for (int z = 1; z < nsplit; ++z) d += part[(size_t)z * mn + i];
+    const int m = (int)(i / (size_t)N), n = (int)(i - (size_t)m * N);
+    if (D) D[i] = d;
+    const f2_t pr = Sp[n];
+    const float out = sa[m] * fmaf(pr.y, (float)d, pr.x * (float)S[m]);
+    if (epi.plain) static_cast<float *>(C)[i] = out;
+    else epi_put(epi, C, m, n, N, out);
 }
 
 hipError_t launch_w4a8_gemm(int M, int K, int N, int Kq, const int8_t *qa, const float *sa,
                             const int32_t *S, const void *Wp, const void *Sp, void *C,
-                            const Epilogue &epi, int32_t *D_debug, hipStream_t s) {
+                            const Epilogue &epi, int32_t *D_debug, int nsplit, int32_t *part,
+                            hipStream_t s) {
     const int nkc = (int)round_up(K, 64) / 64;
     const int tiles_m = div_up(M, WBM), tiles_n = div_up(N, WBN);
     const int xcd_bands = (tiles_n % 8 == 0) ? 1 : 0;
+    if (nsplit > 1) {
+        hipLaunchKernelGGL(w4a8_gemm_kernel<false>, dim3(tiles_m * tiles_n, nsplit), dim3(64 * WNW),
+                           0, s, M, N, Kq, nkc, tiles_n, xcd_bands, qa, sa, S,
+                           static_cast<const uint8_t *>(Wp), static_cast<const f2_t *>(Sp), C, epi,
+                           part);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const size_t mn = (size_t)M * N;
+        hipLaunchKernelGGL(w4a8_splitk_reduce_kernel, dim3((unsigned)((mn + 255) / 256)), dim3(256),
+                           0, s, part, nsplit, M, N, sa, S, static_cast<const f2_t *>(Sp), C, epi,
+                           D_debug);
+        return hipGetLastError();
+    }
     dim3 grid(tiles_m * tiles_n);
     if (D_debug)
         hipLaunchKernelGGL(w4a8_gemm_kernel<true>, grid, dim3(64 * WNW), 0, s, M, N, Kq, nkc,
