@@ -225,9 +225,10 @@ qgemm_status qgemm_workspace_size(int M, int K, int N, qgemm_format f,
  *   C       device, float [M][N] row-major, fully overwritten (no alpha or
  *           beta; K == 0 for F32 writes zeros).
  * Dispatch: every quantised format and F16 with M at most the GEMV threshold
- * (default 8, see qgemm_set_gemv_max_m) and K within the GEMV's limit
- * (16384; 8192 for F16) take a streaming GEMV (the page: M = 8 is the
- * narrow, near-decode case, bounded by GEMV bandwidth); other shapes take
+ * (default 8), within the format's own crossover (see qgemm_set_gemv_max_m)
+ * and K within the GEMV's limit (16384; 8192 for F16) take a streaming GEMV
+ * (the page: M = 8 is the narrow, near-decode case, bounded by GEMV
+ * bandwidth); other shapes take
  * the tiled MFMA kernels (fp16 MFMA; int8 MFMA for W4A8). W4A8 first runs
  * the activation quantiser. F32 runs the fp32 tiled kernel. Any scratch the shape
  * needs (qgemm_workspace_size) is allocated stream-ordered on `stream`
@@ -321,7 +322,9 @@ qgemm_status qgemm_w4a8_debug(int M, int K, int N, const void *A,
                               void *workspace, size_t ws_bytes, void *stream);
 
 /*
- * Sets the largest M that the quantised formats and F16 send to a GEMV kernel
+ * Sets the largest M that may take a GEMV kernel (below it each format keeps
+ * its own crossover: Int8-Block0 up to 4 rows, the Int4 formats up to 4 rows
+ * or up to 8 while M * K * N <= 3 * 2^26, fp16 and W4A8 up to 8 rows)
  * (0..8; default 8, or the QGEMM_GEMV_MAX_M environment variable read at
  * first use) and returns the previous value; a value outside 0..8 is
  * ignored and only the current value returned. Affects only which kernel

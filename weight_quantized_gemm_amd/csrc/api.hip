@@ -98,13 +98,20 @@ static qgemm_status launched(hipError_t e) {
 }
 
 // The Int4 (every block size), Int8-Block0, W4A8 and fp16-weight GEMV kernels
-// serve M <= the current GEMV limit (and K within their register budgets);
-// everything else takes a tiled GEMM.
-static bool use_gemv(qgemm_format f, int M, int K) {
+// serve M <= the current GEMV limit (and K within their register budgets),
+// within each format's own crossover with the tiled MFMA kernels, measured
+// on the benchmark page's shapes: the Int8 GEMV does all its arithmetic on
+// the vector ALUs and loses past 4 rows; the Int4 GEMV loses past 4 rows
+// once M * K * N exceeds about 2^27.6 (the weights are large enough for the
+// split-K GEMM to fill the chip); the fp16 and W4A8 GEMVs win up to 8 rows.
+// Everything else takes a tiled GEMM. A function of the shape alone.
+static bool use_gemv(qgemm_format f, int M, int K, int N) {
     if (M > gemv_max_m()) return false;
     f = kernel_format(f);
-    if (f == QGEMM_INT4_B64 || f == QGEMM_INT8_B0 || f == QGEMM_W4A8)
-        return K <= kGemvMaxK;
+    if (f == QGEMM_INT8_B0) return M <= 4 && K <= kGemvMaxK;
+    if (f == QGEMM_INT4_B64)
+        return K <= kGemvMaxK && (M <= 4 || (long long)M * K * N <= kGemvInt4MaxMKN);
+    if (f == QGEMM_W4A8) return K <= kGemvMaxK;
     if (f == QGEMM_F16) return K <= kGemvF16MaxK;
     return false;
 }
@@ -117,7 +124,7 @@ static qgemm_status run_w4a8(int M, int K, int N, const Geometry &g, const void 
     int8_t *qa = reinterpret_cast<int8_t *>(base + w.qa_off);
     float *sa = reinterpret_cast<float *>(base + w.sa_off);
     int32_t *S = reinterpret_cast<int32_t *>(base + w.S_off);
-    if (use_gemv(QGEMM_W4A8, M, K))     // quantises the activations itself
+    if (use_gemv(QGEMM_W4A8, M, K, N))     // quantises the activations itself
         return launched(launch_w4a8_gemv(M, K, N, w.qa_stride, A, qa, sa, S, Bq, scales, C, epi,
                                          D_debug, s));
     hipError_t e = launch_w4a8_actquant(M, K, w.qa_stride, A, qa, sa, S, s);
@@ -141,7 +148,7 @@ static qgemm_status dispatch(int M, int K, int N, qgemm_format f, const Geometry
                              const void *A, const void *Bq, const void *scales, void *C,
                              const Epilogue &epi, void *ws, hipStream_t s) {
     (void)hipGetLastError();   // start from a clean per-thread error state
-    const bool gemv = use_gemv(f, M, K);
+    const bool gemv = use_gemv(f, M, K, N);
     const RunWorkspace r = run_workspace(f, M, K, N);
     const int nsplit = gemv ? 1 : r.nsplit;
     float *part = nsplit > 1 ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + r.part_off)
@@ -190,7 +197,7 @@ qgemm_status qgemm_run_ex(int M, int K, int N, qgemm_format f, const void *A,
     Epilogue epi;
     st = make_epilogue(epilogue, &epi);
     if (st != QGEMM_OK) return st;
-    const size_t need = used_bytes(run_workspace(f, M, K, N), use_gemv(f, M, K));
+    const size_t need = used_bytes(run_workspace(f, M, K, N), use_gemv(f, M, K, N));
     const bool own = !workspace && ws_bytes == 0;   // scratch, if any, is ours to allocate
     if (need > 0 && !own) {
         if (!workspace) return QGEMM_ERR_NULL;
@@ -225,7 +232,7 @@ qgemm_status qgemm_run_ws(int M, int K, int N, qgemm_format f, const void *A,
         bool empty = false;
         qgemm_status st = check_run(M, K, N, f, A, Bq, scales, C, &g, &empty);
         if (st != QGEMM_OK) return st;
-        if (used_bytes(run_workspace(f, M, K, N), use_gemv(f, M, K)) > 0) return QGEMM_ERR_NULL;
+        if (used_bytes(run_workspace(f, M, K, N), use_gemv(f, M, K, N)) > 0) return QGEMM_ERR_NULL;
     }
     return qgemm_run_ex(M, K, N, f, A, Bq, scales, C, nullptr, workspace, ws_bytes, stream);
 }
@@ -246,7 +253,7 @@ qgemm_status qgemm_w4a8_debug(int M, int K, int N, const void *A, const void *Bq
     if (!qa || !sa || !S || !D || !workspace) return QGEMM_ERR_NULL;
     if (!aligned16(workspace) || !aligned16(D)) return QGEMM_ERR_ALIGN;
     W4A8Workspace w = w4a8_workspace(M, K);
-    if (ws_bytes < used_bytes(run_workspace(QGEMM_W4A8, M, K, N), use_gemv(QGEMM_W4A8, M, K)))
+    if (ws_bytes < used_bytes(run_workspace(QGEMM_W4A8, M, K, N), use_gemv(QGEMM_W4A8, M, K, N)))
         return QGEMM_ERR_SIZE;
     st = check_device();
     if (st != QGEMM_OK) return st;

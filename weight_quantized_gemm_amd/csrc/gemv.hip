@@ -438,17 +438,14 @@ static hipError_t gemv_int8_k(int M, int K, int N, int Kp, const void *A, const 
     if (nch <= 2) return gemv_int8_mr<MR, 2>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
     if (nch <= 4) return gemv_int8_mr<MR, 4>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
     if (nch <= 8) return gemv_int8_mr<MR, 8>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
-    if constexpr (MR < 8) return gemv_int8_mr<MR, 16>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
-    return hipErrorInvalidConfiguration;   // eight rows are only dispatched for Kp <= 8192
+    return gemv_int8_mr<MR, 16>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
 }
 
 hipError_t launch_gemv_int8b0(int M, int K, int N, const void *A, const void *Wp,
                               const void *Sp, void *C, const Epilogue &epi, hipStream_t s) {
     const int Kp = (int)round_up(K, 64);
-    int mr = rows_per_pass(M, K, Kp * 2);
-    if (mr == 8 && Kp > 8192) mr = 4;   // eight rows of 16 slices would spill registers
-    switch (mr) {
-    case 8: return gemv_int8_k<8>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
+    // the dispatcher sends at most four rows here (the tiled kernel wins above)
+    switch (rows_per_pass(M < 4 ? M : 4, K, Kp * 2)) {
     case 4: return gemv_int8_k<4>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
     case 2: return gemv_int8_k<2>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
     default: return gemv_int8_k<1>(M, K, N, Kp, A, Wp, Sp, C, epi, s);

@@ -74,6 +74,9 @@ inline qgemm_format kernel_format(qgemm_format f) {
 constexpr int kGemvMaxM = 8;          // largest M the GEMV kernels take
 constexpr int kGemvF16MaxK = 8192;   // fp16-weight GEMV: 16 slices of 8 per lane
 constexpr int kGemvMaxK = 16384;      // A rows staged in LDS: MR * K * 2 bytes
+// Largest M * K * N the Int4 GEMV takes for 5..8 rows (above it the tiled
+// kernel is faster).
+constexpr long long kGemvInt4MaxMKN = 3LL << 26;
 // LDS a GEMV workgroup may use (gfx950 gives a workgroup up to 160 KiB).
 constexpr size_t kGemvLds = 150 * 1024;
 
