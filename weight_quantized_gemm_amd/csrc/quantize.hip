@@ -67,11 +67,25 @@ __device__ inline float2 block_pair(float lo, float hi, int qmax, bool bad, bool
     return p;
 }
 
-// Code of one weight from its block's stored float pair.
-__device__ inline int code_of(float w, float2 p, int qmax) {
+// Code of one weight from its block's stored float pair: rint of the double
+// quotient (w - offset) / scale, clamped. rcp = 1 / scale, correctly rounded
+// to float (once per block). The float estimate t = RN(RN(w - offset) * rcp)
+// carries three roundings, so |t - exact| <= 3 * 2^-24 * 255 < 5e-5 for every
+// code range here, and the double quotient is within 2^-50 of the exact one.
+// Unless t lies within 2^-12 of a half-integer (or is not finite), all three
+// round to the same integer, and the float estimate's is returned; otherwise
+// the double quotient decides. The result is the double path's in every case.
+__device__ inline int code_of(float w, float2 p, float rcp, int qmax) {
     if (p.y == 0.0f) return 0;
-    double r = rint(((double)w - (double)p.x) / (double)p.y);
-    r = r < 0.0 ? 0.0 : (r > (double)qmax ? (double)qmax : r);
+    const float t = (w - p.x) * rcp;
+    const float rt = rintf(t);
+    float r;
+    if (fabsf(t - rt) < 0.5f - 0x1p-12f) {
+        r = rt;
+    } else {
+        r = (float)rint(((double)w - (double)p.x) / (double)p.y);
+    }
+    r = r < 0.0f ? 0.0f : (r > (float)qmax ? (float)qmax : r);
     return (int)r;
 }
 
@@ -151,7 +165,8 @@ __global__ __launch_bounds__(64 * kQWaves) void quantize_kernel(QParams p) {
                     hi = hi == 0.0f ? z0 : hi;
                 }
                 const float2 pr = block_pair(lo, hi, qmax, bad, live);
-                const int code = (live && !bad) ? code_of(v[u], pr, qmax) : 0;
+                const float rcp = 1.0f / pr.y;     // IEEE division, once per block
+                const int code = (live && !bad) ? code_of(v[u], pr, rcp, qmax) : 0;
                 store_codes<OUT, BITS>(p, n, kc, lane, code);
                 if (lane == 0) {
                     const size_t pi = OUT == QGEMM_F32 ? (size_t)n * p.nkc + kc
@@ -201,6 +216,7 @@ __global__ __launch_bounds__(64 * kQWaves) void quantize_kernel(QParams p) {
             }
         }
         const float2 pr = block_pair(lo, hi, qmax, bad, live);
+        const float rcp = 1.0f / pr.y;             // IEEE division, once per block
         for (int j0 = c0; j0 < c1; j0 += kQUnroll) {
             float v[kQUnroll];
 #pragma unroll
@@ -210,7 +226,7 @@ __global__ __launch_bounds__(64 * kQWaves) void quantize_kernel(QParams p) {
                 const int kc = j0 + u;
                 if (kc >= c1) break;                   // uniform
                 const bool valid = live && !bad && kc * 64 + lane < kend;
-                store_codes<OUT, BITS>(p, n, kc, lane, valid ? code_of(v[u], pr, qmax) : 0);
+                store_codes<OUT, BITS>(p, n, kc, lane, valid ? code_of(v[u], pr, rcp, qmax) : 0);
             }
         }
         float2 *pp = reinterpret_cast<float2 *>(p.pairs);
@@ -223,6 +239,223 @@ __global__ __launch_bounds__(64 * kQWaves) void quantize_kernel(QParams p) {
             pp[n] = pr;
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Four weights per lane (K % 4 == 0): lane l of a 256-element chunk j holds
+// k = 256 j + 4 l .. + 3 (one 16-byte load), so a 64-block spans 16 lanes and
+// its reduction four cross-lane steps, and each load moves four times the
+// bytes. G > 0: blocks of 4 G elements (64, 128 or 256), G lanes each, a
+// whole number of them per chunk. G == 0: blocks of whole chunks (a multiple
+// of 256 elements, or all of K), reduced over a first pass and coded in a
+// second. Same arithmetic, same results as quantize_kernel.
+// ---------------------------------------------------------------------------
+template <int G>
+__device__ inline float group_min(float v) {
+#pragma unroll
+    for (int m = 1; m < G; m <<= 1) v = fminf(v, __shfl_xor(v, m));
+    return v;
+}
+template <int G>
+__device__ inline float group_max(float v) {
+#pragma unroll
+    for (int m = 1; m < G; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+    return v;
+}
+template <int G>
+__device__ inline int group_imin(int v) {
+#pragma unroll
+    for (int m = 1; m < G; m <<= 1) v = min(v, __shfl_xor(v, m));
+    return v;
+}
+
+// Stores the four codes of lane `lane` in chunk j of channel n (k0 = 256 j +
+// 4 lane). Every lane calls it (the W4A8 words pair lanes).
+template <int OUT, int BITS>
+__device__ inline void store_codes4(const QParams &p, int n, int j, int lane, const int (&c)[4]) {
+    const int k0 = 256 * j + 4 * lane;
+    if (OUT == QGEMM_F32) {
+        if (BITS == 8) {
+            if (k0 < p.K)
+                *reinterpret_cast<uint32_t *>(p.q + (size_t)n * p.K + k0) =
+                    (uint32_t)c[0] | (uint32_t)c[1] << 8 | (uint32_t)c[2] << 16 | (uint32_t)c[3] << 24;
+        } else if (k0 < p.K) {
+            *reinterpret_cast<uint16_t *>(p.q + (size_t)n * (p.K / 2) + k0 / 2) =
+                (uint16_t)(c[0] | c[1] << 4 | c[2] << 8 | c[3] << 12);
+        }
+    } else if (OUT == QGEMM_INT4_B64) {
+        // record (n / 32, k0 / 64); piece 32 h + n % 32 holds canonical bytes
+        // [16 h, 16 h + 16) of the 64-block
+        const int o = k0 & 63, h = o >> 5;
+        const size_t rec = (size_t)(n >> 5) * p.nkc + (k0 >> 6);
+        if (k0 < p.K)
+            *reinterpret_cast<uint16_t *>(p.q + rec * 1024 + (size_t)(32 * h + (n & 31)) * 16 + (o & 31) / 2) =
+                (uint16_t)(c[0] | c[1] << 4 | c[2] << 8 | c[3] << 12);
+    } else if (OUT == QGEMM_INT8_B0) {
+        if (k0 < p.kp)
+            *reinterpret_cast<uint32_t *>(p.q + (size_t)n * p.kp + k0) =
+                (uint32_t)c[0] | (uint32_t)c[1] << 8 | (uint32_t)c[2] << 16 | (uint32_t)c[3] << 24;
+    } else {                          // W4A8
+        // word of k8 = 64 kc + 32 s + 16 h + 8 w: byte i = q[k8 + i] | q[k8 + 4 + i] << 4,
+        // the even lane's codes low, the odd lane's high
+        const uint32_t b4 = (uint32_t)c[0] | (uint32_t)c[1] << 8 | (uint32_t)c[2] << 16 | (uint32_t)c[3] << 24;
+        const uint32_t x = b4 | (__shfl_xor(b4, 1) << 4);
+        const int o = k0 & 63, s = o >> 5, h = (o >> 4) & 1, w = (o >> 3) & 1;
+        const size_t rec = (size_t)(n >> 5) * p.nkc + (k0 >> 6);
+        if ((lane & 1) == 0 && k0 < p.kp)
+            *reinterpret_cast<uint32_t *>(p.q + rec * 1024 + (size_t)(32 * h + (n & 31)) * 16 + 8 * s + 4 * w) = x;
+    }
+}
+
+template <int OUT, int BITS, int G>
+__global__ __launch_bounds__(64 * kQWaves) void quantize_vec_kernel(QParams p) {
+    const int lane = threadIdx.x & 63;
+    const int n = blockIdx.x * kQWaves + (threadIdx.x >> 6);
+    if (blockIdx.x == 0 && threadIdx.x < 64)
+        for (int i = lane; i < p.tail_len; i += 64) p.pairs[p.tail_off + i] = 0.0f;
+    if (n >= p.rows) return;                       // whole waves only
+    const bool live = n < p.N;
+    const float *row = p.W + (size_t)(live ? n : p.N - 1) * p.K;
+    constexpr int qmax = (1 << BITS) - 1;
+    const int nch = (p.K + 255) / 256;             // chunks per row
+    float2 *pp = reinterpret_cast<float2 *>(p.pairs);
+    auto load4 = [&](int j) {
+        return *reinterpret_cast<const f4_t *>(row + min(256 * j + 4 * lane, p.K - 4));
+    };
+
+    if (G > 0) {
+        for (int j0 = 0; j0 < nch; j0 += kQUnroll) {
+            f4_t v[kQUnroll];
+#pragma unroll
+            for (int u = 0; u < kQUnroll; ++u) v[u] = load4(j0 + u);
+#pragma unroll
+            for (int u = 0; u < kQUnroll; ++u) {
+                const int j = j0 + u;
+                if (j >= nch) break;               // uniform
+                const f4_t x = v[u];
+                // blocks of whole groups: K % (4 G) == 0, so a group is all in or all past K
+                const bool valid = live && 256 * j + 4 * lane < p.K;
+                const bool fin = __builtin_isfinite(x[0]) && __builtin_isfinite(x[1]) &&
+                                 __builtin_isfinite(x[2]) && __builtin_isfinite(x[3]);
+                const unsigned long long badm = __ballot(valid && !fin);
+                const unsigned long long gmask = G == 64 ? ~0ull : ((1ull << G) - 1) << (lane & ~(G - 1));
+                const bool bad = (badm & gmask) != 0;
+                float lo = group_min<G>(fminf(fminf(x[0], x[1]), fminf(x[2], x[3])));
+                float hi = group_max<G>(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+                if (__ballot(lo == 0.0f || hi == 0.0f) != 0) {
+                    // equal extremes differ only in the sign of zero: the first zero
+                    // in k order (key 2 k + sign) is the one a sequential scan keeps
+                    int key = 0x7fffffff;
+#pragma unroll
+                    for (int e = 3; e >= 0; --e)
+                        if (x[e] == 0.0f) key = (8 * lane + 2 * e) | (__builtin_signbitf(x[e]) ? 1 : 0);
+                    key = group_imin<G>(key);
+                    const float z0 = (key & 1) ? -0.0f : 0.0f;
+                    lo = lo == 0.0f ? z0 : lo;
+                    hi = hi == 0.0f ? z0 : hi;
+                }
+                const float2 pr = block_pair(lo, hi, qmax, bad, live);
+                const float rcp = 1.0f / pr.y;     // IEEE division, once per block
+                int c[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) c[e] = (valid && !bad) ? code_of(x[e], pr, rcp, qmax) : 0;
+                store_codes4<OUT, BITS>(p, n, j, lane, c);
+                const int k0 = 256 * j + 4 * lane;
+                if (OUT == QGEMM_F32) {
+                    if ((lane & (G - 1)) == 0 && k0 < p.K) pp[(size_t)n * p.nblk + k0 / (4 * G)] = pr;
+                } else if (OUT == QGEMM_INT4_B64) {
+                    // packed as Int4-Block64: the block's pair in each of its 64-block records
+                    if ((lane & 15) == 0 && k0 < p.K) pp[((size_t)(n >> 5) * p.nkc + (k0 >> 6)) * 32 + (n & 31)] = pr;
+                } else if (lane == 0) {
+                    pp[n] = pr;                    // per-channel formats: the one block is all of K
+                }
+            }
+        }
+        return;
+    }
+
+    // blocks of whole chunks (or all of K): reduce, then code
+    const int cpb = (p.block + 255) / 256;         // chunks per block
+    for (int blk = 0; blk < p.nblk; ++blk) {
+        const int c0 = blk * cpb, c1 = min(c0 + cpb, nch);
+        const int kend = min((blk + 1) * p.block, p.K);
+        float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+        bool bad_lane = false;
+        for (int j0 = c0; j0 < c1; j0 += kQUnroll) {
+            f4_t v[kQUnroll];
+#pragma unroll
+            for (int u = 0; u < kQUnroll; ++u) v[u] = load4(j0 + u);
+#pragma unroll
+            for (int u = 0; u < kQUnroll; ++u) {
+                const bool valid = live && 256 * (j0 + u) + 4 * lane < kend;   // K % 4 == 0
+                const f4_t x = v[u];
+                lo = valid ? fminf(lo, fminf(fminf(x[0], x[1]), fminf(x[2], x[3]))) : lo;
+                hi = valid ? fmaxf(hi, fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]))) : hi;
+                bad_lane |= valid && !(__builtin_isfinite(x[0]) && __builtin_isfinite(x[1]) &&
+                                       __builtin_isfinite(x[2]) && __builtin_isfinite(x[3]));
+            }
+        }
+        const bool bad = __ballot(bad_lane) != 0;
+        lo = wave_min(lo);
+        hi = wave_max(hi);
+        if ((lo == 0.0f || hi == 0.0f) && !bad) {
+            // an extreme of 0: the first zero in k order carries the sign a
+            // sequential scan keeps (rare, so found by a second scan)
+            for (int j = c0; j < c1; ++j) {
+                const f4_t x = load4(j);
+                int key = 0x7fffffff;
+#pragma unroll
+                for (int e = 3; e >= 0; --e)
+                    if (x[e] == 0.0f && 256 * j + 4 * lane + e < kend)
+                        key = (8 * lane + 2 * e) | (__builtin_signbitf(x[e]) ? 1 : 0);
+                key = group_imin<64>(key);
+                if (key != 0x7fffffff) {
+                    const float z0 = (key & 1) ? -0.0f : 0.0f;
+                    lo = lo == 0.0f ? z0 : lo;
+                    hi = hi == 0.0f ? z0 : hi;
+                    break;
+                }
+            }
+        }
+        const float2 pr = block_pair(lo, hi, qmax, bad, live);
+        const float rcp = 1.0f / pr.y;             // IEEE division, once per block
+        for (int j0 = c0; j0 < c1; j0 += kQUnroll) {
+            f4_t v[kQUnroll];
+#pragma unroll
+            for (int u = 0; u < kQUnroll; ++u) v[u] = load4(j0 + u);
+#pragma unroll
+            for (int u = 0; u < kQUnroll; ++u) {
+                const int j = j0 + u;
+                if (j >= c1) break;                    // uniform
+                const bool valid = live && !bad && 256 * j + 4 * lane < kend;
+                int c[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) c[e] = valid ? code_of(v[u][e], pr, rcp, qmax) : 0;
+                store_codes4<OUT, BITS>(p, n, j, lane, c);
+            }
+        }
+        if (OUT == QGEMM_F32) {
+            if (lane == 0) pp[(size_t)n * p.nblk + blk] = pr;
+        } else if (OUT == QGEMM_INT4_B64) {
+            // packed as Int4-Block64: the pair in every 64-block record of the block
+            const int b0 = blk * (p.block / 64), b1 = min(b0 + p.block / 64, p.nkc);
+            for (int b = b0 + lane; b < b1; b += 64) pp[((size_t)(n >> 5) * p.nkc + b) * 32 + (n & 31)] = pr;
+        } else if (lane == 0) {
+            pp[n] = pr;
+        }
+    }
+}
+
+template <int OUT, int BITS>
+hipError_t launch_vec(const QParams &p, int G, hipStream_t s) {
+    const dim3 grid(div_up(p.rows, kQWaves)), block(64 * kQWaves);
+    switch (G) {
+    case 16: hipLaunchKernelGGL((quantize_vec_kernel<OUT, BITS, 16>), grid, block, 0, s, p); break;
+    case 32: hipLaunchKernelGGL((quantize_vec_kernel<OUT, BITS, 32>), grid, block, 0, s, p); break;
+    case 64: hipLaunchKernelGGL((quantize_vec_kernel<OUT, BITS, 64>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((quantize_vec_kernel<OUT, BITS, 0>), grid, block, 0, s, p); break;
+    }
+    return hipGetLastError();
 }
 
 template <int OUT, int BITS, bool B64, bool REPEAT>
@@ -252,6 +485,20 @@ hipError_t launch_quantize(int K, int N, qgemm_format f, bool packed, const floa
         // the packed pair buffer is padded to its alignment past the Np pairs
         p.tail_off = g.Np * 2;
         p.tail_len = (int)(g.s_bytes / sizeof(float)) - g.Np * 2;
+    }
+    if ((K & 3) == 0) {
+        // four weights per lane: blocks of 64, 128 or 256 as lane groups, or
+        // blocks of whole 256-element chunks (and all of K) over two passes
+        const int G = (g.block == 64 || g.block == 128 || g.block == 256) ? g.block / 4 : 0;
+        if (G > 0 || g.block % 256 == 0 || g.block == K) {
+            if (!packed) {
+                if (f == QGEMM_INT8_B0) return launch_vec<QGEMM_F32, 8>(p, G, s);
+                return launch_vec<QGEMM_F32, 4>(p, G, s);
+            }
+            if (f == QGEMM_INT8_B0) return launch_vec<QGEMM_INT8_B0, 8>(p, G, s);
+            if (f == QGEMM_W4A8) return launch_vec<QGEMM_W4A8, 4>(p, G, s);
+            return launch_vec<QGEMM_INT4_B64, 4>(p, G, s);
+        }
     }
     const bool b64 = g.block == 64;
     if (!packed) {
