@@ -23,19 +23,26 @@
 // contiguous slice of the K-blocks when the shape has too few tiles to fill
 // the chip: split-K, slice blockIdx.y of gridDim.y, written as a partial tile
 // that already carries its slice's share of the regrouped pair terms, for
-// the fixed-order split-K reduce to add); its four
-// waves split K (wave w takes the 64-wide K-blocks w, w+4, ...) and each
-// accumulates the whole tile with v_mfma_f32_16x16x32_f16. Each K-block is
-// consumed as two halves of 32; lane (r, g) = (lane % 16, lane / 16) owns
-// K-elements k0 + 8 g .. +7 of a half for its A rows and B columns alike.
-// Operands come straight from global memory through register rings (A
-// three half-blocks ahead, codes four). Every load is unconditional, from
-// an index clamped into the arrays (rows past M and channels past N are
-// computed and never stored; A past K is replaced by zero, so the padded
-// codes there add nothing); a wave's last iterations past its own count
-// re-load its last half-block and skip only the arithmetic, in a uniform
-// branch that contains no load. The four partial tiles and row sums are
-// added in LDS in a fixed order.
+// the fixed-order split-K reduce to add). Its four waves split K (wave w
+// takes the 64-wide K-blocks w, w+4, ...) and each accumulates the whole tile
+// with v_mfma_f32_16x16x32_f16, so no wave shares an operand with another
+// and the loop has no barrier:
+//  - a wave's A block (128 rows x 64 K-elements) arrives with fully coalesced
+//    loads (8 rows x 128 bytes per instruction; rows of 64 bytes, as the MFMA
+//    lane layout would read them, take about 1.7x as long on this chip) two
+//    blocks ahead through a register ring, and passes through the wave's own
+//    two LDS tiles into the MFMA lane layout;
+//  - B comes straight from the channel rows, one 16-byte load per lane and
+//    block for the codes (two for fp16 weights), also two blocks ahead;
+//  - lane (r, g) = (lane % 16, lane / 16) holds K-elements 16 g + 8 s .. +7
+//    of a block in MFMA step s (s = 0, 1), for its A row and B column alike
+//    (the K order inside an MFMA only has to agree between the operands).
+// Every global load is unconditional, from an index clamped into the arrays
+// (rows past M and channels past N are computed and never stored; A past K is
+// replaced by zero, so the padded codes there add nothing); a wave's last
+// iterations past its own count re-load its last block and skip only the
+// arithmetic, in a uniform branch that contains no load. The four partial
+// tiles and row sums are added in LDS in a fixed order.
 #include <type_traits>
 
 #include "kernels_common.h"
@@ -48,14 +55,16 @@ constexpr int BM = kRowsTileM, BN = kRowsTileN, BK = 64;
 constexpr int RF = BM / 16;   // 16-row accumulator tiles per wave
 constexpr int CF = BN / 16;   // 16-column accumulator tiles per wave
 constexpr int RED_STRIDE = BN + 4;   // floats per LDS row of the reduction
-// Register rings, in half-block iterations (32 K-elements): A is loaded
-// RA - 1 iterations ahead (RA = 4, or 2 for element loads) and codes RB
-// iterations ahead. The main loop is unrolled UNROLL times so every ring
-// slot is a fixed register; a wave's trip count is padded to UNROLL with
-// clamped re-loads, and since these loads touch 16 rows each (the texture
-// path, not bandwidth, limits this kernel) a short unroll keeps that
-// padding small.
-constexpr int RA_FAST = 4, RB = 4, UNROLL = 4;
+constexpr int AS_STRIDE = BK + 8;    // halves per LDS row of an A tile (144 bytes)
+constexpr int A_TILE = BM * AS_STRIDE;            // halves per A tile
+constexpr int A_PIECES = BM * BK / 8 / 64;        // 16-byte A pieces per lane and block (16)
+// A and B are loaded DEPTH blocks ahead through register rings; the loop is
+// unrolled DEPTH times so every ring slot is a fixed register, and each wave
+// has DEPTH LDS tiles for A.
+constexpr int DEPTH = 2;
+constexpr size_t A_LDS = (size_t)4 * DEPTH * A_TILE * 2;
+constexpr size_t RED_LDS = (size_t)4 * BM * RED_STRIDE * 4 + (size_t)4 * BM * 4;
+constexpr size_t ROWS_LDS = A_LDS > RED_LDS ? A_LDS : RED_LDS;
 }
 
 // 8 Int8 codes (two words, k ascending) -> the fp16 values 1024 + q, exact.
@@ -68,18 +77,15 @@ __device__ __forceinline__ h8_t codes_biased(u2_t codes) {
     return __builtin_bit_cast(h8_t, o);
 }
 
-// KMODE 0: K % 64 == 0 (no masking); 1: K % 8 == 0 (16-byte pieces, masked
-// past K); 2: any K (element loads, masked past K). WF16: the rows hold fp16
-// weights (2 bytes each) instead of Int8-Block0 codes.
+// KMODE: 0: K % 64 == 0 (16-byte loads, no mask); 1: K % 8 == 0 (16-byte
+// loads, pieces past K masked); 2: any K (element loads, masked past K).
+// WF16: the rows hold fp16 weights (2 bytes each) instead of Int8-Block0 codes.
 template <int KMODE, bool WF16>
 __global__ __launch_bounds__(256) void gemm_rows_kernel(
     int M, int K, int N, int Kp, int tiles_n, int xcd_order, const _Float16 *__restrict__ A,
     const uint8_t *__restrict__ Wp, const float *__restrict__ Sp, void *__restrict__ C,
     Epilogue epi) {
-    // element loads (any K) keep a shallower A ring to stay in registers
-    constexpr int RA = KMODE == 2 ? 2 : RA_FAST;
-    __shared__ __align__(16) float red[4][BM * RED_STRIDE];   // 4 x 34 KiB
-    __shared__ float rsum[4][BM];
+    __shared__ __align__(16) unsigned char lds[ROWS_LDS];
 
     // Tile of this workgroup. With xcd_order, the workgroups the hardware
     // deals to one XCD (ids equal mod 8) get a contiguous run of tiles.
@@ -96,49 +102,52 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
     // this workgroup's K-blocks [KB0, KB0 + nblk) (all of them unless split)
     const int KB0 = (int)((long long)blockIdx.y * (Kp / BK) / gridDim.y);
     const int nblk = (int)((long long)(blockIdx.y + 1) * (Kp / BK) / gridDim.y) - KB0;
-    const int nb_w = nblk > wave ? (nblk - wave + 3) / 4 : 0;   // K-blocks of this wave
-    const int n_it = 2 * nb_w;                                   // half-block iterations
-    const int n_pad = (n_it + UNROLL - 1) / UNROLL * UNROLL;     // every wave: same unrolled body
+    const int n_it = nblk > wave ? (nblk - wave + 3) / 4 : 0;    // K-blocks of this wave
+    const int n_pad = (n_it + DEPTH - 1) / DEPTH * DEPTH;          // every wave: same unrolled body
     const int it_last = max(n_it - 1, 0);
+    auto k_of = [&](int it) { return (KB0 + wave + 4 * it) * BK; };   // first K-element of a block
 
-    // row and channel of each fragment, clamped into the arrays
-    const _Float16 *a_row[RF];
+    // A loader role: piece i of a block is row 8 i + lane / 8, elements
+    // 8 (lane % 8) .. +7 of the block's 64 (128 bytes per row)
+    const int prow = lane >> 3, ppc = lane & 7;
+    const _Float16 *a_row[A_PIECES];
 #pragma unroll
-    for (int rf = 0; rf < RF; ++rf) a_row[rf] = A + (size_t)min(m0 + rf * 16 + r, M - 1) * K;
-    constexpr int WB = WF16 ? 2 : 1;          // bytes per weight
-    using BV = std::conditional_t<WF16, u4_t, u2_t>;   // one lane's 8 weights
+    for (int i = 0; i < A_PIECES; ++i) a_row[i] = A + (size_t)min(m0 + 8 * i + prow, M - 1) * K;
+    constexpr int WB = WF16 ? 2 : 1;                  // bytes per weight
+    constexpr int BV = WF16 ? 2 : 1;                  // 16-byte loads per lane, column tile and block
     const uint8_t *b_row[CF];
 #pragma unroll
-    for (int cf = 0; cf < CF; ++cf) b_row[cf] = Wp + (size_t)min(n0 + cf * 16 + r, N - 1) * Kp * WB;
+    for (int cf = 0; cf < CF; ++cf)
+        b_row[cf] = Wp + ((size_t)min(n0 + cf * 16 + r, N - 1) * Kp + 16 * g) * WB;
 
-    // lane (r, g) holds K-elements k0 + 8 g .. k0 + 8 g + 7 of each half-block
-    auto k_of = [&](int it) { return (KB0 + wave + 4 * (it >> 1)) * BK + 32 * (it & 1) + 8 * g; };
-    auto load_a = [&](u4_t (&dst)[RF], int it) {
-        const int k = k_of(it);
+    auto load_a = [&](u4_t (&dst)[A_PIECES], int it) {
+        const int k = k_of(it) + 8 * ppc;
 #pragma unroll
-        for (int rf = 0; rf < RF; ++rf) {
+        for (int i = 0; i < A_PIECES; ++i) {
             if (KMODE == 0) {
-                dst[rf] = *reinterpret_cast<const u4_t *>(a_row[rf] + k);
+                dst[i] = *reinterpret_cast<const u4_t *>(a_row[i] + k);
             } else if (KMODE == 1) {
-                const u4_t v = *reinterpret_cast<const u4_t *>(a_row[rf] + min(k, K - 8));
-                const unsigned keep = k < K ? ~0u : 0u;
-                dst[rf] = v & keep;
+                const u4_t v = *reinterpret_cast<const u4_t *>(a_row[i] + min(k, K - 8));
+                dst[i] = v & (k < K ? ~0u : 0u);
             } else {
                 h8_t t8;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const _Float16 v = a_row[rf][min(k + e, K - 1)];
+                    const _Float16 v = a_row[i][min(k + e, K - 1)];
                     t8[e] = k + e < K ? v : (_Float16)0.0f;
                 }
-                dst[rf] = __builtin_bit_cast(u4_t, t8);
+                dst[i] = __builtin_bit_cast(u4_t, t8);
             }
         }
     };
-    auto load_b = [&](BV (&dst)[CF], int it) {
-        const int k = k_of(it);
+    auto load_b = [&](u4_t (&dst)[CF][BV], int it) {
+        const size_t k = (size_t)k_of(it) * WB;
 #pragma unroll
-        for (int cf = 0; cf < CF; ++cf) dst[cf] = *reinterpret_cast<const BV *>(b_row[cf] + (size_t)k * WB);
+        for (int cf = 0; cf < CF; ++cf)
+#pragma unroll
+            for (int v = 0; v < BV; ++v) dst[cf][v] = *reinterpret_cast<const u4_t *>(b_row[cf] + k + 16 * v);
     };
+    _Float16 *const a_tiles = reinterpret_cast<_Float16 *>(lds) + (size_t)wave * DEPTH * A_TILE;
 
     f4_t acc[RF][CF];
 #pragma unroll
@@ -150,51 +159,73 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
     for (int i = 0; i < RF; ++i) rs[i] = 0.f;
     const h2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
 
-    u4_t ra[RA][RF];
-    BV rb[RB][CF];
+    u4_t ra[DEPTH][A_PIECES];
+    u4_t rb[DEPTH][CF][BV];
     if (n_it > 0) {            // a wave with no K-block (K < 256) loads nothing
 #pragma unroll
-        for (int d = 0; d < RA - 1; ++d) load_a(ra[d], min(d, it_last));
-#pragma unroll
-        for (int d = 0; d < RB; ++d) load_b(rb[d], min(d, it_last));
+        for (int d = 0; d < DEPTH; ++d) {
+            load_a(ra[d], min(d, it_last));
+            load_b(rb[d], min(d, it_last));
+        }
         // one full wait: the loop header then merges an empty count with the
         // loop's own, and the compiler's in-order count stays exact
         __builtin_amdgcn_s_waitcnt(0);
 
-        for (int base = 0; base < n_pad; base += UNROLL) {
+        for (int base = 0; base < n_pad; base += DEPTH) {
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
+            for (int u = 0; u < DEPTH; ++u) {
                 const int it = base + u;
-                load_a(ra[(u + RA - 1) % RA], min(it + RA - 1, it_last));
-                h8_t bw[CF];
+                // 1. this block's A into the wave's tile u (the LDS operations of
+                //    one wave run in order, so the tile's reads of DEPTH blocks
+                //    ago are done)
+                _Float16 *At = a_tiles + (size_t)u * A_TILE;
+#pragma unroll
+                for (int i = 0; i < A_PIECES; ++i)
+                    *reinterpret_cast<u4_t *>(At + (8 * i + prow) * AS_STRIDE + 8 * ppc) = ra[u][i];
+                // 2. this block's B operands; then both ring slots take block it + DEPTH
+                h8_t bw[CF][2];
 #pragma unroll
                 for (int cf = 0; cf < CF; ++cf) {
-                    if constexpr (WF16) bw[cf] = __builtin_bit_cast(h8_t, rb[u % RB][cf]);
-                    else bw[cf] = codes_biased(rb[u % RB][cf]);
-                }
-                const u4_t (&av)[RF] = ra[u % RA];
-                if (it < n_it) {
-#pragma unroll
-                    for (int rf = 0; rf < RF; ++rf) {
-                        const h8_t a = __builtin_bit_cast(h8_t, av[rf]);
-                        if constexpr (!WF16) {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                rs[rf] = dot2(h2_t{a[2 * e], a[2 * e + 1]}, ones, rs[rf]);
-                        }
-#pragma unroll
-                        for (int cf = 0; cf < CF; ++cf)
-                            acc[rf][cf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bw[cf], acc[rf][cf], 0, 0, 0);
+                    if constexpr (WF16) {
+                        bw[cf][0] = __builtin_bit_cast(h8_t, rb[u][cf][0]);
+                        bw[cf][1] = __builtin_bit_cast(h8_t, rb[u][cf][BV - 1]);
+                    } else {
+                        bw[cf][0] = codes_biased(u2_t{rb[u][cf][0][0], rb[u][cf][0][1]});
+                        bw[cf][1] = codes_biased(u2_t{rb[u][cf][0][2], rb[u][cf][0][3]});
                     }
                 }
-                load_b(rb[u % RB], min(it + RB, it_last));
+                load_a(ra[u], min(it + DEPTH, it_last));
+                load_b(rb[u], min(it + DEPTH, it_last));
+                // 3. two MFMA steps: lane (r, g) takes K-elements 16 g + 8 s .. +7
+                if (it < n_it) {       // uniform; no global load inside
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+                        for (int rf = 0; rf < RF; ++rf) {
+                            const h8_t a = *reinterpret_cast<const h8_t *>(
+                                At + (rf * 16 + r) * AS_STRIDE + 16 * g + 8 * s2);
+                            if constexpr (!WF16) {
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    rs[rf] = dot2(h2_t{a[2 * e], a[2 * e + 1]}, ones, rs[rf]);
+                            }
+#pragma unroll
+                            for (int cf = 0; cf < CF; ++cf)
+                                acc[rf][cf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bw[cf][s2], acc[rf][cf], 0, 0, 0);
+                        }
+                    }
+                }
             }
         }
     }
 
-    // Partial tiles to LDS: accumulator element i of lane l in tile (rf, cf)
-    // is P[rf*16 + 4*(l/16) + i][cf*16 + l%16]. Row sums: lanes r, r + 16,
+    // Partial tiles to LDS (over the A tiles, once every wave is done with
+    // them): accumulator element i of lane l in tile (rf, cf) is
+    // P[rf*16 + 4*(l/16) + i][cf*16 + l%16]. Row sums: lanes r, r + 16,
     // r + 32, r + 48 hold disjoint K-elements of row rf*16 + r.
+    __syncthreads();
+    float (*red)[BM * RED_STRIDE] = reinterpret_cast<float (*)[BM * RED_STRIDE]>(lds);
+    float (*rsum)[BM] = reinterpret_cast<float (*)[BM]>(lds + (size_t)4 * BM * RED_STRIDE * 4);
     float *mine = red[wave];
 #pragma unroll
     for (int rf = 0; rf < RF; ++rf)
