@@ -24,9 +24,10 @@
  *                   K % 64 == 0.
  *   QGEMM_INT4_BLOCK(b)  Int4 with one pair per b K-elements (the page's
  *                   blockSize parameter, section "Why Conv1x1 is used to
- *                   measure GEMM"), b a multiple of 64 that divides K;
- *                   fp16 activations. QGEMM_INT4_BLOCK(64) behaves as
- *                   QGEMM_INT4_B64 and QGEMM_INT4_BLOCK(K) as QGEMM_INT4_B0.
+ *                   measure GEMM"), b = 32 or a multiple of 64 that divides
+ *                   K, and K % 64 == 0; fp16 activations.
+ *                   QGEMM_INT4_BLOCK(64) behaves as QGEMM_INT4_B64 and
+ *                   QGEMM_INT4_BLOCK(K) as QGEMM_INT4_B0.
  *
  * Format ids 0-3 equal the page's mode numbers. For every format but F32, A
  * is fp16; C is fp32 (or fp16 through qgemm_run_ex).

@@ -171,7 +171,7 @@ def test_sizes():
         Q.qgemm_packed_size(100, 8, "int4b64")
 
 
-@pytest.mark.parametrize("fmt", FMTS + ["int4b128", "int4b192"])
+@pytest.mark.parametrize("fmt", FMTS + ["int4b32", "int4b128", "int4b192"])
 @pytest.mark.parametrize("shape", [(1, 64), (5, 128), (70, 192), (33, 1024)])
 def test_quantizer_matches_oracle_bit_exact(fmt, shape):
     if fmt.startswith("int4b1") and shape[1] % int(fmt[5:]):
@@ -198,7 +198,7 @@ def test_quantizer_rejects_nonfinite():
         Q.qgemm_quantize_weights(np.zeros((4, 64), np.float32), "f32")
 
 
-@pytest.mark.parametrize("fmt", FMTS + ["f32", "int4b128", "int4b320"])
+@pytest.mark.parametrize("fmt", FMTS + ["f32", "int4b32", "int4b128", "int4b320"])
 @pytest.mark.parametrize("shape", [(1, 64), (3, 128), (70, 192), (37, 4160)])
 def test_pack_unpack_round_trip(fmt, shape):
     N, K = shape
@@ -330,9 +330,31 @@ def test_int4_block_size_validation(lib):
                                               ctypes.byref(ctypes.c_size_t()))
     assert size(256, Q.QGEMM_INT4_BLOCK(128)) == 0
     assert size(384, Q.QGEMM_INT4_BLOCK(256)) == SHAPE    # the block must divide K
-    assert size(256, Q.QGEMM_INT4_BLOCK(32)) == FMT       # blocks are multiples of 64
+    assert size(256, Q.QGEMM_INT4_BLOCK(32)) == 0         # a pair per half of each 64-block
+    assert size(96, Q.QGEMM_INT4_BLOCK(32)) == SHAPE      # the kernels' step: K % 64 == 0
+    assert size(256, Q.QGEMM_INT4_BLOCK(16)) == FMT       # 32 or multiples of 64
     assert size(256, Q.QGEMM_INT4_BLOCK(96)) == FMT
     assert size(256, Q.QGEMM_INT4_BLOCK(0)) == FMT
     assert size(256, Q.QGEMM_INT4_BLOCK(-64)) == FMT
     assert Q.qgemm_workspace_size(16, 4096, 256, "int4b128") == \
         Q.qgemm_workspace_size(16, 4096, 256, "int4b64")  # same kernels, same split-K plan
+
+
+def test_int4_block32_pair_records_golden():
+    """Int4 with 32-element blocks: codes as Int4-Block64; pair record (t, b)
+    is 512 bytes, entry 32 h + c holding channel 32 t + c's pair for K-elements
+    64 b + 32 h .. + 31."""
+    N, K = 40, 128
+    nblk = K // 32
+    wc = np.arange(N * K // 2, dtype=np.int64).astype(np.uint8).reshape(N, K // 2)
+    pc = np.arange(N * nblk * 2, dtype=np.float32).reshape(N, nblk, 2)
+    wp, sp = Q.qgemm_pack_weights(K, N, "int4b32", wc, pc)
+    wp64, _ = Q.qgemm_pack_weights(K, N, "int4b64", wc, np.zeros((N, K // 64, 2), np.float32))
+    assert np.array_equal(wp, wp64) and sp.size == 2 * (K // 64) * 512
+    recs = sp.view(np.float32).reshape(-1, 2, 32, 2)
+    for n in range(N):
+        t, c = divmod(n, 32)
+        for b in range(K // 64):
+            for h in range(2):
+                assert list(recs[t * (K // 64) + b, h, c]) == list(pc[n, 2 * b + h])
+    assert not np.any(recs[K // 64:, :, 8:, :])        # channels 40..63: zero padding

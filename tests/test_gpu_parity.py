@@ -133,10 +133,12 @@ def test_f16_shapes(M):
 
 @pytest.mark.parametrize("M", [1, 3, 8, 9, 64, 65, 129])
 def test_int4_other_block_sizes(M):
-    """Int4 with blocks of 128, 256 and 320 K-elements (the page's blockSize
-    parameter) through the Int4 GEMV and GEMM, split-K shapes included."""
+    """Int4 with blocks of 32, 128, 256 and 320 K-elements (the page's
+    blockSize parameter) through the Int4 GEMV and GEMM, split-K shapes
+    included."""
     for fmt, K, N in [("int4b128", 128, 5), ("int4b128", 4096, 256), ("int4b256", 2560, 1024),
-                      ("int4b320", 640, 130), ("int4b128", 9728, 96)]:
+                      ("int4b320", 640, 130), ("int4b128", 9728, 96), ("int4b32", 64, 33),
+                      ("int4b32", 4096, 300), ("int4b32", 2560, 1024)]:
         _parity(fmt, M, K, N, seed=M * 17 + K + N)
 
 

@@ -69,11 +69,12 @@ SHAPES = {
     "int8b0": [(1, 3), (137, 70), (1001, 9), (4096, 256), (5000, 5)],
     "w4a8": [(2, 1), (70, 70), (1002, 33), (3072, 128), (9000, 7)],
     "int4b128": [(128, 1), (256, 70), (4096, 300)],
+    "int4b32": [(64, 1), (128, 70), (4096, 300)],
     "int4b320": [(640, 33), (2560, 40)],
 }
 
 
-@pytest.mark.parametrize("fmt", FMTS + ["int4b128", "int4b320"])
+@pytest.mark.parametrize("fmt", FMTS + ["int4b32", "int4b128", "int4b320"])
 def test_device_quantizer_bit_exact(fmt):
     for i, (K, N) in enumerate(SHAPES[fmt]):
         rng = np.random.default_rng(700 + i)
@@ -100,7 +101,7 @@ def _corner_rows(K):
     return np.stack(rows)
 
 
-@pytest.mark.parametrize("fmt", FMTS + ["int4b128"])
+@pytest.mark.parametrize("fmt", FMTS + ["int4b32", "int4b128"])
 def test_device_quantizer_corner_cases(fmt):
     for K in ((128, 256) if fmt == "int4b128" else (64, 256)):
         W = _corner_rows(K)

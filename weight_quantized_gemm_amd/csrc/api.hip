@@ -158,8 +158,9 @@ static qgemm_status dispatch(int M, int K, int N, qgemm_format f, const Geometry
         return launched(launch_gemm_f32(M, K, N, static_cast<const float *>(A),
                                         static_cast<const float *>(Bq), C, epi, nsplit, part, s));
     case QGEMM_INT4_B64:   // every Int4 format without A8 packs as Int4-Block64
-        return launched(gemv ? launch_gemv_int4b64(M, K, N, A, Bq, scales, C, epi, s)
-                             : launch_gemm_int4b64(M, K, N, A, Bq, scales, C, epi, nsplit, part, s));
+        return launched(gemv ? launch_gemv_int4b64(M, K, N, A, Bq, scales, C, epi, g.block == 32, s)
+                             : launch_gemm_int4b64(M, K, N, A, Bq, scales, C, epi, g.block == 32,
+                                                   nsplit, part, s));
     case QGEMM_INT8_B0:
         return launched(gemv ? launch_gemv_int8b0(M, K, N, A, Bq, scales, C, epi, s)
                              : launch_gemm_int8b0(M, K, N, A, Bq, scales, C, epi, nsplit, part, s));

@@ -100,7 +100,7 @@ __device__ __forceinline__ h8_t dequant8(unsigned word, const DqParams &p, unsig
 __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     int M, int K, int N, int tiles_m, int tiles_n, int xcd_rows,
     const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
-    const float *__restrict__ Sp, void *__restrict__ C, Epilogue epi) {
+    const float *__restrict__ Sp, void *__restrict__ C, Epilogue epi, int half_pairs) {
     __shared__ __align__(16) unsigned char lds[LDS_BYTES];
 
     // ---- tile of this workgroup ----
@@ -186,7 +186,8 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
         for (int cf = 0; cf < CF; ++cf) {
             const size_t rec = b_rec0[cf] + kt;
             codes[cf] = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(Wp + rec * 1024) + lane);
-            pairs[cf] = *reinterpret_cast<const f2_t *>(Sp + rec * 64 + r * 2);
+            pairs[cf] = *reinterpret_cast<const f2_t *>(Sp + (rec << (6 + half_pairs)) +
+                                                        (h << 6) * half_pairs + r * 2);
         }
     };
 
@@ -330,8 +331,8 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
 }
 
 hipError_t launch_gemm_int4b64(int M, int K, int N, const void *A, const void *Wp,
-                               const void *Sp, void *C, const Epilogue &epi, int nsplit,
-                               float *part, hipStream_t s) {
+                               const void *Sp, void *C, const Epilogue &epi, int half_pairs,
+                               int nsplit, float *part, hipStream_t s) {
     const int tiles_m = div_up(M, BM), tiles_n = div_up(N, BN);
     // XCD grid: row bands x column bands = 8, each XCD's L2 then fetches
     // A of its row band and B of its column band; pick the grid the tile
@@ -348,7 +349,8 @@ hipError_t launch_gemm_int4b64(int M, int K, int N, const void *A, const void *W
     void *out = nsplit > 1 ? static_cast<void *>(part) : C;
     hipLaunchKernelGGL(gemm_int4b64_kernel, dim3(tiles_m * tiles_n, nsplit), dim3(64 * NWAVE), 0, s,
                        M, K, N, tiles_m, tiles_n, xcd_rows, static_cast<const _Float16 *>(A),
-                       static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), out, epi);
+                       static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), out, epi,
+                       half_pairs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nsplit <= 1) return e;
     return launch_splitk_reduce_f32(part, nsplit, M, N, C, epi, s);

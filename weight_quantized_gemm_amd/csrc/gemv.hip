@@ -55,7 +55,7 @@ constexpr int TILE_RPW = TILE_PASS / TILE_WAVES;   // blocks per wave and pass
 template <int MR, bool ONE_PASS>
 __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
     int M, int K, int N, const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
-    const float *__restrict__ Sp, void *__restrict__ C, Epilogue epi) {
+    const float *__restrict__ Sp, void *__restrict__ C, Epilogue epi, int half_pairs) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int nblk = K >> 6;
     const int pmax = min(nblk, TILE_PASS);
@@ -102,7 +102,8 @@ __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
         for (int i = 0; i < TILE_RPW; ++i) {
             const int b = b0 + min(wave + TILE_WAVES * i, pb - 1);
             pr[i] = __builtin_nontemporal_load(
-                reinterpret_cast<const f2_t *>(Sp + ((size_t)t * nblk + b) * 64 + c * 2));
+                reinterpret_cast<const f2_t *>(Sp + (((size_t)t * nblk + b) << (6 + half_pairs)) +
+                                               (h << 6) * half_pairs + c * 2));
         }
 #pragma unroll
         for (int i = 0; i < TILE_RPW; ++i) {
@@ -391,7 +392,8 @@ static int rows_per_pass(int M, int K, int kp_bytes_per_row) {
 
 template <int MR>
 static hipError_t gemv_int4_tile(int M, int K, int N, const void *A, const void *Wp,
-                                 const void *Sp, void *C, const Epilogue &epi, hipStream_t s) {
+                                 const void *Sp, void *C, const Epilogue &epi, int hp,
+                                 hipStream_t s) {
     const int pmax = std::min(K / 64, TILE_PASS);
     const size_t lds = (size_t)MR * pmax * 128 + (size_t)MR * pmax * 16 +
                        (size_t)TILE_WAVES * MR * 32 * sizeof(float);
@@ -399,22 +401,23 @@ static hipError_t gemv_int4_tile(int M, int K, int N, const void *A, const void 
     if (K <= 64 * TILE_PASS)
         hipLaunchKernelGGL((gemv_int4b64_tile_kernel<MR, true>), grid, dim3(64 * TILE_WAVES), lds, s,
                            M, K, N, static_cast<const _Float16 *>(A),
-                           static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), C, epi);
+                           static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), C, epi, hp);
     else
         hipLaunchKernelGGL((gemv_int4b64_tile_kernel<MR, false>), grid, dim3(64 * TILE_WAVES), lds, s,
                            M, K, N, static_cast<const _Float16 *>(A),
-                           static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), C, epi);
+                           static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), C, epi, hp);
     return hipGetLastError();
 }
 
 hipError_t launch_gemv_int4b64(int M, int K, int N, const void *A, const void *Wp,
-                               const void *Sp, void *C, const Epilogue &epi, hipStream_t s) {
+                               const void *Sp, void *C, const Epilogue &epi, int half_pairs,
+                               hipStream_t s) {
     // all rows in one pass (at most 88 KiB of LDS for eight), so the weights stream once
     switch (M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8) {
-    case 8: return gemv_int4_tile<8>(M, K, N, A, Wp, Sp, C, epi, s);
-    case 4: return gemv_int4_tile<4>(M, K, N, A, Wp, Sp, C, epi, s);
-    case 2: return gemv_int4_tile<2>(M, K, N, A, Wp, Sp, C, epi, s);
-    default: return gemv_int4_tile<1>(M, K, N, A, Wp, Sp, C, epi, s);
+    case 8: return gemv_int4_tile<8>(M, K, N, A, Wp, Sp, C, epi, half_pairs, s);
+    case 4: return gemv_int4_tile<4>(M, K, N, A, Wp, Sp, C, epi, half_pairs, s);
+    case 2: return gemv_int4_tile<2>(M, K, N, A, Wp, Sp, C, epi, half_pairs, s);
+    default: return gemv_int4_tile<1>(M, K, N, A, Wp, Sp, C, epi, half_pairs, s);
     }
 }
 

@@ -37,12 +37,13 @@ qgemm_status geometry(int K, int N, qgemm_format f, Geometry *g) {
     if (is_int4_blocked(f)) {
         // Int4 with one pair per b K-elements, packed as Int4-Block64 with
         // each pair repeated in the 64-blocks it covers
+        // (blocks of 32: a pair per half of each 64-block, 512-byte pair records)
         const int b = f - QGEMM_INT4_BLOCK_BASE;
-        if (b % 64 != 0) return QGEMM_ERR_FORMAT;
-        if (K == 0 || K % b != 0) return QGEMM_ERR_SHAPE;
+        if (b != 32 && b % 64 != 0) return QGEMM_ERR_FORMAT;
+        if (K == 0 || K % b != 0 || K % 64 != 0) return QGEMM_ERR_SHAPE;
         r.Kp = K; r.Np = (int)round_up(N, 32); r.nblk = K / b; r.block = b;
         r.w_bytes = round_up((size_t)(r.Np / 32) * (K / 64) * 1024, kPackAlign);
-        r.s_bytes = round_up((size_t)(r.Np / 32) * (K / 64) * 256, kPackAlign);
+        r.s_bytes = round_up((size_t)(r.Np / 32) * (K / 64) * (b == 32 ? 512 : 256), kPackAlign);
         *g = r;
         return QGEMM_OK;
     }
@@ -322,14 +323,18 @@ qgemm_status qgemm_pack_weights(int K, int N, qgemm_format f, const void *w_cano
             const int t = n >> 5, c = n & 31;
             for (int b = 0; b < nblk; ++b) {
                 const size_t rec = (size_t)t * nblk + b;
-                // the pair of the block holding 64-block b (one per 64-block
-                // for Block64, the channel's one pair for Block0)
-                const size_t pi = ((size_t)n * g.nblk + (size_t)b * 64 / g.block) * 2;
-                for (int half = 0; half < 2; ++half)
+                for (int half = 0; half < 2; ++half) {
                     std::memcpy(wp + rec * 1024 + (size_t)(32 * half + c) * 16,
                                 wc + (size_t)n * row + (size_t)b * 32 + half * 16, 16);
-                spf[rec * 64 + c * 2 + 0] = pairs_canonical[pi + 0];
-                spf[rec * 64 + c * 2 + 1] = pairs_canonical[pi + 1];
+                    // the pair of the block holding this half (one per 64-block
+                    // for Block64, the channel's one pair for Block0); records
+                    // of 32-element blocks hold one per half
+                    if (g.block != 32 && half == 1) break;
+                    const size_t pi = ((size_t)n * g.nblk + ((size_t)b * 64 + half * 32) / g.block) * 2;
+                    const size_t so = g.block == 32 ? rec * 128 + (32 * half + c) * 2 : rec * 64 + c * 2;
+                    spf[so + 0] = pairs_canonical[pi + 0];
+                    spf[so + 1] = pairs_canonical[pi + 1];
+                }
             }
         }
         break;
@@ -407,12 +412,16 @@ qgemm_status qgemm_unpack_weights(int K, int N, qgemm_format f, const void *w_pa
             const int t = n >> 5, c = n & 31;
             for (int b = 0; b < nblk; ++b) {
                 const size_t rec = (size_t)t * nblk + b;
-                const size_t pi = ((size_t)n * g.nblk + (size_t)b * 64 / g.block) * 2;
-                for (int half = 0; half < 2; ++half)
+                for (int half = 0; half < 2; ++half) {
                     std::memcpy(wc + (size_t)n * row + (size_t)b * 32 + half * 16,
                                 wp + rec * 1024 + (size_t)(32 * half + c) * 16, 16);
-                pairs_canonical[pi + 0] = spf[rec * 64 + c * 2 + 0];   // every 64-block of a block holds it
-                pairs_canonical[pi + 1] = spf[rec * 64 + c * 2 + 1];
+                    if (g.block != 32 && half == 1) break;
+                    // every 64-block of a block holds its pair
+                    const size_t pi = ((size_t)n * g.nblk + ((size_t)b * 64 + half * 32) / g.block) * 2;
+                    const size_t so = g.block == 32 ? rec * 128 + (32 * half + c) * 2 : rec * 64 + c * 2;
+                    pairs_canonical[pi + 0] = spf[so + 0];
+                    pairs_canonical[pi + 1] = spf[so + 1];
+                }
             }
         }
         break;

@@ -31,6 +31,10 @@ constexpr size_t kPackAlign = 256;
 //            a contiguous 64-byte run.
 //   pairs:   256-byte records, record (t, b) at (t * nblk + b) * 256 holding
 //            {offset, scale} of channels 32 t .. 32 t + 31 for block b.
+//            Int4 with 32-element blocks (a pair per half of each 64-block):
+//            512-byte records, entry (h, c) of record (t, b) at
+//            (t * nblk + b) * 512 + (32 h + c) * 8 for K-elements 64 b + 32 h
+//            .. + 31 of channel 32 t + c.
 // INT8_B0, Kp = roundup(K, 64), Np = roundup(N, 4):
 //   weights: [Np][Kp] bytes (canonical rows, zero padded);
 //   pairs:   [Np][2] floats.
@@ -99,16 +103,18 @@ struct Epilogue {
 // arguments and return hipGetLastError() of their launches. C is float or
 // fp16 per the epilogue.
 // ---------------------------------------------------------------------------
+// half_pairs: the pairs are per 32-element half-block (Int4 blocks of 32).
 hipError_t launch_gemv_int4b64(int M, int K, int N, const void *A, const void *Wp,
-                               const void *Sp, void *C, const Epilogue &epi, hipStream_t s);
+                               const void *Sp, void *C, const Epilogue &epi, int half_pairs,
+                               hipStream_t s);
 hipError_t launch_gemv_int8b0(int M, int K, int N, const void *A, const void *Wp,
                               const void *Sp, void *C, const Epilogue &epi, hipStream_t s);
 // Tiled kernels with split-K: nsplit > 1 writes partial tiles to `part`
 // ([nsplit][M][N] fp32) and adds them into C with a fixed-order reduce that
 // applies the epilogue.
 hipError_t launch_gemm_int4b64(int M, int K, int N, const void *A, const void *Wp,
-                               const void *Sp, void *C, const Epilogue &epi, int nsplit,
-                               float *part, hipStream_t s);
+                               const void *Sp, void *C, const Epilogue &epi, int half_pairs,
+                               int nsplit, float *part, hipStream_t s);
 hipError_t launch_splitk_reduce_f32(const float *part, int nsplit, int M, int N, void *C,
                                     const Epilogue &epi, hipStream_t s);
 hipError_t launch_gemm_int8b0(int M, int K, int N, const void *A, const void *Wp,

@@ -245,7 +245,7 @@ __global__ __launch_bounds__(64 * kQWaves) void quantize_kernel(QParams p) {
 // Four weights per lane (K % 4 == 0): lane l of a 256-element chunk j holds
 // k = 256 j + 4 l .. + 3 (one 16-byte load), so a 64-block spans 16 lanes and
 // its reduction four cross-lane steps, and each load moves four times the
-// bytes. G > 0: blocks of 4 G elements (64, 128 or 256), G lanes each, a
+// bytes. G > 0: blocks of 4 G elements (32, 64, 128 or 256), G lanes each, a
 // whole number of them per chunk. G == 0: blocks of whole chunks (a multiple
 // of 256 elements, or all of K), reduced over a first pass and coded in a
 // second. Same arithmetic, same results as quantize_kernel.
@@ -363,6 +363,10 @@ __global__ __launch_bounds__(64 * kQWaves) void quantize_vec_kernel(QParams p) {
                 const int k0 = 256 * j + 4 * lane;
                 if (OUT == QGEMM_F32) {
                     if ((lane & (G - 1)) == 0 && k0 < p.K) pp[(size_t)n * p.nblk + k0 / (4 * G)] = pr;
+                } else if (OUT == QGEMM_INT4_B64 && G == 8) {
+                    // blocks of 32: 512-byte pair records, entry (half, channel)
+                    if ((lane & 7) == 0 && k0 < p.K)
+                        pp[((size_t)(n >> 5) * p.nkc + (k0 >> 6)) * 64 + 32 * ((k0 >> 5) & 1) + (n & 31)] = pr;
                 } else if (OUT == QGEMM_INT4_B64) {
                     // packed as Int4-Block64: the block's pair in each of its 64-block records
                     if ((lane & 15) == 0 && k0 < p.K) pp[((size_t)(n >> 5) * p.nkc + (k0 >> 6)) * 32 + (n & 31)] = pr;
@@ -450,6 +454,7 @@ template <int OUT, int BITS>
 hipError_t launch_vec(const QParams &p, int G, hipStream_t s) {
     const dim3 grid(div_up(p.rows, kQWaves)), block(64 * kQWaves);
     switch (G) {
+    case 8: hipLaunchKernelGGL((quantize_vec_kernel<OUT, BITS, 8>), grid, block, 0, s, p); break;
     case 16: hipLaunchKernelGGL((quantize_vec_kernel<OUT, BITS, 16>), grid, block, 0, s, p); break;
     case 32: hipLaunchKernelGGL((quantize_vec_kernel<OUT, BITS, 32>), grid, block, 0, s, p); break;
     case 64: hipLaunchKernelGGL((quantize_vec_kernel<OUT, BITS, 64>), grid, block, 0, s, p); break;
@@ -489,7 +494,7 @@ hipError_t launch_quantize(int K, int N, qgemm_format f, bool packed, const floa
     if ((K & 3) == 0) {
         // four weights per lane: blocks of 64, 128 or 256 as lane groups, or
         // blocks of whole 256-element chunks (and all of K) over two passes
-        const int G = (g.block == 64 || g.block == 128 || g.block == 256) ? g.block / 4 : 0;
+        const int G = (g.block == 32 || g.block == 64 || g.block == 128 || g.block == 256) ? g.block / 4 : 0;
         if (G > 0 || g.block % 256 == 0 || g.block == K) {
             if (!packed) {
                 if (f == QGEMM_INT8_B0) return launch_vec<QGEMM_F32, 8>(p, G, s);
@@ -500,6 +505,7 @@ hipError_t launch_quantize(int K, int N, qgemm_format f, bool packed, const floa
             return launch_vec<QGEMM_INT4_B64, 4>(p, G, s);
         }
     }
+    if (g.block == 32) return hipErrorInvalidValue;   // K % 64 == 0 always takes the lanes of four
     const bool b64 = g.block == 64;
     if (!packed) {
         if (f == QGEMM_INT8_B0) return launch<QGEMM_F32, 8, false, false>(p, s);
