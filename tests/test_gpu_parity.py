@@ -470,15 +470,22 @@ def test_graph_capture_replays_match_eager():
     result bit for bit. W4A8 goes through qgemm_run_ws (qgemm_run allocates
     its scratch and is not meant for capture)."""
     calls = []
+    # GEMVs (Int4, Int8, W4A8 fused and unfused), tiled GEMMs, and split-K
+    # shapes of every tiled kernel with their reduce (fp32 and W4A8 int32)
     for fmt, M, K, N in [("int4b64", 1, 4096, 1000), ("int4b64", 200, 1024, 300),
                          ("int4b64", 64, 4096, 512),
-                         ("int8b0", 3, 1000, 130), ("w4a8", 100, 640, 256)]:
+                         ("int8b0", 3, 1000, 130), ("w4a8", 100, 640, 256),
+                         ("w4a8", 1, 4096, 512), ("w4a8", 6, 2048, 300), ("w4a8", 40, 3072, 300),
+                         ("int8b0", 32, 2560, 256), ("f16", 9, 4096, 96), ("int4b32", 100, 1024, 300)]:
         A, W, _ = _case(fmt, M, K, N, seed=M + N)
-        q, p = Q.qgemm_quantize_weights(W, fmt)
-        wp, sp = Q.qgemm_pack_weights(K, N, fmt, q, p)
+        if fmt == "f16":
+            wp, sp = Q.qgemm_pack_weights(K, N, fmt, W, None)
+        else:
+            q, p = Q.qgemm_quantize_weights(W, fmt)
+            wp, sp = Q.qgemm_pack_weights(K, N, fmt, q, p)
         nbytes = Q.qgemm_workspace_size(M, K, N, fmt)
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
-        calls.append((fmt, M, K, N, dev(A), dev(wp), dev(sp),
+        calls.append((fmt, M, K, N, dev(A), dev(wp), dev(sp) if sp.size else None,
                       torch.empty((M, N), dtype=torch.float32, device="cuda"), ws, nbytes))
 
     def issue():
