@@ -23,11 +23,6 @@ def dev(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def canonical_from_float(fmt: str, W: np.ndarray):
-    """Library quantiser (host) on float W [N][K] -> canonical (q, pairs)."""
-    return Q.qgemm_quantize_weights(W, fmt)
-
-
 def run(fmt: str, M: int, K: int, N: int, A: np.ndarray, wc: np.ndarray,
         pairs: np.ndarray | None, stream=None, ws: bool = False) -> np.ndarray:
     """Pack on the host, upload, run qgemm_run (or qgemm_run_ws), return C."""

@@ -2,8 +2,11 @@
 fp16, through qgemm_run_ex, against the oracle's product followed by the
 oracle's epilogue (fp16 outputs rounded to nearest even by the oracle).
 
-Every kernel path is covered: both GEMVs, the tiled Int4 / Int8 / fp32 GEMMs,
-the split-K reduce (Int4 and fp32), fp32 K-groups, and W4A8. Tolerances are
+Every kernel path is covered: the GEMVs (Int4, Int8, fp16, W4A8 with and
+without the fused quantiser), the tiled Int4 / Int8 / fp16 / fp32 / W4A8
+GEMMs, every split-K reduce, fp32 K-groups and 32-element Int4 blocks. Both
+sides start from the oracle's quantisation of the seeded weights (the
+library packs it). Tolerances are
 the library's (max-abs 1e-2, relative-Frobenius 2e-3); an fp16 output may
 differ from the oracle's by one fp16 step where the two round values on
 either side of a tie point, which stays inside max-abs for |C| < 16.
@@ -31,7 +34,9 @@ def _gpu():
 SHAPES = [("f32", 16, 256, 256), ("f32", 8, 2560, 1024), ("f32", 130, 512, 200),
           ("int4b64", 1, 4096, 300), ("int4b64", 96, 1024, 300), ("int4b64", 65, 4096, 256),
           ("int8b0", 3, 1000, 130), ("int8b0", 130, 640, 200), ("w4a8", 100, 640, 256),
-          ("f16", 3, 1000, 130), ("f16", 130, 640, 200)]
+          ("f16", 3, 1000, 130), ("f16", 130, 640, 200),
+          ("w4a8", 1, 4096, 300), ("w4a8", 6, 2048, 300), ("w4a8", 40, 3072, 300),
+          ("int8b0", 32, 2560, 256), ("f16", 9, 4096, 96), ("int4b32", 96, 1024, 300)]
 EPILOGUES = [("bias", "silu", "f32", False), ("residual", "gelu", "f16", False),
              ("bias+residual", "relu", "f32", False), ("bias+residual", "gelu", "f16", True),
              ("bias+residual", "none", "f32", True)]
@@ -46,7 +51,7 @@ def _product(fmt, M, K, N, seed):
         wp, sp = Q.qgemm_pack_weights(K, N, fmt, B, None)
         return A, dev(wp), None, O.reference(fmt, A, B=B)
     A = synth.activations(rng, M, K, fp16=True)
-    q, p = Q.qgemm_quantize_weights(synth.normal_weights(rng, N, K), fmt)
+    q, p = O.quantize(synth.normal_weights(rng, N, K), fmt)
     wp, sp = Q.qgemm_pack_weights(K, N, fmt, q, p)
     return A, dev(wp), dev(sp), O.reference(fmt, A, q=q, pairs=p)
 
