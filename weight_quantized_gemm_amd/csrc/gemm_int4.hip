@@ -97,10 +97,12 @@ __device__ __forceinline__ h8_t dequant8(unsigned word, const DqParams &p, unsig
     return o;
 }
 
+// HP: one pair per 32-element half of each 64-block (Int4 blocks of 32).
+template <bool HP>
 __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     int M, int K, int N, int tiles_m, int tiles_n, int xcd_rows,
     const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
-    const float *__restrict__ Sp, void *__restrict__ C, Epilogue epi, int half_pairs) {
+    const float *__restrict__ Sp, void *__restrict__ C, Epilogue epi) {
     __shared__ __align__(16) unsigned char lds[LDS_BYTES];
 
     // ---- tile of this workgroup ----
@@ -186,8 +188,8 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
         for (int cf = 0; cf < CF; ++cf) {
             const size_t rec = b_rec0[cf] + kt;
             codes[cf] = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(Wp + rec * 1024) + lane);
-            pairs[cf] = *reinterpret_cast<const f2_t *>(Sp + (rec << (6 + half_pairs)) +
-                                                        (h << 6) * half_pairs + r * 2);
+            pairs[cf] = *reinterpret_cast<const f2_t *>(HP ? Sp + rec * 128 + h * 64 + r * 2
+                                                           : Sp + rec * 64 + r * 2);
         }
     };
 
@@ -347,10 +349,10 @@ hipError_t launch_gemm_int4b64(int M, int K, int N, const void *A, const void *W
         if (xcd_rows == 0 || fetched < best) { xcd_rows = gr; best = fetched; }
     }
     void *out = nsplit > 1 ? static_cast<void *>(part) : C;
-    hipLaunchKernelGGL(gemm_int4b64_kernel, dim3(tiles_m * tiles_n, nsplit), dim3(64 * NWAVE), 0, s,
+    auto kernel = half_pairs ? gemm_int4b64_kernel<true> : gemm_int4b64_kernel<false>;
+    hipLaunchKernelGGL(kernel, dim3(tiles_m * tiles_n, nsplit), dim3(64 * NWAVE), 0, s,
                        M, K, N, tiles_m, tiles_n, xcd_rows, static_cast<const _Float16 *>(A),
-                       static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), out, epi,
-                       half_pairs);
+                       static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), out, epi);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nsplit <= 1) return e;
     return launch_splitk_reduce_f32(part, nsplit, M, N, C, epi, s);

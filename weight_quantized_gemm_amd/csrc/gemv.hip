@@ -52,10 +52,11 @@ constexpr int TILE_WAVES = 16;
 constexpr int TILE_PASS = 64;                   // K-blocks per pass
 constexpr int TILE_RPW = TILE_PASS / TILE_WAVES;   // blocks per wave and pass
 
-template <int MR, bool ONE_PASS>
+// HP: one pair per 32-element half of each 64-block (Int4 blocks of 32).
+template <int MR, bool ONE_PASS, bool HP>
 __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
     int M, int K, int N, const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
-    const float *__restrict__ Sp, void *__restrict__ C, Epilogue epi, int half_pairs) {
+    const float *__restrict__ Sp, void *__restrict__ C, Epilogue epi) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int nblk = K >> 6;
     const int pmax = min(nblk, TILE_PASS);
@@ -102,8 +103,8 @@ __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
         for (int i = 0; i < TILE_RPW; ++i) {
             const int b = b0 + min(wave + TILE_WAVES * i, pb - 1);
             pr[i] = __builtin_nontemporal_load(
-                reinterpret_cast<const f2_t *>(Sp + (((size_t)t * nblk + b) << (6 + half_pairs)) +
-                                               (h << 6) * half_pairs + c * 2));
+                reinterpret_cast<const f2_t *>(HP ? Sp + ((size_t)t * nblk + b) * 128 + h * 64 + c * 2
+                                                  : Sp + ((size_t)t * nblk + b) * 64 + c * 2));
         }
 #pragma unroll
         for (int i = 0; i < TILE_RPW; ++i) {
@@ -390,23 +391,30 @@ static int rows_per_pass(int M, int K, int kp_bytes_per_row) {
     return mr;
 }
 
-template <int MR>
+template <int MR, bool HP>
 static hipError_t gemv_int4_tile(int M, int K, int N, const void *A, const void *Wp,
-                                 const void *Sp, void *C, const Epilogue &epi, int hp,
-                                 hipStream_t s) {
+                                 const void *Sp, void *C, const Epilogue &epi, hipStream_t s) {
     const int pmax = std::min(K / 64, TILE_PASS);
     const size_t lds = (size_t)MR * pmax * 128 + (size_t)MR * pmax * 16 +
                        (size_t)TILE_WAVES * MR * 32 * sizeof(float);
     dim3 grid(div_up(N, 32), div_up(M, MR));
     if (K <= 64 * TILE_PASS)
-        hipLaunchKernelGGL((gemv_int4b64_tile_kernel<MR, true>), grid, dim3(64 * TILE_WAVES), lds, s,
+        hipLaunchKernelGGL((gemv_int4b64_tile_kernel<MR, true, HP>), grid, dim3(64 * TILE_WAVES), lds, s,
                            M, K, N, static_cast<const _Float16 *>(A),
-                           static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), C, epi, hp);
+                           static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), C, epi);
     else
-        hipLaunchKernelGGL((gemv_int4b64_tile_kernel<MR, false>), grid, dim3(64 * TILE_WAVES), lds, s,
+        hipLaunchKernelGGL((gemv_int4b64_tile_kernel<MR, false, HP>), grid, dim3(64 * TILE_WAVES), lds, s,
                            M, K, N, static_cast<const _Float16 *>(A),
-                           static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), C, epi, hp);
+                           static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), C, epi);
     return hipGetLastError();
+}
+
+template <int MR>
+static hipError_t gemv_int4_tile(int M, int K, int N, const void *A, const void *Wp,
+                                 const void *Sp, void *C, const Epilogue &epi, int hp,
+                                 hipStream_t s) {
+    return hp ? gemv_int4_tile<MR, true>(M, K, N, A, Wp, Sp, C, epi, s)
+              : gemv_int4_tile<MR, false>(M, K, N, A, Wp, Sp, C, epi, s);
 }
 
 hipError_t launch_gemv_int4b64(int M, int K, int N, const void *A, const void *Wp,
