@@ -307,14 +307,38 @@ def time_calls(torch, run, copies: int, steps: int) -> float:
     return e0.elapsed_time(e1) / (reps * copies)
 
 
-def shape_rows(torch, shapes, steps, copies_arg, tag):
+def total_ms(torch, run, copies: int, calls: int = 10) -> float:
+    """Wall time of one eager call and its synchronisation, averaged over
+    `calls` calls (launch, execution and the host's wait: what a caller that
+    waits for each result sees)."""
+    run(0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(calls):
+        run(i % copies)
+        torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / calls
+
+
+def shape_rows(torch, shapes, steps, copies_arg, tag, page_lines=False):
     """One JSON line per (fmt, M, K, N): time per call, rate and the fraction of
-    the bound that applies (HBM for M <= 8, the matrix cores otherwise)."""
+    the bound that applies (HBM for M <= 8, the matrix cores otherwise). With
+    page_lines, a line in the benchmark page's output style instead: the
+    host-timed `total` of a waited call and the event-timed `gpu` time, each
+    with its 2*M*K*N GFLOPS (MNN GemmSpeed page, section "Output format")."""
     for fmt, M, K, N in shapes:
         per = algorithmic_bytes(M, K, N, fmt)
         copies = copies_arg or min(64, max(2, -(-2 * MALL_BYTES // per) + 1))
         w = ShapeWorkload(fmt, M, K, N, copies, seed=K + N + M)
         ms = time_calls(torch, w.run, copies, steps)
+        if page_lines:
+            tot = total_ms(torch, w.run, copies)
+            gf = flops(M, K, N) / 1e6
+            print("%s-gemm M=%d K=%d N=%d total=%.3f ms (%.2f GFLOPS) gpu=%.3f ms (%.2f GFLOPS)"
+                  % ("float" if fmt == "f32" else fmt, M, K, N, tot, gf / tot, ms, gf / ms), flush=True)
+            del w
+            torch.cuda.empty_cache()
+            continue
         fl, by = flops(M, K, N), algorithmic_bytes(M, K, N, fmt)
         if fmt == "w4a8":
             peak, unit = INT8_PEAK_TOPS, "TOP/s"
@@ -367,7 +391,7 @@ def page_grid(args, torch) -> int:
     from weight_quantized_gemm_amd import synth
     shapes = [(fmt, M, K, N) for fmt in args.page_grid.split(",")
               for K, N in synth.PAGE_KN for M in synth.PAGE_M]
-    shape_rows(torch, shapes, args.steps, args.copies, "page_grid")
+    shape_rows(torch, shapes, args.steps, args.copies, "page_grid", page_lines=args.page_lines)
     return 0
 
 
@@ -454,6 +478,8 @@ def main() -> int:
     ap.add_argument("--page-grid", default="", metavar="FORMATS",
                     help="diagnostic: time the benchmark page's default (K, N) x M grid for the "
                          "comma-separated formats (f32,int8b0,int4b64,w4a8), one JSON line each")
+    ap.add_argument("--page-lines", action="store_true",
+                    help="with --page-grid: print the page's total/gpu lines instead of JSON")
     ap.add_argument("--shape", action="append", default=[], metavar="FMT,M,K,N",
                     help="diagnostic: time one shape of one format (repeatable), one JSON line each")
     ap.add_argument("--quantizer", action="append", default=[], metavar="FMT,K,N",
