@@ -377,10 +377,12 @@ def test_w4a8_gemv_debug_bit_exact(M, K, N):
     _w4a8_debug_check(M, K, N, seed=M + K, zero_row=M - 1 if M > 1 else None)
 
 
-@pytest.mark.parametrize("M,K,N", [(9, 3072, 512), (40, 9728, 300), (130, 2560, 250)])
+@pytest.mark.parametrize("M,K,N", [(9, 3072, 512), (40, 9728, 300), (130, 2560, 250), (9, 16000, 64)])
 def test_w4a8_split_k_debug_bit_exact(M, K, N):
     """W4A8 GEMM shapes with few output tiles split K into slices whose int32
-    partial products are added exactly: D stays bit-exact and C matches."""
+    partial products are added exactly: D stays bit-exact and C matches.
+    K of 9728 and 16000 also take the long-row variants of the activation
+    quantiser (24 and 32 chunks per lane), whose qa, sa and S are checked."""
     assert Q.qgemm_workspace_size(M, K, N, "w4a8") > Q.qgemm_workspace_size(M, K, 1, "w4a8")
     _w4a8_debug_check(M, K, N, seed=M + K + N, zero_row=2)
 

@@ -52,7 +52,7 @@ __device__ __forceinline__ void block_sum_store(int v, int *red4, int32_t *dst) 
     if (threadIdx.x == 0) *dst = red4[0] + red4[1] + red4[2] + red4[3];
 }
 
-// K % 8 == 0 and Kq <= 512 * NCH: one wave per row (four rows per
+// K % 8 == 0 and Kq <= 512 * NCH (up to 16384): one wave per row (four rows per
 // workgroup). Every lane requests its NCH 8-element chunks of the row at once,
 // the maximum and the sum are wave reductions (no barrier), and each chunk of
 // codes leaves as one 8-byte store; chunks past K store zeros up to Kq.
@@ -150,6 +150,10 @@ hipError_t launch_w4a8_actquant(int M, int K, int Kq, const void *A, int8_t *qa,
         hipLaunchKernelGGL(w4a8_actquant_wave_kernel<8>, waves4, dim3(256), 0, s, M, K, Kq, a, qa, sa, S);
     else if ((K & 7) == 0 && Kq <= 512 * 16)
         hipLaunchKernelGGL(w4a8_actquant_wave_kernel<16>, waves4, dim3(256), 0, s, M, K, Kq, a, qa, sa, S);
+    else if ((K & 7) == 0 && Kq <= 512 * 24)
+        hipLaunchKernelGGL(w4a8_actquant_wave_kernel<24>, waves4, dim3(256), 0, s, M, K, Kq, a, qa, sa, S);
+    else if ((K & 7) == 0 && Kq <= 512 * 32)
+        hipLaunchKernelGGL(w4a8_actquant_wave_kernel<32>, waves4, dim3(256), 0, s, M, K, Kq, a, qa, sa, S);
     else
         hipLaunchKernelGGL(w4a8_actquant_kernel, dim3(M), dim3(256), 0, s, K, Kq, a, qa, sa, S);
     return hipGetLastError();
