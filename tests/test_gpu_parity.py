@@ -131,6 +131,16 @@ def test_f16_shapes(M):
         _parity("f16", M, K, N, seed=M * 5 + K + N)
 
 
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_int4_gemv_split_k(M):
+    """The Int4 GEMV on shapes with few 32-channel tiles splits K over the
+    workgroups of a tile and adds the partial tiles in a fixed order; ragged N,
+    passes of 64 blocks, Block0 and 32-element blocks included."""
+    for fmt, K, N in [("int4b64", 9728, 2560), ("int4b64", 2560, 1024), ("int4b64", 4096, 300),
+                      ("int4b64", 16384, 70), ("int4b0", 9728, 96), ("int4b32", 9728, 130)]:
+        _parity(fmt, M, K, N, seed=M * 7 + K + N)
+
+
 @pytest.mark.parametrize("M", [1, 3, 8, 9, 64, 65, 129])
 def test_int4_other_block_sizes(M):
     """Int4 with blocks of 32, 128, 256 and 320 K-elements (the page's
@@ -478,7 +488,8 @@ def test_graph_capture_replays_match_eager():
                          ("int4b64", 64, 4096, 512),
                          ("int8b0", 3, 1000, 130), ("w4a8", 100, 640, 256),
                          ("w4a8", 1, 4096, 512), ("w4a8", 6, 2048, 300), ("w4a8", 40, 3072, 300),
-                         ("int8b0", 32, 2560, 256), ("f16", 9, 4096, 96), ("int4b32", 100, 1024, 300)]:
+                         ("int8b0", 32, 2560, 256), ("f16", 9, 4096, 96), ("int4b32", 100, 1024, 300),
+                         ("int4b64", 2, 9728, 640)]:
         A, W, _ = _case(fmt, M, K, N, seed=M + N)
         if fmt == "f16":
             wp, sp = Q.qgemm_pack_weights(K, N, fmt, W, None)

@@ -141,7 +141,8 @@ static qgemm_status run_w4a8(int M, int K, int N, const Geometry &g, const void 
 // callers (run_workspace().bytes) is a function of the shape alone and never
 // smaller than this.
 static size_t used_bytes(const RunWorkspace &r, bool gemv) {
-    return (gemv || r.nsplit <= 1) ? r.w4a8.bytes : r.bytes;
+    const int ns = gemv ? r.gemv_nsplit : r.nsplit;
+    return ns <= 1 ? r.w4a8.bytes : r.bytes;
 }
 
 static qgemm_status dispatch(int M, int K, int N, qgemm_format f, const Geometry &g,
@@ -150,7 +151,7 @@ static qgemm_status dispatch(int M, int K, int N, qgemm_format f, const Geometry
     (void)hipGetLastError();   // start from a clean per-thread error state
     const bool gemv = use_gemv(f, M, K, N);
     const RunWorkspace r = run_workspace(f, M, K, N);
-    const int nsplit = gemv ? 1 : r.nsplit;
+    const int nsplit = gemv ? r.gemv_nsplit : r.nsplit;
     float *part = nsplit > 1 ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + r.part_off)
                              : nullptr;
     switch (kernel_format(f)) {
@@ -158,7 +159,8 @@ static qgemm_status dispatch(int M, int K, int N, qgemm_format f, const Geometry
         return launched(launch_gemm_f32(M, K, N, static_cast<const float *>(A),
                                         static_cast<const float *>(Bq), C, epi, nsplit, part, s));
     case QGEMM_INT4_B64:   // every Int4 format without A8 packs as Int4-Block64
-        return launched(gemv ? launch_gemv_int4b64(M, K, N, A, Bq, scales, C, epi, g.block == 32, s)
+        return launched(gemv ? launch_gemv_int4b64(M, K, N, A, Bq, scales, C, epi, g.block == 32,
+                                                   nsplit, part, s)
                              : launch_gemm_int4b64(M, K, N, A, Bq, scales, C, epi, g.block == 32,
                                                    nsplit, part, s));
     case QGEMM_INT8_B0:

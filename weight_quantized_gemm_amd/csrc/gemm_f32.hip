@@ -123,8 +123,8 @@ __global__ __launch_bounds__(256 * KG) void gemm_f32_kernel(int M, int K, int N,
     // of iterations (a chunk past its share is neither staged nor
     // multiplied: a uniform branch that contains no load)
     const int nch = (K + FK - 1) / FK;
-    const int s0 = (int)((long long)blockIdx.z * nch / gridDim.z);
-    const int s1 = (int)((long long)(blockIdx.z + 1) * nch / gridDim.z);
+    const int s0 = slice_begin(blockIdx.z, nch, gridDim.z);
+    const int s1 = slice_begin(blockIdx.z + 1, nch, gridDim.z);
     const int c0 = s0 + gi * (s1 - s0) / KG, c1 = s0 + (gi + 1) * (s1 - s0) / KG;
     const int npad = ((s1 - s0 + KG - 1) / KG + 1) & ~1;
     const int kend = min(K, c1 * FK);

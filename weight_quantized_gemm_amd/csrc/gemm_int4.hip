@@ -130,8 +130,8 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     const int nblk = K / BK;                       // >= 1
     // split-K: this workgroup's blocks are [KB0, KB1) (all of K when
     // gridDim.y == 1) and its output is partial tile blockIdx.y
-    const int KB0 = (int)((long long)blockIdx.y * nblk / gridDim.y);
-    const int KB1 = (int)((long long)(blockIdx.y + 1) * nblk / gridDim.y);
+    const int KB0 = slice_begin(blockIdx.y, nblk, gridDim.y);
+    const int KB1 = slice_begin(blockIdx.y + 1, nblk, gridDim.y);
     const int nbs = KB1 - KB0;                     // >= 1: the plan keeps gridDim.y <= nblk
     // partial tiles (split-K) and plain fp32 C take the raw store; otherwise
     // every output goes through the epilogue

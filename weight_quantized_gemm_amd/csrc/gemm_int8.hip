@@ -100,8 +100,8 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
     const int wave = uniform(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
     // this workgroup's K-blocks [KB0, KB0 + nblk) (all of them unless split)
-    const int KB0 = (int)((long long)blockIdx.y * (Kp / BK) / gridDim.y);
-    const int nblk = (int)((long long)(blockIdx.y + 1) * (Kp / BK) / gridDim.y) - KB0;
+    const int KB0 = slice_begin(blockIdx.y, Kp / BK, gridDim.y);
+    const int nblk = slice_begin(blockIdx.y + 1, Kp / BK, gridDim.y) - KB0;
     const int n_it = nblk > wave ? (nblk - wave + 3) / 4 : 0;    // K-blocks of this wave
     const int n_pad = (n_it + DEPTH - 1) / DEPTH * DEPTH;          // every wave: same unrolled body
     const int it_last = max(n_it - 1, 0);

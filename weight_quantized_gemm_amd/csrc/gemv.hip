@@ -53,13 +53,19 @@ constexpr int TILE_PASS = 64;                   // K-blocks per pass
 constexpr int TILE_RPW = TILE_PASS / TILE_WAVES;   // blocks per wave and pass
 
 // HP: one pair per 32-element half of each 64-block (Int4 blocks of 32).
-template <int MR, bool ONE_PASS, bool HP>
+// SPLIT: K split over gridDim.z workgroups per tile (its own instantiation:
+// the unsplit kernel keeps 53 registers, so two workgroups share a CU).
+template <int MR, bool ONE_PASS, bool HP, bool SPLIT>
 __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
     int M, int K, int N, const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ Sp, void *__restrict__ C, Epilogue epi) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int nblk = K >> 6;
-    const int pmax = min(nblk, TILE_PASS);
+    // split-K: workgroup z of gridDim.z takes the tile's blocks [KB0, KB1)
+    // (all of them unless split) and then stores a raw partial tile
+    const int KB0 = SPLIT ? slice_begin(blockIdx.z, nblk, gridDim.z) : 0;
+    const int KB1 = SPLIT ? slice_begin(blockIdx.z + 1, nblk, gridDim.z) : nblk;
+    const int pmax = min(SPLIT ? (nblk + (int)gridDim.z - 1) / (int)gridDim.z : nblk, TILE_PASS);
     u4_t *ap = reinterpret_cast<u4_t *>(lds);                                   // [MR][pmax * 8]
     f2_t *hs = reinterpret_cast<f2_t *>(lds + (size_t)MR * pmax * 128);         // [MR][2 pmax]
     float *part = reinterpret_cast<float *>(lds + (size_t)MR * pmax * 128 + (size_t)MR * pmax * 16);
@@ -79,8 +85,8 @@ __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
 
     // ONE_PASS (K <= 4096) compiles the body once without a loop around it,
     // which keeps the single-pass load schedule straight-line
-    for (int b0 = 0; b0 < (ONE_PASS ? 1 : nblk); b0 += TILE_PASS) {   // workgroup-uniform
-        const int pb = min(nblk - b0, TILE_PASS);            // blocks in this pass
+    for (int b0 = KB0; b0 < (ONE_PASS ? KB0 + 1 : KB1); b0 += TILE_PASS) {   // workgroup-uniform
+        const int pb = min(KB1 - b0, TILE_PASS);             // blocks in this pass
         const int nhb = 2 * pb;
         // 1. this pass's activations (one (row, block, half) per thread)
         u4_t araw[4];
@@ -157,7 +163,7 @@ __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
                 acc[r] += fmaf(ce, sv.x, fmaf(co, sv.y, fmaf(sc, Te, sc * 0.0625f * To)));
             }
         }
-        if (!ONE_PASS && b0 + TILE_PASS < nblk) __syncthreads();   // LDS reused by the next pass
+        if (!ONE_PASS && b0 + TILE_PASS < KB1) __syncthreads();   // LDS reused by the next pass
     }
     // 5. halves meet (lanes c and c + 32), then per-wave channel sums to LDS
 #pragma unroll
@@ -176,8 +182,12 @@ __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
 #pragma unroll
         for (int w = 0; w < TILE_WAVES; ++w) total += part[(w * MR + r) * 32 + cc];
         if (n < N && m < M) {
-            if (epi.plain) static_cast<float *>(C)[(size_t)m * N + n] = total;
-            else epi_put(epi, C, m, n, N, total);
+            if (SPLIT)
+                static_cast<float *>(C)[((size_t)blockIdx.z * M + m) * N + n] = total;   // partial tile
+            else if (epi.plain)
+                static_cast<float *>(C)[(size_t)m * N + n] = total;
+            else
+                epi_put(epi, C, m, n, N, total);
         }
     }
 }
@@ -393,39 +403,58 @@ static int rows_per_pass(int M, int K, int kp_bytes_per_row) {
 
 template <int MR, bool HP>
 static hipError_t gemv_int4_tile(int M, int K, int N, const void *A, const void *Wp,
-                                 const void *Sp, void *C, const Epilogue &epi, hipStream_t s) {
-    const int pmax = std::min(K / 64, TILE_PASS);
+                                 const void *Sp, void *C, const Epilogue &epi, int nsplit,
+                                 hipStream_t s) {
+    const int per = div_up(K / 64, nsplit);                // most blocks of a slice
+    const int pmax = std::min(per, TILE_PASS);
     const size_t lds = (size_t)MR * pmax * 128 + (size_t)MR * pmax * 16 +
                        (size_t)TILE_WAVES * MR * 32 * sizeof(float);
-    dim3 grid(div_up(N, 32), div_up(M, MR));
-    if (K <= 64 * TILE_PASS)
-        hipLaunchKernelGGL((gemv_int4b64_tile_kernel<MR, true, HP>), grid, dim3(64 * TILE_WAVES), lds, s,
-                           M, K, N, static_cast<const _Float16 *>(A),
-                           static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), C, epi);
-    else
-        hipLaunchKernelGGL((gemv_int4b64_tile_kernel<MR, false, HP>), grid, dim3(64 * TILE_WAVES), lds, s,
-                           M, K, N, static_cast<const _Float16 *>(A),
-                           static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), C, epi);
+    dim3 grid(div_up(N, 32), div_up(M, MR), nsplit);
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, dim3(64 * TILE_WAVES), lds, s, M, K, N,
+                           static_cast<const _Float16 *>(A), static_cast<const uint8_t *>(Wp),
+                           static_cast<const float *>(Sp), C, epi);
+    };
+    if (nsplit > 1) {
+        if (per <= TILE_PASS) go(gemv_int4b64_tile_kernel<MR, true, HP, true>);
+        else go(gemv_int4b64_tile_kernel<MR, false, HP, true>);
+    } else {
+        if (per <= TILE_PASS) go(gemv_int4b64_tile_kernel<MR, true, HP, false>);
+        else go(gemv_int4b64_tile_kernel<MR, false, HP, false>);
+    }
     return hipGetLastError();
 }
 
 template <int MR>
 static hipError_t gemv_int4_tile(int M, int K, int N, const void *A, const void *Wp,
-                                 const void *Sp, void *C, const Epilogue &epi, int hp,
+                                 const void *Sp, void *C, const Epilogue &epi, int hp, int nsplit,
                                  hipStream_t s) {
-    return hp ? gemv_int4_tile<MR, true>(M, K, N, A, Wp, Sp, C, epi, s)
-              : gemv_int4_tile<MR, false>(M, K, N, A, Wp, Sp, C, epi, s);
+    return hp ? gemv_int4_tile<MR, true>(M, K, N, A, Wp, Sp, C, epi, nsplit, s)
+              : gemv_int4_tile<MR, false>(M, K, N, A, Wp, Sp, C, epi, nsplit, s);
 }
+
+static hipError_t gemv_int4_rows(int M, int K, int N, const void *A, const void *Wp,
+                                 const void *Sp, void *C, const Epilogue &epi, int half_pairs,
+                                 int nsplit, hipStream_t s);
 
 hipError_t launch_gemv_int4b64(int M, int K, int N, const void *A, const void *Wp,
                                const void *Sp, void *C, const Epilogue &epi, int half_pairs,
-                               hipStream_t s) {
+                               int nsplit, float *part, hipStream_t s) {
+    if (nsplit <= 1) return gemv_int4_rows(M, K, N, A, Wp, Sp, C, epi, half_pairs, 1, s);
+    const hipError_t e = gemv_int4_rows(M, K, N, A, Wp, Sp, part, epi, half_pairs, nsplit, s);
+    if (e != hipSuccess) return e;
+    return launch_splitk_reduce_f32(part, nsplit, M, N, C, epi, s);
+}
+
+static hipError_t gemv_int4_rows(int M, int K, int N, const void *A, const void *Wp,
+                                 const void *Sp, void *C, const Epilogue &epi, int half_pairs,
+                                 int nsplit, hipStream_t s) {
     // all rows in one pass (at most 88 KiB of LDS for eight), so the weights stream once
     switch (M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8) {
-    case 8: return gemv_int4_tile<8>(M, K, N, A, Wp, Sp, C, epi, half_pairs, s);
-    case 4: return gemv_int4_tile<4>(M, K, N, A, Wp, Sp, C, epi, half_pairs, s);
-    case 2: return gemv_int4_tile<2>(M, K, N, A, Wp, Sp, C, epi, half_pairs, s);
-    default: return gemv_int4_tile<1>(M, K, N, A, Wp, Sp, C, epi, half_pairs, s);
+    case 8: return gemv_int4_tile<8>(M, K, N, A, Wp, Sp, C, epi, half_pairs, nsplit, s);
+    case 4: return gemv_int4_tile<4>(M, K, N, A, Wp, Sp, C, epi, half_pairs, nsplit, s);
+    case 2: return gemv_int4_tile<2>(M, K, N, A, Wp, Sp, C, epi, half_pairs, nsplit, s);
+    default: return gemv_int4_tile<1>(M, K, N, A, Wp, Sp, C, epi, half_pairs, nsplit, s);
     }
 }
 

@@ -145,12 +145,27 @@ int splitk_plan(qgemm_format f, int M, int K, int N) {
     return sp < 2 ? 1 : (int)sp;
 }
 
+int gemv_split_plan(qgemm_format f, int M, int K, int N) {
+    if (kernel_format(f) != QGEMM_INT4_B64 || M <= 0 || M > kGemvMaxM || N <= 0 || K <= 0) return 1;
+    // one pass over the rows (M <= 8); each slice keeps three or more
+    // 64-blocks per wave (16 waves per tile), since a split costs a second
+    // launch (measured: two per wave lose at K = 4096)
+    const long long tiles = div_up(N, 32);
+    if (tiles >= kSplitTargetCUs / 2) return 1;
+    long long sp = kSplitTargetCUs / tiles;
+    if (sp > kMaxSplit) sp = kMaxSplit;
+    if (sp > K / 64 / 48) sp = K / 64 / 48;
+    return sp < 2 ? 1 : (int)sp;
+}
+
 RunWorkspace run_workspace(qgemm_format f, int M, int K, int N) {
     RunWorkspace r;
     r.w4a8 = f == QGEMM_W4A8 ? w4a8_workspace(M, K) : W4A8Workspace{0, 0, 0, 0, 0};
     r.nsplit = splitk_plan(f, M, K, N);
+    r.gemv_nsplit = gemv_split_plan(f, M, K, N);
+    const int most = r.nsplit > r.gemv_nsplit ? r.nsplit : r.gemv_nsplit;
     r.part_off = round_up(r.w4a8.bytes, kPackAlign);
-    r.part_bytes = r.nsplit > 1 ? round_up((size_t)r.nsplit * M * N * 4, kPackAlign) : 0;
+    r.part_bytes = most > 1 ? round_up((size_t)most * M * N * 4, kPackAlign) : 0;
     r.bytes = r.part_off + r.part_bytes;
     return r;
 }

@@ -34,6 +34,15 @@ __device__ __forceinline__ float dot2(h2_t a, h2_t b, float c) {
     return __builtin_amdgcn_fdot2(a, b, c, false);
 }
 
+// First item of slice z when n items are dealt to Z contiguous slices of
+// near-equal length (z = Z gives n); the split-K kernels' K ranges. 32-bit
+// arithmetic (z <= Z <= 16 and n < 2^27 keep the product exact; a 64-bit
+// division would put hundreds of instructions before a kernel's first
+// load), and none at all for a single slice.
+__device__ __forceinline__ int slice_begin(unsigned z, int n, unsigned Z) {
+    return Z == 1 ? (z == 0 ? 0 : n) : (int)(z * (unsigned)n / Z);
+}
+
 // Wave-uniform value as a scalar (lets the compiler use scalar loads).
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

@@ -104,9 +104,11 @@ struct Epilogue {
 // fp16 per the epilogue.
 // ---------------------------------------------------------------------------
 // half_pairs: the pairs are per 32-element half-block (Int4 blocks of 32).
+// nsplit > 1: K split over nsplit workgroups per tile, partial tiles in
+// `part` ([nsplit][M][N] fp32) added by the fixed-order reduce.
 hipError_t launch_gemv_int4b64(int M, int K, int N, const void *A, const void *Wp,
                                const void *Sp, void *C, const Epilogue &epi, int half_pairs,
-                               hipStream_t s);
+                               int nsplit, float *part, hipStream_t s);
 hipError_t launch_gemv_int8b0(int M, int K, int N, const void *A, const void *Wp,
                               const void *Sp, void *C, const Epilogue &epi, hipStream_t s);
 // Tiled kernels with split-K: nsplit > 1 writes partial tiles to `part`
@@ -179,12 +181,17 @@ int f32_kgroups(int M, int N);
 constexpr int kSplitTargetCUs = 256;
 constexpr int kMaxSplit = 8;
 int splitk_plan(qgemm_format f, int M, int K, int N);      // 1 = no split
+// The same for the Int4 GEMV (M up to the GEMV limit): shapes with few
+// 32-channel tiles split K over the workgroups of a tile.
+int gemv_split_plan(qgemm_format f, int M, int K, int N);
 
 // Full scratch layout of one call: the W4A8 part (if any) first, then the
-// split-K partials [nsplit][M][N] (4 bytes each) when nsplit > 1.
+// split-K partials [S][M][N] (4 bytes each), sized for the larger of the
+// tiled GEMM's plan (nsplit) and the GEMV's (gemv_nsplit), so that the size
+// is a function of the shape alone whichever kernel a call takes.
 struct RunWorkspace {
     W4A8Workspace w4a8;       // bytes == 0 unless W4A8
-    int nsplit;
+    int nsplit, gemv_nsplit;
     size_t part_off, part_bytes, bytes;
 };
 RunWorkspace run_workspace(qgemm_format f, int M, int K, int N);

@@ -224,8 +224,8 @@ __global__ __launch_bounds__(64 * WNW) void w4a8_gemm_kernel(
     // split-K: slice blockIdx.y of gridDim.y takes stages [st0, st0 + nst) of
     // the Kq / WSK (the plan keeps gridDim.y <= Kq / WSK, so nst >= 1)
     const int nst_all = Kq / WSK;
-    const int st0 = (int)((long long)blockIdx.y * nst_all / gridDim.y);
-    const int nst = (int)((long long)(blockIdx.y + 1) * nst_all / gridDim.y) - st0;
+    const int st0 = slice_begin(blockIdx.y, nst_all, gridDim.y);
+    const int nst = slice_begin(blockIdx.y + 1, nst_all, gridDim.y) - st0;
     const int nsteps = (nst + WRING - 1) / WRING * WRING;
     const int ntiles_b = (N + 31) / 32;
 
