@@ -208,10 +208,12 @@ qgemm_status qgemm_unpack_weights(int K, int N, qgemm_format f,
  * (M, K, N, f) alone. It holds, in order: for W4A8 the quantised
  * activations (int8 [M][K rounded up to 128]), the row scales (float [M])
  * and the row sums of the quantised activations (int32 [M]); then, when the
- * shape leaves too few output tiles to fill the GPU and the GEMM therefore
- * splits K into S slices, S partial products ([S][M][N], float; int32 for
- * W4A8) that a second kernel adds in the fixed order 0..S-1 (so results are
- * deterministic). 0 for shapes that need neither.
+ * shape leaves too few output tiles (or, for the Int4 GEMV, too few
+ * 32-channel tiles) to fill the GPU and the kernel therefore splits K into S
+ * slices, S partial products ([S][M][N], float; int32 for W4A8) that a
+ * second kernel adds in the fixed order 0..S-1 (so results are
+ * deterministic). The size covers whichever kernel the shape may take. 0
+ * for shapes that need neither.
  * Errors: ERR_NULL, ERR_FORMAT, ERR_SHAPE.
  */
 qgemm_status qgemm_workspace_size(int M, int K, int N, qgemm_format f,
