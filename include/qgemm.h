@@ -208,8 +208,8 @@ qgemm_status qgemm_unpack_weights(int K, int N, qgemm_format f,
  * (M, K, N, f) alone. It holds, in order: for W4A8 the quantised
  * activations (int8 [M][K rounded up to 128]), the row scales (float [M])
  * and the row sums of the quantised activations (int32 [M]); then, when the
- * shape leaves too few output tiles (or, for the Int4 GEMV, too few
- * 32-channel tiles) to fill the GPU and the kernel therefore splits K into S
+ * shape leaves too few output tiles (or, for the Int4 and W4A8 GEMVs, too
+ * few 32-channel tiles) to fill the GPU and the kernel therefore splits K into S
  * slices, S partial products ([S][M][N], float; int32 for W4A8) that a
  * second kernel adds in the fixed order 0..S-1 (so results are
  * deterministic). The size covers whichever kernel the shape may take. 0
@@ -248,7 +248,8 @@ qgemm_status qgemm_run(int M, int K, int N, qgemm_format f, const void *A,
 /*
  * As qgemm_run, with caller-provided device scratch `workspace` (16-byte
  * aligned) of ws_bytes >= qgemm_workspace_size() bytes (may be NULL when
- * that size is 0, or when the call takes the GEMV, which uses none). The
+ * that size is 0, or when the call touches none of it: a GEMV of a format
+ * other than W4A8 that does not split K). The
  * library allocates nothing. Calls that share a workspace must be ordered
  * (same stream, or synchronised).
  * Errors: as qgemm_run, plus ERR_SIZE for a short workspace.

@@ -387,6 +387,16 @@ def test_w4a8_gemv_debug_bit_exact(M, K, N):
     _w4a8_debug_check(M, K, N, seed=M + K, zero_row=M - 1 if M > 1 else None)
 
 
+@pytest.mark.parametrize("M", [1, 2, 3, 8])
+def test_w4a8_gemv_split_k_debug_bit_exact(M):
+    """The W4A8 GEMV on shapes with few 32-channel tiles: past two rows (and at
+    two rows past K = 8192) the standalone quantiser's codes, int32 partial
+    tiles per K-slice and the exact reduce; one row keeps the fused kernel.
+    D bit-exact, ragged K (a partial last record) and ragged N."""
+    for K, N in [(9728, 2560), (16384, 70), (12350, 130), (6144, 1000)]:
+        _w4a8_debug_check(M, K, N, seed=M * 3 + K + N, zero_row=M - 1 if M > 1 else None)
+
+
 @pytest.mark.parametrize("M,K,N", [(9, 3072, 512), (40, 9728, 300), (130, 2560, 250), (9, 16000, 64)])
 def test_w4a8_split_k_debug_bit_exact(M, K, N):
     """W4A8 GEMM shapes with few output tiles split K into slices whose int32
@@ -489,7 +499,7 @@ def test_graph_capture_replays_match_eager():
                          ("int8b0", 3, 1000, 130), ("w4a8", 100, 640, 256),
                          ("w4a8", 1, 4096, 512), ("w4a8", 6, 2048, 300), ("w4a8", 40, 3072, 300),
                          ("int8b0", 32, 2560, 256), ("f16", 9, 4096, 96), ("int4b32", 100, 1024, 300),
-                         ("int4b64", 2, 9728, 640)]:
+                         ("int4b64", 2, 9728, 640), ("w4a8", 3, 9728, 640)]:
         A, W, _ = _case(fmt, M, K, N, seed=M + N)
         if fmt == "f16":
             wp, sp = Q.qgemm_pack_weights(K, N, fmt, W, None)

@@ -124,9 +124,12 @@ static qgemm_status run_w4a8(int M, int K, int N, const Geometry &g, const void 
     int8_t *qa = reinterpret_cast<int8_t *>(base + w.qa_off);
     float *sa = reinterpret_cast<float *>(base + w.sa_off);
     int32_t *S = reinterpret_cast<int32_t *>(base + w.S_off);
-    if (use_gemv(QGEMM_W4A8, M, K, N))     // quantises the activations itself
+    if (use_gemv(QGEMM_W4A8, M, K, N)) {   // quantises the activations itself unless split
+        const RunWorkspace r = run_workspace(QGEMM_W4A8, M, K, N);
+        int32_t *part = r.gemv_nsplit > 1 ? reinterpret_cast<int32_t *>(base + r.part_off) : nullptr;
         return launched(launch_w4a8_gemv(M, K, N, w.qa_stride, A, qa, sa, S, Bq, scales, C, epi,
-                                         D_debug, s));
+                                         D_debug, r.gemv_nsplit, part, s));
+    }
     hipError_t e = launch_w4a8_actquant(M, K, w.qa_stride, A, qa, sa, S, s);
     if (e != hipSuccess) return QGEMM_ERR_LAUNCH;
     const RunWorkspace r = run_workspace(QGEMM_W4A8, M, K, N);

@@ -146,7 +146,15 @@ int splitk_plan(qgemm_format f, int M, int K, int N) {
 }
 
 int gemv_split_plan(qgemm_format f, int M, int K, int N) {
-    if (kernel_format(f) != QGEMM_INT4_B64 || M <= 0 || M > kGemvMaxM || N <= 0 || K <= 0) return 1;
+    f = kernel_format(f);
+    if ((f != QGEMM_INT4_B64 && f != QGEMM_W4A8) || M <= 0 || M > kGemvMaxM || N <= 0 || K <= 0)
+        return 1;
+    K = (int)round_up((size_t)K, 64);   // W4A8 records cover K rounded up to 64
+    // A split W4A8 GEMV reads the standalone quantiser's codes: not worth it
+    // where the unsplit one quantises inside the kernel (one row, or two rows
+    // up to K = 8192); measured at M = 1, K = 9728, N = 2560: 9.6 us fused,
+    // 13.2 us as quantiser + three slices + reduce.
+    if (f == QGEMM_W4A8 && (M == 1 || (M == 2 && K <= 8192))) return 1;
     // one pass over the rows (M <= 8); each slice keeps three or more
     // 64-blocks per wave (16 waves per tile), since a split costs a second
     // launch (measured: two per wave lose at K = 4096)

@@ -141,9 +141,12 @@ hipError_t launch_w4a8_gemm(int M, int K, int N, int Kq, const int8_t *qa, const
                             int32_t *part, hipStream_t s);
 // M <= 8 (the GEMV limit), K <= kGemvMaxK: quantises A itself (one launch);
 // qa [M][Kq], sa and S are written only with D_debug.
+// nsplit > 1 (shapes with few 32-channel tiles): the standalone quantiser,
+// int32 partial tiles in `part` and the W4A8 reduce.
 hipError_t launch_w4a8_gemv(int M, int K, int N, int Kq, const void *A, int8_t *qa, float *sa,
                             int32_t *S, const void *Wp, const void *Sp, void *C,
-                            const Epilogue &epi, int32_t *D_debug, hipStream_t s);
+                            const Epilogue &epi, int32_t *D_debug, int nsplit, int32_t *part,
+                            hipStream_t s);
 
 // Device quantiser (float W [N][K] -> codes and pairs): canonical layout, or
 // with `packed` the format's packed layout including its zero padding.

@@ -388,7 +388,10 @@ constexpr int WG_WAVES = 16;
 // LDS for MR quantised rows of Kp bytes (the wave partial sums reuse it).
 constexpr size_t kW4A8GemvLds = kGemvLds;
 
-template <int MR, int NREC, bool FUSED, bool DEBUG_D>
+// SPLIT: the tile's records [KC0, KC1) of slice blockIdx.z (gridDim.z
+// slices), and an int32 partial tile into D ([gridDim.z][M][N]) instead of C;
+// only with the standalone quantiser's codes.
+template <int MR, int NREC, bool FUSED, bool DEBUG_D, bool SPLIT>
 __global__ __launch_bounds__(64 * WG_WAVES) void w4a8_gemv_kernel(
     int M, int K, int N, int Kq, int nkc, const _Float16 *__restrict__ A, int8_t *__restrict__ qa,
     float *__restrict__ sa, int32_t *__restrict__ S, const uint8_t *__restrict__ Wp,
@@ -408,6 +411,9 @@ __global__ __launch_bounds__(64 * WG_WAVES) void w4a8_gemv_kernel(
     const int t = blockIdx.x;
     const int m0 = blockIdx.y * MR;
     const int Kp = nkc * 64, npair = K >> 1;
+    static_assert(!(SPLIT && (FUSED || DEBUG_D)), "a split GEMV uses the standalone quantiser");
+    const int KC0 = SPLIT ? slice_begin(blockIdx.z, nkc, gridDim.z) : 0;
+    const int KC1 = SPLIT ? slice_begin(blockIdx.z + 1, nkc, gridDim.z) : nkc;
 
     // 1. this thread's activations (rows past M repeat row M - 1, never
     //    stored), then this wave's records
@@ -419,31 +425,34 @@ __global__ __launch_bounds__(64 * WG_WAVES) void w4a8_gemv_kernel(
 #pragma unroll
         for (int j = 0; j < AP; ++j) ap[j] = arow[min(at + TPR * j, npair - 1)];
     } else {
-        // piece i of the MR code rows: row i / (Kp / 16), bytes 16 (i % (Kp / 16))
-        const int per_row = Kp / 16;
+        // piece i of the MR code rows' records [KC0, KC1): row i / per_row,
+        // bytes 64 KC0 + 16 (i % per_row)
+        const int per_row = 4 * (KC1 - KC0);
 #pragma unroll
         for (int j = 0; j < AP; ++j) {
             const int i = min(tid + 64 * WG_WAVES * j, MR * per_row - 1);
             const int r = i / per_row;
-            qp[j] = *reinterpret_cast<const u4_t *>(qa + (size_t)min(m0 + r, M - 1) * Kq +
+            qp[j] = *reinterpret_cast<const u4_t *>(qa + (size_t)min(m0 + r, M - 1) * Kq + 64 * KC0 +
                                                      16 * (i - r * per_row));
         }
     }
     u4_t rec[NREC];
 #pragma unroll
     for (int i = 0; i < NREC; ++i) {
-        const int kc = min(wave + WG_WAVES * i, nkc - 1);
+        const int kc = min(KC0 + wave + WG_WAVES * i, KC1 - 1);
         rec[i] = __builtin_nontemporal_load(
             reinterpret_cast<const u4_t *>(Wp + ((size_t)t * nkc + kc) * 1024) + lane);
     }
 
     // 2. the codes of the MR rows into LDS
     if (!FUSED) {
-        const int per_row = Kp / 16;
+        const int per_row = 4 * (KC1 - KC0);
 #pragma unroll
         for (int j = 0; j < AP; ++j) {
             const int i = tid + 64 * WG_WAVES * j;
-            if (i < MR * per_row) *reinterpret_cast<u4_t *>(lds + 16 * i) = qp[j];
+            const int r = i / per_row;
+            if (i < MR * per_row)
+                *reinterpret_cast<u4_t *>(lds + r * Kp + 64 * KC0 + 16 * (i - r * per_row)) = qp[j];
         }
         __syncthreads();
     } else {
@@ -508,11 +517,11 @@ __global__ __launch_bounds__(64 * WG_WAVES) void w4a8_gemv_kernel(
     for (int r = 0; r < MR; ++r) acc[r] = 0;
 #pragma unroll
     for (int i = 0; i < NREC; ++i) {
-        const int kc = wave + WG_WAVES * i;
-        const int kk = 64 * min(kc, nkc - 1) + 16 * h;
+        const int kc = KC0 + wave + WG_WAVES * i;
+        const int kk = 64 * min(kc, KC1 - 1) + 16 * h;
         const i4_t b0 = unpack_codes(rec[i][0], rec[i][1]);   // k = 64 kc + 16 h + [0, 16)
         const i4_t b1 = unpack_codes(rec[i][2], rec[i][3]);   // k = 64 kc + 32 + 16 h + [0, 16)
-        if (kc < nkc) {        // uniform; no global load inside
+        if (kc < KC1) {        // uniform; no global load inside
 #pragma unroll
             for (int r = 0; r < MR; ++r) {
                 const i4_t a0 = *reinterpret_cast<const i4_t *>(lds + r * Kp + kk);
@@ -543,6 +552,10 @@ __global__ __launch_bounds__(64 * WG_WAVES) void w4a8_gemv_kernel(
     int d = 0;
 #pragma unroll
     for (int w = 0; w < WG_WAVES; ++w) d += red[(w * MR + r) * 32 + (tid & 31)];
+    if (SPLIT) {
+        D[((size_t)blockIdx.z * M + m) * N + n] = d;      // exact partial; the reduce finishes
+        return;
+    }
     float sa_r;
     int S_r = 0;
     if (FUSED) {
@@ -578,28 +591,33 @@ static void w4a8_gemv_launch(dim3 grid, size_t lds, hipStream_t s, int M, int K,
     const _Float16 *a = static_cast<const _Float16 *>(A);
     const uint8_t *w = static_cast<const uint8_t *>(Wp);
     const f2_t *p = static_cast<const f2_t *>(Sp);
-    if (D)
-        hipLaunchKernelGGL((w4a8_gemv_kernel<MR, NREC, F, true>), grid, dim3(64 * WG_WAVES), lds, s,
+    if (grid.z > 1)            // D is the partial-tile buffer
+        hipLaunchKernelGGL((w4a8_gemv_kernel<MR, NREC, false, false, true>), grid, dim3(64 * WG_WAVES),
+                           lds, s, M, K, N, Kq, nkc, a, qa, sa, S, w, p, C, epi, D);
+    else if (D)
+        hipLaunchKernelGGL((w4a8_gemv_kernel<MR, NREC, F, true, false>), grid, dim3(64 * WG_WAVES), lds, s,
                            M, K, N, Kq, nkc, a, qa, sa, S, w, p, C, epi, D);
     else
-        hipLaunchKernelGGL((w4a8_gemv_kernel<MR, NREC, F, false>), grid, dim3(64 * WG_WAVES), lds, s,
+        hipLaunchKernelGGL((w4a8_gemv_kernel<MR, NREC, F, false, false>), grid, dim3(64 * WG_WAVES), lds, s,
                            M, K, N, Kq, nkc, a, qa, sa, S, w, p, C, epi, D);
 }
 
 template <int MR>
 static hipError_t w4a8_gemv_mr(int M, int K, int N, int Kq, const void *A, int8_t *qa, float *sa,
                                int32_t *S, const void *Wp, const void *Sp, void *C,
-                               const Epilogue &epi, int32_t *D, hipStream_t s) {
+                               const Epilogue &epi, int32_t *D, int nsplit, int32_t *part,
+                               hipStream_t s) {
     const int nkc = (int)round_up(K, 64) / 64;
-    const dim3 grid(div_up(N, 32), div_up(M, MR));
+    const dim3 grid(div_up(N, 32), div_up(M, MR), nsplit);
     const size_t codes = (size_t)MR * nkc * 64, sums = (size_t)WG_WAVES * MR * 32 * sizeof(int);
     const size_t lds = codes > sums ? codes : sums;
-    const int nrec = div_up(nkc, WG_WAVES);   // K <= 16384: at most 16
-    const bool fused = nrec <= 1   ? w4a8_gemv_fused<MR, 1>()
-                       : nrec <= 2 ? w4a8_gemv_fused<MR, 2>()
-                       : nrec <= 4 ? w4a8_gemv_fused<MR, 4>()
-                       : nrec <= 8 ? w4a8_gemv_fused<MR, 8>()
-                                   : w4a8_gemv_fused<MR, 16>();
+    const int nrec = div_up(div_up(nkc, nsplit), WG_WAVES);   // K <= 16384: at most 16
+    const bool fused = nsplit == 1 && (nrec <= 1   ? w4a8_gemv_fused<MR, 1>()
+                                       : nrec <= 2 ? w4a8_gemv_fused<MR, 2>()
+                                       : nrec <= 4 ? w4a8_gemv_fused<MR, 4>()
+                                       : nrec <= 8 ? w4a8_gemv_fused<MR, 8>()
+                                                   : w4a8_gemv_fused<MR, 16>());
+    if (nsplit > 1) D = part;  // the kernel writes partial tiles; the reduce writes C (and D)
     if (!fused) {
         const hipError_t e = launch_w4a8_actquant(M, K, Kq, A, qa, sa, S, s);
         if (e != hipSuccess) return e;
@@ -612,18 +630,45 @@ static hipError_t w4a8_gemv_mr(int M, int K, int N, int Kq, const void *A, int8_
     return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void w4a8_splitk_reduce_kernel(
+    const int32_t *__restrict__ part, int nsplit, int M, int N, const float *__restrict__ sa,
+    const int32_t *__restrict__ S, const f2_t *__restrict__ Sp, void *__restrict__ C, Epilogue epi,
+    int32_t *__restrict__ D);
+static hipError_t launch_w4a8_gemv_rows(int M, int K, int N, int Kq, const void *A, int8_t *qa,
+                                        float *sa, int32_t *S, const void *Wp, const void *Sp,
+                                        void *C, const Epilogue &epi, int32_t *D_debug, int nsplit,
+                                        int32_t *part, hipStream_t s);
+
 hipError_t launch_w4a8_gemv(int M, int K, int N, int Kq, const void *A, int8_t *qa, float *sa,
                             int32_t *S, const void *Wp, const void *Sp, void *C,
-                            const Epilogue &epi, int32_t *D_debug, hipStream_t s) {
+                            const Epilogue &epi, int32_t *D_debug, int nsplit, int32_t *part,
+                            hipStream_t s) {
+    if (nsplit > 1) {
+        hipError_t e = launch_w4a8_gemv_rows(M, K, N, Kq, A, qa, sa, S, Wp, Sp, C, epi, D_debug,
+                                             nsplit, part, s);
+        if (e != hipSuccess) return e;
+        const size_t mn = (size_t)M * N;
+        hipLaunchKernelGGL(w4a8_splitk_reduce_kernel, dim3((unsigned)((mn + 255) / 256)), dim3(256),
+                           0, s, part, nsplit, M, N, sa, S, static_cast<const f2_t *>(Sp), C, epi,
+                           D_debug);
+        return hipGetLastError();
+    }
+    return launch_w4a8_gemv_rows(M, K, N, Kq, A, qa, sa, S, Wp, Sp, C, epi, D_debug, 1, nullptr, s);
+}
+
+static hipError_t launch_w4a8_gemv_rows(int M, int K, int N, int Kq, const void *A, int8_t *qa,
+                                        float *sa, int32_t *S, const void *Wp, const void *Sp,
+                                        void *C, const Epilogue &epi, int32_t *D_debug, int nsplit,
+                                        int32_t *part, hipStream_t s) {
     // rows per pass: up to M (at most 8), as long as their codes fit the LDS
     const size_t Kp = round_up(K, 64);
     int mr = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
     while (mr > 1 && (size_t)mr * Kp > (size_t)kW4A8GemvLds) mr >>= 1;
     switch (mr) {
-    case 1: return w4a8_gemv_mr<1>(M, K, N, Kq, A, qa, sa, S, Wp, Sp, C, epi, D_debug, s);
-    case 2: return w4a8_gemv_mr<2>(M, K, N, Kq, A, qa, sa, S, Wp, Sp, C, epi, D_debug, s);
-    case 4: return w4a8_gemv_mr<4>(M, K, N, Kq, A, qa, sa, S, Wp, Sp, C, epi, D_debug, s);
-    default: return w4a8_gemv_mr<8>(M, K, N, Kq, A, qa, sa, S, Wp, Sp, C, epi, D_debug, s);
+    case 1: return w4a8_gemv_mr<1>(M, K, N, Kq, A, qa, sa, S, Wp, Sp, C, epi, D_debug, nsplit, part, s);
+    case 2: return w4a8_gemv_mr<2>(M, K, N, Kq, A, qa, sa, S, Wp, Sp, C, epi, D_debug, nsplit, part, s);
+    case 4: return w4a8_gemv_mr<4>(M, K, N, Kq, A, qa, sa, S, Wp, Sp, C, epi, D_debug, nsplit, part, s);
+    default: return w4a8_gemv_mr<8>(M, K, N, Kq, A, qa, sa, S, Wp, Sp, C, epi, D_debug, nsplit, part, s);
     }
 }
 
