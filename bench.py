@@ -57,6 +57,8 @@ def algorithmic_bytes(M: int, K: int, N: int, fmt: str = "int4b64", epi: dict | 
         w_bytes, p_bytes = N * K // 2, N * (K // 64) * 8
     elif fmt.startswith("int4b") and fmt != "int4b0":   # Int4 with another block size
         w_bytes, p_bytes = N * K // 2, N * (K // int(fmt[5:])) * 8
+    elif fmt.startswith("int8b"):                        # Int8 with a pair per block
+        w_bytes, p_bytes = K * N, N * (K // int(fmt[5:])) * 8
     else:  # w4a8, int4b0
         w_bytes, p_bytes = N * K // 2, 8 * N
     c_elem = 2 if epi and epi["out"] == "f16" else 4

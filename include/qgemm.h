@@ -28,6 +28,10 @@
  *                   K, and K % 64 == 0; fp16 activations.
  *                   QGEMM_INT4_BLOCK(64) behaves as QGEMM_INT4_B64 and
  *                   QGEMM_INT4_BLOCK(K) as QGEMM_INT4_B0.
+ *   QGEMM_INT8_BLOCK(b)  Int8 (codes 0..255) with one pair per b K-elements,
+ *                   b = 32 or a multiple of 64 that divides K, and
+ *                   K % 64 == 0; fp16 activations. Canonical codes are u8
+ *                   [N][K] as for QGEMM_INT8_B0, pairs [N][K/b][2].
  *
  * Format ids 0-3 equal the page's mode numbers. For every format but F32, A
  * is fp16; C is fp32 (or fp16 through qgemm_run_ex).
@@ -85,11 +89,17 @@ typedef enum qgemm_format {
     QGEMM_W4A8 = 3,
     QGEMM_F16 = 4,
     QGEMM_INT4_B0 = 5,
-    QGEMM_INT4_BLOCK_BASE = 0x10000   /* + b: see QGEMM_INT4_BLOCK */
+    QGEMM_INT4_BLOCK_BASE = 0x10000,  /* + b: see QGEMM_INT4_BLOCK */
+    QGEMM_INT8_BLOCK_BASE = 0x2000000 /* + b: see QGEMM_INT8_BLOCK */
 } qgemm_format;
 
 /* Format id of Int4 weights with one pair per b K-elements. */
 #define QGEMM_INT4_BLOCK(b) ((qgemm_format)(QGEMM_INT4_BLOCK_BASE + (b)))
+/* Format id of Int8 weights (codes 0..255, fp16 activations) with one pair
+ * per b K-elements: the blockSize parameter of the GemmSpeed page ("Why
+ * Conv1x1 is used to measure GEMM") applied to 8-bit codes. b is 32 or a
+ * multiple of 64 that divides K, and K % 64 == 0 (else ERR_FORMAT / ERR_SHAPE). */
+#define QGEMM_INT8_BLOCK(b) ((qgemm_format)(QGEMM_INT8_BLOCK_BASE + (b)))
 
 typedef enum qgemm_status {
     QGEMM_OK = 0,

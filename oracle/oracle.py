@@ -85,8 +85,9 @@ def _check(rc: int, what: str):
         raise ValueError(f"oracle: {what} rejected its arguments")
 
 
-# Format table: name -> (bits, block) ; block None means "all of K". Int4 with
-# any other block size b (the page's blockSize parameter) is named "int4b<b>".
+# Format table: name -> (bits, block) ; block None means "all of K". Int4 or
+# Int8 with any other block size b (the page's blockSize parameter) is named
+# "int4b<b>" or "int8b<b>".
 FORMATS = {"int4b64": (4, 64), "int8b0": (8, None), "w4a8": (4, None), "int4b0": (4, None)}
 
 
@@ -95,6 +96,8 @@ def _bits_block(fmt: str, K: int):
         bits, block = FORMATS[fmt]
     elif fmt.startswith("int4b") and fmt[5:].isdigit():
         bits, block = 4, int(fmt[5:])
+    elif fmt.startswith("int8b") and fmt[5:].isdigit():
+        bits, block = 8, int(fmt[5:])
     else:
         raise ValueError(f"unknown format {fmt}")
     return bits, (K if block is None else block)
@@ -251,7 +254,7 @@ def reference(fmt: str, A, B=None, q=None, pairs=None, lib=None) -> np.ndarray:
         # product of the fp16 values, each widened exactly
         return gemm_f32(np.asarray(A, np.float16).astype(np.float32),
                         np.asarray(B, np.float16).astype(np.float32), lib)
-    if fmt == "int8b0" or (fmt.startswith("int4b") and fmt[5:].isdigit()):
+    if fmt[:5] in ("int4b", "int8b") and fmt[5:].isdigit():
         return gemm_blockq(A, q, pairs, fmt, lib)
     if fmt == "w4a8":
         return w4a8_gemm(A, q, pairs, lib)[0]

@@ -123,7 +123,8 @@ def pin_quantize_roundtrip(lib):
     W = (rng.standard_normal((13, 256)) * 0.02).astype(np.float32)
     W[0, :64] = 0.5                      # a constant Int4 block
     W[1, 5] = 3.0                        # an outlier
-    for fmt, bits, block in [("int4b64", 4, 64), ("int8b0", 8, 256), ("w4a8", 4, 256)]:
+    for fmt, bits, block in [("int4b64", 4, 64), ("int8b0", 8, 256), ("w4a8", 4, 256),
+                             ("int8b64", 8, 64), ("int8b32", 8, 32), ("int4b32", 4, 32)]:
         q, pairs = O.quantize(W, fmt, lib)
         N, K = W.shape
         nb = K // block
@@ -234,7 +235,8 @@ def pin_constant_blocks(lib):
 def pin_blockq_brute_force(lib):
     rng = np.random.default_rng(12)
     cases = [("int4b64", 4, 64, 64, 1, 3), ("int4b64", 4, 64, 128, 3, 5),
-             ("int8b0", 8, None, 12, 2, 4), ("int8b0", 8, None, 64, 3, 2)]
+             ("int8b0", 8, None, 12, 2, 4), ("int8b0", 8, None, 64, 3, 2),
+             ("int8b64", 8, 64, 192, 2, 3), ("int8b32", 8, 32, 96, 3, 2)]
     for fmt, bits, block, K, M, N in cases:
         block = K if block is None else block
         nblk = K // block

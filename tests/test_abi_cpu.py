@@ -177,10 +177,11 @@ def test_sizes():
         Q.qgemm_packed_size(100, 8, "int4b64")
 
 
-@pytest.mark.parametrize("fmt", FMTS + ["int4b32", "int4b128", "int4b192"])
+@pytest.mark.parametrize("fmt", FMTS + ["int4b32", "int4b128", "int4b192", "int8b32", "int8b64",
+                                        "int8b192"])
 @pytest.mark.parametrize("shape", [(1, 64), (5, 128), (70, 192), (33, 1024)])
 def test_quantizer_matches_oracle_bit_exact(fmt, shape):
-    if fmt.startswith("int4b1") and shape[1] % int(fmt[5:]):
+    if fmt[:5] in ("int4b", "int8b") and fmt[5:] not in ("0", "32", "64") and shape[1] % int(fmt[5:]):
         pytest.skip("the block does not divide K")
     N, K = shape
     rng = np.random.default_rng(N * 1000 + K)
@@ -204,11 +205,12 @@ def test_quantizer_rejects_nonfinite():
         Q.qgemm_quantize_weights(np.zeros((4, 64), np.float32), "f32")
 
 
-@pytest.mark.parametrize("fmt", FMTS + ["f32", "int4b32", "int4b128", "int4b320"])
+@pytest.mark.parametrize("fmt", FMTS + ["f32", "int4b32", "int4b128", "int4b320", "int8b32",
+                                        "int8b64", "int8b320"])
 @pytest.mark.parametrize("shape", [(1, 64), (3, 128), (70, 192), (37, 4160)])
 def test_pack_unpack_round_trip(fmt, shape):
     N, K = shape
-    if fmt in ("int4b128", "int4b320") and K % int(fmt[5:]):
+    if fmt in ("int4b128", "int4b320", "int8b320") and K % int(fmt[5:]):
         pytest.skip("the block does not divide K")
     rng = np.random.default_rng(K + N)
     if fmt == "f32":
@@ -224,7 +226,7 @@ def test_pack_unpack_round_trip(fmt, shape):
     if pc is not None:
         assert np.array_equal(p2, pc)
     # padding is zero: the packed buffer holds exactly the canonical content
-    if fmt == "int8b0":
+    if fmt.startswith("int8b"):
         assert int(np.count_nonzero(wp)) == int(np.count_nonzero(wc))
     elif fmt != "f32":
         nz = lambda b: int(np.count_nonzero(b & 15) + np.count_nonzero(b >> 4))
@@ -344,6 +346,41 @@ def test_int4_block_size_validation(lib):
     assert size(256, Q.QGEMM_INT4_BLOCK(-64)) == FMT
     assert Q.qgemm_workspace_size(16, 4096, 256, "int4b128") == \
         Q.qgemm_workspace_size(16, 4096, 256, "int4b64")  # same kernels, same split-K plan
+
+
+def test_int8_block_sizes_layout_golden(lib):
+    """Int8 with block b: codes as channel rows [Np][K] (the Int8-Block0 rows);
+    pairs channel-major, one entry per 64-block repeating the pair of the
+    b-block that holds it (b = 32: one entry per 32-element half)."""
+    N, K = 6, 384
+    wc = (np.arange(N * K, dtype=np.int64) * 7 % 251).astype(np.uint8).reshape(N, K)
+    for b in (32, 64, 128, 384):
+        nb = K // b
+        pc = np.arange(N * nb * 2, dtype=np.float32).reshape(N, nb, 2) + 1
+        wp, sp = Q.qgemm_pack_weights(K, N, f"int8b{b}", wc, pc)
+        Np = 8
+        assert wp.size == -(-Np * K // 256) * 256
+        rows = wp[:Np * K].reshape(Np, K)
+        assert np.array_equal(rows[:N], wc) and not np.any(rows[N:])
+        H = 2 if b == 32 else 1
+        ent = sp.view(np.float32)[:Np * (K // 64) * H * 2].reshape(Np, K // 64 * H, 2)
+        for n in range(N):
+            for e in range(K // 64 * H):
+                k = e * (64 // H)                      # first K-element the entry covers
+                assert list(ent[n, e]) == list(pc[n, k // b])
+        assert not np.any(ent[N:])                     # padding channels
+        assert not np.any(sp.view(np.float32)[Np * (K // 64) * H * 2:])
+    SHAPE, FMT = 2, 3
+    size = lambda K, f: lib.qgemm_packed_size(K, 8, f, ctypes.byref(ctypes.c_size_t()),
+                                              ctypes.byref(ctypes.c_size_t()))
+    assert size(256, Q.QGEMM_INT8_BLOCK(128)) == 0
+    assert size(384, Q.QGEMM_INT8_BLOCK(256)) == SHAPE    # the block must divide K
+    assert size(96, Q.QGEMM_INT8_BLOCK(32)) == SHAPE      # K % 64 == 0
+    assert size(256, Q.QGEMM_INT8_BLOCK(16)) == FMT       # 32 or multiples of 64
+    assert size(256, Q.QGEMM_INT8_BLOCK(96)) == FMT
+    assert size(256, Q.QGEMM_INT8_BLOCK(-64)) == FMT
+    assert Q.qgemm_workspace_size(64, 4096, 512, "int8b64") == \
+        Q.qgemm_workspace_size(64, 4096, 512, "int8b0")   # the channel-row kernel's split-K plan
 
 
 def test_int4_block32_pair_records_golden():

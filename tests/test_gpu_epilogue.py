@@ -37,7 +37,8 @@ SHAPES = [("f32", 16, 256, 256), ("f32", 8, 2560, 1024), ("f32", 130, 512, 200),
           ("f16", 3, 1000, 130), ("f16", 130, 640, 200),
           ("w4a8", 1, 4096, 300), ("w4a8", 6, 2048, 300), ("w4a8", 40, 3072, 300),
           ("int8b0", 32, 2560, 256), ("f16", 9, 4096, 96), ("int4b32", 96, 1024, 300),
-          ("int4b64", 3, 9728, 640), ("w4a8", 2, 9728, 640)]
+          ("int4b64", 3, 9728, 640), ("w4a8", 2, 9728, 640), ("int8b64", 3, 1024, 130),
+          ("int8b32", 130, 640, 200)]
 EPILOGUES = [("bias", "silu", "f32", False), ("residual", "gelu", "f16", False),
              ("bias+residual", "relu", "f32", False), ("bias+residual", "gelu", "f16", True),
              ("bias+residual", "none", "f32", True)]

@@ -152,6 +152,18 @@ def test_int4_other_block_sizes(M):
         _parity(fmt, M, K, N, seed=M * 17 + K + N)
 
 
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 9, 64, 65, 129])
+def test_int8_block_sizes(M):
+    """Int8 with a pair per block of 32, 64, 128, 192 or 320 K-elements: the
+    Int8 GEMV (M <= 4, K <= 8192) adds each 16-code slice with its block's
+    pair; the channel-row GEMM dequantises per weight (split-K shapes, K past
+    the GEMV's limit, ragged N)."""
+    for fmt, K, N in [("int8b64", 64, 5), ("int8b64", 4096, 256), ("int8b32", 2560, 1024),
+                      ("int8b128", 4096, 300), ("int8b320", 640, 130), ("int8b64", 9728, 96),
+                      ("int8b192", 768, 70), ("int8b32", 8192, 40)]:
+        _parity(fmt, M, K, N, seed=M * 19 + K + N)
+
+
 @pytest.mark.parametrize("M", [1, 3, 8, 9, 64, 65, 129])
 def test_int4b0_shapes(M):
     """Int4-Block0 with fp16 activations (per-channel pairs) through the
@@ -499,7 +511,8 @@ def test_graph_capture_replays_match_eager():
                          ("int8b0", 3, 1000, 130), ("w4a8", 100, 640, 256),
                          ("w4a8", 1, 4096, 512), ("w4a8", 6, 2048, 300), ("w4a8", 40, 3072, 300),
                          ("int8b0", 32, 2560, 256), ("f16", 9, 4096, 96), ("int4b32", 100, 1024, 300),
-                         ("int4b64", 2, 9728, 640), ("w4a8", 3, 9728, 640)]:
+                         ("int4b64", 2, 9728, 640), ("w4a8", 3, 9728, 640),
+                         ("int8b64", 2, 4096, 300), ("int8b32", 100, 1024, 300)]:
         A, W, _ = _case(fmt, M, K, N, seed=M + N)
         if fmt == "f16":
             wp, sp = Q.qgemm_pack_weights(K, N, fmt, W, None)

@@ -71,10 +71,15 @@ SHAPES = {
     "int4b128": [(128, 1), (256, 70), (4096, 300)],
     "int4b32": [(64, 1), (128, 70), (4096, 300)],
     "int4b320": [(640, 33), (2560, 40)],
+    "int8b64": [(64, 1), (128, 70), (4096, 300)],
+    "int8b32": [(64, 1), (128, 70), (4096, 300)],
+    "int8b512": [(512, 3), (4096, 70)],
+    "int8b192": [(192, 5), (2304, 40)],
 }
 
 
-@pytest.mark.parametrize("fmt", FMTS + ["int4b32", "int4b128", "int4b320"])
+@pytest.mark.parametrize("fmt", FMTS + ["int4b32", "int4b128", "int4b320", "int8b64", "int8b32",
+                                 "int8b512", "int8b192"])
 def test_device_quantizer_bit_exact(fmt):
     for i, (K, N) in enumerate(SHAPES[fmt]):
         rng = np.random.default_rng(700 + i)
@@ -101,7 +106,7 @@ def _corner_rows(K):
     return np.stack(rows)
 
 
-@pytest.mark.parametrize("fmt", FMTS + ["int4b32", "int4b128"])
+@pytest.mark.parametrize("fmt", FMTS + ["int4b32", "int4b128", "int8b64", "int8b32"])
 def test_device_quantizer_corner_cases(fmt):
     for K in ((128, 256) if fmt == "int4b128" else (64, 256)):
         W = _corner_rows(K)

@@ -97,11 +97,11 @@ static qgemm_status launched(hipError_t e) {
     return e == hipSuccess ? QGEMM_OK : QGEMM_ERR_LAUNCH;
 }
 
-// The Int4 (every block size), Int8-Block0, W4A8 and fp16-weight GEMV kernels
-// serve M <= the current GEMV limit (and K within their register budgets),
-// within each format's own crossover with the tiled MFMA kernels, measured
-// on the benchmark page's shapes: the Int8 GEMV does all its arithmetic on
-// the vector ALUs and loses past 4 rows; the Int4 GEMV loses past 4 rows
+// The Int4 (every block size), Int8 (Block0 and blocked), W4A8 and
+// fp16-weight GEMV kernels serve M <= the current GEMV limit (and K within
+// their register budgets), within each format's own crossover with the tiled
+// MFMA kernels, measured on the benchmark page's shapes: the Int8 GEMV does
+// all its arithmetic on the vector ALUs and loses past 4 rows; the Int4 GEMV loses past 4 rows
 // once M * K * N exceeds about 2^27.6 (the weights are large enough for the
 // split-K GEMM to fill the chip); the fp16 and W4A8 GEMVs win up to 8 rows.
 // Everything else takes a tiled GEMM. A function of the shape alone.
@@ -109,6 +109,7 @@ static bool use_gemv(qgemm_format f, int M, int K, int N) {
     if (M > gemv_max_m()) return false;
     f = kernel_format(f);
     if (f == QGEMM_INT8_B0) return M <= 4 && K <= kGemvMaxK;
+    if (f == QGEMM_INT8_BLOCK_BASE) return M <= 4 && K <= kGemvI8BlkMaxK;
     if (f == QGEMM_INT4_B64)
         return K <= kGemvMaxK && (M <= 4 || (long long)M * K * N <= kGemvInt4MaxMKN);
     if (f == QGEMM_W4A8) return K <= kGemvMaxK;
@@ -169,6 +170,10 @@ static qgemm_status dispatch(int M, int K, int N, qgemm_format f, const Geometry
     case QGEMM_INT8_B0:
         return launched(gemv ? launch_gemv_int8b0(M, K, N, A, Bq, scales, C, epi, s)
                              : launch_gemm_int8b0(M, K, N, A, Bq, scales, C, epi, nsplit, part, s));
+    case QGEMM_INT8_BLOCK_BASE:   // Int8 with a pair per block of K
+        return launched(gemv ? launch_gemv_int8blk(M, K, N, A, Bq, scales, C, epi, g.block == 32, s)
+                             : launch_gemm_int8blk(M, K, N, A, Bq, scales, C, epi, g.block == 32,
+                                                   nsplit, part, s));
     case QGEMM_W4A8:
         return run_w4a8(M, K, N, g, A, Bq, scales, C, epi, ws, s, nullptr);
     case QGEMM_F16:

@@ -1,7 +1,9 @@
 // gemm_int8.hip -- prefill GEMM (M above the GEMV threshold) for weights
 // stored as channel rows [Np][Kp] on the fp16 matrix cores: Int8-Block0
-// codes, or fp16 weights (the float mode at FP16 precision, which the same
-// kernel multiplies as they are, with no pair and no regrouping).
+// codes, fp16 weights (the float mode at FP16 precision, which the same
+// kernel multiplies as they are, with no pair and no regrouping), or Int8
+// codes with a pair per block of K (dequantised per weight in registers, see
+// gemm_rows_kernel's PM mode).
 //
 // What is computed (MNN GemmSpeed benchmark page, section "Why Conv1x1 is
 // used to measure GEMM"): C = A x deq(B), deq(B)[k][n] = offset[n] +
@@ -77,10 +79,25 @@ __device__ __forceinline__ h8_t codes_biased(u2_t codes) {
     return __builtin_bit_cast(h8_t, o);
 }
 
+// 8 fp16 values 1024 + q -> the weights offset + scale * q, each one fp32
+// fused multiply-add x * scale + b (b = offset - 1024 scale, folded once per
+// block) rounded once to fp16.
+__device__ __forceinline__ h8_t dequant8_biased(h8_t x, float scale, float b) {
+    h8_t w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = (_Float16)fmaf((float)x[e], scale, b);
+    return w;
+}
+
 // KMODE: 0: K % 64 == 0 (16-byte loads, no mask); 1: K % 8 == 0 (16-byte
 // loads, pieces past K masked); 2: any K (element loads, masked past K).
 // WF16: the rows hold fp16 weights (2 bytes each) instead of Int8-Block0 codes.
-template <int KMODE, bool WF16>
+// PM (blocked Int8, KMODE 0): the rows hold Int8 codes with a pair per
+// 64-block (PM = 1) or per 32-element half (PM = 2), channel-major; each
+// lane dequantises its 16 codes of a block with their pair (one fused
+// multiply-add per weight, rounded once to fp16) and the MFMAs take the
+// weights, so the epilogue adds no pair term.
+template <int KMODE, bool WF16, int PM = 0>
 __global__ __launch_bounds__(256) void gemm_rows_kernel(
     int M, int K, int N, int Kp, int tiles_n, int xcd_order, const _Float16 *__restrict__ A,
     const uint8_t *__restrict__ Wp, const float *__restrict__ Sp, void *__restrict__ C,
@@ -119,6 +136,21 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
 #pragma unroll
     for (int cf = 0; cf < CF; ++cf)
         b_row[cf] = Wp + ((size_t)min(n0 + cf * 16 + r, N - 1) * Kp + 16 * g) * WB;
+    // PM: this lane's pair entries, channel n0 + 16 cf + r, half g / 2 (PM = 2)
+    constexpr int H = PM == 2 ? 2 : 1;
+    const f2_t *p_row[PM ? CF : 1];
+    if constexpr (PM != 0) {
+#pragma unroll
+        for (int cf = 0; cf < CF; ++cf)
+            p_row[cf] = reinterpret_cast<const f2_t *>(Sp) +
+                        (size_t)min(n0 + cf * 16 + r, N - 1) * (Kp / BK) * H + (PM == 2 ? (g >> 1) : 0);
+    }
+    auto load_p = [&](f2_t (&dst)[PM ? CF : 1], int it) {
+        if constexpr (PM != 0) {
+#pragma unroll
+            for (int cf = 0; cf < CF; ++cf) dst[cf] = p_row[cf][(size_t)(k_of(it) / BK) * H];
+        }
+    };
 
     auto load_a = [&](u4_t (&dst)[A_PIECES], int it) {
         const int k = k_of(it) + 8 * ppc;
@@ -161,11 +193,13 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
 
     u4_t ra[DEPTH][A_PIECES];
     u4_t rb[DEPTH][CF][BV];
+    f2_t rp[DEPTH][PM ? CF : 1];
     if (n_it > 0) {            // a wave with no K-block (K < 256) loads nothing
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
             load_a(ra[d], min(d, it_last));
             load_b(rb[d], min(d, it_last));
+            load_p(rp[d], min(d, it_last));
         }
         // one full wait: the loop header then merges an empty count with the
         // loop's own, and the compiler's in-order count stays exact
@@ -189,6 +223,10 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
                     if constexpr (WF16) {
                         bw[cf][0] = __builtin_bit_cast(h8_t, rb[u][cf][0]);
                         bw[cf][1] = __builtin_bit_cast(h8_t, rb[u][cf][BV - 1]);
+                    } else if constexpr (PM != 0) {
+                        const float sc = rp[u][cf].y, b = fmaf(-1024.0f, sc, rp[u][cf].x);
+                        bw[cf][0] = dequant8_biased(codes_biased(u2_t{rb[u][cf][0][0], rb[u][cf][0][1]}), sc, b);
+                        bw[cf][1] = dequant8_biased(codes_biased(u2_t{rb[u][cf][0][2], rb[u][cf][0][3]}), sc, b);
                     } else {
                         bw[cf][0] = codes_biased(u2_t{rb[u][cf][0][0], rb[u][cf][0][1]});
                         bw[cf][1] = codes_biased(u2_t{rb[u][cf][0][2], rb[u][cf][0][3]});
@@ -196,6 +234,7 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
                 }
                 load_a(ra[u], min(it + DEPTH, it_last));
                 load_b(rb[u], min(it + DEPTH, it_last));
+                load_p(rp[u], min(it + DEPTH, it_last));
                 // 3. two MFMA steps: lane (r, g) takes K-elements 16 g + 8 s .. +7
                 if (it < n_it) {       // uniform; no global load inside
 #pragma unroll
@@ -204,7 +243,7 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
                         for (int rf = 0; rf < RF; ++rf) {
                             const h8_t a = *reinterpret_cast<const h8_t *>(
                                 At + (rf * 16 + r) * AS_STRIDE + 16 * g + 8 * s2);
-                            if constexpr (!WF16) {
+                            if constexpr (!WF16 && PM == 0) {
 #pragma unroll
                                 for (int e = 0; e < 4; ++e)
                                     rs[rf] = dot2(h2_t{a[2 * e], a[2 * e + 1]}, ones, rs[rf]);
@@ -264,7 +303,7 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
         f4_t out;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            if constexpr (WF16) {
+            if constexpr (WF16 || PM != 0) {
                 out[e] = p[e];
             } else {
                 const f2_t pr = *reinterpret_cast<const f2_t *>(Sp + (size_t)min(n0 + c0 + j + e, N - 1) * 2);
@@ -287,7 +326,7 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
     }
 }
 
-template <bool WF16>
+template <bool WF16, int PM = 0>
 static hipError_t launch_rows(int M, int K, int N, const void *A, const void *Wp, const void *Sp,
                               void *C, const Epilogue &epi, int nsplit, float *part,
                               hipStream_t s) {
@@ -302,7 +341,8 @@ static hipError_t launch_rows(int M, int K, int N, const void *A, const void *Wp
                            static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), out,
                            epi);
     };
-    if (K % 64 == 0) launch(gemm_rows_kernel<0, WF16>);
+    if constexpr (PM != 0) launch(gemm_rows_kernel<0, false, PM>);   // K % 64 == 0
+    else if (K % 64 == 0) launch(gemm_rows_kernel<0, WF16>);
     else if (K % 8 == 0) launch(gemm_rows_kernel<1, WF16>);
     else launch(gemm_rows_kernel<2, WF16>);
     const hipError_t e = hipGetLastError();
@@ -319,6 +359,13 @@ hipError_t launch_gemm_int8b0(int M, int K, int N, const void *A, const void *Wp
 hipError_t launch_gemm_f16(int M, int K, int N, const void *A, const void *Wp, void *C,
                            const Epilogue &epi, int nsplit, float *part, hipStream_t s) {
     return launch_rows<true>(M, K, N, A, Wp, nullptr, C, epi, nsplit, part, s);
+}
+
+hipError_t launch_gemm_int8blk(int M, int K, int N, const void *A, const void *Wp,
+                               const void *Sp, void *C, const Epilogue &epi, int half_pairs,
+                               int nsplit, float *part, hipStream_t s) {
+    return half_pairs ? launch_rows<false, 2>(M, K, N, A, Wp, Sp, C, epi, nsplit, part, s)
+                      : launch_rows<false, 1>(M, K, N, A, Wp, Sp, C, epi, nsplit, part, s);
 }
 
 }  // namespace qg

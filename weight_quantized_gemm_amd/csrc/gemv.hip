@@ -204,15 +204,24 @@ __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
 // arithmetic), which keeps the compiler's in-order count of outstanding
 // loads exact. Per channel, sum(a * w) = offset * sum(a) + scale * sum(a * q);
 // sum(a) is formed once per workgroup.
+//
+// Blocked Int8 (PM = 1: a pair per 64-block; PM = 2: per 32-element half,
+// K % 64 == 0): the same regrouping per 16-code slice, whose codes all lie in
+// one block: the slice adds scale * sum(a * (1024 + q)) + (offset - 1024 scale)
+// * sum(a) with its block's pair, sum(a) over the slice's 16 activations
+// coming from per-piece sums staged in LDS with the activations. Each lane
+// requests its slices' pairs (8 bytes, shared by the 4 or 2 lanes of a block)
+// with its codes.
 constexpr int I8_WAVES = 16;
 
-template <int MR, int NCH>
+template <int MR, int NCH, int PM>
 __global__ __launch_bounds__(64 * I8_WAVES) void gemv_int8b0_kernel(
     int M, int K, int N, int Kp, const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
     const f2_t *__restrict__ Sp, void *__restrict__ C, Epilogue epi) {
     extern __shared__ __align__(16) unsigned char lds[];
     _Float16 *As = reinterpret_cast<_Float16 *>(lds);                      // [MR][Kp], zero past K
     float *ssum = reinterpret_cast<float *>(lds + (size_t)MR * Kp * 2);    // [MR][I8_WAVES]
+    float *psum = ssum + MR * I8_WAVES;                                    // PM: [MR][Kp / 8]
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = uniform(tid >> 6);
@@ -230,7 +239,17 @@ __global__ __launch_bounds__(64 * I8_WAVES) void gemv_int8b0_kernel(
         wq[i] = __builtin_nontemporal_load(
             reinterpret_cast<const u4_t *>(Wp + (size_t)nc * Kp + (size_t)ci * 16));
     }
-    const f2_t pr = Sp[nc];
+    // slice ci's pair: entry ci >> SH of the channel's nchunk >> SH entries
+    constexpr int SH = PM == 2 ? 1 : 2;
+    f2_t pb[PM ? NCH : 1];
+    if constexpr (PM != 0) {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int ci = min(lane + 64 * i, nchunk - 1);
+            pb[i] = Sp[(size_t)nc * (nchunk >> SH) + (ci >> SH)];
+        }
+    }
+    const f2_t pr = PM ? f2_t{0.f, 0.f} : Sp[nc];
 
     // 2. activations to LDS (zero past K), and their row sums
     float part[MR];
@@ -248,6 +267,7 @@ __global__ __launch_bounds__(64 * I8_WAVES) void gemv_int8b0_kernel(
             float sp = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) sp = dot2(as_h2(v[i]), one, sp);
+            if (PM) psum[p] = sp;            // p = r * pieces + c
 #pragma unroll
             for (int rr = 0; rr < MR; ++rr) part[rr] += (rr == r) ? sp : 0.f;
         }
@@ -277,6 +297,9 @@ __global__ __launch_bounds__(64 * I8_WAVES) void gemv_int8b0_kernel(
     for (int i = 0; i < NCH; ++i) {
         const int ci = lane + 64 * i;
         if (ci >= nchunk) break;
+        float Ts[MR];                        // PM: this slice's sum(a * (1024 + q))
+#pragma unroll
+        for (int r = 0; r < MR; ++r) Ts[r] = 0.f;
 #pragma unroll
         for (int wi = 0; wi < 4; ++wi) {
             const unsigned word = wq[i][wi];
@@ -286,8 +309,17 @@ __global__ __launch_bounds__(64 * I8_WAVES) void gemv_int8b0_kernel(
 #pragma unroll
             for (int r = 0; r < MR; ++r) {
                 const u2_t av = *reinterpret_cast<const u2_t *>(As + (size_t)r * Kp + ci * 16 + wi * 4);
-                T[r] = dot2(x0, as_h2(av.x), T[r]);
-                T[r] = dot2(x1, as_h2(av.y), T[r]);
+                float &t = PM ? Ts[r] : T[r];
+                t = dot2(x0, as_h2(av.x), t);
+                t = dot2(x1, as_h2(av.y), t);
+            }
+        }
+        if constexpr (PM != 0) {
+            const float c1b = fmaf(-1024.0f, pb[i].y, pb[i].x);
+#pragma unroll
+            for (int r = 0; r < MR; ++r) {
+                const float2 ps = *reinterpret_cast<const float2 *>(psum + (size_t)r * (Kp >> 3) + 2 * ci);
+                T[r] = fmaf(pb[i].y, Ts[r], fmaf(c1b, ps.x + ps.y, T[r]));
             }
         }
     }
@@ -303,7 +335,7 @@ __global__ __launch_bounds__(64 * I8_WAVES) void gemv_int8b0_kernel(
             float sa = 0.f;
 #pragma unroll
             for (int w = 0; w < I8_WAVES; ++w) sa += ssum[r * I8_WAVES + w];
-            const float out = fmaf(c1, sa, pr.y * v);
+            const float out = PM ? v : fmaf(c1, sa, pr.y * v);
             if (epi.plain) static_cast<float *>(C)[(size_t)(m0 + r) * N + n] = out;
             else epi_put(epi, C, m0 + r, n, N, out);
         }
@@ -458,38 +490,54 @@ static hipError_t gemv_int4_rows(int M, int K, int N, const void *A, const void 
     }
 }
 
-template <int MR, int NCH>
+template <int MR, int NCH, int PM>
 static hipError_t gemv_int8_mr(int M, int K, int N, int Kp, const void *A, const void *Wp,
                                const void *Sp, void *C, const Epilogue &epi, hipStream_t s) {
     dim3 grid(div_up(N, I8_WAVES), div_up(M, MR));
-    const size_t lds = (size_t)MR * Kp * sizeof(_Float16) + (size_t)MR * I8_WAVES * sizeof(float);
-    hipLaunchKernelGGL((gemv_int8b0_kernel<MR, NCH>), grid, dim3(64 * I8_WAVES), lds, s, M, K, N,
-                       Kp, static_cast<const _Float16 *>(A), static_cast<const uint8_t *>(Wp),
+    const size_t lds = (size_t)MR * Kp * sizeof(_Float16) + (size_t)MR * I8_WAVES * sizeof(float) +
+                       (PM ? (size_t)MR * (Kp / 8) * sizeof(float) : 0);
+    hipLaunchKernelGGL((gemv_int8b0_kernel<MR, NCH, PM>), grid, dim3(64 * I8_WAVES), lds, s, M, K,
+                       N, Kp, static_cast<const _Float16 *>(A), static_cast<const uint8_t *>(Wp),
                        static_cast<const f2_t *>(Sp), C, epi);
     return hipGetLastError();
 }
 
-template <int MR>
+template <int MR, int PM>
 static hipError_t gemv_int8_k(int M, int K, int N, int Kp, const void *A, const void *Wp,
                               const void *Sp, void *C, const Epilogue &epi, hipStream_t s) {
-    // slices per lane: Kp / 1024, rounded up to a power of two (K <= 16384)
+    // slices per lane: Kp / 1024, rounded up to a power of two (K <= 16384;
+    // blocked Int8: K <= 8192, eight slices and their pairs)
     const int nch = div_up(Kp, 1024);
-    if (nch <= 1) return gemv_int8_mr<MR, 1>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
-    if (nch <= 2) return gemv_int8_mr<MR, 2>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
-    if (nch <= 4) return gemv_int8_mr<MR, 4>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
-    if (nch <= 8) return gemv_int8_mr<MR, 8>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
-    return gemv_int8_mr<MR, 16>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
+    if (nch <= 1) return gemv_int8_mr<MR, 1, PM>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
+    if (nch <= 2) return gemv_int8_mr<MR, 2, PM>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
+    if (nch <= 4) return gemv_int8_mr<MR, 4, PM>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
+    if (PM || nch <= 8) return gemv_int8_mr<MR, 8, PM>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
+    return gemv_int8_mr<MR, 16, 0>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
+}
+
+template <int PM>
+static hipError_t gemv_int8_rows(int M, int K, int N, const void *A, const void *Wp,
+                                 const void *Sp, void *C, const Epilogue &epi, hipStream_t s) {
+    const int Kp = (int)round_up(K, 64);
+    // the dispatcher sends at most four rows here (the tiled kernel wins
+    // above); per row: the fp16 activations, and the piece sums when blocked
+    switch (rows_per_pass(M < 4 ? M : 4, K, Kp * 2 + (PM ? Kp / 2 : 0))) {
+    case 4: return gemv_int8_k<4, PM>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
+    case 2: return gemv_int8_k<2, PM>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
+    default: return gemv_int8_k<1, PM>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
+    }
 }
 
 hipError_t launch_gemv_int8b0(int M, int K, int N, const void *A, const void *Wp,
                               const void *Sp, void *C, const Epilogue &epi, hipStream_t s) {
-    const int Kp = (int)round_up(K, 64);
-    // the dispatcher sends at most four rows here (the tiled kernel wins above)
-    switch (rows_per_pass(M < 4 ? M : 4, K, Kp * 2)) {
-    case 4: return gemv_int8_k<4>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
-    case 2: return gemv_int8_k<2>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
-    default: return gemv_int8_k<1>(M, K, N, Kp, A, Wp, Sp, C, epi, s);
-    }
+    return gemv_int8_rows<0>(M, K, N, A, Wp, Sp, C, epi, s);
+}
+
+hipError_t launch_gemv_int8blk(int M, int K, int N, const void *A, const void *Wp,
+                               const void *Sp, void *C, const Epilogue &epi, int half_pairs,
+                               hipStream_t s) {
+    return half_pairs ? gemv_int8_rows<2>(M, K, N, A, Wp, Sp, C, epi, s)
+                      : gemv_int8_rows<1>(M, K, N, A, Wp, Sp, C, epi, s);
 }
 
 template <int MR, int NCH>

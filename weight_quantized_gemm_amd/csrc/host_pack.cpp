@@ -16,7 +16,7 @@ namespace qg {
 
 static bool valid_format(int f) {
     return f == QGEMM_F32 || f == QGEMM_INT4_B64 || f == QGEMM_INT8_B0 || f == QGEMM_W4A8 ||
-           f == QGEMM_F16 || f == QGEMM_INT4_B0 || is_int4_blocked(f);
+           f == QGEMM_F16 || f == QGEMM_INT4_B0 || is_int4_blocked(f) || is_int8_blocked(f);
 }
 
 // Shapes are capped so that every element count and byte offset the kernels
@@ -44,6 +44,21 @@ qgemm_status geometry(int K, int N, qgemm_format f, Geometry *g) {
         r.Kp = K; r.Np = (int)round_up(N, 32); r.nblk = K / b; r.block = b;
         r.w_bytes = round_up((size_t)(r.Np / 32) * (K / 64) * 1024, kPackAlign);
         r.s_bytes = round_up((size_t)(r.Np / 32) * (K / 64) * (b == 32 ? 512 : 256), kPackAlign);
+        *g = r;
+        return QGEMM_OK;
+    }
+    if (is_int8_blocked(f)) {
+        // Int8 with one pair per b K-elements: channel rows of codes [Np][K]
+        // (as Int8-Block0) and the pairs channel-major with one entry per
+        // 64-block, repeated over the 64-blocks of a block (blocks of 32: one
+        // per 32-element half)
+        const int b = f - QGEMM_INT8_BLOCK_BASE;
+        if (b != 32 && b % 64 != 0) return QGEMM_ERR_FORMAT;
+        if (K == 0 || K % b != 0 || K % 64 != 0) return QGEMM_ERR_SHAPE;
+        r.Kp = K; r.Np = (int)round_up(N, 4); r.nblk = K / b; r.block = b;
+        r.w_bytes = round_up((size_t)r.Np * K, kPackAlign);
+        r.s_bytes = round_up((size_t)r.Np * (K / 64) * (b == 32 ? 2 : 1) * 2 * sizeof(float),
+                             kPackAlign);
         *g = r;
         return QGEMM_OK;
     }
@@ -126,6 +141,7 @@ int splitk_plan(qgemm_format f, int M, int K, int N) {
     }
     case QGEMM_INT8_B0:
     case QGEMM_F16:
+    case QGEMM_INT8_BLOCK_BASE:
         // four waves, two or more 64-blocks each
         tiles = (long long)div_up(M, kRowsTileM) * div_up(N, kRowsTileN);
         kunits = (int)(round_up((size_t)K, 64) / 64) / 8;
@@ -179,10 +195,11 @@ RunWorkspace run_workspace(qgemm_format f, int M, int K, int N) {
 }
 
 static size_t canonical_q_bytes(const Geometry &g, qgemm_format f) {
-    switch (f) {
+    switch (kernel_format(f)) {
     case QGEMM_F32: return (size_t)g.K * g.N * sizeof(float);
     case QGEMM_F16: return (size_t)g.K * g.N * 2;
-    case QGEMM_INT8_B0: return (size_t)g.N * g.K;
+    case QGEMM_INT8_B0:
+    case QGEMM_INT8_BLOCK_BASE: return (size_t)g.N * g.K;
     default: return (size_t)g.N * (g.K / 2);
     }
 }
@@ -268,7 +285,7 @@ qgemm_status qgemm_quantize_weights(int K, int N, qgemm_format f, const float *W
     for (size_t i = 0; i < total; ++i)
         if (!std::isfinite(W[i])) return QGEMM_ERR_VALUE;
 
-    const int bits = (f == QGEMM_INT8_B0) ? 8 : 4;
+    const int bits = (f == QGEMM_INT8_B0 || is_int8_blocked(f)) ? 8 : 4;
     const int block = g.block;
     const int nblk = K / block;
     const int qmax = (1 << bits) - 1;
@@ -369,6 +386,22 @@ qgemm_status qgemm_pack_weights(int K, int N, qgemm_format f, const void *w_cano
             spf[(size_t)n * 2 + 1] = pairs_canonical[(size_t)n * 2 + 1];
         }
         break;
+    case QGEMM_INT8_BLOCK_BASE: {
+        // entry (n, 64-block b, half h) = pair of the block holding
+        // k = 64 b + 32 h
+        const int H = g.block == 32 ? 2 : 1, nb = K / 64;
+        for (int n = 0; n < N; ++n) {
+            std::memcpy(wp + (size_t)n * K, wc + (size_t)n * K, (size_t)K);
+            for (int b = 0; b < nb; ++b)
+                for (int h = 0; h < H; ++h) {
+                    const size_t pi = ((size_t)n * g.nblk + ((size_t)b * 64 + h * 32) / g.block) * 2;
+                    const size_t so = (((size_t)n * nb + b) * H + h) * 2;
+                    spf[so + 0] = pairs_canonical[pi + 0];
+                    spf[so + 1] = pairs_canonical[pi + 1];
+                }
+        }
+        break;
+    }
     case QGEMM_W4A8: {
         // 1 KiB records (g, kc) of 32 channels x 64 codes; piece 32 h + c
         // (16 bytes) holds channel 32 g + c's codes of k = 64 kc + 32 s +
@@ -456,6 +489,20 @@ qgemm_status qgemm_unpack_weights(int K, int N, qgemm_format f, const void *w_pa
             pairs_canonical[(size_t)n * 2 + 1] = spf[(size_t)n * 2 + 1];
         }
         break;
+    case QGEMM_INT8_BLOCK_BASE: {
+        // each block's pair from the first entry it covers
+        const int H = g.block == 32 ? 2 : 1, nb = K / 64;
+        for (int n = 0; n < N; ++n) {
+            std::memcpy(wc + (size_t)n * K, wp + (size_t)n * K, (size_t)K);
+            for (int j = 0; j < g.nblk; ++j) {
+                const size_t k = (size_t)j * g.block;
+                const size_t so = (((size_t)n * nb + k / 64) * H + (k % 64) / 32) * 2;
+                pairs_canonical[((size_t)n * g.nblk + j) * 2 + 0] = spf[so + 0];
+                pairs_canonical[((size_t)n * g.nblk + j) * 2 + 1] = spf[so + 1];
+            }
+        }
+        break;
+    }
     case QGEMM_W4A8: {
         const int nkc = g.Kp / 64;
         const size_t row = (size_t)K / 2;

@@ -68,15 +68,24 @@ constexpr int kMaxBlock = 1 << 24;
 inline bool is_int4_blocked(int f) {
     return f > QGEMM_INT4_BLOCK_BASE && f <= QGEMM_INT4_BLOCK_BASE + kMaxBlock;
 }
+// Int8 with a block size in the format id (QGEMM_INT8_BLOCK(b)).
+inline bool is_int8_blocked(int f) {
+    return f > QGEMM_INT8_BLOCK_BASE && f <= QGEMM_INT8_BLOCK_BASE + kMaxBlock;
+}
 // The format the kernels see: every Int4 weight format (Block64, Block0 and
 // the other block sizes) is packed as Int4-Block64, its pairs repeated in
-// each 64-block of their block.
+// each 64-block of their block; every blocked Int8 format is packed as
+// channel rows of codes with a pair per 64-block (per 32-element half for
+// blocks of 32), named QGEMM_INT8_BLOCK_BASE here.
 inline qgemm_format kernel_format(qgemm_format f) {
-    return (f == QGEMM_INT4_B0 || is_int4_blocked(f)) ? QGEMM_INT4_B64 : f;
+    if (f == QGEMM_INT4_B0 || is_int4_blocked(f)) return QGEMM_INT4_B64;
+    if (is_int8_blocked(f)) return QGEMM_INT8_BLOCK_BASE;
+    return f;
 }
 
 constexpr int kGemvMaxM = 8;          // largest M the GEMV kernels take
 constexpr int kGemvF16MaxK = 8192;   // fp16-weight GEMV: 16 slices of 8 per lane
+constexpr int kGemvI8BlkMaxK = 8192; // blocked Int8 GEMV: eight code slices and pairs per lane
 constexpr int kGemvMaxK = 16384;      // A rows staged in LDS: MR * K * 2 bytes
 // Largest M * K * N the Int4 GEMV takes for 5..8 rows (above it the tiled
 // kernel is faster).
@@ -111,6 +120,14 @@ hipError_t launch_gemv_int4b64(int M, int K, int N, const void *A, const void *W
                                int nsplit, float *part, hipStream_t s);
 hipError_t launch_gemv_int8b0(int M, int K, int N, const void *A, const void *Wp,
                               const void *Sp, void *C, const Epilogue &epi, hipStream_t s);
+// Blocked Int8: channel rows [Np][K] of codes and pairs [Np][K/64][H] (H = 2
+// with half_pairs, blocks of 32; else 1), K % 64 == 0.
+hipError_t launch_gemv_int8blk(int M, int K, int N, const void *A, const void *Wp,
+                               const void *Sp, void *C, const Epilogue &epi, int half_pairs,
+                               hipStream_t s);
+hipError_t launch_gemm_int8blk(int M, int K, int N, const void *A, const void *Wp,
+                               const void *Sp, void *C, const Epilogue &epi, int half_pairs,
+                               int nsplit, float *part, hipStream_t s);
 // Tiled kernels with split-K: nsplit > 1 writes partial tiles to `part`
 // ([nsplit][M][N] fp32) and adds them into C with a fixed-order reduce that
 // applies the epilogue.

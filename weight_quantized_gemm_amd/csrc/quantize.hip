@@ -115,7 +115,7 @@ __device__ inline void store_codes(const QParams &p, int n, int kc, int lane, in
         const size_t rec = (size_t)(n >> 5) * p.nkc + kc;
         if ((lane & 7) == 0)
             *reinterpret_cast<uint32_t *>(p.q + rec * 1024 + (size_t)(32 * h + (n & 31)) * 16 + 4 * w) = x;
-    } else if (OUT == QGEMM_INT8_B0) {
+    } else if (OUT == QGEMM_INT8_B0 || OUT == QGEMM_INT8_BLOCK_BASE) {
         const uint32_t x = group_or((uint32_t)code << (8 * (lane & 3)), 4);
         if ((lane & 3) == 0)
             *reinterpret_cast<uint32_t *>(p.q + (size_t)n * p.kp + k) = x;
@@ -169,8 +169,9 @@ __global__ __launch_bounds__(64 * kQWaves) void quantize_kernel(QParams p) {
                 const int code = (live && !bad) ? code_of(v[u], pr, rcp, qmax) : 0;
                 store_codes<OUT, BITS>(p, n, kc, lane, code);
                 if (lane == 0) {
-                    const size_t pi = OUT == QGEMM_F32 ? (size_t)n * p.nkc + kc
-                                                       : ((size_t)(n >> 5) * p.nkc + kc) * 32 + (n & 31);
+                    const size_t pi = (OUT == QGEMM_F32 || OUT == QGEMM_INT8_BLOCK_BASE)
+                                          ? (size_t)n * p.nkc + kc
+                                          : ((size_t)(n >> 5) * p.nkc + kc) * 32 + (n & 31);
                     reinterpret_cast<float2 *>(p.pairs)[pi] = pr;
                 }
             }
@@ -232,6 +233,9 @@ __global__ __launch_bounds__(64 * kQWaves) void quantize_kernel(QParams p) {
         float2 *pp = reinterpret_cast<float2 *>(p.pairs);
         if (OUT == QGEMM_F32) {
             if (lane == 0) pp[(size_t)n * p.nblk + blk] = pr;
+        } else if (REPEAT && OUT == QGEMM_INT8_BLOCK_BASE) {
+            // blocked Int8: the pair in every 64-block entry of the block
+            for (int b = c0 + lane; b < c1; b += 64) pp[(size_t)n * p.nkc + b] = pr;
         } else if (REPEAT) {
             // packed as Int4-Block64: the pair in every 64-block record of the block
             for (int b = c0 + lane; b < c1; b += 64) pp[((size_t)(n >> 5) * p.nkc + b) * 32 + (n & 31)] = pr;
@@ -291,7 +295,7 @@ __device__ inline void store_codes4(const QParams &p, int n, int j, int lane, co
         if (k0 < p.K)
             *reinterpret_cast<uint16_t *>(p.q + rec * 1024 + (size_t)(32 * h + (n & 31)) * 16 + (o & 31) / 2) =
                 (uint16_t)(c[0] | c[1] << 4 | c[2] << 8 | c[3] << 12);
-    } else if (OUT == QGEMM_INT8_B0) {
+    } else if (OUT == QGEMM_INT8_B0 || OUT == QGEMM_INT8_BLOCK_BASE) {
         if (k0 < p.kp)
             *reinterpret_cast<uint32_t *>(p.q + (size_t)n * p.kp + k0) =
                 (uint32_t)c[0] | (uint32_t)c[1] << 8 | (uint32_t)c[2] << 16 | (uint32_t)c[3] << 24;
@@ -363,6 +367,13 @@ __global__ __launch_bounds__(64 * kQWaves) void quantize_vec_kernel(QParams p) {
                 const int k0 = 256 * j + 4 * lane;
                 if (OUT == QGEMM_F32) {
                     if ((lane & (G - 1)) == 0 && k0 < p.K) pp[(size_t)n * p.nblk + k0 / (4 * G)] = pr;
+                } else if (OUT == QGEMM_INT8_BLOCK_BASE && G == 8) {
+                    // blocked Int8, blocks of 32: entry (channel, 64-block, half)
+                    if ((lane & 7) == 0 && k0 < p.K)
+                        pp[((size_t)n * p.nkc + (k0 >> 6)) * 2 + ((k0 >> 5) & 1)] = pr;
+                } else if (OUT == QGEMM_INT8_BLOCK_BASE) {
+                    // blocked Int8: the block's pair in each of its 64-block entries
+                    if ((lane & 15) == 0 && k0 < p.K) pp[(size_t)n * p.nkc + (k0 >> 6)] = pr;
                 } else if (OUT == QGEMM_INT4_B64 && G == 8) {
                     // blocks of 32: 512-byte pair records, entry (half, channel)
                     if ((lane & 7) == 0 && k0 < p.K)
@@ -440,6 +451,10 @@ __global__ __launch_bounds__(64 * kQWaves) void quantize_vec_kernel(QParams p) {
         }
         if (OUT == QGEMM_F32) {
             if (lane == 0) pp[(size_t)n * p.nblk + blk] = pr;
+        } else if (OUT == QGEMM_INT8_BLOCK_BASE) {
+            // blocked Int8: the pair in every 64-block entry of the block
+            const int b0 = blk * (p.block / 64), b1 = min(b0 + p.block / 64, p.nkc);
+            for (int b = b0 + lane; b < b1; b += 64) pp[(size_t)n * p.nkc + b] = pr;
         } else if (OUT == QGEMM_INT4_B64) {
             // packed as Int4-Block64: the pair in every 64-block record of the block
             const int b0 = blk * (p.block / 64), b1 = min(b0 + p.block / 64, p.nkc);
@@ -486,10 +501,11 @@ hipError_t launch_quantize(int K, int N, qgemm_format f, bool packed, const floa
     p.kp = g.Kp;
     p.q = static_cast<uint8_t *>(q);
     p.pairs = pairs;
-    if (packed && f == QGEMM_INT8_B0) {
-        // the packed pair buffer is padded to its alignment past the Np pairs
-        p.tail_off = g.Np * 2;
-        p.tail_len = (int)(g.s_bytes / sizeof(float)) - g.Np * 2;
+    const bool i8blk = kernel_format(f) == QGEMM_INT8_BLOCK_BASE;
+    if (packed && (f == QGEMM_INT8_B0 || i8blk)) {
+        // the packed pair buffer is padded to its alignment past the last pair
+        p.tail_off = f == QGEMM_INT8_B0 ? g.Np * 2 : g.Np * p.nkc * (g.block == 32 ? 2 : 1) * 2;
+        p.tail_len = (int)(g.s_bytes / sizeof(float)) - p.tail_off;
     }
     if ((K & 3) == 0) {
         // four weights per lane: blocks of 64, 128 or 256 as lane groups, or
@@ -497,10 +513,11 @@ hipError_t launch_quantize(int K, int N, qgemm_format f, bool packed, const floa
         const int G = (g.block == 32 || g.block == 64 || g.block == 128 || g.block == 256) ? g.block / 4 : 0;
         if (G > 0 || g.block % 256 == 0 || g.block == K) {
             if (!packed) {
-                if (f == QGEMM_INT8_B0) return launch_vec<QGEMM_F32, 8>(p, G, s);
+                if (f == QGEMM_INT8_B0 || i8blk) return launch_vec<QGEMM_F32, 8>(p, G, s);
                 return launch_vec<QGEMM_F32, 4>(p, G, s);
             }
             if (f == QGEMM_INT8_B0) return launch_vec<QGEMM_INT8_B0, 8>(p, G, s);
+            if (i8blk) return launch_vec<QGEMM_INT8_BLOCK_BASE, 8>(p, G, s);
             if (f == QGEMM_W4A8) return launch_vec<QGEMM_W4A8, 4>(p, G, s);
             return launch_vec<QGEMM_INT4_B64, 4>(p, G, s);
         }
@@ -508,11 +525,12 @@ hipError_t launch_quantize(int K, int N, qgemm_format f, bool packed, const floa
     if (g.block == 32) return hipErrorInvalidValue;   // K % 64 == 0 always takes the lanes of four
     const bool b64 = g.block == 64;
     if (!packed) {
-        if (f == QGEMM_INT8_B0) return launch<QGEMM_F32, 8, false, false>(p, s);
+        if (f == QGEMM_INT8_B0 || i8blk) return launch<QGEMM_F32, 8, false, false>(p, s);
         return b64 ? launch<QGEMM_F32, 4, true, false>(p, s)
                    : launch<QGEMM_F32, 4, false, false>(p, s);   // W4A8 and the other Int4 blocks
     }
     if (f == QGEMM_INT8_B0) return launch<QGEMM_INT8_B0, 8, false, false>(p, s);
+    if (i8blk) return launch<QGEMM_INT8_BLOCK_BASE, 8, false, true>(p, s);   // blocks of 64 x odd > 1
     if (f == QGEMM_W4A8) return launch<QGEMM_W4A8, 4, false, false>(p, s);
     return b64 ? launch<QGEMM_INT4_B64, 4, true, false>(p, s)
                : launch<QGEMM_INT4_B64, 4, false, true>(p, s);   // Int4-Block0, other blocks

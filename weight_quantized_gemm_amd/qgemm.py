@@ -97,6 +97,7 @@ class Epilogue(ctypes.Structure):
 
 
 QGEMM_INT4_BLOCK_BASE = 0x10000
+QGEMM_INT8_BLOCK_BASE = 0x2000000
 
 
 def QGEMM_INT4_BLOCK(b: int) -> int:
@@ -104,16 +105,29 @@ def QGEMM_INT4_BLOCK(b: int) -> int:
     return QGEMM_INT4_BLOCK_BASE + b
 
 
+def QGEMM_INT8_BLOCK(b: int) -> int:
+    """Format id of Int8 weights with one pair per b K-elements."""
+    return QGEMM_INT8_BLOCK_BASE + b
+
+
 def _fmt(f) -> int:
-    """Format id from a name ("int4b64", "int8b0", ..., "int4b<b>" for any other
-    Int4 block size b) or an id."""
+    """Format id from a name ("int4b64", "int8b0", ..., "int4b<b>" / "int8b<b>"
+    for any other Int4 / Int8 block size b) or an id."""
     if not isinstance(f, str):
         return int(f)
     if f in FORMATS:
         return FORMATS[f]
     if f.startswith("int4b") and f[5:].isdigit():
         return QGEMM_INT4_BLOCK(int(f[5:]))
+    if f.startswith("int8b") and f[5:].isdigit() and int(f[5:]) > 0:
+        return QGEMM_INT8_BLOCK(int(f[5:]))
     raise ValueError(f"unknown format {f}")
+
+
+def is_int8(fmt) -> bool:
+    """Whether a format stores one byte per code (Int8-Block0 and blocked Int8)."""
+    f = _fmt(fmt)
+    return f == QGEMM_INT8_B0 or f > QGEMM_INT8_BLOCK_BASE
 
 
 def pairs_per_channel(fmt, K: int) -> int:
@@ -121,6 +135,8 @@ def pairs_per_channel(fmt, K: int) -> int:
     f = _fmt(fmt)
     if f == QGEMM_INT4_B64:
         return K // 64
+    if f > QGEMM_INT8_BLOCK_BASE:
+        return K // (f - QGEMM_INT8_BLOCK_BASE)
     if f > QGEMM_INT4_BLOCK_BASE:
         return K // (f - QGEMM_INT4_BLOCK_BASE)
     return 1
@@ -194,7 +210,7 @@ def qgemm_quantize_weights(W: np.ndarray, fmt):
     _check(load().qgemm_quantize_weights(K, N, _fmt(fmt), _np_ptr(W), _np_ptr(q), qb,
                                          _np_ptr(pairs), pf), "qgemm_quantize_weights")
     f = _fmt(fmt)
-    qshape = (N, K) if f == QGEMM_INT8_B0 else (N, K // 2)
+    qshape = (N, K) if is_int8(f) else (N, K // 2)
     return q.reshape(qshape), pairs.reshape(N, pairs_per_channel(f, K), 2)
 
 
@@ -270,7 +286,7 @@ def qgemm_quantize_weights_device(W, fmt, q=None, pairs=None, stream=None):
         pairs = torch.empty(max(pf, 1), dtype=torch.float32, device=W.device)
     _check(load().qgemm_quantize_weights_device(K, N, f, _dev_ptr(W), _dev_ptr(q), _dev_ptr(pairs),
                                                 _stream(stream)), "qgemm_quantize_weights_device")
-    qshape = (N, K) if f == QGEMM_INT8_B0 else (N, K // 2)
+    qshape = (N, K) if is_int8(f) else (N, K // 2)
     return q[:qb].view(qshape), pairs[:pf].view(N, pairs_per_channel(f, K), 2)
 
 
