@@ -498,8 +498,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {args.gpus}); "
-              "multi-GPU sharding is described in the design notes but not built.",
+        print(f"bench.py: the library runs on exactly one GPU (asked for --gpus {args.gpus}); "
+              "sharding over several GPUs is described in the design notes, not implemented.",
               file=sys.stderr)
         return 2
 
