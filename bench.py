@@ -631,7 +631,7 @@ def main() -> int:
         },
         "decode_roofline": {
             "bound": "hbm",
-            "kernel": "gemv_int4b64_tile_kernel (decode M=1 K=4096 N=11008)",
+            "kernel": "gemv_int4b64_half_kernel (decode M=1 K=4096 N=11008)",
             "achieved": dec_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
