@@ -337,8 +337,9 @@ qgemm_status qgemm_w4a8_debug(int M, int K, int N, const void *A,
 
 /*
  * Sets the largest M that may take a GEMV kernel (below it each format keeps
- * its own crossover: Int8-Block0 up to 4 rows, the Int4 formats up to 4 rows
- * or up to 8 while M * K * N <= 3 * 2^26, fp16 and W4A8 up to 8 rows)
+ * its own crossover: Int8 up to 4 rows, the Int4 formats up to 4 rows or up
+ * to 8 while M * K * N <= 2^29 (K <= 4096) or 3 * 2^26 (larger K), fp16 and
+ * W4A8 up to 8 rows)
  * (0..8; default 8, or the QGEMM_GEMV_MAX_M environment variable read at
  * first use) and returns the previous value; a value outside 0..8 is
  * ignored and only the current value returned. Affects only which kernel

@@ -101,9 +101,11 @@ static qgemm_status launched(hipError_t e) {
 // fp16-weight GEMV kernels serve M <= the current GEMV limit (and K within
 // their register budgets), within each format's own crossover with the tiled
 // MFMA kernels, measured on the benchmark page's shapes: the Int8 GEMV does
-// all its arithmetic on the vector ALUs and loses past 4 rows; the Int4 GEMV loses past 4 rows
-// once M * K * N exceeds about 2^27.6 (the weights are large enough for the
-// split-K GEMM to fill the chip); the fp16 and W4A8 GEMVs win up to 8 rows.
+// all its arithmetic on the vector ALUs and loses past 4 rows; the Int4 GEMV
+// loses past 4 rows once M * K * N exceeds about 2^27.6 for K > 4096, or 2^29
+// for K <= 4096 (the half-tile kernel; 8 x 4096 x 16384 is a tie), where the
+// weights are large enough for the split-K GEMM to fill the chip; the fp16
+// and W4A8 GEMVs win up to 8 rows.
 // Everything else takes a tiled GEMM. A function of the shape alone.
 static bool use_gemv(qgemm_format f, int M, int K, int N) {
     if (M > gemv_max_m()) return false;
@@ -111,7 +113,8 @@ static bool use_gemv(qgemm_format f, int M, int K, int N) {
     if (f == QGEMM_INT8_B0) return M <= 4 && K <= kGemvMaxK;
     if (f == QGEMM_INT8_BLOCK_BASE) return M <= 4 && K <= kGemvI8BlkMaxK;
     if (f == QGEMM_INT4_B64)
-        return K <= kGemvMaxK && (M <= 4 || (long long)M * K * N <= kGemvInt4MaxMKN);
+        return K <= kGemvMaxK &&
+               (M <= 4 || (long long)M * K * N <= (K <= 4096 ? kGemvInt4HalfMaxMKN : kGemvInt4MaxMKN));
     if (f == QGEMM_W4A8) return K <= kGemvMaxK;
     if (f == QGEMM_F16) return K <= kGemvF16MaxK;
     return false;

@@ -19,6 +19,7 @@
 // activations, so no per-weight subtract is needed; v_dot2_f32_f16 forms the
 // products with fp32 accumulation.
 #include <algorithm>
+#include <type_traits>
 
 #include "kernels_common.h"
 #include "qgemm_internal.h"
@@ -192,45 +193,52 @@ __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
     }
 }
 
-// One row, K <= 4096 (one pass), no split: a 512-thread workgroup per 16
-// channels, half of a 32-channel tile, so a shape has twice as many
-// workgroups of half the bytes and they spread more evenly over the CUs
-// (11008 channels: 688 half tiles, at most 3 per CU against an average of
-// 2.7, instead of 344 tiles at most 2 per CU against 1.3; 4096 channels: all
-// 256 CUs instead of 128). Lane (c, h, j) = (lane % 16, lane / 16 % 2,
-// lane / 32) takes channel c of the half, K-half h of block 2 (w + 8 i) + j
-// in step i of wave w: one load instruction covers the 16 channels' pieces of
-// both halves of two blocks (four 256-byte runs). The three lanes of each
-// channel meet by one exchange across 16 lanes and one v_permlane32_swap; the
-// eight waves in LDS in a fixed order.
+// MR <= 8 rows (one pass over them), K <= 4096 (one pass over K), no split:
+// a 512-thread workgroup per 16 channels, half of a 32-channel tile, so a
+// shape has twice as many workgroups of half the bytes and they spread more
+// evenly over the CUs (11008 channels: 688 half tiles, at most 3 per CU
+// against an average of 2.7, instead of 344 tiles at most 2 per CU against
+// 1.3; 4096 channels: all 256 CUs instead of 128). Lane (c, h, j) =
+// (lane % 16, lane / 16 % 2, lane / 32) takes channel c of the half, K-half h
+// of block 2 (w + 8 i) + j in step i of wave w: one load instruction covers
+// the 16 channels' pieces of both halves of two blocks (four 256-byte runs).
+// The four lanes of each channel meet by one exchange across 16 lanes and one
+// v_permlane32_swap; the eight waves in LDS in a fixed order.
 constexpr int HALF_WAVES = 8;
 
-template <bool HP>
+template <int MR, bool HP>
 __global__ __launch_bounds__(64 * HALF_WAVES) void gemv_int4b64_half_kernel(
-    int K, int N, const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
+    int M, int K, int N, const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ Sp, void *__restrict__ C, Epilogue epi) {
     extern __shared__ __align__(16) unsigned char lds[];
-    const int nblk = K >> 6;                                              // 1 .. 64
-    u4_t *ap = reinterpret_cast<u4_t *>(lds);                             // [nblk * 8]
-    f2_t *hs = reinterpret_cast<f2_t *>(lds + (size_t)nblk * 128);        // [2 nblk]
-    float *part = reinterpret_cast<float *>(lds + (size_t)nblk * 144);    // [HALF_WAVES][16]
+    constexpr int AS = (MR * 128 + 64 * HALF_WAVES - 1) / (64 * HALF_WAVES);   // staging slots per thread
+    const int nblk = K >> 6;                                                  // 1 .. 64
+    u4_t *ap = reinterpret_cast<u4_t *>(lds);                                 // [MR][nblk * 8]
+    f2_t *hs = reinterpret_cast<f2_t *>(lds + (size_t)MR * nblk * 128);       // [MR][2 nblk]
+    float *part = reinterpret_cast<float *>(lds + (size_t)MR * nblk * 144);   // [HALF_WAVES][MR][16]
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = uniform(tid >> 6);
     const int t = blockIdx.x >> 1;                   // 32-channel tile
+    const int m0 = blockIdx.y * MR;
     const int c16 = lane & 15, h = (lane >> 4) & 1, j = lane >> 5;
     const int c = (blockIdx.x & 1) * 16 + c16;       // channel within the tile
     const unsigned magic = 0x64646464u;
     const int nhb = 2 * nblk;
 
-    // 1. the activations (one (block, half) per thread), then every pair and
-    //    record load of this wave, unconditional from clamped block indices
-    u4_t araw[4];
-    const bool alive = tid < nhb;
-    {
-        const u4_t *src = reinterpret_cast<const u4_t *>(A + (size_t)(alive ? tid : 0) * 32);
+    // 1. the activations (one (row, block, half) per thread and slot), then
+    //    every pair and record load of this wave, unconditional from clamped
+    //    block indices
+    u4_t araw[AS][4];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) araw[w] = alive ? src[w] : u4_t{0u, 0u, 0u, 0u};
+    for (int sl = 0; sl < AS; ++sl) {
+        const int idx = tid + 64 * HALF_WAVES * sl;
+        const int ar = idx / nhb, ahb = idx - ar * nhb;
+        const bool alive = ar < MR && m0 + ar < M;
+        const u4_t *src = reinterpret_cast<const u4_t *>(
+            A + (size_t)(alive ? m0 + ar : 0) * K + (size_t)(alive ? ahb : 0) * 32);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) araw[sl][w] = alive ? src[w] : u4_t{0u, 0u, 0u, 0u};
     }
     f2_t pr[TILE_RPW];
     u4_t wq[TILE_RPW];
@@ -248,27 +256,34 @@ __global__ __launch_bounds__(64 * HALF_WAVES) void gemv_int4b64_half_kernel(
             reinterpret_cast<const u4_t *>(Wp + ((size_t)t * nblk + b) * 1024) + 32 * h + c);
     }
 
-    // 2. activations to LDS in decode pair order, with even / odd sums
-    if (alive) {
-        float se = 0.f, so = 0.f;
+    // 2. activations to LDS in decode pair order, with even / odd sums (rows
+    //    past M are staged as zeros and never stored)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const u4_t v = araw[w];
-            const h2_t p01 = as_h2(v.x), p23 = as_h2(v.y), p45 = as_h2(v.z), p67 = as_h2(v.w);
-            const h2_t e0 = {p01.x, p45.x}, e1 = {p23.x, p67.x};
-            const h2_t o0 = {p01.y, p45.y}, o1 = {p23.y, p67.y};
-            const h2_t one = {(_Float16)1.0f, (_Float16)1.0f};
-            se = dot2(e1, one, dot2(e0, one, se));
-            so = dot2(o1, one, dot2(o0, one, so));
-            ap[tid * 4 + w] = u4_t{as_u(e0), as_u(e1), as_u(o0), as_u(o1)};
+    for (int sl = 0; sl < AS; ++sl) {
+        const int idx = tid + 64 * HALF_WAVES * sl;
+        if (idx < MR * nhb) {
+            float se = 0.f, so = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const u4_t v = araw[sl][w];
+                const h2_t p01 = as_h2(v.x), p23 = as_h2(v.y), p45 = as_h2(v.z), p67 = as_h2(v.w);
+                const h2_t e0 = {p01.x, p45.x}, e1 = {p23.x, p67.x};
+                const h2_t o0 = {p01.y, p45.y}, o1 = {p23.y, p67.y};
+                const h2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+                se = dot2(e1, one, dot2(e0, one, se));
+                so = dot2(o1, one, dot2(o0, one, so));
+                ap[idx * 4 + w] = u4_t{as_u(e0), as_u(e1), as_u(o0), as_u(o1)};
+            }
+            hs[idx] = f2_t{se, so};            // idx = row * nhb + half-block
         }
-        hs[tid] = f2_t{se, so};
     }
     __syncthreads();
 
     // 3. decode and accumulate; a lane whose block lies past K (odd block
     //    count) computes on the clamped block and adds zero
-    float acc = 0.f;
+    float acc[MR];
+#pragma unroll
+    for (int r = 0; r < MR; ++r) acc[r] = 0.f;
 #pragma unroll
     for (int i = 0; i < TILE_RPW; ++i) {
         const int bl = 2 * (wave + HALF_WAVES * i) + j;
@@ -277,38 +292,45 @@ __global__ __launch_bounds__(64 * HALF_WAVES) void gemv_int4b64_half_kernel(
         const float off = pr[i].x, sc = pr[i].y;
         const float ce = fmaf(-1024.0f, sc, off);
         const float co = fmaf(-64.0f, sc, off);
-        float Te = 0.f, To = 0.f;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const u4_t av = ap[hbg * 4 + d];
-            const unsigned word = wq[i][d];
-            const unsigned y0 = __builtin_amdgcn_perm(magic, word, 0x04020400u);
-            const unsigned y1 = __builtin_amdgcn_perm(magic, word, 0x04030401u);
-            Te = dot2(as_h2(y0 & 0xFF0FFF0Fu), as_h2(av.x), Te);
-            Te = dot2(as_h2(y1 & 0xFF0FFF0Fu), as_h2(av.y), Te);
-            To = dot2(as_h2(y0 & 0xFFF0FFF0u), as_h2(av.z), To);
-            To = dot2(as_h2(y1 & 0xFFF0FFF0u), as_h2(av.w), To);
+        for (int r = 0; r < MR; ++r) {
+            float Te = 0.f, To = 0.f;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const u4_t av = ap[((size_t)r * nhb + hbg) * 4 + d];
+                const unsigned word = wq[i][d];
+                const unsigned y0 = __builtin_amdgcn_perm(magic, word, 0x04020400u);
+                const unsigned y1 = __builtin_amdgcn_perm(magic, word, 0x04030401u);
+                Te = dot2(as_h2(y0 & 0xFF0FFF0Fu), as_h2(av.x), Te);
+                Te = dot2(as_h2(y1 & 0xFF0FFF0Fu), as_h2(av.y), Te);
+                To = dot2(as_h2(y0 & 0xFFF0FFF0u), as_h2(av.z), To);
+                To = dot2(as_h2(y1 & 0xFFF0FFF0u), as_h2(av.w), To);
+            }
+            const f2_t sv = hs[(size_t)r * nhb + hbg];
+            const float v = fmaf(ce, sv.x, fmaf(co, sv.y, fmaf(sc, Te, sc * 0.0625f * To)));
+            acc[r] += bl < nblk ? v : 0.f;
         }
-        const f2_t sv = hs[hbg];
-        const float v = fmaf(ce, sv.x, fmaf(co, sv.y, fmaf(sc, Te, sc * 0.0625f * To)));
-        acc += bl < nblk ? v : 0.f;
     }
 
     // 4. the K-halves (lanes c and c + 16), then the block parities (lanes
     //    l and l + 32), then the waves in a fixed order
-    float x = acc + __shfl_xor(acc, 16);
-    float y = x;
-    swap32(x, y);
-    if (lane < 16) part[wave * 16 + c16] = x + y;
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+        float x = acc[r] + __shfl_xor(acc[r], 16);
+        float y = x;
+        swap32(x, y);
+        if (lane < 16) part[(wave * MR + r) * 16 + c16] = x + y;
+    }
     __syncthreads();
-    if (tid < 16) {
-        const int n = 32 * t + (blockIdx.x & 1) * 16 + tid;
+    if (tid < MR * 16) {
+        const int r = tid >> 4, cc = tid & 15;
+        const int n = 32 * t + (blockIdx.x & 1) * 16 + cc, m = m0 + r;
         float total = 0.f;
 #pragma unroll
-        for (int w = 0; w < HALF_WAVES; ++w) total += part[w * 16 + tid];
-        if (n < N) {
-            if (epi.plain) static_cast<float *>(C)[n] = total;
-            else epi_put(epi, C, 0, n, N, total);
+        for (int w = 0; w < HALF_WAVES; ++w) total += part[(w * MR + r) * 16 + cc];
+        if (n < N && m < M) {
+            if (epi.plain) static_cast<float *>(C)[(size_t)m * N + n] = total;
+            else epi_put(epi, C, m, n, N, total);
         }
     }
 }
@@ -602,17 +624,27 @@ hipError_t launch_gemv_int4b64(int M, int K, int N, const void *A, const void *W
 static hipError_t gemv_int4_rows(int M, int K, int N, const void *A, const void *Wp,
                                  const void *Sp, void *C, const Epilogue &epi, int half_pairs,
                                  int nsplit, hipStream_t s) {
-    if (M == 1 && K <= 64 * TILE_PASS && nsplit <= 1) {
-        // one row, one pass: half tiles
-        const size_t lds = (size_t)(K / 64) * 144 + (size_t)HALF_WAVES * 16 * sizeof(float);
-        auto go = [&](auto kernel) {
-            hipLaunchKernelGGL(kernel, dim3(div_up(N, 16)), dim3(64 * HALF_WAVES), lds, s, K, N,
-                               static_cast<const _Float16 *>(A), static_cast<const uint8_t *>(Wp),
-                               static_cast<const float *>(Sp), C, epi);
+    if (K <= 64 * TILE_PASS && nsplit <= 1) {
+        // one pass over K and over the rows: half tiles
+        auto half = [&](auto mr) {
+            constexpr int MR = decltype(mr)::value;
+            const size_t lds = (size_t)MR * (K / 64) * 144 + (size_t)HALF_WAVES * MR * 16 * sizeof(float);
+            auto go = [&](auto kernel) {
+                hipLaunchKernelGGL(kernel, dim3(div_up(N, 16), div_up(M, MR)), dim3(64 * HALF_WAVES),
+                                   lds, s, M, K, N, static_cast<const _Float16 *>(A),
+                                   static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp),
+                                   C, epi);
+            };
+            if (half_pairs) go(gemv_int4b64_half_kernel<MR, true>);
+            else go(gemv_int4b64_half_kernel<MR, false>);
+            return hipGetLastError();
         };
-        if (half_pairs) go(gemv_int4b64_half_kernel<true>);
-        else go(gemv_int4b64_half_kernel<false>);
-        return hipGetLastError();
+        switch (M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8) {
+        case 8: return half(std::integral_constant<int, 8>{});
+        case 4: return half(std::integral_constant<int, 4>{});
+        case 2: return half(std::integral_constant<int, 2>{});
+        default: return half(std::integral_constant<int, 1>{});
+        }
     }
     // all rows in one pass (at most 88 KiB of LDS for eight), so the weights stream once
     switch (M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8) {

@@ -88,8 +88,10 @@ constexpr int kGemvF16MaxK = 8192;   // fp16-weight GEMV: 16 slices of 8 per lan
 constexpr int kGemvI8BlkMaxK = 8192; // blocked Int8 GEMV: eight code slices and pairs per lane
 constexpr int kGemvMaxK = 16384;      // A rows staged in LDS: MR * K * 2 bytes
 // Largest M * K * N the Int4 GEMV takes for 5..8 rows (above it the tiled
-// kernel is faster).
+// kernel is faster): with K > 4096 (the whole-tile GEMV, passes over K), and
+// with K <= 4096 (the half-tile GEMV).
 constexpr long long kGemvInt4MaxMKN = 3LL << 26;
+constexpr long long kGemvInt4HalfMaxMKN = 1LL << 29;
 // LDS a GEMV workgroup may use (gfx950 gives a workgroup up to 160 KiB).
 constexpr size_t kGemvLds = 150 * 1024;
 
