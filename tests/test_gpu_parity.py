@@ -141,6 +141,15 @@ def test_int4_gemv_split_k(M):
         _parity(fmt, M, K, N, seed=M * 7 + K + N)
 
 
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
+def test_int4_gemv_k_passes(M):
+    """The half-tile Int4 GEMV over K in passes of 64 blocks (K > 4096) with
+    enough channel tiles not to split: ragged N, an odd block count in the
+    last pass, blocks of 32."""
+    for fmt, K, N in [("int4b64", 8192, 4100), ("int4b32", 5120, 1000), ("int4b64", 12352, 4128)]:
+        _parity(fmt, M, K, N, seed=M * 23 + K + N)
+
+
 @pytest.mark.parametrize("M", [1, 3, 8, 9, 64, 65, 129])
 def test_int4_other_block_sizes(M):
     """Int4 with blocks of 32, 128, 256 and 320 K-elements (the page's

@@ -193,8 +193,8 @@ __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
     }
 }
 
-// MR <= 8 rows (one pass over them), K <= 4096 (one pass over K), no split:
-// a 512-thread workgroup per 16 channels, half of a 32-channel tile, so a
+// MR <= 8 rows (one pass over them), K in passes of up to 64 blocks (one
+// pass for K <= 4096), no split: a 512-thread workgroup per 16 channels, half of a 32-channel tile, so a
 // shape has twice as many workgroups of half the bytes and they spread more
 // evenly over the CUs (11008 channels: 688 half tiles, at most 3 per CU
 // against an average of 2.7, instead of 344 tiles at most 2 per CU against
@@ -206,16 +206,17 @@ __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
 // v_permlane32_swap; the eight waves in LDS in a fixed order.
 constexpr int HALF_WAVES = 8;
 
-template <int MR, bool HP>
+template <int MR, bool ONE_PASS, bool HP>
 __global__ __launch_bounds__(64 * HALF_WAVES) void gemv_int4b64_half_kernel(
     int M, int K, int N, const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ Sp, void *__restrict__ C, Epilogue epi) {
     extern __shared__ __align__(16) unsigned char lds[];
     constexpr int AS = (MR * 128 + 64 * HALF_WAVES - 1) / (64 * HALF_WAVES);   // staging slots per thread
-    const int nblk = K >> 6;                                                  // 1 .. 64
-    u4_t *ap = reinterpret_cast<u4_t *>(lds);                                 // [MR][nblk * 8]
-    f2_t *hs = reinterpret_cast<f2_t *>(lds + (size_t)MR * nblk * 128);       // [MR][2 nblk]
-    float *part = reinterpret_cast<float *>(lds + (size_t)MR * nblk * 144);   // [HALF_WAVES][MR][16]
+    const int nblk = K >> 6;
+    const int pmax = min(nblk, TILE_PASS);                                     // blocks per pass
+    u4_t *ap = reinterpret_cast<u4_t *>(lds);                                  // [MR][pmax * 8]
+    f2_t *hs = reinterpret_cast<f2_t *>(lds + (size_t)MR * pmax * 128);        // [MR][2 pmax]
+    float *part = reinterpret_cast<float *>(lds + (size_t)MR * pmax * 144);    // [HALF_WAVES][MR][16]
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = uniform(tid >> 6);
@@ -224,11 +225,18 @@ __global__ __launch_bounds__(64 * HALF_WAVES) void gemv_int4b64_half_kernel(
     const int c16 = lane & 15, h = (lane >> 4) & 1, j = lane >> 5;
     const int c = (blockIdx.x & 1) * 16 + c16;       // channel within the tile
     const unsigned magic = 0x64646464u;
-    const int nhb = 2 * nblk;
+    float acc[MR];
+#pragma unroll
+    for (int r = 0; r < MR; ++r) acc[r] = 0.f;
 
-    // 1. the activations (one (row, block, half) per thread and slot), then
-    //    every pair and record load of this wave, unconditional from clamped
-    //    block indices
+    // ONE_PASS (K <= 4096) compiles the body once without a loop around it
+    for (int b0 = 0; b0 < (ONE_PASS ? 1 : nblk); b0 += TILE_PASS) {   // workgroup-uniform
+    const int pb = min(nblk - b0, TILE_PASS);                          // blocks in this pass
+    const int nhb = 2 * pb;
+
+    // 1. the pass's activations (one (row, block, half) per thread and slot),
+    //    then every pair and record load of this wave, unconditional from
+    //    clamped block indices
     u4_t araw[AS][4];
 #pragma unroll
     for (int sl = 0; sl < AS; ++sl) {
@@ -236,7 +244,7 @@ __global__ __launch_bounds__(64 * HALF_WAVES) void gemv_int4b64_half_kernel(
         const int ar = idx / nhb, ahb = idx - ar * nhb;
         const bool alive = ar < MR && m0 + ar < M;
         const u4_t *src = reinterpret_cast<const u4_t *>(
-            A + (size_t)(alive ? m0 + ar : 0) * K + (size_t)(alive ? ahb : 0) * 32);
+            A + (size_t)(alive ? m0 + ar : 0) * K + (size_t)(alive ? 2 * b0 + ahb : 0) * 32);
 #pragma unroll
         for (int w = 0; w < 4; ++w) araw[sl][w] = alive ? src[w] : u4_t{0u, 0u, 0u, 0u};
     }
@@ -244,14 +252,14 @@ __global__ __launch_bounds__(64 * HALF_WAVES) void gemv_int4b64_half_kernel(
     u4_t wq[TILE_RPW];
 #pragma unroll
     for (int i = 0; i < TILE_RPW; ++i) {
-        const int b = min(2 * (wave + HALF_WAVES * i) + j, nblk - 1);
+        const int b = b0 + min(2 * (wave + HALF_WAVES * i) + j, pb - 1);
         pr[i] = __builtin_nontemporal_load(
             reinterpret_cast<const f2_t *>(HP ? Sp + ((size_t)t * nblk + b) * 128 + h * 64 + c * 2
                                               : Sp + ((size_t)t * nblk + b) * 64 + c * 2));
     }
 #pragma unroll
     for (int i = 0; i < TILE_RPW; ++i) {
-        const int b = min(2 * (wave + HALF_WAVES * i) + j, nblk - 1);
+        const int b = b0 + min(2 * (wave + HALF_WAVES * i) + j, pb - 1);
         wq[i] = __builtin_nontemporal_load(
             reinterpret_cast<const u4_t *>(Wp + ((size_t)t * nblk + b) * 1024) + 32 * h + c);
     }
@@ -279,16 +287,13 @@ __global__ __launch_bounds__(64 * HALF_WAVES) void gemv_int4b64_half_kernel(
     }
     __syncthreads();
 
-    // 3. decode and accumulate; a lane whose block lies past K (odd block
-    //    count) computes on the clamped block and adds zero
-    float acc[MR];
-#pragma unroll
-    for (int r = 0; r < MR; ++r) acc[r] = 0.f;
+    // 3. decode and accumulate; a lane whose block lies past the pass (odd
+    //    block count) computes on the clamped block and adds zero
 #pragma unroll
     for (int i = 0; i < TILE_RPW; ++i) {
         const int bl = 2 * (wave + HALF_WAVES * i) + j;
-        if (2 * (wave + HALF_WAVES * i) >= nblk) break;   // wave-uniform
-        const int hbg = 2 * min(bl, nblk - 1) + h;
+        if (2 * (wave + HALF_WAVES * i) >= pb) break;     // wave-uniform
+        const int hbg = 2 * min(bl, pb - 1) + h;
         const float off = pr[i].x, sc = pr[i].y;
         const float ce = fmaf(-1024.0f, sc, off);
         const float co = fmaf(-64.0f, sc, off);
@@ -308,8 +313,10 @@ __global__ __launch_bounds__(64 * HALF_WAVES) void gemv_int4b64_half_kernel(
             }
             const f2_t sv = hs[(size_t)r * nhb + hbg];
             const float v = fmaf(ce, sv.x, fmaf(co, sv.y, fmaf(sc, Te, sc * 0.0625f * To)));
-            acc[r] += bl < nblk ? v : 0.f;
+            acc[r] += bl < pb ? v : 0.f;
         }
+    }
+    if (!ONE_PASS && b0 + TILE_PASS < nblk) __syncthreads();   // LDS reused by the next pass
     }
 
     // 4. the K-halves (lanes c and c + 16), then the block parities (lanes
@@ -624,19 +631,23 @@ hipError_t launch_gemv_int4b64(int M, int K, int N, const void *A, const void *W
 static hipError_t gemv_int4_rows(int M, int K, int N, const void *A, const void *Wp,
                                  const void *Sp, void *C, const Epilogue &epi, int half_pairs,
                                  int nsplit, hipStream_t s) {
-    if (K <= 64 * TILE_PASS && nsplit <= 1) {
-        // one pass over K and over the rows: half tiles
+    if (nsplit <= 1) {
+        // one pass over the rows: half tiles
         auto half = [&](auto mr) {
             constexpr int MR = decltype(mr)::value;
-            const size_t lds = (size_t)MR * (K / 64) * 144 + (size_t)HALF_WAVES * MR * 16 * sizeof(float);
+            const size_t lds = (size_t)MR * std::min(K / 64, TILE_PASS) * 144 +
+                               (size_t)HALF_WAVES * MR * 16 * sizeof(float);
             auto go = [&](auto kernel) {
                 hipLaunchKernelGGL(kernel, dim3(div_up(N, 16), div_up(M, MR)), dim3(64 * HALF_WAVES),
                                    lds, s, M, K, N, static_cast<const _Float16 *>(A),
                                    static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp),
                                    C, epi);
             };
-            if (half_pairs) go(gemv_int4b64_half_kernel<MR, true>);
-            else go(gemv_int4b64_half_kernel<MR, false>);
+            const bool one = K <= 64 * TILE_PASS;
+            if (half_pairs) one ? go(gemv_int4b64_half_kernel<MR, true, true>)
+                                : go(gemv_int4b64_half_kernel<MR, false, true>);
+            else one ? go(gemv_int4b64_half_kernel<MR, true, false>)
+                     : go(gemv_int4b64_half_kernel<MR, false, false>);
             return hipGetLastError();
         };
         switch (M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8) {
