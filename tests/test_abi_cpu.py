@@ -98,8 +98,9 @@ def test_split_k_workspace_plan():
     assert Q.qgemm_workspace_size(32, 9728, 2560, "f16") == 6 * 32 * 2560 * 4     # 40 tiles
     assert Q.qgemm_workspace_size(512, 2560, 4096, "f16") == 0                    # 256 tiles
     assert Q.qgemm_workspace_size(64, 448, 512, "int8b0") == 0                   # 7 K-blocks
-    # Int4 GEMV (M <= 8): fewer than 128 32-channel tiles split K, slices of
-    # >= 48 blocks; the size covers the larger of the GEMV and GEMM plans
+    # Int4 GEMV (M <= 8): fewer than 128 32-channel tiles split K into three or
+    # more slices of >= 48 blocks; the size covers the larger of the GEMV and
+    # GEMM plans
     assert Q.qgemm_workspace_size(8, 9728, 2560, "int4b64") == 8 * 8 * 2560 * 4   # GEMM plan 8 > GEMV 3
     assert Q.qgemm_workspace_size(2, 16384, 70, "int4b64") == -(-8 * 2 * 70 * 4 // 256) * 256   # GEMM plan 8 > GEMV 5
     assert Q.qgemm_workspace_size(1, 16384, 70, "int4b64") == -(-8 * 1 * 70 * 4 // 256) * 256

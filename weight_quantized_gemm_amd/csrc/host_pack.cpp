@@ -179,6 +179,11 @@ int gemv_split_plan(qgemm_format f, int M, int K, int N) {
     long long sp = kSplitTargetCUs / tiles;
     if (sp > kMaxSplit) sp = kMaxSplit;
     if (sp > K / 64 / 48) sp = K / 64 / 48;
+    // the unsplit Int4 GEMV runs half tiles (twice the workgroups), which a
+    // two-way split does not beat (measured: 16384 x 3072 11.1 us unsplit
+    // against 11.6 split in two, 6144 x 2560 5.7 against 7.0); three or more
+    // slices still win (9728 x 2560: 7.6 us in three, 9.4 in two)
+    if (f == QGEMM_INT4_B64 && sp < 3) return 1;
     return sp < 2 ? 1 : (int)sp;
 }
 
