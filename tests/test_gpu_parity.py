@@ -145,8 +145,10 @@ def test_int4_gemv_split_k(M):
 def test_int4_gemv_k_passes(M):
     """The half-tile Int4 GEMV over K in passes of 64 blocks (K > 4096) with
     enough channel tiles not to split: ragged N, an odd block count in the
-    last pass, blocks of 32."""
-    for fmt, K, N in [("int4b64", 8192, 4100), ("int4b32", 5120, 1000), ("int4b64", 12352, 4128)]:
+    last pass, blocks of 32; with at most one half tile per CU (N <= 4096 at
+    one row group) the sixteen-wave kernel, a two-block last pass among them."""
+    for fmt, K, N in [("int4b64", 8192, 4100), ("int4b32", 5120, 1000), ("int4b64", 12352, 4128),
+                      ("int4b64", 8320, 4000), ("int4b64", 11008, 4096)]:
         _parity(fmt, M, K, N, seed=M * 23 + K + N)
 
 

@@ -194,29 +194,37 @@ __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
 }
 
 // MR <= 8 rows (one pass over them), K in passes of up to 64 blocks (one
-// pass for K <= 4096), no split: a 512-thread workgroup per 16 channels, half of a 32-channel tile, so a
+// pass for K <= 4096), no split: a workgroup of NW waves (eight; sixteen in the case below) per 16
+// channels, half of a 32-channel tile, so a
 // shape has twice as many workgroups of half the bytes and they spread more
 // evenly over the CUs (11008 channels: 688 half tiles, at most 3 per CU
 // against an average of 2.7, instead of 344 tiles at most 2 per CU against
 // 1.3; 4096 channels: all 256 CUs instead of 128). Lane (c, h, j) =
 // (lane % 16, lane / 16 % 2, lane / 32) takes channel c of the half, K-half h
-// of block 2 (w + 8 i) + j in step i of wave w: one load instruction covers
+// of block 2 (w + NW i) + j in step i of wave w of NW: one load instruction covers
 // the 16 channels' pieces of both halves of two blocks (four 256-byte runs).
 // The four lanes of each channel meet by one exchange across 16 lanes and one
-// v_permlane32_swap; the eight waves in LDS in a fixed order.
+// v_permlane32_swap; the waves in LDS in a fixed order.
 constexpr int HALF_WAVES = 8;
+// Sixteen waves for K in passes when every half tile has a CU of its own:
+// twice the loads in flight per CU (measured at M = 1, K = 11008, N = 4096:
+// 8.76 us against 9.11 with eight). Where the half tiles outnumber the CUs
+// the eight-wave kernel stays: two sixteen-wave workgroups per CU would not
+// hold them all at once (K = 4096, N = 11008: 7.9 us against 7.6).
+constexpr int HALF_WAVES_WIDE = 16;
 
-template <int MR, bool ONE_PASS, bool HP>
-__global__ __launch_bounds__(64 * HALF_WAVES) void gemv_int4b64_half_kernel(
+template <int MR, bool ONE_PASS, bool HP, int NW>
+__global__ __launch_bounds__(64 * NW) void gemv_int4b64_half_kernel(
     int M, int K, int N, const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ Sp, void *__restrict__ C, Epilogue epi) {
     extern __shared__ __align__(16) unsigned char lds[];
-    constexpr int AS = (MR * 128 + 64 * HALF_WAVES - 1) / (64 * HALF_WAVES);   // staging slots per thread
+    constexpr int RPW = TILE_PASS / (2 * NW);                                  // blocks per wave and pass
+    constexpr int AS = (MR * 128 + 64 * NW - 1) / (64 * NW);   // staging slots per thread
     const int nblk = K >> 6;
     const int pmax = min(nblk, TILE_PASS);                                     // blocks per pass
     u4_t *ap = reinterpret_cast<u4_t *>(lds);                                  // [MR][pmax * 8]
     f2_t *hs = reinterpret_cast<f2_t *>(lds + (size_t)MR * pmax * 128);        // [MR][2 pmax]
-    float *part = reinterpret_cast<float *>(lds + (size_t)MR * pmax * 144);    // [HALF_WAVES][MR][16]
+    float *part = reinterpret_cast<float *>(lds + (size_t)MR * pmax * 144);    // [NW][MR][16]
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = uniform(tid >> 6);
@@ -240,7 +248,7 @@ __global__ __launch_bounds__(64 * HALF_WAVES) void gemv_int4b64_half_kernel(
     u4_t araw[AS][4];
 #pragma unroll
     for (int sl = 0; sl < AS; ++sl) {
-        const int idx = tid + 64 * HALF_WAVES * sl;
+        const int idx = tid + 64 * NW * sl;
         const int ar = idx / nhb, ahb = idx - ar * nhb;
         const bool alive = ar < MR && m0 + ar < M;
         const u4_t *src = reinterpret_cast<const u4_t *>(
@@ -248,18 +256,18 @@ __global__ __launch_bounds__(64 * HALF_WAVES) void gemv_int4b64_half_kernel(
 #pragma unroll
         for (int w = 0; w < 4; ++w) araw[sl][w] = alive ? src[w] : u4_t{0u, 0u, 0u, 0u};
     }
-    f2_t pr[TILE_RPW];
-    u4_t wq[TILE_RPW];
+    f2_t pr[RPW];
+    u4_t wq[RPW];
 #pragma unroll
-    for (int i = 0; i < TILE_RPW; ++i) {
-        const int b = b0 + min(2 * (wave + HALF_WAVES * i) + j, pb - 1);
+    for (int i = 0; i < RPW; ++i) {
+        const int b = b0 + min(2 * (wave + NW * i) + j, pb - 1);
         pr[i] = __builtin_nontemporal_load(
             reinterpret_cast<const f2_t *>(HP ? Sp + ((size_t)t * nblk + b) * 128 + h * 64 + c * 2
                                               : Sp + ((size_t)t * nblk + b) * 64 + c * 2));
     }
 #pragma unroll
-    for (int i = 0; i < TILE_RPW; ++i) {
-        const int b = b0 + min(2 * (wave + HALF_WAVES * i) + j, pb - 1);
+    for (int i = 0; i < RPW; ++i) {
+        const int b = b0 + min(2 * (wave + NW * i) + j, pb - 1);
         wq[i] = __builtin_nontemporal_load(
             reinterpret_cast<const u4_t *>(Wp + ((size_t)t * nblk + b) * 1024) + 32 * h + c);
     }
@@ -268,7 +276,7 @@ __global__ __launch_bounds__(64 * HALF_WAVES) void gemv_int4b64_half_kernel(
     //    past M are staged as zeros and never stored)
 #pragma unroll
     for (int sl = 0; sl < AS; ++sl) {
-        const int idx = tid + 64 * HALF_WAVES * sl;
+        const int idx = tid + 64 * NW * sl;
         if (idx < MR * nhb) {
             float se = 0.f, so = 0.f;
 #pragma unroll
@@ -290,9 +298,9 @@ __global__ __launch_bounds__(64 * HALF_WAVES) void gemv_int4b64_half_kernel(
     // 3. decode and accumulate; a lane whose block lies past the pass (odd
     //    block count) computes on the clamped block and adds zero
 #pragma unroll
-    for (int i = 0; i < TILE_RPW; ++i) {
-        const int bl = 2 * (wave + HALF_WAVES * i) + j;
-        if (2 * (wave + HALF_WAVES * i) >= pb) break;     // wave-uniform
+    for (int i = 0; i < RPW; ++i) {
+        const int bl = 2 * (wave + NW * i) + j;
+        if (2 * (wave + NW * i) >= pb) break;     // wave-uniform
         const int hbg = 2 * min(bl, pb - 1) + h;
         const float off = pr[i].x, sc = pr[i].y;
         const float ce = fmaf(-1024.0f, sc, off);
@@ -334,7 +342,7 @@ __global__ __launch_bounds__(64 * HALF_WAVES) void gemv_int4b64_half_kernel(
         const int n = 32 * t + (blockIdx.x & 1) * 16 + cc, m = m0 + r;
         float total = 0.f;
 #pragma unroll
-        for (int w = 0; w < HALF_WAVES; ++w) total += part[(w * MR + r) * 16 + cc];
+        for (int w = 0; w < NW; ++w) total += part[(w * MR + r) * 16 + cc];
         if (n < N && m < M) {
             if (epi.plain) static_cast<float *>(C)[(size_t)m * N + n] = total;
             else epi_put(epi, C, m, n, N, total);
@@ -635,19 +643,24 @@ static hipError_t gemv_int4_rows(int M, int K, int N, const void *A, const void 
         // one pass over the rows: half tiles
         auto half = [&](auto mr) {
             constexpr int MR = decltype(mr)::value;
+            const bool one = K <= 64 * TILE_PASS;
+            const long long groups = (long long)div_up(N, 16) * div_up(M, MR);
+            const int nw = !one && groups <= kSplitTargetCUs ? HALF_WAVES_WIDE : HALF_WAVES;
             const size_t lds = (size_t)MR * std::min(K / 64, TILE_PASS) * 144 +
-                               (size_t)HALF_WAVES * MR * 16 * sizeof(float);
+                               (size_t)nw * MR * 16 * sizeof(float);
             auto go = [&](auto kernel) {
-                hipLaunchKernelGGL(kernel, dim3(div_up(N, 16), div_up(M, MR)), dim3(64 * HALF_WAVES),
+                hipLaunchKernelGGL(kernel, dim3(div_up(N, 16), div_up(M, MR)), dim3(64 * nw),
                                    lds, s, M, K, N, static_cast<const _Float16 *>(A),
                                    static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp),
                                    C, epi);
             };
-            const bool one = K <= 64 * TILE_PASS;
-            if (half_pairs) one ? go(gemv_int4b64_half_kernel<MR, true, true>)
-                                : go(gemv_int4b64_half_kernel<MR, false, true>);
-            else one ? go(gemv_int4b64_half_kernel<MR, true, false>)
-                     : go(gemv_int4b64_half_kernel<MR, false, false>);
+            constexpr int W8 = HALF_WAVES, W16 = HALF_WAVES_WIDE;
+            if (one) half_pairs ? go(gemv_int4b64_half_kernel<MR, true, true, W8>)
+                                : go(gemv_int4b64_half_kernel<MR, true, false, W8>);
+            else if (nw == W16) half_pairs ? go(gemv_int4b64_half_kernel<MR, false, true, W16>)
+                                           : go(gemv_int4b64_half_kernel<MR, false, false, W16>);
+            else half_pairs ? go(gemv_int4b64_half_kernel<MR, false, true, W8>)
+                            : go(gemv_int4b64_half_kernel<MR, false, false, W8>);
             return hipGetLastError();
         };
         switch (M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8) {
