@@ -402,3 +402,57 @@ def test_int4_block32_pair_records_golden():
             for h in range(2):
                 assert list(recs[t * (K // 64) + b, h, c]) == list(pc[n, 2 * b + h])
     assert not np.any(recs[K // 64:, :, 8:, :])        # channels 40..63: zero padding
+
+
+def test_binding_checks_dtypes_and_sizes_before_the_library():
+    """The Python binding rejects device buffers of the wrong element type or
+    too few bytes before calling into C, where the kernels would read or write
+    past them (CPU tensors stand in: the dtype and size checks come before the
+    device check)."""
+    import torch
+    M, K, N = 4, 128, 64
+    wb, sb = Q.qgemm_packed_size(K, N, "int4b64")
+    A16 = torch.zeros((M, K), dtype=torch.float16)
+    C32 = torch.zeros((M, N), dtype=torch.float32)
+    Bq = torch.zeros(wb, dtype=torch.uint8)
+    Sc = torch.zeros(sb, dtype=torch.uint8)
+    bad = [
+        dict(A=torch.zeros((M, K), dtype=torch.float32)),     # fp32 A for an fp16 format
+        dict(A=torch.zeros((M, K - 1), dtype=torch.float16)),  # too few A elements
+        dict(C=torch.zeros((M, N - 1), dtype=torch.float32)),  # C smaller than M x N
+        dict(C=torch.zeros((M, N), dtype=torch.float16)),      # fp16 C with fp32 output
+        dict(Bq=torch.zeros(wb - 1, dtype=torch.uint8)),       # packed weights too short
+        dict(scales=torch.zeros(sb - 16, dtype=torch.uint8)),  # packed pairs too short
+    ]
+    for override in bad:
+        args = dict(A=A16, Bq=Bq, scales=Sc, C=C32)
+        args.update(override)
+        with pytest.raises(ValueError):
+            Q.qgemm_run(M, K, N, "int4b64", args["A"], args["Bq"], args["scales"], args["C"])
+    # the fp32 format takes fp32 A; an fp16 A is rejected
+    Bf = torch.zeros(K * N, dtype=torch.float32)
+    with pytest.raises(ValueError, match="dtype"):
+        Q.qgemm_run(M, K, N, "f32", A16, Bf, None, C32)
+    # epilogue operands: residual in C's type, bias fp32 [N]
+    with pytest.raises(ValueError, match="residual"):
+        Q.qgemm_run_ex(M, K, N, "int4b64", A16, Bq, Sc, C32,
+                       residual=torch.zeros((M, N), dtype=torch.float16))
+    with pytest.raises(ValueError, match="bias"):
+        Q.qgemm_run_ex(M, K, N, "int4b64", A16, Bq, Sc, C32, bias=torch.zeros(N - 4))
+    with pytest.raises(ValueError, match="C"):
+        Q.qgemm_run_ex(M, K, N, "int4b64", A16, Bq, Sc, C32, out_type="f16")
+    # a workspace smaller than the size claimed for it
+    with pytest.raises(ValueError, match="workspace"):
+        Q.qgemm_run_ws(M, K, N, "int4b64", A16, Bq, Sc, C32, torch.zeros(16, dtype=torch.uint8), 4096)
+    # well-typed CPU tensors get past these checks and stop at the device check
+    with pytest.raises(ValueError, match="GPU"):
+        Q.qgemm_run(M, K, N, "int4b64", A16, Bq, Sc, C32)
+
+
+def test_packed_weight_checks_activation_shape():
+    import torch
+    K, N = 128, 32
+    w = Q.PackedWeight.__new__(Q.PackedWeight)
+    w.fmt, w.K, w.N = Q.QGEMM_INT4_B64, K, N
+    with pytest.raises(ValueError, match="shape"):
+        w(torch.zeros((2, K + 64), dtype=torch.float16))

@@ -120,46 +120,52 @@ static bool use_gemv(qgemm_format f, int M, int K, int N) {
     return false;
 }
 
-static qgemm_status run_w4a8(int M, int K, int N, const Geometry &g, const void *A,
+// What one call does, decided once from the shape and the GEMV limit in force
+// when the call starts: the kernel family and the scratch layout the caller's
+// workspace was checked against. Every later step of the call reads this
+// plan, so a concurrent qgemm_set_gemv_max_m cannot make one call size its
+// scratch for one kernel and launch another.
+struct CallPlan {
+    bool gemv;
+    RunWorkspace r;
+    int nsplit() const { return gemv ? r.gemv_nsplit : r.nsplit; }
+    // Scratch bytes the call touches: the W4A8 activation codes first, then
+    // (when the kernel splits K) the partial tiles. The size reported to
+    // callers (run_workspace().bytes) is a function of the shape alone and
+    // never smaller than this.
+    size_t used_bytes() const { return nsplit() <= 1 ? r.w4a8.bytes : r.bytes; }
+};
+
+static CallPlan plan_call(qgemm_format f, int M, int K, int N) {
+    return CallPlan{use_gemv(f, M, K, N), run_workspace(f, M, K, N)};
+}
+
+static qgemm_status run_w4a8(int M, int K, int N, const CallPlan &p, const void *A,
                              const void *Bq, const void *scales, void *C, const Epilogue &epi,
                              void *ws, hipStream_t s, int32_t *D_debug) {
-    W4A8Workspace w = w4a8_workspace(M, K);
+    const W4A8Workspace &w = p.r.w4a8;
     uint8_t *base = static_cast<uint8_t *>(ws);
     int8_t *qa = reinterpret_cast<int8_t *>(base + w.qa_off);
     float *sa = reinterpret_cast<float *>(base + w.sa_off);
     int32_t *S = reinterpret_cast<int32_t *>(base + w.S_off);
-    if (use_gemv(QGEMM_W4A8, M, K, N)) {   // quantises the activations itself unless split
-        const RunWorkspace r = run_workspace(QGEMM_W4A8, M, K, N);
-        int32_t *part = r.gemv_nsplit > 1 ? reinterpret_cast<int32_t *>(base + r.part_off) : nullptr;
+    int32_t *part = p.nsplit() > 1 ? reinterpret_cast<int32_t *>(base + p.r.part_off) : nullptr;
+    if (p.gemv)   // quantises the activations itself unless split
         return launched(launch_w4a8_gemv(M, K, N, w.qa_stride, A, qa, sa, S, Bq, scales, C, epi,
-                                         D_debug, r.gemv_nsplit, part, s));
-    }
+                                         D_debug, p.nsplit(), part, s));
     hipError_t e = launch_w4a8_actquant(M, K, w.qa_stride, A, qa, sa, S, s);
     if (e != hipSuccess) return QGEMM_ERR_LAUNCH;
-    const RunWorkspace r = run_workspace(QGEMM_W4A8, M, K, N);
-    int32_t *part = r.nsplit > 1 ? reinterpret_cast<int32_t *>(base + r.part_off) : nullptr;
     return launched(launch_w4a8_gemm(M, K, N, w.qa_stride, qa, sa, S, Bq, scales, C, epi, D_debug,
-                                     r.nsplit, part, s));
+                                     p.nsplit(), part, s));
 }
 
-
-// Scratch bytes one call actually touches: the W4A8 activation codes first,
-// then (when the GEMM is split along K) the partial tiles. The size reported to
-// callers (run_workspace().bytes) is a function of the shape alone and never
-// smaller than this.
-static size_t used_bytes(const RunWorkspace &r, bool gemv) {
-    const int ns = gemv ? r.gemv_nsplit : r.nsplit;
-    return ns <= 1 ? r.w4a8.bytes : r.bytes;
-}
 
 static qgemm_status dispatch(int M, int K, int N, qgemm_format f, const Geometry &g,
-                             const void *A, const void *Bq, const void *scales, void *C,
-                             const Epilogue &epi, void *ws, hipStream_t s) {
+                             const CallPlan &p, const void *A, const void *Bq, const void *scales,
+                             void *C, const Epilogue &epi, void *ws, hipStream_t s) {
     (void)hipGetLastError();   // start from a clean per-thread error state
-    const bool gemv = use_gemv(f, M, K, N);
-    const RunWorkspace r = run_workspace(f, M, K, N);
-    const int nsplit = gemv ? r.gemv_nsplit : r.nsplit;
-    float *part = nsplit > 1 ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + r.part_off)
+    const bool gemv = p.gemv;
+    const int nsplit = p.nsplit();
+    float *part = nsplit > 1 ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + p.r.part_off)
                              : nullptr;
     switch (kernel_format(f)) {
     case QGEMM_F32:
@@ -178,7 +184,7 @@ static qgemm_status dispatch(int M, int K, int N, qgemm_format f, const Geometry
                              : launch_gemm_int8blk(M, K, N, A, Bq, scales, C, epi, g.block == 32,
                                                    nsplit, part, s));
     case QGEMM_W4A8:
-        return run_w4a8(M, K, N, g, A, Bq, scales, C, epi, ws, s, nullptr);
+        return run_w4a8(M, K, N, p, A, Bq, scales, C, epi, ws, s, nullptr);
     case QGEMM_F16:
         return launched(gemv ? launch_gemv_f16(M, K, N, A, Bq, C, epi, s)
                              : launch_gemm_f16(M, K, N, A, Bq, C, epi, nsplit, part, s));
@@ -211,7 +217,8 @@ qgemm_status qgemm_run_ex(int M, int K, int N, qgemm_format f, const void *A,
     Epilogue epi;
     st = make_epilogue(epilogue, &epi);
     if (st != QGEMM_OK) return st;
-    const size_t need = used_bytes(run_workspace(f, M, K, N), use_gemv(f, M, K, N));
+    const CallPlan plan = plan_call(f, M, K, N);
+    const size_t need = plan.used_bytes();
     const bool own = !workspace && ws_bytes == 0;   // scratch, if any, is ours to allocate
     if (need > 0 && !own) {
         if (!workspace) return QGEMM_ERR_NULL;
@@ -221,14 +228,14 @@ qgemm_status qgemm_run_ex(int M, int K, int N, qgemm_format f, const void *A,
     st = check_device();
     if (st != QGEMM_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (need == 0 || !own) return dispatch(M, K, N, f, g, A, Bq, scales, C, epi, workspace, s);
+    if (need == 0 || !own) return dispatch(M, K, N, f, g, plan, A, Bq, scales, C, epi, workspace, s);
     // Scratch (W4A8 codes, split-K partials), allocated and released in stream order.
     void *ws = nullptr;
     if (hipMallocAsync(&ws, need, s) != hipSuccess || !ws) {
         (void)hipGetLastError();
         return QGEMM_ERR_NOMEM;
     }
-    st = dispatch(M, K, N, f, g, A, Bq, scales, C, epi, ws, s);
+    st = dispatch(M, K, N, f, g, plan, A, Bq, scales, C, epi, ws, s);
     if (hipFreeAsync(ws, s) != hipSuccess) {
         (void)hipGetLastError();
         if (st == QGEMM_OK) st = QGEMM_ERR_LAUNCH;
@@ -246,7 +253,7 @@ qgemm_status qgemm_run_ws(int M, int K, int N, qgemm_format f, const void *A,
         bool empty = false;
         qgemm_status st = check_run(M, K, N, f, A, Bq, scales, C, &g, &empty);
         if (st != QGEMM_OK) return st;
-        if (used_bytes(run_workspace(f, M, K, N), use_gemv(f, M, K, N)) > 0) return QGEMM_ERR_NULL;
+        if (plan_call(f, M, K, N).used_bytes() > 0) return QGEMM_ERR_NULL;
     }
     return qgemm_run_ex(M, K, N, f, A, Bq, scales, C, nullptr, workspace, ws_bytes, stream);
 }
@@ -266,15 +273,15 @@ qgemm_status qgemm_w4a8_debug(int M, int K, int N, const void *A, const void *Bq
     if (st != QGEMM_OK || empty) return st;
     if (!qa || !sa || !S || !D || !workspace) return QGEMM_ERR_NULL;
     if (!aligned16(workspace) || !aligned16(D)) return QGEMM_ERR_ALIGN;
-    W4A8Workspace w = w4a8_workspace(M, K);
-    if (ws_bytes < used_bytes(run_workspace(QGEMM_W4A8, M, K, N), use_gemv(QGEMM_W4A8, M, K, N)))
-        return QGEMM_ERR_SIZE;
+    const CallPlan plan = plan_call(QGEMM_W4A8, M, K, N);
+    const W4A8Workspace &w = plan.r.w4a8;
+    if (ws_bytes < plan.used_bytes()) return QGEMM_ERR_SIZE;
     st = check_device();
     if (st != QGEMM_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     const Epilogue plain{nullptr, nullptr, QGEMM_ACT_NONE, 0, true};
-    st = run_w4a8(M, K, N, g, A, Bq, scales, C, plain, workspace, s, D);
+    st = run_w4a8(M, K, N, plan, A, Bq, scales, C, plain, workspace, s, D);
     if (st != QGEMM_OK) return st;
     const uint8_t *base = static_cast<const uint8_t *>(workspace);
     if (hipMemcpy2DAsync(qa, (size_t)K, base + w.qa_off, (size_t)w.qa_stride, (size_t)K, (size_t)M,

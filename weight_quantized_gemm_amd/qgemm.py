@@ -164,6 +164,60 @@ def _dev_ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+_TORCH_DTYPE_NAMES = {torch.float32: "float32", torch.float16: "float16", torch.uint8: "uint8",
+                      torch.int8: "int8", torch.int32: "int32"}
+
+
+def _need(t, name: str, dtypes, numel: int | None = None, nbytes: int | None = None):
+    """Checks a device-buffer argument before anything reaches the library:
+    its dtype (one of `dtypes`, or any when None), at least `numel` elements
+    and at least `nbytes` bytes. Raw integer addresses and None pass through
+    (the C side checks for NULL). Raises ValueError. The kernels would
+    otherwise read or write past a buffer that is too small or of the wrong
+    element type."""
+    if t is None or isinstance(t, int):
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch tensor or a device address, got {type(t).__name__}")
+    if t.numel() == 0 and not numel and not nbytes:
+        return   # an empty placeholder for an operand the shape never reads
+    if dtypes is not None and t.dtype not in dtypes:
+        want = " or ".join(_TORCH_DTYPE_NAMES.get(d, str(d)) for d in dtypes)
+        raise ValueError(f"{name}: dtype {t.dtype} where {want} is required")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements, at least {numel} required")
+    if nbytes is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name}: {t.numel() * t.element_size()} bytes, at least {nbytes} required")
+
+
+def _check_run_args(M: int, K: int, N: int, fmt, A, Bq, scales, C, out_type=0, bias=None,
+                    residual=None, workspace=None, ws_bytes: int = 0):
+    """Dtype and size checks shared by the run entry points: A fp32 for the
+    fp32 format, fp16 otherwise, [M][K]; C (and the residual) fp32, or fp16
+    with the fp16 output; the packed buffers at least the packed sizes of
+    (K, N, fmt); the bias [N] fp32; the workspace at least ws_bytes."""
+    f = _fmt(fmt)
+    if M < 0 or N < 0 or K < 0:
+        raise ValueError(f"negative shape M={M} K={K} N={N}")
+    if M == 0 or N == 0:
+        return
+    a_dt = torch.float32 if f == QGEMM_F32 else torch.float16
+    _need(A, "A", (a_dt,), numel=M * K)
+    c_dt = torch.float16 if out_type in (1, "f16") else torch.float32
+    _need(C, "C", (c_dt,), numel=M * N)
+    _need(residual, "residual", (c_dt,), numel=M * N)
+    _need(bias, "bias", (torch.float32,), numel=N)
+    try:
+        wb, sb = qgemm_packed_size(K, N, f)
+    except QGemmError:
+        wb = sb = None   # the library reports the bad shape or format itself
+    _need(Bq, "Bq", None, nbytes=wb)
+    _need(scales, "scales", None, nbytes=sb)
+    if isinstance(workspace, torch.Tensor) and workspace.numel() * workspace.element_size() < ws_bytes:
+        raise ValueError(f"workspace: {workspace.numel() * workspace.element_size()} bytes, "
+                         f"ws_bytes={ws_bytes} claimed")
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -241,12 +295,14 @@ def qgemm_unpack_weights(K: int, N: int, fmt, w_packed: np.ndarray, s_packed: np
 
 def qgemm_run(M: int, K: int, N: int, fmt, A, Bq, scales, C, stream=None) -> None:
     """C = A x B on the GPU (torch tensors or raw device addresses)."""
+    _check_run_args(M, K, N, fmt, A, Bq, scales, C)
     _check(load().qgemm_run(M, K, N, _fmt(fmt), _dev_ptr(A), _dev_ptr(Bq), _dev_ptr(scales),
                             _dev_ptr(C), _stream(stream)), "qgemm_run")
 
 
 def qgemm_run_ws(M: int, K: int, N: int, fmt, A, Bq, scales, C, workspace, ws_bytes: int,
                  stream=None) -> None:
+    _check_run_args(M, K, N, fmt, A, Bq, scales, C, workspace=workspace, ws_bytes=ws_bytes)
     _check(load().qgemm_run_ws(M, K, N, _fmt(fmt), _dev_ptr(A), _dev_ptr(Bq), _dev_ptr(scales),
                                _dev_ptr(C), _dev_ptr(workspace), ws_bytes, _stream(stream)),
            "qgemm_run_ws")
@@ -258,6 +314,8 @@ def qgemm_run_ex(M: int, K: int, N: int, fmt, A, Bq, scales, C, bias=None, resid
     """C = act(A x B + bias + residual) on the GPU; C (and residual) fp32 or fp16
     per out_type. With no workspace the library allocates any scratch the shape
     needs in stream order."""
+    _check_run_args(M, K, N, fmt, A, Bq, scales, C, out_type=out_type, bias=bias,
+                    residual=residual, workspace=workspace, ws_bytes=ws_bytes)
     epi = Epilogue(_dev_ptr(bias), _dev_ptr(residual),
                    ACTIVATIONS[activation] if isinstance(activation, str) else int(activation),
                    OUT_TYPES[out_type] if isinstance(out_type, str) else int(out_type))
@@ -268,6 +326,11 @@ def qgemm_run_ex(M: int, K: int, N: int, fmt, A, Bq, scales, C, bias=None, resid
 
 def qgemm_w4a8_debug(M: int, K: int, N: int, A, Bq, scales, C, qa, sa, S, D, workspace,
                      ws_bytes: int, stream=None) -> None:
+    _check_run_args(M, K, N, QGEMM_W4A8, A, Bq, scales, C, workspace=workspace, ws_bytes=ws_bytes)
+    _need(qa, "qa", (torch.int8, torch.uint8), numel=M * K)
+    _need(sa, "sa", (torch.float32,), numel=M)
+    _need(S, "S", (torch.int32,), numel=M)
+    _need(D, "D", (torch.int32,), numel=M * N)
     _check(load().qgemm_w4a8_debug(M, K, N, _dev_ptr(A), _dev_ptr(Bq), _dev_ptr(scales),
                                    _dev_ptr(C), _dev_ptr(qa), _dev_ptr(sa), _dev_ptr(S),
                                    _dev_ptr(D), _dev_ptr(workspace), ws_bytes, _stream(stream)),
@@ -334,6 +397,8 @@ class PackedWeight:
         return cls(f, K, N, q, pairs, device)
 
     def __call__(self, A: torch.Tensor, C: torch.Tensor | None = None, stream=None):
+        if A.dim() != 2 or A.shape[1] != self.K:
+            raise ValueError(f"A: shape {tuple(A.shape)}, expected [M][{self.K}]")
         M = A.shape[0]
         if C is None:
             C = torch.empty((M, self.N), dtype=torch.float32, device=A.device)
