@@ -461,6 +461,109 @@ def vendor_reference(args, torch) -> int:
     return 0
 
 
+def _probe_lib():
+    """libqgemm_probe.so (measured-peak probes, include/qgemm_probe.h)."""
+    import ctypes
+    path = os.path.join(ROOT, "weight_quantized_gemm_amd", "libqgemm_probe.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is missing: build it with python -m weight_quantized_gemm_amd.build_lib")
+    lib = ctypes.CDLL(path)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.qgemm_probe_read.argtypes = [P, Z, P, I, P]
+    lib.qgemm_probe_copy.argtypes = [P, P, Z, I, P]
+    lib.qgemm_probe_mfma.argtypes = [I, I, I, I, P, P, P]
+    lib.qgemm_probe_l2.argtypes = [P, Z, I, I, I, I, I, I, P, P, P]
+    for f in (lib.qgemm_probe_read, lib.qgemm_probe_copy, lib.qgemm_probe_mfma, lib.qgemm_probe_l2):
+        f.restype = I
+    return lib
+
+
+def peak_probes(args, torch) -> int:
+    """Measured peaks of this chip for plain kernels (context for the roofline
+    fractions, which stay against the published peaks): an HBM read stream and
+    copy at the decode GEMV's size and at a 117 MB weight, rotated past twice
+    the Infinity Cache and timed like the GEMM workloads (replayed graph, HIP
+    events); an fp16 MFMA loop with and without same-wave VALU work, with the
+    shader clock read in-kernel; L2-resident reads in the GEMM's operand
+    patterns, in bytes per clock per CU. One JSON line per measurement."""
+    import ctypes
+    lib = _probe_lib()
+    stream = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def chk(rc, what):
+        if rc != 0:
+            raise SystemExit(f"{what}: probe returned {rc}")
+
+    # HBM streams: the decode GEMV's algorithmic bytes and a 117 MB weight
+    for nbytes in (algorithmic_bytes(1, 4096, 11008) // 16 * 16, 117_440_512):
+        copies = max(2, -(-2 * MALL_BYTES // nbytes) + 1)
+        bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(i)
+                for i in range(copies)]
+        # grids that give each thread 1, 2 or 4 turns of eight 16-byte loads
+        grids = [-(-(nbytes // 16) // (256 * 8 * turns)) for turns in (1, 2, 4)]
+        for grid in grids:
+            sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+            run = lambda i, g=grid, sk=sink: chk(lib.qgemm_probe_read(
+                bufs[i % copies].data_ptr(), nbytes, sk.data_ptr(), g, stream()), "read")
+            ms = time_calls(torch, run, copies, args.steps)
+            print(json.dumps({"peak_probe": "hbm_read", "bytes": nbytes, "grid": grid,
+                              "rotation_copies": copies, "ms_per_call": ms,
+                              "gb_s": nbytes / ms / 1e6,
+                              "frac_of_hbm_peak": nbytes / ms / 1e6 / HBM_PEAK_GBS}), flush=True)
+        dsts = [torch.empty_like(b) for b in bufs[: max(2, copies // 2 + 1)]]
+        for grid in grids[:2]:
+            run = lambda i, g=grid: chk(lib.qgemm_probe_copy(
+                bufs[i % copies].data_ptr(), dsts[i % len(dsts)].data_ptr(), nbytes, g, stream()), "copy")
+            ms = time_calls(torch, run, copies, args.steps)
+            print(json.dumps({"peak_probe": "hbm_copy", "bytes_read": nbytes, "grid": grid,
+                              "ms_per_call": ms, "gb_s": 2 * nbytes / ms / 1e6,
+                              "frac_of_hbm_peak": 2 * nbytes / ms / 1e6 / HBM_PEAK_GBS}), flush=True)
+        del bufs, dsts
+        torch.cuda.empty_cache()
+
+    # fp16 MFMA loop: one workgroup per CU, 4 or 8 waves
+    iters = 2048
+    for waves in (4, 8):
+        for valu in (0, 4, 8, 16):
+            grid = 256
+            clk = torch.zeros(4 * grid, dtype=torch.int64, device="cuda")
+            sink = torch.empty(grid * 64 * waves, dtype=torch.float32, device="cuda")
+            run = lambda i, w=waves, v=valu: chk(lib.qgemm_probe_mfma(
+                iters, v, w, grid, clk.data_ptr(), sink.data_ptr(), stream()), "mfma")
+            ms = time_calls(torch, run, 4, max(8, args.steps // 8))
+            c = clk.view(grid, 4).cpu().numpy().astype(np.float64)
+            cycles = c[:, 1] - c[:, 0]
+            ref_s = (c[:, 3] - c[:, 2]) / 100e6
+            mhz = float(np.median(cycles / ref_s) / 1e6)
+            fl = 2.0 * 32 * 32 * 16 * 4 * iters * waves * grid
+            per_simd = 4 * iters * waves / 4              # MFMAs issued per SIMD
+            print(json.dumps({"peak_probe": "mfma_f16_32x32x16", "waves_per_cu": waves,
+                              "valu_per_mfma": valu, "ms_per_call": ms,
+                              "tflops": fl / ms / 1e9, "frac_of_fp16_peak": fl / ms / 1e9 / FP16_PEAK_TFLOPS,
+                              "shader_mhz": mhz,
+                              "cycles_per_mfma_per_simd": float(np.median(cycles)) / per_simd}),
+                  flush=True)
+
+    # L2-resident reads (2 MiB window, every XCD's L2 holds it), 8 waves per CU
+    buf = torch.zeros(4 << 20, dtype=torch.uint8, device="cuda")
+    grid, waves, it = 256, 8, 512
+    for pattern, name in ((0, "1 KiB contiguous"), (1, "8 rows x 128 B, stride 8 KiB"),
+                          (2, "16 rows x 64 B, stride 8 KiB")):
+        clk = torch.zeros(2 * grid, dtype=torch.int64, device="cuda")
+        sink = torch.empty(grid * 64 * waves, dtype=torch.int32, device="cuda")
+        run = lambda i, p=pattern: chk(lib.qgemm_probe_l2(
+            buf.data_ptr(), buf.numel(), 21, p, 8192, it, waves, grid, clk.data_ptr(),
+            sink.data_ptr(), stream()), "l2")
+        ms = time_calls(torch, run, 4, max(8, args.steps // 8))
+        c = clk.view(grid, 2).cpu().numpy().astype(np.float64)
+        cyc = float(np.median(c[:, 1] - c[:, 0]))
+        per_cu = it * 8 * 1024.0 * waves
+        print(json.dumps({"peak_probe": "l2_read", "pattern": name, "waves_per_cu": waves,
+                          "ms_per_call": ms, "bytes_per_clk_per_cu": per_cu / cyc,
+                          "tb_s_chip": per_cu * grid / ms / 1e9}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -492,6 +595,9 @@ def main() -> int:
                          "libraries) on the prefill shapes (or, with 'page-grid', fp16 on the "
                          "benchmark page's grid plus a trivial-kernel floor) with the same "
                          "rotation and print one JSON line per shape")
+    ap.add_argument("--peak", action="store_true",
+                    help="measured peaks of this chip for plain kernels (HBM read stream and copy, "
+                         "fp16 MFMA loop with the shader clock, L2-resident reads), one JSON line each")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch's plain device copy of MIB MiB (fp32) 10 times, "
                          "the reference kernel for scaling the HBM byte counters")
@@ -515,6 +621,8 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes": 4 * n, "launches": 10}), flush=True)
         return 0
 
+    if args.peak:
+        return peak_probes(args, torch)
     if args.workload:
         return single_workload(args, torch)
     if args.vendor_reference:

@@ -11,28 +11,36 @@
 // tiles exact and never narrows accumulators before the epilogue).
 //
 // Decomposition, chosen from what limits this shape on CDNA4 (a 512 x 4096
-// output gives each of 256 CUs only 8192 outputs, so operand traffic from L2
-// and the per-weight dequantisation work bound the kernel before the matrix
-// cores do):
-//  - a 512-thread workgroup owns a 64 x 128 tile of C (a taller-than-wide
-//    tile would read A from L2 twice as often);
-//  - wave (h, q) owns the 64 x 64 half h of the tile for the contiguous K
-//    quarter q and accumulates it with v_mfma_f32_32x32x16_f16 (2 x 2
+// output gives each of 256 CUs only 8192 outputs, so the bytes entering a CU
+// and the per-weight dequantisation bound the kernel before the matrix cores
+// do; each CU's L2 port delivers 64 bytes per clock):
+//  - a 256-thread workgroup owns a BM x BN tile of C, one workgroup per CU:
+//    128 x 64 once M reaches 128 (each dequantised weight then serves 128
+//    rows, which halves the dequantising instructions per matrix
+//    instruction: the vector ALUs, not the matrix cores, bound this kernel),
+//    64 x 128 below (half the rows of a 128-row tile would be padding);
+//  - each of its four waves (one per SIMD) accumulates the whole tile over
+//    one contiguous quarter of K with v_mfma_f32_32x32x16_f16 (BM/32 x BN/32
 //    accumulator tiles), so every B element is fetched and dequantised once
-//    per workgroup; two waves per SIMD let one wave's dequantisation issue
-//    while the other's matrix instructions run;
-//  - the two waves of a quarter share its A tiles in LDS: each fetches 32 of
-//    the 64 rows with fully coalesced loads (8 rows x 128 bytes per
-//    instruction) four blocks ahead through a register ring; four LDS tiles
-//    per quarter and one barrier per block keep writers behind readers;
+//    per workgroup and no operand is shared between waves: the main loop has
+//    no barrier, and each SIMD's matrix pipe is fed by its own wave, whose
+//    dequantising instructions issue while its matrix instructions run;
+//  - a wave's A block (BM rows x 64 K-elements) arrives through buffer loads
+//    with a scalar per-block offset, fully coalesced (8 rows x 128 bytes per
+//    instruction), one (BM = 128) or two (BM = 64) blocks ahead through a
+//    register ring, and passes through the wave's own two LDS tiles into the
+//    MFMA lane layout (one wave's LDS operations execute in order, so a tile
+//    is rewritten only after its last read);
 //  - a K-block of a 32-channel B tile is one contiguous 1 KiB record already
-//    in operand lane order (see the packed layout), fetched three blocks
-//    ahead through a register ring and dequantised in registers (one fp32
+//    in operand lane order (see the packed layout), fetched four blocks ahead
+//    through a register ring and dequantised in registers (one fp32
 //    multiply-add per weight, no LDS round trip);
 //  - the operands of MFMA step s + 1 are read and dequantised while the
 //    matrix cores run step s;
-//  - the eight partial tiles meet in LDS and the four K quarters are summed
-//    in a fixed order.
+//  - the instructions of one MFMA step stay in one scheduling region, and
+//    each dequantised operand is pinned where it is produced, so no matrix
+//    instruction waits on a vector instruction moved next to it;
+//  - the four partial tiles meet in LDS and are summed in a fixed order.
 // Lane (r, h) = (lane % 32, lane / 32) holds K-elements 32 h + 8 s .. +7 of
 // every 64-wide block in MFMA step s, for its A row and B column alike (the K
 // order inside an MFMA only has to agree between A and B).
@@ -48,18 +56,30 @@
 namespace qg {
 
 namespace {
-constexpr int BM = kInt4TileM, BN = kInt4TileN, BK = 64;
-constexpr int NWAVE = 8;               // (N half, K quarter) per wave
-constexpr int WN = BN / 2;             // columns per wave
-constexpr int RF = BM / 32;            // 32-row accumulator tiles per wave
-constexpr int CF = WN / 32;            // 32-column accumulator tiles per wave
+constexpr int BK = 64;
+constexpr int NWAVE = 4;               // one K quarter per wave
 constexpr int AS_STRIDE = BK + 8;      // halves per LDS row of an A tile (144 bytes)
-constexpr int RING = 4;                // B register ring (3 blocks ahead) = A tiles per quarter
-constexpr int RED_STRIDE = WN + 4;     // floats per LDS row of the reduction
-constexpr size_t AS_BYTES = (size_t)BM * AS_STRIDE * 2;                 // one A tile
-constexpr size_t A_LDS = (size_t)4 * RING * AS_BYTES;                   // all quarters
-constexpr size_t RED_BYTES = (size_t)NWAVE * BM * RED_STRIDE * 4;       // all waves
-constexpr size_t LDS_BYTES = RED_BYTES > A_LDS ? RED_BYTES : A_LDS;
+constexpr int A_TILES = 2;             // LDS A tiles per wave
+constexpr int B_RING = 4;              // B code ring (loads four blocks ahead)
+constexpr int P_RING = 2;              // pair ring (loads two blocks ahead)
+constexpr int UNROLL = 4;              // lcm of the rings: every slot a fixed register
+
+// Shape-dependent constants of one tile.
+template <int BM_, int BN_>
+struct TileCfg {
+    static constexpr int BM = BM_, BN = BN_;
+    static constexpr int RF = BM / 32;                  // 32-row accumulator tiles per wave
+    static constexpr int CF = BN / 32;                  // 32-column accumulator tiles per wave
+    static constexpr int A_SETS = BM == 64 ? 2 : 1;     // A register sets (blocks loaded ahead)
+    static constexpr int A_PIECES = BM * BK / 8 / 64;   // 16-byte A pieces per lane and block
+    static constexpr int RED_STRIDE = BN + 4;           // floats per LDS row of the reduction
+    static constexpr size_t AS_BYTES = (size_t)BM * AS_STRIDE * 2;          // one A tile
+    static constexpr size_t A_LDS = (size_t)NWAVE * A_TILES * AS_BYTES;     // all waves
+    static constexpr size_t RED_BYTES = (size_t)NWAVE * BM * RED_STRIDE * 4;
+    static constexpr size_t LDS_BYTES = RED_BYTES > A_LDS ? RED_BYTES : A_LDS;
+    static_assert(UNROLL % A_SETS == 0 && UNROLL % A_TILES == 0, "ring sizes");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 workgroup");
+};
 
 // Per (channel tile, block) dequantisation constants. Even codes decode as
 // x = 1024 + q and odd codes as x = 1024 + 16 q (the nibble is left in
@@ -68,16 +88,36 @@ struct DqParams {
     float s_lo, b_lo, s_hi, b_hi;
 };
 
-__device__ __forceinline__ DqParams dq_params(f2_t pair) {
-    const float off = pair.x, sc = pair.y;
+// keep = 0 (a padded block past the quarter's end) gives all-zero
+// constants: every weight of the block dequantises to +0 and adds nothing.
+__device__ __forceinline__ DqParams dq_params(f2_t pair, bool keep) {
+    const float off = keep ? pair.x : 0.f, sc = keep ? pair.y : 0.f;
     return {sc, fmaf(-1024.0f, sc, off), sc * 0.0625f, fmaf(-64.0f, sc, off)};
 }
+
+// Buffer resource of a raw byte range (gfx9 format word: 32-bit data,
+// no swizzle); loads through it take a per-lane and a scalar byte offset, so
+// a per-block advance is one scalar add.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_rsrc(const void *base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+template <int AUX = 0>
+__device__ __forceinline__ u4_t buf_load16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+    return __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, AUX));
+}
+__device__ __forceinline__ f2_t buf_load8(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+    return __builtin_bit_cast(f2_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+}
+constexpr int kNonTemporal = 2;   // cache policy of a streamed load (read once per workgroup)
 }
 
 // 8 Int4 codes (one word, k ascending, low nibble first) -> 8 fp16 weights
 // in k order, each one fp32 fused multiply-add rounded once to fp16. m_lo,
 // m_hi and magic are the constants 0x000F000F, 0x00F000F0 and 0x64006400 held
-// in registers, so each pair of codes costs one v_and_or_b32.
+// in registers, so each pair of codes costs one v_and_or_b32. The decode is
+// the published magic-exponent conversion of integer codes to fp16 (Kim et
+// al., "Who Says Elephants Can't Run", 2022): OR-ing a code into the
+// mantissa of 1024.0 gives 1024 + q exactly.
 __device__ __forceinline__ h8_t dequant8(unsigned word, const DqParams &p, unsigned m_lo,
                                          unsigned m_hi, unsigned magic) {
     const unsigned w8 = word >> 8;
@@ -97,13 +137,21 @@ __device__ __forceinline__ h8_t dequant8(unsigned word, const DqParams &p, unsig
     return o;
 }
 
+// Marks a value as produced here: the optimiser may not sink its
+// computation below this point (towards its use in a later MFMA step, where
+// it would stall the matrix instruction that reads it).
+__device__ __forceinline__ void pin(h8_t &v) { asm volatile("" : "+v"(v)); }
+
 // HP: one pair per 32-element half of each 64-block (Int4 blocks of 32).
-template <bool HP>
+template <class T, bool HP>
 __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     int M, int K, int N, int tiles_m, int tiles_n, int xcd_rows,
     const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ Sp, void *__restrict__ C, Epilogue epi) {
-    __shared__ __align__(16) unsigned char lds[LDS_BYTES];
+    constexpr int BM = T::BM, BN = T::BN, RF = T::RF, CF = T::CF;
+    constexpr int A_SETS = T::A_SETS, A_PIECES = T::A_PIECES, RED_STRIDE = T::RED_STRIDE;
+    constexpr size_t AS_BYTES = T::AS_BYTES;
+    __shared__ __align__(16) unsigned char lds[T::LDS_BYTES];
 
     // ---- tile of this workgroup ----
     const int L = blockIdx.x;
@@ -124,8 +172,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = uniform(tid >> 6);
-    const int nh = wave & 1, kq = wave >> 1;      // N half, K quarter
+    const int kq = uniform(tid >> 6);              // this wave's K quarter
     const int r = lane & 31, h = lane >> 5;
     const int nblk = K / BK;                       // >= 1
     // split-K: this workgroup's blocks are [KB0, KB1) (all of K when
@@ -140,57 +187,59 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     const int kb0 = KB0 + kq * nbs / 4, kb1 = KB0 + (kq + 1) * nbs / 4;   // contiguous quarter
     const int nb = kb1 - kb0;                      // kb0 is a valid block even when nb == 0
     const int last = max(kb1 - 1, kb0);
-    // every wave runs the same number of (padded) blocks: the largest
-    // quarter rounded up to the ring, so all waves meet every barrier
-    const int nsteps = ((nbs + 3) / 4 + RING - 1) / RING * RING;
+    // every wave runs its quarter's blocks rounded up to the unroll; blocks
+    // past the quarter's end re-load its last block and add exactly zero
+    const int nsteps = (nb + UNROLL - 1) / UNROLL * UNROLL;
     const int ntiles_b = (N + 31) / 32;            // packed 32-channel tiles
 
-    auto a_tile = [&](int slot) {
-        return reinterpret_cast<_Float16 *>(lds + (size_t)(kq * RING + slot) * AS_BYTES);
-    };
+    _Float16 *const a_lds = reinterpret_cast<_Float16 *>(lds + (size_t)kq * A_TILES * AS_BYTES);
+    auto a_tile = [&](int slot) { return a_lds + (size_t)slot * (AS_BYTES / 2); };
 
-    // A loader role: the two waves of a quarter each fetch 32 of the 64 rows,
-    // 8 rows x 128 bytes per instruction, lane -> (row, 16 B piece); byte
+    // A loader role: piece i of a block is row 8 i + lane / 8, elements
+    // 8 (lane % 8) .. +7 (128 bytes per row, 8 rows per instruction); byte
     // offsets from the tile's first row (rows past M are clamped: loaded,
-    // never stored).
+    // never stored) and, per block, a scalar advance of 128 bytes.
     const int arow = lane >> 3, apc = lane & 7;
-    const char *A_tile = reinterpret_cast<const char *>(A + (size_t)m0 * K);
-    unsigned a_off[4];
+    const int arows = min(BM, M - m0);
+    const __amdgpu_buffer_rsrc_t a_rs = byte_rsrc(A + (size_t)m0 * K, (unsigned)arows * K * 2u);
+    unsigned a_off[A_PIECES];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        a_off[i] = (unsigned)(min(32 * nh + 8 * i + arow, M - 1 - m0) * K + 8 * apc) * 2u;
-    // B: packed tile of each accumulator column tile (tiles past N: loaded, never stored)
-    size_t b_rec0[CF];
+    for (int i = 0; i < A_PIECES; ++i)
+        a_off[i] = (unsigned)(min(8 * i + arow, arows - 1) * K + 8 * apc) * 2u;
+    // B: records of each accumulator column tile (tiles past N: loaded, never
+    // stored), one 1 KiB record and one pair record per block
+    constexpr unsigned PREC = HP ? 512u : 256u;   // bytes per pair record
+    __amdgpu_buffer_rsrc_t b_rs[CF], p_rs[CF];
 #pragma unroll
-    for (int cf = 0; cf < CF; ++cf)
-        b_rec0[cf] = (size_t)min(n0 / 32 + CF * nh + cf, ntiles_b - 1) * nblk;
+    for (int cf = 0; cf < CF; ++cf) {
+        const size_t rec0 = (size_t)min(n0 / 32 + cf, ntiles_b - 1) * nblk;
+        b_rs[cf] = byte_rsrc(Wp + rec0 * 1024, (unsigned)nblk * 1024u);
+        p_rs[cf] = byte_rsrc(reinterpret_cast<const char *>(Sp) + rec0 * PREC, (unsigned)nblk * PREC);
+    }
+    const unsigned b_off = (unsigned)lane * 16u;
+    const unsigned p_off = HP ? (unsigned)(h * 64 + r * 2) * 4u : (unsigned)r * 8u;
 
-    auto load_a = [&](u4_t (&dst)[4], int kt) {
+    auto load_a = [&](u4_t (&dst)[A_PIECES], int kt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            dst[i] = *reinterpret_cast<const u4_t *>(A_tile + a_off[i] + (unsigned)kt * (BK * 2));
+        for (int i = 0; i < A_PIECES; ++i) dst[i] = buf_load16(a_rs, a_off[i], (unsigned)kt * (BK * 2));
     };
-    // every word ANDed with a uniform mask (all ones, or zero for a block
-    // past the quarter's end): no branch, so no merge point for the
-    // compiler's count of outstanding loads
-    auto store_a = [&](_Float16 *As, const u4_t (&src)[4], unsigned mask) {
+    auto store_a = [&](_Float16 *As, const u4_t (&src)[A_PIECES]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<u4_t *>(As + (32 * nh + 8 * i + arow) * AS_STRIDE + 8 * apc) = src[i] & mask;
+        for (int i = 0; i < A_PIECES; ++i)
+            *reinterpret_cast<u4_t *>(As + (8 * i + arow) * AS_STRIDE + 8 * apc) = src[i];
     };
     auto read_a = [&](const _Float16 *As, int s, h8_t (&af)[RF]) {
 #pragma unroll
         for (int rf = 0; rf < RF; ++rf)
             af[rf] = *reinterpret_cast<const h8_t *>(As + (32 * rf + r) * AS_STRIDE + 32 * h + 8 * s);
     };
-    auto load_b = [&](u4_t (&codes)[CF], f2_t (&pairs)[CF], int kt) {
+    auto load_b = [&](u4_t (&codes)[CF], int kt) {
 #pragma unroll
-        for (int cf = 0; cf < CF; ++cf) {
-            const size_t rec = b_rec0[cf] + kt;
-            codes[cf] = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(Wp + rec * 1024) + lane);
-            pairs[cf] = *reinterpret_cast<const f2_t *>(HP ? Sp + rec * 128 + h * 64 + r * 2
-                                                           : Sp + rec * 64 + r * 2);
-        }
+        for (int cf = 0; cf < CF; ++cf) codes[cf] = buf_load16<kNonTemporal>(b_rs[cf], b_off, (unsigned)kt * 1024u);
+    };
+    auto load_p = [&](f2_t (&pairs)[CF], int kt) {
+#pragma unroll
+        for (int cf = 0; cf < CF; ++cf) pairs[cf] = buf_load8(p_rs[cf], p_off, (unsigned)kt * PREC);
     };
 
     // decode constants, opaque to the optimiser so they stay in registers
@@ -206,9 +255,9 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    u4_t an[RING][4];          // A register ring: stage j holds a block = j mod RING
-    u4_t bc[RING][CF];
-    f2_t bp[RING][CF];
+    u4_t an[A_SETS][A_PIECES];  // A register sets: set j % A_SETS holds block j
+    u4_t bc[B_RING][CF];        // B code ring: slot j % 4 holds block j
+    f2_t bp[P_RING][CF];        // pair ring: slot j % 2 holds block j
     DqParams prm[CF];
     h8_t acur[RF], anxt[RF], bcur[CF], bnxt[CF];
 
@@ -216,53 +265,64 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     // into the quarter (kb0 is valid even for an empty quarter): with no
     // skipped loads the compiler's in-order count of outstanding loads stays
     // exact, so a wait only ever covers the data it needs. What a clamped
-    // load brings is never used: a block past the quarter's end gets an
-    // all-zero A tile instead, and adds exactly zero.
+    // load brings is never used: a block past the quarter's end gets all-zero
+    // dequantisation constants instead (every weight +0), and adds exactly
+    // zero.
     //
-    // prologue: block 0's A in tile 0 and blocks 1 .. RING in flight in the
-    // A ring, B of blocks 0 .. RING - 1 in flight, step (0, 0) operands ready
-    load_a(an[0], kb0);
+    // prologue: A of blocks 0 .. A_SETS - 1 in flight, then the pairs of
+    // blocks 0 and 1 and the codes of blocks 0 .. 3; block 0's A into tile 0
+    // and its step-0 operands ready; A of block A_SETS in flight
 #pragma unroll
-    for (int d = 0; d < RING; ++d) load_b(bc[d], bp[d], min(kb0 + d, last));
-    store_a(a_tile(0), an[0], nb > 0 ? ~0u : 0u);
+    for (int d = 0; d < A_SETS; ++d) load_a(an[d], min(kb0 + d, last));
+    load_p(bp[0], kb0);
+    load_p(bp[1], min(kb0 + 1, last));
 #pragma unroll
-    for (int d = 1; d <= RING; ++d) load_a(an[d % RING], min(kb0 + d, last));
-    __syncthreads();
+    for (int d = 0; d < B_RING; ++d) load_b(bc[d], min(kb0 + d, last));
+    store_a(a_tile(0), an[0]);
+    load_a(an[0], min(kb0 + A_SETS, last));
 #pragma unroll
-    for (int cf = 0; cf < CF; ++cf) prm[cf] = dq_params(bp[0][cf]);
+    for (int cf = 0; cf < CF; ++cf) prm[cf] = dq_params(bp[0][cf], nb > 0);
     read_a(a_tile(0), 0, acur);
 #pragma unroll
     for (int cf = 0; cf < CF; ++cf) bcur[cf] = dequant8(bc[0][cf][0], prm[cf], m_lo, m_hi, magic);
 
-    // Block i uses A tile i % RING and B slot i % RING. A padded block
-    // (i >= nb) has an all-zero A tile and adds exactly zero.
-    for (int base = 0; base < nsteps; base += RING) {
+    // Block i reads A tile i % 2 and B slot i % 4; at its start, block i + 1's
+    // A (register set (i + 1) % A_SETS, loaded A_SETS blocks ago) goes into
+    // tile (i + 1) % 2, whose last reads (block i - 1) were issued before, and
+    // the set then takes block i + 1 + A_SETS.
+    for (int base = 0; base < nsteps; base += UNROLL) {
 #pragma unroll
-        for (int u = 0; u < RING; ++u) {
+        for (int u = 0; u < UNROLL; ++u) {
             const int i = base + u;
-            // block i + 1's A (loaded RING blocks ago) into its tile, which
-            // was last read in block i - 3, before the previous barrier; its
-            // ring stage then takes block i + 1 + RING
-            store_a(a_tile((u + 1) % RING), an[(u + 1) % RING], i + 1 < nb ? ~0u : 0u);
-            load_a(an[(u + 1) % RING], min(kb0 + i + 1 + RING, last));
-            __syncthreads();
+            const int sa = (u + 1) % A_SETS;
+            store_a(a_tile((u + 1) % A_TILES), an[sa]);
+            load_a(an[sa], min(kb0 + i + 1 + A_SETS, last));
+            // pair slot i % 2 was last read for block i's constants (end of
+            // block i - 1): it takes block i + 2
+            load_p(bp[u % P_RING], min(kb0 + i + P_RING, last));
+            // keep the loads here, ahead of the arithmetic: moved down next to
+            // their use they would wait for memory instead of hiding it
+            __builtin_amdgcn_sched_barrier(0);
             // four MFMA steps; while the matrix cores work on step s the
             // operands of the next step (this block's s + 1, or the next
             // block's step 0) are read and dequantised
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 if (s < 3) {
-                    read_a(a_tile(u), s + 1, anxt);
-#pragma unroll
-                    for (int cf = 0; cf < CF; ++cf)
-                        bnxt[cf] = dequant8(bc[u][cf][s + 1], prm[cf], m_lo, m_hi, magic);
-                } else {
-                    const int un = (u + 1) % RING;
-                    read_a(a_tile(un), 0, anxt);
+                    read_a(a_tile(u % A_TILES), s + 1, anxt);
 #pragma unroll
                     for (int cf = 0; cf < CF; ++cf) {
-                        prm[cf] = dq_params(bp[un][cf]);
+                        bnxt[cf] = dequant8(bc[u][cf][s + 1], prm[cf], m_lo, m_hi, magic);
+                        pin(bnxt[cf]);
+                    }
+                } else {
+                    const int un = (u + 1) % B_RING;
+                    read_a(a_tile((u + 1) % A_TILES), 0, anxt);
+#pragma unroll
+                    for (int cf = 0; cf < CF; ++cf) {
+                        prm[cf] = dq_params(bp[(u + 1) % P_RING][cf], i + 1 < nb);
                         bnxt[cf] = dequant8(bc[un][cf][0], prm[cf], m_lo, m_hi, magic);
+                        pin(bnxt[cf]);
                     }
                 }
 #pragma unroll
@@ -273,22 +333,29 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
 #pragma unroll
                 for (int j = 0; j < RF * CF; ++j) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
                 }
+                // one MFMA step per scheduling region: the next step's MFMAs,
+                // each on an accumulator of this step, stay RF * CF apart
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int rf = 0; rf < RF; ++rf) acur[rf] = anxt[rf];
 #pragma unroll
                 for (int cf = 0; cf < CF; ++cf) bcur[cf] = bnxt[cf];
+                // slot u is free once its last codes were dequantised (step
+                // 2): refill it with block i + 4
+                if (s == 2) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_b(bc[u], min(kb0 + i + B_RING, last));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
-            // slot u is free now (its last use was the dequantisation in
-            // step 2): refill it with block i + RING
-            load_b(bc[u], bp[u], min(kb0 + i + RING, last));
         }
     }
 
-    // ---- the eight partial tiles to LDS (reusing the A tiles' space) ----
+    // ---- the four partial tiles to LDS (reusing the A tiles' space) ----
     __syncthreads();
-    float *red = reinterpret_cast<float *>(lds) + (size_t)wave * BM * RED_STRIDE;
+    float *red = reinterpret_cast<float *>(lds) + (size_t)kq * BM * RED_STRIDE;
 #pragma unroll
     for (int rf = 0; rf < RF; ++rf)
 #pragma unroll
@@ -299,23 +366,22 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     __syncthreads();
 
     // ---- sum the four K quarters in a fixed order and store:
-    //      thread -> row tid / 8, 16 columns ----
-    const int row = tid >> 3;
-    const int c0 = (tid & 7) * 16;                 // column in the 128-wide tile
+    //      thread -> one row, 32 consecutive columns ----
+    constexpr int TPR = 64 * NWAVE / BM;           // threads per row
+    const int row = tid / TPR;
+    const int c0 = (tid % TPR) * 32;               // column in the tile
     const int gm = m0 + row;
     if (gm >= M) return;
-    const int half = c0 / WN, ch = c0 % WN;
     const float *red0 = reinterpret_cast<const float *>(lds);
     float *dst = out + (size_t)gm * N + n0 + c0;
-    const bool vec_store = (N & 3) == 0 && n0 + c0 + 16 <= N;
+    const bool vec_store = (N & 3) == 0 && n0 + c0 + 32 <= N;
 #pragma unroll
-    for (int j = 0; j < 16; j += 4) {
-        const size_t o = (size_t)row * RED_STRIDE + ch + j;
+    for (int j = 0; j < 32; j += 4) {
+        const size_t o = (size_t)row * RED_STRIDE + c0 + j;
         const size_t W = (size_t)BM * RED_STRIDE;
-        f4_t sum = *reinterpret_cast<const f4_t *>(red0 + (size_t)half * W + o);
+        f4_t sum = *reinterpret_cast<const f4_t *>(red0 + o);
 #pragma unroll
-        for (int q = 1; q < 4; ++q)
-            sum += *reinterpret_cast<const f4_t *>(red0 + (size_t)(2 * q + half) * W + o);
+        for (int q = 1; q < NWAVE; ++q) sum += *reinterpret_cast<const f4_t *>(red0 + (size_t)q * W + o);
         if (!raw && vec_store) {
             epi_put4(epi, C, gm, n0 + c0 + j, N, sum);
         } else if (!raw) {
@@ -332,10 +398,11 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     }
 }
 
-hipError_t launch_gemm_int4b64(int M, int K, int N, const void *A, const void *Wp,
-                               const void *Sp, void *C, const Epilogue &epi, int half_pairs,
-                               int nsplit, float *part, hipStream_t s) {
-    const int tiles_m = div_up(M, BM), tiles_n = div_up(N, BN);
+template <class T>
+static hipError_t launch_tiles(int M, int K, int N, const void *A, const void *Wp, const void *Sp,
+                               void *out, const Epilogue &epi, int half_pairs, int nsplit,
+                               hipStream_t s) {
+    const int tiles_m = div_up(M, T::BM), tiles_n = div_up(N, T::BN);
     // XCD grid: row bands x column bands = 8, each XCD's L2 then fetches
     // A of its row band and B of its column band; pick the grid the tile
     // counts divide that fetches the fewest bytes (0: plain order)
@@ -348,12 +415,21 @@ hipError_t launch_gemm_int4b64(int M, int K, int N, const void *A, const void *W
         const double fetched = gc * a_bytes + gr * b_bytes;
         if (xcd_rows == 0 || fetched < best) { xcd_rows = gr; best = fetched; }
     }
-    void *out = nsplit > 1 ? static_cast<void *>(part) : C;
-    auto kernel = half_pairs ? gemm_int4b64_kernel<true> : gemm_int4b64_kernel<false>;
+    auto kernel = half_pairs ? gemm_int4b64_kernel<T, true> : gemm_int4b64_kernel<T, false>;
     hipLaunchKernelGGL(kernel, dim3(tiles_m * tiles_n, nsplit), dim3(64 * NWAVE), 0, s,
                        M, K, N, tiles_m, tiles_n, xcd_rows, static_cast<const _Float16 *>(A),
                        static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), out, epi);
-    hipError_t e = hipGetLastError();
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_int4b64(int M, int K, int N, const void *A, const void *Wp,
+                               const void *Sp, void *C, const Epilogue &epi, int half_pairs,
+                               int nsplit, float *part, hipStream_t s) {
+    void *out = nsplit > 1 ? static_cast<void *>(part) : C;
+    const Int4Tile t = int4_tile(M);
+    hipError_t e = t.bm == 128
+        ? launch_tiles<TileCfg<128, 64>>(M, K, N, A, Wp, Sp, out, epi, half_pairs, nsplit, s)
+        : launch_tiles<TileCfg<64, 128>>(M, K, N, A, Wp, Sp, out, epi, half_pairs, nsplit, s);
     if (e != hipSuccess || nsplit <= 1) return e;
     return launch_splitk_reduce_f32(part, nsplit, M, N, C, epi, s);
 }

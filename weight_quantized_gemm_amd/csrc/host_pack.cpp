@@ -126,7 +126,7 @@ int splitk_plan(qgemm_format f, int M, int K, int N) {
     switch (f) {
     case QGEMM_INT4_B64:
     case QGEMM_INT4_B0:
-        tiles = (long long)div_up(M, kInt4TileM) * div_up(N, kInt4TileN);
+        tiles = (long long)div_up(M, int4_tile(M).bm) * div_up(N, int4_tile(M).bn);
         kunits = K / 64 / 8;         // four waves, two or more 64-blocks each
         break;
     case QGEMM_F32: {

@@ -187,8 +187,12 @@ W4A8Workspace w4a8_workspace(int M, int K);
 // plan is a pure function of the shape (sized for a 256-CU part), so the
 // workspace size never depends on the device.
 // Output tile of the Int4-Block64 prefill GEMM (rows x columns), shared by
-// the kernel and the split-K planner.
-constexpr int kInt4TileM = 64, kInt4TileN = 128;
+// the kernel and the split-K planner: 128 x 64 once M reaches 128 (each
+// dequantised weight serves 128 rows), else 64 x 128.
+struct Int4Tile {
+    int bm, bn;
+};
+inline Int4Tile int4_tile(int M) { return M >= 128 ? Int4Tile{128, 64} : Int4Tile{64, 128}; }
 // Output tile of the channel-row (Int8-Block0, fp16-weight) prefill GEMM.
 constexpr int kRowsTileM = 128, kRowsTileN = 64;
 // Output tile of the W4A8 prefill GEMM and its K stage (qa bytes per row).
