@@ -323,6 +323,32 @@ qgemm_status qgemm_run_ex(int M, int K, int N, qgemm_format f, const void *A,
                           size_t ws_bytes, void *stream);
 
 /*
+ * qgemm_run_ex (fused epilogue, NULL for none) for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation. It calls no hipMalloc, hipFree or other
+ * allocating routine. Whatever scratch the shape needs (W4A8 activation
+ * codes, split-K partial tiles; qgemm_workspace_size reports it) lives in
+ * one fixed array of QGEMM_NOALLOC_SCRATCH_BYTES in each GPU's memory,
+ * reserved when the library's code is loaded on that GPU and held until the
+ * process ends. Its address is looked up once per device, on the first call
+ * on that device.
+ *
+ * Every call on one GPU shares that array and leaves its contents behind
+ * (no call relies on them): calls that may overlap on one GPU (different
+ * streams, or different host threads without ordering) race on it and
+ * must be serialised by the caller. Calls on different GPUs do not
+ * interact.
+ *
+ * Errors: as qgemm_run_ex, plus QGEMM_ERR_SIZE, checked before anything is
+ * enqueued, when the shape needs more scratch than
+ * QGEMM_NOALLOC_SCRATCH_BYTES (use qgemm_run_ex with a workspace then).
+ */
+#define QGEMM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+qgemm_status qgemm_run_noalloc(int M, int K, int N, qgemm_format f, const void *A,
+                               const void *Bq, const void *scales, void *C,
+                               const qgemm_epilogue *epi, void *stream);
+
+/*
  * W4A8 with its intermediate results exposed, for bit-exact checks of the
  * integer path: the quantised activations qa (int8 [M][K]), the row scales
  * sa (float [M]), the row sums S of qa (int32 [M]) and the exact integer

@@ -456,3 +456,19 @@ def test_packed_weight_checks_activation_shape():
     w.fmt, w.K, w.N = Q.QGEMM_INT4_B64, K, N
     with pytest.raises(ValueError, match="shape"):
         w(torch.zeros((2, K + 64), dtype=torch.float16))
+
+
+def test_noalloc_rejects_oversized_scratch_before_device(lib):
+    """qgemm_run_noalloc refuses a shape whose scratch exceeds its fixed
+    per-GPU array with QGEMM_ERR_SIZE, before any device call (no GPU here);
+    a shape that fits gets past the size check and stops at the device check."""
+    SIZE, DEV = 8, 6
+    v = ctypes.c_void_p
+    big = (65536, 1024, 64)                      # W4A8 codes alone: 64 MiB
+    assert Q.qgemm_workspace_size(*big, "w4a8") > Q.NOALLOC_SCRATCH_BYTES
+    st = lib.qgemm_run_noalloc(*big, Q.QGEMM_W4A8, v(256), v(256), v(256), v(256), None, None)
+    assert st == SIZE
+    small = (64, 1024, 64)
+    assert 0 < Q.qgemm_workspace_size(*small, "w4a8") <= Q.NOALLOC_SCRATCH_BYTES
+    st = lib.qgemm_run_noalloc(*small, Q.QGEMM_W4A8, v(256), v(256), v(256), v(256), None, None)
+    assert st == DEV

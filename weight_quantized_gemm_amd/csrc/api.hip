@@ -9,6 +9,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "qgemm_internal.h"
 
@@ -194,6 +195,37 @@ static qgemm_status dispatch(int M, int K, int N, qgemm_format f, const Geometry
     return QGEMM_ERR_FORMAT;
 }
 
+// Scratch of qgemm_run_noalloc: one array in each GPU's memory, reserved
+// when this code object is loaded on the device. In host code the array's
+// name is only a stand-in: its device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current,
+// and only that address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[QGEMM_NOALLOC_SCRATCH_BYTES];
+static std::atomic<void *> g_scratch_ptr[64];
+static std::mutex g_scratch_mutex;
+
+static qgemm_status scratch_address(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return QGEMM_ERR_DEVICE;
+    }
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+                (void)hipGetLastError();
+                return QGEMM_ERR_DEVICE;
+            }
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return QGEMM_OK;
+}
+
 }  // namespace qg
 
 using namespace qg;
@@ -241,6 +273,29 @@ qgemm_status qgemm_run_ex(int M, int K, int N, qgemm_format f, const void *A,
         if (st == QGEMM_OK) st = QGEMM_ERR_LAUNCH;
     }
     return st;
+}
+
+qgemm_status qgemm_run_noalloc(int M, int K, int N, qgemm_format f, const void *A,
+                               const void *Bq, const void *scales, void *C,
+                               const qgemm_epilogue *epilogue, void *stream) {
+    Geometry g;
+    bool empty = false;
+    qgemm_status st = check_run(M, K, N, f, A, Bq, scales, C, &g, &empty);
+    if (st != QGEMM_OK || empty) return st;
+    Epilogue epi;
+    st = make_epilogue(epilogue, &epi);
+    if (st != QGEMM_OK) return st;
+    const CallPlan plan = plan_call(f, M, K, N);
+    const size_t need = plan.used_bytes();
+    if (need > QGEMM_NOALLOC_SCRATCH_BYTES) return QGEMM_ERR_SIZE;
+    st = check_device();
+    if (st != QGEMM_OK) return st;
+    void *ws = nullptr;
+    if (need > 0) {
+        st = scratch_address(&ws);
+        if (st != QGEMM_OK) return st;
+    }
+    return dispatch(M, K, N, f, g, plan, A, Bq, scales, C, epi, ws, static_cast<hipStream_t>(stream));
 }
 
 qgemm_status qgemm_run_ws(int M, int K, int N, qgemm_format f, const void *A,

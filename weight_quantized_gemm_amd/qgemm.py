@@ -35,7 +35,7 @@ STATUS = {0: "QGEMM_OK", 1: "QGEMM_ERR_NULL", 2: "QGEMM_ERR_SHAPE", 3: "QGEMM_ER
 EXPORTS = ["qgemm_status_string", "qgemm_abi_version", "qgemm_canonical_size",
            "qgemm_quantize_weights", "qgemm_packed_size", "qgemm_pack_weights",
            "qgemm_unpack_weights", "qgemm_workspace_size", "qgemm_run", "qgemm_run_ws",
-           "qgemm_run_ex", "qgemm_w4a8_debug", "qgemm_set_gemv_max_m",
+           "qgemm_run_ex", "qgemm_run_noalloc", "qgemm_w4a8_debug", "qgemm_set_gemv_max_m",
            "qgemm_quantize_weights_device", "qgemm_quantize_pack_device"]
 
 
@@ -72,6 +72,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "qgemm_run": ([I, I, I, I, P, P, P, P, P], I),
         "qgemm_run_ws": ([I, I, I, I, P, P, P, P, P, Z, P], I),
         "qgemm_run_ex": ([I, I, I, I, P, P, P, P, ctypes.POINTER(Epilogue), P, Z, P], I),
+        "qgemm_run_noalloc": ([I, I, I, I, P, P, P, P, ctypes.POINTER(Epilogue), P], I),
         "qgemm_w4a8_debug": ([I, I, I, P, P, P, P, P, P, P, P, P, Z, P], I),
         "qgemm_set_gemv_max_m": ([I], I),
         "qgemm_quantize_weights_device": ([I, I, I, P, P, P, P], I),
@@ -322,6 +323,24 @@ def qgemm_run_ex(M: int, K: int, N: int, fmt, A, Bq, scales, C, bias=None, resid
     _check(load().qgemm_run_ex(M, K, N, _fmt(fmt), _dev_ptr(A), _dev_ptr(Bq), _dev_ptr(scales),
                                _dev_ptr(C), ctypes.byref(epi), _dev_ptr(workspace), ws_bytes,
                                _stream(stream)), "qgemm_run_ex")
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # QGEMM_NOALLOC_SCRATCH_BYTES
+
+
+def qgemm_run_noalloc(M: int, K: int, N: int, fmt, A, Bq, scales, C, bias=None, residual=None,
+                      activation="none", out_type="f32", stream=None) -> None:
+    """qgemm_run_ex without any allocation: the scratch the shape needs lives in
+    the library's fixed per-GPU array (NOALLOC_SCRATCH_BYTES); calls that may
+    overlap on one GPU must be serialised by the caller."""
+    _check_run_args(M, K, N, fmt, A, Bq, scales, C, out_type=out_type, bias=bias,
+                    residual=residual)
+    epi = Epilogue(_dev_ptr(bias), _dev_ptr(residual),
+                   ACTIVATIONS[activation] if isinstance(activation, str) else int(activation),
+                   OUT_TYPES[out_type] if isinstance(out_type, str) else int(out_type))
+    _check(load().qgemm_run_noalloc(M, K, N, _fmt(fmt), _dev_ptr(A), _dev_ptr(Bq), _dev_ptr(scales),
+                                    _dev_ptr(C), ctypes.byref(epi), _stream(stream)),
+           "qgemm_run_noalloc")
 
 
 def qgemm_w4a8_debug(M: int, K: int, N: int, A, Bq, scales, C, qa, sa, S, D, workspace,
