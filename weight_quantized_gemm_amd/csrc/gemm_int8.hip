@@ -62,8 +62,12 @@ constexpr int A_TILE = BM * AS_STRIDE;            // halves per A tile
 constexpr int A_PIECES = BM * BK / 8 / 64;        // 16-byte A pieces per lane and block (16)
 // A and B are loaded DEPTH blocks ahead through register rings; the loop is
 // unrolled DEPTH times so every ring slot is a fixed register, and each wave
-// has DEPTH LDS tiles for A.
+// has DEPTH LDS tiles for A. The any-K mode (KMODE 2) loads A element by
+// element, eight registers per 16-byte piece, and keeps one block in flight
+// (two would not fit the register file beside the accumulators).
 constexpr int DEPTH = 2;
+template <int KMODE>
+constexpr int depth_of() { return KMODE == 2 ? 1 : DEPTH; }
 constexpr size_t A_LDS = (size_t)4 * DEPTH * A_TILE * 2;
 constexpr size_t RED_LDS = (size_t)4 * BM * RED_STRIDE * 4 + (size_t)4 * BM * 4;
 constexpr size_t ROWS_LDS = A_LDS > RED_LDS ? A_LDS : RED_LDS;
@@ -103,6 +107,7 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
     const uint8_t *__restrict__ Wp, const float *__restrict__ Sp, void *__restrict__ C,
     Epilogue epi) {
     __shared__ __align__(16) unsigned char lds[ROWS_LDS];
+    constexpr int DEPTH = depth_of<KMODE>();
 
     // Tile of this workgroup. With xcd_order, the workgroups the hardware
     // deals to one XCD (ids equal mod 8) get a contiguous run of tiles.
@@ -169,6 +174,9 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
                     t8[e] = k + e < K ? v : (_Float16)0.0f;
                 }
                 dst[i] = __builtin_bit_cast(u4_t, t8);
+                // element loads: at most four pieces (32 loads) in flight, so
+                // their destination registers fit beside the accumulators
+                if (i % 4 == 3) __builtin_amdgcn_sched_barrier(0);
             }
         }
     };

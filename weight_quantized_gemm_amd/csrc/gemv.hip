@@ -143,6 +143,11 @@ __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
             const int bl = wave + TILE_WAVES * i;
             if (bl >= pb) break;                             // wave-uniform
             const int hbg = 2 * bl + h;                      // half-block within the pass
+            // row strides, opaque per block: computed here rather than for
+            // every (row, block) up front, where they would hold more
+            // registers than a 1024-thread workgroup has
+            int pm = pmax;
+            asm volatile("" : "+s"(pm));
             const float off = pr[i].x, sc = pr[i].y;
             const float ce = fmaf(-1024.0f, sc, off);
             const float co = fmaf(-64.0f, sc, off);
@@ -151,7 +156,7 @@ __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
                 float Te = 0.f, To = 0.f;
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
-                    const u4_t av = ap[(size_t)r * (pmax * 8) + hbg * 4 + d];
+                    const u4_t av = ap[(size_t)r * (pm * 8) + hbg * 4 + d];
                     const unsigned word = wq[i][d];
                     const unsigned y0 = __builtin_amdgcn_perm(magic, word, 0x04020400u);
                     const unsigned y1 = __builtin_amdgcn_perm(magic, word, 0x04030401u);
@@ -160,7 +165,7 @@ __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
                     To = dot2(as_h2(y0 & 0xFFF0FFF0u), as_h2(av.z), To);
                     To = dot2(as_h2(y1 & 0xFFF0FFF0u), as_h2(av.w), To);
                 }
-                const f2_t sv = hs[(size_t)r * (2 * pmax) + hbg];
+                const f2_t sv = hs[(size_t)r * (2 * pm) + hbg];
                 acc[r] += fmaf(ce, sv.x, fmaf(co, sv.y, fmaf(sc, Te, sc * 0.0625f * To)));
             }
         }

@@ -52,42 +52,43 @@ __device__ __forceinline__ void block_sum_store(int v, int *red4, int32_t *dst) 
     if (threadIdx.x == 0) *dst = red4[0] + red4[1] + red4[2] + red4[3];
 }
 
-// K % 8 == 0 and Kq <= 512 * NCH (up to 16384): one wave per row (four rows per
-// workgroup). Every lane requests its NCH 8-element chunks of the row at once,
-// the maximum and the sum are wave reductions (no barrier), and each chunk of
-// codes leaves as one 8-byte store; chunks past K store zeros up to Kq.
-template <int NCH>
-__global__ __launch_bounds__(256) void w4a8_actquant_wave_kernel(int M, int K, int Kq,
-                                                                 const _Float16 *__restrict__ A,
-                                                                 int8_t *__restrict__ qa,
-                                                                 float *__restrict__ sa,
-                                                                 int32_t *__restrict__ S) {
-    const int lane = threadIdx.x & 63;
-    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (m >= M) return;                                   // whole waves
+// K % 8 == 0 and Kq <= 2048 * NPT: one 256-thread workgroup per row (four
+// waves per row, sixteen per CU at M = 1024, so a SIMD starts quantising as
+// soon as the chunks of one of its waves have arrived). Thread t requests
+// the row's 8-element chunks t, t + 256, ... at once (clamped, so every load
+// is unconditional); the maximum and the sum meet in LDS once each.
+template <int NPT>
+__global__ __launch_bounds__(256) void w4a8_actquant_row_kernel(int K, int Kq,
+                                                                const _Float16 *__restrict__ A,
+                                                                int8_t *__restrict__ qa,
+                                                                float *__restrict__ sa,
+                                                                int32_t *__restrict__ S) {
+    __shared__ float red_f[4];
+    __shared__ int red_i[4];
+    const int m = blockIdx.x;
+    const int tid = threadIdx.x;
     const _Float16 *row = A + (size_t)m * K;
     int8_t *qrow = qa + (size_t)m * Kq;
     const int nch = K >> 3, nchq = Kq >> 3;
-    h8_t v[NCH];
+    h8_t v[NPT];
 #pragma unroll
-    for (int i = 0; i < NCH; ++i)
-        v[i] = *reinterpret_cast<const h8_t *>(row + 8 * min(lane + 64 * i, nch - 1));
-    float amax = 0.0f;
+    for (int i = 0; i < NPT; ++i)
+        v[i] = *reinterpret_cast<const h8_t *>(row + 8 * min(tid + 256 * i, nch - 1));
+    float mx = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        float mx = 0.0f;
+    for (int i = 0; i < NPT; ++i) {
+        float c = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf((float)v[i][e]));
-        amax = lane + 64 * i < nch ? fmaxf(amax, mx) : amax;
+        for (int e = 0; e < 8; ++e) c = fmaxf(c, fabsf((float)v[i][e]));
+        mx = tid + 256 * i < nch ? fmaxf(mx, c) : mx;
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const float amax = block_max(mx, red_f);
     const float s = amax / 127.0f;           // IEEE division, one rounding
     const float rs = 1.0f / s;               // IEEE division, one rounding
     int sum = 0;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const int c = lane + 64 * i;
+    for (int i = 0; i < NPT; ++i) {
+        const int c = tid + 256 * i;
         if (c >= nchq) continue;
         unsigned lo = 0u, hi = 0u;
         if (c < nch && amax != 0.0f) {
@@ -102,12 +103,8 @@ __global__ __launch_bounds__(256) void w4a8_actquant_wave_kernel(int M, int K, i
         }
         *reinterpret_cast<u2_t *>(qrow + 8 * c) = u2_t{lo, hi};
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-    if (lane == 0) {
-        sa[m] = amax != 0.0f ? s : 0.0f;
-        S[m] = sum;
-    }
+    if (tid == 0) sa[m] = amax != 0.0f ? s : 0.0f;
+    block_sum_store(sum, red_i, S + m);
 }
 
 // Any even K: two passes over the row, element by element.
@@ -141,21 +138,17 @@ __global__ __launch_bounds__(256) void w4a8_actquant_kernel(int K, int Kq,
 hipError_t launch_w4a8_actquant(int M, int K, int Kq, const void *A, int8_t *qa, float *sa,
                                 int32_t *S, hipStream_t s) {
     const _Float16 *a = static_cast<const _Float16 *>(A);
-    const dim3 waves4(div_up(M, 4));
-    if ((K & 7) == 0 && Kq <= 512 * 2)
-        hipLaunchKernelGGL(w4a8_actquant_wave_kernel<2>, waves4, dim3(256), 0, s, M, K, Kq, a, qa, sa, S);
-    else if ((K & 7) == 0 && Kq <= 512 * 4)
-        hipLaunchKernelGGL(w4a8_actquant_wave_kernel<4>, waves4, dim3(256), 0, s, M, K, Kq, a, qa, sa, S);
-    else if ((K & 7) == 0 && Kq <= 512 * 8)
-        hipLaunchKernelGGL(w4a8_actquant_wave_kernel<8>, waves4, dim3(256), 0, s, M, K, Kq, a, qa, sa, S);
-    else if ((K & 7) == 0 && Kq <= 512 * 16)
-        hipLaunchKernelGGL(w4a8_actquant_wave_kernel<16>, waves4, dim3(256), 0, s, M, K, Kq, a, qa, sa, S);
-    else if ((K & 7) == 0 && Kq <= 512 * 24)
-        hipLaunchKernelGGL(w4a8_actquant_wave_kernel<24>, waves4, dim3(256), 0, s, M, K, Kq, a, qa, sa, S);
-    else if ((K & 7) == 0 && Kq <= 512 * 32)
-        hipLaunchKernelGGL(w4a8_actquant_wave_kernel<32>, waves4, dim3(256), 0, s, M, K, Kq, a, qa, sa, S);
+    const dim3 rows(M);
+    if ((K & 7) == 0 && Kq <= 2048 * 1)
+        hipLaunchKernelGGL(w4a8_actquant_row_kernel<1>, rows, dim3(256), 0, s, K, Kq, a, qa, sa, S);
+    else if ((K & 7) == 0 && Kq <= 2048 * 2)
+        hipLaunchKernelGGL(w4a8_actquant_row_kernel<2>, rows, dim3(256), 0, s, K, Kq, a, qa, sa, S);
+    else if ((K & 7) == 0 && Kq <= 2048 * 4)
+        hipLaunchKernelGGL(w4a8_actquant_row_kernel<4>, rows, dim3(256), 0, s, K, Kq, a, qa, sa, S);
+    else if ((K & 7) == 0 && Kq <= 2048 * 8)
+        hipLaunchKernelGGL(w4a8_actquant_row_kernel<8>, rows, dim3(256), 0, s, K, Kq, a, qa, sa, S);
     else
-        hipLaunchKernelGGL(w4a8_actquant_kernel, dim3(M), dim3(256), 0, s, K, Kq, a, qa, sa, S);
+        hipLaunchKernelGGL(w4a8_actquant_kernel, rows, dim3(256), 0, s, K, Kq, a, qa, sa, S);
     return hipGetLastError();
 }
 
