@@ -22,6 +22,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -148,9 +149,40 @@ def traffic_record(kernel_src: str, kernel: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(dec: Workload, pre: Workload, budget_s: float):
+PARITY_MAX_ABS, PARITY_REL_F = 1e-2, 2e-3     # the tolerances of the parity tests
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _omp_threads(n: int | None):
+    """Sets the OpenMP thread count of this process (the oracle's runtime);
+    returns the previous count, or None when libgomp is not loaded."""
+    import ctypes
+    try:
+        gomp = ctypes.CDLL("libgomp.so.1")
+    except OSError:
+        return None
+    prev = gomp.omp_get_max_threads()
+    if n is not None:
+        gomp.omp_set_num_threads(int(n))
+    return prev
+
+
+def oracle_pass(dec: Workload, pre: Workload, budget_s: float):
     """The CPU oracle, as it stands, on a bounded sample of the step: the full
-    decode GEMV and a row sample of the prefill, scaled to one step."""
+    decode GEMV and a row sample of the prefill, timed and scaled to one step
+    (cpu_baseline), and the parity gate on the same sample: the GPU's outputs
+    of the same inputs against the oracle's, to the parity tests' tolerances
+    (max-abs 1e-2, relative Frobenius 2e-3)."""
     from oracle import oracle as O
     threads = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
     lib = O.load()
@@ -158,6 +190,12 @@ def cpu_baseline(dec: Workload, pre: Workload, budget_s: float):
     t0 = time.perf_counter()
     c_dec = O.gemm_blockq(dec.A_host, q, p, "int4b64", lib)
     t_dec = time.perf_counter() - t0
+    # the same decode GEMV on one host thread
+    prev = _omp_threads(1)
+    t0 = time.perf_counter()
+    O.gemm_blockq(dec.A_host, q, p, "int4b64", lib)
+    t_dec_1 = time.perf_counter() - t0
+    _omp_threads(prev)
     qp, pp = O.quantize(pre.W_host, "int4b64")
     probe = 2
     t0 = time.perf_counter()
@@ -170,11 +208,20 @@ def cpu_baseline(dec: Workload, pre: Workload, budget_s: float):
     t_pre = time.perf_counter() - t0
     step_s = t_dec + t_pre * pre.M / rows
     step_flops = flops(dec.M, dec.K, dec.N) + flops(pre.M, pre.K, pre.N)
-    # the GPU's outputs on the same sample
-    g_dec = dec.C[0].cpu().numpy().astype(np.float64)
-    g_pre = pre.C[0].cpu().numpy().astype(np.float64)[sel]
-    err = max(float(np.abs(g_dec - c_dec).max()), float(np.abs(g_pre - c_pre).max()))
-    return {
+    # parity: the GPU's outputs on the same sample
+    g = np.concatenate([dec.C[0].cpu().numpy().astype(np.float64).ravel(),
+                        pre.C[0].cpu().numpy().astype(np.float64)[sel].ravel()])
+    r = np.concatenate([c_dec.ravel(), c_pre.ravel()])
+    err = np.abs(g - r)
+    finite = bool(np.all(np.isfinite(g)))
+    max_abs = float(err.max()) if finite else float("inf")
+    rel_f = float(np.linalg.norm(g - r) / np.linalg.norm(r)) if finite else float("inf")
+    wrong = int(np.count_nonzero(~(err <= PARITY_MAX_ABS)))
+    parity = {"ok": finite and max_abs <= PARITY_MAX_ABS and rel_f <= PARITY_REL_F,
+              "max_abs": max_abs, "rel_F": rel_f, "wrong": wrong, "outputs": int(r.size),
+              "tolerance": {"max_abs": PARITY_MAX_ABS, "rel_F": PARITY_REL_F},
+              "sample": f"decode 1x{dec.N} (all), prefill {rows} of {pre.M} rows x {pre.N}"}
+    baseline = {
         "value": step_flops / step_s / 1e9,
         "unit": "GFLOPS",
         "cores": threads,
@@ -183,8 +230,43 @@ def cpu_baseline(dec: Workload, pre: Workload, budget_s: float):
                    f"(x4096x4096), fp64 naive loops, scaled to one step; "
                    f"{t_dec + t_pre:.1f} s of CPU time"),
         "seconds_per_step": step_s,
-        "gpu_max_abs_err_on_sample": err,
+        "cpu_model": cpu_model(),
+        "decode_seconds_one_thread": t_dec_1,
+        "decode_seconds": t_dec,
     }
+    return baseline, parity
+
+
+def gpu_clocks():
+    """Shader and memory clocks (MHz) and temperatures (C) of the first AMD GPU,
+    read from the amdgpu driver's hwmon files in sysfs (no child process: under
+    a profiler whose preloaded library opens the GPU, a child that re-executes
+    itself is refused); None when they are not readable."""
+    import glob
+
+    def read(path):
+        try:
+            with open(path) as f:
+                return f.read().strip()
+        except OSError:
+            return None
+
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        if read(os.path.join(dev, "vendor")) != "0x1002":
+            continue
+        for hw in sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*"))):
+            out = {"source": "sysfs hwmon"}
+            for i, key in ((1, "sclk_mhz"), (2, "mclk_mhz")):
+                v = read(os.path.join(hw, f"freq{i}_input"))
+                out[key] = int(v) / 1e6 if v and v.isdigit() else None
+            for t in sorted(glob.glob(os.path.join(hw, "temp*_input"))):
+                label = read(t.replace("_input", "_label")) or os.path.basename(t)
+                v = read(t)
+                if v and v.lstrip("-").isdigit():
+                    out["temp_" + label.lower() + "_c"] = int(v) / 1000
+            if len(out) > 1 and any(v is not None for k, v in out.items() if k != "source"):
+                return out
+    return None
 
 
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
@@ -221,8 +303,7 @@ def single_workload(args, torch) -> int:
     with torch.cuda.graph(g):
         for i in range(copies):
             w.run(i)
-    g.replay()
-    torch.cuda.synchronize()
+    warm(torch, g)
     reps = max(1, -(-args.steps // copies))
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -286,6 +367,18 @@ class ShapeWorkload(Workload):
         self.Q = Q
 
 
+def warm(torch, g, seconds: float = 0.1) -> None:
+    """Replays graph `g` for about `seconds` of wall time: an idle GPU's
+    clocks take tens of milliseconds to come back up, and a timed region that
+    starts cold reads low."""
+    t0 = time.perf_counter()
+    while True:
+        g.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return
+
+
 def time_calls(torch, run, copies: int, steps: int) -> float:
     """ms per call: `copies` calls captured in one graph, replayed about
     `steps` times over, HIP events on the launching stream."""
@@ -296,8 +389,7 @@ def time_calls(torch, run, copies: int, steps: int) -> float:
     with torch.cuda.graph(g):
         for i in range(copies):
             run(i)
-    g.replay()
-    torch.cuda.synchronize()
+    warm(torch, g)
     reps = max(1, -(-steps // copies))
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -567,8 +659,11 @@ def peak_probes(args, torch) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 2000; 200 launches per shape for the diagnostics)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps right before the timed ones (default 2000; "
+                         "10 eager calls for the diagnostics)")
     ap.add_argument("--copies", type=int, default=0, help="rotation copies (0: auto)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of CPU oracle work for cpu_baseline")
@@ -598,10 +693,19 @@ def main() -> int:
     ap.add_argument("--peak", action="store_true",
                     help="measured peaks of this chip for plain kernels (HBM read stream and copy, "
                          "fp16 MFMA loop with the shader clock, L2-resident reads), one JSON line each")
+    ap.add_argument("--context", action="store_true",
+                    help="also time a cache-resident step (one copy of the inputs, replayed); "
+                         "context only, off by default")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch's plain device copy of MIB MiB (fp32) 10 times, "
                          "the reference kernel for scaling the HBM byte counters")
     args = ap.parse_args()
+    diagnostic = bool(args.workload or args.page_grid or args.shape or args.quantizer
+                      or args.vendor_reference or args.peak)
+    if args.steps is None:
+        args.steps = 200 if diagnostic else 2000
+    if args.warmup is None:
+        args.warmup = 10 if diagnostic else 2000
 
     if args.gpus != 1:
         print(f"bench.py: the library runs on exactly one GPU (asked for --gpus {args.gpus}); "
@@ -644,23 +748,30 @@ def main() -> int:
     if args.page_grid:
         return page_grid(args, torch)
 
+    clocks_before = gpu_clocks()
     # one decode + one prefill copy is ~50 MB; rotate past 2x the MALL
-    per_step_bytes = (algorithmic_bytes(1, 4096, 11008) + algorithmic_bytes(512, 4096, 4096))
-    copies = args.copies or max(2, -(-2 * MALL_BYTES // per_step_bytes) + 1)
+    # Rotation: every launch reads inputs no launch of the last ~4 x the
+    # last-level cache's capacity touched, for the step and for each kernel
+    # repeated on its own (the smaller per-kernel footprint sets the count).
+    per_kernel_bytes = min(algorithmic_bytes(1, 4096, 11008), algorithmic_bytes(512, 4096, 4096))
+    copies = args.copies or max(2, -(-4 * MALL_BYTES // per_kernel_bytes) + 1)
     dec = Workload(DECODE, copies)
     pre = Workload(PREFILL, copies)
 
-    for i in range(args.warmup):
+    for i in range(copies):
         pre.run(i)
         dec.run(i)
     torch.cuda.synchronize()
 
+    # Parity gate, before anything is timed: the outputs of copy 0 against
+    # the CPU oracle on the same inputs. The oracle's time on that sample is
+    # the cpu_baseline.
+    baseline, parity = oracle_pass(dec, pre, args.cpu_budget)
+
     # One graph holds `copies` steps (prefill then decode, each on its own
     # rotation copy); replaying it keeps the GPU fed without per-launch host
-    # work. A second graph holds the remaining steps % copies steps, so the
-    # timed region runs exactly --steps steps. Two more graphs hold `copies`
-    # back-to-back launches of one kernel each and give that kernel's average
-    # launch duration.
+    # work. Graphs of the remaining steps make the warm-up and the timed
+    # region run exactly --warmup and --steps steps.
     def capture(fn, count):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -668,15 +779,16 @@ def main() -> int:
                 fn(i)
         return g
 
-    full, rem = divmod(args.steps, copies)
+    def steps_graphs(n):
+        full, rem = divmod(n, copies)
+        return [g_step] * full + ([capture(step, rem)] if rem else [])
+
     step = lambda i: (pre.run(i), dec.run(i))
     g_step = capture(step, copies)
-    g_rem = capture(step, rem) if rem else None
-    g_pre = capture(pre.run, copies)
-    g_dec = capture(dec.run, copies)
-    for g in (g_step, g_rem, g_pre, g_dec):
-        if g is not None:
-            g.replay()
+    timed_graphs = steps_graphs(args.steps)
+    warm_graphs = steps_graphs(args.warmup)
+    for g in set(timed_graphs + warm_graphs):
+        g.replay()
     torch.cuda.synchronize()
 
     def timed(graphs, launches):
@@ -695,11 +807,35 @@ def main() -> int:
         wall = (time.perf_counter() - t0) * 1e3
         return start.elapsed_time(stop) / launches, wall / launches
 
+    # Warm-up right before the timed region: the GPU idles while the oracle
+    # runs on the CPU, and its clocks take tens of milliseconds to come back.
     K = args.steps
-    ms_step, wall_ms_step = timed([g_step] * full + ([g_rem] if g_rem else []), K)
-    kr = max(1, -(-K // copies))              # kernel-only graphs: about K launches each
+    timed(warm_graphs, max(1, args.warmup))
+    ms_step, wall_ms_step = timed(timed_graphs, K)
+
+    # Each kernel's average launch duration: a graph of back-to-back launches
+    # of that kernel alone over all rotation copies (each launch reads its
+    # inputs from HBM, as in the step), events around the replays on the
+    # launching stream, divided by the launches. In-step durations from a
+    # kernel trace of this same run agree with these within a few percent.
+    kr = max(1, -(-K // copies))
+    g_pre = capture(pre.run, copies)
+    g_dec = capture(dec.run, copies)
+    for g in (g_pre, g_dec):
+        g.replay()
+    torch.cuda.synchronize()
     pre_ms, _ = timed([g_pre] * kr, kr * copies)
     dec_ms, _ = timed([g_dec] * kr, kr * copies)
+    how = ("graph of back-to-back launches of this kernel over all rotation copies, "
+           "HIP events around the replays on the launching stream / launches")
+    hot_ms = None
+    if args.context:
+        # cache-resident step on one copy of the inputs: context only, never
+        # the metric
+        g_hot = capture(lambda i: (pre.run(0), dec.run(0)), copies)
+        g_hot.replay()
+        hot_ms, _ = timed([g_hot] * kr, kr * copies)
+    clocks_after = gpu_clocks()
 
     step_flops = flops(dec.M, dec.K, dec.N) + flops(pre.M, pre.K, pre.N)
     value = step_flops / (ms_step * 1e-3) / 1e9
@@ -726,6 +862,8 @@ def main() -> int:
             "rotated_bytes": copies * (dec.bytes_per_copy() + pre.bytes_per_copy()),
             "wall_ms_per_step": wall_ms_step,
             "launch": "HIP graph of rotation-copies steps, replayed",
+            "hot_ms_per_step": hot_ms,
+            "hot_note": "one copy of the inputs (cache-resident), context only",
         },
         "roofline": {
             "bound": "mfma",
@@ -736,6 +874,7 @@ def main() -> int:
             "frac": pre_tflops / FP16_PEAK_TFLOPS,
             "traffic": traffic_record(os.path.join(src, "gemm_int4.hip"), "gemm_int4b64"),
             "avg_launch_ms": pre_ms,
+            "timing": how,
         },
         "decode_roofline": {
             "bound": "hbm",
@@ -747,10 +886,20 @@ def main() -> int:
             "traffic": traffic_record(os.path.join(src, "gemv.hip"), "gemv_int4b64"),
             "avg_launch_ms": dec_ms,
             "gflops": flops(dec.M, dec.K, dec.N) / (dec_ms * 1e-3) / 1e9,
+            "timing": how,
         },
+        "parity": parity,
+        "gpu_clocks": {"before": clocks_before, "after": clocks_after},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(dec, pre, args.cpu_budget)
+        out["cpu_baseline"] = baseline
+    if not parity["ok"]:
+        out["parity_ok"] = False
+        print(json.dumps(out), flush=True)
+        print("bench.py: parity gate failed: the GPU's outputs do not match the oracle "
+              f"(max_abs {parity['max_abs']:.3e}, rel_F {parity['rel_F']:.3e}, "
+              f"{parity['wrong']} of {parity['outputs']} outputs off)", file=sys.stderr)
+        return 3
     print(json.dumps(out), flush=True)
     return 0
 

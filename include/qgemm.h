@@ -233,7 +233,8 @@ qgemm_status qgemm_workspace_size(int M, int K, int N, qgemm_format f,
  * C = A x B on the GPU, enqueued on `stream`; returns without waiting.
  *   A       device, [M][K] row-major: float for F32, fp16 otherwise.
  *   Bq      device, packed weights from qgemm_pack_weights (for F32 the
- *           packed B is the float [K][N] matrix itself).
+ *           packed B is the float [K][N] matrix itself, read no further
+ *           than its K*N elements).
  *   scales  device, packed pairs; must be NULL for F32.
  *   C       device, float [M][N] row-major, fully overwritten (no alpha or
  *           beta; K == 0 for F32 writes zeros).

@@ -433,6 +433,16 @@ def test_binding_checks_dtypes_and_sizes_before_the_library():
     Bf = torch.zeros(K * N, dtype=torch.float32)
     with pytest.raises(ValueError, match="dtype"):
         Q.qgemm_run(M, K, N, "f32", A16, Bf, None, C32)
+    # the fp32 format's B is the [K][N] matrix itself: exactly K*N floats pass
+    # (137 x 70 x 4 bytes is not a multiple of the packed size's 256-byte
+    # rounding), one float fewer does not
+    Kf, Nf = 137, 70
+    Af = torch.zeros((M, Kf), dtype=torch.float32)
+    Cf = torch.zeros((M, Nf), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU"):
+        Q.qgemm_run(M, Kf, Nf, "f32", Af, torch.zeros(Kf * Nf, dtype=torch.float32), None, Cf)
+    with pytest.raises(ValueError, match="Bq"):
+        Q.qgemm_run(M, Kf, Nf, "f32", Af, torch.zeros(Kf * Nf - 1, dtype=torch.float32), None, Cf)
     # epilogue operands: residual in C's type, bias fp32 [N]
     with pytest.raises(ValueError, match="residual"):
         Q.qgemm_run_ex(M, K, N, "int4b64", A16, Bq, Sc, C32,

@@ -212,6 +212,10 @@ def _check_run_args(M: int, K: int, N: int, fmt, A, Bq, scales, C, out_type=0, b
         wb, sb = qgemm_packed_size(K, N, f)
     except QGemmError:
         wb = sb = None   # the library reports the bad shape or format itself
+    if f == QGEMM_F32 and wb is not None:
+        # the fp32 format's B is the float [K][N] matrix itself, read no
+        # further than its K*N elements (the packed size rounds it up to 256)
+        wb = K * N * 4
     _need(Bq, "Bq", None, nbytes=wb)
     _need(scales, "scales", None, nbytes=sb)
     if isinstance(workspace, torch.Tensor) and workspace.numel() * workspace.element_size() < ws_bytes:
