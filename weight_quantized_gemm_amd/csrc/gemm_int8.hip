@@ -210,10 +210,16 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
             load_p(rp[d], min(d, it_last));
         }
         // one full wait: the loop header then merges an empty count with the
-        // loop's own, and the compiler's in-order count stays exact
+        // loop's own, and the compiler's in-order count stays exact (the
+        // scheduling barriers keep the loads above the wait)
+        __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_sched_barrier(0);
 
-        for (int base = 0; base < n_pad; base += DEPTH) {
+        // a do-while (n_pad >= DEPTH here): no guard branch in front of the
+        // loop, so the loads above cannot be sunk below the wait
+        int base = 0;
+        do {
 #pragma unroll
             for (int u = 0; u < DEPTH; ++u) {
                 const int it = base + u;
@@ -263,7 +269,8 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
                     }
                 }
             }
-        }
+            base += DEPTH;
+        } while (base < n_pad);
     }
 
     // Partial tiles to LDS (over the A tiles, once every wave is done with

@@ -157,7 +157,9 @@ hipError_t launch_w4a8_actquant(int M, int K, int Kq, const void *A, int8_t *qa,
 // the 128 x 32 column block 32 w and runs every K step with
 // v_mfma_i32_32x32x32_i8 (4 accumulator tiles). Each wave loads only its own
 // weight record, so no weight byte enters a CU twice; two waves per SIMD
-// overlap one wave's loads and LDS reads with the other's matrix work.
+// overlap one wave's loads and LDS reads with the other's matrix work. (The
+// wave grid is a parameter: a 2 x 4 grid of 64 x 64 wave tiles halves the
+// LDS reads of A but loads every weight record twice, and measured slower.)
 //  - qa is staged in LDS 128 K-columns (one 128-byte run per row) at a time,
 //    four stages deep, loaded three stages ahead through a register ring;
 //    one barrier per stage;
@@ -169,13 +171,21 @@ hipError_t launch_w4a8_actquant(int M, int K, int Kq, const void *A, int8_t *qa,
 //    stored or, for padded stages, meets an all-zero A tile), which keeps
 //    the compiler's in-order count of outstanding loads exact;
 //  - the epilogue applies C = sa * (scale * D + offset * S) with the row
-//    scales and sums staged in LDS.
+//    scales and sums staged in LDS; for a plain fp32 C each wave passes its
+//    results through LDS in 64 x 32 blocks so that every lane stores
+//    16-byte pieces of rows: storing the accumulator layout directly (one
+//    float per lane down a column) made the store phase a third of the
+//    kernel's time at 1024 x 3072 x 8192.
 // Lane (r, h) = (lane % 32, lane / 32) holds K-elements 32 s + 16 h .. +15 of
 // each 64-wide block in step s for its A row and B column alike.
 // ---------------------------------------------------------------------------
 namespace {
 constexpr int WBM = kW4A8TileM, WBN = kW4A8TileN, WSK = kW4A8StageK;
-constexpr int WNW = 8;                    // waves, one per 32-column block
+constexpr int WNW = 8;                    // waves
+constexpr int WGN = 8, WGM = WNW / WGN;          // wave grid: WGM rows x WGN columns
+constexpr int WRF = WBM / (32 * WGM);            // 32-row fragments per wave
+constexpr int WCF = WBN / (32 * WGN);            // 32-column fragments per wave
+static_assert(WRF % 2 == 0 && WCF >= 1 && WRF * WCF <= 4, "wave tile of 64k x 32 rows x columns");
 constexpr int WAROW = WSK + 16;           // bytes per LDS row of an A stage (144)
 constexpr int WRING = 4;                  // stages: LDS A tiles = A and B register ring slots
 constexpr size_t WAS_BYTES = (size_t)WBM * WAROW;
@@ -212,7 +222,7 @@ __global__ __launch_bounds__(64 * WNW) void w4a8_gemm_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = uniform(tid >> 6);
-    const int wn = wave;
+    const int wm = wave / WGN, wn = wave % WGN;   // wave tile rows 32 WRF wm.., columns 32 WCF wn..
     const int r = lane & 31, h = lane >> 5;
     // split-K: slice blockIdx.y of gridDim.y takes stages [st0, st0 + nst) of
     // the Kq / WSK (the plan keeps gridDim.y <= Kq / WSK, so nst >= 1)
@@ -258,24 +268,31 @@ __global__ __launch_bounds__(64 * WNW) void w4a8_gemm_kernel(
             *reinterpret_cast<u4_t *>(T + (idx >> 3) * WAROW + (idx & 7) * 16) = src[i] & mask;
         }
     };
-    // B: the record of the wave's 32-channel tile, two K-blocks per stage
-    const size_t b_rec0 = (size_t)min(n0 / 32 + wn, ntiles_b - 1) * nkc;
-    auto load_b = [&](u4_t (&dst)[2], int st) {
+    // B: the records of the wave's two 32-channel tiles, two K-blocks per stage
+    size_t b_rec0[WCF];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const size_t rec = b_rec0 + min(2 * (st0 + st) + kk, nkc - 1);
-            dst[kk] = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(Wp + rec * 1024) + lane);
-        }
+    for (int cf = 0; cf < WCF; ++cf)
+        b_rec0[cf] = (size_t)min(n0 / 32 + WCF * wn + cf, ntiles_b - 1) * nkc;
+    auto load_b = [&](u4_t (&dst)[2][WCF], int st) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int cf = 0; cf < WCF; ++cf) {
+                const size_t rec = b_rec0[cf] + min(2 * (st0 + st) + kk, nkc - 1);
+                dst[kk][cf] = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(Wp + rec * 1024) + lane);
+            }
     };
 
-    i16_t acc[4];
+    i16_t acc[WRF][WCF];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < WRF; ++a)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) acc[a][j] = 0;
+        for (int b = 0; b < WCF; ++b)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[a][b][j] = 0;
 
     u4_t an[WRING][2];
-    u4_t bq[WRING][2];
+    u4_t bq[WRING][2][WCF];
 
     // prologue: stage 0 in LDS tile 0, stages 1 .. WRING of A and 0 .. WRING - 1
     // of B in flight (clamped past the end: never used)
@@ -289,9 +306,17 @@ __global__ __launch_bounds__(64 * WNW) void w4a8_gemm_kernel(
     // this path with the back edge, and the compiler may have issued these
     // loads in any order, so without this wait it would count the slot the
     // loop reads first as the newest load and drain everything every stage.
+    // The scheduling barriers keep the loads above the wait (the wait alone
+    // does not stop the scheduler from sinking loads below it).
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_sched_barrier(0);
 
-    for (int base = 0; base < nsteps; base += WRING) {
+    // a do-while (nsteps >= WRING always): with no guard branch in front of
+    // the loop, the compiler cannot sink the prologue's loads below the wait
+    // into a preheader of their own
+    int base = 0;
+    do {
 #pragma unroll
         for (int u = 0; u < WRING; ++u) {
             const int i = base + u;
@@ -300,50 +325,107 @@ __global__ __launch_bounds__(64 * WNW) void w4a8_gemm_kernel(
             store_a_masked(a_tile((u + 1) % WRING), an[(u + 1) % WRING], i + 1 < nst ? ~0u : 0u);
             load_a(an[(u + 1) % WRING], min(i + 1 + WRING, nst - 1));
             __syncthreads();
-            const int8_t *T = a_tile(u);
+            const int8_t *T = a_tile(u) + (32 * WRF * wm + r) * WAROW + 16 * h;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    i4_t af[4];
+                    i4_t af[WRF], bf[WCF];
 #pragma unroll
-                    for (int rf = 0; rf < 4; ++rf)
-                        af[rf] = *reinterpret_cast<const i4_t *>(
-                            T + (32 * rf + r) * WAROW + 64 * kk + 32 * s + 16 * h);
-                    const i4_t bf = unpack_codes(bq[u][kk][2 * s], bq[u][kk][2 * s + 1]);
+                    for (int rf = 0; rf < WRF; ++rf)
+                        af[rf] = *reinterpret_cast<const i4_t *>(T + 32 * rf * WAROW + 64 * kk + 32 * s);
 #pragma unroll
-                    for (int rf = 0; rf < 4; ++rf)
-                        acc[rf] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[rf], bf, acc[rf], 0, 0, 0);
+                    for (int cf = 0; cf < WCF; ++cf)
+                        bf[cf] = unpack_codes(bq[u][kk][cf][2 * s], bq[u][kk][cf][2 * s + 1]);
+#pragma unroll
+                    for (int rf = 0; rf < WRF; ++rf)
+#pragma unroll
+                        for (int cf = 0; cf < WCF; ++cf)
+                            acc[rf][cf] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[rf], bf[cf],
+                                                                                acc[rf][cf], 0, 0, 0);
                 }
             // B slot u is free: refill it with stage i + WRING
             load_b(bq[u], min(i + WRING, nst - 1));
         }
-    }
+        base += WRING;
+    } while (base < nsteps);
 
     // ---- epilogue: C = sa * (scale * D + offset * S), or this slice's D ----
-    {
-        const int col = n0 + 32 * wn + r;
-        if (col >= N) return;
+    // Plain fp32 C of a whole 64 x 32 wave block: through LDS (over the A
+    // tiles, a private 64 x 36-float region per wave) so that each lane
+    // stores 16-byte pieces of rows instead of single floats down a column.
+    const bool staged = gridDim.y == 1 && !DEBUG_D && epi.plain && (N & 3) == 0 &&
+                        (reinterpret_cast<uintptr_t>(C) & 15) == 0;
+    if (staged) {
+        __syncthreads();   // every wave is done with the A tiles
+        float *stg = reinterpret_cast<float *>(As) + wave * (64 * 36);
+#pragma unroll
+        for (int cf = 0; cf < WCF; ++cf)
+#pragma unroll
+            for (int rh = 0; rh < WRF / 2; ++rh) {
+                const int c0 = n0 + 32 * WCF * wn + 32 * cf;
+                const int rb = 32 * WRF * wm + 64 * rh;     // first tile row of this 64-row block
+                if (m0 + rb + 64 > M || c0 + 32 > N) {
+                    // a ragged block: element stores (uniform branch per wave)
+                    const int col = c0 + r;
+                    if (col >= N) continue;
+                    const f2_t pr = Sp[col];
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) {
+                            const int rl = rb + 32 * q + 8 * (j >> 2) + 4 * h + (j & 3);
+                            if (m0 + rl >= M) continue;
+                            static_cast<float *>(C)[(size_t)(m0 + rl) * N + col] =
+                                sa_s[rl] * fmaf(pr.y, (float)acc[2 * rh + q][cf][j], pr.x * (float)S_s[rl]);
+                        }
+                    continue;
+                }
+                const f2_t pr = Sp[c0 + r];
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int rw = 32 * q + 8 * (j >> 2) + 4 * h + (j & 3);
+                        const int rl = rb + rw;
+                        stg[rw * 36 + r] = sa_s[rl] * fmaf(pr.y, (float)acc[2 * rh + q][cf][j], pr.x * (float)S_s[rl]);
+                    }
+                // the wave's own LDS writes precede its reads (one wave's LDS
+                // operations complete in order); its next block's writes
+                // follow these reads likewise
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int rw = 8 * i + (lane >> 3), c4 = lane & 7;
+                    const f4_t v = *reinterpret_cast<const f4_t *>(stg + rw * 36 + 4 * c4);
+                    *reinterpret_cast<f4_t *>(static_cast<float *>(C) + (size_t)(m0 + rb + rw) * N + c0 + 4 * c4) = v;
+                }
+            }
+        return;
+    }
+#pragma unroll
+    for (int cf = 0; cf < WCF; ++cf) {
+        const int col = n0 + 32 * WCF * wn + 32 * cf + r;
+        if (col >= N) continue;
         if (gridDim.y > 1) {       // exact int32 partial tile; the reduce finishes
             int32_t *dp = D + (size_t)blockIdx.y * M * N;
 #pragma unroll
-            for (int rf = 0; rf < 4; ++rf)
+            for (int rf = 0; rf < WRF; ++rf)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    const int row = m0 + 32 * rf + 8 * (j >> 2) + 4 * h + (j & 3);
-                    if (row < M) dp[(size_t)row * N + col] = acc[rf][j];
+                    const int row = m0 + 32 * WRF * wm + 32 * rf + 8 * (j >> 2) + 4 * h + (j & 3);
+                    if (row < M) dp[(size_t)row * N + col] = acc[rf][cf][j];
                 }
-            return;
+            continue;
         }
         const f2_t pr = Sp[col];
 #pragma unroll
-        for (int rf = 0; rf < 4; ++rf) {
+        for (int rf = 0; rf < WRF; ++rf) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const int rl = 32 * rf + 8 * (j >> 2) + 4 * h + (j & 3);
+                const int rl = 32 * WRF * wm + 32 * rf + 8 * (j >> 2) + 4 * h + (j & 3);
                 const int row = m0 + rl;
                 if (row >= M) continue;
-                const int d = acc[rf][j];
+                const int d = acc[rf][cf][j];
                 if (DEBUG_D) D[(size_t)row * N + col] = d;
                 const float out = sa_s[rl] * fmaf(pr.y, (float)d, pr.x * (float)S_s[rl]);
                 if (epi.plain) static_cast<float *>(C)[(size_t)row * N + col] = out;
