@@ -365,35 +365,41 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
                 red[(32 * rf + 8 * (e >> 2) + 4 * h + (e & 3)) * RED_STRIDE + 32 * cf + r] = acc[rf][cf][e];
     __syncthreads();
 
-    // ---- sum the four K quarters in a fixed order and store:
-    //      thread -> one row, 32 consecutive columns ----
-    constexpr int TPR = 64 * NWAVE / BM;           // threads per row
-    const int row = tid / TPR;
-    const int c0 = (tid % TPR) * 32;               // column in the tile
-    const int gm = m0 + row;
-    if (gm >= M) return;
+    // ---- sum the four K quarters in a fixed order and store: each pass
+    //      covers RPI whole rows, lane -> 16 consecutive bytes of a row, so
+    //      one store instruction writes whole rows of the tile contiguously
+    //      (a row per thread, strided down the rows, touched a different
+    //      cache line in every lane) ----
+    constexpr int CPT = BN / 4;                    // float4 columns per tile row
+    constexpr int RPI = 64 * NWAVE / CPT;          // rows per pass
+    static_assert(BM % RPI == 0, "whole passes");
+    const int c4 = tid % CPT, r0 = tid / CPT;
+    const int gc = n0 + 4 * c4;
     const float *red0 = reinterpret_cast<const float *>(lds);
-    float *dst = out + (size_t)gm * N + n0 + c0;
-    const bool vec_store = (N & 3) == 0 && n0 + c0 + 32 <= N;
+    const size_t W = (size_t)BM * RED_STRIDE;
+    const bool vec_store = (N & 3) == 0 && gc + 4 <= N;
 #pragma unroll
-    for (int j = 0; j < 32; j += 4) {
-        const size_t o = (size_t)row * RED_STRIDE + c0 + j;
-        const size_t W = (size_t)BM * RED_STRIDE;
+    for (int it = 0; it < BM / RPI; ++it) {
+        const int row = it * RPI + r0;
+        const int gm = m0 + row;
+        if (gm >= M) break;
+        const size_t o = (size_t)row * RED_STRIDE + 4 * c4;
         f4_t sum = *reinterpret_cast<const f4_t *>(red0 + o);
 #pragma unroll
         for (int q = 1; q < NWAVE; ++q) sum += *reinterpret_cast<const f4_t *>(red0 + (size_t)q * W + o);
+        float *dst = out + (size_t)gm * N + gc;
         if (!raw && vec_store) {
-            epi_put4(epi, C, gm, n0 + c0 + j, N, sum);
+            epi_put4(epi, C, gm, gc, N, sum);
         } else if (!raw) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if (n0 + c0 + j + e < N) epi_put(epi, C, gm, n0 + c0 + j + e, N, sum[e]);
+                if (gc + e < N) epi_put(epi, C, gm, gc + e, N, sum[e]);
         } else if (vec_store) {
-            *reinterpret_cast<f4_t *>(dst + j) = sum;
+            *reinterpret_cast<f4_t *>(dst) = sum;
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if (n0 + c0 + j + e < N) dst[j + e] = sum[e];
+                if (gc + e < N) dst[e] = sum[e];
         }
     }
 }

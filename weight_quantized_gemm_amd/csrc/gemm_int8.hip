@@ -297,20 +297,31 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
     }
     __syncthreads();
 
-    // Sum the four partials (fixed order), apply the channel pairs and store:
-    // thread -> row tid/2, 32 consecutive columns. A split-K slice stores its
-    // raw partial tile (plain fp32) at slice blockIdx.y of C.
-    const int row = tid >> 1;
-    const int c0 = (tid & 1) * 32;
-    const int gm = m0 + row;
-    if (gm >= M) return;
+    // Sum the four partials (fixed order), apply the channel pairs and store.
+    // Each pass covers 16 whole rows, lane -> 16 consecutive bytes of a row,
+    // so one store instruction writes whole rows of the tile contiguously. A
+    // split-K slice stores its raw partial tile (plain fp32) at slice
+    // blockIdx.y of C.
+    constexpr int CPT = BN / 4, RPI = 256 / CPT;
+    static_assert(BM % RPI == 0, "whole passes");
+    const int c4 = tid % CPT, r0 = tid / CPT;
+    const int gc = n0 + 4 * c4;
     const bool raw = gridDim.y > 1 || epi.plain;
-    const float rsm = ((rsum[0][row] + rsum[1][row]) + rsum[2][row]) + rsum[3][row];
-    float *dst = static_cast<float *>(C) + (size_t)blockIdx.y * M * N + (size_t)gm * N + n0 + c0;
-    const bool vec_store = (N & 3) == 0 && n0 + c0 + 32 <= N;
+    const bool vec_store = (N & 3) == 0 && gc + 4 <= N;
+    float *const out_base = static_cast<float *>(C) + (size_t)blockIdx.y * M * N;
+    f2_t pr[4];
 #pragma unroll
-    for (int j = 0; j < 32; j += 4) {
-        const int o = row * RED_STRIDE + c0 + j;
+    for (int e = 0; e < 4; ++e) {
+        if constexpr (WF16 || PM != 0) pr[e] = f2_t{0.0f, 0.0f};
+        else pr[e] = *reinterpret_cast<const f2_t *>(Sp + (size_t)min(gc + e, N - 1) * 2);
+    }
+#pragma unroll
+    for (int it = 0; it < BM / RPI; ++it) {
+        const int row = it * RPI + r0;
+        const int gm = m0 + row;
+        if (gm >= M) break;
+        const float rsm = ((rsum[0][row] + rsum[1][row]) + rsum[2][row]) + rsum[3][row];
+        const int o = row * RED_STRIDE + 4 * c4;
         const f4_t p = *reinterpret_cast<const f4_t *>(&red[0][o]) +
                        *reinterpret_cast<const f4_t *>(&red[1][o]) +
                        *reinterpret_cast<const f4_t *>(&red[2][o]) +
@@ -318,25 +329,22 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
         f4_t out;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            if constexpr (WF16 || PM != 0) {
-                out[e] = p[e];
-            } else {
-                const f2_t pr = *reinterpret_cast<const f2_t *>(Sp + (size_t)min(n0 + c0 + j + e, N - 1) * 2);
-                out[e] = fmaf(pr.y, p[e], fmaf(-1024.0f, pr.y, pr.x) * rsm);
-            }
+            if constexpr (WF16 || PM != 0) out[e] = p[e];
+            else out[e] = fmaf(pr[e].y, p[e], fmaf(-1024.0f, pr[e].y, pr[e].x) * rsm);
         }
+        float *dst = out_base + (size_t)gm * N + gc;
         if (!raw && vec_store) {
-            epi_put4(epi, C, gm, n0 + c0 + j, N, out);
+            epi_put4(epi, C, gm, gc, N, out);
         } else if (!raw) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if (n0 + c0 + j + e < N) epi_put(epi, C, gm, n0 + c0 + j + e, N, out[e]);
+                if (gc + e < N) epi_put(epi, C, gm, gc + e, N, out[e]);
         } else if (vec_store) {
-            *reinterpret_cast<f4_t *>(dst + j) = out;
+            *reinterpret_cast<f4_t *>(dst) = out;
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if (n0 + c0 + j + e < N) dst[j + e] = out[e];
+                if (gc + e < N) dst[e] = out[e];
         }
     }
 }
