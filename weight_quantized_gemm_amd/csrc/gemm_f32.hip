@@ -1,8 +1,13 @@
 // gemm_f32.hip -- the float-weight GEMM (MNN GemmSpeed benchmark page, mode 0
 // "float-gemm": C = A[M,K] x B[K,N] with B laid out {ic, oc} = {K, N}).
 //
-// An LDS-tiled fp32 FMA kernel (16 x 64 or 64 x 64 tiles, K in chunks of 64
-// loaded two chunks ahead) that handles any M, K, N. Every global load is
+// An LDS-tiled kernel on the fp32 matrix cores (16 x 64 or 64 x 64 tiles, K
+// in chunks of 64 loaded two chunks ahead) that handles any M, K, N. Each
+// 256-thread group's four waves own a quadrant (64 x 64 tile: 32 x 32, with
+// v_mfma_f32_32x32x2_f32) or a 16-column strip (16 x 64 tile: 16 x 16, with
+// v_mfma_f32_16x16x4_f32) and read their operands straight from the
+// transposed A and row-major B chunks in LDS (consecutive lanes, consecutive
+// words: no bank conflicts). Every global load is
 // unconditional, from indices clamped into the arrays; values past K are
 // replaced by zero on both operands (so they add exactly zero) and rows or
 // columns past M or N are computed and never stored. With no skippable load
@@ -15,8 +20,9 @@
 //  - across workgroups, a third grid dimension splits the chunks into
 //    contiguous slices; slice z writes partial tile z of a [nsplit][M][N]
 //    scratch array, which a second kernel adds in slice order.
-// Each output of a group's share is one fp32 FMA chain over k in increasing
-// order. K == 0 writes zeros.
+// Each output of a group's share is accumulated in fp32 by the matrix cores
+// over k in increasing order of MFMA steps (2 or 4 products per step), so
+// repeated runs give identical bits. K == 0 writes zeros.
 #include "kernels_common.h"
 #include "qgemm_internal.h"
 
@@ -84,11 +90,11 @@ __global__ __launch_bounds__(256 * KG) void gemm_f32_kernel(int M, int K, int N,
     F32Tiles<TM> &T = reinterpret_cast<F32Tiles<TM> *>(smem)[gi];
     const int tx = tid & 15, ty = tid >> 4;
     const int m0 = blockIdx.y * BM, n0 = blockIdx.x * FT;
-    float acc[TM][4];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    const int lane = tid & 63, wv = tid >> 6;
+    // matrix-core accumulators: 64 x 64 tile -> wave quadrant (wv >> 1, wv & 1)
+    // of 32 x 32; 16 x 64 tile -> wave strip wv of 16 x 16
+    f16_t mc32 = {};
+    f4_t mc16 = {};
 
     // values at k >= kend (past K or past this group's share) are stored as zero
     auto stage = [&](const Chunk<TM> &c, int k0, int kend) {
@@ -103,18 +109,22 @@ __global__ __launch_bounds__(256 * KG) void gemm_f32_kernel(int M, int K, int N,
             T.Bs[idx / FT][idx % FT] = k0 + idx / FT < kend ? c.b[i] : 0.f;
         }
     };
+    // lane l of a 32x32x2 step holds A[row l % 32][k + l / 32] and
+    // B[k + l / 32][col l % 32]; of a 16x16x4 step A[row l % 16][k + l / 16]
+    // and B[k + l / 16][col l % 16]
     auto multiply = [&]() {
+        if constexpr (TM == 4) {
+            const int r = lane & 31, h = lane >> 5;
+            const int ma = 32 * (wv >> 1) + r, nb = 32 * (wv & 1) + r;
 #pragma unroll 8
-        for (int kk = 0; kk < FK; ++kk) {
-            float a[TM], b[4];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) a[i] = T.As[kk][ty * TM + i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = T.Bs[kk][tx * 4 + j];
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+            for (int kk = 0; kk < FK; kk += 2)
+                mc32 = __builtin_amdgcn_mfma_f32_32x32x2f32(T.As[kk + h][ma], T.Bs[kk + h][nb], mc32, 0, 0, 0);
+        } else {
+            const int r = lane & 15, q = lane >> 4;
+            const int nb = 16 * wv + r;
+#pragma unroll 8
+            for (int kk = 0; kk < FK; kk += 4)
+                mc16 = __builtin_amdgcn_mfma_f32_16x16x4f32(T.As[kk + q][r], T.Bs[kk + q][nb], mc16, 0, 0, 0);
         }
     };
 
@@ -144,6 +154,30 @@ __global__ __launch_bounds__(256 * KG) void gemm_f32_kernel(int M, int K, int N,
         __syncthreads();
         load_chunk<TM>(r1, min(c0 + c + 3, nch) * FK, m0, n0, M, K, N, A, B, tid);
         if (live1) multiply();
+        __syncthreads();
+    }
+
+    // the matrix-core layout to thread (tx, ty)'s rows ty * TM .. and
+    // columns tx * 4 .. (through this group's part of LDS, over its tiles;
+    // the loop's last barrier has passed)
+    float acc[TM][4];
+    {
+        float *cv = reinterpret_cast<float *>(smem) + (size_t)gi * BM * (FT + 4);
+        if constexpr (TM == 4) {
+            const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                cv[(32 * (wv >> 1) + 8 * (i >> 2) + 4 * h + (i & 3)) * (FT + 4) + 32 * (wv & 1) + r] = mc32[i];
+        } else {
+            const int r = lane & 15, q = lane >> 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cv[(4 * q + i) * (FT + 4) + 16 * wv + r] = mc16[i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = cv[(ty * TM + i) * (FT + 4) + tx * 4 + j];
         __syncthreads();
     }
 
