@@ -8,7 +8,7 @@ current stream. GFLOPS follow the MNN GemmSpeed page's convention
 2*M*K*N / t (section "Measurement flow").
 
 The weights, activations and outputs rotate over enough copies that the
-working set of the timed region exceeds twice the 256 MB Infinity Cache, so
+working set of the timed region exceeds four times the 256 MB Infinity Cache, so
 every launch streams its weights from HBM as a real multi-layer model would.
 
 Printed: one JSON line (the metric of the run) with a `roofline` object for
@@ -131,6 +131,16 @@ class Workload:
             return
         self.Q.qgemm_run_ws(self.M, self.K, self.N, self.fmt, self.A[c], self.B[c], self.S[c],
                             self.C[c], self.ws, self.ws_bytes)
+
+
+ROTATE_MALL = 4     # rotated inputs span this many times the last-level cache
+
+
+def rotation_copies(per_copy_bytes: int, cap: int) -> int:
+    """Copies of a launch's inputs to rotate through so that each launch reads
+    inputs no launch of the last ROTATE_MALL x the last-level cache's capacity
+    touched (at least 2, at most cap)."""
+    return min(cap, max(2, -(-ROTATE_MALL * MALL_BYTES // max(1, per_copy_bytes)) + 1))
 
 
 def traffic_record(kernel_src: str, kernel: str):
@@ -296,13 +306,13 @@ def parse_epilogue(spec: str):
 
 def single_workload(args, torch) -> int:
     """Times one named workload alone (all launches of one qgemm_run call,
-    weights rotated past twice the Infinity Cache) and prints a diagnostic
+    inputs rotated past four times the last-level cache) and prints a diagnostic
     JSON line with its roofline fraction."""
     from weight_quantized_gemm_amd import synth
     fmt, M, K, N, _ = synth.CONFIGS[args.workload]
     epi = parse_epilogue(args.epilogue)
     per_copy = algorithmic_bytes(M, K, N, fmt, epi)
-    copies = args.copies or min(256, max(2, -(-2 * MALL_BYTES // per_copy) + 1))
+    copies = args.copies or rotation_copies(per_copy, 256)
     w = Workload(args.workload, copies, epi)
     for i in range(args.warmup):
         w.run(i)
@@ -430,7 +440,7 @@ def shape_rows(torch, shapes, steps, copies_arg, tag, page_lines=False):
     with its 2*M*K*N GFLOPS (MNN GemmSpeed page, section "Output format")."""
     for fmt, M, K, N in shapes:
         per = algorithmic_bytes(M, K, N, fmt)
-        copies = copies_arg or min(64, max(2, -(-2 * MALL_BYTES // per) + 1))
+        copies = copies_arg or rotation_copies(per, 64)
         w = ShapeWorkload(fmt, M, K, N, copies, seed=K + N + M)
         ms = time_calls(torch, w.run, copies, steps)
         if page_lines:
@@ -467,7 +477,7 @@ def quantizer_rows(torch, specs, steps, copies_arg) -> None:
     for fmt, K, N in specs:
         wb, sb = Q.qgemm_packed_size(K, N, fmt)
         per = 4 * N * K + wb + sb
-        copies = copies_arg or min(16, max(2, -(-2 * MALL_BYTES // per) + 1))
+        copies = copies_arg or rotation_copies(per, 16)
         W0 = torch.from_numpy(synth.normal_weights(np.random.default_rng(K + N), N, K)).cuda()
         Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
         Bs = [torch.empty(wb, dtype=torch.uint8, device="cuda") for _ in range(copies)]
@@ -508,7 +518,7 @@ def launch_floor(torch, steps: int) -> None:
 
 def vendor_reference(args, torch) -> int:
     """The vendor libraries on the same prefill shapes, same protocol (rotated
-    copies past twice the Infinity Cache, replayed graph, HIP events): dense
+    copies past four times the Infinity Cache, replayed graph, HIP events): dense
     fp16 x fp16 -> fp16 (torch.matmul) and int8 x int8 -> int32
     (torch._int_mm). Context for what the matrix cores reach on these shapes;
     never part of the metric."""
@@ -523,7 +533,7 @@ def vendor_reference(args, torch) -> int:
                  ("int8 _int_mm", torch.int8, 1024, 3072, 8192)]
     for name, dt, M, K, N in cases:
         per = M * K * dt.itemsize + K * N * dt.itemsize + M * N * 4
-        copies = max(2, -(-2 * MALL_BYTES // per) + 1)
+        copies = rotation_copies(per, 64)
         g = torch.Generator(device="cuda").manual_seed(7)
         if dt == torch.int8:
             A = [torch.randint(-127, 128, (M, K), dtype=dt, device="cuda", generator=g) for _ in range(copies)]
@@ -581,7 +591,7 @@ def _probe_lib():
 def peak_probes(args, torch) -> int:
     """Measured peaks of this chip for plain kernels (context for the roofline
     fractions, which stay against the published peaks): an HBM read stream and
-    copy at the decode GEMV's size and at a 117 MB weight, rotated past twice
+    copy at the decode GEMV's size and at a 117 MB weight, rotated past four times
     the Infinity Cache and timed like the GEMM workloads (replayed graph, HIP
     events); an fp16 MFMA loop with and without same-wave VALU work, with the
     shader clock read in-kernel; L2-resident reads in the GEMM's operand
@@ -596,7 +606,7 @@ def peak_probes(args, torch) -> int:
 
     # HBM streams: the decode GEMV's algorithmic bytes and a 117 MB weight
     for nbytes in (algorithmic_bytes(1, 4096, 11008) // 16 * 16, 117_440_512):
-        copies = max(2, -(-2 * MALL_BYTES // nbytes) + 1)
+        copies = rotation_copies(nbytes, 64)
         bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(i)
                 for i in range(copies)]
         # grids that give each thread 1, 2 or 4 turns of eight 16-byte loads
@@ -754,12 +764,11 @@ def main() -> int:
         return page_grid(args, torch)
 
     clocks_before = gpu_clocks()
-    # one decode + one prefill copy is ~50 MB; rotate past 2x the MALL
     # Rotation: every launch reads inputs no launch of the last ~4 x the
     # last-level cache's capacity touched, for the step and for each kernel
     # repeated on its own (the smaller per-kernel footprint sets the count).
     per_kernel_bytes = min(algorithmic_bytes(1, 4096, 11008), algorithmic_bytes(512, 4096, 4096))
-    copies = args.copies or max(2, -(-4 * MALL_BYTES // per_kernel_bytes) + 1)
+    copies = args.copies or rotation_copies(per_kernel_bytes, 256)
     dec = Workload(DECODE, copies)
     pre = Workload(PREFILL, copies)
 
