@@ -60,7 +60,6 @@ constexpr int BK = 64;
 constexpr int NWAVE = 4;               // one K quarter per wave
 constexpr int AS_STRIDE = BK + 8;      // halves per LDS row of an A tile (144 bytes)
 constexpr int A_TILES = 2;             // LDS A tiles per wave
-constexpr int B_RING = 4;              // B code ring (loads four blocks ahead)
 constexpr int P_RING = 2;              // pair ring (loads two blocks ahead)
 constexpr int UNROLL = 4;              // lcm of the rings: every slot a fixed register
 
@@ -71,13 +70,19 @@ struct TileCfg {
     static constexpr int RF = BM / 32;                  // 32-row accumulator tiles per wave
     static constexpr int CF = BN / 32;                  // 32-column accumulator tiles per wave
     static constexpr int A_SETS = BM == 64 ? 2 : 1;     // A register sets (blocks loaded ahead)
+    // B code ring: loads four blocks ahead, two with four column tiles (the
+    // register file would not hold four blocks of 128 codes per lane)
+    static constexpr int B_RING = CF >= 4 ? 2 : 4;
     static constexpr int A_PIECES = BM * BK / 8 / 64;   // 16-byte A pieces per lane and block
     static constexpr int RED_STRIDE = BN + 4;           // floats per LDS row of the reduction
     static constexpr size_t AS_BYTES = (size_t)BM * AS_STRIDE * 2;          // one A tile
     static constexpr size_t A_LDS = (size_t)NWAVE * A_TILES * AS_BYTES;     // all waves
-    static constexpr size_t RED_BYTES = (size_t)NWAVE * BM * RED_STRIDE * 4;
+    // the four partial tiles meet in LDS RCH rows at a time (all BM rows when
+    // they fit next to nothing else, else 64-row chunks)
+    static constexpr int RCH = (size_t)NWAVE * BM * RED_STRIDE * 4 <= 160 * 1024 ? BM : 64;
+    static constexpr size_t RED_BYTES = (size_t)NWAVE * RCH * RED_STRIDE * 4;
     static constexpr size_t LDS_BYTES = RED_BYTES > A_LDS ? RED_BYTES : A_LDS;
-    static_assert(UNROLL % A_SETS == 0 && UNROLL % A_TILES == 0, "ring sizes");
+    static_assert(UNROLL % A_SETS == 0 && UNROLL % A_TILES == 0 && UNROLL % B_RING == 0, "ring sizes");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 workgroup");
 };
 
@@ -150,6 +155,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     const float *__restrict__ Sp, void *__restrict__ C, Epilogue epi) {
     constexpr int BM = T::BM, BN = T::BN, RF = T::RF, CF = T::CF;
     constexpr int A_SETS = T::A_SETS, A_PIECES = T::A_PIECES, RED_STRIDE = T::RED_STRIDE;
+    constexpr int B_RING = T::B_RING;
     constexpr size_t AS_BYTES = T::AS_BYTES;
     __shared__ __align__(16) unsigned char lds[T::LDS_BYTES];
 
@@ -256,7 +262,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     u4_t an[A_SETS][A_PIECES];  // A register sets: set j % A_SETS holds block j
-    u4_t bc[B_RING][CF];        // B code ring: slot j % 4 holds block j
+    u4_t bc[B_RING][CF];        // B code ring: slot j % B_RING holds block j
     f2_t bp[P_RING][CF];        // pair ring: slot j % 2 holds block j
     DqParams prm[CF];
     h8_t acur[RF], anxt[RF], bcur[CF], bnxt[CF];
@@ -312,7 +318,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
                     read_a(a_tile(u % A_TILES), s + 1, anxt);
 #pragma unroll
                     for (int cf = 0; cf < CF; ++cf) {
-                        bnxt[cf] = dequant8(bc[u][cf][s + 1], prm[cf], m_lo, m_hi, magic);
+                        bnxt[cf] = dequant8(bc[u % B_RING][cf][s + 1], prm[cf], m_lo, m_hi, magic);
                         pin(bnxt[cf]);
                     }
                 } else {
@@ -342,64 +348,67 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
                 for (int rf = 0; rf < RF; ++rf) acur[rf] = anxt[rf];
 #pragma unroll
                 for (int cf = 0; cf < CF; ++cf) bcur[cf] = bnxt[cf];
-                // slot u is free once its last codes were dequantised (step
-                // 2): refill it with block i + 4
+                // slot u % B_RING is free once its last codes were
+                // dequantised (step 2): refill it with block i + B_RING
                 if (s == 2) {
                     __builtin_amdgcn_sched_barrier(0);
-                    load_b(bc[u], min(kb0 + i + B_RING, last));
+                    load_b(bc[u % B_RING], min(kb0 + i + B_RING, last));
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
     }
 
-    // ---- the four partial tiles to LDS (reusing the A tiles' space) ----
-    __syncthreads();
-    float *red = reinterpret_cast<float *>(lds) + (size_t)kq * BM * RED_STRIDE;
-#pragma unroll
-    for (int rf = 0; rf < RF; ++rf)
-#pragma unroll
-        for (int cf = 0; cf < CF; ++cf)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                red[(32 * rf + 8 * (e >> 2) + 4 * h + (e & 3)) * RED_STRIDE + 32 * cf + r] = acc[rf][cf][e];
-    __syncthreads();
-
-    // ---- sum the four K quarters in a fixed order and store: each pass
-    //      covers RPI whole rows, lane -> 16 consecutive bytes of a row, so
-    //      one store instruction writes whole rows of the tile contiguously
-    //      (a row per thread, strided down the rows, touched a different
-    //      cache line in every lane) ----
+    // ---- the four partial tiles to LDS (reusing the A tiles' space), RCH
+    //      rows at a time; each chunk summed over the K quarters in a fixed
+    //      order and stored: each pass covers RPI whole rows, lane -> 16
+    //      consecutive bytes of a row, so one store instruction writes whole
+    //      rows of the tile contiguously ----
+    constexpr int RCH = T::RCH;
     constexpr int CPT = BN / 4;                    // float4 columns per tile row
     constexpr int RPI = 64 * NWAVE / CPT;          // rows per pass
-    static_assert(BM % RPI == 0, "whole passes");
+    static_assert(BM % RCH == 0 && RCH % 32 == 0 && RCH % RPI == 0, "whole chunks and passes");
     const int c4 = tid % CPT, r0 = tid / CPT;
     const int gc = n0 + 4 * c4;
     const float *red0 = reinterpret_cast<const float *>(lds);
-    const size_t W = (size_t)BM * RED_STRIDE;
+    float *red = reinterpret_cast<float *>(lds) + (size_t)kq * RCH * RED_STRIDE;
+    const size_t W = (size_t)RCH * RED_STRIDE;
     const bool vec_store = (N & 3) == 0 && gc + 4 <= N;
 #pragma unroll
-    for (int it = 0; it < BM / RPI; ++it) {
-        const int row = it * RPI + r0;
-        const int gm = m0 + row;
-        if (gm >= M) break;
-        const size_t o = (size_t)row * RED_STRIDE + 4 * c4;
-        f4_t sum = *reinterpret_cast<const f4_t *>(red0 + o);
+    for (int ch = 0; ch < BM / RCH; ++ch) {
+        __syncthreads();   // the A tiles (first chunk) or the last chunk's sums are read
 #pragma unroll
-        for (int q = 1; q < NWAVE; ++q) sum += *reinterpret_cast<const f4_t *>(red0 + (size_t)q * W + o);
-        float *dst = out + (size_t)gm * N + gc;
-        if (!raw && vec_store) {
-            epi_put4(epi, C, gm, gc, N, sum);
-        } else if (!raw) {
+        for (int rf = ch * (RCH / 32); rf < (ch + 1) * (RCH / 32); ++rf)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (gc + e < N) epi_put(epi, C, gm, gc + e, N, sum[e]);
-        } else if (vec_store) {
-            *reinterpret_cast<f4_t *>(dst) = sum;
-        } else {
+            for (int cf = 0; cf < CF; ++cf)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (gc + e < N) dst[e] = sum[e];
+                for (int e = 0; e < 16; ++e)
+                    red[(32 * (rf - ch * (RCH / 32)) + 8 * (e >> 2) + 4 * h + (e & 3)) * RED_STRIDE +
+                        32 * cf + r] = acc[rf][cf][e];
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < RCH / RPI; ++it) {
+            const int row = it * RPI + r0;             // row within the chunk
+            const int gm = m0 + ch * RCH + row;
+            if (gm >= M) break;
+            const size_t o = (size_t)row * RED_STRIDE + 4 * c4;
+            f4_t sum = *reinterpret_cast<const f4_t *>(red0 + o);
+#pragma unroll
+            for (int q = 1; q < NWAVE; ++q) sum += *reinterpret_cast<const f4_t *>(red0 + (size_t)q * W + o);
+            float *dst = out + (size_t)gm * N + gc;
+            if (!raw && vec_store) {
+                epi_put4(epi, C, gm, gc, N, sum);
+            } else if (!raw) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (gc + e < N) epi_put(epi, C, gm, gc + e, N, sum[e]);
+            } else if (vec_store) {
+                *reinterpret_cast<f4_t *>(dst) = sum;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (gc + e < N) dst[e] = sum[e];
+            }
         }
     }
 }
