@@ -263,6 +263,18 @@ def test_w4a8_shapes(M):
         _parity("w4a8", M, K, N, seed=M * 13 + K + N)
 
 
+@pytest.mark.parametrize("fmt", ["int4b64", "int8b0", "f16", "w4a8", "f32"])
+def test_many_tiles_with_ragged_edges(fmt):
+    """Shapes with enough output tiles that no K split is planned, and a ragged
+    last row tile and last column tile: the tiled kernels' store phases (whole
+    tile rows per store instruction; the W4A8 GEMM's 64 x 32 blocks through LDS,
+    with partial blocks stored element by element) on full and partial tiles."""
+    M, K, N = 1000, 256, 4100
+    ws = Q.qgemm_workspace_size(M, K, N, fmt)
+    assert ws < M * N * 4, "no split-K partial tiles for this shape"
+    _parity(fmt, M, K, N, seed=4100 + len(fmt))
+
+
 @pytest.mark.parametrize("M,K,N", [(1, 1, 1), (3, 137, 70), (16, 256, 256), (65, 17, 129),
                                    (130, 300, 67), (64, 64, 64)])
 def test_f32_shapes(M, K, N):

@@ -38,18 +38,41 @@ constexpr int FVB = FT * FK / 256;   // values of B each thread loads per chunk
 // between its global loads and its LDS stores: A rows m0 + idx / FK,
 // k = k0 + idx % FK and B rows k0 + idx / FT, columns n0 + idx % FT,
 // idx = i * 256 + tid (coalesced runs).
-template <int TM>
+// VEC (K and N multiples of 4): the same chunk in 16-byte pieces, A piece
+// idx = i * 256 + tid being row m0 + idx / 16, k = k0 + 4 (idx % 16) .. + 3
+// and B piece idx row k0 + idx / 16, columns n0 + 4 (idx % 16) .. + 3; a piece
+// lies wholly inside or wholly past K and N.
+template <int TM, bool VEC>
 struct Chunk {
     static constexpr int FVA = 16 * TM * FK / 256;
     float a[FVA], b[FVB];
 };
 
-template <int TM>
-__device__ __forceinline__ void load_chunk(Chunk<TM> &c, int k0, int m0, int n0, int M, int K,
+template <int TM, bool VEC>
+__device__ __forceinline__ void load_chunk(Chunk<TM, VEC> &c, int k0, int m0, int n0, int M, int K,
                                            int N, const float *__restrict__ A,
                                            const float *__restrict__ B, int tid) {
+    if constexpr (VEC) {
 #pragma unroll
-    for (int i = 0; i < Chunk<TM>::FVA; ++i) {
+        for (int i = 0; i < Chunk<TM, VEC>::FVA / 4; ++i) {
+            const int idx = i * 256 + tid;
+            const int gm = m0 + idx / 16, gk = k0 + 4 * (idx % 16);
+            const f4_t v = *reinterpret_cast<const f4_t *>(A + (size_t)min(gm, M - 1) * K + min(gk, K - 4));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c.a[4 * i + j] = v[j];
+        }
+#pragma unroll
+        for (int i = 0; i < FVB / 4; ++i) {
+            const int idx = i * 256 + tid;
+            const int bk = k0 + idx / 16, bn = n0 + 4 * (idx % 16);
+            const f4_t v = *reinterpret_cast<const f4_t *>(B + (size_t)min(bk, K - 1) * N + min(bn, N - 4));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c.b[4 * i + j] = v[j];
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < Chunk<TM, VEC>::FVA; ++i) {
         const int idx = i * 256 + tid;
         const int gm = m0 + idx / FK, gk = k0 + idx % FK;
         const float v = A[(size_t)min(gm, M - 1) * K + min(gk, K - 1)];
@@ -71,11 +94,11 @@ __device__ __forceinline__ void load_chunk(Chunk<TM> &c, int k0, int m0, int n0,
 // idle rows.
 template <int TM>
 struct F32Tiles {
-    float As[FK][16 * TM + 4];   // A chunk transposed: As[k][m]
+    float As[FK][16 * TM + 1];   // A chunk transposed: As[k][m] (odd row stride: the transposing stores of consecutive k hit distinct banks)
     float Bs[FK][FT + 4];
 };
 
-template <int TM, int KG>
+template <int TM, int KG, bool VEC>
 __global__ __launch_bounds__(256 * KG) void gemm_f32_kernel(int M, int K, int N,
                                                             const float *__restrict__ A,
                                                             const float *__restrict__ B,
@@ -97,9 +120,29 @@ __global__ __launch_bounds__(256 * KG) void gemm_f32_kernel(int M, int K, int N,
     f4_t mc16 = {};
 
     // values at k >= kend (past K or past this group's share) are stored as zero
-    auto stage = [&](const Chunk<TM> &c, int k0, int kend) {
+    auto stage = [&](const Chunk<TM, VEC> &c, int k0, int kend) {
+        if constexpr (VEC) {
 #pragma unroll
-        for (int i = 0; i < Chunk<TM>::FVA; ++i) {
+            for (int i = 0; i < Chunk<TM, VEC>::FVA / 4; ++i) {
+                const int idx = i * 256 + tid;
+                const int m = idx / 16, k = 4 * (idx % 16);
+                const bool in = k0 + k < kend;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) T.As[k + j][m] = in ? c.a[4 * i + j] : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < FVB / 4; ++i) {
+                const int idx = i * 256 + tid;
+                const int k = idx / 16, n = 4 * (idx % 16);
+                const bool in = k0 + k < kend;
+                *reinterpret_cast<f4_t *>(&T.Bs[k][n]) =
+                    in ? f4_t{c.b[4 * i], c.b[4 * i + 1], c.b[4 * i + 2], c.b[4 * i + 3]}
+                       : f4_t{0.f, 0.f, 0.f, 0.f};
+            }
+            return;
+        }
+#pragma unroll
+        for (int i = 0; i < Chunk<TM, VEC>::FVA; ++i) {
             const int idx = i * 256 + tid;
             T.As[idx % FK][idx / FK] = k0 + idx % FK < kend ? c.a[i] : 0.f;
         }
@@ -138,21 +181,21 @@ __global__ __launch_bounds__(256 * KG) void gemm_f32_kernel(int M, int K, int N,
     const int c0 = s0 + gi * (s1 - s0) / KG, c1 = s0 + (gi + 1) * (s1 - s0) / KG;
     const int npad = ((s1 - s0 + KG - 1) / KG + 1) & ~1;
     const int kend = min(K, c1 * FK);
-    Chunk<TM> r0, r1;
+    Chunk<TM, VEC> r0, r1;
     if (npad > 0) {            // K == 0 (or an empty slice) reads nothing
-        load_chunk<TM>(r0, c0 * FK, m0, n0, M, K, N, A, B, tid);
-        load_chunk<TM>(r1, (c0 + 1) * FK, m0, n0, M, K, N, A, B, tid);
+        load_chunk<TM, VEC>(r0, c0 * FK, m0, n0, M, K, N, A, B, tid);
+        load_chunk<TM, VEC>(r1, (c0 + 1) * FK, m0, n0, M, K, N, A, B, tid);
     }
     for (int c = 0; c < npad; c += 2) {
         const bool live0 = c0 + c < c1, live1 = c0 + c + 1 < c1;
         if (live0) stage(r0, (c0 + c) * FK, kend);
         __syncthreads();
-        load_chunk<TM>(r0, min(c0 + c + 2, nch) * FK, m0, n0, M, K, N, A, B, tid);
+        load_chunk<TM, VEC>(r0, min(c0 + c + 2, nch) * FK, m0, n0, M, K, N, A, B, tid);
         if (live0) multiply();
         __syncthreads();
         if (live1) stage(r1, (c0 + c + 1) * FK, kend);
         __syncthreads();
-        load_chunk<TM>(r1, min(c0 + c + 3, nch) * FK, m0, n0, M, K, N, A, B, tid);
+        load_chunk<TM, VEC>(r1, min(c0 + c + 3, nch) * FK, m0, n0, M, K, N, A, B, tid);
         if (live1) multiply();
         __syncthreads();
     }
@@ -229,13 +272,19 @@ hipError_t launch_gemm_f32(int M, int K, int N, const float *A, const float *B, 
     void *out = nsplit > 1 ? static_cast<void *>(part) : C;
     const bool small = M <= kF32TileMSmall;
     const dim3 grid(div_up(N, FT), div_up(M, small ? kF32TileMSmall : kF32TileM), nsplit);
-    if (f32_kgroups(M, N) > 1) {
-        if (small) hipLaunchKernelGGL((gemm_f32_kernel<1, kF32KGroups>), grid, dim3(256 * kF32KGroups), 0, s, M, K, N, A, B, out, epi);
-        else hipLaunchKernelGGL((gemm_f32_kernel<4, kF32KGroups>), grid, dim3(256 * kF32KGroups), 0, s, M, K, N, A, B, out, epi);
-    } else {
-        if (small) hipLaunchKernelGGL((gemm_f32_kernel<1, 1>), grid, dim3(256), 0, s, M, K, N, A, B, out, epi);
-        else hipLaunchKernelGGL((gemm_f32_kernel<4, 1>), grid, dim3(256), 0, s, M, K, N, A, B, out, epi);
-    }
+    // 16-byte pieces when every row of A and B starts 16-byte aligned
+    const bool vec = (K & 3) == 0 && (N & 3) == 0 && K > 0 &&
+                     ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
+    auto go = [&](auto kernel, int threads) {
+        hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, s, M, K, N, A, B, out, epi);
+    };
+    const bool kg = f32_kgroups(M, N) > 1;
+    if (kg && small) vec ? go(gemm_f32_kernel<1, kF32KGroups, true>, 256 * kF32KGroups)
+                         : go(gemm_f32_kernel<1, kF32KGroups, false>, 256 * kF32KGroups);
+    else if (kg) vec ? go(gemm_f32_kernel<4, kF32KGroups, true>, 256 * kF32KGroups)
+                     : go(gemm_f32_kernel<4, kF32KGroups, false>, 256 * kF32KGroups);
+    else if (small) vec ? go(gemm_f32_kernel<1, 1, true>, 256) : go(gemm_f32_kernel<1, 1, false>, 256);
+    else vec ? go(gemm_f32_kernel<4, 1, true>, 256) : go(gemm_f32_kernel<4, 1, false>, 256);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nsplit <= 1) return e;
     return launch_splitk_reduce_f32(part, nsplit, M, N, C, epi, s);
