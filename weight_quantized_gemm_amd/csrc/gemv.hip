@@ -250,6 +250,9 @@ __global__ __launch_bounds__(64 * NW) void gemv_int4b64_half_kernel(
     // 1. the pass's activations (one (row, block, half) per thread and slot),
     //    then every pair and record load of this wave, unconditional from
     //    clamped block indices
+    // (a wave none of whose threads stages an activation issues no load for
+    // the slot: at one row only two of the eight waves do, and the others'
+    // clamped loads would sit in the CU's address queue ahead of the weights)
     u4_t araw[AS][4];
 #pragma unroll
     for (int sl = 0; sl < AS; ++sl) {
@@ -258,8 +261,13 @@ __global__ __launch_bounds__(64 * NW) void gemv_int4b64_half_kernel(
         const bool alive = ar < MR && m0 + ar < M;
         const u4_t *src = reinterpret_cast<const u4_t *>(
             A + (size_t)(alive ? m0 + ar : 0) * K + (size_t)(alive ? 2 * b0 + ahb : 0) * 32);
+        if (64 * (NW * sl + wave) < MR * nhb) {     // wave-uniform
 #pragma unroll
-        for (int w = 0; w < 4; ++w) araw[sl][w] = alive ? src[w] : u4_t{0u, 0u, 0u, 0u};
+            for (int w = 0; w < 4; ++w) araw[sl][w] = alive ? src[w] : u4_t{0u, 0u, 0u, 0u};
+        } else {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) araw[sl][w] = u4_t{0u, 0u, 0u, 0u};
+        }
     }
     f2_t pr[RPW];
     u4_t wq[RPW];
