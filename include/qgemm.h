@@ -24,13 +24,13 @@
  *                   K % 64 == 0.
  *   QGEMM_INT4_BLOCK(b)  Int4 with one pair per b K-elements (the page's
  *                   blockSize parameter, section "Why Conv1x1 is used to
- *                   measure GEMM"), b = 32 or a multiple of 64 that divides
- *                   K, and K % 64 == 0; fp16 activations.
+ *                   measure GEMM"), b a multiple of 16 that divides K, and
+ *                   K % 64 == 0; fp16 activations.
  *                   QGEMM_INT4_BLOCK(64) behaves as QGEMM_INT4_B64 and
  *                   QGEMM_INT4_BLOCK(K) as QGEMM_INT4_B0.
  *   QGEMM_INT8_BLOCK(b)  Int8 (codes 0..255) with one pair per b K-elements,
- *                   b = 32 or a multiple of 64 that divides K, and
- *                   K % 64 == 0; fp16 activations. Canonical codes are u8
+ *                   b a multiple of 16 that divides K, and K % 64 == 0;
+ *                   fp16 activations. Canonical codes are u8
  *                   [N][K] as for QGEMM_INT8_B0, pairs [N][K/b][2].
  *
  * Format ids 0-3 equal the page's mode numbers. For every format but F32, A
@@ -97,8 +97,8 @@ typedef enum qgemm_format {
 #define QGEMM_INT4_BLOCK(b) ((qgemm_format)(QGEMM_INT4_BLOCK_BASE + (b)))
 /* Format id of Int8 weights (codes 0..255, fp16 activations) with one pair
  * per b K-elements: the blockSize parameter of the GemmSpeed page ("Why
- * Conv1x1 is used to measure GEMM") applied to 8-bit codes. b is 32 or a
- * multiple of 64 that divides K, and K % 64 == 0 (else ERR_FORMAT / ERR_SHAPE). */
+ * Conv1x1 is used to measure GEMM") applied to 8-bit codes. b is a multiple
+ * of 16 that divides K, and K % 64 == 0 (else ERR_FORMAT / ERR_SHAPE). */
 #define QGEMM_INT8_BLOCK(b) ((qgemm_format)(QGEMM_INT8_BLOCK_BASE + (b)))
 
 typedef enum qgemm_status {
@@ -162,8 +162,11 @@ qgemm_status qgemm_quantize_weights(int K, int N, qgemm_format f,
  * NaN or infinite weight before it runs, so instead of ERR_VALUE the block
  * (the channel, for the per-channel formats) that holds one gets NaN offset
  * and scale and zero codes.
- * Errors: ERR_FORMAT (F32, F16, unknown), ERR_SHAPE, ERR_NULL, ERR_ALIGN (a
- * pointer not 16-byte aligned), ERR_DEVICE, ERR_LAUNCH. N == 0 is a no-op.
+ * Errors: ERR_FORMAT (F32, F16, unknown, and INT4_BLOCK(b) / INT8_BLOCK(b)
+ * with b other than 16, 32 or a multiple of 64: blocks that straddle the
+ * quantiser's 64-element steps; quantise those with qgemm_quantize_weights),
+ * ERR_SHAPE, ERR_NULL, ERR_ALIGN (a pointer not 16-byte aligned), ERR_DEVICE,
+ * ERR_LAUNCH. N == 0 is a no-op.
  */
 qgemm_status qgemm_quantize_weights_device(int K, int N, qgemm_format f, const float *W,
                                            void *q, float *pairs, void *stream);

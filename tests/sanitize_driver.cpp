@@ -143,7 +143,7 @@ static void oracle_small() {
     std::vector<float> W((size_t)N * K);
     for (auto &w : W) w = rndf();
     for (int bits : {4, 8})
-        for (int block : {32, 64, K}) {
+        for (int block : {16, 32, 64, K}) {
             std::vector<uint8_t> q((size_t)N * K * bits / 8);
             std::vector<float> pairs((size_t)N * (K / block) * 2);
             CHECK(orc_quantize(N, K, bits, block, W.data(), q.data(), pairs.data()) == 0, "quantize");
@@ -192,9 +192,13 @@ int main() {
         {QGEMM_INT8_B0, 8, 0, 1},
         {QGEMM_W4A8, 4, 0, 2},
         {QGEMM_INT4_B0, 4, 0, 64},
+        {QGEMM_INT4_BLOCK(16), 4, 16, 16},
         {QGEMM_INT4_BLOCK(32), 4, 32, 32},
+        {QGEMM_INT4_BLOCK(48), 4, 48, 48},
         {QGEMM_INT4_BLOCK(128), 4, 128, 128},
+        {QGEMM_INT8_BLOCK(16), 8, 16, 16},
         {QGEMM_INT8_BLOCK(32), 8, 32, 32},
+        {QGEMM_INT8_BLOCK(80), 8, 80, 80},
         {QGEMM_INT8_BLOCK(192), 8, 192, 192},
     };
     const int Ks[] = {2, 30, 64, 66, 128, 130, 192, 320, 384, 1024};

@@ -178,11 +178,11 @@ def test_sizes():
         Q.qgemm_packed_size(100, 8, "int4b64")
 
 
-@pytest.mark.parametrize("fmt", FMTS + ["int4b32", "int4b128", "int4b192", "int8b32", "int8b64",
-                                        "int8b192"])
+@pytest.mark.parametrize("fmt", FMTS + ["int4b16", "int4b32", "int4b48", "int4b128", "int4b192",
+                                        "int8b16", "int8b32", "int8b64", "int8b80", "int8b192"])
 @pytest.mark.parametrize("shape", [(1, 64), (5, 128), (70, 192), (33, 1024)])
 def test_quantizer_matches_oracle_bit_exact(fmt, shape):
-    if fmt[:5] in ("int4b", "int8b") and fmt[5:] not in ("0", "32", "64") and shape[1] % int(fmt[5:]):
+    if fmt[:5] in ("int4b", "int8b") and fmt[5:] != "0" and shape[1] % int(fmt[5:]):
         pytest.skip("the block does not divide K")
     N, K = shape
     rng = np.random.default_rng(N * 1000 + K)
@@ -206,12 +206,13 @@ def test_quantizer_rejects_nonfinite():
         Q.qgemm_quantize_weights(np.zeros((4, 64), np.float32), "f32")
 
 
-@pytest.mark.parametrize("fmt", FMTS + ["f32", "int4b32", "int4b128", "int4b320", "int8b32",
-                                        "int8b64", "int8b320"])
+@pytest.mark.parametrize("fmt", FMTS + ["f32", "int4b16", "int4b32", "int4b48", "int4b128",
+                                        "int4b320", "int8b16", "int8b32", "int8b64", "int8b80",
+                                        "int8b96", "int8b320"])
 @pytest.mark.parametrize("shape", [(1, 64), (3, 128), (70, 192), (37, 4160)])
 def test_pack_unpack_round_trip(fmt, shape):
     N, K = shape
-    if fmt in ("int4b128", "int4b320", "int8b320") and K % int(fmt[5:]):
+    if fmt[:5] in ("int4b", "int8b") and fmt[5:] != "0" and K % int(fmt[5:]):
         pytest.skip("the block does not divide K")
     rng = np.random.default_rng(K + N)
     if fmt == "f32":
@@ -299,6 +300,9 @@ def test_device_quantizer_validation_before_device(lib):
         assert q(96, 4, 5) == SHAPE                   # Int4-Block0 packs as Block64
         assert q(65, 4, 3) == SHAPE                   # W4A8: even K
         assert q(0, 4, 2) == SHAPE
+        assert q(192, 4, Q.QGEMM_INT4_BLOCK(48)) == FMT    # multiples of 16 other than
+        assert q(320, 4, Q.QGEMM_INT8_BLOCK(80)) == FMT    # 16, 32, 64 k: host quantiser
+        assert q(384, 4, Q.QGEMM_INT4_BLOCK(96)) == FMT
         assert q(64, 0, 1, None, None, None) == OK    # nothing to do
         assert q(64, 4, 1, W=None) == NULL
         assert q(64, 4, 2, a=None) == NULL
@@ -341,8 +345,12 @@ def test_int4_block_size_validation(lib):
     assert size(384, Q.QGEMM_INT4_BLOCK(256)) == SHAPE    # the block must divide K
     assert size(256, Q.QGEMM_INT4_BLOCK(32)) == 0         # a pair per half of each 64-block
     assert size(96, Q.QGEMM_INT4_BLOCK(32)) == SHAPE      # the kernels' step: K % 64 == 0
-    assert size(256, Q.QGEMM_INT4_BLOCK(16)) == FMT       # 32 or multiples of 64
-    assert size(256, Q.QGEMM_INT4_BLOCK(96)) == FMT
+    assert size(256, Q.QGEMM_INT4_BLOCK(16)) == 0         # a pair per quarter of each 64-block
+    assert size(192, Q.QGEMM_INT4_BLOCK(48)) == 0         # any multiple of 16 that divides K
+    assert size(384, Q.QGEMM_INT4_BLOCK(96)) == 0
+    assert size(256, Q.QGEMM_INT4_BLOCK(96)) == SHAPE
+    assert size(256, Q.QGEMM_INT4_BLOCK(8)) == FMT        # multiples of 16 only
+    assert size(256, Q.QGEMM_INT4_BLOCK(24)) == FMT
     assert size(256, Q.QGEMM_INT4_BLOCK(0)) == FMT
     assert size(256, Q.QGEMM_INT4_BLOCK(-64)) == FMT
     assert Q.qgemm_workspace_size(16, 4096, 256, "int4b128") == \
@@ -352,10 +360,11 @@ def test_int4_block_size_validation(lib):
 def test_int8_block_sizes_layout_golden(lib):
     """Int8 with block b: codes as channel rows [Np][K] (the Int8-Block0 rows);
     pairs channel-major, one entry per 64-block repeating the pair of the
-    b-block that holds it (b = 32: one entry per 32-element half)."""
+    b-block that holds it (b = 32, 96: one entry per 32-element half; other
+    multiples of 16: one per 16-element quarter)."""
     N, K = 6, 384
     wc = (np.arange(N * K, dtype=np.int64) * 7 % 251).astype(np.uint8).reshape(N, K)
-    for b in (32, 64, 128, 384):
+    for b in (16, 32, 48, 64, 96, 128, 384):
         nb = K // b
         pc = np.arange(N * nb * 2, dtype=np.float32).reshape(N, nb, 2) + 1
         wp, sp = Q.qgemm_pack_weights(K, N, f"int8b{b}", wc, pc)
@@ -363,7 +372,7 @@ def test_int8_block_sizes_layout_golden(lib):
         assert wp.size == -(-Np * K // 256) * 256
         rows = wp[:Np * K].reshape(Np, K)
         assert np.array_equal(rows[:N], wc) and not np.any(rows[N:])
-        H = 2 if b == 32 else 1
+        H = 1 if b % 64 == 0 else 2 if b % 32 == 0 else 4
         ent = sp.view(np.float32)[:Np * (K // 64) * H * 2].reshape(Np, K // 64 * H, 2)
         for n in range(N):
             for e in range(K // 64 * H):
@@ -377,8 +386,10 @@ def test_int8_block_sizes_layout_golden(lib):
     assert size(256, Q.QGEMM_INT8_BLOCK(128)) == 0
     assert size(384, Q.QGEMM_INT8_BLOCK(256)) == SHAPE    # the block must divide K
     assert size(96, Q.QGEMM_INT8_BLOCK(32)) == SHAPE      # K % 64 == 0
-    assert size(256, Q.QGEMM_INT8_BLOCK(16)) == FMT       # 32 or multiples of 64
-    assert size(256, Q.QGEMM_INT8_BLOCK(96)) == FMT
+    assert size(256, Q.QGEMM_INT8_BLOCK(16)) == 0         # multiples of 16
+    assert size(320, Q.QGEMM_INT8_BLOCK(80)) == 0
+    assert size(256, Q.QGEMM_INT8_BLOCK(96)) == SHAPE
+    assert size(256, Q.QGEMM_INT8_BLOCK(40)) == FMT
     assert size(256, Q.QGEMM_INT8_BLOCK(-64)) == FMT
     assert Q.qgemm_workspace_size(64, 4096, 512, "int8b64") == \
         Q.qgemm_workspace_size(64, 4096, 512, "int8b0")   # the channel-row kernel's split-K plan
@@ -402,6 +413,31 @@ def test_int4_block32_pair_records_golden():
             for h in range(2):
                 assert list(recs[t * (K // 64) + b, h, c]) == list(pc[n, 2 * b + h])
     assert not np.any(recs[K // 64:, :, 8:, :])        # channels 40..63: zero padding
+
+
+@pytest.mark.parametrize("b", [16, 48])
+def test_int4_quarter_pair_records_golden(b):
+    """Int4 with blocks that are multiples of 16 but not of 32: codes as
+    Int4-Block64; pair record (t, b64) is 1024 bytes, entry 4 c + j holding
+    channel 32 t + c's pair for the quarter K-elements 64 b64 + 16 j .. + 15
+    (the two quarters of one 32-element half are adjacent)."""
+    N, K = 40, 192
+    nblk = K // b
+    wc = np.arange(N * K // 2, dtype=np.int64).astype(np.uint8).reshape(N, K // 2)
+    pc = np.arange(N * nblk * 2, dtype=np.float32).reshape(N, nblk, 2)
+    wp, sp = Q.qgemm_pack_weights(K, N, f"int4b{b}", wc, pc)
+    wp64, _ = Q.qgemm_pack_weights(K, N, "int4b64", wc, np.zeros((N, K // 64, 2), np.float32))
+    assert np.array_equal(wp, wp64) and sp.size == 2 * (K // 64) * 1024
+    recs = sp.view(np.float32).reshape(-1, 32, 4, 2)
+    for n in range(N):
+        t, c = divmod(n, 32)
+        for b64 in range(K // 64):
+            for j in range(4):
+                k = 64 * b64 + 16 * j
+                assert list(recs[t * (K // 64) + b64, c, j]) == list(pc[n, k // b])
+    assert not np.any(recs[K // 64:, 8:, :, :])        # channels 40..63: zero padding
+    q2, p2 = Q.qgemm_unpack_weights(K, N, f"int4b{b}", wp, sp)
+    assert np.array_equal(q2, wc.reshape(-1)) and np.array_equal(p2, pc.reshape(-1))
 
 
 def test_binding_checks_dtypes_and_sizes_before_the_library():

@@ -4,7 +4,8 @@ oracle's epilogue (fp16 outputs rounded to nearest even by the oracle).
 
 Every kernel path is covered: the GEMVs (Int4, Int8, fp16, W4A8 with and
 without the fused quantiser), the tiled Int4 / Int8 / fp16 / fp32 / W4A8
-GEMMs, every split-K reduce, fp32 K-groups and 32-element Int4 blocks. Both
+GEMMs, every split-K reduce, fp32 K-groups and Int4 / Int8 blocks of 16, 32
+and 48 elements. Both
 sides start from the oracle's quantisation of the seeded weights (the
 library packs it). Tolerances are
 the library's (max-abs 1e-2, relative-Frobenius 2e-3); an fp16 output may
@@ -38,7 +39,8 @@ SHAPES = [("f32", 16, 256, 256), ("f32", 8, 2560, 1024), ("f32", 130, 512, 200),
           ("w4a8", 1, 4096, 300), ("w4a8", 6, 2048, 300), ("w4a8", 40, 3072, 300),
           ("int8b0", 32, 2560, 256), ("f16", 9, 4096, 96), ("int4b32", 96, 1024, 300),
           ("int4b64", 3, 9728, 640), ("w4a8", 2, 9728, 640), ("int8b64", 3, 1024, 130),
-          ("int8b32", 130, 640, 200)]
+          ("int8b32", 130, 640, 200), ("int4b16", 96, 1024, 300), ("int8b16", 3, 1024, 130),
+          ("int4b48", 2, 2496, 300)]
 EPILOGUES = [("bias", "silu", "f32", False), ("residual", "gelu", "f16", False),
              ("bias+residual", "relu", "f32", False), ("bias+residual", "gelu", "f16", True),
              ("bias+residual", "none", "f32", True)]

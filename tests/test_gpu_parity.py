@@ -127,9 +127,10 @@ def test_f16_shapes(M):
 def test_int4_gemv_split_k(M):
     """The Int4 GEMV on shapes with few 32-channel tiles splits K over the
     workgroups of a tile and adds the partial tiles in a fixed order; ragged N,
-    passes of 64 blocks, Block0 and 32-element blocks included."""
+    passes of 64 blocks, Block0 and blocks of 16, 32 and 48 included."""
     for fmt, K, N in [("int4b64", 9728, 2560), ("int4b64", 2560, 1024), ("int4b64", 4096, 300),
-                      ("int4b64", 16384, 70), ("int4b0", 9728, 96), ("int4b32", 9728, 130)]:
+                      ("int4b64", 16384, 70), ("int4b0", 9728, 96), ("int4b32", 9728, 130),
+                      ("int4b16", 9728, 130), ("int4b48", 2496, 1024)]:
         _parity(fmt, M, K, N, seed=M * 7 + K + N)
 
 
@@ -137,33 +138,38 @@ def test_int4_gemv_split_k(M):
 def test_int4_gemv_k_passes(M):
     """The half-tile Int4 GEMV over K in passes of 64 blocks (K > 4096) with
     enough channel tiles not to split: ragged N, an odd block count in the
-    last pass, blocks of 32; with at most one half tile per CU (N <= 4096 at
+    last pass, blocks of 16 and 32; with at most one half tile per CU (N <= 4096 at
     one row group) the sixteen-wave kernel, a two-block last pass among them."""
     for fmt, K, N in [("int4b64", 8192, 4100), ("int4b32", 5120, 1000), ("int4b64", 12352, 4128),
-                      ("int4b64", 8320, 4000), ("int4b64", 11008, 4096)]:
+                      ("int4b64", 8320, 4000), ("int4b64", 11008, 4096), ("int4b16", 5120, 1000)]:
         _parity(fmt, M, K, N, seed=M * 23 + K + N)
 
 
 @pytest.mark.parametrize("M", [1, 3, 8, 9, 64, 65, 129])
 def test_int4_other_block_sizes(M):
-    """Int4 with blocks of 32, 128, 256 and 320 K-elements (the page's
-    blockSize parameter) through the Int4 GEMV and GEMM, split-K shapes
-    included."""
+    """Int4 with blocks of 16, 32, 48, 80, 96, 128, 256 and 320 K-elements (the
+    page's blockSize parameter, any multiple of 16 that divides K) through
+    the Int4 GEMV and GEMM, split-K shapes included."""
     for fmt, K, N in [("int4b128", 128, 5), ("int4b128", 4096, 256), ("int4b256", 2560, 1024),
                       ("int4b320", 640, 130), ("int4b128", 9728, 96), ("int4b32", 64, 33),
-                      ("int4b32", 4096, 300), ("int4b32", 2560, 1024)]:
+                      ("int4b32", 4096, 300), ("int4b32", 2560, 1024), ("int4b16", 64, 33),
+                      ("int4b16", 4096, 300), ("int4b48", 192, 70), ("int4b48", 2496, 1024),
+                      ("int4b80", 640, 256), ("int4b96", 3072, 130)]:
         _parity(fmt, M, K, N, seed=M * 17 + K + N)
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 9, 64, 65, 129])
 def test_int8_block_sizes(M):
-    """Int8 with a pair per block of 32, 64, 128, 192 or 320 K-elements: the
+    """Int8 with a pair per block of 16, 32, 48, 64, 80, 96, 128, 192 or 320
+    K-elements: the
     Int8 GEMV (M <= 4, K <= 8192) adds each 16-code slice with its block's
     pair; the channel-row GEMM dequantises per weight (split-K shapes, K past
     the GEMV's limit, ragged N)."""
     for fmt, K, N in [("int8b64", 64, 5), ("int8b64", 4096, 256), ("int8b32", 2560, 1024),
                       ("int8b128", 4096, 300), ("int8b320", 640, 130), ("int8b64", 9728, 96),
-                      ("int8b192", 768, 70), ("int8b32", 8192, 40)]:
+                      ("int8b192", 768, 70), ("int8b32", 8192, 40), ("int8b16", 2560, 1024),
+                      ("int8b16", 8192, 40), ("int8b48", 768, 70), ("int8b80", 640, 130),
+                      ("int8b96", 4608, 300)]:
         _parity(fmt, M, K, N, seed=M * 19 + K + N)
 
 

@@ -75,11 +75,13 @@ SHAPES = {
     "int8b32": [(64, 1), (128, 70), (4096, 300)],
     "int8b512": [(512, 3), (4096, 70)],
     "int8b192": [(192, 5), (2304, 40)],
+    "int4b16": [(64, 1), (128, 70), (4096, 300)],
+    "int8b16": [(64, 1), (128, 70), (4096, 300)],
 }
 
 
 @pytest.mark.parametrize("fmt", FMTS + ["int4b32", "int4b128", "int4b320", "int8b64", "int8b32",
-                                 "int8b512", "int8b192"])
+                                 "int8b512", "int8b192", "int4b16", "int8b16"])
 def test_device_quantizer_bit_exact(fmt):
     for i, (K, N) in enumerate(SHAPES[fmt]):
         rng = np.random.default_rng(700 + i)
@@ -106,7 +108,8 @@ def _corner_rows(K):
     return np.stack(rows)
 
 
-@pytest.mark.parametrize("fmt", FMTS + ["int4b32", "int4b128", "int8b64", "int8b32"])
+@pytest.mark.parametrize("fmt", FMTS + ["int4b32", "int4b128", "int8b64", "int8b32", "int4b16",
+                                 "int8b16"])
 def test_device_quantizer_corner_cases(fmt):
     for K in ((128, 256) if fmt == "int4b128" else (64, 256)):
         W = _corner_rows(K)

@@ -173,16 +173,16 @@ static qgemm_status dispatch(int M, int K, int N, qgemm_format f, const Geometry
         return launched(launch_gemm_f32(M, K, N, static_cast<const float *>(A),
                                         static_cast<const float *>(Bq), C, epi, nsplit, part, s));
     case QGEMM_INT4_B64:   // every Int4 format without A8 packs as Int4-Block64
-        return launched(gemv ? launch_gemv_int4b64(M, K, N, A, Bq, scales, C, epi, g.block == 32,
+        return launched(gemv ? launch_gemv_int4b64(M, K, N, A, Bq, scales, C, epi, pair_groups(g.block),
                                                    nsplit, part, s)
-                             : launch_gemm_int4b64(M, K, N, A, Bq, scales, C, epi, g.block == 32,
+                             : launch_gemm_int4b64(M, K, N, A, Bq, scales, C, epi, pair_groups(g.block),
                                                    nsplit, part, s));
     case QGEMM_INT8_B0:
         return launched(gemv ? launch_gemv_int8b0(M, K, N, A, Bq, scales, C, epi, s)
                              : launch_gemm_int8b0(M, K, N, A, Bq, scales, C, epi, nsplit, part, s));
     case QGEMM_INT8_BLOCK_BASE:   // Int8 with a pair per block of K
-        return launched(gemv ? launch_gemv_int8blk(M, K, N, A, Bq, scales, C, epi, g.block == 32, s)
-                             : launch_gemm_int8blk(M, K, N, A, Bq, scales, C, epi, g.block == 32,
+        return launched(gemv ? launch_gemv_int8blk(M, K, N, A, Bq, scales, C, epi, pair_groups(g.block), s)
+                             : launch_gemm_int8blk(M, K, N, A, Bq, scales, C, epi, pair_groups(g.block),
                                                    nsplit, part, s));
     case QGEMM_W4A8:
         return run_w4a8(M, K, N, p, A, Bq, scales, C, epi, ws, s, nullptr);
@@ -357,6 +357,11 @@ static qgemm_status check_quantize(int K, int N, qgemm_format f, const float *W,
     if (f == QGEMM_F32 || f == QGEMM_F16) return QGEMM_ERR_FORMAT;   // float weights are not quantised
     qgemm_status st = geometry(K, N, f, g);
     if (st != QGEMM_OK) return st;
+    // blocked formats: blocks of 16, 32 or a multiple of 64 (other multiples
+    // of 16 straddle the kernel's 64-element chunks; quantise them on the host)
+    if ((is_int4_blocked(f) || is_int8_blocked(f)) && g->block != 16 && g->block != 32 &&
+        g->block % 64 != 0)
+        return QGEMM_ERR_FORMAT;
     *empty = N == 0;
     if (*empty) return QGEMM_OK;
     if (!W || !q || !pairs) return QGEMM_ERR_NULL;

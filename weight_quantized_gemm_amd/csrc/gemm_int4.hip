@@ -50,6 +50,8 @@
 // bands: each XCD fetches only its bands of A and B. For 512 x 4096 the
 // host picks 2 x 4 (A read by four XCDs, B by two), fewer bytes than one
 // column band per XCD across all rows.
+#include <type_traits>
+
 #include "kernels_common.h"
 #include "qgemm_internal.h"
 
@@ -147,8 +149,11 @@ __device__ __forceinline__ h8_t dequant8(unsigned word, const DqParams &p, unsig
 // it would stall the matrix instruction that reads it).
 __device__ __forceinline__ void pin(h8_t &v) { asm volatile("" : "+v"(v)); }
 
-// HP: one pair per 32-element half of each 64-block (Int4 blocks of 32).
-template <class T, bool HP>
+// G: pair entries per 64-block (1; 2: one per 32-element half, blocks of
+// 32; 4: one per 16-element quarter, blocks that are odd multiples of 16).
+// A lane decodes one 32-element half of each block: with G = 4 its steps 0-1
+// and 2-3 take the two quarters' pairs, one 16-byte load for both.
+template <class T, int G>
 __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     int M, int K, int N, int tiles_m, int tiles_n, int xcd_rows,
     const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
@@ -214,7 +219,9 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
         a_off[i] = (unsigned)(min(8 * i + arow, arows - 1) * K + 8 * apc) * 2u;
     // B: records of each accumulator column tile (tiles past N: loaded, never
     // stored), one 1 KiB record and one pair record per block
-    constexpr unsigned PREC = HP ? 512u : 256u;   // bytes per pair record
+    constexpr unsigned PREC = 256u * G;           // bytes per pair record
+    constexpr int GQ = G == 4 ? 2 : 1;            // pair constants per lane and block
+    using PairT = typename std::conditional<G == 4, f4_t, f2_t>::type;
     __amdgpu_buffer_rsrc_t b_rs[CF], p_rs[CF];
 #pragma unroll
     for (int cf = 0; cf < CF; ++cf) {
@@ -223,7 +230,8 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
         p_rs[cf] = byte_rsrc(reinterpret_cast<const char *>(Sp) + rec0 * PREC, (unsigned)nblk * PREC);
     }
     const unsigned b_off = (unsigned)lane * 16u;
-    const unsigned p_off = HP ? (unsigned)(h * 64 + r * 2) * 4u : (unsigned)r * 8u;
+    const unsigned p_off = G == 4 ? (unsigned)(4 * r + 2 * h) * 8u
+                         : G == 2 ? (unsigned)(32 * h + r) * 8u : (unsigned)r * 8u;
 
     auto load_a = [&](u4_t (&dst)[A_PIECES], int kt) {
 #pragma unroll
@@ -243,9 +251,24 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
 #pragma unroll
         for (int cf = 0; cf < CF; ++cf) codes[cf] = buf_load16<kNonTemporal>(b_rs[cf], b_off, (unsigned)kt * 1024u);
     };
-    auto load_p = [&](f2_t (&pairs)[CF], int kt) {
+    auto load_p = [&](PairT (&pairs)[CF], int kt) {
 #pragma unroll
-        for (int cf = 0; cf < CF; ++cf) pairs[cf] = buf_load8(p_rs[cf], p_off, (unsigned)kt * PREC);
+        for (int cf = 0; cf < CF; ++cf) {
+            if constexpr (G == 4)
+                pairs[cf] = __builtin_bit_cast(f4_t, buf_load16(p_rs[cf], p_off, (unsigned)kt * PREC));
+            else
+                pairs[cf] = buf_load8(p_rs[cf], p_off, (unsigned)kt * PREC);
+        }
+    };
+    // a block's dequantisation constants: set 0 for MFMA steps 0-1, set
+    // GQ - 1 for steps 2-3
+    auto make_prm = [&](const PairT &pp, bool keep, DqParams (&dst)[GQ]) {
+        if constexpr (G == 4) {
+            dst[0] = dq_params(f2_t{pp.x, pp.y}, keep);
+            dst[GQ - 1] = dq_params(f2_t{pp.z, pp.w}, keep);
+        } else {
+            dst[0] = dq_params(pp, keep);
+        }
     };
 
     // decode constants, opaque to the optimiser so they stay in registers
@@ -263,8 +286,8 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
 
     u4_t an[A_SETS][A_PIECES];  // A register sets: set j % A_SETS holds block j
     u4_t bc[B_RING][CF];        // B code ring: slot j % B_RING holds block j
-    f2_t bp[P_RING][CF];        // pair ring: slot j % 2 holds block j
-    DqParams prm[CF];
+    PairT bp[P_RING][CF];       // pair ring: slot j % 2 holds block j
+    DqParams prm[CF][GQ];
     h8_t acur[RF], anxt[RF], bcur[CF], bnxt[CF];
 
     // Every global load below is unconditional, from a block index clamped
@@ -287,10 +310,10 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     store_a(a_tile(0), an[0]);
     load_a(an[0], min(kb0 + A_SETS, last));
 #pragma unroll
-    for (int cf = 0; cf < CF; ++cf) prm[cf] = dq_params(bp[0][cf], nb > 0);
+    for (int cf = 0; cf < CF; ++cf) make_prm(bp[0][cf], nb > 0, prm[cf]);
     read_a(a_tile(0), 0, acur);
 #pragma unroll
-    for (int cf = 0; cf < CF; ++cf) bcur[cf] = dequant8(bc[0][cf][0], prm[cf], m_lo, m_hi, magic);
+    for (int cf = 0; cf < CF; ++cf) bcur[cf] = dequant8(bc[0][cf][0], prm[cf][0], m_lo, m_hi, magic);
 
     // Block i reads A tile i % 2 and B slot i % 4; at its start, block i + 1's
     // A (register set (i + 1) % A_SETS, loaded A_SETS blocks ago) goes into
@@ -318,7 +341,8 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
                     read_a(a_tile(u % A_TILES), s + 1, anxt);
 #pragma unroll
                     for (int cf = 0; cf < CF; ++cf) {
-                        bnxt[cf] = dequant8(bc[u % B_RING][cf][s + 1], prm[cf], m_lo, m_hi, magic);
+                        bnxt[cf] = dequant8(bc[u % B_RING][cf][s + 1], prm[cf][(s + 1) * GQ / 4],
+                                            m_lo, m_hi, magic);
                         pin(bnxt[cf]);
                     }
                 } else {
@@ -326,8 +350,8 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
                     read_a(a_tile((u + 1) % A_TILES), 0, anxt);
 #pragma unroll
                     for (int cf = 0; cf < CF; ++cf) {
-                        prm[cf] = dq_params(bp[(u + 1) % P_RING][cf], i + 1 < nb);
-                        bnxt[cf] = dequant8(bc[un][cf][0], prm[cf], m_lo, m_hi, magic);
+                        make_prm(bp[(u + 1) % P_RING][cf], i + 1 < nb, prm[cf]);
+                        bnxt[cf] = dequant8(bc[un][cf][0], prm[cf][0], m_lo, m_hi, magic);
                         pin(bnxt[cf]);
                     }
                 }
@@ -415,7 +439,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
 
 template <class T>
 static hipError_t launch_tiles(int M, int K, int N, const void *A, const void *Wp, const void *Sp,
-                               void *out, const Epilogue &epi, int half_pairs, int nsplit,
+                               void *out, const Epilogue &epi, int pair_g, int nsplit,
                                hipStream_t s) {
     const int tiles_m = div_up(M, T::BM), tiles_n = div_up(N, T::BN);
     // XCD grid: row bands x column bands = 8, each XCD's L2 then fetches
@@ -430,7 +454,8 @@ static hipError_t launch_tiles(int M, int K, int N, const void *A, const void *W
         const double fetched = gc * a_bytes + gr * b_bytes;
         if (xcd_rows == 0 || fetched < best) { xcd_rows = gr; best = fetched; }
     }
-    auto kernel = half_pairs ? gemm_int4b64_kernel<T, true> : gemm_int4b64_kernel<T, false>;
+    auto kernel = pair_g == 4 ? gemm_int4b64_kernel<T, 4>
+                : pair_g == 2 ? gemm_int4b64_kernel<T, 2> : gemm_int4b64_kernel<T, 1>;
     hipLaunchKernelGGL(kernel, dim3(tiles_m * tiles_n, nsplit), dim3(64 * NWAVE), 0, s,
                        M, K, N, tiles_m, tiles_n, xcd_rows, static_cast<const _Float16 *>(A),
                        static_cast<const uint8_t *>(Wp), static_cast<const float *>(Sp), out, epi);
@@ -438,13 +463,13 @@ static hipError_t launch_tiles(int M, int K, int N, const void *A, const void *W
 }
 
 hipError_t launch_gemm_int4b64(int M, int K, int N, const void *A, const void *Wp,
-                               const void *Sp, void *C, const Epilogue &epi, int half_pairs,
+                               const void *Sp, void *C, const Epilogue &epi, int pair_g,
                                int nsplit, float *part, hipStream_t s) {
     void *out = nsplit > 1 ? static_cast<void *>(part) : C;
     const Int4Tile t = int4_tile(M);
     hipError_t e = t.bm == 128
-        ? launch_tiles<TileCfg<128, 64>>(M, K, N, A, Wp, Sp, out, epi, half_pairs, nsplit, s)
-        : launch_tiles<TileCfg<64, 128>>(M, K, N, A, Wp, Sp, out, epi, half_pairs, nsplit, s);
+        ? launch_tiles<TileCfg<128, 64>>(M, K, N, A, Wp, Sp, out, epi, pair_g, nsplit, s)
+        : launch_tiles<TileCfg<64, 128>>(M, K, N, A, Wp, Sp, out, epi, pair_g, nsplit, s);
     if (e != hipSuccess || nsplit <= 1) return e;
     return launch_splitk_reduce_f32(part, nsplit, M, N, C, epi, s);
 }

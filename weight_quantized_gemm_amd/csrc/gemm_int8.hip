@@ -97,7 +97,8 @@ __device__ __forceinline__ h8_t dequant8_biased(h8_t x, float scale, float b) {
 // loads, pieces past K masked); 2: any K (element loads, masked past K).
 // WF16: the rows hold fp16 weights (2 bytes each) instead of Int8-Block0 codes.
 // PM (blocked Int8, KMODE 0): the rows hold Int8 codes with a pair per
-// 64-block (PM = 1) or per 32-element half (PM = 2), channel-major; each
+// 64-block (PM = 1), per 32-element half (PM = 2) or per 16-element quarter
+// (PM = 4), channel-major; each
 // lane dequantises its 16 codes of a block with their pair (one fused
 // multiply-add per weight, rounded once to fp16) and the MFMAs take the
 // weights, so the epilogue adds no pair term.
@@ -141,14 +142,15 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
 #pragma unroll
     for (int cf = 0; cf < CF; ++cf)
         b_row[cf] = Wp + ((size_t)min(n0 + cf * 16 + r, N - 1) * Kp + 16 * g) * WB;
-    // PM: this lane's pair entries, channel n0 + 16 cf + r, half g / 2 (PM = 2)
-    constexpr int H = PM == 2 ? 2 : 1;
+    // PM: this lane's pair entries, channel n0 + 16 cf + r, sub-block g PM / 4
+    // of each 64-block (the lane's 16 codes lie in one quarter)
+    constexpr int H = PM ? PM : 1;
     const f2_t *p_row[PM ? CF : 1];
     if constexpr (PM != 0) {
 #pragma unroll
         for (int cf = 0; cf < CF; ++cf)
             p_row[cf] = reinterpret_cast<const f2_t *>(Sp) +
-                        (size_t)min(n0 + cf * 16 + r, N - 1) * (Kp / BK) * H + (PM == 2 ? (g >> 1) : 0);
+                        (size_t)min(n0 + cf * 16 + r, N - 1) * (Kp / BK) * H + g * H / 4;
     }
     auto load_p = [&](f2_t (&dst)[PM ? CF : 1], int it) {
         if constexpr (PM != 0) {
@@ -385,10 +387,11 @@ hipError_t launch_gemm_f16(int M, int K, int N, const void *A, const void *Wp, v
 }
 
 hipError_t launch_gemm_int8blk(int M, int K, int N, const void *A, const void *Wp,
-                               const void *Sp, void *C, const Epilogue &epi, int half_pairs,
+                               const void *Sp, void *C, const Epilogue &epi, int pair_g,
                                int nsplit, float *part, hipStream_t s) {
-    return half_pairs ? launch_rows<false, 2>(M, K, N, A, Wp, Sp, C, epi, nsplit, part, s)
-                      : launch_rows<false, 1>(M, K, N, A, Wp, Sp, C, epi, nsplit, part, s);
+    return pair_g == 4 ? launch_rows<false, 4>(M, K, N, A, Wp, Sp, C, epi, nsplit, part, s)
+         : pair_g == 2 ? launch_rows<false, 2>(M, K, N, A, Wp, Sp, C, epi, nsplit, part, s)
+                       : launch_rows<false, 1>(M, K, N, A, Wp, Sp, C, epi, nsplit, part, s);
 }
 
 }  // namespace qg

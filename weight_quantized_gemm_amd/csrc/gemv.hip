@@ -34,6 +34,83 @@ __device__ __forceinline__ void swap32(float &x, float &y) {
     y = __uint_as_float(r[1]);
 }
 
+// Int4 pair entries (G per 64-block; see the packed layout): lane (c, h)
+// decodes channel c's 32-element half h of a block, so it needs one pair
+// (G = 1, 2) or the two pairs of its quarters (G = 4, one 16-byte load).
+template <int G>
+using Int4Pair = typename std::conditional<G == 4, f4_t, f2_t>::type;
+
+template <int G>
+__device__ __forceinline__ Int4Pair<G> load_int4_pair(const float *Sp, size_t rec, int c, int h) {
+    if constexpr (G == 4)
+        return __builtin_nontemporal_load(reinterpret_cast<const f4_t *>(Sp + rec * 256 + (4 * c + 2 * h) * 2));
+    else if constexpr (G == 2)
+        return __builtin_nontemporal_load(reinterpret_cast<const f2_t *>(Sp + rec * 128 + (32 * h + c) * 2));
+    else
+        return __builtin_nontemporal_load(reinterpret_cast<const f2_t *>(Sp + rec * 64 + c * 2));
+}
+
+// One 32-code half of a block against its staged activations (the pieces
+// av[d] of words d = 0..3 and, per quarter qh, the even / odd activation sums
+// sv[qh]): sum_k a_k (offset + scale q_k), regrouped per pair as offset * sum(a)
+// + scale * sum(a * q) with q read off the fp16 magic decode (1024 + q or
+// 1024 + 16 q), the 1024 bias removed through the sums.
+template <int G>
+__device__ __forceinline__ float int4_half_dot(const u4_t (&av)[4], const unsigned (&word)[4],
+                                               const f2_t *sv, const Int4Pair<G> &pp,
+                                               unsigned magic) {
+    constexpr int GQ = G == 4 ? 2 : 1;
+    float total = 0.f;
+#pragma unroll
+    for (int qh = 0; qh < GQ; ++qh) {
+        float Te = 0.f, To = 0.f;
+#pragma unroll
+        for (int d = qh * 4 / GQ; d < (qh + 1) * 4 / GQ; ++d) {
+            const unsigned y0 = __builtin_amdgcn_perm(magic, word[d], 0x04020400u);
+            const unsigned y1 = __builtin_amdgcn_perm(magic, word[d], 0x04030401u);
+            Te = dot2(as_h2(y0 & 0xFF0FFF0Fu), as_h2(av[d].x), Te);
+            Te = dot2(as_h2(y1 & 0xFF0FFF0Fu), as_h2(av[d].y), Te);
+            To = dot2(as_h2(y0 & 0xFFF0FFF0u), as_h2(av[d].z), To);
+            To = dot2(as_h2(y1 & 0xFFF0FFF0u), as_h2(av[d].w), To);
+        }
+        float off, sc;
+        if constexpr (G == 4) {
+            off = qh ? pp.z : pp.x;
+            sc = qh ? pp.w : pp.y;
+        } else {
+            off = pp.x;
+            sc = pp.y;
+        }
+        const float ce = fmaf(-1024.0f, sc, off);
+        const float co = fmaf(-64.0f, sc, off);
+        total += fmaf(ce, sv[qh].x, fmaf(co, sv[qh].y, fmaf(sc, Te, sc * 0.0625f * To)));
+    }
+    return total;
+}
+
+// Stages one (row, half-block) of activations: the four 16-byte pieces in
+// decode pair order into ap, and the even / odd sums of each of its GQ
+// quarters-of-a-half into hs.
+template <int GQ>
+__device__ __forceinline__ void stage_int4_half(const u4_t (&araw)[4], u4_t *ap, f2_t *hs) {
+    const h2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int qh = 0; qh < GQ; ++qh) {
+        float se = 0.f, so = 0.f;
+#pragma unroll
+        for (int w = qh * 4 / GQ; w < (qh + 1) * 4 / GQ; ++w) {
+            const u4_t v = araw[w];
+            const h2_t p01 = as_h2(v.x), p23 = as_h2(v.y), p45 = as_h2(v.z), p67 = as_h2(v.w);
+            const h2_t e0 = {p01.x, p45.x}, e1 = {p23.x, p67.x};
+            const h2_t o0 = {p01.y, p45.y}, o1 = {p23.y, p67.y};
+            se = dot2(e1, one, dot2(e0, one, se));
+            so = dot2(o1, one, dot2(o0, one, so));
+            ap[w] = u4_t{as_u(e0), as_u(e1), as_u(o0), as_u(o1)};
+        }
+        hs[qh] = f2_t{se, so};
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Int4-Block64
 // ---------------------------------------------------------------------------
@@ -53,10 +130,10 @@ constexpr int TILE_WAVES = 16;
 constexpr int TILE_PASS = 64;                   // K-blocks per pass
 constexpr int TILE_RPW = TILE_PASS / TILE_WAVES;   // blocks per wave and pass
 
-// HP: one pair per 32-element half of each 64-block (Int4 blocks of 32).
+// G: pair entries per 64-block (1, 2 or 4; see load_int4_pair).
 // SPLIT: K split over gridDim.z workgroups per tile (its own instantiation:
 // the unsplit kernel keeps 53 registers, so two workgroups share a CU).
-template <int MR, bool ONE_PASS, bool HP, bool SPLIT>
+template <int MR, bool ONE_PASS, int G, bool SPLIT>
 __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
     int M, int K, int N, const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ Sp, void *__restrict__ C, Epilogue epi) {
@@ -67,9 +144,10 @@ __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
     const int KB0 = SPLIT ? slice_begin(blockIdx.z, nblk, gridDim.z) : 0;
     const int KB1 = SPLIT ? slice_begin(blockIdx.z + 1, nblk, gridDim.z) : nblk;
     const int pmax = min(SPLIT ? (nblk + (int)gridDim.z - 1) / (int)gridDim.z : nblk, TILE_PASS);
+    constexpr int GQ = G == 4 ? 2 : 1;                                          // sums per half-block
     u4_t *ap = reinterpret_cast<u4_t *>(lds);                                   // [MR][pmax * 8]
-    f2_t *hs = reinterpret_cast<f2_t *>(lds + (size_t)MR * pmax * 128);         // [MR][2 pmax]
-    float *part = reinterpret_cast<float *>(lds + (size_t)MR * pmax * 128 + (size_t)MR * pmax * 16);
+    f2_t *hs = reinterpret_cast<f2_t *>(lds + (size_t)MR * pmax * 128);         // [MR][2 pmax][GQ]
+    float *part = reinterpret_cast<float *>(lds + (size_t)MR * pmax * (128 + 16 * GQ));
     // part: [TILE_WAVES][MR][32]
 
     const int tid = threadIdx.x;
@@ -104,14 +182,12 @@ __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
         //    with no skipped loads the compiler's in-order count of
         //    outstanding loads stays exact, so each block waits only for its
         //    own data. Clamped blocks are never used.
-        f2_t pr[TILE_RPW];
+        Int4Pair<G> pr[TILE_RPW];
         u4_t wq[TILE_RPW];
 #pragma unroll
         for (int i = 0; i < TILE_RPW; ++i) {
             const int b = b0 + min(wave + TILE_WAVES * i, pb - 1);
-            pr[i] = __builtin_nontemporal_load(
-                reinterpret_cast<const f2_t *>(HP ? Sp + ((size_t)t * nblk + b) * 128 + h * 64 + c * 2
-                                                  : Sp + ((size_t)t * nblk + b) * 64 + c * 2));
+            pr[i] = load_int4_pair<G>(Sp, (size_t)t * nblk + b, c, h);
         }
 #pragma unroll
         for (int i = 0; i < TILE_RPW; ++i) {
@@ -120,21 +196,9 @@ __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
                 reinterpret_cast<const u4_t *>(Wp + ((size_t)t * nblk + b) * 1024) + lane);
         }
         // 3. activations to LDS in decode pair order, with even / odd sums
-        if (tid < MR * nhb) {
-            float se = 0.f, so = 0.f;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const u4_t v = araw[w];
-                const h2_t p01 = as_h2(v.x), p23 = as_h2(v.y), p45 = as_h2(v.z), p67 = as_h2(v.w);
-                const h2_t e0 = {p01.x, p45.x}, e1 = {p23.x, p67.x};
-                const h2_t o0 = {p01.y, p45.y}, o1 = {p23.y, p67.y};
-                const h2_t one = {(_Float16)1.0f, (_Float16)1.0f};
-                se = dot2(e1, one, dot2(e0, one, se));
-                so = dot2(o1, one, dot2(o0, one, so));
-                ap[(size_t)ar * (pmax * 8) + ahb * 4 + w] = u4_t{as_u(e0), as_u(e1), as_u(o0), as_u(o1)};
-            }
-            hs[(size_t)ar * (2 * pmax) + ahb] = f2_t{se, so};
-        }
+        if (tid < MR * nhb)
+            stage_int4_half<GQ>(araw, ap + (size_t)ar * (pmax * 8) + ahb * 4,
+                                hs + ((size_t)ar * (2 * pmax) + ahb) * GQ);
         __syncthreads();
 
         // 4. decode and accumulate this wave's blocks of the pass
@@ -146,27 +210,20 @@ __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
             // row strides, opaque per block: computed here rather than for
             // every (row, block) up front, where they would hold more
             // registers than a 1024-thread workgroup has
+            // (with G = 4 the compiler keeps pmax in a vector register and
+            // cannot copy it to a scalar one)
             int pm = pmax;
-            asm volatile("" : "+s"(pm));
-            const float off = pr[i].x, sc = pr[i].y;
-            const float ce = fmaf(-1024.0f, sc, off);
-            const float co = fmaf(-64.0f, sc, off);
+            if constexpr (G == 4)
+                asm volatile("" : "+v"(pm));
+            else
+                asm volatile("" : "+s"(pm));
+            const unsigned word[4] = {wq[i][0], wq[i][1], wq[i][2], wq[i][3]};
 #pragma unroll
             for (int r = 0; r < MR; ++r) {
-                float Te = 0.f, To = 0.f;
+                u4_t av[4];
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const u4_t av = ap[(size_t)r * (pm * 8) + hbg * 4 + d];
-                    const unsigned word = wq[i][d];
-                    const unsigned y0 = __builtin_amdgcn_perm(magic, word, 0x04020400u);
-                    const unsigned y1 = __builtin_amdgcn_perm(magic, word, 0x04030401u);
-                    Te = dot2(as_h2(y0 & 0xFF0FFF0Fu), as_h2(av.x), Te);
-                    Te = dot2(as_h2(y1 & 0xFF0FFF0Fu), as_h2(av.y), Te);
-                    To = dot2(as_h2(y0 & 0xFFF0FFF0u), as_h2(av.z), To);
-                    To = dot2(as_h2(y1 & 0xFFF0FFF0u), as_h2(av.w), To);
-                }
-                const f2_t sv = hs[(size_t)r * (2 * pm) + hbg];
-                acc[r] += fmaf(ce, sv.x, fmaf(co, sv.y, fmaf(sc, Te, sc * 0.0625f * To)));
+                for (int d = 0; d < 4; ++d) av[d] = ap[(size_t)r * (pm * 8) + hbg * 4 + d];
+                acc[r] += int4_half_dot<G>(av, word, hs + ((size_t)r * (2 * pm) + hbg) * GQ, pr[i], magic);
             }
         }
         if (!ONE_PASS && b0 + TILE_PASS < KB1) __syncthreads();   // LDS reused by the next pass
@@ -218,7 +275,7 @@ constexpr int HALF_WAVES = 8;
 // hold them all at once (K = 4096, N = 11008: 7.9 us against 7.6).
 constexpr int HALF_WAVES_WIDE = 16;
 
-template <int MR, bool ONE_PASS, bool HP, int NW>
+template <int MR, bool ONE_PASS, int G, int NW>
 __global__ __launch_bounds__(64 * NW) void gemv_int4b64_half_kernel(
     int M, int K, int N, const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ Sp, void *__restrict__ C, Epilogue epi) {
@@ -227,9 +284,10 @@ __global__ __launch_bounds__(64 * NW) void gemv_int4b64_half_kernel(
     constexpr int AS = (MR * 128 + 64 * NW - 1) / (64 * NW);   // staging slots per thread
     const int nblk = K >> 6;
     const int pmax = min(nblk, TILE_PASS);                                     // blocks per pass
+    constexpr int GQ = G == 4 ? 2 : 1;                                         // sums per half-block
     u4_t *ap = reinterpret_cast<u4_t *>(lds);                                  // [MR][pmax * 8]
-    f2_t *hs = reinterpret_cast<f2_t *>(lds + (size_t)MR * pmax * 128);        // [MR][2 pmax]
-    float *part = reinterpret_cast<float *>(lds + (size_t)MR * pmax * 144);    // [NW][MR][16]
+    f2_t *hs = reinterpret_cast<f2_t *>(lds + (size_t)MR * pmax * 128);        // [MR][2 pmax][GQ]
+    float *part = reinterpret_cast<float *>(lds + (size_t)MR * pmax * (128 + 16 * GQ));   // [NW][MR][16]
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = uniform(tid >> 6);
@@ -269,14 +327,12 @@ __global__ __launch_bounds__(64 * NW) void gemv_int4b64_half_kernel(
             for (int w = 0; w < 4; ++w) araw[sl][w] = u4_t{0u, 0u, 0u, 0u};
         }
     }
-    f2_t pr[RPW];
+    Int4Pair<G> pr[RPW];
     u4_t wq[RPW];
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         const int b = b0 + min(2 * (wave + NW * i) + j, pb - 1);
-        pr[i] = __builtin_nontemporal_load(
-            reinterpret_cast<const f2_t *>(HP ? Sp + ((size_t)t * nblk + b) * 128 + h * 64 + c * 2
-                                              : Sp + ((size_t)t * nblk + b) * 64 + c * 2));
+        pr[i] = load_int4_pair<G>(Sp, (size_t)t * nblk + b, c, h);
     }
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
@@ -290,21 +346,8 @@ __global__ __launch_bounds__(64 * NW) void gemv_int4b64_half_kernel(
 #pragma unroll
     for (int sl = 0; sl < AS; ++sl) {
         const int idx = tid + 64 * NW * sl;
-        if (idx < MR * nhb) {
-            float se = 0.f, so = 0.f;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const u4_t v = araw[sl][w];
-                const h2_t p01 = as_h2(v.x), p23 = as_h2(v.y), p45 = as_h2(v.z), p67 = as_h2(v.w);
-                const h2_t e0 = {p01.x, p45.x}, e1 = {p23.x, p67.x};
-                const h2_t o0 = {p01.y, p45.y}, o1 = {p23.y, p67.y};
-                const h2_t one = {(_Float16)1.0f, (_Float16)1.0f};
-                se = dot2(e1, one, dot2(e0, one, se));
-                so = dot2(o1, one, dot2(o0, one, so));
-                ap[idx * 4 + w] = u4_t{as_u(e0), as_u(e1), as_u(o0), as_u(o1)};
-            }
-            hs[idx] = f2_t{se, so};            // idx = row * nhb + half-block
-        }
+        if (idx < MR * nhb)                  // idx = row * nhb + half-block
+            stage_int4_half<GQ>(araw[sl], ap + (size_t)idx * 4, hs + (size_t)idx * GQ);
     }
     __syncthreads();
 
@@ -315,25 +358,13 @@ __global__ __launch_bounds__(64 * NW) void gemv_int4b64_half_kernel(
         const int bl = 2 * (wave + NW * i) + j;
         if (2 * (wave + NW * i) >= pb) break;     // wave-uniform
         const int hbg = 2 * min(bl, pb - 1) + h;
-        const float off = pr[i].x, sc = pr[i].y;
-        const float ce = fmaf(-1024.0f, sc, off);
-        const float co = fmaf(-64.0f, sc, off);
+        const unsigned word[4] = {wq[i][0], wq[i][1], wq[i][2], wq[i][3]};
 #pragma unroll
         for (int r = 0; r < MR; ++r) {
-            float Te = 0.f, To = 0.f;
+            u4_t av[4];
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const u4_t av = ap[((size_t)r * nhb + hbg) * 4 + d];
-                const unsigned word = wq[i][d];
-                const unsigned y0 = __builtin_amdgcn_perm(magic, word, 0x04020400u);
-                const unsigned y1 = __builtin_amdgcn_perm(magic, word, 0x04030401u);
-                Te = dot2(as_h2(y0 & 0xFF0FFF0Fu), as_h2(av.x), Te);
-                Te = dot2(as_h2(y1 & 0xFF0FFF0Fu), as_h2(av.y), Te);
-                To = dot2(as_h2(y0 & 0xFFF0FFF0u), as_h2(av.z), To);
-                To = dot2(as_h2(y1 & 0xFFF0FFF0u), as_h2(av.w), To);
-            }
-            const f2_t sv = hs[(size_t)r * nhb + hbg];
-            const float v = fmaf(ce, sv.x, fmaf(co, sv.y, fmaf(sc, Te, sc * 0.0625f * To)));
+            for (int d = 0; d < 4; ++d) av[d] = ap[((size_t)r * nhb + hbg) * 4 + d];
+            const float v = int4_half_dot<G>(av, word, hs + ((size_t)r * nhb + hbg) * GQ, pr[i], magic);
             acc[r] += bl < pb ? v : 0.f;
         }
     }
@@ -376,13 +407,14 @@ __global__ __launch_bounds__(64 * NW) void gemv_int4b64_half_kernel(
 // loads exact. Per channel, sum(a * w) = offset * sum(a) + scale * sum(a * q);
 // sum(a) is formed once per workgroup.
 //
-// Blocked Int8 (PM = 1: a pair per 64-block; PM = 2: per 32-element half,
-// K % 64 == 0): the same regrouping per 16-code slice, whose codes all lie in
-// one block: the slice adds scale * sum(a * (1024 + q)) + (offset - 1024 scale)
-// * sum(a) with its block's pair, sum(a) over the slice's 16 activations
-// coming from per-piece sums staged in LDS with the activations. Each lane
-// requests its slices' pairs (8 bytes, shared by the 4 or 2 lanes of a block)
-// with its codes.
+// Blocked Int8 (PM = 1: a pair per 64-block; PM = 2: per 32-element half;
+// PM = 4: per 16-element quarter; K % 64 == 0): the same regrouping per
+// 16-code slice, whose codes all lie in one block: the slice adds
+// scale * sum(a * (1024 + q)) + (offset - 1024 scale) * sum(a) with its
+// block's pair, sum(a) over the slice's 16 activations coming from per-piece
+// sums staged in LDS with the activations. Each lane requests its slices'
+// pairs (8 bytes, shared by the 4, 2 or 1 lanes of a pair entry) with its
+// codes.
 constexpr int I8_WAVES = 16;
 
 template <int MR, int NCH, int PM>
@@ -411,7 +443,7 @@ __global__ __launch_bounds__(64 * I8_WAVES) void gemv_int8b0_kernel(
             reinterpret_cast<const u4_t *>(Wp + (size_t)nc * Kp + (size_t)ci * 16));
     }
     // slice ci's pair: entry ci >> SH of the channel's nchunk >> SH entries
-    constexpr int SH = PM == 2 ? 1 : 2;
+    constexpr int SH = PM == 4 ? 0 : PM == 2 ? 1 : 2;
     f2_t pb[PM ? NCH : 1];
     if constexpr (PM != 0) {
 #pragma unroll
@@ -604,13 +636,13 @@ static int rows_per_pass(int M, int K, int kp_bytes_per_row) {
     return mr;
 }
 
-template <int MR, bool HP>
+template <int MR, int G>
 static hipError_t gemv_int4_tile(int M, int K, int N, const void *A, const void *Wp,
                                  const void *Sp, void *C, const Epilogue &epi, int nsplit,
                                  hipStream_t s) {
     const int per = div_up(K / 64, nsplit);                // most blocks of a slice
     const int pmax = std::min(per, TILE_PASS);
-    const size_t lds = (size_t)MR * pmax * 128 + (size_t)MR * pmax * 16 +
+    const size_t lds = (size_t)MR * pmax * (128 + 16 * (G == 4 ? 2 : 1)) +
                        (size_t)TILE_WAVES * MR * 32 * sizeof(float);
     dim3 grid(div_up(N, 32), div_up(M, MR), nsplit);
     auto go = [&](auto kernel) {
@@ -619,38 +651,39 @@ static hipError_t gemv_int4_tile(int M, int K, int N, const void *A, const void 
                            static_cast<const float *>(Sp), C, epi);
     };
     if (nsplit > 1) {
-        if (per <= TILE_PASS) go(gemv_int4b64_tile_kernel<MR, true, HP, true>);
-        else go(gemv_int4b64_tile_kernel<MR, false, HP, true>);
+        if (per <= TILE_PASS) go(gemv_int4b64_tile_kernel<MR, true, G, true>);
+        else go(gemv_int4b64_tile_kernel<MR, false, G, true>);
     } else {
-        if (per <= TILE_PASS) go(gemv_int4b64_tile_kernel<MR, true, HP, false>);
-        else go(gemv_int4b64_tile_kernel<MR, false, HP, false>);
+        if (per <= TILE_PASS) go(gemv_int4b64_tile_kernel<MR, true, G, false>);
+        else go(gemv_int4b64_tile_kernel<MR, false, G, false>);
     }
     return hipGetLastError();
 }
 
 template <int MR>
 static hipError_t gemv_int4_tile(int M, int K, int N, const void *A, const void *Wp,
-                                 const void *Sp, void *C, const Epilogue &epi, int hp, int nsplit,
-                                 hipStream_t s) {
-    return hp ? gemv_int4_tile<MR, true>(M, K, N, A, Wp, Sp, C, epi, nsplit, s)
-              : gemv_int4_tile<MR, false>(M, K, N, A, Wp, Sp, C, epi, nsplit, s);
+                                 const void *Sp, void *C, const Epilogue &epi, int pair_g,
+                                 int nsplit, hipStream_t s) {
+    return pair_g == 4 ? gemv_int4_tile<MR, 4>(M, K, N, A, Wp, Sp, C, epi, nsplit, s)
+         : pair_g == 2 ? gemv_int4_tile<MR, 2>(M, K, N, A, Wp, Sp, C, epi, nsplit, s)
+                       : gemv_int4_tile<MR, 1>(M, K, N, A, Wp, Sp, C, epi, nsplit, s);
 }
 
 static hipError_t gemv_int4_rows(int M, int K, int N, const void *A, const void *Wp,
-                                 const void *Sp, void *C, const Epilogue &epi, int half_pairs,
+                                 const void *Sp, void *C, const Epilogue &epi, int pair_g,
                                  int nsplit, hipStream_t s);
 
 hipError_t launch_gemv_int4b64(int M, int K, int N, const void *A, const void *Wp,
-                               const void *Sp, void *C, const Epilogue &epi, int half_pairs,
+                               const void *Sp, void *C, const Epilogue &epi, int pair_g,
                                int nsplit, float *part, hipStream_t s) {
-    if (nsplit <= 1) return gemv_int4_rows(M, K, N, A, Wp, Sp, C, epi, half_pairs, 1, s);
-    const hipError_t e = gemv_int4_rows(M, K, N, A, Wp, Sp, part, epi, half_pairs, nsplit, s);
+    if (nsplit <= 1) return gemv_int4_rows(M, K, N, A, Wp, Sp, C, epi, pair_g, 1, s);
+    const hipError_t e = gemv_int4_rows(M, K, N, A, Wp, Sp, part, epi, pair_g, nsplit, s);
     if (e != hipSuccess) return e;
     return launch_splitk_reduce_f32(part, nsplit, M, N, C, epi, s);
 }
 
 static hipError_t gemv_int4_rows(int M, int K, int N, const void *A, const void *Wp,
-                                 const void *Sp, void *C, const Epilogue &epi, int half_pairs,
+                                 const void *Sp, void *C, const Epilogue &epi, int pair_g,
                                  int nsplit, hipStream_t s) {
     if (nsplit <= 1) {
         // one pass over the rows: half tiles
@@ -659,7 +692,7 @@ static hipError_t gemv_int4_rows(int M, int K, int N, const void *A, const void 
             const bool one = K <= 64 * TILE_PASS;
             const long long groups = (long long)div_up(N, 16) * div_up(M, MR);
             const int nw = !one && groups <= kSplitTargetCUs ? HALF_WAVES_WIDE : HALF_WAVES;
-            const size_t lds = (size_t)MR * std::min(K / 64, TILE_PASS) * 144 +
+            const size_t lds = (size_t)MR * std::min(K / 64, TILE_PASS) * (128 + 16 * (pair_g == 4 ? 2 : 1)) +
                                (size_t)nw * MR * 16 * sizeof(float);
             auto go = [&](auto kernel) {
                 hipLaunchKernelGGL(kernel, dim3(div_up(N, 16), div_up(M, MR)), dim3(64 * nw),
@@ -668,12 +701,16 @@ static hipError_t gemv_int4_rows(int M, int K, int N, const void *A, const void 
                                    C, epi);
             };
             constexpr int W8 = HALF_WAVES, W16 = HALF_WAVES_WIDE;
-            if (one) half_pairs ? go(gemv_int4b64_half_kernel<MR, true, true, W8>)
-                                : go(gemv_int4b64_half_kernel<MR, true, false, W8>);
-            else if (nw == W16) half_pairs ? go(gemv_int4b64_half_kernel<MR, false, true, W16>)
-                                           : go(gemv_int4b64_half_kernel<MR, false, false, W16>);
-            else half_pairs ? go(gemv_int4b64_half_kernel<MR, false, true, W8>)
-                            : go(gemv_int4b64_half_kernel<MR, false, false, W8>);
+            auto pick = [&](auto one_pass, auto waves) {
+                constexpr bool OP = decltype(one_pass)::value;
+                constexpr int NWV = decltype(waves)::value;
+                if (pair_g == 4) go(gemv_int4b64_half_kernel<MR, OP, 4, NWV>);
+                else if (pair_g == 2) go(gemv_int4b64_half_kernel<MR, OP, 2, NWV>);
+                else go(gemv_int4b64_half_kernel<MR, OP, 1, NWV>);
+            };
+            if (one) pick(std::true_type{}, std::integral_constant<int, W8>{});
+            else if (nw == W16) pick(std::false_type{}, std::integral_constant<int, W16>{});
+            else pick(std::false_type{}, std::integral_constant<int, W8>{});
             return hipGetLastError();
         };
         switch (M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8) {
@@ -685,10 +722,10 @@ static hipError_t gemv_int4_rows(int M, int K, int N, const void *A, const void 
     }
     // all rows in one pass (at most 88 KiB of LDS for eight), so the weights stream once
     switch (M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8) {
-    case 8: return gemv_int4_tile<8>(M, K, N, A, Wp, Sp, C, epi, half_pairs, nsplit, s);
-    case 4: return gemv_int4_tile<4>(M, K, N, A, Wp, Sp, C, epi, half_pairs, nsplit, s);
-    case 2: return gemv_int4_tile<2>(M, K, N, A, Wp, Sp, C, epi, half_pairs, nsplit, s);
-    default: return gemv_int4_tile<1>(M, K, N, A, Wp, Sp, C, epi, half_pairs, nsplit, s);
+    case 8: return gemv_int4_tile<8>(M, K, N, A, Wp, Sp, C, epi, pair_g, nsplit, s);
+    case 4: return gemv_int4_tile<4>(M, K, N, A, Wp, Sp, C, epi, pair_g, nsplit, s);
+    case 2: return gemv_int4_tile<2>(M, K, N, A, Wp, Sp, C, epi, pair_g, nsplit, s);
+    default: return gemv_int4_tile<1>(M, K, N, A, Wp, Sp, C, epi, pair_g, nsplit, s);
     }
 }
 
@@ -736,10 +773,11 @@ hipError_t launch_gemv_int8b0(int M, int K, int N, const void *A, const void *Wp
 }
 
 hipError_t launch_gemv_int8blk(int M, int K, int N, const void *A, const void *Wp,
-                               const void *Sp, void *C, const Epilogue &epi, int half_pairs,
+                               const void *Sp, void *C, const Epilogue &epi, int pair_g,
                                hipStream_t s) {
-    return half_pairs ? gemv_int8_rows<2>(M, K, N, A, Wp, Sp, C, epi, s)
-                      : gemv_int8_rows<1>(M, K, N, A, Wp, Sp, C, epi, s);
+    return pair_g == 4 ? gemv_int8_rows<4>(M, K, N, A, Wp, Sp, C, epi, s)
+         : pair_g == 2 ? gemv_int8_rows<2>(M, K, N, A, Wp, Sp, C, epi, s)
+                       : gemv_int8_rows<1>(M, K, N, A, Wp, Sp, C, epi, s);
 }
 
 template <int MR, int NCH>

@@ -35,29 +35,30 @@ qgemm_status geometry(int K, int N, qgemm_format f, Geometry *g) {
     r.K = K;
     r.N = N;
     if (is_int4_blocked(f)) {
-        // Int4 with one pair per b K-elements, packed as Int4-Block64 with
-        // each pair repeated in the 64-blocks it covers
-        // (blocks of 32: a pair per half of each 64-block, 512-byte pair records)
+        // Int4 with one pair per b K-elements (b a multiple of 16), packed as
+        // Int4-Block64 with each pair repeated in the 64-blocks it covers;
+        // pair records hold pair_groups(b) entries per channel and 64-block
+        // (256, 512 or 1024 bytes)
         const int b = f - QGEMM_INT4_BLOCK_BASE;
-        if (b != 32 && b % 64 != 0) return QGEMM_ERR_FORMAT;
+        if (b % 16 != 0) return QGEMM_ERR_FORMAT;
         if (K == 0 || K % b != 0 || K % 64 != 0) return QGEMM_ERR_SHAPE;
         r.Kp = K; r.Np = (int)round_up(N, 32); r.nblk = K / b; r.block = b;
         r.w_bytes = round_up((size_t)(r.Np / 32) * (K / 64) * 1024, kPackAlign);
-        r.s_bytes = round_up((size_t)(r.Np / 32) * (K / 64) * (b == 32 ? 512 : 256), kPackAlign);
+        r.s_bytes = round_up((size_t)(r.Np / 32) * (K / 64) * 256 * pair_groups(b), kPackAlign);
         *g = r;
         return QGEMM_OK;
     }
     if (is_int8_blocked(f)) {
-        // Int8 with one pair per b K-elements: channel rows of codes [Np][K]
-        // (as Int8-Block0) and the pairs channel-major with one entry per
-        // 64-block, repeated over the 64-blocks of a block (blocks of 32: one
-        // per 32-element half)
+        // Int8 with one pair per b K-elements (b a multiple of 16): channel
+        // rows of codes [Np][K] (as Int8-Block0) and the pairs channel-major
+        // with pair_groups(b) entries per 64-block (one per 64-block, 32-half
+        // or 16-quarter), repeated over the entries a block covers
         const int b = f - QGEMM_INT8_BLOCK_BASE;
-        if (b != 32 && b % 64 != 0) return QGEMM_ERR_FORMAT;
+        if (b % 16 != 0) return QGEMM_ERR_FORMAT;
         if (K == 0 || K % b != 0 || K % 64 != 0) return QGEMM_ERR_SHAPE;
         r.Kp = K; r.Np = (int)round_up(N, 4); r.nblk = K / b; r.block = b;
         r.w_bytes = round_up((size_t)r.Np * K, kPackAlign);
-        r.s_bytes = round_up((size_t)r.Np * (K / 64) * (b == 32 ? 2 : 1) * 2 * sizeof(float),
+        r.s_bytes = round_up((size_t)r.Np * (K / 64) * pair_groups(b) * 2 * sizeof(float),
                              kPackAlign);
         *g = r;
         return QGEMM_OK;
@@ -364,19 +365,19 @@ qgemm_status qgemm_pack_weights(int K, int N, qgemm_format f, const void *w_cano
     case QGEMM_INT4_B0: {
         const int nblk = K / 64;
         const size_t row = (size_t)K / 2;
+        const int G = pair_groups(g.block);
         for (int n = 0; n < N; ++n) {
             const int t = n >> 5, c = n & 31;
             for (int b = 0; b < nblk; ++b) {
                 const size_t rec = (size_t)t * nblk + b;
-                for (int half = 0; half < 2; ++half) {
+                for (int half = 0; half < 2; ++half)
                     std::memcpy(wp + rec * 1024 + (size_t)(32 * half + c) * 16,
                                 wc + (size_t)n * row + (size_t)b * 32 + half * 16, 16);
-                    // the pair of the block holding this half (one per 64-block
-                    // for Block64, the channel's one pair for Block0); records
-                    // of 32-element blocks hold one per half
-                    if (g.block != 32 && half == 1) break;
-                    const size_t pi = ((size_t)n * g.nblk + ((size_t)b * 64 + half * 32) / g.block) * 2;
-                    const size_t so = g.block == 32 ? rec * 128 + (32 * half + c) * 2 : rec * 64 + c * 2;
+                // entry sub of the record: the pair of the block holding
+                // K-elements 64 b + sub * 64 / G (Block0: the channel's one pair)
+                for (int sub = 0; sub < G; ++sub) {
+                    const size_t pi = ((size_t)n * g.nblk + ((size_t)b * 64 + sub * (64 / G)) / g.block) * 2;
+                    const size_t so = int4_pair_entry(rec, c, sub, G);
                     spf[so + 0] = pairs_canonical[pi + 0];
                     spf[so + 1] = pairs_canonical[pi + 1];
                 }
@@ -392,14 +393,14 @@ qgemm_status qgemm_pack_weights(int K, int N, qgemm_format f, const void *w_cano
         }
         break;
     case QGEMM_INT8_BLOCK_BASE: {
-        // entry (n, 64-block b, half h) = pair of the block holding
-        // k = 64 b + 32 h
-        const int H = g.block == 32 ? 2 : 1, nb = K / 64;
+        // entry (n, 64-block b, sub-block h) = pair of the block holding
+        // k = 64 b + h * 64 / H
+        const int H = pair_groups(g.block), nb = K / 64;
         for (int n = 0; n < N; ++n) {
             std::memcpy(wp + (size_t)n * K, wc + (size_t)n * K, (size_t)K);
             for (int b = 0; b < nb; ++b)
                 for (int h = 0; h < H; ++h) {
-                    const size_t pi = ((size_t)n * g.nblk + ((size_t)b * 64 + h * 32) / g.block) * 2;
+                    const size_t pi = ((size_t)n * g.nblk + ((size_t)b * 64 + h * (64 / H)) / g.block) * 2;
                     const size_t so = (((size_t)n * nb + b) * H + h) * 2;
                     spf[so + 0] = pairs_canonical[pi + 0];
                     spf[so + 1] = pairs_canonical[pi + 1];
@@ -468,18 +469,19 @@ qgemm_status qgemm_unpack_weights(int K, int N, qgemm_format f, const void *w_pa
     case QGEMM_INT4_B64:
     case QGEMM_INT4_B0: {
         const int nblk = K / 64;
+        const int G = pair_groups(g.block);
         const size_t row = (size_t)K / 2;
         for (int n = 0; n < N; ++n) {
             const int t = n >> 5, c = n & 31;
             for (int b = 0; b < nblk; ++b) {
                 const size_t rec = (size_t)t * nblk + b;
-                for (int half = 0; half < 2; ++half) {
+                for (int half = 0; half < 2; ++half)
                     std::memcpy(wc + (size_t)n * row + (size_t)b * 32 + half * 16,
                                 wp + rec * 1024 + (size_t)(32 * half + c) * 16, 16);
-                    if (g.block != 32 && half == 1) break;
-                    // every 64-block of a block holds its pair
-                    const size_t pi = ((size_t)n * g.nblk + ((size_t)b * 64 + half * 32) / g.block) * 2;
-                    const size_t so = g.block == 32 ? rec * 128 + (32 * half + c) * 2 : rec * 64 + c * 2;
+                // every entry a block covers holds its pair
+                for (int sub = 0; sub < G; ++sub) {
+                    const size_t pi = ((size_t)n * g.nblk + ((size_t)b * 64 + sub * (64 / G)) / g.block) * 2;
+                    const size_t so = int4_pair_entry(rec, c, sub, G);
                     pairs_canonical[pi + 0] = spf[so + 0];
                     pairs_canonical[pi + 1] = spf[so + 1];
                 }
@@ -496,12 +498,12 @@ qgemm_status qgemm_unpack_weights(int K, int N, qgemm_format f, const void *w_pa
         break;
     case QGEMM_INT8_BLOCK_BASE: {
         // each block's pair from the first entry it covers
-        const int H = g.block == 32 ? 2 : 1, nb = K / 64;
+        const int H = pair_groups(g.block), nb = K / 64;
         for (int n = 0; n < N; ++n) {
             std::memcpy(wc + (size_t)n * K, wp + (size_t)n * K, (size_t)K);
             for (int j = 0; j < g.nblk; ++j) {
                 const size_t k = (size_t)j * g.block;
-                const size_t so = (((size_t)n * nb + k / 64) * H + (k % 64) / 32) * 2;
+                const size_t so = (((size_t)n * nb + k / 64) * H + (k % 64) / (64 / H)) * 2;
                 pairs_canonical[((size_t)n * g.nblk + j) * 2 + 0] = spf[so + 0];
                 pairs_canonical[((size_t)n * g.nblk + j) * 2 + 1] = spf[so + 1];
             }

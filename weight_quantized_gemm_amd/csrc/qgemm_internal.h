@@ -31,10 +31,13 @@ constexpr size_t kPackAlign = 256;
 //            a contiguous 64-byte run.
 //   pairs:   256-byte records, record (t, b) at (t * nblk + b) * 256 holding
 //            {offset, scale} of channels 32 t .. 32 t + 31 for block b.
-//            Int4 with 32-element blocks (a pair per half of each 64-block):
-//            512-byte records, entry (h, c) of record (t, b) at
-//            (t * nblk + b) * 512 + (32 h + c) * 8 for K-elements 64 b + 32 h
-//            .. + 31 of channel 32 t + c.
+//            Int4 with blocks that are odd multiples of 32 (a pair per half
+//            of each 64-block): 512-byte records, entry (h, c) of record
+//            (t, b) at (t * nblk + b) * 512 + (32 h + c) * 8 for K-elements
+//            64 b + 32 h .. + 31 of channel 32 t + c. Other multiples of 16
+//            (a pair per quarter): 1024-byte records, entry (c, j) at
+//            (t * nblk + b) * 1024 + (4 c + j) * 8 for K-elements 64 b + 16 j
+//            .. + 15 (int4_pair_entry).
 // INT8_B0, Kp = roundup(K, 64), Np = roundup(N, 4):
 //   weights: [Np][Kp] bytes (canonical rows, zero padded);
 //   pairs:   [Np][2] floats.
@@ -61,6 +64,21 @@ struct Geometry {
 };
 
 qgemm_status geometry(int K, int N, qgemm_format f, Geometry *g);
+
+// Pair entries per 64-element K step in the packed pair layouts of the
+// blocked formats: one per 64-block when 64 divides the block size, one per
+// 32-element half when 32 does, else one per 16-element quarter (block sizes
+// that are multiples of 16). Every entry holds the pair of the block that
+// contains its K-elements.
+inline int pair_groups(int block) { return block % 64 == 0 ? 1 : block % 32 == 0 ? 2 : 4; }
+
+// Float offset of entry (channel c of the 32-channel tile, sub-block sub) of
+// pair record rec in an Int4 packed pair buffer: records of 256 G bytes;
+// entry c (G = 1), 32 sub + c (G = 2), or 4 c + sub (G = 4: the two quarters
+// of one 32-element half, which one lane decodes, are one 16-byte piece).
+__host__ __device__ inline size_t int4_pair_entry(size_t rec, int c, int sub, int G) {
+    return rec * 64 * (size_t)G + (size_t)(G == 4 ? 4 * c + sub : 32 * sub + c) * 2;
+}
 
 // Int4 with a block size given in the format id (QGEMM_INT4_BLOCK(b)); the
 // id carries b, which geometry() checks against K.
@@ -114,27 +132,28 @@ struct Epilogue {
 // arguments and return hipGetLastError() of their launches. C is float or
 // fp16 per the epilogue.
 // ---------------------------------------------------------------------------
-// half_pairs: the pairs are per 32-element half-block (Int4 blocks of 32).
+// pair_g: pair entries per 64-element block, pair_groups(block) (1; 2 per
+// 32-element half; 4 per 16-element quarter).
 // nsplit > 1: K split over nsplit workgroups per tile, partial tiles in
 // `part` ([nsplit][M][N] fp32) added by the fixed-order reduce.
 hipError_t launch_gemv_int4b64(int M, int K, int N, const void *A, const void *Wp,
-                               const void *Sp, void *C, const Epilogue &epi, int half_pairs,
+                               const void *Sp, void *C, const Epilogue &epi, int pair_g,
                                int nsplit, float *part, hipStream_t s);
 hipError_t launch_gemv_int8b0(int M, int K, int N, const void *A, const void *Wp,
                               const void *Sp, void *C, const Epilogue &epi, hipStream_t s);
-// Blocked Int8: channel rows [Np][K] of codes and pairs [Np][K/64][H] (H = 2
-// with half_pairs, blocks of 32; else 1), K % 64 == 0.
+// Blocked Int8: channel rows [Np][K] of codes and pairs [Np][K/64][pair_g],
+// K % 64 == 0.
 hipError_t launch_gemv_int8blk(int M, int K, int N, const void *A, const void *Wp,
-                               const void *Sp, void *C, const Epilogue &epi, int half_pairs,
+                               const void *Sp, void *C, const Epilogue &epi, int pair_g,
                                hipStream_t s);
 hipError_t launch_gemm_int8blk(int M, int K, int N, const void *A, const void *Wp,
-                               const void *Sp, void *C, const Epilogue &epi, int half_pairs,
+                               const void *Sp, void *C, const Epilogue &epi, int pair_g,
                                int nsplit, float *part, hipStream_t s);
 // Tiled kernels with split-K: nsplit > 1 writes partial tiles to `part`
 // ([nsplit][M][N] fp32) and adds them into C with a fixed-order reduce that
 // applies the epilogue.
 hipError_t launch_gemm_int4b64(int M, int K, int N, const void *A, const void *Wp,
-                               const void *Sp, void *C, const Epilogue &epi, int half_pairs,
+                               const void *Sp, void *C, const Epilogue &epi, int pair_g,
                                int nsplit, float *part, hipStream_t s);
 hipError_t launch_splitk_reduce_f32(const float *part, int nsplit, int M, int N, void *C,
                                     const Epilogue &epi, hipStream_t s);

@@ -367,17 +367,22 @@ __global__ __launch_bounds__(64 * kQWaves) void quantize_vec_kernel(QParams p) {
                 const int k0 = 256 * j + 4 * lane;
                 if (OUT == QGEMM_F32) {
                     if ((lane & (G - 1)) == 0 && k0 < p.K) pp[(size_t)n * p.nblk + k0 / (4 * G)] = pr;
-                } else if (OUT == QGEMM_INT8_BLOCK_BASE && G == 8) {
-                    // blocked Int8, blocks of 32: entry (channel, 64-block, half)
-                    if ((lane & 7) == 0 && k0 < p.K)
-                        pp[((size_t)n * p.nkc + (k0 >> 6)) * 2 + ((k0 >> 5) & 1)] = pr;
+                } else if (OUT == QGEMM_INT8_BLOCK_BASE && G > 0 && G <= 8) {
+                    // blocked Int8, blocks of 16 or 32: entry (channel, 64-block,
+                    // quarter or half)
+                    constexpr int H = G > 0 ? 16 / G : 1;          // entries per 64-block
+                    if ((lane & (G - 1)) == 0 && k0 < p.K)
+                        pp[((size_t)n * p.nkc + (k0 >> 6)) * H + ((k0 & 63) / (4 * G))] = pr;
                 } else if (OUT == QGEMM_INT8_BLOCK_BASE) {
                     // blocked Int8: the block's pair in each of its 64-block entries
                     if ((lane & 15) == 0 && k0 < p.K) pp[(size_t)n * p.nkc + (k0 >> 6)] = pr;
-                } else if (OUT == QGEMM_INT4_B64 && G == 8) {
-                    // blocks of 32: 512-byte pair records, entry (half, channel)
-                    if ((lane & 7) == 0 && k0 < p.K)
-                        pp[((size_t)(n >> 5) * p.nkc + (k0 >> 6)) * 64 + 32 * ((k0 >> 5) & 1) + (n & 31)] = pr;
+                } else if (OUT == QGEMM_INT4_B64 && G > 0 && G <= 8) {
+                    // blocks of 16 or 32: records of 1024 or 512 bytes, the
+                    // quarter's or half's entry of the channel
+                    constexpr int H = G > 0 ? 16 / G : 1;          // entries per 64-block
+                    if ((lane & (G - 1)) == 0 && k0 < p.K)
+                        pp[int4_pair_entry((size_t)(n >> 5) * p.nkc + (k0 >> 6), n & 31,
+                                           (k0 & 63) / (4 * G), H) / 2] = pr;
                 } else if (OUT == QGEMM_INT4_B64) {
                     // packed as Int4-Block64: the block's pair in each of its 64-block records
                     if ((lane & 15) == 0 && k0 < p.K) pp[((size_t)(n >> 5) * p.nkc + (k0 >> 6)) * 32 + (n & 31)] = pr;
@@ -469,6 +474,7 @@ template <int OUT, int BITS>
 hipError_t launch_vec(const QParams &p, int G, hipStream_t s) {
     const dim3 grid(div_up(p.rows, kQWaves)), block(64 * kQWaves);
     switch (G) {
+    case 4: hipLaunchKernelGGL((quantize_vec_kernel<OUT, BITS, 4>), grid, block, 0, s, p); break;
     case 8: hipLaunchKernelGGL((quantize_vec_kernel<OUT, BITS, 8>), grid, block, 0, s, p); break;
     case 16: hipLaunchKernelGGL((quantize_vec_kernel<OUT, BITS, 16>), grid, block, 0, s, p); break;
     case 32: hipLaunchKernelGGL((quantize_vec_kernel<OUT, BITS, 32>), grid, block, 0, s, p); break;
@@ -504,13 +510,15 @@ hipError_t launch_quantize(int K, int N, qgemm_format f, bool packed, const floa
     const bool i8blk = kernel_format(f) == QGEMM_INT8_BLOCK_BASE;
     if (packed && (f == QGEMM_INT8_B0 || i8blk)) {
         // the packed pair buffer is padded to its alignment past the last pair
-        p.tail_off = f == QGEMM_INT8_B0 ? g.Np * 2 : g.Np * p.nkc * (g.block == 32 ? 2 : 1) * 2;
+        p.tail_off = f == QGEMM_INT8_B0 ? g.Np * 2 : g.Np * p.nkc * pair_groups(g.block) * 2;
         p.tail_len = (int)(g.s_bytes / sizeof(float)) - p.tail_off;
     }
     if ((K & 3) == 0) {
-        // four weights per lane: blocks of 64, 128 or 256 as lane groups, or
-        // blocks of whole 256-element chunks (and all of K) over two passes
-        const int G = (g.block == 32 || g.block == 64 || g.block == 128 || g.block == 256) ? g.block / 4 : 0;
+        // four weights per lane: blocks of 16 to 256 elements (powers of two)
+        // as lane groups, or blocks of whole 256-element chunks (and all of K)
+        // over two passes
+        const int G = (g.block == 16 || g.block == 32 || g.block == 64 || g.block == 128 ||
+                       g.block == 256) ? g.block / 4 : 0;
         if (G > 0 || g.block % 256 == 0 || g.block == K) {
             if (!packed) {
                 if (f == QGEMM_INT8_B0 || i8blk) return launch_vec<QGEMM_F32, 8>(p, G, s);
@@ -522,7 +530,7 @@ hipError_t launch_quantize(int K, int N, qgemm_format f, bool packed, const floa
             return launch_vec<QGEMM_INT4_B64, 4>(p, G, s);
         }
     }
-    if (g.block == 32) return hipErrorInvalidValue;   // K % 64 == 0 always takes the lanes of four
+    if (g.block % 64 != 0 && g.block != K) return hipErrorInvalidValue;   // blocks of 16, 32: lanes of four
     const bool b64 = g.block == 64;
     if (!packed) {
         if (f == QGEMM_INT8_B0 || i8blk) return launch<QGEMM_F32, 8, false, false>(p, s);
