@@ -25,12 +25,15 @@
 //    per workgroup and no operand is shared between waves: the main loop has
 //    no barrier, and each SIMD's matrix pipe is fed by its own wave, whose
 //    dequantising instructions issue while its matrix instructions run;
-//  - a wave's A block (BM rows x 64 K-elements) arrives through buffer loads
-//    with a scalar per-block offset, fully coalesced (8 rows x 128 bytes per
-//    instruction), one (BM = 128) or two (BM = 64) blocks ahead through a
-//    register ring, and passes through the wave's own two LDS tiles into the
-//    MFMA lane layout (one wave's LDS operations execute in order, so a tile
-//    is rewritten only after its last read);
+//  - a wave's A block (BM rows x 64 K-elements) goes from memory straight
+//    into one of the wave's own LDS tiles by DMA (buffer loads with the LDS
+//    as destination: no registers and no LDS write instructions, which
+//    measured about 6 % of the kernel), fully coalesced (8 rows x 128 bytes
+//    per instruction), one (BM = 128, two tiles) or three (BM = 64, four
+//    tiles) blocks ahead; rows are stored XOR-swizzled so that the MFMA
+//    reads of 32 rows at one K offset hit distinct banks. The compiler does
+//    not order the DMA's LDS writes against later reads, so the wave waits
+//    for them explicitly before it reads a tile;
 //  - a K-block of a 32-channel B tile is one contiguous 1 KiB record already
 //    in operand lane order (see the packed layout), fetched four blocks ahead
 //    through a register ring and dequantised in registers (one fp32
@@ -60,8 +63,6 @@ namespace qg {
 namespace {
 constexpr int BK = 64;
 constexpr int NWAVE = 4;               // one K quarter per wave
-constexpr int AS_STRIDE = BK + 8;      // halves per LDS row of an A tile (144 bytes)
-constexpr int A_TILES = 2;             // LDS A tiles per wave
 constexpr int P_RING = 2;              // pair ring (loads two blocks ahead)
 constexpr int UNROLL = 4;              // lcm of the rings: every slot a fixed register
 
@@ -71,20 +72,24 @@ struct TileCfg {
     static constexpr int BM = BM_, BN = BN_;
     static constexpr int RF = BM / 32;                  // 32-row accumulator tiles per wave
     static constexpr int CF = BN / 32;                  // 32-column accumulator tiles per wave
-    static constexpr int A_SETS = BM == 64 ? 2 : 1;     // A register sets (blocks loaded ahead)
-    // B code ring: loads four blocks ahead, two with four column tiles (the
-    // register file would not hold four blocks of 128 codes per lane)
-    static constexpr int B_RING = CF >= 4 ? 2 : 4;
+    // LDS A tiles per wave (a ring: the DMA runs A_TILES - 1 blocks ahead)
+    static constexpr int A_TILES = BM == 64 ? 4 : 2;
+    // B code ring: loads four blocks ahead
+    static constexpr int B_RING = 4;
     static constexpr int A_PIECES = BM * BK / 8 / 64;   // 16-byte A pieces per lane and block
     static constexpr int RED_STRIDE = BN + 4;           // floats per LDS row of the reduction
-    static constexpr size_t AS_BYTES = (size_t)BM * AS_STRIDE * 2;          // one A tile
+    static constexpr size_t AS_BYTES = (size_t)BM * BK * 2;                 // one A tile
     static constexpr size_t A_LDS = (size_t)NWAVE * A_TILES * AS_BYTES;     // all waves
     // the four partial tiles meet in LDS RCH rows at a time (all BM rows when
     // they fit next to nothing else, else 64-row chunks)
     static constexpr int RCH = (size_t)NWAVE * BM * RED_STRIDE * 4 <= 160 * 1024 ? BM : 64;
     static constexpr size_t RED_BYTES = (size_t)NWAVE * RCH * RED_STRIDE * 4;
     static constexpr size_t LDS_BYTES = RED_BYTES > A_LDS ? RED_BYTES : A_LDS;
-    static_assert(UNROLL % A_SETS == 0 && UNROLL % A_TILES == 0 && UNROLL % B_RING == 0, "ring sizes");
+    // loads issued after the DMA of the block a wave reads next, by the time
+    // it reads it (see the main loop)
+    static constexpr int A_WAIT = CF + (A_TILES - 2) * (2 * CF + A_PIECES);
+    static_assert(UNROLL % A_TILES == 0 && UNROLL % B_RING == 0, "ring sizes");
+    static_assert(A_WAIT <= 63, "vmcnt range");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 workgroup");
 };
 
@@ -116,6 +121,19 @@ __device__ __forceinline__ f2_t buf_load8(__amdgpu_buffer_rsrc_t r, unsigned vof
     return __builtin_bit_cast(f2_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
 }
 constexpr int kNonTemporal = 2;   // cache policy of a streamed load (read once per workgroup)
+
+// 16 bytes per lane from a buffer straight into LDS, lane l's at lds + 16 l
+// (no registers, no LDS write instruction).
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void *lds, unsigned voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
+                                             (int)voff, 0, 0, 0);
+#endif
+}
+
+// s_waitcnt operand that waits until at most n vector memory loads are
+// outstanding and nothing else (vmcnt split over bits 3:0 and 15:14).
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 }
 
 // 8 Int4 codes (one word, k ascending, low nibble first) -> 8 fp16 weights
@@ -159,7 +177,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ Sp, void *__restrict__ C, Epilogue epi) {
     constexpr int BM = T::BM, BN = T::BN, RF = T::RF, CF = T::CF;
-    constexpr int A_SETS = T::A_SETS, A_PIECES = T::A_PIECES, RED_STRIDE = T::RED_STRIDE;
+    constexpr int A_TILES = T::A_TILES, A_PIECES = T::A_PIECES, RED_STRIDE = T::RED_STRIDE;
     constexpr int B_RING = T::B_RING;
     constexpr size_t AS_BYTES = T::AS_BYTES;
     __shared__ __align__(16) unsigned char lds[T::LDS_BYTES];
@@ -203,20 +221,22 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     const int nsteps = (nb + UNROLL - 1) / UNROLL * UNROLL;
     const int ntiles_b = (N + 31) / 32;            // packed 32-channel tiles
 
-    _Float16 *const a_lds = reinterpret_cast<_Float16 *>(lds + (size_t)kq * A_TILES * AS_BYTES);
-    auto a_tile = [&](int slot) { return a_lds + (size_t)slot * (AS_BYTES / 2); };
+    unsigned char *const a_lds = lds + (size_t)kq * A_TILES * AS_BYTES;
+    auto a_tile = [&](int slot) { return a_lds + (size_t)slot * AS_BYTES; };
 
-    // A loader role: piece i of a block is row 8 i + lane / 8, elements
-    // 8 (lane % 8) .. +7 (128 bytes per row, 8 rows per instruction); byte
-    // offsets from the tile's first row (rows past M are clamped: loaded,
-    // never stored) and, per block, a scalar advance of 128 bytes.
+    // A by LDS DMA: a tile is BM rows of 128 bytes (one block), 16-byte slot
+    // j of row rho holding the row's piece j ^ (rho % 8), so that the MFMA
+    // reads (32 rows at one piece) fall in distinct banks. DMA instruction i
+    // fills rows 8 i .. 8 i + 7: lane l's 16 bytes land in row 8 i + l / 8,
+    // slot l % 8, so it fetches piece (l % 8) ^ (l / 8) of that row (rows
+    // past M are clamped: loaded, never stored). Per block the buffer's base
+    // advances by 128 bytes.
     const int arow = lane >> 3, apc = lane & 7;
     const int arows = min(BM, M - m0);
-    const __amdgpu_buffer_rsrc_t a_rs = byte_rsrc(A + (size_t)m0 * K, (unsigned)arows * K * 2u);
     unsigned a_off[A_PIECES];
 #pragma unroll
     for (int i = 0; i < A_PIECES; ++i)
-        a_off[i] = (unsigned)(min(8 * i + arow, arows - 1) * K + 8 * apc) * 2u;
+        a_off[i] = (unsigned)(min(8 * i + arow, arows - 1) * K + 8 * (apc ^ arow)) * 2u;
     // B: records of each accumulator column tile (tiles past N: loaded, never
     // stored), one 1 KiB record and one pair record per block
     constexpr unsigned PREC = 256u * G;           // bytes per pair record
@@ -233,19 +253,17 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     const unsigned p_off = G == 4 ? (unsigned)(4 * r + 2 * h) * 8u
                          : G == 2 ? (unsigned)(32 * h + r) * 8u : (unsigned)r * 8u;
 
-    auto load_a = [&](u4_t (&dst)[A_PIECES], int kt) {
+    auto dma_a = [&](unsigned char *As, int kt) {
+        const __amdgpu_buffer_rsrc_t rs = byte_rsrc(A + (size_t)m0 * K + (size_t)kt * BK,
+                                                    (unsigned)arows * K * 2u - (unsigned)kt * (BK * 2));
 #pragma unroll
-        for (int i = 0; i < A_PIECES; ++i) dst[i] = buf_load16(a_rs, a_off[i], (unsigned)kt * (BK * 2));
+        for (int i = 0; i < A_PIECES; ++i) lds_dma16(rs, As + i * 1024, a_off[i]);
     };
-    auto store_a = [&](_Float16 *As, const u4_t (&src)[A_PIECES]) {
-#pragma unroll
-        for (int i = 0; i < A_PIECES; ++i)
-            *reinterpret_cast<u4_t *>(As + (8 * i + arow) * AS_STRIDE + 8 * apc) = src[i];
-    };
-    auto read_a = [&](const _Float16 *As, int s, h8_t (&af)[RF]) {
+    // MFMA step s: lane (r, h) takes piece 4 h + s of rows 32 rf + r
+    auto read_a = [&](const unsigned char *As, int s, h8_t (&af)[RF]) {
 #pragma unroll
         for (int rf = 0; rf < RF; ++rf)
-            af[rf] = *reinterpret_cast<const h8_t *>(As + (32 * rf + r) * AS_STRIDE + 32 * h + 8 * s);
+            af[rf] = *reinterpret_cast<const h8_t *>(As + (32 * rf + r) * 128 + 16 * ((4 * h + s) ^ (r & 7)));
     };
     auto load_b = [&](u4_t (&codes)[CF], int kt) {
 #pragma unroll
@@ -284,7 +302,6 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    u4_t an[A_SETS][A_PIECES];  // A register sets: set j % A_SETS holds block j
     u4_t bc[B_RING][CF];        // B code ring: slot j % B_RING holds block j
     PairT bp[P_RING][CF];       // pair ring: slot j % 2 holds block j
     DqParams prm[CF][GQ];
@@ -298,37 +315,42 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     // dequantisation constants instead (every weight +0), and adds exactly
     // zero.
     //
-    // prologue: A of blocks 0 .. A_SETS - 1 in flight, then the pairs of
-    // blocks 0 and 1 and the codes of blocks 0 .. 3; block 0's A into tile 0
-    // and its step-0 operands ready; A of block A_SETS in flight
-#pragma unroll
-    for (int d = 0; d < A_SETS; ++d) load_a(an[d], min(kb0 + d, last));
+    // prologue: the pairs of blocks 0 and 1, the codes of blocks
+    // 0 .. B_RING - 1 and the A of blocks 0 .. A_TILES - 2 (tiles 0 ..),
+    // all of it waited for; block 0's step-0 operands ready
     load_p(bp[0], kb0);
     load_p(bp[1], min(kb0 + 1, last));
 #pragma unroll
     for (int d = 0; d < B_RING; ++d) load_b(bc[d], min(kb0 + d, last));
-    store_a(a_tile(0), an[0]);
-    load_a(an[0], min(kb0 + A_SETS, last));
+#pragma unroll
+    for (int d = 0; d < A_TILES - 1; ++d) dma_a(a_tile(d), min(kb0 + d, last));
 #pragma unroll
     for (int cf = 0; cf < CF; ++cf) make_prm(bp[0][cf], nb > 0, prm[cf]);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vm_wait(0));
+    __builtin_amdgcn_sched_barrier(0);
     read_a(a_tile(0), 0, acur);
 #pragma unroll
     for (int cf = 0; cf < CF; ++cf) bcur[cf] = dequant8(bc[0][cf][0], prm[cf][0], m_lo, m_hi, magic);
 
-    // Block i reads A tile i % 2 and B slot i % 4; at its start, block i + 1's
-    // A (register set (i + 1) % A_SETS, loaded A_SETS blocks ago) goes into
-    // tile (i + 1) % 2, whose last reads (block i - 1) were issued before, and
-    // the set then takes block i + 1 + A_SETS.
+    // Block i reads A tile i % A_TILES and B slot i % B_RING. At its start
+    // the tile of block i - 1, whose reads were all consumed by block i - 1's
+    // matrix instructions, takes block i + A_TILES - 1 by DMA. Its step 3
+    // reads block i + 1's first operands: that tile's DMA was issued at the
+    // start of block i + 2 - A_TILES (or in the prologue, which waited for
+    // it), and since then each block issued its pair loads, its DMA and its
+    // code loads (CF + A_PIECES + CF), this block the pairs and the DMA
+    // before the codes: A_WAIT loads may still be outstanding, which the
+    // explicit wait below allows (the compiler does not track the DMA's
+    // writes to LDS).
     for (int base = 0; base < nsteps; base += UNROLL) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int i = base + u;
-            const int sa = (u + 1) % A_SETS;
-            store_a(a_tile((u + 1) % A_TILES), an[sa]);
-            load_a(an[sa], min(kb0 + i + 1 + A_SETS, last));
             // pair slot i % 2 was last read for block i's constants (end of
             // block i - 1): it takes block i + 2
             load_p(bp[u % P_RING], min(kb0 + i + P_RING, last));
+            dma_a(a_tile((u + A_TILES - 1) % A_TILES), min(kb0 + i + A_TILES - 1, last));
             // keep the loads here, ahead of the arithmetic: moved down next to
             // their use they would wait for memory instead of hiding it
             __builtin_amdgcn_sched_barrier(0);
@@ -347,6 +369,9 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
                     }
                 } else {
                     const int un = (u + 1) % B_RING;
+                    __builtin_amdgcn_sched_barrier(0);
+                    __builtin_amdgcn_s_waitcnt(vm_wait(T::A_WAIT));
+                    __builtin_amdgcn_sched_barrier(0);
                     read_a(a_tile((u + 1) % A_TILES), 0, anxt);
 #pragma unroll
                     for (int cf = 0; cf < CF; ++cf) {
@@ -398,6 +423,8 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     float *red = reinterpret_cast<float *>(lds) + (size_t)kq * RCH * RED_STRIDE;
     const size_t W = (size_t)RCH * RED_STRIDE;
     const bool vec_store = (N & 3) == 0 && gc + 4 <= N;
+    // the last DMAs (clamped blocks, never read) land before LDS is reused
+    __builtin_amdgcn_s_waitcnt(vm_wait(0));
 #pragma unroll
     for (int ch = 0; ch < BM / RCH; ++ch) {
         __syncthreads();   // the A tiles (first chunk) or the last chunk's sums are read
