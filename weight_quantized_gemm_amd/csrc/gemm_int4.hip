@@ -107,12 +107,6 @@ __device__ __forceinline__ DqParams dq_params(f2_t pair, bool keep) {
     return {sc, fmaf(-1024.0f, sc, off), sc * 0.0625f, fmaf(-64.0f, sc, off)};
 }
 
-// Buffer resource of a raw byte range (gfx9 format word: 32-bit data,
-// no swizzle); loads through it take a per-lane and a scalar byte offset, so
-// a per-block advance is one scalar add.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_rsrc(const void *base, unsigned bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
-}
 template <int AUX = 0>
 __device__ __forceinline__ u4_t buf_load16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
     return __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, AUX));
@@ -122,18 +116,6 @@ __device__ __forceinline__ f2_t buf_load8(__amdgpu_buffer_rsrc_t r, unsigned vof
 }
 constexpr int kNonTemporal = 2;   // cache policy of a streamed load (read once per workgroup)
 
-// 16 bytes per lane from a buffer straight into LDS, lane l's at lds + 16 l
-// (no registers, no LDS write instruction).
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void *lds, unsigned voff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
-                                             (int)voff, 0, 0, 0);
-#endif
-}
-
-// s_waitcnt operand that waits until at most n vector memory loads are
-// outstanding and nothing else (vmcnt split over bits 3:0 and 15:14).
-constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 }
 
 // 8 Int4 codes (one word, k ascending, low nibble first) -> 8 fp16 weights

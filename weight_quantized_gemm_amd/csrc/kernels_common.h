@@ -46,6 +46,28 @@ __device__ __forceinline__ int slice_begin(unsigned z, int n, unsigned Z) {
 // Wave-uniform value as a scalar (lets the compiler use scalar loads).
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Buffer resource of a raw byte range (gfx9 format word: 32-bit data,
+// no swizzle); loads through it take a per-lane and a scalar byte offset, so
+// a per-block advance is one scalar add.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_rsrc(const void *base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from a buffer straight into LDS, lane l's at lds + 16 l
+// (the gfx950 16-byte form of the LDS DMA: no registers, no LDS write
+// instruction). The compiler does not order these LDS writes against later
+// LDS reads: a reader waits for them with an explicit vm_wait.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void *lds, unsigned voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
+                                             (int)voff, 0, 0, 0);
+#endif
+}
+
+// s_waitcnt operand that waits until at most n vector memory loads are
+// outstanding and nothing else (vmcnt split over bits 3:0 and 15:14).
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+
 // ---------------------------------------------------------------------------
 // Fused epilogue (SimdPaddleOCR pull request: fp32 accumulators are never
 // narrowed before bias, residual and activation): for output (m, n) at

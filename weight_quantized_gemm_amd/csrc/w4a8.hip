@@ -397,7 +397,7 @@ __global__ __launch_bounds__(64 * WNW) void w4a8_gemm_kernel(
                 for (int i = 0; i < 8; ++i) {
                     const int rw = 8 * i + (lane >> 3), c4 = lane & 7;
                     const f4_t v = *reinterpret_cast<const f4_t *>(stg + rw * 36 + 4 * c4);
-                    *reinterpret_cast<f4_t *>(static_cast<float *>(C) + (size_t)(m0 + rb + rw) * N + c0 + 4 * c4) = v;
+                    __builtin_nontemporal_store(v, reinterpret_cast<f4_t *>(static_cast<float *>(C) + (size_t)(m0 + rb + rw) * N + c0 + 4 * c4));
                 }
             }
         return;
