@@ -12,8 +12,9 @@
 // 1 KiB of contiguous bytes (64 lanes x 16 bytes), all issued before the
 // arithmetic needs them.
 //
-// Codes become fp16 by a magic-number decode (one byte permute per pair of
-// codes): a 4-bit code placed in mantissa bits 4..7 under exponent 2^10 reads
+// Codes become fp16 by a magic-number decode (one v_and_or_b32 per pair of
+// 4-bit codes, a byte permute per pair of 8-bit codes): a 4-bit code placed
+// in mantissa bits 4..7 under exponent 2^10 reads
 // as 1024 + 16 q, in bits 0..3 as 1024 + q; an 8-bit code in bits 0..7 reads
 // as 1024 + q. The 1024 bias is removed per block with the block sums of the
 // activations, so no per-weight subtract is needed; v_dot2_f32_f16 forms the
@@ -50,15 +51,33 @@ __device__ __forceinline__ Int4Pair<G> load_int4_pair(const float *Sp, size_t re
         return __builtin_nontemporal_load(reinterpret_cast<const f2_t *>(Sp + rec * 64 + c * 2));
 }
 
+// The decode's constants, opaque to the optimiser so that each lives in a
+// register once (an instruction here takes at most one scalar operand and
+// no literal): the nibble masks 0x000F000F / 0x00F000F0 and the fp16 pair
+// 1024.0, 1024.0.
+struct Int4Magic {
+    unsigned m_lo, m_hi, magic;
+};
+__device__ __forceinline__ Int4Magic int4_magic() {
+    Int4Magic k{0x000F000Fu, 0x00F000F0u, 0x64006400u};
+    asm volatile("" : "+s"(k.m_lo), "+s"(k.m_hi));
+    asm volatile("" : "+v"(k.magic));
+    return k;
+}
+
 // One 32-code half of a block against its staged activations (the pieces
 // av[d] of words d = 0..3 and, per quarter qh, the even / odd activation sums
 // sv[qh]): sum_k a_k (offset + scale q_k), regrouped per pair as offset * sum(a)
-// + scale * sum(a * q) with q read off the fp16 magic decode (1024 + q or
-// 1024 + 16 q), the 1024 bias removed through the sums.
+// + scale * sum(a * q) with q read off the fp16 magic decode (OR-ing a code
+// into the mantissa of 1024.0: 1024 + q for a low nibble, 1024 + 16 q for a
+// high one left in place; one v_and_or_b32 per two codes), the 1024 bias
+// removed through the sums. Word byte i holds codes 2 i (low nibble) and
+// 2 i + 1, so the masked word gives codes (0, 4) and (1, 5), the word shifted
+// by 8 codes (2, 6) and (3, 7): the activation pieces' pair order.
 template <int G>
 __device__ __forceinline__ float int4_half_dot(const u4_t (&av)[4], const unsigned (&word)[4],
                                                const f2_t *sv, const Int4Pair<G> &pp,
-                                               unsigned magic) {
+                                               const Int4Magic &k) {
     constexpr int GQ = G == 4 ? 2 : 1;
     float total = 0.f;
 #pragma unroll
@@ -66,12 +85,11 @@ __device__ __forceinline__ float int4_half_dot(const u4_t (&av)[4], const unsign
         float Te = 0.f, To = 0.f;
 #pragma unroll
         for (int d = qh * 4 / GQ; d < (qh + 1) * 4 / GQ; ++d) {
-            const unsigned y0 = __builtin_amdgcn_perm(magic, word[d], 0x04020400u);
-            const unsigned y1 = __builtin_amdgcn_perm(magic, word[d], 0x04030401u);
-            Te = dot2(as_h2(y0 & 0xFF0FFF0Fu), as_h2(av[d].x), Te);
-            Te = dot2(as_h2(y1 & 0xFF0FFF0Fu), as_h2(av[d].y), Te);
-            To = dot2(as_h2(y0 & 0xFFF0FFF0u), as_h2(av[d].z), To);
-            To = dot2(as_h2(y1 & 0xFFF0FFF0u), as_h2(av[d].w), To);
+            const unsigned w = word[d], w8 = w >> 8;
+            Te = dot2(as_h2((w & k.m_lo) | k.magic), as_h2(av[d].x), Te);
+            Te = dot2(as_h2((w8 & k.m_lo) | k.magic), as_h2(av[d].y), Te);
+            To = dot2(as_h2((w & k.m_hi) | k.magic), as_h2(av[d].z), To);
+            To = dot2(as_h2((w8 & k.m_hi) | k.magic), as_h2(av[d].w), To);
         }
         float off, sc;
         if constexpr (G == 4) {
@@ -156,7 +174,7 @@ __global__ __launch_bounds__(64 * TILE_WAVES) void gemv_int4b64_tile_kernel(
     const int t = blockIdx.x;                // 32-channel tile
     const int m0 = blockIdx.y * MR;
     const int c = lane & 31, h = lane >> 5;
-    const unsigned magic = 0x64646464u;
+    const Int4Magic magic = int4_magic();
 
     float acc[MR];
 #pragma unroll
@@ -295,7 +313,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_int4b64_half_kernel(
     const int m0 = blockIdx.y * MR;
     const int c16 = lane & 15, h = (lane >> 4) & 1, j = lane >> 5;
     const int c = (blockIdx.x & 1) * 16 + c16;       // channel within the tile
-    const unsigned magic = 0x64646464u;
+    const Int4Magic magic = int4_magic();
     float acc[MR];
 #pragma unroll
     for (int r = 0; r < MR; ++r) acc[r] = 0.f;
