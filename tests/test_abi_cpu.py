@@ -83,12 +83,19 @@ def test_run_ws_validation(lib):
 
 def test_split_k_workspace_plan():
     """Workspace is a function of the shape: Int4 GEMMs with few output tiles
-    (64 x 128 each) split K into at most 8 slices of >= 8 K-blocks of 64 and
-    need S partial [M][N] float tiles; shapes that fill the GPU need none."""
+    split K into at most 8 slices and need S partial [M][N] float tiles;
+    shapes that fill the GPU need none. Up to M = 64 (the skinny kernel: a
+    32-channel tile of every row per workgroup) slices keep >= 8 K-blocks
+    of 64 and split while tiles x slices fit the 256 CUs; above, 64 x 128 or
+    128 x 64 tiles split below 128 tiles, slices of >= 8 K-blocks."""
     def sz(M, K, N):
         return Q.qgemm_workspace_size(M, K, N, "int4b64")
-    assert sz(64, 4096, 512) == 8 * 64 * 512 * 4          # 4 tiles -> 8 slices
+    assert sz(64, 4096, 512) == 8 * 64 * 512 * 4          # 16 tiles -> 8 slices
     assert sz(64, 1920, 384) == 3 * 64 * 384 * 4          # 30 K-blocks -> 3 slices
+    assert sz(32, 2560, 4096) == 2 * 32 * 4096 * 4        # 128 tiles -> 2 slices
+    assert sz(48, 4096, 11008) == 2 * 48 * 11008 * 4      # 344 tiles: 64 x 128 tiles, 86 -> 2 slices
+    assert sz(32, 9728, 2560) == 3 * 32 * 2560 * 4        # 80 tiles -> 3 slices (240 <= 256)
+    assert sz(96, 4096, 512) == 8 * 96 * 512 * 4          # 64 x 128 tiles: 4 -> 8 slices
     assert sz(512, 4096, 4096) == 0                       # 256 tiles fill the GPU
     assert sz(64, 448, 128) == 0                          # 7 K-blocks: too short to split
     assert sz(1, 4096, 4096) == sz(1, 4096, 4096)         # pure function of the shape
@@ -101,10 +108,10 @@ def test_split_k_workspace_plan():
     # Int4 GEMV (M <= 8): fewer than 128 32-channel tiles split K into three or
     # more slices of >= 48 blocks; the size covers the larger of the GEMV and
     # GEMM plans
-    assert Q.qgemm_workspace_size(8, 9728, 2560, "int4b64") == 8 * 8 * 2560 * 4   # GEMM plan 8 > GEMV 3
+    assert Q.qgemm_workspace_size(8, 9728, 2560, "int4b64") == 3 * 8 * 2560 * 4   # GEMM plan 3 = GEMV 3
     assert Q.qgemm_workspace_size(2, 16384, 70, "int4b64") == -(-8 * 2 * 70 * 4 // 256) * 256   # GEMM plan 8 > GEMV 5
     assert Q.qgemm_workspace_size(1, 16384, 70, "int4b64") == -(-8 * 1 * 70 * 4 // 256) * 256
-    assert Q.qgemm_workspace_size(1, 4096, 11008, "int4b64") == 2 * 11008 * 4     # GEMM plan: 86 tiles
+    assert Q.qgemm_workspace_size(1, 4096, 11008, "int4b64") == 2 * 11008 * 4     # GEMM plan: 86 tiles of 64 x 128
     w4 = Q.qgemm_workspace_size(32, 9728, 2560, "w4a8")
     assert w4 - Q.qgemm_workspace_size(32, 9728, 32, "w4a8") >= 8 * 32 * 2560 * 4 - 8 * 32 * 32 * 4
     # fp32: 16x64 / 64x64 tiles; below 256 tiles each workgroup has two

@@ -35,25 +35,35 @@ def _asm(tmpdir: str) -> str:
     return open(out).read()
 
 
-def _loops(asm: str):
-    """(kernel name, loop body lines) for every gemm_int4b64 kernel's main loop."""
+def _loops(asm: str, kernel: str = "gemm_int4b64_kernel"):
+    """(kernel name, loop body lines in execution order) for every such
+    kernel's first loop: the header's block and the loop blocks after it in
+    file order, then the loop's blocks placed before the header (a latch)."""
     lines = asm.splitlines()
-    name = None
-    i = 0
-    while i < len(lines):
-        m = re.match(r"^(_Z\w*gemm_int4b64_kernel\w*):", lines[i])
-        if m:
-            name = m.group(1)
-        m = re.match(r"^(\.LBB\w+):.*Loop Header", lines[i])
-        if m and name:
-            hdr = m.group(1)
-            j = i + 1
-            while j < len(lines) and not re.search(r"s_c?branch\w*\s+" + re.escape(hdr) + r"\b", lines[j]):
-                j += 1
-            yield name, lines[i + 1:j + 1]
-            name = None
-            i = j
-        i += 1
+    starts = [i for i, ln in enumerate(lines) if re.match(r"^(_Z\w*" + kernel + r"\w*):", ln)]
+    for k, st in enumerate(starts):
+        name = re.match(r"^(_Z\w*):", lines[st]).group(1)
+        end = next((i for i in range(st, len(lines)) if "s_endpgm" in lines[i]), len(lines))
+        # blocks: (label line index, label, comment)
+        blocks = [(i, ln) for i in range(st, end) for ln in [lines[i]] if re.match(r"^\.LBB\w+:", ln)]
+        hdr = next((b for b in blocks if "Loop Header" in b[1]), None)
+        if hdr is None:
+            continue
+        hname = "BB" + re.match(r"^\.LBB(\w+):", hdr[1]).group(1)
+        member = lambda ln: ln is hdr[1] or ("Header=" + hname + " ") in ln + " "
+        def block_lines(idx):
+            nxt = next((b[0] for b in blocks if b[0] > idx), end)
+            return lines[idx:nxt]
+        body = []
+        after = [b for b in blocks if b[0] >= hdr[0]]
+        for b in after:
+            if not member(b[1]):
+                break
+            body += block_lines(b[0])
+        for b in blocks:
+            if b[0] < hdr[0] and member(b[1]):
+                body += block_lines(b[0])
+        yield name, body
 
 
 def _replay(body, a_tiles, a_pieces, a_wait):
@@ -113,3 +123,23 @@ def test_replay_catches_a_load_moved_below_the_wait():
             ["s_waitcnt vmcnt(2)", "buffer_load_dwordx4 v[2:5], v0, s[4:7], 0 offen",
              "buffer_load_dwordx4 v[6:9], v0, s[4:7], 0 offen", "ds_read_b128 v[10:13], v20"]
     assert _replay(moved * 4, 2, 16, 2)[0]
+
+
+# skinny kernel (M <= 64): DMA loads per wave and pass (either row count)
+SKINNY_NDMA = 8
+
+
+@pytest.mark.skipif(not (shutil.which(HIPCC) or os.path.exists(HIPCC)), reason="hipcc not found")
+def test_int4_skinny_dma_waits_cover_every_lds_read(tmp_path):
+    """The skinny kernel double-buffers A in passes: at every LDS read only
+    the next pass's DMA group may be outstanding."""
+    asm = _asm(str(tmp_path))
+    seen = 0
+    problems = []
+    for name, body in _loops(asm, "gemm_int4b64_skinny_kernel"):
+        bad, n = _replay(body, 2, SKINNY_NDMA, -1)
+        assert n >= 2 * 2 * SKINNY_NDMA and n % SKINNY_NDMA == 0, f"{name}: {n // 2} DMA loads per round"
+        problems += [f"{name[:80]}: {b}" for b in bad]
+        seen += 1
+    assert seen == 21, f"{seen} skinny kernel loops found"   # (RF, NB) x 3 pair layouts
+    assert not problems, "\n".join(problems[:20])

@@ -158,6 +158,18 @@ def test_int4_other_block_sizes(M):
         _parity(fmt, M, K, N, seed=M * 17 + K + N)
 
 
+@pytest.mark.parametrize("M", [9, 16, 31, 32, 33, 48, 64])
+def test_int4_skinny(M):
+    """The skinny prefill kernel (GEMV threshold < M <= 64: a 32-channel tile of
+    every row per workgroup, passes of 16 or 8 blocks double-buffered): one
+    and several passes (a short last pass), split K and not, ragged N, pairs
+    per 64-block, per 32-half and per 16-quarter."""
+    for fmt, K, N in [("int4b64", 64, 33), ("int4b64", 2560, 4096), ("int4b64", 9728, 300),
+                      ("int4b64", 4096, 11008), ("int4b0", 1088, 70), ("int4b32", 3072, 1000),
+                      ("int4b16", 2560, 130), ("int4b48", 768, 100)]:
+        _parity(fmt, M, K, N, seed=M * 29 + K + N)
+
+
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 9, 64, 65, 129])
 def test_int8_block_sizes(M):
     """Int8 with a pair per block of 16, 32, 48, 64, 80, 96, 128, 192 or 320

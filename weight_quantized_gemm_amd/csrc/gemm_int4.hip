@@ -446,6 +446,244 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Skinny prefill (GEMV threshold < M <= 64): few rows, so the weights are the
+// bytes that matter (the MNN GemmSpeed page, section "Sample data": small M
+// is bound by the weight stream) and a tile of the wide GEMM would be mostly
+// padding rows and few workgroups. A 512-thread workgroup owns one 32-channel
+// tile of every row (RF 32-row fragments, all of M) over one K slice; its
+// eight waves take the slice's 64-blocks round-robin. As in the decode GEMV,
+// every weight record and pair of a wave's blocks is requested at once (up to
+// 8 NB blocks per workgroup; a longer slice repeats this), so the weight
+// stream costs one round trip; A, which every tile reads and the L2 holds,
+// goes into LDS by DMA in passes of SK_PB blocks, double-buffered, rows
+// XOR-swizzled as in the wide kernel. Per block a wave dequantises its 1 KiB
+// record as the wide kernel does and runs four MFMA steps per row fragment;
+// the eight waves' partial tiles meet in LDS in a fixed order. Every load is
+// unconditional from clamped indices; blocks past the slice get all-zero
+// dequantisation constants and add exactly zero.
+// ---------------------------------------------------------------------------
+constexpr int SK_WAVES = 8;
+constexpr int SK_BUF = 64 * 1024;                   // A bytes per pass buffer (two buffers)
+
+template <int RF, int NB>
+struct SkinnyCfg {
+    static constexpr int MR = 32 * RF;                               // rows staged (M padded)
+    static constexpr int PB = SK_BUF / (MR * 128);                   // blocks per pass
+    static constexpr int NDMA = PB * MR / 8 / SK_WAVES;              // DMA instructions per wave and pass
+    static constexpr int NBW = PB / SK_WAVES;                        // blocks per wave and pass
+    static constexpr int SPB = SK_WAVES * NB;                        // blocks per round of weight loads
+    static constexpr int NPASS = NB / NBW;                           // passes per round
+    static constexpr size_t RED_BYTES = (size_t)SK_WAVES * MR * 32 * 4;  // the waves' partial tiles
+    static_assert(NDMA * SK_WAVES * 8 == PB * MR && NBW * SK_WAVES == PB, "whole passes");
+    static_assert(NB % NBW == 0, "whole passes per round");
+    static_assert(RED_BYTES <= SK_BUF, "reduction fits one A buffer");
+    // loads issued after pass 0's DMA when the wave first waits for it (the
+    // round's weight records and pairs, then pass 1's DMA), and after pass
+    // p's DMA when it waits for that (pass p + 1's DMA)
+    static constexpr int WAIT0 = 2 * NB + NDMA;
+    static constexpr int WAIT = NDMA;
+    static_assert(WAIT0 <= 63, "vmcnt range");
+};
+
+// A workgroup barrier without __syncthreads' release fence, which would also
+// wait for the LDS DMA just issued for the next pass: the waves' own waits
+// cover the DMA they read, and every LDS read before the barrier has been
+// consumed; the acquire fence keeps later LDS reads below the barrier.
+__device__ __forceinline__ void sk_barrier() {
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+template <int RF, int G, int NB>
+__global__ __launch_bounds__(64 * SK_WAVES) void gemm_int4b64_skinny_kernel(
+    int M, int K, int N, const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
+    const float *__restrict__ Sp, void *__restrict__ C, Epilogue epi) {
+    using T = SkinnyCfg<RF, NB>;
+    constexpr int MR = T::MR, PB = T::PB, NDMA = T::NDMA, NBW = T::NBW, SPB = T::SPB;
+    // one array per A buffer: the compiler orders LDS reads after any DMA
+    // into the same array (it does not see the explicit waits), and only
+    // separate arrays let it tell one buffer's DMA from reads of the other
+    __shared__ __align__(16) unsigned char lds0[SK_BUF], lds1[SK_BUF];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = uniform(tid >> 6);
+    const int r = lane & 31, h = lane >> 5;
+    const int t = blockIdx.x;                                  // 32-channel tile
+    const int nblk = K / BK;
+    const int KB0 = slice_begin(blockIdx.y, nblk, gridDim.y);
+    const int KB1 = slice_begin(blockIdx.y + 1, nblk, gridDim.y);
+    const int last = KB1 - 1;
+    const bool raw = gridDim.y > 1 || epi.plain;
+    float *const out = static_cast<float *>(C) + (size_t)blockIdx.y * M * N;
+
+    constexpr unsigned PREC = 256u * G;
+    constexpr int GQ = G == 4 ? 2 : 1;
+    using PairT = typename std::conditional<G == 4, f4_t, f2_t>::type;
+    const int ntiles_b = (N + 31) / 32;
+    const size_t rec0 = (size_t)min(t, ntiles_b - 1) * nblk;
+    const __amdgpu_buffer_rsrc_t b_rs = byte_rsrc(Wp + rec0 * 1024, (unsigned)nblk * 1024u);
+    const __amdgpu_buffer_rsrc_t p_rs = byte_rsrc(reinterpret_cast<const char *>(Sp) + rec0 * PREC,
+                                                  (unsigned)nblk * PREC);
+    const unsigned b_off = (unsigned)lane * 16u;
+    const unsigned p_off = G == 4 ? (unsigned)(4 * r + 2 * h) * 8u
+                         : G == 2 ? (unsigned)(32 * h + r) * 8u : (unsigned)r * 8u;
+
+    // DMA instruction g = wave + 8 q of a pass fills rows 8 (g % (MR / 8)) ..
+    // + 7 of its block g / (MR / 8): lane l's 16 bytes land in row
+    // rho = 8 (g % (MR / 8)) + l / 8, slot l % 8, and are piece (l % 8) ^ (l / 8)
+    // of that row of A (rows past M clamped: loaded, never stored)
+    unsigned a_off[NDMA];
+#pragma unroll
+    for (int q = 0; q < NDMA; ++q) {
+        const int g = wave + SK_WAVES * q;
+        const int row = 8 * (g % (MR / 8)) + (lane >> 3);
+        a_off[q] = (unsigned)(min(row, M - 1) * K + 8 * ((lane & 7) ^ (lane >> 3))) * 2u;
+    }
+    auto dma = [&](unsigned char *buf, int b0) {    // the pass starting at block b0
+#pragma unroll
+        for (int q = 0; q < NDMA; ++q) {
+            const int g = wave + SK_WAVES * q;
+            const int b = min(b0 + g / (MR / 8), last);
+            const __amdgpu_buffer_rsrc_t rs =
+                byte_rsrc(A + (size_t)b * BK, (unsigned)M * K * 2u - (unsigned)b * (BK * 2));
+            lds_dma16(rs, buf + (size_t)g * 1024, a_off[q]);
+        }
+    };
+
+    unsigned m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, magic = 0x64006400u;
+    asm volatile("" : "+s"(m_lo), "+s"(m_hi));
+    asm volatile("" : "+v"(magic));
+
+    f16_t acc[RF];
+#pragma unroll
+    for (int i = 0; i < RF; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+
+    u4_t bq[NB];
+    PairT bp[NB];
+    // pass p of a round (blocks s0 + p PB ..): the wave's blocks are k =
+    // p NBW + kk, block s0 + wave + 8 k of the round
+    auto compute = [&](const unsigned char *buf, int p, int spb) {
+#pragma unroll
+        for (int kk = 0; kk < NBW; ++kk) {
+            const int k = p * NBW + kk;
+            const int j = wave + SK_WAVES * k;                 // block within the round
+            DqParams prm[GQ];
+            if constexpr (G == 4) {
+                prm[0] = dq_params(f2_t{bp[k].x, bp[k].y}, j < spb);
+                prm[GQ - 1] = dq_params(f2_t{bp[k].z, bp[k].w}, j < spb);
+            } else {
+                prm[0] = dq_params(bp[k], j < spb);
+            }
+            const unsigned char *tile = buf + (size_t)(wave + SK_WAVES * kk) * MR * 128;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const h8_t bop = dequant8(bq[k][st], prm[st * GQ / 4], m_lo, m_hi, magic);
+#pragma unroll
+                for (int rf = 0; rf < RF; ++rf) {
+                    const h8_t aop = *reinterpret_cast<const h8_t *>(
+                        tile + (32 * rf + r) * 128 + 16 * ((4 * h + st) ^ (r & 7)));
+                    acc[rf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, bop, acc[rf], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    // Rounds of SPB blocks (usually one). A round issues pass 0's DMA, every
+    // weight record and pair of the wave's blocks, and pass 1's DMA; before
+    // pass p is read the wave waits for its DMA (loads complete in order:
+    // WAIT0 newer loads may stay in flight for pass 0, WAIT for the others,
+    // each pass having issued the next one's DMA first; if the compiler moved
+    // weight loads below a wait, the count still covers the DMA issued before
+    // them), and the barrier makes every wave's share visible; the second
+    // barrier keeps a buffer from being refilled while a wave still reads it.
+    for (int s0 = KB0; s0 < KB1; s0 += SPB) {                 // workgroup-uniform
+        const int spb = min(SPB, KB1 - s0);
+        dma(lds0, s0);
+#pragma unroll
+        for (int k = 0; k < NB; ++k)
+            bq[k] = buf_load16<kNonTemporal>(b_rs, b_off, (unsigned)min(s0 + wave + SK_WAVES * k, last) * 1024u);
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const unsigned b = (unsigned)min(s0 + wave + SK_WAVES * k, last);
+            if constexpr (G == 4)
+                bp[k] = __builtin_bit_cast(f4_t, buf_load16(p_rs, p_off, b * PREC));
+            else
+                bp[k] = buf_load8(p_rs, p_off, b * PREC);
+        }
+        dma(lds1, s0 + PB);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(vm_wait(T::WAIT0));
+        sk_barrier();
+        compute(lds0, 0, spb);
+        sk_barrier();
+#pragma unroll
+        for (int p = 1; p < T::NPASS; ++p) {
+            if (p * PB >= spb) break;                          // workgroup-uniform
+            dma((p & 1) ? lds0 : lds1, s0 + (p + 1) * PB);
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(vm_wait(T::WAIT));
+            sk_barrier();
+            compute((p & 1) ? lds1 : lds0, p, spb);
+            sk_barrier();
+        }
+        // the last (clamped) DMA lands before the buffers are refilled or reused
+        __builtin_amdgcn_s_waitcnt(vm_wait(0));
+        sk_barrier();
+    }
+
+    // ---- the eight partial tiles meet in LDS (over the first A buffer),
+    //      summed in wave order ----
+    float *red = reinterpret_cast<float *>(lds0);
+#pragma unroll
+    for (int rf = 0; rf < RF; ++rf)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            red[((size_t)wave * MR + 32 * rf + 8 * (e >> 2) + 4 * h + (e & 3)) * 32 + r] = acc[rf][e];
+    __syncthreads();
+    for (int o = tid; o < MR * 32; o += 64 * SK_WAVES) {
+        const int row = o >> 5, col = o & 31;
+        const int n = 32 * t + col;
+        if (row >= M || n >= N) continue;
+        float total = 0.f;
+#pragma unroll
+        for (int w = 0; w < SK_WAVES; ++w) total += red[((size_t)w * MR + row) * 32 + col];
+        if (raw)
+            out[(size_t)row * N + n] = total;
+        else
+            epi_put(epi, C, row, n, N, total);
+    }
+}
+
+template <int RF, int NB>
+static hipError_t launch_skinny_nb(int M, int K, int N, const void *A, const void *Wp, const void *Sp,
+                                   void *out, const Epilogue &epi, int pair_g, int nsplit, hipStream_t s) {
+    auto kernel = pair_g == 4 ? gemm_int4b64_skinny_kernel<RF, 4, NB>
+                : pair_g == 2 ? gemm_int4b64_skinny_kernel<RF, 2, NB> : gemm_int4b64_skinny_kernel<RF, 1, NB>;
+    hipLaunchKernelGGL(kernel, dim3(div_up(N, 32), nsplit), dim3(64 * SK_WAVES), 0, s, M, K, N,
+                       static_cast<const _Float16 *>(A), static_cast<const uint8_t *>(Wp),
+                       static_cast<const float *>(Sp), out, epi);
+    return hipGetLastError();
+}
+
+// NB, the weight records a wave requests at once: the fewest that cover the
+// slice (at least one pass), at most 16 (8 with 64 rows; longer slices take
+// several rounds)
+template <int RF>
+static hipError_t launch_skinny(int M, int K, int N, const void *A, const void *Wp, const void *Sp,
+                                void *out, const Epilogue &epi, int pair_g, int nsplit, hipStream_t s) {
+    const int per = div_up(K / BK, nsplit);                       // blocks of the longest slice
+    const int need = div_up(per, SK_WAVES);
+    if (need <= 2) return launch_skinny_nb<RF, 2>(M, K, N, A, Wp, Sp, out, epi, pair_g, nsplit, s);
+    if (need <= 4) return launch_skinny_nb<RF, 4>(M, K, N, A, Wp, Sp, out, epi, pair_g, nsplit, s);
+    // (with 64 rows, sixteen one-block passes per round would not stay unrolled)
+    if (need <= 8 || RF == 2) return launch_skinny_nb<RF, 8>(M, K, N, A, Wp, Sp, out, epi, pair_g, nsplit, s);
+    return launch_skinny_nb<RF, RF == 2 ? 8 : 16>(M, K, N, A, Wp, Sp, out, epi, pair_g, nsplit, s);
+}
+
 template <class T>
 static hipError_t launch_tiles(int M, int K, int N, const void *A, const void *Wp, const void *Sp,
                                void *out, const Epilogue &epi, int pair_g, int nsplit,
@@ -475,8 +713,10 @@ hipError_t launch_gemm_int4b64(int M, int K, int N, const void *A, const void *W
                                const void *Sp, void *C, const Epilogue &epi, int pair_g,
                                int nsplit, float *part, hipStream_t s) {
     void *out = nsplit > 1 ? static_cast<void *>(part) : C;
-    const Int4Tile t = int4_tile(M);
-    hipError_t e = t.bm == 128
+    const Int4Tile t = int4_tile(M, N);
+    hipError_t e = t.bn == 32 ? (t.bm == 32 ? launch_skinny<1>(M, K, N, A, Wp, Sp, out, epi, pair_g, nsplit, s)
+                                            : launch_skinny<2>(M, K, N, A, Wp, Sp, out, epi, pair_g, nsplit, s))
+                 : t.bm == 128
         ? launch_tiles<TileCfg<128, 64>>(M, K, N, A, Wp, Sp, out, epi, pair_g, nsplit, s)
         : launch_tiles<TileCfg<64, 128>>(M, K, N, A, Wp, Sp, out, epi, pair_g, nsplit, s);
     if (e != hipSuccess || nsplit <= 1) return e;

@@ -127,7 +127,18 @@ int splitk_plan(qgemm_format f, int M, int K, int N) {
     switch (f) {
     case QGEMM_INT4_B64:
     case QGEMM_INT4_B0:
-        tiles = (long long)div_up(M, int4_tile(M).bm) * div_up(N, int4_tile(M).bn);
+        if (int4_tile(M, N).bn == 32) {
+            // the skinny kernel: one workgroup per 32-channel tile and slice
+            // streams its weights; it splits as far as the tiles and slices
+            // still fit the CUs in one round (its LDS holds one workgroup per
+            // CU), eight waves with one or more 64-blocks each
+            const long long nt = div_up(N, 32);
+            long long sp = kSplitTargetCUs / nt;
+            if (sp > kMaxSplit) sp = kMaxSplit;
+            if (sp > K / 64 / 8) sp = K / 64 / 8;
+            return sp < 2 ? 1 : (int)sp;
+        }
+        tiles = (long long)div_up(M, int4_tile(M, N).bm) * div_up(N, int4_tile(M, N).bn);
         kunits = K / 64 / 8;         // four waves, two or more 64-blocks each
         break;
     case QGEMM_F32: {

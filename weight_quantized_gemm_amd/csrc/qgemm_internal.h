@@ -207,11 +207,23 @@ W4A8Workspace w4a8_workspace(int M, int K);
 // workspace size never depends on the device.
 // Output tile of the Int4-Block64 prefill GEMM (rows x columns), shared by
 // the kernel and the split-K planner: 128 x 64 once M reaches 128 (each
-// dequantised weight serves 128 rows), else 64 x 128.
+// dequantised weight serves 128 rows), else 64 x 128, or the skinny
+// kernel's 32- or 64-row tiles of 32 channels (below).
 struct Int4Tile {
     int bm, bn;
 };
-inline Int4Tile int4_tile(int M) { return M >= 128 ? Int4Tile{128, 64} : Int4Tile{64, 128}; }
+// CUs a launch should cover (split-K plans, the skinny kernel's choice).
+constexpr int kSplitTargetCUs = 256;
+// Up to kSkinnyMaxM rows, while the 32-channel tiles are fewer than the CUs,
+// the skinny kernel runs: a 32-channel tile of all rows (32 or 64, M padded)
+// per workgroup. (With more tiles than CUs it re-reads A once per tile and
+// takes a second round of workgroups; the 64 x 128 tiles do better there.)
+constexpr int kSkinnyMaxM = 64;
+inline Int4Tile int4_tile(int M, int N) {
+    return M >= 128 ? Int4Tile{128, 64}
+         : M > kSkinnyMaxM || (N + 31) / 32 >= kSplitTargetCUs ? Int4Tile{64, 128}
+         : M > 32 ? Int4Tile{64, 32} : Int4Tile{32, 32};
+}
 // Output tile of the channel-row (Int8-Block0, fp16-weight) prefill GEMM.
 constexpr int kRowsTileM = 128, kRowsTileN = 64;
 // Output tile of the W4A8 prefill GEMM and its K stage (qa bytes per row).
@@ -223,7 +235,6 @@ constexpr int kF32TileN = 64, kF32TileMSmall = 16, kF32TileM = 64, kF32ChunkK = 
 // fewer output tiles than CUs; 1 otherwise.
 constexpr int kF32KGroups = 2;
 int f32_kgroups(int M, int N);
-constexpr int kSplitTargetCUs = 256;
 constexpr int kMaxSplit = 8;
 int splitk_plan(qgemm_format f, int M, int K, int N);      // 1 = no split
 // The same for the Int4 GEMV (M up to the GEMV limit): shapes with few
