@@ -112,6 +112,54 @@ def test_int4_gemm_dma_waits_cover_every_lds_read(tmp_path):
     assert not problems, "\n".join(problems[:20])
 
 
+def _prologues(asm: str, kernel: str = "gemm_int4b64_kernel"):
+    """(kernel name, lines from the kernel's entry to its first loop header)."""
+    lines = asm.splitlines()
+    for st, ln in enumerate(lines):
+        m = re.match(r"^(_Z\w*" + kernel + r"\w*):", ln)
+        if not m:
+            continue
+        hdr = next(i for i in range(st, len(lines)) if "Loop Header" in lines[i])
+        yield m.group(1), lines[st:hdr]
+
+
+def _replay_prologue(lines):
+    """DMA loads still outstanding at each LDS read before the main loop
+    (the prologue waits for all of its DMAs before the first read)."""
+    queue = []
+    bad = []
+    for ln in lines:
+        t = ln.strip()
+        if re.match(r"(buffer|global)_load", t):
+            queue.append(t.endswith(" lds"))
+        elif t.startswith("s_waitcnt") and "vmcnt(" in t:
+            n = int(re.search(r"vmcnt\((\d+)\)", t).group(1))
+            while len(queue) > n:
+                queue.pop(0)
+        elif t.startswith("ds_read") and any(queue):
+            bad.append(f"{t}: {sum(queue)} DMA loads outstanding")
+    return bad
+
+
+@pytest.mark.skipif(not (shutil.which(HIPCC) or os.path.exists(HIPCC)), reason="hipcc not found")
+def test_int4_gemm_prologue_waits_for_its_dma(tmp_path):
+    """The prologue's explicit wait leaves block 0's neighbours' B loads in
+    flight; it must still cover every DMA issued before it, whatever order
+    the compiler gave the loads."""
+    asm = _asm(str(tmp_path))
+    seen = 0
+    problems = []
+    for name, lines in _prologues(asm):
+        assert any(ln.strip().endswith(" lds") for ln in lines), f"{name}: no DMA in the prologue"
+        problems += [f"{name[:80]}: {b}" for b in _replay_prologue(lines)]
+        seen += 1
+    assert seen >= 6
+    assert not problems, "\n".join(problems[:20])
+    moved = ["buffer_load_dwordx4 v1, s[0:3], 0 offen lds"] * 4 + ["s_waitcnt vmcnt(2)",
+             "buffer_load_dwordx4 v[2:5], v0, s[4:7], 0 offen", "ds_read_b128 v[10:13], v20"]
+    assert _replay_prologue(moved)
+
+
 def test_replay_catches_a_load_moved_below_the_wait():
     """The replay itself: a B load issued after the wait leaves the DMA group
     outstanding at the next LDS read."""

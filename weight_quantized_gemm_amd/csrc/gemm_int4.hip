@@ -77,20 +77,20 @@ struct TileCfg {
     // B code ring: loads four blocks ahead
     static constexpr int B_RING = 4;
     static constexpr int A_PIECES = BM * BK / 8 / 64;   // 16-byte A pieces per lane and block
-    static constexpr int RED_STRIDE = BN + 4;           // floats per LDS row of the reduction
     static constexpr size_t AS_BYTES = (size_t)BM * BK * 2;                 // one A tile
-    static constexpr size_t A_LDS = (size_t)NWAVE * A_TILES * AS_BYTES;     // all waves
-    // the four partial tiles meet in LDS RCH rows at a time (all BM rows when
-    // they fit next to nothing else, else 64-row chunks)
-    static constexpr int RCH = (size_t)NWAVE * BM * RED_STRIDE * 4 <= 160 * 1024 ? BM : 64;
-    static constexpr size_t RED_BYTES = (size_t)NWAVE * RCH * RED_STRIDE * 4;
-    static constexpr size_t LDS_BYTES = RED_BYTES > A_LDS ? RED_BYTES : A_LDS;
+    static constexpr size_t WAVE_LDS = (size_t)A_TILES * AS_BYTES;          // one wave's tiles
+    static constexpr size_t LDS_BYTES = (size_t)NWAVE * WAVE_LDS;
     // loads issued after the DMA of the block a wave reads next, by the time
     // it reads it (see the main loop)
     static constexpr int A_WAIT = CF + (A_TILES - 2) * (2 * CF + A_PIECES);
+    // loads issued after block 0's codes in the prologue (the pairs of block
+    // 1 and the codes of blocks 1 .. B_RING - 1)
+    static constexpr int PRO_WAIT = B_RING * CF;
     static_assert(UNROLL % A_TILES == 0 && UNROLL % B_RING == 0, "ring sizes");
-    static_assert(A_WAIT <= 63, "vmcnt range");
+    static_assert(A_WAIT <= 63 && PRO_WAIT <= 63, "vmcnt range");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 workgroup");
+    // a wave's partial tile (BM x BN fp32) takes exactly its A tiles' space
+    static_assert((size_t)BM * BN * 4 == WAVE_LDS, "partial tile fills the wave's LDS");
 };
 
 // Per (channel tile, block) dequantisation constants. Even codes decode as
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     const _Float16 *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ Sp, void *__restrict__ C, Epilogue epi) {
     constexpr int BM = T::BM, BN = T::BN, RF = T::RF, CF = T::CF;
-    constexpr int A_TILES = T::A_TILES, A_PIECES = T::A_PIECES, RED_STRIDE = T::RED_STRIDE;
+    constexpr int A_TILES = T::A_TILES, A_PIECES = T::A_PIECES;
     constexpr int B_RING = T::B_RING;
     constexpr size_t AS_BYTES = T::AS_BYTES;
     __shared__ __align__(16) unsigned char lds[T::LDS_BYTES];
@@ -198,12 +198,13 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     const int kb0 = KB0 + kq * nbs / 4, kb1 = KB0 + (kq + 1) * nbs / 4;   // contiguous quarter
     const int nb = kb1 - kb0;                      // kb0 is a valid block even when nb == 0
     const int last = max(kb1 - 1, kb0);
-    // every wave runs its quarter's blocks rounded up to the unroll; blocks
-    // past the quarter's end re-load its last block and add exactly zero
-    const int nsteps = (nb + UNROLL - 1) / UNROLL * UNROLL;
+    // every wave runs its quarter's blocks rounded up to the unroll, at least
+    // one unroll (so no path skips the main loop); blocks past the quarter's
+    // end re-load its last block and add exactly zero
+    const int nsteps = max((nb + UNROLL - 1) / UNROLL, 1) * UNROLL;
     const int ntiles_b = (N + 31) / 32;            // packed 32-channel tiles
 
-    unsigned char *const a_lds = lds + (size_t)kq * A_TILES * AS_BYTES;
+    unsigned char *const a_lds = lds + (size_t)kq * T::WAVE_LDS;
     auto a_tile = [&](int slot) { return a_lds + (size_t)slot * AS_BYTES; };
 
     // A by LDS DMA: a tile is BM rows of 128 bytes (one block), 16-byte slot
@@ -297,20 +298,23 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     // dequantisation constants instead (every weight +0), and adds exactly
     // zero.
     //
-    // prologue: the pairs of blocks 0 and 1, the codes of blocks
-    // 0 .. B_RING - 1 and the A of blocks 0 .. A_TILES - 2 (tiles 0 ..),
-    // all of it waited for; block 0's step-0 operands ready
-    load_p(bp[0], kb0);
-    load_p(bp[1], min(kb0 + 1, last));
-#pragma unroll
-    for (int d = 0; d < B_RING; ++d) load_b(bc[d], min(kb0 + d, last));
+    // prologue: the A of blocks 0 .. A_TILES - 2 (tiles 0 ..), the pairs and
+    // codes of block 0, then the pairs of block 1 and the codes of blocks
+    // 1 .. B_RING - 1. Only what precedes the last PRO_WAIT loads is waited
+    // for (all the DMAs and block 0's B), so block 0 starts while the rest
+    // of the rings is still on its way; block 0's step-0 operands ready
 #pragma unroll
     for (int d = 0; d < A_TILES - 1; ++d) dma_a(a_tile(d), min(kb0 + d, last));
+    load_p(bp[0], kb0);
+    load_b(bc[0], kb0);
+    load_p(bp[1], min(kb0 + 1, last));
+#pragma unroll
+    for (int d = 1; d < B_RING; ++d) load_b(bc[d], min(kb0 + d, last));
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vm_wait(T::PRO_WAIT));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int cf = 0; cf < CF; ++cf) make_prm(bp[0][cf], nb > 0, prm[cf]);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(vm_wait(0));
-    __builtin_amdgcn_sched_barrier(0);
     read_a(a_tile(0), 0, acur);
 #pragma unroll
     for (int cf = 0; cf < CF; ++cf) bcur[cf] = dequant8(bc[0][cf][0], prm[cf][0], m_lo, m_hi, magic);
@@ -320,7 +324,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     // matrix instructions, takes block i + A_TILES - 1 by DMA. Its step 3
     // reads block i + 1's first operands: that tile's DMA was issued at the
     // start of block i + 2 - A_TILES (or in the prologue, which waited for
-    // it), and since then each block issued its pair loads, its DMA and its
+    // all its DMAs), and since then each block issued its pair loads, its DMA and its
     // code loads (CF + A_PIECES + CF), this block the pairs and the DMA
     // before the codes: A_WAIT loads may still be outstanding, which the
     // explicit wait below allows (the compiler does not track the DMA's
@@ -390,57 +394,71 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
         }
     }
 
-    // ---- the four partial tiles to LDS (reusing the A tiles' space), RCH
-    //      rows at a time; each chunk summed over the K quarters in a fixed
-    //      order and stored: each pass covers RPI whole rows, lane -> 16
-    //      consecutive bytes of a row, so one store instruction writes whole
-    //      rows of the tile contiguously ----
-    constexpr int RCH = T::RCH;
-    constexpr int CPT = BN / 4;                    // float4 columns per tile row
-    constexpr int RPI = 64 * NWAVE / CPT;          // rows per pass
-    static_assert(BM % RCH == 0 && RCH % 32 == 0 && RCH % RPI == 0, "whole chunks and passes");
-    const int c4 = tid % CPT, r0 = tid / CPT;
-    const int gc = n0 + 4 * c4;
-    const float *red0 = reinterpret_cast<const float *>(lds);
-    float *red = reinterpret_cast<float *>(lds) + (size_t)kq * RCH * RED_STRIDE;
-    const size_t W = (size_t)RCH * RED_STRIDE;
-    const bool vec_store = (N & 3) == 0 && gc + 4 <= N;
-    // the last DMAs (clamped blocks, never read) land before LDS is reused
+    // ---- the four partial tiles meet in LDS. A wave whose own DMAs have
+    //      landed (the last ones, of clamped blocks, are never read) writes
+    //      its partial tile into its own A tiles, which no other wave uses,
+    //      so the waves that finish first do not wait for the last one; after
+    //      one barrier every thread sums four rows of one column over the K
+    //      quarters in a fixed order and stores them. A wave's partial tile
+    //      is column-major in groups of four rows, group R of column col at
+    //      slot R ^ (col % 16): the 16 lanes of a 16-byte LDS access, on 16
+    //      consecutive columns, then cover all 64 banks, when written from
+    //      the accumulator layout and when read back. One store instruction
+    //      writes 64 consecutive columns of a row. ----
+    constexpr int RG = BM / 4;                     // four-row groups per column
+    constexpr int GPP = 64 * NWAVE / BN;           // row groups per pass
+    static_assert(RG % GPP == 0 && RG >= 16, "whole passes, swizzle within the column");
     __builtin_amdgcn_s_waitcnt(vm_wait(0));
+    {
+        float *mine = reinterpret_cast<float *>(a_lds);
 #pragma unroll
-    for (int ch = 0; ch < BM / RCH; ++ch) {
-        __syncthreads();   // the A tiles (first chunk) or the last chunk's sums are read
-#pragma unroll
-        for (int rf = ch * (RCH / 32); rf < (ch + 1) * (RCH / 32); ++rf)
+        for (int rf = 0; rf < RF; ++rf)
 #pragma unroll
             for (int cf = 0; cf < CF; ++cf)
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    red[(32 * (rf - ch * (RCH / 32)) + 8 * (e >> 2) + 4 * h + (e & 3)) * RED_STRIDE +
-                        32 * cf + r] = acc[rf][cf][e];
-        __syncthreads();
+                for (int g = 0; g < 4; ++g) {
+                    // rows 32 rf + 8 g + 4 h + (0 .. 3) of column 32 cf + r
+                    const int R = 8 * rf + 2 * g + h, col = 32 * cf + r;
+                    *reinterpret_cast<f4_t *>(mine + (size_t)col * BM + 4 * (R ^ (col & 15))) =
+                        f4_t{acc[rf][cf][4 * g], acc[rf][cf][4 * g + 1], acc[rf][cf][4 * g + 2],
+                             acc[rf][cf][4 * g + 3]};
+                }
+    }
+    __syncthreads();
+    const int col = tid % BN, g0 = tid / BN;       // g0 is wave-uniform (BN >= 64)
+    const int gc = n0 + col;
+    const float *red0 = reinterpret_cast<const float *>(lds);
+    constexpr size_t W = T::WAVE_LDS / 4;          // floats per wave's partial tile
+    auto sum4 = [&](int R) {
+        const size_t o = (size_t)col * BM + 4 * (R ^ (col & 15));
+        f4_t v = *reinterpret_cast<const f4_t *>(red0 + o);
 #pragma unroll
-        for (int it = 0; it < RCH / RPI; ++it) {
-            const int row = it * RPI + r0;             // row within the chunk
-            const int gm = m0 + ch * RCH + row;
+        for (int q = 1; q < NWAVE; ++q) v += *reinterpret_cast<const f4_t *>(red0 + (size_t)q * W + o);
+        return v;
+    };
+    // (the two store forms in separate loops, the epilogue one not unrolled:
+    // one copy of its code per row group would not stay in the instruction
+    // cache)
+    if (raw) {
+#pragma unroll
+        for (int it = 0; it < RG / GPP; ++it) {
+            const int R = it * GPP + g0, gm = m0 + 4 * R;
             if (gm >= M) break;
-            const size_t o = (size_t)row * RED_STRIDE + 4 * c4;
-            f4_t sum = *reinterpret_cast<const f4_t *>(red0 + o);
-#pragma unroll
-            for (int q = 1; q < NWAVE; ++q) sum += *reinterpret_cast<const f4_t *>(red0 + (size_t)q * W + o);
-            float *dst = out + (size_t)gm * N + gc;
-            if (!raw && vec_store) {
-                epi_put4(epi, C, gm, gc, N, sum);
-            } else if (!raw) {
+            const f4_t v = sum4(R);
+            if (gc < N) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (gc + e < N) epi_put(epi, C, gm, gc + e, N, sum[e]);
-            } else if (vec_store) {
-                *reinterpret_cast<f4_t *>(dst) = sum;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (gc + e < N) dst[e] = sum[e];
+                    if (gm + e < M) out[(size_t)(gm + e) * N + gc] = v[e];
+            }
+        }
+    } else {
+#pragma unroll 1
+        for (int it = 0; it < RG / GPP; ++it) {
+            const int R = it * GPP + g0, gm = m0 + 4 * R;
+            if (gm >= M) break;
+            const f4_t v = sum4(R);
+            if (gc < N) {
+                for (int e = 0; e < 4 && gm + e < M; ++e) epi_put(epi, C, gm + e, gc, N, v[e]);
             }
         }
     }
