@@ -452,6 +452,26 @@ __global__ __launch_bounds__(64 * I8_WAVES) void gemv_int8b0_kernel(
     const int nc = min(n, Np - 1);
     const int nchunk = Kp >> 4;              // 16-byte slices per channel
 
+    // 0. the activation pieces this thread stages, requested first: loads
+    //    complete in order, so staged after the weights they would wait for
+    //    the wave's whole weight stream (when at most two per thread; else
+    //    they are loaded in step 2)
+    const int pieces = Kp >> 3;
+    constexpr int AS = (MR * NCH * 128 + 64 * I8_WAVES - 1) / (64 * I8_WAVES);   // >= slots needed
+    constexpr bool A_FIRST = AS <= 2;
+    const bool vec_a = (K & 7) == 0;
+    u4_t araw[A_FIRST ? AS : 1];
+    if constexpr (A_FIRST) {
+#pragma unroll
+        for (int sl = 0; sl < AS; ++sl) {
+            const int p = tid + 64 * I8_WAVES * sl;
+            const int r = p / pieces, c = p - r * pieces;
+            araw[sl] = u4_t{0u, 0u, 0u, 0u};
+            if (vec_a && p < MR * pieces && m0 + r < M && c * 8 < K)
+                araw[sl] = *reinterpret_cast<const u4_t *>(A + (size_t)(m0 + r) * K + (size_t)c * 8);
+        }
+    }
+
     // 1. this wave's code slices and pair
     u4_t wq[NCH];
 #pragma unroll
@@ -477,12 +497,13 @@ __global__ __launch_bounds__(64 * I8_WAVES) void gemv_int8b0_kernel(
 #pragma unroll
     for (int r = 0; r < MR; ++r) part[r] = 0.f;
     const h2_t one = {(_Float16)1.0f, (_Float16)1.0f};
-    if ((K & 7) == 0) {
-        const int pieces = Kp >> 3;
-        for (int p = tid; p < MR * pieces; p += 64 * I8_WAVES) {
+    if (vec_a) {
+        for (int p = tid, sl = 0; p < MR * pieces; p += 64 * I8_WAVES, ++sl) {
             const int r = p / pieces, c = p - r * pieces;
             u4_t v = {0u, 0u, 0u, 0u};
-            if (m0 + r < M && c * 8 < K)
+            if constexpr (A_FIRST)
+                v = araw[sl < AS ? sl : 0];
+            else if (m0 + r < M && c * 8 < K)
                 v = *reinterpret_cast<const u4_t *>(A + (size_t)(m0 + r) * K + (size_t)c * 8);
             *reinterpret_cast<u4_t *>(As + (size_t)r * Kp + (size_t)c * 8) = v;
             float sp = 0.f;
