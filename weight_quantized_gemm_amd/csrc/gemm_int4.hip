@@ -438,7 +438,9 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     };
     // (the two store forms in separate loops, the epilogue one not unrolled:
     // one copy of its code per row group would not stay in the instruction
-    // cache)
+    // cache). The raw stores are non-temporal: C is not read again here, and
+    // streamed past the caches its write-back no longer competes with the
+    // next kernel's loads.
     if (raw) {
 #pragma unroll
         for (int it = 0; it < RG / GPP; ++it) {
@@ -448,7 +450,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
             if (gc < N) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (gm + e < M) out[(size_t)(gm + e) * N + gc] = v[e];
+                    if (gm + e < M) __builtin_nontemporal_store(v[e], out + (size_t)(gm + e) * N + gc);
             }
         }
     } else {
