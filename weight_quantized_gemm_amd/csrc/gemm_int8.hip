@@ -342,11 +342,11 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
             for (int e = 0; e < 4; ++e)
                 if (gc + e < N) epi_put(epi, C, gm, gc + e, N, out[e]);
         } else if (vec_store) {
-            *reinterpret_cast<f4_t *>(dst) = out;
+            __builtin_nontemporal_store(out, reinterpret_cast<f4_t *>(dst));   // C is not read again here
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if (gc + e < N) dst[e] = out[e];
+                if (gc + e < N) __builtin_nontemporal_store(out[e], dst + e);
         }
     }
 }
