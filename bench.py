@@ -207,7 +207,7 @@ def oracle_pass(dec: Workload, pre: Workload, budget_s: float):
     t_dec_1 = time.perf_counter() - t0
     _omp_threads(prev)
     qp, pp = O.quantize(pre.W_host, "int4b64")
-    probe = 2
+    probe = 16    # (two rows keep most threads idle and overstate the per-row time about fivefold)
     t0 = time.perf_counter()
     O.gemm_blockq(pre.A_host[:probe], qp, pp, "int4b64", lib)
     t_probe = (time.perf_counter() - t0) / probe
