@@ -23,7 +23,7 @@ from weight_quantized_gemm_amd import build_lib
 HIPCC = build_lib.HIPCC
 
 # (BM, BN) -> (A_TILES, A_PIECES, A_WAIT); mirrors TileCfg in gemm_int4.hip
-TILES = {(128, 64): (2, 16, 2), (64, 128): (4, 8, 36)}
+TILES = {(128, 64): (2, 16, 2), (64, 128): (4, 8, 36), (128, 128): (2, 16, 4)}
 
 
 def _asm(tmpdir: str) -> str:

@@ -40,7 +40,7 @@ SHAPES = [("f32", 16, 256, 256), ("f32", 8, 2560, 1024), ("f32", 130, 512, 200),
           ("int8b0", 32, 2560, 256), ("f16", 9, 4096, 96), ("int4b32", 96, 1024, 300),
           ("int4b64", 3, 9728, 640), ("w4a8", 2, 9728, 640), ("int8b64", 3, 1024, 130),
           ("int8b32", 130, 640, 200), ("int4b16", 96, 1024, 300), ("int8b16", 3, 1024, 130),
-          ("int4b48", 2, 2496, 300)]
+          ("int4b48", 2, 2496, 300), ("int4b64", 1000, 640, 2300)]
 EPILOGUES = [("bias", "silu", "f32", False), ("residual", "gelu", "f16", False),
              ("bias+residual", "relu", "f32", False), ("bias+residual", "gelu", "f16", True),
              ("bias+residual", "none", "f32", True)]

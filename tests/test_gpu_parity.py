@@ -225,6 +225,20 @@ def test_int4b64_split_k(M, K, N):
     assert np.array_equal(C1, C2) and np.array_equal(C1, C3)
 
 
+@pytest.mark.parametrize("fmt,M,K,N,sample", [("int4b64", 1000, 640, 2300, False),
+                                               ("int4b32", 1000, 640, 2300, False),
+                                               ("int4b16", 1024, 320, 2304, False),
+                                               ("int4b64", 2000, 1088, 4000, True)])
+def test_int4_wide_tiles(fmt, M, K, N, sample):
+    """Shapes whose 128 x 128 tiles take fewer rounds of the CUs than 128 x 64
+    ones (8 x 18 = 144 tiles in one round against 288 in two; 16 x 32 = 512
+    in two against 1008 in four): the wide tile's two-chunk reduction, ragged
+    last row and column tiles, and K quarters of unequal length. The largest
+    shape is compared on rows spanning every row tile and its edges."""
+    rows = sorted({*range(0, M, 61), 127, 128, 1919, 1920, M - 1}) if sample else None
+    _parity(fmt, M, K, N, seed=M + K + N, rows=rows)
+
+
 @pytest.mark.parametrize("M,K,N,split", [(16, 256, 256, False), (3, 137, 70, False),
                                          (8, 2560, 1024, True), (1, 9728, 64, True),
                                          (40, 640, 100, False), (17, 4096, 4096, True),

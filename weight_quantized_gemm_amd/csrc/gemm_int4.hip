@@ -18,7 +18,12 @@
 //    128 x 64 once M reaches 128 (each dequantised weight then serves 128
 //    rows, which halves the dequantising instructions per matrix
 //    instruction: the vector ALUs, not the matrix cores, bound this kernel),
-//    64 x 128 below (half the rows of a 128-row tile would be padding);
+//    64 x 128 below (half the rows of a 128-row tile would be padding), and
+//    128 x 128 where those tiles need fewer rounds of the CUs (M >= 1024 at
+//    N = 4096): each A byte brought into the CU then serves twice the
+//    columns, which the texture unit carrying A into LDS (busy two thirds of
+//    the 128 x 64 kernel's life) had limited; its 256 accumulators per lane
+//    take all the AGPRs;
 //  - each of its four waves (one per SIMD) accumulates the whole tile over
 //    one contiguous quarter of K with v_mfma_f32_32x32x16_f16 (BM/32 x BN/32
 //    accumulator tiles), so every B element is fetched and dequantised once
@@ -43,7 +48,8 @@
 //  - the instructions of one MFMA step stay in one scheduling region, and
 //    each dequantised operand is pinned where it is produced, so no matrix
 //    instruction waits on a vector instruction moved next to it;
-//  - the four partial tiles meet in LDS and are summed in a fixed order.
+//  - the four partial tiles meet in LDS and are summed in a fixed order (a
+//    128 x 128 tile in two chunks of 64 columns).
 // Lane (r, h) = (lane % 32, lane / 32) holds K-elements 32 h + 8 s .. +7 of
 // every 64-wide block in MFMA step s, for its A row and B column alike (the K
 // order inside an MFMA only has to agree between A and B).
@@ -93,8 +99,11 @@ struct TileCfg {
     static_assert(UNROLL % A_TILES == 0 && UNROLL % B_RING == 0, "ring sizes");
     static_assert(A_WAIT <= 63 && PRO_WAIT <= 63, "vmcnt range");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 workgroup");
-    // a wave's partial tile (BM x BN fp32) takes exactly its A tiles' space
-    static_assert((size_t)BM * BN * 4 == WAVE_LDS, "partial tile fills the wave's LDS");
+    // a wave's partial tile (BM x BN fp32) goes through its A tiles' space in
+    // NCH chunks of CWID columns
+    static constexpr int CWID = (int)(WAVE_LDS / ((size_t)BM * 4));
+    static constexpr int NCH = BN / CWID;
+    static_assert(NCH * CWID == BN && CWID % 32 == 0 && CWID >= 64, "whole column chunks");
 };
 
 // Per (channel tile, block) dequantisation constants. Even codes decode as
@@ -229,13 +238,20 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     constexpr unsigned PREC = 256u * G;           // bytes per pair record
     constexpr int GQ = G == 4 ? 2 : 1;            // pair constants per lane and block
     using PairT = typename std::conditional<G == 4, f4_t, f2_t>::type;
-    __amdgpu_buffer_rsrc_t b_rs[CF], p_rs[CF];
+    // (the pair records of the CF tiles are consecutive: one resource over
+    // them, each tile at a scalar offset, saves the scalar registers of
+    // CF - 1 resources)
+    __amdgpu_buffer_rsrc_t b_rs[CF];
+    unsigned p_tile[CF];
+    const int t0 = min(n0 / 32, ntiles_b - 1);
 #pragma unroll
     for (int cf = 0; cf < CF; ++cf) {
         const size_t rec0 = (size_t)min(n0 / 32 + cf, ntiles_b - 1) * nblk;
         b_rs[cf] = byte_rsrc(Wp + rec0 * 1024, (unsigned)nblk * 1024u);
-        p_rs[cf] = byte_rsrc(reinterpret_cast<const char *>(Sp) + rec0 * PREC, (unsigned)nblk * PREC);
+        p_tile[cf] = (unsigned)(min(n0 / 32 + cf, ntiles_b - 1) - t0) * (unsigned)nblk * PREC;
     }
+    const __amdgpu_buffer_rsrc_t p_rs = byte_rsrc(reinterpret_cast<const char *>(Sp) + (size_t)t0 * nblk * PREC,
+                                                  p_tile[CF - 1] + (unsigned)nblk * PREC);
     const unsigned b_off = (unsigned)lane * 16u;
     const unsigned p_off = G == 4 ? (unsigned)(4 * r + 2 * h) * 8u
                          : G == 2 ? (unsigned)(32 * h + r) * 8u : (unsigned)r * 8u;
@@ -260,9 +276,9 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
 #pragma unroll
         for (int cf = 0; cf < CF; ++cf) {
             if constexpr (G == 4)
-                pairs[cf] = __builtin_bit_cast(f4_t, buf_load16(p_rs[cf], p_off, (unsigned)kt * PREC));
+                pairs[cf] = __builtin_bit_cast(f4_t, buf_load16(p_rs, p_off, p_tile[cf] + (unsigned)kt * PREC));
             else
-                pairs[cf] = buf_load8(p_rs[cf], p_off, (unsigned)kt * PREC);
+                pairs[cf] = buf_load8(p_rs, p_off, p_tile[cf] + (unsigned)kt * PREC);
         }
     };
     // a block's dequantisation constants: set 0 for MFMA steps 0-1, set
@@ -410,27 +426,11 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
     //      the accumulator layout and when read back. One store instruction
     //      writes 64 consecutive columns of a row. ----
     constexpr int RG = BM / 4;                     // four-row groups per column
-    constexpr int GPP = 64 * NWAVE / BN;           // row groups per pass
+    constexpr int CWID = T::CWID, NCH = T::NCH;
+    constexpr int GPP = 64 * NWAVE / CWID;         // row groups per pass
     static_assert(RG % GPP == 0 && RG >= 16, "whole passes, swizzle within the column");
     __builtin_amdgcn_s_waitcnt(vm_wait(0));
-    {
-        float *mine = reinterpret_cast<float *>(a_lds);
-#pragma unroll
-        for (int rf = 0; rf < RF; ++rf)
-#pragma unroll
-            for (int cf = 0; cf < CF; ++cf)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    // rows 32 rf + 8 g + 4 h + (0 .. 3) of column 32 cf + r
-                    const int R = 8 * rf + 2 * g + h, col = 32 * cf + r;
-                    *reinterpret_cast<f4_t *>(mine + (size_t)col * BM + 4 * (R ^ (col & 15))) =
-                        f4_t{acc[rf][cf][4 * g], acc[rf][cf][4 * g + 1], acc[rf][cf][4 * g + 2],
-                             acc[rf][cf][4 * g + 3]};
-                }
-    }
-    __syncthreads();
-    const int col = tid % BN, g0 = tid / BN;       // g0 is wave-uniform (BN >= 64)
-    const int gc = n0 + col;
+    const int col = tid % CWID, g0 = tid / CWID;   // g0 is wave-uniform (CWID >= 64)
     const float *red0 = reinterpret_cast<const float *>(lds);
     constexpr size_t W = T::WAVE_LDS / 4;          // floats per wave's partial tile
     auto sum4 = [&](int R) {
@@ -440,31 +440,56 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_int4b64_kernel(
         for (int q = 1; q < NWAVE; ++q) v += *reinterpret_cast<const f4_t *>(red0 + (size_t)q * W + o);
         return v;
     };
-    // (the two store forms in separate loops, the epilogue one not unrolled:
-    // one copy of its code per row group would not stay in the instruction
-    // cache). The raw stores are non-temporal: C is not read again here, and
-    // streamed past the caches its write-back no longer competes with the
-    // next kernel's loads.
-    if (raw) {
+    // A tile wider than the wave's LDS space (BN > CWID) goes through it in
+    // column chunks, a barrier before each chunk's writes and each chunk's
+    // reads.
 #pragma unroll
-        for (int it = 0; it < RG / GPP; ++it) {
-            const int R = it * GPP + g0, gm = m0 + 4 * R;
-            if (gm >= M) break;
-            const f4_t v = sum4(R);
-            if (gc < N) {
+    for (int ch = 0; ch < NCH; ++ch) {
+        if (ch > 0) __syncthreads();
+        {
+            float *mine = reinterpret_cast<float *>(a_lds);
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (gm + e < M) __builtin_nontemporal_store(v[e], out + (size_t)(gm + e) * N + gc);
-            }
+            for (int rf = 0; rf < RF; ++rf)
+#pragma unroll
+                for (int cc = 0; cc < CWID / 32; ++cc)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        // rows 32 rf + 8 g + 4 h + (0 .. 3) of chunk column 32 cc + r
+                        const int cf = ch * (CWID / 32) + cc;
+                        const int R = 8 * rf + 2 * g + h, lc = 32 * cc + r;
+                        *reinterpret_cast<f4_t *>(mine + (size_t)lc * BM + 4 * (R ^ (lc & 15))) =
+                            f4_t{acc[rf][cf][4 * g], acc[rf][cf][4 * g + 1], acc[rf][cf][4 * g + 2],
+                                 acc[rf][cf][4 * g + 3]};
+                    }
         }
-    } else {
+        __syncthreads();
+        const int gc = n0 + ch * CWID + col;
+        // (the two store forms in separate loops, the epilogue one not
+        // unrolled: one copy of its code per row group would not stay in the
+        // instruction cache). The raw stores are non-temporal: C is not read
+        // again here, and streamed past the caches its write-back no longer
+        // competes with the next kernel's loads.
+        if (raw) {
+#pragma unroll
+            for (int it = 0; it < RG / GPP; ++it) {
+                const int R = it * GPP + g0, gm = m0 + 4 * R;
+                if (gm >= M) break;
+                const f4_t v = sum4(R);
+                if (gc < N) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (gm + e < M) __builtin_nontemporal_store(v[e], out + (size_t)(gm + e) * N + gc);
+                }
+            }
+        } else {
 #pragma unroll 1
-        for (int it = 0; it < RG / GPP; ++it) {
-            const int R = it * GPP + g0, gm = m0 + 4 * R;
-            if (gm >= M) break;
-            const f4_t v = sum4(R);
-            if (gc < N) {
-                for (int e = 0; e < 4 && gm + e < M; ++e) epi_put(epi, C, gm + e, gc, N, v[e]);
+            for (int it = 0; it < RG / GPP; ++it) {
+                const int R = it * GPP + g0, gm = m0 + 4 * R;
+                if (gm >= M) break;
+                const f4_t v = sum4(R);
+                if (gc < N) {
+                    for (int e = 0; e < 4 && gm + e < M; ++e) epi_put(epi, C, gm + e, gc, N, v[e]);
+                }
             }
         }
     }
@@ -746,6 +771,8 @@ hipError_t launch_gemm_int4b64(int M, int K, int N, const void *A, const void *W
     const Int4Tile t = int4_tile(M, N);
     hipError_t e = t.bn == 32 ? (t.bm == 32 ? launch_skinny<1>(M, K, N, A, Wp, Sp, out, epi, pair_g, nsplit, s)
                                             : launch_skinny<2>(M, K, N, A, Wp, Sp, out, epi, pair_g, nsplit, s))
+                 : t.bm == 128 && t.bn == 128
+        ? launch_tiles<TileCfg<128, 128>>(M, K, N, A, Wp, Sp, out, epi, pair_g, nsplit, s)
                  : t.bm == 128
         ? launch_tiles<TileCfg<128, 64>>(M, K, N, A, Wp, Sp, out, epi, pair_g, nsplit, s)
         : launch_tiles<TileCfg<64, 128>>(M, K, N, A, Wp, Sp, out, epi, pair_g, nsplit, s);

@@ -207,8 +207,9 @@ W4A8Workspace w4a8_workspace(int M, int K);
 // workspace size never depends on the device.
 // Output tile of the Int4-Block64 prefill GEMM (rows x columns), shared by
 // the kernel and the split-K planner: 128 x 64 once M reaches 128 (each
-// dequantised weight serves 128 rows), else 64 x 128, or the skinny
-// kernel's 32- or 64-row tiles of 32 channels (below).
+// dequantised weight serves 128 rows) or 128 x 128 where that takes fewer
+// rounds of the CUs, else 64 x 128, or the skinny kernel's 32- or 64-row
+// tiles of 32 channels (below).
 struct Int4Tile {
     int bm, bn;
 };
@@ -220,8 +221,18 @@ constexpr int kSplitTargetCUs = 256;
 // takes a second round of workgroups; the 64 x 128 tiles do better there.)
 constexpr int kSkinnyMaxM = 64;
 inline Int4Tile int4_tile(int M, int N) {
-    return M >= 128 ? Int4Tile{128, 64}
-         : M > kSkinnyMaxM || (N + 31) / 32 >= kSplitTargetCUs ? Int4Tile{64, 128}
+    if (M >= 128) {
+        // 128 x 128 tiles (each A element serves twice the columns per byte
+        // brought into the CU) take 1.73x the time of a 128 x 64 tile per
+        // round of 256 CUs (1024 x 4096 x 4096: 41.6 us in one round against
+        // 48.0 in two); they run where their rounds cost less, which needs
+        // more than 128 of them (so they never split K)
+        const int tm = div_up(M, 128);
+        const long long r128 = ((long long)tm * div_up(N, 128) + kSplitTargetCUs - 1) / kSplitTargetCUs;
+        const long long r64 = ((long long)tm * div_up(N, 64) + kSplitTargetCUs - 1) / kSplitTargetCUs;
+        return 7 * r128 < 4 * r64 ? Int4Tile{128, 128} : Int4Tile{128, 64};
+    }
+    return M > kSkinnyMaxM || (N + 31) / 32 >= kSplitTargetCUs ? Int4Tile{64, 128}
          : M > 32 ? Int4Tile{64, 32} : Int4Tile{32, 32};
 }
 // Output tile of the channel-row (Int8-Block0, fp16-weight) prefill GEMM.
