@@ -162,7 +162,28 @@ int splitk_plan(qgemm_format f, int M, int K, int N) {
         // each slice keeps four or more K stages (one turn of the load ring)
         tiles = (long long)div_up(M, kW4A8TileM) * div_up(N, kW4A8TileN);
         kunits = (int)(round_up((size_t)K, kW4A8StageK) / kW4A8StageK) / 4;
-        break;
+        {
+            // The slices' int32 partial tiles and their reduce cost time in
+            // proportion to (slices + 1) x M x N, which outweighs the shorter
+            // K of each slice where M x N is large and K short (512 x 2560 x
+            // 4096: 24.5 us unsplit, 31.6 in four slices). Estimated time,
+            // fitted to the benchmark page's shapes at M = 128 and 512 (us):
+            // 4 per 1000 K-elements of a slice, plus for a split 4 and 0.2
+            // per MB of (slices + 1) x M x N x 4 bytes.
+            tiles = (long long)div_up(M, kW4A8TileM) * div_up(N, kW4A8TileN);
+            if (tiles >= kSplitTargetCUs / 2) return 1;
+            long long cap = kSplitTargetCUs / tiles;
+            if (cap > kMaxSplit) cap = kMaxSplit;
+            if (cap > kunits) cap = kunits;
+            const double mn_mb = (double)M * N * 4 / 1e6;
+            int best = 1;
+            double best_t = 0.004 * K;
+            for (int sp = 2; sp <= cap; ++sp) {
+                const double t = 0.004 * K / sp + 4.0 + 0.2 * (sp + 1) * mn_mb;
+                if (t < best_t) { best = sp; best_t = t; }
+            }
+            return best;
+        }
     default:
         return 1;
     }
