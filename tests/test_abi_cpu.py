@@ -122,7 +122,8 @@ def test_split_k_workspace_plan():
     assert Q.qgemm_workspace_size(512, 4096, 4096, "f32") == 0       # 512 tiles
     w = Q.qgemm_workspace_size(8, 128, 16, "w4a8")
     assert w == Q.qgemm_workspace_size(8, 128, 16000, "w4a8")   # W4A8 scratch has no N part
-    # W4A8 GEMM: the slice count minimises 4 us per 1000 K of a slice plus, when
+    # W4A8 GEMM: shapes with fewer than 128 tiles split K; the slice count
+    # minimises 4 us per 1000 K of a slice plus, when
     # split, 4 us + 0.2 us per MB of (slices + 1) x M x N x 4 bytes (the plan
     # is a pure function of the shape); int32 partials follow the quantiser's
     # scratch, so the size less that of N = 1 (up to 8 slices x M x 4 bytes of
@@ -131,13 +132,19 @@ def test_split_k_workspace_plan():
         return Q.qgemm_workspace_size(M, K, N, "w4a8") - Q.qgemm_workspace_size(M, K, 1, "w4a8")
     assert w4a8_part(512, 2560, 4096) <= 0                     # 64 tiles, yet unsplit (8 MB per slice)
     assert w4a8_part(128, 2560, 9728) <= 0                     # 38 tiles, unsplit
-    assert w4a8_part(512, 4096, 2560) >= 4 * 512 * 2560 * 4 - 8 * 512 * 4    # four slices
+    assert w4a8_part(512, 4096, 2560) >= 3 * 512 * 2560 * 4 - 8 * 512 * 4    # three slices of 80 tiles
     assert w4a8_part(128, 2560, 1024) >= 5 * 128 * 1024 * 4 - 8 * 128 * 4    # five (the K cap)
     # the estimate written out: slices for a shape with few tiles
     def est(M, K, N, sp):
         return 0.004 * K / sp + (0 if sp == 1 else 4 + 0.2 * (sp + 1) * M * N * 4 / 1e6)
-    for M, K, N in [(512, 2560, 4096), (512, 9728, 2560), (128, 9728, 2560), (300, 4096, 1000)]:
-        tiles = -(-M // 128) * -(-N // 256)
+    # (tiles of 128 x 128 while those fit 256 CUs, else 128 x 256)
+    for M, K, N in [(512, 2560, 4096), (512, 9728, 2560), (128, 9728, 2560), (300, 4096, 1000),
+                    (1024, 4096, 4096), (2048, 2048, 2048)]:
+        t128 = -(-M // 128) * -(-N // 128)
+        tiles = t128 if t128 <= 256 else -(-M // 128) * -(-N // 256)
+        if tiles >= 128:
+            assert w4a8_part(M, K, N) <= 0, (M, K, N)
+            continue
         cap = min(256 // tiles, 8, -(-K // 128) // 4)
         sp = min(range(1, cap + 1), key=lambda s: (est(M, K, N, s), s))
         part = w4a8_part(M, K, N)

@@ -239,6 +239,17 @@ def test_int4_wide_tiles(fmt, M, K, N, sample):
     _parity(fmt, M, K, N, seed=M + K + N, rows=rows)
 
 
+@pytest.mark.parametrize("M,K,N", [(1000, 256, 4000), (512, 2560, 4096), (200, 8190, 1000)])
+def test_w4a8_half_width_tiles(M, K, N):
+    """W4A8 shapes whose 128 x 128 tiles fit one round of the CUs (two rows of
+    four waves, 64 x 32 each): 256 tiles with ragged last row and column
+    tiles (the staged fp32 store's element path), 128 tiles unsplit, and a
+    split shape with a ragged K; D bit-exact where checked."""
+    _parity("w4a8", M, K, N, seed=M + K + N)
+    if M <= 512:
+        _w4a8_debug_check(M, K, N, seed=M + K + N + 1, zero_row=3)
+
+
 @pytest.mark.parametrize("M,K,N,split", [(16, 256, 256, False), (3, 137, 70, False),
                                          (8, 2560, 1024, True), (1, 9728, 64, True),
                                          (40, 640, 100, False), (17, 4096, 4096, True),

@@ -160,7 +160,7 @@ int splitk_plan(qgemm_format f, int M, int K, int N) {
         break;
     case QGEMM_W4A8:
         // each slice keeps four or more K stages (one turn of the load ring)
-        tiles = (long long)div_up(M, kW4A8TileM) * div_up(N, kW4A8TileN);
+        tiles = (long long)div_up(M, kW4A8TileM) * div_up(N, w4a8_tile_n(M, N));
         kunits = (int)(round_up((size_t)K, kW4A8StageK) / kW4A8StageK) / 4;
         {
             // The slices' int32 partial tiles and their reduce cost time in
@@ -170,7 +170,7 @@ int splitk_plan(qgemm_format f, int M, int K, int N) {
             // fitted to the benchmark page's shapes at M = 128 and 512 (us):
             // 4 per 1000 K-elements of a slice, plus for a split 4 and 0.2
             // per MB of (slices + 1) x M x N x 4 bytes.
-            tiles = (long long)div_up(M, kW4A8TileM) * div_up(N, kW4A8TileN);
+            tiles = (long long)div_up(M, kW4A8TileM) * div_up(N, w4a8_tile_n(M, N));
             if (tiles >= kSplitTargetCUs / 2) return 1;
             long long cap = kSplitTargetCUs / tiles;
             if (cap > kMaxSplit) cap = kMaxSplit;

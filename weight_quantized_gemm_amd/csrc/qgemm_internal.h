@@ -239,6 +239,16 @@ inline Int4Tile int4_tile(int M, int N) {
 constexpr int kRowsTileM = 128, kRowsTileN = 64;
 // Output tile of the W4A8 prefill GEMM and its K stage (qa bytes per row).
 constexpr int kW4A8TileM = 128, kW4A8TileN = 256, kW4A8StageK = 128;
+// Columns of a W4A8 tile for a shape: 128 while 128-column tiles fit one
+// round of the CUs (twice the workgroups for shapes with few tiles, so less
+// K splitting), else 256. Measured on the benchmark page's shapes at M = 32
+// to 1024 (us, 256 -> 128 columns): 512 x 2560 x 4096 24.5 -> 20.3, 1024 x
+// 4096 x 2560 36.3 -> 29.0, 128 x 2560 x 9728 23.5 -> 19.8; with more tiles
+// than that 256 columns stay faster (1024 x 3072 x 8192: 36.6 against 43.6).
+inline int w4a8_tile_n(int M, int N) {
+    return (long long)div_up(M, kW4A8TileM) * div_up(N, kW4A8TileN / 2) <= kSplitTargetCUs ? kW4A8TileN / 2
+                                                                                          : kW4A8TileN;
+}
 // Output tiles of the fp32 GEMM: 16 x 64 for M <= 16, else 64 x 64; K in
 // chunks of 64.
 constexpr int kF32TileN = 64, kF32TileMSmall = 16, kF32TileM = 64, kF32ChunkK = 64;

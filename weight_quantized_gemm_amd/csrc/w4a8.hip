@@ -155,7 +155,9 @@ hipError_t launch_w4a8_actquant(int M, int K, int Kq, const void *A, int8_t *qa,
 // ---------------------------------------------------------------------------
 // int8 GEMM. A 512-thread workgroup owns a 128 x 256 tile of C; wave w owns
 // the 128 x 32 column block 32 w and runs every K step with
-// v_mfma_i32_32x32x32_i8 (4 accumulator tiles). Each wave loads only its own
+// v_mfma_i32_32x32x32_i8 (4 accumulator tiles). Shapes whose 128 x 128
+// tiles fit one round of the CUs take those instead (two rows of four
+// waves, each wave 64 x 32): twice the workgroups, so fewer K slices. Each wave loads only its own
 // weight record, so no weight byte enters a CU twice; two waves per SIMD
 // overlap one wave's loads and LDS reads with the other's matrix work. (The
 // wave grid is a parameter: a 2 x 4 grid of 64 x 64 wave tiles halves the
@@ -180,12 +182,18 @@ hipError_t launch_w4a8_actquant(int M, int K, int Kq, const void *A, int8_t *qa,
 // each 64-wide block in step s for its A row and B column alike.
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int WBM = kW4A8TileM, WBN = kW4A8TileN, WSK = kW4A8StageK;
+constexpr int WBM = kW4A8TileM, WSK = kW4A8StageK;
 constexpr int WNW = 8;                    // waves
-constexpr int WGN = 8, WGM = WNW / WGN;          // wave grid: WGM rows x WGN columns
-constexpr int WRF = WBM / (32 * WGM);            // 32-row fragments per wave
-constexpr int WCF = WBN / (32 * WGN);            // 32-column fragments per wave
-static_assert(WRF % 2 == 0 && WCF >= 1 && WRF * WCF <= 4, "wave tile of 64k x 32 rows x columns");
+// Wave grid: WGM_ rows x (8 / WGM_) columns of (128 / WGM_) x 32 wave tiles,
+// so the tile is 128 x 256 (one row of waves) or 128 x 128 (two).
+template <int WGM_>
+struct W4Grid {
+    static constexpr int WGM = WGM_, WGN = WNW / WGM_;
+    static constexpr int WBN = 32 * WGN;                 // tile columns
+    static constexpr int WRF = WBM / (32 * WGM);         // 32-row fragments per wave
+    static constexpr int WCF = 1;                        // 32-column fragments per wave
+    static_assert(WRF % 2 == 0 && WRF * WCF <= 4 && WBN == kW4A8TileN / WGM_, "wave tile of 64k x 32 rows");
+};
 constexpr int WAROW = WSK + 16;           // bytes per LDS row of an A stage (144)
 constexpr int WRING = 4;                  // stages: LDS A tiles = A and B register ring slots
 constexpr size_t WAS_BYTES = (size_t)WBM * WAROW;
@@ -196,11 +204,13 @@ __device__ __forceinline__ i4_t unpack_codes(unsigned w0, unsigned w1) {
     return i4_t{(int)(w0 & m), (int)((w0 >> 4) & m), (int)(w1 & m), (int)((w1 >> 4) & m)};
 }
 
-template <bool DEBUG_D>
+template <bool DEBUG_D, int WGM_>
 __global__ __launch_bounds__(64 * WNW) void w4a8_gemm_kernel(
     int M, int N, int Kq, int nkc, int tiles_n, const int8_t *__restrict__ qa,
     const float *__restrict__ sa, const int32_t *__restrict__ S, const uint8_t *__restrict__ Wp,
     const f2_t *__restrict__ Sp, void *__restrict__ C, Epilogue epi, int32_t *__restrict__ D) {
+    using G = W4Grid<WGM_>;
+    constexpr int WGM = G::WGM, WGN = G::WGN, WBN = G::WBN, WRF = G::WRF, WCF = G::WCF;
     __shared__ __align__(16) int8_t As[WRING * WAS_BYTES];
     __shared__ float sa_s[WBM];
     __shared__ int S_s[WBM];
@@ -763,14 +773,15 @@ __global__ __launch_bounds__(256) void w4a8_splitk_reduce_kernel(
     else epi_put(epi, C, m, n, N, out);
 }
 
-hipError_t launch_w4a8_gemm(int M, int K, int N, int Kq, const int8_t *qa, const float *sa,
-                            const int32_t *S, const void *Wp, const void *Sp, void *C,
-                            const Epilogue &epi, int32_t *D_debug, int nsplit, int32_t *part,
-                            hipStream_t s) {
+template <int WGM_>
+static hipError_t launch_w4a8_gemm_grid(int M, int K, int N, int Kq, const int8_t *qa, const float *sa,
+                                        const int32_t *S, const void *Wp, const void *Sp, void *C,
+                                        const Epilogue &epi, int32_t *D_debug, int nsplit, int32_t *part,
+                                        hipStream_t s) {
     const int nkc = (int)round_up(K, 64) / 64;
-    const int tiles_m = div_up(M, WBM), tiles_n = div_up(N, WBN);
+    const int tiles_m = div_up(M, WBM), tiles_n = div_up(N, W4Grid<WGM_>::WBN);
     if (nsplit > 1) {
-        hipLaunchKernelGGL(w4a8_gemm_kernel<false>, dim3(tiles_m * tiles_n, nsplit), dim3(64 * WNW),
+        hipLaunchKernelGGL((w4a8_gemm_kernel<false, WGM_>), dim3(tiles_m * tiles_n, nsplit), dim3(64 * WNW),
                            0, s, M, N, Kq, nkc, tiles_n, qa, sa, S,
                            static_cast<const uint8_t *>(Wp), static_cast<const f2_t *>(Sp), C, epi,
                            part);
@@ -784,14 +795,23 @@ hipError_t launch_w4a8_gemm(int M, int K, int N, int Kq, const int8_t *qa, const
     }
     dim3 grid(tiles_m * tiles_n);
     if (D_debug)
-        hipLaunchKernelGGL(w4a8_gemm_kernel<true>, grid, dim3(64 * WNW), 0, s, M, N, Kq, nkc,
+        hipLaunchKernelGGL((w4a8_gemm_kernel<true, WGM_>), grid, dim3(64 * WNW), 0, s, M, N, Kq, nkc,
                            tiles_n, qa, sa, S, static_cast<const uint8_t *>(Wp),
                            static_cast<const f2_t *>(Sp), C, epi, D_debug);
     else
-        hipLaunchKernelGGL(w4a8_gemm_kernel<false>, grid, dim3(64 * WNW), 0, s, M, N, Kq, nkc,
+        hipLaunchKernelGGL((w4a8_gemm_kernel<false, WGM_>), grid, dim3(64 * WNW), 0, s, M, N, Kq, nkc,
                            tiles_n, qa, sa, S, static_cast<const uint8_t *>(Wp),
                            static_cast<const f2_t *>(Sp), C, epi, D_debug);
     return hipGetLastError();
+}
+
+hipError_t launch_w4a8_gemm(int M, int K, int N, int Kq, const int8_t *qa, const float *sa,
+                            const int32_t *S, const void *Wp, const void *Sp, void *C,
+                            const Epilogue &epi, int32_t *D_debug, int nsplit, int32_t *part,
+                            hipStream_t s) {
+    return w4a8_tile_n(M, N) == kW4A8TileN
+               ? launch_w4a8_gemm_grid<1>(M, K, N, Kq, qa, sa, S, Wp, Sp, C, epi, D_debug, nsplit, part, s)
+               : launch_w4a8_gemm_grid<2>(M, K, N, Kq, qa, sa, S, Wp, Sp, C, epi, D_debug, nsplit, part, s);
 }
 
 }  // namespace qg
